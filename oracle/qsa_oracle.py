@@ -1,0 +1,264 @@
+"""fp64 CPU oracle of the QSA layer forward pass.
+
+TEST INFRASTRUCTURE.  Only the tests, the package's smoke check and the CPU
+baseline leg of the benchmark may import this module.  The product path (the
+HIP library and its Python binding) never imports, links or calls it, and it
+imports nothing from the product.
+
+It follows the method step by step, in the pages' order and notation, in
+plain NumPy fp64, one query row at a time.  Sources:
+
+[concept] "QSA (Qwen Sparse Attention)" research-hub concept page,
+    section "Key math / How it works": (A) compressed lightweight indexer --
+    MQA layout (4 query heads, one shared key head, dim 128); block
+    compression k_hat_b = RMSNorm(AvgPool(keys of a block of r tokens));
+    partial RoPE on 64 of 128 dims, applied after compression; block
+    importance I_ib = sum_h ReLU(<q_i^h, k_bar_b>) with block-causal masking;
+    top-k_B selection, k_B = ceil(K/r), expanded to tokens plus the tail of
+    the current block.  (B) sparse core attention: full scaled-dot-product
+    attention restricted to the selected tokens.  "Config": K=2048, r=4.
+[gallery] "Qwen Sparse Attention" architecture-gallery page: the selection
+    unit/budget table (complete four-token blocks, up to 512 blocks plus the
+    current tail); "How block selection works" (blocks of keys preceding the
+    query, mean per complete block, normalisation, RoPE at each block's first
+    position, relu-sum scoring over indexer heads, top-k, expansion to token
+    positions plus the current incomplete block); the QSA-vs-DSA table (the
+    current incomplete block is included directly).
+
+Readings where the pages are silent (each is listed in the design doc):
+  * k_hat_b and k_bar_b are one vector: AvgPool -> RMSNorm -> partial RoPE.
+  * RMSNorm(x) = x / sqrt(mean(x^2) + eps) * g, over all idx_dim dims.
+  * RoPE rotates dims [0, rope_dims) in rotate-half pairs (j, j + rope_dims/2)
+    with theta_j = base^(-2j/rope_dims), at absolute position r*b.
+    PARITY UNPINNED: the pages fix neither the pairing nor the frequency
+    schedule; the tests pin only properties every RoPE has.
+  * Candidate blocks of a query at position p: b < floor(p/r) (complete
+    blocks strictly before the query's own block).  Tail: positions
+    r*floor(p/r) .. p inclusive (always contains p).
+  * Ties in I are broken toward the lower block index; the selection is
+    reported in ascending block order.
+  * Attention scale 1/sqrt(head_dim); main head h reads KV head
+    floor(h * Hkv / Hq); one selection per query is shared by every main head.
+  * Index rows are stored in the layer's storage dtype (bf16 or fp32),
+    rounded to nearest-even, before scoring ("storage" argument).
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass
+
+import numpy as np
+
+__all__ = [
+    "round_to_bf16", "round_to_f32", "avg_pool_blocks", "rms_norm", "rope_angles",
+    "partial_rope", "compress_index", "block_importance", "top_k_blocks",
+    "expand_with_tail", "sparse_attention", "RowResult", "qsa_row",
+]
+
+
+# ---------------------------------------------------------------------------
+# storage rounding (the index rows are kept in the layer's dtype)
+# ---------------------------------------------------------------------------
+def round_to_bf16(x) -> np.ndarray:
+    """Nearest bf16 value (8 significant bits), ties to even, as fp64.
+
+    Written from the definition: x = m * 2^e with m in [0.5, 1); keep 8 bits
+    of m with round-half-even (np.rint).  Values are O(1) here, so the bf16
+    exponent range (that of fp32) is never exceeded.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    m, e = np.frexp(x)
+    return np.ldexp(np.rint(np.ldexp(m, 8)), e - 8)
+
+
+def round_to_f32(x) -> np.ndarray:
+    """Nearest fp32 value, ties to even, as fp64."""
+    return np.asarray(x, dtype=np.float64).astype(np.float32).astype(np.float64)
+
+
+_STORAGE = {"bf16": round_to_bf16, "f32": round_to_f32, "f64": lambda x: np.asarray(x, np.float64)}
+
+
+# ---------------------------------------------------------------------------
+# (A) compressed lightweight indexer -- block compression
+# ---------------------------------------------------------------------------
+def avg_pool_blocks(k_idx: np.ndarray, r: int, n_blocks: int) -> np.ndarray:
+    """AvgPool of the raw indexer keys over each complete block of r tokens.
+
+    [concept] (A) block compression; [gallery] "How block selection works":
+    the keys of each complete block are averaged.  Block b covers positions
+    r*b .. r*b + r - 1.
+    """
+    k = np.asarray(k_idx, dtype=np.float64)[: n_blocks * r]
+    return k.reshape(n_blocks, r, k.shape[-1]).mean(axis=1)
+
+
+def rms_norm(x: np.ndarray, gain, eps: float) -> np.ndarray:
+    """RMSNorm over the last axis: x / sqrt(mean(x^2) + eps) * g.
+
+    [concept] (A): k_hat_b = RMSNorm(AvgPool(...)); [gallery]: a normalisation
+    step follows the mean.  eps and g are not given by the pages.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    g = np.asarray(gain, dtype=np.float64)
+    ms = np.mean(x * x, axis=-1, keepdims=True)
+    return x / np.sqrt(ms + eps) * g
+
+
+def rope_angles(positions, rope_dims: int, base: float) -> np.ndarray:
+    """Rotation angle of pair j at each position: pos * base^(-2j/rope_dims)."""
+    j = np.arange(rope_dims // 2, dtype=np.float64)
+    theta = np.power(float(base), -2.0 * j / rope_dims)
+    return np.asarray(positions, dtype=np.float64)[:, None] * theta[None, :]
+
+
+def partial_rope(x: np.ndarray, positions, rope_dims: int, base: float) -> np.ndarray:
+    """Rotate dims [0, rope_dims) of each row at its position; keep the rest.
+
+    [concept] (A): RoPE on 64 of 128 dims, applied after compression.
+    Pair j = (j, j + rope_dims/2) is rotated by angle pos*theta_j:
+      x'_j = x_j cos a - x_{j+h} sin a ;  x'_{j+h} = x_{j+h} cos a + x_j sin a.
+    """
+    x = np.array(x, dtype=np.float64, copy=True)
+    h = rope_dims // 2
+    a = rope_angles(positions, rope_dims, base)
+    c, s = np.cos(a), np.sin(a)
+    lo = x[:, :h].copy()
+    hi = x[:, h:rope_dims].copy()
+    x[:, :h] = lo * c - hi * s
+    x[:, h:rope_dims] = hi * c + lo * s
+    return x
+
+
+def compress_index(k_idx: np.ndarray, n_blocks: int, *, r: int = 4, gain=None,
+                   eps: float = 1e-6, rope_dims: int = 64, base: float = 10000.0,
+                   storage: str = "bf16") -> np.ndarray:
+    """k_hat for blocks 0..n_blocks-1 of one sequence: AvgPool -> RMSNorm ->
+    partial RoPE at the block's first position r*b -> storage rounding.
+
+    [gallery] "How block selection works": mean per complete block, then a
+    normalisation step, then RoPE using the first position in each block.
+    """
+    d = np.asarray(k_idx).shape[-1]
+    g = np.ones(d) if gain is None else gain
+    pooled = avg_pool_blocks(k_idx, r, n_blocks)
+    normed = rms_norm(pooled, g, eps)
+    rotated = partial_rope(normed, r * np.arange(n_blocks), rope_dims, base)
+    return _STORAGE[storage](rotated)
+
+
+# ---------------------------------------------------------------------------
+# (A) block importance and top-k_B selection
+# ---------------------------------------------------------------------------
+def block_importance(q_idx_row: np.ndarray, k_hat: np.ndarray, c: int) -> np.ndarray:
+    """I_b = sum over indexer heads h of ReLU(<q^h, k_hat_b>) for b < c.
+
+    [concept] (A), block-importance equation; [gallery] pseudocode "scores"
+    line.  Block-causal masking: only the c complete blocks before the
+    query's own block are candidates.  ReLU returns +0.0 for x <= 0.
+    """
+    q = np.asarray(q_idx_row, dtype=np.float64)           # [H, d]
+    if c == 0:
+        return np.zeros(0)
+    dots = q @ np.asarray(k_hat[:c], dtype=np.float64).T  # [H, c]
+    return np.where(dots > 0.0, dots, 0.0).sum(axis=0)
+
+
+@dataclass
+class Selection:
+    blocks: np.ndarray   # ascending block ids, length count
+    count: int
+    order: np.ndarray    # all candidates by (I desc, b asc)
+    margin: float        # (I_(k) - I_(k+1)) / |I_(k)|, inf when c <= k_B
+
+
+def top_k_blocks(I: np.ndarray, k_B: int) -> Selection:
+    """The min(k_B, c) highest-scoring blocks, ties to the lower index.
+
+    [concept] (A): keep the k_B = ceil(K/r) highest-scoring blocks; the
+    selection is returned in ascending block order.
+    """
+    c = I.shape[0]
+    order = np.argsort(-I, kind="stable")  # stable: equal I keep index order
+    count = min(k_B, c)
+    blocks = np.sort(order[:count])
+    if c > k_B:
+        ik, ik1 = I[order[k_B - 1]], I[order[k_B]]
+        margin = (ik - ik1) / abs(ik) if ik != 0.0 else 0.0
+    else:
+        margin = math.inf
+    return Selection(blocks=blocks.astype(np.int64), count=count, order=order, margin=margin)
+
+
+def expand_with_tail(blocks: np.ndarray, p: int, r: int = 4) -> np.ndarray:
+    """Token positions attended by the query at position p.
+
+    [gallery] pseudocode "attention_input" line and the QSA-vs-DSA table:
+    every token of each selected block, plus the visible tokens of the
+    current incomplete block, positions r*floor(p/r) .. p.
+    """
+    toks = (r * np.asarray(blocks, dtype=np.int64)[:, None] + np.arange(r)[None, :]).reshape(-1)
+    tail = np.arange(r * (p // r), p + 1, dtype=np.int64)
+    return np.concatenate([toks, tail])
+
+
+# ---------------------------------------------------------------------------
+# (B) sparse core attention
+# ---------------------------------------------------------------------------
+def sparse_attention(q_row: np.ndarray, K: np.ndarray, V: np.ndarray, S: np.ndarray,
+                     scale: float):
+    """Scaled-dot-product attention of one query over the token set S.
+
+    [concept] (B).  q_row [Hq, d]; K, V [T, Hkv, d] of the query's sequence.
+    Head h reads KV head floor(h*Hkv/Hq).  Returns (o [Hq, d], lse [Hq]) with
+    lse the natural-log sum of exp of the scaled logits.
+    """
+    q = np.asarray(q_row, dtype=np.float64)
+    Hq, d = q.shape
+    Hkv = K.shape[1]
+    Ks = np.asarray(K[S], dtype=np.float64)   # [|S|, Hkv, d]
+    Vs = np.asarray(V[S], dtype=np.float64)
+    o = np.empty((Hq, d))
+    lse = np.empty(Hq)
+    for h in range(Hq):
+        g = (h * Hkv) // Hq
+        logits = scale * (Ks[:, g, :] @ q[h])
+        m = logits.max()
+        w = np.exp(logits - m)
+        z = w.sum()
+        o[h] = (w @ Vs[:, g, :]) / z
+        lse[h] = m + math.log(z)
+    return o, lse
+
+
+# ---------------------------------------------------------------------------
+# one query row, end to end
+# ---------------------------------------------------------------------------
+@dataclass
+class RowResult:
+    p: int
+    c: int
+    scores: np.ndarray      # full I row, length c
+    sel: Selection
+    S: np.ndarray
+    o: np.ndarray
+    lse: np.ndarray
+
+
+def qsa_row(p: int, q_idx_row, q_row, k_hat, K, V, *, k_B: int, r: int = 4,
+            scale: float | None = None, attend: bool = True) -> RowResult:
+    """Every step for the query at absolute position p of one sequence.
+
+    k_hat must hold at least floor(p/r) compressed blocks.
+    """
+    c = p // r
+    I = block_importance(q_idx_row, k_hat, c)
+    sel = top_k_blocks(I, k_B)
+    S = expand_with_tail(sel.blocks, p, r)
+    if attend:
+        d = np.asarray(q_row).shape[-1]
+        s = 1.0 / math.sqrt(d) if scale is None else scale
+        o, lse = sparse_attention(q_row, K, V, S, s)
+    else:
+        o = lse = None
+    return RowResult(p=p, c=c, scores=I, sel=sel, S=S, o=o, lse=lse)

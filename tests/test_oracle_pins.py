@@ -1,0 +1,372 @@
+"""Pins of the fp64 oracle against facts the method and mathematics fix.
+
+None of these re-types the oracle's formula: each checks a closed form, an
+invariant, a hand-worked example (tests/golden), a reduction to a library
+routine (torch CPU fp64 attention) or a brute-force count on tiny inputs.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+from hypothesis import given, settings, strategies as st
+
+from oracle import qsa_oracle as O
+from block_sparse_trainable_amd import synth
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "hand_examples.json")
+
+
+def _golden():
+    with open(GOLDEN) as f:
+        return {c["name"]: c for c in json.load(f)["cases"]}
+
+
+# ---------------------------------------------------------------- golden ----
+def test_golden_select_then_attend():
+    c = _golden()["select-then-attend"]
+    e = c["expect"]
+    k_idx = np.array(c["k_idx"], float)
+    nb = 2
+    kh = O.compress_index(k_idx, nb, r=c["r"], eps=c["eps"], rope_dims=c["rope_dims"],
+                          base=c["rope_base"], storage="f64")
+    np.testing.assert_allclose(kh, e["k_hat"], rtol=0, atol=1e-15)
+    res = O.qsa_row(c["p"], np.array(c["q_idx"], float), np.array(c["q"], float), kh,
+                    np.array(c["K"], float), np.array(c["V"], float), k_B=c["k_B"], r=c["r"])
+    np.testing.assert_allclose(res.scores, e["scores"], atol=1e-15)
+    assert res.sel.blocks.tolist() == e["selected"]
+    assert res.sel.margin == pytest.approx(e["margin"])
+    assert res.S.tolist() == e["tokens"]
+    np.testing.assert_allclose(res.o, e["o"], rtol=1e-13)
+    np.testing.assert_allclose(res.lse, e["lse"], rtol=1e-13)
+
+
+def test_golden_rope_at_block_start():
+    c = _golden()["rope-at-block-start"]
+    e = c["expect"]
+    kh = O.compress_index(np.array(c["k_idx"], float), 2, r=4, eps=0.0, rope_dims=2,
+                          base=c["rope_base"], storage="f64")
+    np.testing.assert_allclose(kh, e["k_hat"], atol=1e-14)
+    I = O.block_importance(np.array(c["q_idx"], float), kh, c["p"] // 4)
+    np.testing.assert_allclose(I, e["scores"], atol=1e-14)
+    sel = O.top_k_blocks(I, c["k_B"])
+    assert sel.blocks.tolist() == e["selected"]
+    assert O.expand_with_tail(sel.blocks, c["p"]).tolist() == e["tokens"]
+
+
+def test_golden_budget_constants():
+    e = _golden()["budget-constants"]["expect"]
+    lay = synth.Layout()
+    assert lay.k_blocks == e["k_B_2048_4"]
+    S = O.expand_with_tail(np.arange(lay.k_blocks), 4 * 10_000 + 3)
+    assert S.size == e["max_tokens_2048_4"]
+    assert synth.Layout(token_budget=64).k_blocks == e["k_B_64_4"]
+
+
+# ------------------------------------------------------------- AvgPool ------
+def test_avgpool_is_block_mean():
+    rng = np.random.default_rng(0)
+    mu = rng.standard_normal((7, 128))
+    delta = rng.standard_normal((7, 4, 128))
+    delta -= delta.mean(axis=1, keepdims=True)          # sum_t delta_t = 0
+    k = (mu[:, None, :] + delta).reshape(28, 128)
+    np.testing.assert_allclose(O.avg_pool_blocks(k, 4, 7), mu, atol=1e-13)
+
+
+def test_avgpool_ignores_incomplete_block():
+    k = np.arange(11 * 3, dtype=float).reshape(11, 3)
+    p = O.avg_pool_blocks(k, 4, 11 // 4)
+    assert p.shape == (2, 3)
+    np.testing.assert_allclose(p[1], k[4:8].sum(0) / 4)
+
+
+# ------------------------------------------------------------- RMSNorm ------
+def test_rmsnorm_unit_mean_square_and_scale_invariance():
+    rng = np.random.default_rng(1)
+    x = rng.standard_normal((5, 128)) * 3.7
+    y = O.rms_norm(x, np.ones(128), 0.0)
+    np.testing.assert_allclose((y * y).mean(axis=1), 1.0, rtol=1e-14)
+    np.testing.assert_allclose(O.rms_norm(x * 41.0, np.ones(128), 0.0), y, rtol=1e-13)
+    g = rng.uniform(0.5, 2.0, 128)
+    np.testing.assert_allclose(O.rms_norm(x, g, 0.0) / g, y, rtol=1e-13)
+
+
+def test_rmsnorm_eps_closed_form():
+    x = np.full((1, 4), 2.0)                 # mean square 4
+    y = O.rms_norm(x, np.ones(4), 5.0)       # 2 / sqrt(4 + 5) = 2/3
+    np.testing.assert_allclose(y, 2.0 / 3.0, rtol=1e-15)
+
+
+# ---------------------------------------------------------------- RoPE ------
+def test_rope_properties():
+    rng = np.random.default_rng(2)
+    x = rng.standard_normal((6, 128))
+    pos = np.array([0, 4, 8, 1000, 131072, 1048572])
+    y = O.partial_rope(x, pos, 64, 10000.0)
+    np.testing.assert_array_equal(y[0], x[0])                     # position 0: identity
+    np.testing.assert_array_equal(y[:, 64:], x[:, 64:])           # unrotated half
+    nx = x[:, :32] ** 2 + x[:, 32:64] ** 2                        # pair norms kept
+    ny = y[:, :32] ** 2 + y[:, 32:64] ** 2
+    np.testing.assert_allclose(ny, nx, rtol=1e-12)
+    # R(a) R(b) = R(a + b)
+    two = O.partial_rope(O.partial_rope(x[1:2], [4], 64, 1e4), [8], 64, 1e4)
+    np.testing.assert_allclose(two, O.partial_rope(x[1:2], [12], 64, 1e4), atol=1e-12)
+    # <R(p)x, R(p)z> = <x, z>, and <R(p)x, R(q)z> depends only on p - q
+    z = rng.standard_normal((1, 128))
+    a = O.partial_rope(x[2:3], [40], 64, 1e4) @ O.partial_rope(z, [40], 64, 1e4).T
+    np.testing.assert_allclose(a, x[2:3] @ z.T, rtol=1e-12)
+    d1 = O.partial_rope(x[2:3], [100], 64, 1e4) @ O.partial_rope(z, [60], 64, 1e4).T
+    d2 = O.partial_rope(x[2:3], [1040], 64, 1e4) @ O.partial_rope(z, [1000], 64, 1e4).T
+    np.testing.assert_allclose(d1, d2, rtol=1e-10)
+
+
+def test_rope_frequency_closed_form():
+    # pair j=16 of 32 has theta = 10000^(-1/2) = 0.01: at position 100 the
+    # angle is exactly 1 rad; unit vector on dim 16 goes to (cos1, sin1).
+    x = np.zeros((1, 128))
+    x[0, 16] = 1.0
+    y = O.partial_rope(x, [100], 64, 10000.0)
+    assert y[0, 16] == pytest.approx(math.cos(1.0), abs=1e-14)
+    assert y[0, 48] == pytest.approx(math.sin(1.0), abs=1e-14)
+
+
+def test_compress_rope_uses_block_first_position():
+    rng = np.random.default_rng(3)
+    k = rng.standard_normal((40, 128))
+    kh = O.compress_index(k, 10, storage="f64")
+    pooled = k.reshape(10, 4, 128).mean(1)
+    ms = (pooled ** 2).mean(1, keepdims=True)
+    # the norm of each rotated pair equals the norm of the normalised pair
+    n = pooled / np.sqrt(ms + 1e-6)
+    np.testing.assert_allclose(kh[:, :32] ** 2 + kh[:, 32:64] ** 2,
+                               n[:, :32] ** 2 + n[:, 32:64] ** 2, rtol=1e-12)
+    # block 3 is rotated as position 12 (its first token), not 13..15
+    alt = O.partial_rope(n[3:4], [13], 64, 1e4)
+    assert not np.allclose(alt, kh[3:4])
+    np.testing.assert_allclose(O.partial_rope(n[3:4], [12], 64, 1e4), kh[3:4], rtol=1e-12)
+
+
+# ------------------------------------------------------- storage rounding ---
+def test_round_to_bf16_matches_bit_definition():
+    rng = np.random.default_rng(4)
+    x = rng.standard_normal(200000).astype(np.float32)
+    # bf16 values are fp32 values with 16 zero low bits; neighbours differ
+    # by one unit in bit 16.  The rounded value must be one of the two
+    # neighbours and the nearer one (even on a tie).
+    u = x.view(np.uint32)
+    lo = (u & 0xFFFF0000).view(np.float32).astype(np.float64)
+    hi = ((u & 0xFFFF0000) + 0x10000).astype(np.uint32).view(np.float32).astype(np.float64)
+    r = O.round_to_bf16(x.astype(np.float64))
+    xd = x.astype(np.float64)
+    ok = (r == lo) | (r == hi)
+    assert ok.all()
+    dlo, dhi = np.abs(xd - lo), np.abs(xd - hi)
+    nearer = np.where(dlo < dhi, lo, np.where(dhi < dlo, hi, np.nan))
+    tie = np.isnan(nearer)
+    np.testing.assert_array_equal(r[~tie], nearer[~tie])
+    even_lo = ((u[tie] >> 16) & 1) == 0
+    np.testing.assert_array_equal(r[tie], np.where(even_lo, lo[tie], hi[tie]))
+    # the generator's fp32 -> bf16 rounding agrees on exact fp32 inputs
+    np.testing.assert_array_equal(synth.bf16_to_f32(synth.f32_to_bf16(x)).astype(np.float64), r)
+
+
+def test_round_to_bf16_ties():
+    # 1 + 2^-8 is halfway between 1 and 1 + 2^-7: ties to even -> 1
+    assert O.round_to_bf16(1.0 + 2.0 ** -8) == 1.0
+    # 1 + 3*2^-8 is halfway between 1+2^-7 and 1+2^-6: ties to even -> 1+2^-6
+    assert O.round_to_bf16(1.0 + 3 * 2.0 ** -8) == 1.0 + 2.0 ** -6
+    assert O.round_to_bf16(-(1.0 + 2.0 ** -8 + 2.0 ** -20)) == -(1.0 + 2.0 ** -7)
+
+
+# ------------------------------------------------------------- scores -------
+def test_scores_nonnegative_and_zero_iff_all_heads_nonpositive():
+    rng = np.random.default_rng(5)
+    q = rng.standard_normal((4, 16))
+    kh = rng.standard_normal((50, 16))
+    I = O.block_importance(q, kh, 50)
+    assert (I >= 0).all()
+    dots = kh @ q.T
+    np.testing.assert_array_equal(I == 0, (dots <= 0).all(axis=1))
+    # head permutation invariance
+    np.testing.assert_allclose(O.block_importance(q[[2, 0, 3, 1]], kh, 50), I, rtol=1e-14)
+
+
+def test_scores_reduce_to_matmul_for_nonnegative_inputs():
+    rng = np.random.default_rng(6)
+    q = np.abs(rng.standard_normal((4, 128)))
+    kh = np.abs(rng.standard_normal((300, 128)))
+    I = O.block_importance(q, kh, 300)
+    ref = np.matmul(kh, q.sum(axis=0))      # ReLU is the identity here
+    np.testing.assert_allclose(I, ref, rtol=1e-13)
+
+
+def test_scores_block_causal_mask():
+    rng = np.random.default_rng(7)
+    kh = rng.standard_normal((100, 8))
+    q = rng.standard_normal((4, 8))
+    for p in [0, 3, 4, 7, 8, 399]:
+        assert O.block_importance(q, kh, p // 4).shape == (p // 4,)
+
+
+# ------------------------------------------------------------- top-k --------
+def _brute_select(I, k):
+    """Rank by counting: b is selected iff fewer than k blocks beat it, where
+    b' beats b if I[b'] > I[b], or I[b'] == I[b] and b' < b."""
+    c = len(I)
+    chosen = []
+    for b in range(c):
+        beats = sum(1 for bb in range(c) if I[bb] > I[b] or (I[bb] == I[b] and bb < b))
+        if beats < k:
+            chosen.append(b)
+    return chosen
+
+
+@settings(max_examples=300, deadline=None)
+@given(st.lists(st.sampled_from([0.0, 0.0, 1.0, 2.0, 2.5, 3.0, 7.25]), min_size=0, max_size=64),
+       st.integers(min_value=1, max_value=8))
+def test_topk_matches_brute_force_with_ties(vals, k):
+    I = np.array(vals, dtype=float)
+    sel = O.top_k_blocks(I, k)
+    assert sel.blocks.tolist() == _brute_select(vals, k)
+    assert sel.count == min(k, len(vals))
+
+
+@settings(max_examples=200, deadline=None)
+@given(st.lists(st.floats(min_value=0, max_value=100, allow_nan=False), min_size=1, max_size=64),
+       st.integers(min_value=1, max_value=8))
+def test_topk_matches_brute_force_continuous(vals, k):
+    I = np.array(vals, dtype=float)
+    assert O.top_k_blocks(I, k).blocks.tolist() == _brute_select(vals, k)
+
+
+def test_topk_all_zero_row_takes_lowest_indices():
+    sel = O.top_k_blocks(np.zeros(20), 5)
+    assert sel.blocks.tolist() == [0, 1, 2, 3, 4]
+    assert sel.margin == 0.0
+
+
+def test_selection_invariants_on_random_rows():
+    rng = np.random.default_rng(8)
+    kh = rng.standard_normal((600, 128))
+    for p in [0, 1, 3, 4, 5, 63, 64, 67, 68, 2047, 2051, 2052, 2399]:
+        q = rng.standard_normal((4, 128))
+        res = O.qsa_row(p, q, None, kh, None, None, k_B=512, attend=False)
+        c = p // 4
+        assert res.sel.count == min(512, c)
+        b = res.sel.blocks
+        assert (np.diff(b) > 0).all() and (b < c).all() and (b >= 0).all()
+        assert res.S.size == 4 * res.sel.count + (p % 4) + 1
+        assert res.S.max() == p and p in res.S and (res.S >= 0).all()
+        assert len(set(res.S.tolist())) == res.S.size
+
+
+# ----------------------------------------------------------- attention ------
+def _torch_masked_attention(q, K, V, allowed, scale):
+    """torch CPU fp64 scaled_dot_product_attention with a boolean mask.
+    q [Hq, d] for one query; K, V [T, Hkv, d]; allowed [T] bool."""
+    Hq = q.shape[0]
+    Hkv = K.shape[1]
+    rep = Hq // Hkv
+    qt = torch.tensor(q, dtype=torch.float64)[:, None, :]                   # [Hq, 1, d]
+    kt = torch.tensor(K, dtype=torch.float64).permute(1, 0, 2).repeat_interleave(rep, 0)
+    vt = torch.tensor(V, dtype=torch.float64).permute(1, 0, 2).repeat_interleave(rep, 0)
+    m = torch.tensor(allowed)[None, None, :].expand(Hq, 1, -1)
+    o = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, attn_mask=m, scale=scale)
+    return o[:, 0, :].numpy()
+
+
+def test_attention_equals_library_masked_sdpa():
+    rng = np.random.default_rng(9)
+    T, Hq, Hkv, d = 300, 16, 2, 128
+    K = rng.standard_normal((T, Hkv, d))
+    V = rng.standard_normal((T, Hkv, d))
+    for trial in range(5):
+        q = rng.standard_normal((Hq, d))
+        S = np.sort(rng.choice(T, size=rng.integers(1, T), replace=False))
+        o, lse = O.sparse_attention(q, K, V, S, 1 / math.sqrt(d))
+        allowed = np.zeros(T, bool)
+        allowed[S] = True
+        ref = _torch_masked_attention(q, K, V, allowed, 1 / math.sqrt(d))
+        np.testing.assert_allclose(o, ref, atol=1e-12)
+        # lse: log of the softmax normaliser, checked against logsumexp
+        for h in range(Hq):
+            g = h * Hkv // Hq
+            lg = (K[S, g] @ q[h]) / math.sqrt(d)
+            assert lse[h] == pytest.approx(float(torch.logsumexp(torch.tensor(lg), 0)), abs=1e-12)
+
+
+def _tiny_full(n=256, token_budget=64):
+    x = synth.tiny(n=n, token_budget=token_budget)
+    lay = x.layout
+    kf = lambda a: synth.as_f32(a, lay.dtype).astype(np.float64)
+    k_idx, q_idx, q, K, V = (kf(a)[0] for a in (x.k_idx, x.q_idx, x.q, x.k, x.v))
+    kh = O.compress_index(k_idx, n // 4, storage="f32")
+    return x, lay, k_idx, q_idx, q, K, V, kh
+
+
+def test_full_budget_equals_dense_causal_attention():
+    # K = 256 (k_B = 64 >= every c) -> every row attends all of 0..p
+    x, lay, k_idx, q_idx, q, K, V, kh = _tiny_full(token_budget=256)
+    n = q.shape[0]
+    qt = torch.tensor(q).permute(1, 0, 2)                         # [Hq, n, d]
+    kt = torch.tensor(K[:n]).permute(1, 0, 2).repeat_interleave(4, 0)
+    vt = torch.tensor(V[:n]).permute(1, 0, 2).repeat_interleave(4, 0)
+    dense = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, is_causal=True)
+    dense = dense.permute(1, 0, 2).numpy()
+    for p in range(0, n, 5):
+        res = O.qsa_row(p, q_idx[p], q[p], kh, K, V, k_B=lay.k_blocks)
+        assert res.sel.count == p // 4
+        np.testing.assert_allclose(res.o, dense[p], atol=1e-12)
+
+
+def test_small_budget_rows_below_budget_are_dense():
+    # K = 64 (k_B = 16): rows with p <= 67 still see every block
+    x, lay, k_idx, q_idx, q, K, V, kh = _tiny_full(token_budget=64)
+    for p in [0, 1, 3, 4, 30, 63, 64, 66, 67]:
+        res = O.qsa_row(p, q_idx[p], q[p], kh, K, V, k_B=16)
+        assert res.S.tolist() == list(range(p + 1))
+
+
+def test_chunked_equals_monolithic_and_decode_equals_prefill_row():
+    # The oracle's row result depends only on (p, inputs); a chunk starting
+    # at any offset, or a decode step at p, gives the same row.  Check that
+    # building the index for a prefix (as a chunked call would) changes
+    # nothing for rows that only see that prefix.
+    x, lay, k_idx, q_idx, q, K, V, kh = _tiny_full(token_budget=64)
+    for cut in [37, 64, 130]:
+        kh_prefix = O.compress_index(k_idx[:cut], cut // 4, storage="f32")
+        for p in [cut, cut + 1, cut + 2, cut + 3]:
+            a = O.qsa_row(p, q_idx[p], q[p], kh, K, V, k_B=16)
+            # blocks needed by row p: floor(p/4) <= floor((cut+3)/4); extend
+            need = p // 4
+            kh2 = kh_prefix if need <= kh_prefix.shape[0] else O.compress_index(
+                k_idx[:4 * need], need, storage="f32")
+            b = O.qsa_row(p, q_idx[p], q[p], kh2, K[:p + 1], V[:p + 1], k_B=16)
+            assert a.sel.blocks.tolist() == b.sel.blocks.tolist()
+            np.testing.assert_array_equal(a.o, b.o)
+
+
+# -------------------------------------------------------------- needles -----
+def test_needle_queries_select_their_needle():
+    x = synth.prefill(n=6144, needle_frac=0.02)
+    lay = x.layout
+    k_idx = synth.as_f32(x.k_idx[0], "bf16").astype(np.float64)
+    q_idx = synth.as_f32(x.q_idx[0], "bf16").astype(np.float64)
+    kh = O.compress_index(k_idx, 6144 // 4, storage="bf16")
+    rows = np.nonzero(x.target_block[0] >= 0)[0]
+    rows = rows[rows > 2100][:60]
+    assert rows.size > 20
+    for i in rows:
+        res = O.qsa_row(int(i), q_idx[i], None, kh, None, None, k_B=lay.k_blocks, attend=False)
+        assert int(x.target_block[0, i]) in set(res.sel.blocks.tolist())
+
+
+def test_tiny_margins_are_mostly_clear():
+    x, lay, k_idx, q_idx, q, K, V, kh = _tiny_full(token_budget=64)
+    ms = []
+    for p in range(68, 256):
+        res = O.qsa_row(p, q_idx[p], q[p], kh, K, V, k_B=16, attend=False)
+        ms.append(res.sel.margin)
+    assert np.mean(np.array(ms) > 1e-3) > 0.8
