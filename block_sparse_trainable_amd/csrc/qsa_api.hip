@@ -1,0 +1,266 @@
+// C-ABI entry points of libqsa: argument validation (before anything is
+// enqueued), workspace sizing and kernel dispatch.  The operations and their
+// sources are documented in include/qsa.h.
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <cmath>
+
+#include "qsa_common.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+qsa_status fail(qsa_status st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+qsa_status ok() {
+  g_err[0] = '\0';
+  return QSA_OK;
+}
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+bool aligned16(const void* p) { return aligned(p, 16); }
+
+// Required pointer with its alignment: 16 for tensors read with 16-byte
+// vector loads, 8 or 4 for the rest.
+#define QSA_REQUIRE_PTR(p, a)                                                            \
+  do {                                                                                   \
+    if (!(p)) return fail(QSA_ERR_INVALID_ARGUMENT, "%s: %s must not be NULL", fn, #p); \
+    if (!aligned((p), (a)))                                                              \
+      return fail(QSA_ERR_INVALID_ARGUMENT, "%s: %s must be %d-byte aligned", fn, #p,   \
+                  (int)(a));                                                             \
+  } while (0)
+
+// Validates the configuration and fills the kernel-side dimensions.
+qsa_status check_config(const char* fn, const qsa_config* cfg, qsa::Dims* d) {
+  if (!cfg) return fail(QSA_ERR_INVALID_ARGUMENT, "%s: cfg must not be NULL", fn);
+  if (cfg->block_size <= 0 || cfg->token_budget <= 0 || cfg->idx_heads <= 0 ||
+      cfg->idx_dim <= 0 || cfg->rope_dims < 0 || cfg->q_heads <= 0 || cfg->kv_heads <= 0 ||
+      cfg->head_dim <= 0)
+    return fail(QSA_ERR_INVALID_ARGUMENT, "%s: sizes in cfg must be positive", fn);
+  if (cfg->dtype != QSA_F32 && cfg->dtype != QSA_BF16)
+    return fail(QSA_ERR_INVALID_ARGUMENT, "%s: unknown dtype %d", fn, cfg->dtype);
+  if (cfg->q_heads % cfg->kv_heads != 0)
+    return fail(QSA_ERR_INVALID_ARGUMENT, "%s: q_heads (%d) must be a multiple of kv_heads (%d)",
+                fn, cfg->q_heads, cfg->kv_heads);
+  if (!(cfg->rope_base > 0.0) || !std::isfinite(cfg->rope_base))
+    return fail(QSA_ERR_INVALID_ARGUMENT, "%s: rope_base must be positive", fn);
+  if (!(cfg->rms_eps >= 0.0f))
+    return fail(QSA_ERR_INVALID_ARGUMENT, "%s: rms_eps must be >= 0", fn);
+  if (cfg->block_size != 4)
+    return fail(QSA_ERR_UNSUPPORTED, "%s: block_size %d (only 4 is built)", fn, cfg->block_size);
+  if (cfg->idx_dim != 128)
+    return fail(QSA_ERR_UNSUPPORTED, "%s: idx_dim %d (only 128 is built)", fn, cfg->idx_dim);
+  if (cfg->idx_heads > 16)
+    return fail(QSA_ERR_UNSUPPORTED, "%s: idx_heads %d (at most 16)", fn, cfg->idx_heads);
+  if (cfg->rope_dims % 4 != 0 || cfg->rope_dims > cfg->idx_dim)
+    return fail(QSA_ERR_UNSUPPORTED, "%s: rope_dims %d (a multiple of 4 up to idx_dim)", fn,
+                cfg->rope_dims);
+  if (cfg->head_dim != 64 && cfg->head_dim != 128)
+    return fail(QSA_ERR_UNSUPPORTED, "%s: head_dim %d (64 or 128)", fn, cfg->head_dim);
+  if (cfg->q_heads > 64)
+    return fail(QSA_ERR_UNSUPPORTED, "%s: q_heads %d (at most 64)", fn, cfg->q_heads);
+  const int kB = (cfg->token_budget + cfg->block_size - 1) / cfg->block_size;
+  if (kB > 512)
+    return fail(QSA_ERR_UNSUPPORTED, "%s: k_B = ceil(K/r) = %d (at most 512)", fn, kB);
+  d->r = cfg->block_size;
+  d->kB = kB;
+  d->idx_heads = cfg->idx_heads;
+  d->idx_dim = cfg->idx_dim;
+  d->rope_dims = cfg->rope_dims;
+  d->q_heads = cfg->q_heads;
+  d->kv_heads = cfg->kv_heads;
+  d->head_dim = cfg->head_dim;
+  d->bf16 = cfg->dtype == QSA_BF16;
+  d->eps = cfg->rms_eps;
+  d->scale = cfg->softmax_scale > 0.0f ? cfg->softmax_scale
+                                       : (float)(1.0 / std::sqrt((double)cfg->head_dim));
+  d->base = cfg->rope_base;
+  return QSA_OK;
+}
+
+qsa_status check_sizes(const char* fn, int32_t batch, int32_t n_q, int64_t cap_tokens,
+                       int32_t max_pos_end) {
+  if (batch <= 0) return fail(QSA_ERR_INVALID_ARGUMENT, "%s: batch must be > 0", fn);
+  if (n_q <= 0) return fail(QSA_ERR_INVALID_ARGUMENT, "%s: n_q must be > 0", fn);
+  if (cap_tokens < 4)
+    return fail(QSA_ERR_INVALID_ARGUMENT, "%s: cap_tokens must be >= block_size", fn);
+  if (max_pos_end <= 0 || (int64_t)max_pos_end > cap_tokens)
+    return fail(QSA_ERR_INVALID_ARGUMENT,
+                "%s: max_pos_end %d must be in [1, cap_tokens=%lld]", fn, max_pos_end,
+                (long long)cap_tokens);
+  if ((int64_t)batch * n_q > (int64_t)INT32_MAX / 16)
+    return fail(QSA_ERR_INVALID_ARGUMENT, "%s: batch * n_q too large", fn);
+  return QSA_OK;
+}
+
+size_t select_ws(const qsa::Dims& d, int32_t batch, int32_t n_q, int32_t max_pos_end) {
+  const int64_t W = qsa::score_row_width(d.r, max_pos_end);
+  return sizeof(float) * (size_t)batch * (size_t)n_q * (size_t)W;
+}
+
+qsa_status launched(const char* fn, hipError_t e) {
+  if (e != hipSuccess)
+    return fail(QSA_ERR_DEVICE, "%s: launch failed: %s", fn, hipGetErrorString(e));
+  return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t qsa_abi_version(void) { return 1; }
+
+const char* qsa_last_error(void) { return g_err; }
+
+const char* qsa_status_string(qsa_status st) {
+  switch (st) {
+    case QSA_OK: return "QSA_OK";
+    case QSA_ERR_INVALID_ARGUMENT: return "QSA_ERR_INVALID_ARGUMENT";
+    case QSA_ERR_UNSUPPORTED: return "QSA_ERR_UNSUPPORTED";
+    case QSA_ERR_WORKSPACE: return "QSA_ERR_WORKSPACE";
+    case QSA_ERR_DEVICE: return "QSA_ERR_DEVICE";
+  }
+  return "QSA_UNKNOWN_STATUS";
+}
+
+qsa_status qsa_workspace_size(const qsa_config* cfg, int32_t op, int32_t batch, int32_t n_q,
+                              int32_t max_pos_end, size_t* bytes) {
+  const char* fn = "qsa_workspace_size";
+  qsa::Dims d;
+  qsa_status st = check_config(fn, cfg, &d);
+  if (st != QSA_OK) return st;
+  if (!bytes) return fail(QSA_ERR_INVALID_ARGUMENT, "%s: bytes must not be NULL", fn);
+  if (batch <= 0 || n_q <= 0 || max_pos_end <= 0)
+    return fail(QSA_ERR_INVALID_ARGUMENT, "%s: batch, n_q and max_pos_end must be > 0", fn);
+  switch (op) {
+    case QSA_OP_INDEX_BUILD: *bytes = 0; break;
+    case QSA_OP_SELECT: *bytes = select_ws(d, batch, n_q, max_pos_end); break;
+    case QSA_OP_PREFILL: *bytes = qsa::attn_workspace_bytes(d, batch * n_q, false); break;
+    case QSA_OP_DECODE: *bytes = qsa::attn_workspace_bytes(d, batch, true); break;
+    default: return fail(QSA_ERR_INVALID_ARGUMENT, "%s: unknown op %d", fn, op);
+  }
+  return ok();
+}
+
+qsa_status qsa_index_build(const qsa_config* cfg, int32_t batch, const void* k_idx,
+                           int64_t cap_tokens, const int32_t* len_before,
+                           const int32_t* len_after, int32_t max_new_blocks,
+                           const float* rms_gain, void* k_cmp, hipStream_t stream) {
+  const char* fn = "qsa_index_build";
+  qsa::Dims d;
+  qsa_status st = check_config(fn, cfg, &d);
+  if (st != QSA_OK) return st;
+  if (batch <= 0) return fail(QSA_ERR_INVALID_ARGUMENT, "%s: batch must be > 0", fn);
+  if (cap_tokens < 4)
+    return fail(QSA_ERR_INVALID_ARGUMENT, "%s: cap_tokens must be >= block_size", fn);
+  if (max_new_blocks < 0)
+    return fail(QSA_ERR_INVALID_ARGUMENT, "%s: max_new_blocks must be >= 0", fn);
+  QSA_REQUIRE_PTR(k_idx, 8);
+  QSA_REQUIRE_PTR(len_before, 4);
+  QSA_REQUIRE_PTR(len_after, 4);
+  QSA_REQUIRE_PTR(k_cmp, 8);
+  if (rms_gain && !aligned(rms_gain, 8))
+    return fail(QSA_ERR_INVALID_ARGUMENT, "%s: rms_gain must be 8-byte aligned", fn);
+  return launched(fn, qsa::launch_compress(d, batch, k_idx, cap_tokens, len_before, len_after,
+                                           max_new_blocks, rms_gain, k_cmp, stream));
+}
+
+qsa_status qsa_select_topk(const qsa_config* cfg, int32_t batch, int32_t n_q,
+                           const void* q_idx, const int32_t* q_pos0, int32_t max_pos_end,
+                           const void* k_cmp, int64_t cap_tokens, int32_t* sel_blocks,
+                           int32_t* sel_count, float* sel_scores, void* workspace,
+                           size_t workspace_bytes, hipStream_t stream) {
+  const char* fn = "qsa_select_topk";
+  qsa::Dims d;
+  qsa_status st = check_config(fn, cfg, &d);
+  if (st != QSA_OK) return st;
+  st = check_sizes(fn, batch, n_q, cap_tokens, max_pos_end);
+  if (st != QSA_OK) return st;
+  QSA_REQUIRE_PTR(q_idx, 16);
+  QSA_REQUIRE_PTR(q_pos0, 4);
+  QSA_REQUIRE_PTR(k_cmp, 16);
+  QSA_REQUIRE_PTR(sel_blocks, 4);
+  QSA_REQUIRE_PTR(sel_count, 4);
+  if (sel_scores && !aligned(sel_scores, 4))
+    return fail(QSA_ERR_INVALID_ARGUMENT, "%s: sel_scores must be 4-byte aligned", fn);
+  const size_t need = select_ws(d, batch, n_q, max_pos_end);
+  if (!workspace || workspace_bytes < need)
+    return fail(QSA_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn, need,
+                workspace ? workspace_bytes : (size_t)0);
+  if (!aligned16(workspace))
+    return fail(QSA_ERR_INVALID_ARGUMENT, "%s: workspace must be 16-byte aligned", fn);
+  const int64_t W = qsa::score_row_width(d.r, max_pos_end);
+  float* scores = static_cast<float*>(workspace);
+  hipError_t e = qsa::launch_score(d, batch, n_q, q_idx, q_pos0, max_pos_end, k_cmp, cap_tokens,
+                                   scores, W, stream);
+  if (e == hipSuccess)
+    e = qsa::launch_select(d, batch, n_q, q_pos0, cap_tokens, scores, W, sel_blocks, sel_count,
+                           sel_scores, stream);
+  return launched(fn, e);
+}
+
+static qsa_status attn_common(const char* fn, const qsa_config* cfg, int32_t batch, int32_t n_q,
+                              const void* q, const void* k_cache, const void* v_cache,
+                              int64_t cap_tokens, const int32_t* q_pos0, int32_t max_pos_end,
+                              const int32_t* sel_blocks, const int32_t* sel_count, void* out,
+                              float* lse, void* workspace, size_t workspace_bytes, bool decode,
+                              hipStream_t stream) {
+  qsa::Dims d;
+  qsa_status st = check_config(fn, cfg, &d);
+  if (st != QSA_OK) return st;
+  st = check_sizes(fn, batch, n_q, cap_tokens, max_pos_end);
+  if (st != QSA_OK) return st;
+  QSA_REQUIRE_PTR(q, 16);
+  QSA_REQUIRE_PTR(k_cache, 16);
+  QSA_REQUIRE_PTR(v_cache, 16);
+  QSA_REQUIRE_PTR(q_pos0, 4);
+  QSA_REQUIRE_PTR(sel_blocks, 4);
+  QSA_REQUIRE_PTR(sel_count, 4);
+  QSA_REQUIRE_PTR(out, 4);
+  if (lse && !aligned(lse, 4))
+    return fail(QSA_ERR_INVALID_ARGUMENT, "%s: lse must be 4-byte aligned", fn);
+  const size_t need = qsa::attn_workspace_bytes(d, batch * n_q, decode);
+  if (need > 0) {
+    if (!workspace || workspace_bytes < need)
+      return fail(QSA_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn, need,
+                  workspace ? workspace_bytes : (size_t)0);
+    if (!aligned16(workspace))
+      return fail(QSA_ERR_INVALID_ARGUMENT, "%s: workspace must be 16-byte aligned", fn);
+  }
+  return launched(fn, qsa::launch_attn(d, batch, n_q, q, k_cache, v_cache, cap_tokens, q_pos0,
+                                       sel_blocks, sel_count, out, lse, workspace, decode,
+                                       stream));
+}
+
+qsa_status qsa_sparse_attn_prefill(const qsa_config* cfg, int32_t batch, int32_t n_q,
+                                   const void* q, const void* k_cache, const void* v_cache,
+                                   int64_t cap_tokens, const int32_t* q_pos0,
+                                   int32_t max_pos_end, const int32_t* sel_blocks,
+                                   const int32_t* sel_count, void* out, float* lse,
+                                   void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  return attn_common("qsa_sparse_attn_prefill", cfg, batch, n_q, q, k_cache, v_cache, cap_tokens,
+                     q_pos0, max_pos_end, sel_blocks, sel_count, out, lse, workspace,
+                     workspace_bytes, false, stream);
+}
+
+qsa_status qsa_sparse_attn_decode(const qsa_config* cfg, int32_t batch, const void* q,
+                                  const void* k_cache, const void* v_cache, int64_t cap_tokens,
+                                  const int32_t* q_pos, int32_t max_pos_end,
+                                  const int32_t* sel_blocks, const int32_t* sel_count,
+                                  void* out, float* lse, void* workspace,
+                                  size_t workspace_bytes, hipStream_t stream) {
+  return attn_common("qsa_sparse_attn_decode", cfg, batch, 1, q, k_cache, v_cache, cap_tokens,
+                     q_pos, max_pos_end, sel_blocks, sel_count, out, lse, workspace,
+                     workspace_bytes, true, stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,262 @@
+// Block-importance scoring (kernel b).
+//
+// "QSA (Qwen Sparse Attention)", Key math / How it works, (A): each query i
+// scores each complete earlier block b as I_ib = sum over the indexer's query
+// heads of ReLU(<q_i^h, k_b>), with block-causal masking (b < floor(p_i/r)).
+// Output: one fp32 row of I per query, row stride W, entries b < c_i written.
+//
+// MFMA layout (v_mfma_f32_16x16x32_bf16, wave64).  The 16 rows of an A tile
+// are (query, head) pairs ordered row = 4*query + head, the 16 columns of a B
+// tile are blocks, and the contraction runs over the 128 dims in 4 k-steps.
+// The accumulator of lane l holds rows 4*(l/16)+0..3 of column l%16, i.e.
+// the four heads of one query for one block, so ReLU and the head sum happen
+// in registers with no cross-lane traffic.  A and B fill each k-slot with the
+// same dims, so the sum over k does not depend on the hardware's k order.
+#include "qsa_common.h"
+
+namespace qsa {
+namespace {
+
+// ----------------------------------------------------------------- VALU ----
+// Any dtype / head count: one workgroup per (query, 256 blocks), the query's
+// heads staged in LDS as fp32.  Used for fp32 layers and non-MFMA layouts.
+template <bool BF16>
+__global__ __launch_bounds__(256) void score_valu_kernel(
+    const void* __restrict__ q_idx_v, const int32_t* __restrict__ q_pos0, int n_q, int H,
+    int D, const void* __restrict__ k_cmp_v, int64_t cap_blocks, float* __restrict__ scores,
+    int64_t W) {
+  extern __shared__ float qs[];  // [H][D]
+  const int64_t row = blockIdx.x;
+  const int s = (int)(row / n_q);
+  const int j = (int)(row % n_q);
+  const int64_t p = (int64_t)q_pos0[s] + j;
+  const int64_t c = min(min(p / 4, cap_blocks), W);
+  for (int i = threadIdx.x; i < H * D; i += blockDim.x) {
+    const int64_t off = row * H * D + i;
+    qs[i] = BF16 ? bf16_to_f32(static_cast<const uint16_t*>(q_idx_v)[off])
+                 : static_cast<const float*>(q_idx_v)[off];
+  }
+  __syncthreads();
+  const int64_t b = (int64_t)blockIdx.y * blockDim.x + threadIdx.x;
+  if (b >= c) return;
+  const int64_t kb = ((int64_t)s * cap_blocks + b) * D;
+  float acc = 0.0f;
+  for (int h = 0; h < H; ++h) {
+    float dot = 0.0f;
+    for (int d = 0; d < D; ++d) {
+      const float kv = BF16 ? bf16_to_f32(static_cast<const uint16_t*>(k_cmp_v)[kb + d])
+                            : static_cast<const float*>(k_cmp_v)[kb + d];
+      dot = fmaf(qs[h * D + d], kv, dot);
+    }
+    acc += relu(dot);
+  }
+  scores[row * W + b] = acc;
+}
+
+// ------------------------------------------------------ MFMA, prefill ------
+// Workgroup tile: 64 queries x one segment of blocks.  Wave w owns queries
+// 16w..16w+15 (4 A row-tiles of 4 queries x 4 heads, kept in registers for
+// the whole segment).  The segment is walked in chunks of 64 blocks; each
+// chunk (64 x 256 B) is staged once in LDS, double-buffered, and read by all
+// four waves as B tiles.
+constexpr int kPQ = 64;       // queries per workgroup
+constexpr int kChunk = 64;    // blocks per LDS chunk
+constexpr int kRowB = 272;    // LDS bytes per block row (256 + 16 pad)
+
+__global__ __launch_bounds__(256) void score_mfma_prefill_kernel(
+    const uint16_t* __restrict__ q_idx, const int32_t* __restrict__ q_pos0, int n_q,
+    const uint16_t* __restrict__ k_cmp, int64_t cap_blocks, int seg_blocks,
+    float* __restrict__ scores, int64_t W) {
+  __shared__ __attribute__((aligned(16))) unsigned char lds[2][kChunk * kRowB];
+  const int s = blockIdx.z;
+  // longest rows first: the last query tiles have the most blocks
+  const int qt = gridDim.x - 1 - blockIdx.x;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int l16 = lane & 15;
+  const int gq = lane >> 4;
+
+  const int j0 = qt * kPQ;
+  const int j_last = min(j0 + kPQ, n_q) - 1;
+  const int64_t pos0 = q_pos0[s];
+  const int64_t c_tile = min(min((pos0 + j_last) / 4, cap_blocks), W);
+  const int64_t b_lo = (int64_t)blockIdx.y * seg_blocks;
+  const int64_t b_hi = min(b_lo + seg_blocks, c_tile);
+  if (b_lo >= b_hi) return;
+
+  // A operands: row tile rt covers queries j0 + 16w + 4rt + (0..3)
+  u32x4 qa[4][4];
+  int64_t cq[4];  // candidate count of this lane's output query in each row tile
+#pragma unroll
+  for (int rt = 0; rt < 4; ++rt) {
+    const int jq_a = j0 + 16 * wave + 4 * rt + (l16 >> 2);  // query of A row l16
+    const int head = l16 & 3;
+    const bool ok = jq_a < n_q;
+    const uint16_t* src = q_idx + (((int64_t)s * n_q + (ok ? jq_a : 0)) * 4 + head) * 128 + 8 * gq;
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) qa[rt][kk] = ok ? ld16(src + 32 * kk) : u32x4{0, 0, 0, 0};
+    const int jq_o = j0 + 16 * wave + 4 * rt + gq;            // query of output rows 4gq..
+    cq[rt] = jq_o < n_q ? min(min((pos0 + jq_o) / 4, cap_blocks), W) : 0;
+  }
+
+  // cooperative chunk load: 1024 pieces of 16 B, four per thread
+  const uint16_t* kbase = k_cmp + (int64_t)s * cap_blocks * 128;
+  auto load_chunk = [&](int64_t cb, u32x4 (&r)[4]) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int piece = threadIdx.x + 256 * u;
+      const int blk = piece >> 4, col = piece & 15;
+      const int64_t b = cb + blk;
+      r[u] = b < b_hi ? ld16(kbase + b * 128 + col * 8) : u32x4{0, 0, 0, 0};
+    }
+  };
+  auto store_chunk = [&](int buf, const u32x4 (&r)[4]) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int piece = threadIdx.x + 256 * u;
+      const int blk = piece >> 4, col = piece & 15;
+      *reinterpret_cast<u32x4*>(&lds[buf][blk * kRowB + col * 16]) = r[u];
+    }
+  };
+
+  u32x4 pre[4];
+  load_chunk(b_lo, pre);
+  store_chunk(0, pre);
+  __syncthreads();
+  int buf = 0;
+  for (int64_t cb = b_lo; cb < b_hi; cb += kChunk) {
+    const bool more = cb + kChunk < b_hi;
+    if (more) load_chunk(cb + kChunk, pre);
+
+    f32x4 acc[4][4];
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct) acc[rt][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct) {
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        const u32x4 bv = *reinterpret_cast<const u32x4*>(
+            &lds[buf][(16 * ct + l16) * kRowB + 64 * kk + 16 * gq]);
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt)
+          acc[rt][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(qa[rt][kk]),
+                                                                as_bf16x8(bv), acc[rt][ct], 0, 0, 0);
+      }
+    }
+    // epilogue: lane holds 4 heads of query (4rt + gq) for block 16ct + l16
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt) {
+      const int jq = j0 + 16 * wave + 4 * rt + gq;
+      float* dst = scores + ((int64_t)s * n_q + jq) * W;
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct) {
+        const int64_t b = cb + 16 * ct + l16;
+        const f32x4 a = acc[rt][ct];
+        const float v = relu(a[0]) + relu(a[1]) + relu(a[2]) + relu(a[3]);
+        if (b < cq[rt]) dst[b] = v;
+      }
+    }
+    if (more) {
+      store_chunk(buf ^ 1, pre);
+      __syncthreads();
+      buf ^= 1;
+    }
+  }
+}
+
+// ------------------------------------------------------- MFMA, decode ------
+// Few queries, long rows: workgroup = (segment of blocks, 4 queries).  The
+// four waves take disjoint 64-block chunks of the segment and read their B
+// tiles straight from HBM (no reuse to stage); rows are 4 queries x 4 heads.
+constexpr int kDecSeg = 1024;
+
+__global__ __launch_bounds__(256) void score_mfma_decode_kernel(
+    const uint16_t* __restrict__ q_idx, const int32_t* __restrict__ q_pos0, int n_q,
+    const uint16_t* __restrict__ k_cmp, int64_t cap_blocks, float* __restrict__ scores,
+    int64_t W) {
+  const int s = blockIdx.z;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int l16 = lane & 15;
+  const int gq = lane >> 4;
+  const int j0 = 4 * blockIdx.y;
+  const int64_t pos0 = q_pos0[s];
+  const int j_last = min(j0 + 4, n_q) - 1;
+  const int64_t c_tile = min(min((pos0 + j_last) / 4, cap_blocks), W);
+  const int64_t seg_lo = (int64_t)blockIdx.x * kDecSeg;
+  const int64_t seg_hi = min(seg_lo + kDecSeg, c_tile);
+  if (seg_lo >= seg_hi) return;
+
+  u32x4 qa[4];
+  {
+    const int jq_a = j0 + (l16 >> 2);
+    const bool ok = jq_a < n_q;
+    const uint16_t* src = q_idx + (((int64_t)s * n_q + (ok ? jq_a : 0)) * 4 + (l16 & 3)) * 128 + 8 * gq;
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) qa[kk] = ok ? ld16(src + 32 * kk) : u32x4{0, 0, 0, 0};
+  }
+  const int jq_o = j0 + gq;
+  const int64_t cq = jq_o < n_q ? min(min((pos0 + jq_o) / 4, cap_blocks), W) : 0;
+  float* dst = scores + ((int64_t)s * n_q + (jq_o < n_q ? jq_o : 0)) * W;
+  const uint16_t* kbase = k_cmp + (int64_t)s * cap_blocks * 128 + 8 * gq;
+
+  for (int64_t cb = seg_lo + 64 * wave; cb < seg_hi; cb += 256) {
+    u32x4 kb[4][4];
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct) {
+      const int64_t b = cb + 16 * ct + l16;
+      const bool ok = b < seg_hi;
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk)
+        kb[ct][kk] = ok ? ld16(kbase + b * 128 + 32 * kk) : u32x4{0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct) {
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk)
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(qa[kk]), as_bf16x8(kb[ct][kk]),
+                                                      acc, 0, 0, 0);
+      const int64_t b = cb + 16 * ct + l16;
+      const float v = relu(acc[0]) + relu(acc[1]) + relu(acc[2]) + relu(acc[3]);
+      if (b < cq) dst[b] = v;
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_score(const Dims& d, int batch, int n_q, const void* q_idx,
+                        const int32_t* q_pos0, int32_t max_pos_end, const void* k_cmp,
+                        int64_t cap, float* scores, int64_t W, hipStream_t st) {
+  const int64_t cap_blocks = cap / d.r;
+  const int64_t c_max = min((int64_t)(max_pos_end - 1) / d.r, min(cap_blocks, W));
+  if (c_max <= 0) return hipSuccess;
+  const bool mfma = d.bf16 && d.idx_heads == 4 && d.idx_dim == 128;
+  if (mfma && n_q >= 16) {
+    const int seg = 2048;
+    dim3 grid((unsigned)((n_q + kPQ - 1) / kPQ), (unsigned)((c_max + seg - 1) / seg), (unsigned)batch);
+    hipLaunchKernelGGL(score_mfma_prefill_kernel, grid, dim3(256), 0, st,
+                       static_cast<const uint16_t*>(q_idx), q_pos0, n_q,
+                       static_cast<const uint16_t*>(k_cmp), cap_blocks, seg, scores, W);
+  } else if (mfma) {
+    dim3 grid((unsigned)((c_max + kDecSeg - 1) / kDecSeg), (unsigned)((n_q + 3) / 4), (unsigned)batch);
+    hipLaunchKernelGGL(score_mfma_decode_kernel, grid, dim3(256), 0, st,
+                       static_cast<const uint16_t*>(q_idx), q_pos0, n_q,
+                       static_cast<const uint16_t*>(k_cmp), cap_blocks, scores, W);
+  } else {
+    dim3 grid((unsigned)(batch * n_q), (unsigned)((c_max + 255) / 256));
+    const size_t shm = sizeof(float) * d.idx_heads * d.idx_dim;
+    if (d.bf16)
+      hipLaunchKernelGGL(score_valu_kernel<true>, grid, dim3(256), shm, st, q_idx, q_pos0, n_q,
+                         d.idx_heads, d.idx_dim, k_cmp, cap_blocks, scores, W);
+    else
+      hipLaunchKernelGGL(score_valu_kernel<false>, grid, dim3(256), shm, st, q_idx, q_pos0, n_q,
+                         d.idx_heads, d.idx_dim, k_cmp, cap_blocks, scores, W);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace qsa

@@ -1,0 +1,160 @@
+"""Device buffers of one QSA layer and the call sequences that drive it.
+
+Marshalling only: tensors are uploaded once, outputs and workspaces are
+allocated once, and each method enqueues the C-ABI entry points on the
+current stream.  A prefill chunk is index_build (blocks completed by the
+chunk) -> select_topk -> sparse_attn_prefill; a decode step is
+index_build (the block the new token may complete) -> select_topk (one
+query per sequence) -> sparse_attn_decode.
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+from . import _binding as B
+from .synth import LayerInputs
+
+
+def to_device(a: np.ndarray, dtype: str, device) -> torch.Tensor:
+    """numpy storage tensor (uint16 bf16 bits or fp32) -> device tensor."""
+    if dtype == "bf16":
+        t = torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16)
+    else:
+        t = torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32))
+    return t.to(device)
+
+
+def bf16_bits(t: torch.Tensor) -> np.ndarray:
+    """bf16 device tensor -> uint16 numpy bit patterns."""
+    return t.detach().view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def to_f32(t: torch.Tensor) -> np.ndarray:
+    return t.detach().float().cpu().numpy()
+
+
+class DeviceLayer:
+    """One layer's caches and query tensors on the GPU."""
+
+    def __init__(self, x: LayerInputs, device="cuda:0"):
+        self.x = x
+        self.layout = x.layout
+        self.cfg = B.QsaConfig.from_layout(x.layout)
+        self.device = torch.device(device)
+        dt = x.layout.dtype
+        self.tdtype = torch.bfloat16 if dt == "bf16" else torch.float32
+        self.batch = x.batch
+        self.cap = x.cap_tokens
+        self.n_q = x.n_q
+        self.k_idx = to_device(x.k_idx, dt, self.device)
+        self.k = to_device(x.k, dt, self.device)
+        self.v = to_device(x.v, dt, self.device)
+        self.q_idx = to_device(x.q_idx, dt, self.device)
+        self.q = to_device(x.q, dt, self.device)
+        self.gain = torch.from_numpy(np.ascontiguousarray(x.gain, np.float32)).to(self.device)
+        self.k_cmp = torch.zeros((self.batch, self.cap // self.layout.block_size,
+                                  self.layout.idx_dim), dtype=self.tdtype, device=self.device)
+        self.kB = self.cfg.k_blocks
+        self._ws = {}
+
+    # ------------------------------------------------------------ helpers --
+    def i32(self, values) -> torch.Tensor:
+        return torch.tensor(np.asarray(values, dtype=np.int32), device=self.device)
+
+    def workspace(self, op: int, batch: int, n_q: int, max_pos_end: int) -> torch.Tensor:
+        n = B.qsa_workspace_size(self.cfg, op, batch, n_q, max_pos_end)
+        key = (op,)
+        ws = self._ws.get(key)
+        if ws is None or ws.numel() < max(n, 16):
+            ws = torch.empty(max(n, 16), dtype=torch.uint8, device=self.device)
+            self._ws[key] = ws
+        return ws
+
+    # -------------------------------------------------------- entry points --
+    def index_build(self, len_before, len_after, max_new_blocks: int) -> None:
+        B.qsa_index_build(self.cfg, self.batch, self.k_idx, self.cap, len_before, len_after,
+                          int(max_new_blocks), self.gain, self.k_cmp)
+
+    def build_prefix(self, lengths) -> None:
+        """Build every complete block of the first lengths[s] tokens (setup)."""
+        lengths = np.asarray(lengths, np.int64)
+        self.index_build(self.i32(np.zeros(self.batch)), self.i32(lengths),
+                         int(lengths.max()) // self.layout.block_size + 1)
+
+    def alloc_select(self, batch: int, n_q: int):
+        sel = torch.empty((batch, n_q, self.kB), dtype=torch.int32, device=self.device)
+        cnt = torch.empty((batch, n_q), dtype=torch.int32, device=self.device)
+        scs = torch.empty((batch, n_q, self.kB), dtype=torch.float32, device=self.device)
+        return sel, cnt, scs
+
+    def select(self, q_idx, q_pos0, max_pos_end: int, sel, cnt, scs, batch=None, n_q=None):
+        batch = self.batch if batch is None else batch
+        n_q = q_idx.shape[1] if n_q is None else n_q
+        ws = self.workspace(B.QSA_OP_SELECT, batch, n_q, max_pos_end)
+        B.qsa_select_topk(self.cfg, batch, n_q, q_idx, q_pos0, int(max_pos_end), self.k_cmp,
+                          self.cap, sel, cnt, scs, ws, ws.numel())
+
+    def attend_prefill(self, q, q_pos0, max_pos_end: int, sel, cnt, out, lse):
+        n_q = q.shape[1]
+        ws = self.workspace(B.QSA_OP_PREFILL, self.batch, n_q, max_pos_end)
+        B.qsa_sparse_attn_prefill(self.cfg, self.batch, n_q, q, self.k, self.v, self.cap, q_pos0,
+                                  int(max_pos_end), sel, cnt, out, lse, ws, ws.numel())
+
+    def attend_decode(self, q, q_pos, max_pos_end: int, sel, cnt, out, lse):
+        ws = self.workspace(B.QSA_OP_DECODE, self.batch, 1, max_pos_end)
+        B.qsa_sparse_attn_decode(self.cfg, self.batch, q, self.k, self.v, self.cap, q_pos,
+                                 int(max_pos_end), sel, cnt, out, lse, ws, ws.numel())
+
+    # -------------------------------------------------------- call chains --
+    def prefill_chunk(self, outputs=None):
+        """index_build + select_topk + sparse_attn_prefill for the chunk of
+        n_q queries at q_pos0 (blocks before cache_len already built)."""
+        x = self.x
+        r = self.layout.block_size
+        q_pos0 = self.i32(x.q_pos0)
+        end = x.q_pos0.astype(np.int64) + self.n_q
+        max_pos_end = int(end.max())
+        new_blocks = int((end // r - x.cache_len // r).max())
+        if outputs is None:
+            outputs = self.alloc_prefill_outputs()
+        sel, cnt, scs, out, lse = outputs
+        self.index_build(self.i32(x.cache_len), self.i32(end), new_blocks)
+        self.select(self.q_idx, q_pos0, max_pos_end, sel, cnt, scs)
+        self.attend_prefill(self.q, q_pos0, max_pos_end, sel, cnt, out, lse)
+        return outputs
+
+    def alloc_prefill_outputs(self):
+        sel, cnt, scs = self.alloc_select(self.batch, self.n_q)
+        out = torch.empty_like(self.q)
+        lse = torch.empty((self.batch, self.n_q, self.layout.q_heads), dtype=torch.float32,
+                          device=self.device)
+        return sel, cnt, scs, out, lse
+
+    def decode_plan(self, steps: int):
+        """Per-step device inputs of a decode run: step-major copies of the
+        indexer/main queries and the position arrays."""
+        x = self.x
+        q_idx_s = self.q_idx.transpose(0, 1).contiguous()    # [steps][B][H][d]
+        q_s = self.q.transpose(0, 1).contiguous()
+        pos = np.stack([x.q_pos0 + t for t in range(steps)]).astype(np.int32)
+        pos_t = torch.tensor(pos, device=self.device)          # [steps][B]
+        pos1_t = torch.tensor(pos + 1, device=self.device)
+        max_pos_end = int(pos.max()) + 1
+        return q_idx_s, q_s, pos_t, pos1_t, max_pos_end
+
+    def alloc_decode_outputs(self):
+        sel, cnt, scs = self.alloc_select(self.batch, 1)
+        out = torch.empty((self.batch, self.layout.q_heads, self.layout.head_dim),
+                          dtype=self.tdtype, device=self.device)
+        lse = torch.empty((self.batch, self.layout.q_heads), dtype=torch.float32,
+                          device=self.device)
+        return sel, cnt, scs, out, lse
+
+    def decode_step(self, plan, t: int, outputs):
+        q_idx_s, q_s, pos_t, pos1_t, max_pos_end = plan
+        sel, cnt, scs, out, lse = outputs
+        self.index_build(pos_t[t], pos1_t[t], 1)
+        self.select(q_idx_s[t].unsqueeze(1), pos_t[t], max_pos_end, sel, cnt, scs, n_q=1)
+        self.attend_decode(q_s[t], pos_t[t], max_pos_end, sel, cnt, out, lse)
+        return outputs

@@ -1,0 +1,201 @@
+/*
+ * qsa.h -- C ABI of libqsa, the gfx950 (MI355X) forward pass of one Qwen
+ * Sparse Attention (QSA) layer: the compressed lightweight indexer followed by
+ * sparse core attention.
+ *
+ * Sources (cited by page title and section):
+ *   [concept]  "QSA (Qwen Sparse Attention)" research-hub concept page,
+ *              "Key math / How it works": (A) compressed lightweight indexer,
+ *              (B) sparse core attention, and "Config" (K = 2048, r = 4).
+ *   [gallery]  "Qwen Sparse Attention" architecture-gallery page: the
+ *              selection unit/budget table, "How block selection works"
+ *              (its pseudocode) and the QSA-vs-DSA table.
+ *
+ * Conventions shared by every entry point
+ *   - Every tensor argument is DEVICE memory owned by the caller, dense and
+ *     row-major in the layout stated.  The library never allocates, frees
+ *     or synchronises; it only enqueues kernels on the caller's stream.
+ *     Scratch memory comes from a caller-supplied workspace whose size
+ *     qsa_workspace_size() returns.
+ *   - Positions are absolute, 0-based token indices; K/V/raw-key row t of a
+ *     sequence holds the token at position t.  Blocks are r = block_size
+ *     consecutive positions: block b covers r*b .. r*b + r - 1.
+ *   - dtype QSA_BF16: tensors marked "(dtype)" hold bf16; QSA_F32: fp32.
+ *     Arithmetic always accumulates in fp32 (compression: fp64).
+ *   - Host validation runs before anything is enqueued.  A non-QSA_OK
+ *     return means nothing was launched; qsa_last_error() (thread-local)
+ *     then describes the problem.  QSA_ERR_DEVICE reports a failed launch.
+ *   - Device-resident position arrays are read by the kernels only.  They
+ *     must satisfy the stated preconditions; kernels clamp every index so a
+ *     violation gives wrong values, never an out-of-bounds access.
+ *   - Calls are re-entrant and enqueue-only; concurrent calls on different
+ *     streams must use different workspaces.
+ */
+#ifndef QSA_H
+#define QSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  QSA_OK = 0,
+  QSA_ERR_INVALID_ARGUMENT = 1, /* null pointer, bad size, misalignment    */
+  QSA_ERR_UNSUPPORTED = 2,      /* a setting this build does not implement */
+  QSA_ERR_WORKSPACE = 3,        /* workspace missing or too small          */
+  QSA_ERR_DEVICE = 4            /* HIP reported an error at launch         */
+} qsa_status;
+
+typedef enum { QSA_F32 = 0, QSA_BF16 = 1 } qsa_dtype;
+
+typedef enum {
+  QSA_OP_INDEX_BUILD = 0,
+  QSA_OP_SELECT = 1,
+  QSA_OP_PREFILL = 2,
+  QSA_OP_DECODE = 3
+} qsa_op;
+
+/* Layer configuration.  Supported values are listed per field; anything
+ * else returns QSA_ERR_UNSUPPORTED (or INVALID_ARGUMENT when meaningless). */
+typedef struct {
+  int32_t block_size;    /* r: tokens per micro-block.  4 ([concept] Config;
+                            [gallery] selection-unit table).                */
+  int32_t token_budget;  /* K: selected tokens; k_B = ceil(K / r) blocks are
+                            kept ([concept] (A) top-k_B; Config K = 2048).
+                            Supported: 1 <= k_B <= 512.                     */
+  int32_t idx_heads;     /* indexer query heads sharing one key head: 4
+                            ([concept] (A) MQA head layout).                */
+  int32_t idx_dim;       /* indexer head dim: 128 ([concept] (A)).          */
+  int32_t rope_dims;     /* rotated dims [0, rope_dims) of each compressed
+                            key, rotate-half pairs (j, j + rope_dims/2):
+                            64 of 128 ([concept] (A) partial RoPE).  Any
+                            multiple of 4 up to idx_dim.                    */
+  int32_t q_heads;       /* main attention query heads (Hq).                */
+  int32_t kv_heads;      /* main attention KV heads (Hkv), Hq % Hkv == 0;
+                            head h reads KV head floor(h * Hkv / Hq).       */
+  int32_t head_dim;      /* main attention head dim: 64 or 128.             */
+  int32_t dtype;         /* qsa_dtype of every tensor marked (dtype).       */
+  float rms_eps;         /* RMSNorm epsilon of the pooled key (the pages
+                            give none; 1e-6 is the customary value).        */
+  float softmax_scale;   /* attention logit scale; <= 0 means
+                            1/sqrt(head_dim) ([concept] (B) "scaled").      */
+  double rope_base;      /* RoPE base: theta_j = base^(-2j/rope_dims).      */
+} qsa_config;
+
+/* qsa_index_build -- block compression of the indexer keys.
+ * [concept] (A) block compression and partial RoPE; [gallery] "How block
+ * selection works": the keys of each complete block are averaged, the
+ * pooled key is normalised, then rotated at the block's first position.
+ *
+ * For every sequence s, builds each block b with
+ *     floor(len_before[s] / r) <= b < floor(len_after[s] / r)
+ * as  k_cmp[s][b] = RoPE_{r*b}( RMSNorm( mean_{t<r} k_idx[s][r*b+t] ) * gain ),
+ * computed in fp64 and rounded to nearest-even into the storage dtype.
+ *
+ *   k_idx      (dtype) [batch][cap_tokens][idx_dim] raw indexer keys.
+ *   len_before int32 [batch] device: tokens already covered by built blocks.
+ *   len_after  int32 [batch] device: tokens present after this call
+ *              (precondition: len_before <= len_after <= cap_tokens).
+ *   max_new_blocks  host upper bound of floor(len_after/r) -
+ *              floor(len_before/r) over sequences; sizes the grid only
+ *              (every block in range is built whatever the bound).
+ *   rms_gain   float [idx_dim] device, or NULL for a gain of 1.
+ *   k_cmp      (dtype) [batch][cap_tokens / r][idx_dim]; only the rows of
+ *              the built blocks are written.
+ * A decode step calls it with len_after = len_before + 1; it builds a block
+ * only when that token completes one.                                     */
+qsa_status qsa_index_build(const qsa_config* cfg, int32_t batch, const void* k_idx,
+                           int64_t cap_tokens, const int32_t* len_before,
+                           const int32_t* len_after, int32_t max_new_blocks,
+                           const float* rms_gain, void* k_cmp, hipStream_t stream);
+
+/* qsa_select_topk -- block importance and top-k_B block selection.
+ * [concept] (A) block-importance equation I_ib = sum_h ReLU(<q_i^h, k_b>)
+ * with block-causal masking, and top-k_B selection; [gallery] pseudocode
+ * ("scores", "selected_blocks") and budget table (up to 512 blocks).
+ *
+ * Query j of sequence s sits at position p = q_pos0[s] + j.  Its candidate
+ * blocks are the complete blocks before its own block, b < c = floor(p/r).
+ * It keeps count = min(k_B, c) blocks of largest I; equal scores go to the
+ * lower block id.  The selection is written in ascending block order.
+ *
+ *   q_idx      (dtype) [batch][n_q][idx_heads][idx_dim], used as given.
+ *   q_pos0     int32 [batch] device.
+ *   max_pos_end host bound: q_pos0[s] + n_q <= max_pos_end <= cap_tokens.
+ *   k_cmp      (dtype) [batch][cap_tokens / r][idx_dim]; blocks < c built.
+ *   sel_blocks int32 [batch][n_q][k_B]: ascending ids, then -1 padding.
+ *   sel_count  int32 [batch][n_q].
+ *   sel_scores float [batch][n_q][k_B] or NULL: I of each selected block
+ *              (same order as sel_blocks; 0 in padding).
+ *   workspace  >= qsa_workspace_size(QSA_OP_SELECT, batch, n_q, max_pos_end).
+ */
+qsa_status qsa_select_topk(const qsa_config* cfg, int32_t batch, int32_t n_q,
+                           const void* q_idx, const int32_t* q_pos0, int32_t max_pos_end,
+                           const void* k_cmp, int64_t cap_tokens, int32_t* sel_blocks,
+                           int32_t* sel_count, float* sel_scores, void* workspace,
+                           size_t workspace_bytes, hipStream_t stream);
+
+/* qsa_sparse_attn_prefill -- sparse core attention for a chunk of queries.
+ * [concept] (B): full scaled-dot-product attention restricted to the
+ * selected blocks' tokens; [concept] (A) and [gallery] pseudocode/table:
+ * each selected block is expanded to its r tokens and the visible tokens of
+ * the query's own (incomplete) block are always added.
+ *
+ * The token set of the query at p is S = { r*b + t : b in selection, t < r }
+ * plus the tail r*floor(p/r) .. p; every main head attends over S.
+ *
+ *   q          (dtype) [batch][n_q][q_heads][head_dim].
+ *   k_cache, v_cache (dtype) [batch][cap_tokens][kv_heads][head_dim];
+ *              rows 0 .. p written for every query.
+ *   q_pos0, max_pos_end  as in qsa_select_topk.
+ *   sel_blocks, sel_count  as written by qsa_select_topk (any ascending or
+ *              unordered list of distinct complete blocks b < floor(p/r)).
+ *   out        (dtype) [batch][n_q][q_heads][head_dim].
+ *   lse        float [batch][n_q][q_heads] natural-log normaliser, or NULL.
+ *   workspace  >= qsa_workspace_size(QSA_OP_PREFILL, ...) (may be 0 bytes).
+ */
+qsa_status qsa_sparse_attn_prefill(const qsa_config* cfg, int32_t batch, int32_t n_q,
+                                   const void* q, const void* k_cache, const void* v_cache,
+                                   int64_t cap_tokens, const int32_t* q_pos0,
+                                   int32_t max_pos_end, const int32_t* sel_blocks,
+                                   const int32_t* sel_count, void* out, float* lse,
+                                   void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* qsa_sparse_attn_decode -- sparse core attention for one new token per
+ * sequence (the decode loop), split over the token set for parallelism and
+ * combined with a log-sum-exp merge.  Same token set as the prefill call.
+ * [concept] (B); the concept page's "Why it matters" reports decode-phase
+ * kernel speed-ups at 1M context.
+ *
+ *   q          (dtype) [batch][q_heads][head_dim].
+ *   q_pos      int32 [batch] device: position of the new token, whose K/V
+ *              rows are already written.  max_pos_end > every q_pos[s].
+ *   sel_blocks int32 [batch][k_B]; sel_count int32 [batch].
+ *   out        (dtype) [batch][q_heads][head_dim]; lse float [batch][q_heads]
+ *              or NULL.
+ *   workspace  >= qsa_workspace_size(QSA_OP_DECODE, batch, 1, max_pos_end).
+ */
+qsa_status qsa_sparse_attn_decode(const qsa_config* cfg, int32_t batch, const void* q,
+                                  const void* k_cache, const void* v_cache, int64_t cap_tokens,
+                                  const int32_t* q_pos, int32_t max_pos_end,
+                                  const int32_t* sel_blocks, const int32_t* sel_count,
+                                  void* out, float* lse, void* workspace,
+                                  size_t workspace_bytes, hipStream_t stream);
+
+/* Workspace bytes needed by op (a qsa_op) for these sizes.  n_q is 1 for
+ * QSA_OP_DECODE; QSA_OP_INDEX_BUILD needs none.                           */
+qsa_status qsa_workspace_size(const qsa_config* cfg, int32_t op, int32_t batch, int32_t n_q,
+                              int32_t max_pos_end, size_t* bytes);
+
+const char* qsa_status_string(qsa_status status);
+const char* qsa_last_error(void);  /* thread-local text of the last failure */
+int32_t qsa_abi_version(void);     /* 1 */
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* QSA_H */

@@ -1,0 +1,148 @@
+"""Host-side tests of the C ABI (no GPU needed).
+
+The library must load, export every function include/qsa.h declares, and
+reject every invalid argument before anything is enqueued (these calls never
+reach the HIP runtime, so they run on a machine without a GPU).
+"""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import block_sparse_trainable_amd as qsa
+from block_sparse_trainable_amd import _binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "qsa.h")
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(qsa_[a-z_0-9]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(B.library_path()):
+        from block_sparse_trainable_amd import build
+        build.build()
+    return B.load()
+
+
+def cfg(**kw):
+    base = dict(block_size=4, token_budget=2048, idx_heads=4, idx_dim=128, rope_dims=64,
+                q_heads=16, kv_heads=2, head_dim=128, dtype=B.QSA_BF16, rms_eps=1e-6,
+                softmax_scale=0.0, rope_base=10000.0)
+    base.update(kw)
+    return B.QsaConfig(**base)
+
+
+def test_exports_every_declared_symbol(lib):
+    names = _declared()
+    assert set(B.EXPORTED) == set(names), names
+    out = subprocess.run(["nm", "-D", "--defined-only", B.library_path()], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\b(qsa_[a-z_0-9]+)$", out, flags=re.M))
+    for n in names:
+        assert n in exported, n
+        assert hasattr(lib, n)
+    assert lib.qsa_abi_version() == 1
+
+
+def test_config_struct_layout_matches_header():
+    # int32 x 9, float x 2, double -> 9*4 + 2*4 = 44, padded to 48 for the double
+    assert ctypes.sizeof(B.QsaConfig) == 56
+    assert B.QsaConfig.rope_base.offset == 48
+
+
+def test_status_strings(lib):
+    for code, name in enumerate(["QSA_OK", "QSA_ERR_INVALID_ARGUMENT", "QSA_ERR_UNSUPPORTED",
+                                 "QSA_ERR_WORKSPACE", "QSA_ERR_DEVICE"]):
+        assert lib.qsa_status_string(code).decode() == name
+
+
+def test_workspace_sizes(lib):
+    c = cfg()
+    # select: one fp32 score row per query, width = ceil4(floor((end-1)/4))
+    assert qsa.qsa_workspace_size(c, B.QSA_OP_SELECT, 2, 8192, 139264) == 4 * 2 * 8192 * 34816
+    assert qsa.qsa_workspace_size(c, B.QSA_OP_INDEX_BUILD, 1, 1, 10) == 0
+    assert qsa.qsa_workspace_size(c, B.QSA_OP_PREFILL, 1, 100, 100) == 0
+    # decode: 17 splits of 32 pseudo-blocks, each 16 heads x (128 + 2) floats
+    assert qsa.qsa_workspace_size(c, B.QSA_OP_DECODE, 8, 1, 300000) == 4 * 8 * 17 * (16 * 128 + 32)
+    assert qsa.qsa_workspace_size(cfg(dtype=B.QSA_F32), B.QSA_OP_DECODE, 8, 1, 300000) == 0
+
+
+@pytest.mark.parametrize("field,value,status,word", [
+    ("block_size", 8, B.QSA_ERR_UNSUPPORTED, "block_size"),
+    ("block_size", 0, B.QSA_ERR_INVALID_ARGUMENT, "positive"),
+    ("idx_dim", 64, B.QSA_ERR_UNSUPPORTED, "idx_dim"),
+    ("rope_dims", 62, B.QSA_ERR_UNSUPPORTED, "rope_dims"),
+    ("head_dim", 96, B.QSA_ERR_UNSUPPORTED, "head_dim"),
+    ("token_budget", 2052, B.QSA_ERR_UNSUPPORTED, "k_B"),      # k_B = 513
+    ("kv_heads", 3, B.QSA_ERR_INVALID_ARGUMENT, "kv_heads"),
+    ("dtype", 7, B.QSA_ERR_INVALID_ARGUMENT, "dtype"),
+    ("rope_base", -1.0, B.QSA_ERR_INVALID_ARGUMENT, "rope_base"),
+    ("rms_eps", -1.0, B.QSA_ERR_INVALID_ARGUMENT, "rms_eps"),
+])
+def test_config_validation(lib, field, value, status, word):
+    c = cfg(**{field: value})
+    with pytest.raises(B.QsaError) as e:
+        qsa.qsa_workspace_size(c, B.QSA_OP_SELECT, 1, 1, 8)
+    assert e.value.status == status
+    assert word in str(e.value)
+
+
+FAKE = 1 << 20  # a 16-byte-aligned non-null address; never dereferenced
+
+
+def test_null_and_alignment_rejected_before_launch(lib):
+    c = cfg()
+    with pytest.raises(B.QsaError) as e:
+        qsa.qsa_index_build(c, 1, None, 64, FAKE, FAKE, 1, None, FAKE, stream=0)
+    assert e.value.status == B.QSA_ERR_INVALID_ARGUMENT and "k_idx" in str(e.value)
+    with pytest.raises(B.QsaError) as e:
+        qsa.qsa_select_topk(c, 1, 4, FAKE + 4, FAKE, 8, FAKE, 64, FAKE, FAKE, None, FAKE, 1 << 20,
+                            stream=0)
+    assert "q_idx" in str(e.value) and "16-byte" in str(e.value)
+    with pytest.raises(B.QsaError) as e:
+        qsa.qsa_sparse_attn_prefill(c, 1, 4, FAKE, FAKE, FAKE, 64, FAKE, 8, FAKE, FAKE, None,
+                                    None, None, 0, stream=0)
+    assert "out" in str(e.value)
+
+
+def test_sizes_rejected_before_launch(lib):
+    c = cfg()
+    for args, word in [((0, 4, 8), "batch"), ((1, 0, 8), "n_q"), ((1, 4, 0), "max_pos_end"),
+                       ((1, 4, 65), "max_pos_end")]:
+        b, nq, mpe = args
+        with pytest.raises(B.QsaError) as e:
+            qsa.qsa_sparse_attn_prefill(c, b, nq, FAKE, FAKE, FAKE, 64, FAKE, mpe, FAKE, FAKE, FAKE,
+                                        None, None, 0, stream=0)
+        assert e.value.status == B.QSA_ERR_INVALID_ARGUMENT and word in str(e.value)
+
+
+def test_workspace_too_small_rejected(lib):
+    c = cfg()
+    need = qsa.qsa_workspace_size(c, B.QSA_OP_SELECT, 1, 16, 64)
+    with pytest.raises(B.QsaError) as e:
+        qsa.qsa_select_topk(c, 1, 16, FAKE, FAKE, 64, FAKE, 64, FAKE, FAKE, None, FAKE, need - 1,
+                            stream=0)
+    assert e.value.status == B.QSA_ERR_WORKSPACE
+    dneed = qsa.qsa_workspace_size(c, B.QSA_OP_DECODE, 2, 1, 64)
+    with pytest.raises(B.QsaError) as e:
+        qsa.qsa_sparse_attn_decode(c, 2, FAKE, FAKE, FAKE, 64, FAKE, 64, FAKE, FAKE, FAKE, None,
+                                   None, dneed, stream=0)
+    assert e.value.status == B.QSA_ERR_WORKSPACE
+
+
+def test_product_has_no_oracle_dependency():
+    pkg = os.path.join(ROOT, "block_sparse_trainable_amd")
+    pat = re.compile(r"^\s*(import\s+oracle|from\s+oracle|from\s+\.\.oracle)|#include\s+.*oracle",
+                     re.M)
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".h", ".cpp")):
+                assert not pat.search(open(os.path.join(dirpath, f)).read()), f
