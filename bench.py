@@ -1,0 +1,294 @@
+"""QSA layer forward pass benchmark on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--workload chunked|prefill]
+                    [--decode {decode,stack,none}] [--no-cpu-baseline]
+
+One step = one pass of the whole hot path over one batch of synthetic input:
+index build of the chunk's new blocks -> block scoring + top-k_B selection ->
+sparse attention.  The headline workload is chunked prefill at 128K context
+(2 sequences, 131,072 cached tokens, 8,192 new queries each, 16Q/2KV heads,
+d=128, K=2048, r=4, bf16); `value` is prefill tokens/s with every input
+resident in HBM.  Alongside, the decode loop (8 sequences at 256K context,
+one token per sequence per step: index build, selection, split attention)
+is timed over 64 steps and reported as microseconds per step.
+
+Timing: torch.cuda events on the stream every kernel is launched on (the
+binding launches on torch's current stream), a device synchronisation on
+both sides of the timed region.  The dominant kernel's average duration is
+taken from events around its launches inside the timed region.
+
+Prints one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "QSA prefill tok/s + decode µs/step at 128K–1M ctx; % of HBM/MFMA roofline"
+HBM_PEAK_GBS = 8000.0
+BF16_MFMA_PEAK_TFLOPS = 2500.0
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", choices=["chunked", "prefill"], default="chunked")
+    ap.add_argument("--decode", choices=["decode", "none"], default="decode")
+    ap.add_argument("--decode-steps", type=int, default=64)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-rows", type=int, default=768,
+                    help="query rows in the oracle's timed sample")
+    return ap.parse_args()
+
+
+# ------------------------------------------------------------ workloads ----
+def make_prefill_inputs(name):
+    from block_sparse_trainable_amd import synth
+    if name == "chunked":
+        return synth.chunked(), {"workload": "chunked-prefill-128k", "batch": 2,
+                                 "cached_tokens": 131072, "chunk_tokens": 8192}
+    return synth.prefill(), {"workload": "prefill-32k", "batch": 1, "cached_tokens": 0,
+                             "chunk_tokens": 32768}
+
+
+def token_visits(x) -> int:
+    """sum over queries of |S_i| = 4*min(k_B, c_i) + (p_i mod 4) + 1."""
+    kB = x.layout.k_blocks
+    tot = 0
+    for s in range(x.batch):
+        p = x.q_pos0[s] + np.arange(x.n_q, dtype=np.int64)
+        c = p // 4
+        tot += int((4 * np.minimum(kB, c) + (p % 4) + 1).sum())
+    return tot
+
+
+def score_pairs(x) -> int:
+    """sum over queries of c_i (visible candidate blocks)."""
+    tot = 0
+    for s in range(x.batch):
+        p = x.q_pos0[s] + np.arange(x.n_q, dtype=np.int64)
+        tot += int((p // 4).sum())
+    return tot
+
+
+# ---------------------------------------------------------------- prefill --
+def bench_prefill(args, torch):
+    from block_sparse_trainable_amd.runtime import DeviceLayer
+    t0 = time.time()
+    x, cfg = make_prefill_inputs(args.workload)
+    log(f"generated {x.name} in {time.time() - t0:.1f}s")
+    dl = DeviceLayer(x, "cuda:0")
+    dl.build_prefix(x.cache_len)
+    torch.cuda.synchronize()
+    outs = dl.alloc_prefill_outputs()
+    sel, cnt, scs, out, lse = outs
+    r = x.layout.block_size
+    q_pos0 = dl.i32(x.q_pos0)
+    cache_len = dl.i32(x.cache_len)
+    end_np = x.q_pos0.astype(np.int64) + x.n_q
+    end = dl.i32(end_np)
+    max_pos_end = int(end_np.max())
+    new_blocks = int((end_np // r - x.cache_len // r).max())
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+
+    def step(rec=None):
+        e = [ev() for _ in range(4)] if rec is not None else None
+        if e: e[0].record()
+        dl.index_build(cache_len, end, new_blocks)
+        if e: e[1].record()
+        dl.select(dl.q_idx, q_pos0, max_pos_end, sel, cnt, scs)
+        if e: e[2].record()
+        dl.attend_prefill(dl.q, q_pos0, max_pos_end, sel, cnt, out, lse)
+        if e:
+            e[3].record()
+            rec.append(e)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log("prefill warm")
+    recs = []
+    start, stop = ev(), ev()
+    torch.cuda.synchronize()
+    start.record()
+    for _ in range(args.steps):
+        step(recs)
+    stop.record()
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(stop)
+    ms = total_ms / args.steps
+    build_ms = np.mean([e[0].elapsed_time(e[1]) for e in recs])
+    select_ms = np.mean([e[1].elapsed_time(e[2]) for e in recs])
+    attn_ms = np.mean([e[2].elapsed_time(e[3]) for e in recs])
+    toks = x.batch * x.n_q
+    visits = token_visits(x)
+    pairs = score_pairs(x)
+    attn_bytes = visits * x.layout.kv_heads * x.layout.head_dim * 2 * 2
+    res = {
+        "ms_per_step": ms, "tok_s": toks / (ms / 1e3), "tokens": toks,
+        "stages_ms": {"index_build": build_ms, "score_select": select_ms,
+                      "sparse_attn_prefill": attn_ms},
+        "attn_bytes": attn_bytes, "token_visits": visits, "score_pairs": pairs,
+        "score_flops": pairs * 2 * x.layout.idx_heads * x.layout.idx_dim,
+    }
+    cfg.update({"q_heads": x.layout.q_heads, "kv_heads": x.layout.kv_heads,
+                "head_dim": x.layout.head_dim, "token_budget": x.layout.token_budget,
+                "block_size": r, "idx_heads": x.layout.idx_heads, "idx_dim": x.layout.idx_dim})
+    del dl, outs
+    torch.cuda.empty_cache()
+    return x, cfg, res
+
+
+# ----------------------------------------------------------------- decode --
+def bench_decode(args, torch):
+    from block_sparse_trainable_amd import synth
+    from block_sparse_trainable_amd.runtime import DeviceLayer
+    steps = args.decode_steps
+    t0 = time.time()
+    x = synth.decode(steps=steps)
+    log(f"generated {x.name} in {time.time() - t0:.1f}s")
+    dl = DeviceLayer(x, "cuda:0")
+    dl.build_prefix(x.cache_len)
+    plan = dl.decode_plan(steps)
+    outs = dl.alloc_decode_outputs()
+    torch.cuda.synchronize()
+    for t in range(min(8, steps)):          # warm-up (rebuilding a block is idempotent)
+        dl.decode_step(plan, t, outs)
+    torch.cuda.synchronize()
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    torch.cuda.synchronize()
+    evs[0].record()
+    for t in range(steps):
+        dl.decode_step(plan, t, outs)
+        evs[t + 1].record()
+    torch.cuda.synchronize()
+    per = np.array([evs[t].elapsed_time(evs[t + 1]) for t in range(steps)]) * 1e3
+    total_us = evs[0].elapsed_time(evs[-1]) * 1e3
+    kB = x.layout.k_blocks
+    ctx = x.q_pos0.astype(np.int64)
+    scan_bytes = int(sum((ctx[s] + t) // 4 for s in range(x.batch) for t in range(steps))) * 256 // steps
+    gather = int(x.batch * (4 * kB + 4) * x.layout.kv_heads * x.layout.head_dim * 4)
+    res = {"workload": "decode-256k", "batch": x.batch, "context": int(ctx.min()),
+           "steps": steps, "us_per_step": total_us / steps,
+           "p50_us": float(np.percentile(per, 50)), "p99_us": float(np.percentile(per, 99)),
+           "algorithmic_bytes_per_step": scan_bytes + gather,
+           "hbm_frac": (scan_bytes + gather) / (total_us / steps * 1e-6) / (HBM_PEAK_GBS * 1e9)}
+    del dl, outs
+    torch.cuda.empty_cache()
+    return res
+
+
+# ------------------------------------------------------------ cpu oracle --
+def cpu_baseline(x, rows: int):
+    """The fp64 oracle on a bounded sample of the same chunk: compression of
+    every new block of the chunk, then `rows` query rows (scoring, top-k,
+    attention), single-threaded; extrapolated to the full chunk."""
+    from threadpoolctl import threadpool_limits
+    from oracle import qsa_oracle as O
+    from block_sparse_trainable_amd import synth
+    lay = x.layout
+    f64 = lambda a: synth.as_f32(a, lay.dtype).astype(np.float64)
+    rng = np.random.default_rng(7)
+    with threadpool_limits(limits=1):
+        t_comp = 0.0
+        khat = []
+        for s in range(x.batch):
+            # the cached prefix is setup work on both sides; only the chunk's
+            # new blocks are timed
+            nb_all = (int(x.q_pos0[s]) + x.n_q) // lay.block_size
+            nb_old = int(x.cache_len[s]) // lay.block_size
+            k_idx = f64(x.k_idx[s, :nb_all * lay.block_size])
+            kh_old = O.compress_index(k_idx[:nb_old * 4], nb_old, gain=x.gain.astype(np.float64),
+                                      eps=float(np.float32(lay.rms_eps)), storage=lay.dtype)
+            t = time.perf_counter()
+            kh_all = O.compress_index(k_idx, nb_all, gain=x.gain.astype(np.float64),
+                                      eps=float(np.float32(lay.rms_eps)), storage=lay.dtype)
+            t_comp += (time.perf_counter() - t) * (nb_all - nb_old) / max(nb_all, 1)
+            khat.append(kh_all)
+            del kh_old
+        per_seq = max(1, rows // x.batch)
+        t_rows = 0.0
+        n_rows = 0
+        for s in range(x.batch):
+            K, V = f64(x.k[s]), f64(x.v[s])
+            q_idx, q = f64(x.q_idx[s]), f64(x.q[s])
+            for j in rng.choice(x.n_q, size=min(per_seq, x.n_q), replace=False):
+                p = int(x.q_pos0[s]) + int(j)
+                t = time.perf_counter()
+                O.qsa_row(p, q_idx[j], q[j], khat[s], K, V, k_B=lay.k_blocks)
+                t_rows += time.perf_counter() - t
+                n_rows += 1
+    total = x.batch * x.n_q
+    est = t_comp + t_rows * total / n_rows
+    return {"value": total / est, "unit": "tok/s", "cores": 1, "kind": "oracle",
+            "sample": (f"{n_rows} of {total} query rows (uniform seeded sample) plus the "
+                       f"compression of the chunk's new blocks, single thread; extrapolated "
+                       f"to the full chunk"),
+            "measured_s": t_comp + t_rows}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py runs on exactly one GPU: the QSA forward path here is single-GPU "
+              "(no sharding or collectives are built); use --gpus 1", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import block_sparse_trainable_amd as qsa
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    qsa.load()
+    torch.cuda.set_device(0)
+
+    x, cfg, pre = bench_prefill(args, torch)
+    log(f"prefill {pre['tok_s']:.0f} tok/s, {pre['ms_per_step']:.3f} ms/step, "
+        f"stages {pre['stages_ms']}")
+    dec = bench_decode(args, torch) if args.decode != "none" else None
+    if dec:
+        log(f"decode {dec['us_per_step']:.1f} us/step")
+
+    attn_ms = pre["stages_ms"]["sparse_attn_prefill"]
+    achieved = pre["attn_bytes"] / (attn_ms * 1e-3) / 1e9
+    roofline = {"kernel": "sparse_attn_prefill (attn_mfma_kernel<2,128>)", "bound": "hbm",
+                "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                "algorithmic_bytes_per_launch": pre["attn_bytes"],
+                "avg_launch_ms": attn_ms}
+    score_tflops = pre["score_flops"] / (pre["stages_ms"]["score_select"] * 1e-3) / 1e12
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle) ...")
+        cpu = cpu_baseline(x, args.cpu_rows)
+        log(f"cpu baseline {cpu['value']:.2f} tok/s over {cpu['measured_s']:.1f}s")
+
+    line = {
+        "metric": METRIC, "value": pre["tok_s"], "unit": "tok/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": pre["ms_per_step"],
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic", "config": cfg, "roofline": roofline, "cpu_baseline": cpu,
+        "stages_ms": pre["stages_ms"],
+        "score_select_effective_tflops": score_tflops,
+        "decode": dec,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

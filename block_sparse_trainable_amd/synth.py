@@ -40,12 +40,19 @@ _STREAMS = ("k_idx", "q_idx", "q", "k", "v", "structure", "steps")
 # --------------------------------------------------------------------------
 # storage dtype helpers (input preparation only)
 # --------------------------------------------------------------------------
-def f32_to_bf16(x: np.ndarray) -> np.ndarray:
-    """fp32 -> bf16 bit patterns, round to nearest, ties to even."""
+def f32_to_bf16(x: np.ndarray, chunk: int = 1 << 24) -> np.ndarray:
+    """fp32 -> bf16 bit patterns, round to nearest, ties to even.
+
+    uint32 arithmetic cannot overflow for finite inputs (the largest finite
+    pattern plus the rounding bias stays below 2^32); chunked to bound memory.
+    """
     x = np.ascontiguousarray(x, dtype=np.float32)
-    u = x.view(np.uint32).astype(np.uint64)
-    u = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
-    return u.astype(np.uint16)
+    u = x.reshape(-1).view(np.uint32)
+    out = np.empty(u.size, dtype=np.uint16)
+    for s in range(0, u.size, chunk):
+        v = u[s:s + chunk]
+        out[s:s + chunk] = ((v + np.uint32(0x7FFF) + ((v >> 16) & np.uint32(1))) >> 16).astype(np.uint16)
+    return out.reshape(x.shape)
 
 
 def bf16_to_f32(u: np.ndarray) -> np.ndarray:

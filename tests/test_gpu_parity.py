@@ -98,7 +98,8 @@ def test_index_build_matches_oracle_with_ragged_ranges(dtype):
         ulp = np.abs(ref) * (2.0 ** -7 if dtype == "bf16" else 2.0 ** -23)
         diff = np.abs(built - ref)
         assert (diff <= ulp + 1e-30).all(), f"seq {s}: compression error {diff.max():.3e}"
-        assert np.mean(diff > 0) < 1e-3
+        if diff.size:
+            assert np.mean(diff > 0) < 1e-3
         assert (got[s, :b0] == sentinel).all() and (got[s, b1:] == sentinel).all()
 
 
