@@ -30,6 +30,9 @@
 //     read feeding two MFMAs.
 //   * The 4 waves of a workgroup interleave tiles and merge their (m, l, O)
 //     states in LDS at the end.
+//   * Decode splits a query's token set over workgroups; each writes its
+//     merged (m, l, O) state and the last one to finish (device-scope
+//     counter per row, left at zero) merges all splits.
 #include <math.h>
 
 #include "qsa_common.h"
@@ -137,7 +140,7 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(
     const uint16_t* __restrict__ vc, int64_t cap, int n_q, const int32_t* __restrict__ q_pos0,
     const int32_t* __restrict__ sel, const int32_t* __restrict__ cnt, int kB, float scale_log2,
     uint16_t* __restrict__ out, float* __restrict__ lse, float* __restrict__ part,
-    int n_split, int pb_per_split) {
+    uint32_t* __restrict__ counters, int n_split, int pb_per_split) {
   using S = MfmaShape<HKV, D>;
   constexpr int KD = S::KD, NK = S::NK, ROWB = S::ROWB, G = S::G;
   static_assert(4 * S::MERGE_FLOATS * 4 <= 4 * S::TILE_LDS, "merge area must fit");
@@ -342,14 +345,17 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(
       }
     }
   }
-}
+  if (n_split == 1) return;
 
-// Log-sum-exp merge of the decode splits of one row.
-template <int D>
-__global__ __launch_bounds__(256) void attn_combine_kernel(const float* __restrict__ part,
-                                                           int n_split, uint16_t* __restrict__ out,
-                                                           float* __restrict__ lse) {
-  const int64_t row = blockIdx.x;
+  // ---- decode: the last split of the row merges every split's state
+  __threadfence();
+  __syncthreads();
+  __shared__ uint32_t last;
+  if (threadIdx.x == 0) last = (atomicAdd(&counters[row], 1u) == (uint32_t)n_split - 1u) ? 1u : 0u;
+  __syncthreads();
+  if (!last) return;
+  __threadfence();
+  if (threadIdx.x == 0) counters[row] = 0u;  // leave the counter zeroed
   const float* base = part + row * n_split * (16 * D + 32);
   for (int idx = threadIdx.x; idx < 16 * D; idx += 256) {
     const int n = idx / D, dd = idx % D;
@@ -384,23 +390,16 @@ hipError_t launch_mfma(const Dims& d, int rows, int n_q, const void* q, const vo
                        const int32_t* cnt, void* out, float* lse, void* ws, bool decode,
                        hipStream_t st) {
   const float sl2 = d.scale * kLog2e;
-  if (!decode) {
-    hipLaunchKernelGGL((attn_mfma_kernel<HKV, D>), dim3(rows), dim3(256), 0, st,
-                       static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(kc),
-                       static_cast<const uint16_t*>(vc), cap, n_q, q_pos0, sel, cnt, d.kB, sl2,
-                       static_cast<uint16_t*>(out), lse, (float*)nullptr, 1, d.kB + 1);
-    return hipGetLastError();
-  }
-  const int ns = decode_splits(d);
-  float* part = static_cast<float*>(ws);
+  const int ns = decode ? decode_splits(d) : 1;
+  uint32_t* counters = decode ? static_cast<uint32_t*>(ws) : nullptr;
+  float* part = decode ? reinterpret_cast<float*>(static_cast<char*>(ws) +
+                                                  sizeof(uint32_t) * kAttnCounterRows)
+                       : nullptr;
   hipLaunchKernelGGL((attn_mfma_kernel<HKV, D>), dim3((unsigned)(rows * ns)), dim3(256), 0, st,
                      static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(kc),
                      static_cast<const uint16_t*>(vc), cap, n_q, q_pos0, sel, cnt, d.kB, sl2,
-                     static_cast<uint16_t*>(out), lse, part, ns, kDecodeSplitPB);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((attn_combine_kernel<D>), dim3(rows), dim3(256), 0, st, part, ns,
-                     static_cast<uint16_t*>(out), lse);
+                     static_cast<uint16_t*>(out), lse, part, counters, ns,
+                     decode ? kDecodeSplitPB : d.kB + 1);
   return hipGetLastError();
 }
 
@@ -408,7 +407,8 @@ hipError_t launch_mfma(const Dims& d, int rows, int n_q, const void* q, const vo
 
 size_t attn_workspace_bytes(const Dims& d, int rows, bool decode) {
   if (!decode || !use_mfma(d)) return 0;
-  return sizeof(float) * (size_t)rows * decode_splits(d) * (16 * d.head_dim + 32);
+  return sizeof(uint32_t) * kAttnCounterRows +
+         sizeof(float) * (size_t)rows * decode_splits(d) * (16 * d.head_dim + 32);
 }
 
 hipError_t launch_attn(const Dims& d, int batch, int n_q, const void* q, const void* k_cache,

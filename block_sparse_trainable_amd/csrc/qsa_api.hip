@@ -103,8 +103,7 @@ qsa_status check_sizes(const char* fn, int32_t batch, int32_t n_q, int64_t cap_t
 }
 
 size_t select_ws(const qsa::Dims& d, int32_t batch, int32_t n_q, int32_t max_pos_end) {
-  const int64_t W = qsa::score_row_width(d.r, max_pos_end);
-  return sizeof(float) * (size_t)batch * (size_t)n_q * (size_t)W;
+  return qsa::select_plan(d, batch, n_q, max_pos_end).bytes;
 }
 
 qsa_status launched(const char* fn, hipError_t e) {
@@ -198,13 +197,12 @@ qsa_status qsa_select_topk(const qsa_config* cfg, int32_t batch, int32_t n_q,
                 workspace ? workspace_bytes : (size_t)0);
   if (!aligned16(workspace))
     return fail(QSA_ERR_INVALID_ARGUMENT, "%s: workspace must be 16-byte aligned", fn);
-  const int64_t W = qsa::score_row_width(d.r, max_pos_end);
-  float* scores = static_cast<float*>(workspace);
-  hipError_t e = qsa::launch_score(d, batch, n_q, q_idx, q_pos0, max_pos_end, k_cmp, cap_tokens,
-                                   scores, W, stream);
+  const qsa::SelectPlan pl = qsa::select_plan(d, batch, n_q, max_pos_end);
+  hipError_t e = qsa::launch_score(d, pl, batch, n_q, q_idx, q_pos0, k_cmp, cap_tokens,
+                                   workspace, stream);
   if (e == hipSuccess)
-    e = qsa::launch_select(d, batch, n_q, q_pos0, cap_tokens, scores, W, sel_blocks, sel_count,
-                           sel_scores, stream);
+    e = qsa::launch_select(d, pl, batch, n_q, q_pos0, cap_tokens, workspace, sel_blocks,
+                           sel_count, sel_scores, stream);
   return launched(fn, e);
 }
 
@@ -228,6 +226,9 @@ static qsa_status attn_common(const char* fn, const qsa_config* cfg, int32_t bat
   QSA_REQUIRE_PTR(out, 4);
   if (lse && !aligned(lse, 4))
     return fail(QSA_ERR_INVALID_ARGUMENT, "%s: lse must be 4-byte aligned", fn);
+  if (decode && batch > qsa::kAttnCounterRows)
+    return fail(QSA_ERR_UNSUPPORTED, "%s: batch %d (at most %lld)", fn, batch,
+                (long long)qsa::kAttnCounterRows);
   const size_t need = qsa::attn_workspace_bytes(d, batch * n_q, decode);
   if (need > 0) {
     if (!workspace || workspace_bytes < need)

@@ -58,6 +58,24 @@ __device__ __forceinline__ u32x4 ld16(const void* p) {
 
 __device__ __forceinline__ float relu(float x) { return x > 0.0f ? x : 0.0f; }
 
+// ------------------------------------------------- score histogram bins ----
+// Scores are >= +0.0.  bin() maps a score's IEEE bits to one of 256 bins, 8
+// per octave over [2^-16, 2^16) (exponent and top 3 mantissa bits), scores
+// outside clamped to the end bins.  It is monotone non-decreasing in the
+// score, which is all the selection relies on.
+constexpr int kHistBins = 256;
+constexpr int kHistWords = kHistBins / 2;  // two u16 counts per u32 word
+
+__device__ __forceinline__ uint32_t score_bin(uint32_t bits) {
+  const int k = (int)(bits >> 20) - 888;  // 888 = 111 * 8: exponent of 2^-16
+  return (uint32_t)min(max(k, 0), kHistBins - 1);
+}
+
+// Per-segment histogram slot of (row, segment): kHistWords u32 words.
+__host__ __device__ inline int64_t hist_offset(int64_t row, int64_t seg, int64_t n_seg) {
+  return (row * n_seg + seg) * kHistWords;
+}
+
 // --------------------------------------------------------- launch params ----
 struct Dims {
   int r, kB, idx_heads, idx_dim, rope_dims, q_heads, kv_heads, head_dim;
@@ -74,6 +92,24 @@ inline int64_t score_row_width(int r, int32_t max_pos_end) {
   return (c + 3) / 4 * 4;
 }
 
+// Layout of the select workspace, derived from the call's sizes only.
+//   scores  [rows][W] f32          block-importance rows
+//   hist    [rows][n_sseg][128] u32 per-score-segment histograms (u16 pairs)
+//   slots   [rows][n_fseg][kSlotCap] u32x2 candidates of each filter segment
+//   slotcnt [rows][n_fseg] u32
+//   done    [rows] u32             filter-segment completion counters
+struct SelectPlan {
+  int kernel;        // 0 = VALU, 1 = MFMA prefill, 2 = MFMA decode
+  int64_t W;         // score row width
+  int64_t sseg;      // blocks per score segment
+  int64_t n_sseg;
+  int64_t fseg;      // scores per filter segment
+  int64_t n_fseg;
+  size_t off_hist, off_slots, off_slotcnt, off_done, bytes;
+};
+constexpr int kSlotCap = 1024;      // candidates one filter segment may hand over
+SelectPlan select_plan(const struct Dims& d, int batch, int n_q, int32_t max_pos_end);
+
 // ------------------------------------------------------------ launchers ----
 // Each returns hipSuccess or the launch error; arguments are pre-validated.
 hipError_t launch_compress(const Dims& d, int batch, const void* k_idx, int64_t cap,
@@ -81,14 +117,18 @@ hipError_t launch_compress(const Dims& d, int batch, const void* k_idx, int64_t 
                            int max_new_blocks, const float* gain, void* k_cmp,
                            hipStream_t st);
 
-hipError_t launch_score(const Dims& d, int batch, int n_q, const void* q_idx,
-                        const int32_t* q_pos0, int32_t max_pos_end, const void* k_cmp,
-                        int64_t cap, float* scores, int64_t W, hipStream_t st);
+hipError_t launch_score(const Dims& d, const SelectPlan& pl, int batch, int n_q,
+                        const void* q_idx, const int32_t* q_pos0, const void* k_cmp,
+                        int64_t cap, void* workspace, hipStream_t st);
 
-hipError_t launch_select(const Dims& d, int batch, int n_q, const int32_t* q_pos0,
-                         int64_t cap, const float* scores, int64_t W, int32_t* sel,
+hipError_t launch_select(const Dims& d, const SelectPlan& pl, int batch, int n_q,
+                         const int32_t* q_pos0, int64_t cap, void* workspace, int32_t* sel,
                          int32_t* cnt, float* sel_scores, hipStream_t st);
 
+// Decode attention workspace: [kAttnCounterRows] u32 completion counters
+// (must be zero before the first call; every call leaves them zero), then
+// the per-split partial states.
+constexpr int64_t kAttnCounterRows = 65536;
 size_t attn_workspace_bytes(const Dims& d, int rows, bool decode);
 
 hipError_t launch_attn(const Dims& d, int batch, int n_q, const void* q, const void* k_cache,

@@ -12,10 +12,28 @@
 // the four heads of one query for one block, so ReLU and the head sum happen
 // in registers with no cross-lane traffic.  A and B fill each k-slot with the
 // same dims, so the sum over k does not depend on the hardware's k order.
+//
+// Every kernel also leaves, per (query row, score segment), a 256-bin
+// histogram of the scores it wrote (score_bin; u16 counts packed in pairs,
+// accumulated in LDS and written once per workgroup), and zeroes the row's
+// filter completion counter; the selection kernel reads both.
 #include "qsa_common.h"
 
 namespace qsa {
 namespace {
+
+__device__ __forceinline__ void hist_add(uint32_t* h, float v) {
+  const uint32_t b = score_bin(__float_as_uint(v));
+  atomicAdd(&h[b >> 1], 1u << ((b & 1u) << 4));
+}
+
+struct ScoreOut {
+  float* scores;      // [rows][W]
+  int64_t W;
+  uint32_t* hist;     // [rows][n_sseg][kHistWords]
+  int64_t n_sseg;
+  uint32_t* done;     // [rows]
+};
 
 // ----------------------------------------------------------------- VALU ----
 // Any dtype / head count: one workgroup per (query, 256 blocks), the query's
@@ -23,14 +41,16 @@ namespace {
 template <bool BF16>
 __global__ __launch_bounds__(256) void score_valu_kernel(
     const void* __restrict__ q_idx_v, const int32_t* __restrict__ q_pos0, int n_q, int H,
-    int D, const void* __restrict__ k_cmp_v, int64_t cap_blocks, float* __restrict__ scores,
-    int64_t W) {
+    int D, const void* __restrict__ k_cmp_v, int64_t cap_blocks, ScoreOut o) {
   extern __shared__ float qs[];  // [H][D]
+  __shared__ uint32_t hist[kHistWords];
   const int64_t row = blockIdx.x;
   const int s = (int)(row / n_q);
   const int j = (int)(row % n_q);
   const int64_t p = (int64_t)q_pos0[s] + j;
-  const int64_t c = min(min(p / 4, cap_blocks), W);
+  const int64_t c = min(min(p / 4, cap_blocks), o.W);
+  if (blockIdx.y == 0 && threadIdx.x == 0) o.done[row] = 0u;
+  for (int i = threadIdx.x; i < kHistWords; i += blockDim.x) hist[i] = 0u;
   for (int i = threadIdx.x; i < H * D; i += blockDim.x) {
     const int64_t off = row * H * D + i;
     qs[i] = BF16 ? bf16_to_f32(static_cast<const uint16_t*>(q_idx_v)[off])
@@ -38,19 +58,25 @@ __global__ __launch_bounds__(256) void score_valu_kernel(
   }
   __syncthreads();
   const int64_t b = (int64_t)blockIdx.y * blockDim.x + threadIdx.x;
-  if (b >= c) return;
-  const int64_t kb = ((int64_t)s * cap_blocks + b) * D;
-  float acc = 0.0f;
-  for (int h = 0; h < H; ++h) {
-    float dot = 0.0f;
-    for (int d = 0; d < D; ++d) {
-      const float kv = BF16 ? bf16_to_f32(static_cast<const uint16_t*>(k_cmp_v)[kb + d])
-                            : static_cast<const float*>(k_cmp_v)[kb + d];
-      dot = fmaf(qs[h * D + d], kv, dot);
+  if (b < c) {
+    const int64_t kb = ((int64_t)s * cap_blocks + b) * D;
+    float acc = 0.0f;
+    for (int h = 0; h < H; ++h) {
+      float dot = 0.0f;
+      for (int d = 0; d < D; ++d) {
+        const float kv = BF16 ? bf16_to_f32(static_cast<const uint16_t*>(k_cmp_v)[kb + d])
+                              : static_cast<const float*>(k_cmp_v)[kb + d];
+        dot = fmaf(qs[h * D + d], kv, dot);
+      }
+      acc += relu(dot);
     }
-    acc += relu(dot);
+    o.scores[row * o.W + b] = acc;
+    hist_add(hist, acc);
   }
-  scores[row * W + b] = acc;
+  __syncthreads();
+  if ((int64_t)blockIdx.y < o.n_sseg)
+    for (int i = threadIdx.x; i < kHistWords; i += blockDim.x)
+      o.hist[hist_offset(row, blockIdx.y, o.n_sseg) + i] = hist[i];
 }
 
 // ------------------------------------------------------ MFMA, prefill ------
@@ -65,9 +91,11 @@ constexpr int kRowB = 272;    // LDS bytes per block row (256 + 16 pad)
 
 __global__ __launch_bounds__(256) void score_mfma_prefill_kernel(
     const uint16_t* __restrict__ q_idx, const int32_t* __restrict__ q_pos0, int n_q,
-    const uint16_t* __restrict__ k_cmp, int64_t cap_blocks, int seg_blocks,
-    float* __restrict__ scores, int64_t W) {
+    const uint16_t* __restrict__ k_cmp, int64_t cap_blocks, int seg_blocks, ScoreOut o) {
   __shared__ __attribute__((aligned(16))) unsigned char lds[2][kChunk * kRowB];
+  __shared__ uint32_t hist[kPQ][kHistWords];
+  float* __restrict__ scores = o.scores;
+  const int64_t W = o.W;
   const int s = blockIdx.z;
   // longest rows first: the last query tiles have the most blocks
   const int qt = gridDim.x - 1 - blockIdx.x;
@@ -79,10 +107,13 @@ __global__ __launch_bounds__(256) void score_mfma_prefill_kernel(
   const int j0 = qt * kPQ;
   const int j_last = min(j0 + kPQ, n_q) - 1;
   const int64_t pos0 = q_pos0[s];
+  if (blockIdx.y == 0 && threadIdx.x < kPQ && j0 + (int)threadIdx.x < n_q)
+    o.done[(int64_t)s * n_q + j0 + threadIdx.x] = 0u;
   const int64_t c_tile = min(min((pos0 + j_last) / 4, cap_blocks), W);
   const int64_t b_lo = (int64_t)blockIdx.y * seg_blocks;
   const int64_t b_hi = min(b_lo + seg_blocks, c_tile);
-  if (b_lo >= b_hi) return;
+  if (b_lo >= b_hi) return;  // no query of the tile reaches this segment
+  for (int i = threadIdx.x; i < kPQ * kHistWords; i += 256) (&hist[0][0])[i] = 0u;
 
   // A operands: row tile rt covers queries j0 + 16w + 4rt + (0..3)
   u32x4 qa[4][4];
@@ -148,14 +179,18 @@ __global__ __launch_bounds__(256) void score_mfma_prefill_kernel(
     // epilogue: lane holds 4 heads of query (4rt + gq) for block 16ct + l16
 #pragma unroll
     for (int rt = 0; rt < 4; ++rt) {
-      const int jq = j0 + 16 * wave + 4 * rt + gq;
+      const int ql = 16 * wave + 4 * rt + gq;
+      const int jq = j0 + ql;
       float* dst = scores + ((int64_t)s * n_q + jq) * W;
 #pragma unroll
       for (int ct = 0; ct < 4; ++ct) {
         const int64_t b = cb + 16 * ct + l16;
         const f32x4 a = acc[rt][ct];
         const float v = relu(a[0]) + relu(a[1]) + relu(a[2]) + relu(a[3]);
-        if (b < cq[rt]) dst[b] = v;
+        if (b < cq[rt]) {
+          dst[b] = v;
+          hist_add(hist[ql], v);
+        }
       }
     }
     if (more) {
@@ -164,18 +199,26 @@ __global__ __launch_bounds__(256) void score_mfma_prefill_kernel(
       buf ^= 1;
     }
   }
+  __syncthreads();
+  for (int i = threadIdx.x; i < kPQ * kHistWords; i += 256) {
+    const int ql = i / kHistWords, w = i % kHistWords;
+    if (j0 + ql < n_q)
+      o.hist[hist_offset((int64_t)s * n_q + j0 + ql, blockIdx.y, o.n_sseg) + w] = hist[ql][w];
+  }
 }
 
 // ------------------------------------------------------- MFMA, decode ------
 // Few queries, long rows: workgroup = (segment of blocks, 4 queries).  The
 // four waves take disjoint 64-block chunks of the segment and read their B
 // tiles straight from HBM (no reuse to stage); rows are 4 queries x 4 heads.
-constexpr int kDecSeg = 1024;
+constexpr int kDecSeg = 2048;
 
 __global__ __launch_bounds__(256) void score_mfma_decode_kernel(
     const uint16_t* __restrict__ q_idx, const int32_t* __restrict__ q_pos0, int n_q,
-    const uint16_t* __restrict__ k_cmp, int64_t cap_blocks, float* __restrict__ scores,
-    int64_t W) {
+    const uint16_t* __restrict__ k_cmp, int64_t cap_blocks, ScoreOut o) {
+  __shared__ uint32_t hist[4][kHistWords];
+  float* __restrict__ scores = o.scores;
+  const int64_t W = o.W;
   const int s = blockIdx.z;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -184,10 +227,14 @@ __global__ __launch_bounds__(256) void score_mfma_decode_kernel(
   const int j0 = 4 * blockIdx.y;
   const int64_t pos0 = q_pos0[s];
   const int j_last = min(j0 + 4, n_q) - 1;
+  if (blockIdx.x == 0 && threadIdx.x < 4 && j0 + (int)threadIdx.x < n_q)
+    o.done[(int64_t)s * n_q + j0 + threadIdx.x] = 0u;
   const int64_t c_tile = min(min((pos0 + j_last) / 4, cap_blocks), W);
   const int64_t seg_lo = (int64_t)blockIdx.x * kDecSeg;
   const int64_t seg_hi = min(seg_lo + kDecSeg, c_tile);
-  if (seg_lo >= seg_hi) return;
+  if (seg_lo >= seg_hi) return;  // no query of the tile reaches this segment
+  for (int i = threadIdx.x; i < 4 * kHistWords; i += 256) (&hist[0][0])[i] = 0u;
+  __syncthreads();
 
   u32x4 qa[4];
   {
@@ -221,40 +268,49 @@ __global__ __launch_bounds__(256) void score_mfma_decode_kernel(
                                                       acc, 0, 0, 0);
       const int64_t b = cb + 16 * ct + l16;
       const float v = relu(acc[0]) + relu(acc[1]) + relu(acc[2]) + relu(acc[3]);
-      if (b < cq) dst[b] = v;
+      if (b < cq) {
+        dst[b] = v;
+        hist_add(hist[gq], v);
+      }
     }
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < 4 * kHistWords; i += 256) {
+    const int ql = i / kHistWords, w = i % kHistWords;
+    if (j0 + ql < n_q)
+      o.hist[hist_offset((int64_t)s * n_q + j0 + ql, blockIdx.x, o.n_sseg) + w] = hist[ql][w];
   }
 }
 
 }  // namespace
 
-hipError_t launch_score(const Dims& d, int batch, int n_q, const void* q_idx,
-                        const int32_t* q_pos0, int32_t max_pos_end, const void* k_cmp,
-                        int64_t cap, float* scores, int64_t W, hipStream_t st) {
+hipError_t launch_score(const Dims& d, const SelectPlan& pl, int batch, int n_q,
+                        const void* q_idx, const int32_t* q_pos0, const void* k_cmp,
+                        int64_t cap, void* workspace, hipStream_t st) {
   const int64_t cap_blocks = cap / d.r;
-  const int64_t c_max = min((int64_t)(max_pos_end - 1) / d.r, min(cap_blocks, W));
-  if (c_max <= 0) return hipSuccess;
-  const bool mfma = d.bf16 && d.idx_heads == 4 && d.idx_dim == 128;
-  if (mfma && n_q >= 16) {
-    const int seg = 2048;
-    dim3 grid((unsigned)((n_q + kPQ - 1) / kPQ), (unsigned)((c_max + seg - 1) / seg), (unsigned)batch);
+  char* ws = static_cast<char*>(workspace);
+  ScoreOut o{reinterpret_cast<float*>(ws), pl.W, reinterpret_cast<uint32_t*>(ws + pl.off_hist),
+             pl.n_sseg, reinterpret_cast<uint32_t*>(ws + pl.off_done)};
+  const unsigned segs = (unsigned)pl.n_sseg;
+  if (pl.kernel == 1) {
+    dim3 grid((unsigned)((n_q + kPQ - 1) / kPQ), segs, (unsigned)batch);
     hipLaunchKernelGGL(score_mfma_prefill_kernel, grid, dim3(256), 0, st,
                        static_cast<const uint16_t*>(q_idx), q_pos0, n_q,
-                       static_cast<const uint16_t*>(k_cmp), cap_blocks, seg, scores, W);
-  } else if (mfma) {
-    dim3 grid((unsigned)((c_max + kDecSeg - 1) / kDecSeg), (unsigned)((n_q + 3) / 4), (unsigned)batch);
+                       static_cast<const uint16_t*>(k_cmp), cap_blocks, (int)pl.sseg, o);
+  } else if (pl.kernel == 2) {
+    dim3 grid(segs, (unsigned)((n_q + 3) / 4), (unsigned)batch);
     hipLaunchKernelGGL(score_mfma_decode_kernel, grid, dim3(256), 0, st,
                        static_cast<const uint16_t*>(q_idx), q_pos0, n_q,
-                       static_cast<const uint16_t*>(k_cmp), cap_blocks, scores, W);
+                       static_cast<const uint16_t*>(k_cmp), cap_blocks, o);
   } else {
-    dim3 grid((unsigned)(batch * n_q), (unsigned)((c_max + 255) / 256));
+    dim3 grid((unsigned)(batch * n_q), segs);
     const size_t shm = sizeof(float) * d.idx_heads * d.idx_dim;
     if (d.bf16)
       hipLaunchKernelGGL(score_valu_kernel<true>, grid, dim3(256), shm, st, q_idx, q_pos0, n_q,
-                         d.idx_heads, d.idx_dim, k_cmp, cap_blocks, scores, W);
+                         d.idx_heads, d.idx_dim, k_cmp, cap_blocks, o);
     else
       hipLaunchKernelGGL(score_valu_kernel<false>, grid, dim3(256), shm, st, q_idx, q_pos0, n_q,
-                         d.idx_heads, d.idx_dim, k_cmp, cap_blocks, scores, W);
+                         d.idx_heads, d.idx_dim, k_cmp, cap_blocks, o);
   }
   return hipGetLastError();
 }

@@ -63,11 +63,15 @@ class DeviceLayer:
         return torch.tensor(np.asarray(values, dtype=np.int32), device=self.device)
 
     def workspace(self, op: int, batch: int, n_q: int, max_pos_end: int) -> torch.Tensor:
+        """One workspace per op, grown on demand.  Zero-filled when allocated:
+        the decode attention keeps its completion counters at the head of its
+        workspace and needs them zero before the first call (every call
+        leaves them zero)."""
         n = B.qsa_workspace_size(self.cfg, op, batch, n_q, max_pos_end)
         key = (op,)
         ws = self._ws.get(key)
         if ws is None or ws.numel() < max(n, 16):
-            ws = torch.empty(max(n, 16), dtype=torch.uint8, device=self.device)
+            ws = torch.zeros(max(n, 16), dtype=torch.uint8, device=self.device)
             self._ws[key] = ws
         return ws
 
@@ -158,3 +162,40 @@ class DeviceLayer:
         self.select(q_idx_s[t].unsqueeze(1), pos_t[t], max_pos_end, sel, cnt, scs, n_q=1)
         self.attend_decode(q_s[t], pos_t[t], max_pos_end, sel, cnt, out, lse)
         return outputs
+
+    def capture_decode(self, plan, steps: int, outputs, overlap_build: bool = True):
+        """Capture `steps` decode steps into one HIP graph (torch.cuda.CUDAGraph).
+
+        With overlap_build, step t's index_build runs on a side stream: the
+        block it may complete is first a candidate at step t+1, so it only has
+        to finish before step t+1's selection, not before step t's.
+        """
+        q_idx_s, q_s, pos_t, pos1_t, max_pos_end = plan
+        sel, cnt, scs, out, lse = outputs
+        # allocate workspaces outside the capture
+        self.workspace(B.QSA_OP_SELECT, self.batch, 1, max_pos_end)
+        self.workspace(B.QSA_OP_DECODE, self.batch, 1, max_pos_end)
+        g = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream(device=self.device)
+        main = torch.cuda.current_stream(self.device)
+        side.wait_stream(main)
+        main.synchronize()
+        with torch.cuda.graph(g):
+            cap_stream = torch.cuda.current_stream(self.device)
+            built = None
+            for t in range(steps):
+                if overlap_build:
+                    side.wait_stream(cap_stream)
+                    with torch.cuda.stream(side):
+                        self.index_build(pos_t[t], pos1_t[t], 1)
+                    if built is not None:
+                        cap_stream.wait_event(built)
+                    built = torch.cuda.Event()
+                    built.record(side)
+                else:
+                    self.index_build(pos_t[t], pos1_t[t], 1)
+                self.select(q_idx_s[t].unsqueeze(1), pos_t[t], max_pos_end, sel, cnt, scs, n_q=1)
+                self.attend_decode(q_s[t], pos_t[t], max_pos_end, sel, cnt, out, lse)
+            if built is not None:
+                cap_stream.wait_event(built)
+        return g

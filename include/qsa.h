@@ -171,6 +171,11 @@ qsa_status qsa_sparse_attn_prefill(const qsa_config* cfg, int32_t batch, int32_t
  * [concept] (B); the concept page's "Why it matters" reports decode-phase
  * kernel speed-ups at 1M context.
  *
+ * Workspace state: the first 256 KiB of the decode workspace hold per-row
+ * completion counters that must be zero before the FIRST call using that
+ * buffer (e.g. one hipMemset after allocation); every call leaves them zero
+ * again.  batch <= 65536.
+ *
  *   q          (dtype) [batch][q_heads][head_dim].
  *   q_pos      int32 [batch] device: position of the new token, whose K/V
  *              rows are already written.  max_pos_end > every q_pos[s].
@@ -187,7 +192,12 @@ qsa_status qsa_sparse_attn_decode(const qsa_config* cfg, int32_t batch, const vo
                                   size_t workspace_bytes, hipStream_t stream);
 
 /* Workspace bytes needed by op (a qsa_op) for these sizes.  n_q is 1 for
- * QSA_OP_DECODE; QSA_OP_INDEX_BUILD needs none.                           */
+ * QSA_OP_DECODE; QSA_OP_INDEX_BUILD needs none.  The select workspace
+ * holds the materialised score rows, per-segment score histograms and the
+ * candidate hand-over area of long rows; it carries no state between
+ * calls.  Alignment: tensors read with 16-byte vector loads (q_idx, k_cmp
+ * in select, q, k_cache, v_cache, workspaces) must be 16-byte aligned, the
+ * others 4- or 8-byte aligned as the validation messages state.           */
 qsa_status qsa_workspace_size(const qsa_config* cfg, int32_t op, int32_t batch, int32_t n_q,
                               int32_t max_pos_end, size_t* bytes);
 

@@ -64,14 +64,37 @@ def test_status_strings(lib):
         assert lib.qsa_status_string(code).decode() == name
 
 
+def _al(v):
+    return (v + 255) // 256 * 256
+
+
 def test_workspace_sizes(lib):
     c = cfg()
-    # select: one fp32 score row per query, width = ceil4(floor((end-1)/4))
-    assert qsa.qsa_workspace_size(c, B.QSA_OP_SELECT, 2, 8192, 139264) == 4 * 2 * 8192 * 34816
+    # select, many rows: fp32 score rows of width ceil4(floor((end-1)/4)), then
+    # per-2048-block-segment histograms (128 words), filter counts and counters
+    rows, W = 2 * 8192, 34816
+    nseg = -(-34815 // 2048)
+    want = _al(4 * rows * W)
+    want = _al(want + 4 * rows * nseg * 128)
+    want = _al(want + 4 * rows)          # one filter segment per row
+    want = _al(want + 4 * rows)
+    assert qsa.qsa_workspace_size(c, B.QSA_OP_SELECT, 2, 8192, 139264) == want
+    # select, few long rows: candidate hand-over slots of 8192-score segments
+    rows, c_max = 8, (262211 - 1) // 4
+    W = -(-c_max // 4) * 4
+    nseg, nf = -(-c_max // 2048), -(-c_max // 8192)
+    want = _al(4 * rows * W)
+    want = _al(want + 4 * rows * nseg * 128)
+    want = _al(want + 8 * rows * nf * 1024)
+    want = _al(want + 4 * rows * nf)
+    want = _al(want + 4 * rows)
+    assert qsa.qsa_workspace_size(c, B.QSA_OP_SELECT, 8, 1, 262211) == want
     assert qsa.qsa_workspace_size(c, B.QSA_OP_INDEX_BUILD, 1, 1, 10) == 0
     assert qsa.qsa_workspace_size(c, B.QSA_OP_PREFILL, 1, 100, 100) == 0
-    # decode: 17 splits of 32 pseudo-blocks, each 16 heads x (128 + 2) floats
-    assert qsa.qsa_workspace_size(c, B.QSA_OP_DECODE, 8, 1, 300000) == 4 * 8 * 17 * (16 * 128 + 32)
+    # decode: 256 KiB of counters, then 17 splits of 32 pseudo-blocks, each
+    # 16 heads x (128 + 2) floats
+    assert (qsa.qsa_workspace_size(c, B.QSA_OP_DECODE, 8, 1, 300000)
+            == 4 * 65536 + 4 * 8 * 17 * (16 * 128 + 32))
     assert qsa.qsa_workspace_size(cfg(dtype=B.QSA_F32), B.QSA_OP_DECODE, 8, 1, 300000) == 0
 
 

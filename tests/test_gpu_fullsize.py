@@ -1,0 +1,175 @@
+"""GPU parity at the full workload sizes, on sampled rows.
+
+The HIP path runs in the same launch configuration the benchmark times; the
+oracle recomputes a seeded, stratified sample of rows one by one (every p mod
+4 residue, rows around the c = k_B boundary, needle rows, first/last rows).
+"""
+import math
+import sys
+import time
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import qsa_oracle as O
+from block_sparse_trainable_amd import synth
+from block_sparse_trainable_amd.runtime import DeviceLayer, to_f32
+from tests import _compare as C
+
+pytestmark = pytest.mark.gpu
+
+
+def say(msg):
+    print(f"[gpu-fullsize] {msg}", flush=True)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    torch.cuda.set_device(0)
+    yield
+    torch.cuda.empty_cache()
+
+
+def _prefill_and_check(x, rows_per_seq, check_recall=True):
+    say(f"{x.name}: upload + prefill")
+    dl = DeviceLayer(x)
+    if (x.cache_len > 0).any():
+        dl.build_prefix(x.cache_len)
+    outs = dl.prefill_chunk()
+    torch.cuda.synchronize()
+    sel, cnt, scs, out, lse = (outs[0].cpu().numpy(), outs[1].cpu().numpy(),
+                               outs[2].cpu().numpy(), to_f32(outs[3]), outs[4].cpu().numpy())
+    kmp = to_f32(dl.k_cmp)
+    del dl, outs
+    torch.cuda.empty_cache()
+    lay = x.layout
+    scale = 1.0 / math.sqrt(lay.head_dim)
+    stats, recall = [], []
+    for s in range(x.batch):
+        nb = (int(x.q_pos0[s]) + x.n_q) // 4
+        t0 = time.time()
+        kh = C.oracle_khat(x, s, nb)
+        # compression parity over every block of the sequence
+        diff = np.abs(kmp[s, :nb].astype(np.float64) - kh)
+        assert (diff <= np.abs(kh) * 2.0 ** -7 + 1e-30).all()
+        assert np.mean(diff > 0) < 1e-4
+        say(f"seq {s}: {nb} blocks compressed and checked in {time.time() - t0:.1f}s")
+        q_idx, q = C.f64(x.q_idx[s], "bf16"), C.f64(x.q[s], "bf16")
+        K, V = C.f64(x.k[s], "bf16"), C.f64(x.v[s], "bf16")
+        needle_rows = np.nonzero(x.target_block[s] >= 0)[0][:16] if x.target_block is not None else []
+        rows = C.stratified_rows(x.n_q, int(x.q_pos0[s]), extra=needle_rows, k=rows_per_seq,
+                                 seed=s)
+        for j in rows:
+            p = int(x.q_pos0[s]) + j
+            res = O.qsa_row(p, q_idx[j], q[j], kh, K, V, k_B=lay.k_blocks, attend=False)
+            stats.append(C.check_selection(res, sel[s, j], int(cnt[s, j]), scs[s, j],
+                                           lay.k_blocks))
+            C.check_attention(p, sel[s, j, :cnt[s, j]], q[j], K, V, out[s, j], lse[s, j],
+                              scale, "bf16")
+            tb = int(x.target_block[s, j]) if x.target_block is not None else -1
+            if tb >= 0 and check_recall:
+                recall.append(tb in set(sel[s, j, :cnt[s, j]].tolist()))
+    say(f"{len(stats)} rows: {np.mean([r.exact_eligible for r in stats]):.2f} margin-eligible, "
+        f"{np.mean([r.exact for r in stats]):.2f} identical to the oracle, "
+        f"needle recall {np.mean(recall) if recall else float('nan'):.3f}")
+    if recall:
+        assert np.mean(recall) >= 0.95
+    return stats
+
+
+def test_prefill_32k_full_size():
+    x = synth.prefill()
+    _prefill_and_check(x, rows_per_seq=96)
+
+
+def test_chunked_128k_full_size():
+    x = synth.chunked()
+    _prefill_and_check(x, rows_per_seq=48)
+
+
+def test_decode_256k_full_size_eager_and_graph():
+    steps = 64
+    x = synth.decode(steps=steps)
+    say("decode 8 x 256K: upload")
+    dl = DeviceLayer(x)
+    dl.build_prefix(x.cache_len)
+    plan = dl.decode_plan(steps)
+    outs = dl.alloc_decode_outputs()
+    check_steps = [0, 1, 2, 3, 21, 63]
+    got = {}
+    for t in range(steps):
+        dl.decode_step(plan, t, outs)
+        if t in check_steps:
+            torch.cuda.synchronize()
+            got[t] = [o.clone() for o in outs]
+    torch.cuda.synchronize()
+    say("decode eager done; graph capture + replays")
+    # graph replay of all steps, several times, with eager work in between
+    g = dl.capture_decode(plan, steps, outs)
+    for rep in range(3):
+        g.replay()
+        torch.cuda.synchronize()
+        for a, b in zip(got[63], outs):
+            assert torch.equal(a, b), f"graph replay {rep} differs from eager"
+        dl.decode_step(plan, 5, outs)   # eager work between replays
+        torch.cuda.synchronize()
+    del g
+    lay = x.layout
+    scale = 1.0 / math.sqrt(lay.head_dim)
+    recall = []
+    for s in range(x.batch):
+        p_last = int(x.q_pos0[s]) + steps
+        kh = C.oracle_khat(x, s, p_last // 4)
+        K, V = C.f64(x.k[s], "bf16"), C.f64(x.v[s], "bf16")
+        for t in check_steps:
+            sel, cnt, scs, out, lse = got[t]
+            p = int(x.q_pos0[s]) + t
+            q_idx, q = C.f64(x.q_idx[s, t], "bf16"), C.f64(x.q[s, t], "bf16")
+            res = O.qsa_row(p, q_idx, q, kh, K, V, k_B=lay.k_blocks, attend=False)
+            c_sel = sel[s, 0].cpu().numpy()
+            n = int(cnt[s, 0])
+            C.check_selection(res, c_sel, n, scs[s, 0].cpu().numpy(), lay.k_blocks)
+            C.check_attention(p, c_sel[:n], q, K, V, to_f32(out[s]), lse[s].cpu().numpy(),
+                              scale, "bf16")
+            recall.append(int(x.target_block[s, t]) in set(c_sel[:n].tolist()))
+        say(f"seq {s} checked")
+    assert np.mean(recall) == 1.0
+
+
+def test_stack_layer_1m_decode_and_companion():
+    say("1M-context layer: decode steps")
+    x = synth.stack_layer(0, steps=8)
+    dl = DeviceLayer(x)
+    dl.build_prefix(x.cache_len)
+    plan = dl.decode_plan(8)
+    outs = dl.alloc_decode_outputs()
+    got = {}
+    for t in range(8):
+        dl.decode_step(plan, t, outs)
+        if t in (0, 3, 7):
+            torch.cuda.synchronize()
+            got[t] = [o.clone() for o in outs]
+    kmp_rows = to_f32(dl.k_cmp[0, -(64 + 8):])  # the newest blocks only
+    del dl, outs
+    torch.cuda.empty_cache()
+    lay = x.layout
+    scale = 1.0 / math.sqrt(lay.head_dim)
+    kh = C.oracle_khat(x, 0, (int(x.q_pos0[0]) + 8) // 4)
+    K, V = C.f64(x.k[0], "bf16"), C.f64(x.v[0], "bf16")
+    for t, (sel, cnt, scs, out, lse) in got.items():
+        p = int(x.q_pos0[0]) + t
+        res = O.qsa_row(p, C.f64(x.q_idx[0, t], "bf16"), C.f64(x.q[0, t], "bf16"), kh, K, V,
+                        k_B=lay.k_blocks, attend=False)
+        c_sel = sel[0, 0].cpu().numpy()
+        n = int(cnt[0, 0])
+        C.check_selection(res, c_sel, n, scs[0, 0].cpu().numpy(), lay.k_blocks)
+        C.check_attention(p, c_sel[:n], C.f64(x.q[0, t], "bf16"), K, V, to_f32(out[0]),
+                          lse[0].cpu().numpy(), scale, "bf16")
+        assert int(x.target_block[0, t]) in set(c_sel[:n].tolist())
+    del x, K, V, kh
+    say("1M-context layer: companion prefill of the last 4096 queries")
+    y = synth.stack_layer(0, companion=4096)
+    _prefill_and_check(y, rows_per_seq=12)

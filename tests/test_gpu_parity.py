@@ -294,3 +294,42 @@ def test_decode_steps_match_oracle_and_prefill_rows():
         assert np.array_equal(sel.cpu().numpy()[:, 0], sel2[:, t])
         assert np.array_equal(scs.cpu().numpy()[:, 0], scs2[:, t])
         assert np.abs(to_f32(out) - out2[:, t]).max() <= 1e-2
+
+
+def test_decode_graph_replay_matches_eager():
+    say("decode graph replay == eager (small)")
+    x = synth.decode(context=6000, batch=3, steps=9, n_needles=8)
+    dl = DeviceLayer(x)
+    dl.build_prefix(x.cache_len)
+    plan = dl.decode_plan(9)
+    outs = dl.alloc_decode_outputs()
+    for t in range(9):
+        dl.decode_step(plan, t, outs)
+    torch.cuda.synchronize()
+    ref = [o.clone() for o in outs]
+    for overlap in (True, False):
+        g = dl.capture_decode(plan, 9, outs, overlap_build=overlap)
+        for rep in range(3):
+            for o in outs:
+                o.zero_()
+            g.replay()
+            torch.cuda.synchronize()
+            for a, b in zip(ref, outs):
+                assert torch.equal(a, b), f"replay {rep} (overlap={overlap}) differs"
+            dl.decode_step(plan, 2, outs)       # eager work between replays
+            torch.cuda.synchronize()
+
+
+def test_long_rows_split_filter_matches_oracle():
+    say("select with split filter segments (few long rows)")
+    # 3 queries per sequence at ~40K context: rows < 256 and c > 8192, so the
+    # row is split over filter workgroups and finished by the last one
+    x = synth.decode(context=40000, batch=2, steps=3, n_needles=16)
+    y = synth.LayerInputs(x.layout, x.k_idx, x.q_idx, x.q, x.k, x.v, q_pos0=x.q_pos0,
+                          cache_len=x.cache_len, gain=x.gain, target_block=x.target_block)
+    dl, outs = _run_prefill(y)
+    _check_rows(y, dl, outs, {0: [0, 1, 2], 1: [0, 1, 2]})
+    sel = outs[0].cpu().numpy()
+    for s in range(2):
+        for j in range(3):
+            assert int(x.target_block[s, j]) in set(sel[s, j].tolist())
