@@ -49,6 +49,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", choices=["chunked", "prefill"], default="chunked")
     ap.add_argument("--decode", choices=["decode", "none"], default="decode")
+    ap.add_argument("--only", choices=["prefill", "decode"], default=None,
+                    help="profile one leg only (the JSON line then carries that leg)")
     ap.add_argument("--decode-steps", type=int, default=64)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=768,
@@ -274,10 +276,15 @@ def main():
     qsa.load()
     torch.cuda.set_device(0)
 
+    if args.only == "decode":
+        dec = bench_decode(args, torch)
+        print(json.dumps({"metric": METRIC, "value": None, "unit": "tok/s", "n_gpus": 1,
+                          "decode": dec, "note": "decode leg only"}), flush=True)
+        return
     x, cfg, pre = bench_prefill(args, torch)
     log(f"prefill {pre['tok_s']:.0f} tok/s, {pre['ms_per_step']:.3f} ms/step, "
         f"stages {pre['stages_ms']}")
-    dec = bench_decode(args, torch) if args.decode != "none" else None
+    dec = bench_decode(args, torch) if (args.decode != "none" and args.only is None) else None
     if dec:
         log(f"decode {dec['us_per_step']:.1f} us/step")
 

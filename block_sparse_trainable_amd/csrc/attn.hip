@@ -25,9 +25,12 @@
 //     row (position p) and get weight 0.
 //   * O^T += V_tile^T * P^T: P^T is already in the B-operand layout (each
 //     lane's 8 probabilities fill its 8 k-slots, the k<->token map chosen to
-//     match), V is staged in a per-wave LDS tile (row stride Hkv*D*2 + 16
-//     bytes, conflict-free 4-byte reads) and read transposed, two dims per
-//     read feeding two MFMAs.
+//     match).  V rows go from HBM straight into a per-wave LDS tile
+//     (global_load_lds_dwordx4, 16-byte chunks XOR-swizzled so four token
+//     rows read together fall in distinct banks) and are read transposed,
+//     two dims per 4-byte read feeding two MFMAs.  No V staging registers.
+//   * Each query's selected-block list is loaded into LDS once, so the K/V
+//     addresses of a tile never wait on a dependent global load.
 //   * The 4 waves of a workgroup interleave tiles and merge their (m, l, O)
 //     states in LDS at the end.
 //   * Decode splits a query's token set over workgroups; each writes its
@@ -129,22 +132,36 @@ struct MfmaShape {
   static constexpr int G = HQ / HKV;        // query heads per KV head
   static constexpr int KD = HKV * D;        // concatenated KV row (elements)
   static constexpr int NK = KD / 32;        // k-steps of S, dim pairs-of-16 of PV
-  static constexpr int ROWB = KD * 2 + 16;  // LDS bytes per staged V row
+  static constexpr int ROWB = KD * 2;       // bytes per staged V row
+  static constexpr int CH = KD / 8;         // 16-byte chunks per V row
+  static constexpr int RPI = 64 / CH;       // V rows per wave-wide load
   static constexpr int TILE_LDS = 32 * ROWB;
   static constexpr int MERGE_FLOATS = 2 * HQ + HQ * D;  // per wave
+  static constexpr int LDS_BYTES = (4 * TILE_LDS > 4 * MERGE_FLOATS * 4) ? 4 * TILE_LDS
+                                                                          : 4 * MERGE_FLOATS * 4;
+  static_assert(CH == 16 || CH == 32, "the V swizzle needs 16 or 32 chunks per row");
 };
 
+constexpr int kMaxPB = 4 * 512 / 4 + 1;   // pseudo-blocks of one query (k_B + tail)
+constexpr int kMaxSplits = 17;            // decode splits: ceil((k_B + 1) / 32)
+
+// XOR swizzle of a V row's 16-byte chunks: rows 4 apart start their chunks
+// at different 64-byte offsets, so the transposed 4-byte reads of one wave
+// (four token rows at a time) hit distinct banks.
+__device__ __forceinline__ int vswz(int tk) { return 4 * ((tk >> 2) & 3); }
+
 template <int HKV, int D>
-__global__ __launch_bounds__(256) void attn_mfma_kernel(
+__global__ __launch_bounds__(256, 2) void attn_mfma_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kc,
     const uint16_t* __restrict__ vc, int64_t cap, int n_q, const int32_t* __restrict__ q_pos0,
     const int32_t* __restrict__ sel, const int32_t* __restrict__ cnt, int kB, float scale_log2,
     uint16_t* __restrict__ out, float* __restrict__ lse, float* __restrict__ part,
     uint32_t* __restrict__ counters, int n_split, int pb_per_split) {
   using S = MfmaShape<HKV, D>;
-  constexpr int KD = S::KD, NK = S::NK, ROWB = S::ROWB, G = S::G;
-  static_assert(4 * S::MERGE_FLOATS * 4 <= 4 * S::TILE_LDS, "merge area must fit");
-  __shared__ __attribute__((aligned(16))) unsigned char lds[4 * S::TILE_LDS];
+  constexpr int KD = S::KD, NK = S::NK, ROWB = S::ROWB, G = S::G, CH = S::CH, RPI = S::RPI;
+  static_assert(2 * kMaxSplits * 16 * 4 <= S::LDS_BYTES, "decode merge area must fit");
+  __shared__ __attribute__((aligned(16))) unsigned char lds[S::LDS_BYTES];
+  __shared__ int32_t sbid[kMaxPB];
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -161,17 +178,20 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(
   const int n_pb = count + 1;
   const int pb_lo = split * pb_per_split;
   const int pb_hi = min(pb_lo + pb_per_split, n_pb);
-  const int32_t* srow = sel + row * kB;
   const uint16_t* kbase = kc + (int64_t)s * cap * KD;
   const uint16_t* vbase = vc + (int64_t)s * cap * KD;
 
-  // block id of pseudo-block pb, -1 when outside this work item
-  auto bid = [&](int pb) -> int64_t {
-    if (pb < pb_lo || pb >= pb_hi) return -1;
-    if (pb == count) return c;
-    const int64_t b = srow[pb];
-    return min(max(b, (int64_t)0), c - 1);
-  };
+  // block ids of this work item's pseudo-blocks, relative to pb_lo
+  {
+    const int32_t* srow = sel + row * kB;
+    for (int i = pb_lo + (int)threadIdx.x; i < pb_hi; i += 256) {
+      int32_t b = (int32_t)c;
+      if (i < count) b = (int32_t)min(max((int64_t)srow[i], (int64_t)0), c - 1);
+      sbid[i - pb_lo] = b;
+    }
+  }
+  // block id of pseudo-block pb, -1 outside this work item
+  auto bid = [&](int pb) -> int64_t { return (pb < pb_hi) ? (int64_t)sbid[pb - pb_lo] : -1; };
 
   // block-diagonal query operand: head l16 is non-zero on its KV head's dims
   u32x4 qb[NK];
@@ -185,6 +205,7 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(
                            : u32x4{0, 0, 0, 0};
     }
   }
+  __syncthreads();
 
   float m_run = -INFINITY, l_run = 0.0f;
   f32x4 oacc[NK][2];
@@ -193,7 +214,20 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(
   unsigned char* vt = lds + wave * S::TILE_LDS;
 
   for (int pb0 = pb_lo + 8 * wave; pb0 < pb_hi; pb0 += 32) {
-    // ---- gather K (registers) and V (LDS) rows of the tile's 32 tokens
+    // ---- V rows of the tile's 32 tokens: straight from HBM into this wave's
+    // LDS tile (lane-ordered 1 KiB per instruction, chunk-swizzled)
+#pragma unroll
+    for (int u = 0; u < 32 / RPI; ++u) {
+      const int tk = RPI * u + lane / CH;
+      const int chunk = (lane % CH) ^ vswz(tk);
+      const int64_t b = bid(pb0 + (tk >> 2));
+      const int64_t tp = 4 * b + (tk & 3);
+      const int64_t rp = (b >= 0 && tp <= p) ? tp : p;
+      __builtin_amdgcn_global_load_lds(
+          (const __attribute__((address_space(1))) void*)(vbase + rp * KD + chunk * 8),
+          (__attribute__((address_space(3))) void*)(vt + u * 1024), 16, 0, 0);
+    }
+    // ---- K rows straight into A-operand registers
     u32x4 kreg[2][NK];
 #pragma unroll
     for (int st = 0; st < 2; ++st) {
@@ -204,20 +238,6 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(
       const uint16_t* kp = kbase + rp * KD + 8 * gq;
 #pragma unroll
       for (int kk = 0; kk < NK; ++kk) kreg[st][kk] = ld16(kp + 32 * kk);
-    }
-    {
-      constexpr int CH = KD / 8;          // 16-byte chunks per row
-      constexpr int RPI = 64 / CH;        // rows per load instruction
-#pragma unroll
-      for (int u = 0; u < 32 / RPI; ++u) {
-        const int tk = RPI * u + lane / CH;
-        const int col = lane % CH;
-        const int64_t b = bid(pb0 + (tk >> 2));
-        const int64_t tp = 4 * b + (tk & 3);
-        const int64_t rp = (b >= 0 && tp <= p) ? tp : p;
-        const u32x4 v = ld16(vbase + rp * KD + col * 8);
-        *reinterpret_cast<u32x4*>(vt + tk * ROWB + col * 16) = v;
-      }
     }
     // ---- S^T = K * Qbd: lane holds tokens 16st + 4gq + i for head l16
     f32x4 sacc[2];
@@ -268,6 +288,7 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(
       const int st = e >> 1, i0 = 2 * (e & 1);
       pv[e] = f32_to_bf16(pr[st][i0]) | (f32_to_bf16(pr[st][i0 + 1]) << 16);
     }
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's V tile has landed in LDS
     wave_sync();
     // ---- O^T += V^T * P^T; k-slot (gq, e) <-> token (e<4 ? 4gq+e : 16+4gq+e-4)
 #pragma unroll
@@ -276,7 +297,8 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const int tr = (e < 4) ? (4 * gq + e) : (16 + 4 * gq + e - 4);
-        w[e] = *reinterpret_cast<const uint32_t*>(vt + tr * ROWB + (32 * pp + 2 * l16) * 2);
+        const int chunk = (4 * pp + (l16 >> 2)) ^ vswz(tr);
+        w[e] = *reinterpret_cast<const uint32_t*>(vt + tr * ROWB + chunk * 16 + 4 * (l16 & 3));
       }
       u32x4 a0, a1;
 #pragma unroll
@@ -289,7 +311,7 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(
       oacc[pp][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a1), as_bf16x8(pv),
                                                             oacc[pp][1], 0, 0, 0);
     }
-    wave_sync();
+    wave_sync();  // all reads of this tile issued before the next tile's loads
   }
 
   // ---- merge the four waves' states
@@ -357,29 +379,54 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(
   __threadfence();
   if (threadIdx.x == 0) counters[row] = 0u;  // leave the counter zeroed
   const float* base = part + row * n_split * (16 * D + 32);
-  for (int idx = threadIdx.x; idx < 16 * D; idx += 256) {
-    const int n = idx / D, dd = idx % D;
+  float* wk = mg;                   // [kMaxSplits][16] split weights
+  float* ms = mg + kMaxSplits * 16; // [kMaxSplits][16] split maxima, then [16] lse
+  for (int i = threadIdx.x; i < n_split * 16; i += 256) {
+    const int k = i / 16, n = i % 16;
+    ms[i] = base[k * (16 * D + 32) + n];
+    wk[i] = base[k * (16 * D + 32) + 16 + n];
+  }
+  __syncthreads();
+  if (threadIdx.x < 16) {
+    const int n = threadIdx.x;
     float mx = -INFINITY;
-    for (int k = 0; k < n_split; ++k) mx = fmaxf(mx, base[k * (16 * D + 32) + n]);
-    float z = 0.0f, o = 0.0f;
+    for (int k = 0; k < n_split; ++k) mx = fmaxf(mx, ms[k * 16 + n]);
+    float z = 0.0f;
     for (int k = 0; k < n_split; ++k) {
-      const float* pk = base + k * (16 * D + 32);
-      const float m = pk[n];
-      if (m == -INFINITY) continue;
-      const float f = exp2f(m - mx);
-      z += f * pk[16 + n];
-      o += f * pk[32 + n * D + dd];
+      const float m = ms[k * 16 + n];
+      const float f = m == -INFINITY ? 0.0f : exp2f(m - mx);
+      ms[k * 16 + n] = f;
+      z += f * wk[k * 16 + n];
     }
-    out[(row * 16 + n) * D + dd] = (uint16_t)f32_to_bf16(o / z);
-    if (lse && dd == 0) lse[row * 16 + n] = (mx + log2f(z)) * kLn2;
+    for (int k = 0; k < n_split; ++k) wk[k * 16 + n] = ms[k * 16 + n] / z;
+    if (lse) lse[row * 16 + n] = (mx + log2f(z)) * kLn2;
+  }
+  __syncthreads();
+  // each thread: 8 consecutive dims of one head, splits loaded independently
+  for (int gi = threadIdx.x; gi < 16 * (D / 8); gi += 256) {
+    const int n = gi / (D / 8), d0 = (gi % (D / 8)) * 8;
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
+    for (int k = 0; k < n_split; ++k) {
+      const float f = wk[k * 16 + n];
+      const float4* src = reinterpret_cast<const float4*>(base + k * (16 * D + 32) + 32 + n * D + d0);
+      const float4 a = src[0], b = src[1];
+      acc[0] += f * a.x; acc[1] += f * a.y; acc[2] += f * a.z; acc[3] += f * a.w;
+      acc[4] += f * b.x; acc[5] += f * b.y; acc[6] += f * b.z; acc[7] += f * b.w;
+    }
+    u32x4 pk;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) pk[e] = f32_to_bf16(acc[2 * e]) | (f32_to_bf16(acc[2 * e + 1]) << 16);
+    *reinterpret_cast<u32x4*>(out + (row * 16 + n) * D + d0) = pk;
   }
 }
 
 constexpr int kDecodeSplitPB = 32;  // pseudo-blocks per decode work item
 
 bool use_mfma(const Dims& d) {
-  return d.bf16 && d.q_heads == 16 && (d.kv_heads == 1 || d.kv_heads == 2) &&
-         (d.head_dim == 64 || d.head_dim == 128);
+  return d.bf16 && d.q_heads == 16 &&
+         ((d.kv_heads == 2 && (d.head_dim == 64 || d.head_dim == 128)) ||
+          (d.kv_heads == 1 && d.head_dim == 128));
 }
 
 int decode_splits(const Dims& d) { return (d.kB + 1 + kDecodeSplitPB - 1) / kDecodeSplitPB; }
@@ -424,7 +471,6 @@ hipError_t launch_attn(const Dims& d, int batch, int n_q, const void* q, const v
     QSA_MFMA(2, 128)
     QSA_MFMA(1, 128)
     QSA_MFMA(2, 64)
-    QSA_MFMA(1, 64)
 #undef QSA_MFMA
   }
   if (d.bf16)
