@@ -34,8 +34,9 @@
 //   * The 4 waves of a workgroup interleave tiles and merge their (m, l, O)
 //     states in LDS at the end.
 //   * Decode splits a query's token set over workgroups; each writes its
-//     merged (m, l, O) state and the last one to finish (device-scope
-//     counter per row, left at zero) merges all splits.
+//     merged (m, l, O) state and a small second kernel merges the splits
+//     (log-sum-exp) -- a kernel boundary is a far cheaper hand-off here than
+//     coherent cross-workgroup stores of 8 KiB states.
 #include <math.h>
 
 #include "qsa_common.h"
@@ -156,7 +157,7 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(
     const uint16_t* __restrict__ vc, int64_t cap, int n_q, const int32_t* __restrict__ q_pos0,
     const int32_t* __restrict__ sel, const int32_t* __restrict__ cnt, int kB, float scale_log2,
     uint16_t* __restrict__ out, float* __restrict__ lse, float* __restrict__ part,
-    uint32_t* __restrict__ counters, int n_split, int pb_per_split) {
+    int n_split, int pb_per_split) {
   using S = MfmaShape<HKV, D>;
   constexpr int KD = S::KD, NK = S::NK, ROWB = S::ROWB, G = S::G, CH = S::CH, RPI = S::RPI;
   static_assert(2 * kMaxSplits * 16 * 4 <= S::LDS_BYTES, "decode merge area must fit");
@@ -367,58 +368,44 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(
       }
     }
   }
-  if (n_split == 1) return;
+}
 
-  // ---- decode: the last split of the row merges every split's state
-  __threadfence();
-  __syncthreads();
-  __shared__ uint32_t last;
-  if (threadIdx.x == 0) last = (atomicAdd(&counters[row], 1u) == (uint32_t)n_split - 1u) ? 1u : 0u;
-  __syncthreads();
-  if (!last) return;
-  __threadfence();
-  if (threadIdx.x == 0) counters[row] = 0u;  // leave the counter zeroed
+// Decode: log-sum-exp merge of a row's split states.  One workgroup per
+// (row, head); thread d owns output dim d.  The splits' states were written
+// by the previous kernel, so plain loads see them.
+template <int D>
+__global__ __launch_bounds__(D) void attn_merge_kernel(const float* __restrict__ part,
+                                                       int n_split, uint16_t* __restrict__ out,
+                                                       float* __restrict__ lse) {
+  const int64_t row = blockIdx.x / 16;
+  const int n = (int)(blockIdx.x % 16);
+  const int dd = threadIdx.x;
   const float* base = part + row * n_split * (16 * D + 32);
-  float* wk = mg;                   // [kMaxSplits][16] split weights
-  float* ms = mg + kMaxSplits * 16; // [kMaxSplits][16] split maxima, then [16] lse
-  for (int i = threadIdx.x; i < n_split * 16; i += 256) {
-    const int k = i / 16, n = i % 16;
-    ms[i] = base[k * (16 * D + 32) + n];
-    wk[i] = base[k * (16 * D + 32) + 16 + n];
-  }
-  __syncthreads();
-  if (threadIdx.x < 16) {
-    const int n = threadIdx.x;
-    float mx = -INFINITY;
-    for (int k = 0; k < n_split; ++k) mx = fmaxf(mx, ms[k * 16 + n]);
-    float z = 0.0f;
-    for (int k = 0; k < n_split; ++k) {
-      const float m = ms[k * 16 + n];
-      const float f = m == -INFINITY ? 0.0f : exp2f(m - mx);
-      ms[k * 16 + n] = f;
-      z += f * wk[k * 16 + n];
-    }
-    for (int k = 0; k < n_split; ++k) wk[k * 16 + n] = ms[k * 16 + n] / z;
-    if (lse) lse[row * 16 + n] = (mx + log2f(z)) * kLn2;
-  }
-  __syncthreads();
-  // each thread: 8 consecutive dims of one head, splits loaded independently
-  for (int gi = threadIdx.x; gi < 16 * (D / 8); gi += 256) {
-    const int n = gi / (D / 8), d0 = (gi % (D / 8)) * 8;
-    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-#pragma unroll 4
-    for (int k = 0; k < n_split; ++k) {
-      const float f = wk[k * 16 + n];
-      const float4* src = reinterpret_cast<const float4*>(base + k * (16 * D + 32) + 32 + n * D + d0);
-      const float4 a = src[0], b = src[1];
-      acc[0] += f * a.x; acc[1] += f * a.y; acc[2] += f * a.z; acc[3] += f * a.w;
-      acc[4] += f * b.x; acc[5] += f * b.y; acc[6] += f * b.z; acc[7] += f * b.w;
-    }
-    u32x4 pk;
+  float m[kMaxSplits], z[kMaxSplits], o[kMaxSplits];
+  float mx = -INFINITY;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) pk[e] = f32_to_bf16(acc[2 * e]) | (f32_to_bf16(acc[2 * e + 1]) << 16);
-    *reinterpret_cast<u32x4*>(out + (row * 16 + n) * D + d0) = pk;
+  for (int k = 0; k < kMaxSplits; ++k) {  // every split's loads in flight at once
+    if (k < n_split) {
+      const float* pk = base + k * (16 * D + 32);
+      m[k] = pk[n];
+      z[k] = pk[16 + n];
+      o[k] = pk[32 + n * D + dd];
+    }
   }
+#pragma unroll
+  for (int k = 0; k < kMaxSplits; ++k)
+    if (k < n_split) mx = fmaxf(mx, m[k]);
+  float zs = 0.0f, acc = 0.0f;
+#pragma unroll
+  for (int k = 0; k < kMaxSplits; ++k) {
+    if (k < n_split && m[k] != -INFINITY) {
+      const float f = exp2f(m[k] - mx);
+      zs += f * z[k];
+      acc += f * o[k];
+    }
+  }
+  out[(row * 16 + n) * D + dd] = (uint16_t)f32_to_bf16(acc / zs);
+  if (lse && dd == 0) lse[row * 16 + n] = (mx + log2f(zs)) * kLn2;
 }
 
 constexpr int kDecodeSplitPB = 32;  // pseudo-blocks per decode work item
@@ -438,15 +425,16 @@ hipError_t launch_mfma(const Dims& d, int rows, int n_q, const void* q, const vo
                        hipStream_t st) {
   const float sl2 = d.scale * kLog2e;
   const int ns = decode ? decode_splits(d) : 1;
-  uint32_t* counters = decode ? static_cast<uint32_t*>(ws) : nullptr;
-  float* part = decode ? reinterpret_cast<float*>(static_cast<char*>(ws) +
-                                                  sizeof(uint32_t) * kAttnCounterRows)
-                       : nullptr;
+  float* part = decode ? static_cast<float*>(ws) : nullptr;
   hipLaunchKernelGGL((attn_mfma_kernel<HKV, D>), dim3((unsigned)(rows * ns)), dim3(256), 0, st,
                      static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(kc),
                      static_cast<const uint16_t*>(vc), cap, n_q, q_pos0, sel, cnt, d.kB, sl2,
-                     static_cast<uint16_t*>(out), lse, part, counters, ns,
+                     static_cast<uint16_t*>(out), lse, part, ns,
                      decode ? kDecodeSplitPB : d.kB + 1);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || !decode) return e;
+  hipLaunchKernelGGL((attn_merge_kernel<D>), dim3((unsigned)(rows * 16)), dim3(D), 0, st, part,
+                     ns, static_cast<uint16_t*>(out), lse);
   return hipGetLastError();
 }
 
@@ -454,8 +442,7 @@ hipError_t launch_mfma(const Dims& d, int rows, int n_q, const void* q, const vo
 
 size_t attn_workspace_bytes(const Dims& d, int rows, bool decode) {
   if (!decode || !use_mfma(d)) return 0;
-  return sizeof(uint32_t) * kAttnCounterRows +
-         sizeof(float) * (size_t)rows * decode_splits(d) * (16 * d.head_dim + 32);
+  return sizeof(float) * (size_t)rows * decode_splits(d) * (16 * d.head_dim + 32);
 }
 
 hipError_t launch_attn(const Dims& d, int batch, int n_q, const void* q, const void* k_cache,

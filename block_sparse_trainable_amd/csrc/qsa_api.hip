@@ -226,9 +226,6 @@ static qsa_status attn_common(const char* fn, const qsa_config* cfg, int32_t bat
   QSA_REQUIRE_PTR(out, 4);
   if (lse && !aligned(lse, 4))
     return fail(QSA_ERR_INVALID_ARGUMENT, "%s: lse must be 4-byte aligned", fn);
-  if (decode && batch > qsa::kAttnCounterRows)
-    return fail(QSA_ERR_UNSUPPORTED, "%s: batch %d (at most %lld)", fn, batch,
-                (long long)qsa::kAttnCounterRows);
   const size_t need = qsa::attn_workspace_bytes(d, batch * n_q, decode);
   if (need > 0) {
     if (!workspace || workspace_bytes < need)

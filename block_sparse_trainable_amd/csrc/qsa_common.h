@@ -58,6 +58,31 @@ __device__ __forceinline__ u32x4 ld16(const void* p) {
 
 __device__ __forceinline__ float relu(float x) { return x > 0.0f ? x : 0.0f; }
 
+// Cross-workgroup hand-off without cache maintenance.  A device-scope fence
+// on this multi-XCD part writes back and invalidates the whole L2 of the
+// issuing XCD; instead, data handed from one workgroup to another within a
+// kernel is written and read with agent-scope relaxed atomics (coherent
+// accesses that bypass the XCD-private L2 state), and ordered by waiting for
+// the stores to complete before the completion counter is bumped.
+template <class T>
+__device__ __forceinline__ void coherent_store(T* p, T v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+template <class T>
+__device__ __forceinline__ T coherent_load(const T* p) {
+  return __hip_atomic_load(const_cast<T*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// Every store this workgroup made has completed (called by all threads,
+// followed by a barrier, before one thread bumps the counter).
+__device__ __forceinline__ void stores_complete() {
+  __builtin_amdgcn_s_waitcnt(0);
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+}
+// Counter bump; returns true in the workgroup that arrives last.
+__device__ __forceinline__ bool arrive_last(uint32_t* counter, uint32_t n) {
+  return __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == n - 1u;
+}
+
 // ------------------------------------------------- score histogram bins ----
 // Scores are >= +0.0.  bin() maps a score's IEEE bits to one of 256 bins, 8
 // per octave over [2^-16, 2^16) (exponent and top 3 mantissa bits), scores
@@ -67,6 +92,7 @@ constexpr int kHistBins = 256;
 constexpr int kHistWords = kHistBins / 2;  // two u16 counts per u32 word
 
 __device__ __forceinline__ uint32_t score_bin(uint32_t bits) {
+  if (bits & 0x80000000u) return 0u;      // never produced; treated as 0
   const int k = (int)(bits >> 20) - 888;  // 888 = 111 * 8: exponent of 2^-16
   return (uint32_t)min(max(k, 0), kHistBins - 1);
 }
@@ -95,19 +121,18 @@ inline int64_t score_row_width(int r, int32_t max_pos_end) {
 // Layout of the select workspace, derived from the call's sizes only.
 //   scores  [rows][W] f32          block-importance rows
 //   hist    [rows][n_sseg][128] u32 per-score-segment histograms (u16 pairs)
-//   slots   [rows][n_fseg][kSlotCap] u32x2 candidates of each filter segment
-//   slotcnt [rows][n_fseg] u32
-//   done    [rows] u32             filter-segment completion counters
+//   cand    [rows][kCandCap] u32x2 candidates of rows split over workgroups
+//   done    [rows] u32             completion counters of split rows
 struct SelectPlan {
   int kernel;        // 0 = VALU, 1 = MFMA prefill, 2 = MFMA decode
   int64_t W;         // score row width
   int64_t sseg;      // blocks per score segment
   int64_t n_sseg;
-  int64_t fseg;      // scores per filter segment
-  int64_t n_fseg;
+  int64_t fseg;      // score segments per filter workgroup
+  int64_t n_fseg;    // filter workgroups per row
   size_t off_hist, off_slots, off_slotcnt, off_done, bytes;
 };
-constexpr int kSlotCap = 1024;      // candidates one filter segment may hand over
+constexpr int kCandCap = 4096;      // candidates a row may have (else fallback)
 SelectPlan select_plan(const struct Dims& d, int batch, int n_q, int32_t max_pos_end);
 
 // ------------------------------------------------------------ launchers ----
@@ -125,10 +150,7 @@ hipError_t launch_select(const Dims& d, const SelectPlan& pl, int batch, int n_q
                          const int32_t* q_pos0, int64_t cap, void* workspace, int32_t* sel,
                          int32_t* cnt, float* sel_scores, hipStream_t st);
 
-// Decode attention workspace: [kAttnCounterRows] u32 completion counters
-// (must be zero before the first call; every call leaves them zero), then
-// the per-split partial states.
-constexpr int64_t kAttnCounterRows = 65536;
+// Decode attention workspace: the per-split partial states.
 size_t attn_workspace_bytes(const Dims& d, int rows, bool decode);
 
 hipError_t launch_attn(const Dims& d, int batch, int n_q, const void* q, const void* k_cache,

@@ -49,7 +49,7 @@ __global__ __launch_bounds__(256) void score_valu_kernel(
   const int j = (int)(row % n_q);
   const int64_t p = (int64_t)q_pos0[s] + j;
   const int64_t c = min(min(p / 4, cap_blocks), o.W);
-  if (blockIdx.y == 0 && threadIdx.x == 0) o.done[row] = 0u;
+  if (blockIdx.y == 0 && threadIdx.x == 0) coherent_store(&o.done[row], 0u);
   for (int i = threadIdx.x; i < kHistWords; i += blockDim.x) hist[i] = 0u;
   for (int i = threadIdx.x; i < H * D; i += blockDim.x) {
     const int64_t off = row * H * D + i;
@@ -108,7 +108,7 @@ __global__ __launch_bounds__(256) void score_mfma_prefill_kernel(
   const int j_last = min(j0 + kPQ, n_q) - 1;
   const int64_t pos0 = q_pos0[s];
   if (blockIdx.y == 0 && threadIdx.x < kPQ && j0 + (int)threadIdx.x < n_q)
-    o.done[(int64_t)s * n_q + j0 + threadIdx.x] = 0u;
+    coherent_store(&o.done[(int64_t)s * n_q + j0 + threadIdx.x], 0u);
   const int64_t c_tile = min(min((pos0 + j_last) / 4, cap_blocks), W);
   const int64_t b_lo = (int64_t)blockIdx.y * seg_blocks;
   const int64_t b_hi = min(b_lo + seg_blocks, c_tile);
@@ -208,12 +208,14 @@ __global__ __launch_bounds__(256) void score_mfma_prefill_kernel(
 }
 
 // ------------------------------------------------------- MFMA, decode ------
-// Few queries, long rows: workgroup = (segment of blocks, 4 queries).  The
-// four waves take disjoint 64-block chunks of the segment and read their B
-// tiles straight from HBM (no reuse to stage); rows are 4 queries x 4 heads.
-constexpr int kDecSeg = 2048;
+// Few queries, long rows: workgroup = (segment of 1024 blocks, 4 queries).
+// Each of the eight waves takes 128 blocks of the segment and issues all of
+// their B-tile loads (32 KiB) straight from HBM before the MFMAs (no reuse to
+// stage through LDS); rows are 4 queries x 4 heads.
+constexpr int kDecSeg = 1024;
+constexpr int kDecWaves = 8;
 
-__global__ __launch_bounds__(256) void score_mfma_decode_kernel(
+__global__ __launch_bounds__(512) void score_mfma_decode_kernel(
     const uint16_t* __restrict__ q_idx, const int32_t* __restrict__ q_pos0, int n_q,
     const uint16_t* __restrict__ k_cmp, int64_t cap_blocks, ScoreOut o) {
   __shared__ uint32_t hist[4][kHistWords];
@@ -228,12 +230,12 @@ __global__ __launch_bounds__(256) void score_mfma_decode_kernel(
   const int64_t pos0 = q_pos0[s];
   const int j_last = min(j0 + 4, n_q) - 1;
   if (blockIdx.x == 0 && threadIdx.x < 4 && j0 + (int)threadIdx.x < n_q)
-    o.done[(int64_t)s * n_q + j0 + threadIdx.x] = 0u;
+    coherent_store(&o.done[(int64_t)s * n_q + j0 + threadIdx.x], 0u);
   const int64_t c_tile = min(min((pos0 + j_last) / 4, cap_blocks), W);
   const int64_t seg_lo = (int64_t)blockIdx.x * kDecSeg;
   const int64_t seg_hi = min(seg_lo + kDecSeg, c_tile);
   if (seg_lo >= seg_hi) return;  // no query of the tile reaches this segment
-  for (int i = threadIdx.x; i < 4 * kHistWords; i += 256) (&hist[0][0])[i] = 0u;
+  for (int i = threadIdx.x; i < 4 * kHistWords; i += 64 * kDecWaves) (&hist[0][0])[i] = 0u;
   __syncthreads();
 
   u32x4 qa[4];
@@ -249,10 +251,10 @@ __global__ __launch_bounds__(256) void score_mfma_decode_kernel(
   float* dst = scores + ((int64_t)s * n_q + (jq_o < n_q ? jq_o : 0)) * W;
   const uint16_t* kbase = k_cmp + (int64_t)s * cap_blocks * 128 + 8 * gq;
 
-  for (int64_t cb = seg_lo + 64 * wave; cb < seg_hi; cb += 256) {
-    u32x4 kb[4][4];
+  for (int64_t cb = seg_lo + 128 * wave; cb < seg_hi; cb += 128 * kDecWaves) {
+    u32x4 kb[8][4];
 #pragma unroll
-    for (int ct = 0; ct < 4; ++ct) {
+    for (int ct = 0; ct < 8; ++ct) {
       const int64_t b = cb + 16 * ct + l16;
       const bool ok = b < seg_hi;
 #pragma unroll
@@ -260,7 +262,7 @@ __global__ __launch_bounds__(256) void score_mfma_decode_kernel(
         kb[ct][kk] = ok ? ld16(kbase + b * 128 + 32 * kk) : u32x4{0, 0, 0, 0};
     }
 #pragma unroll
-    for (int ct = 0; ct < 4; ++ct) {
+    for (int ct = 0; ct < 8; ++ct) {
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk)
@@ -275,7 +277,7 @@ __global__ __launch_bounds__(256) void score_mfma_decode_kernel(
     }
   }
   __syncthreads();
-  for (int i = threadIdx.x; i < 4 * kHistWords; i += 256) {
+  for (int i = threadIdx.x; i < 4 * kHistWords; i += 64 * kDecWaves) {
     const int ql = i / kHistWords, w = i % kHistWords;
     if (j0 + ql < n_q)
       o.hist[hist_offset((int64_t)s * n_q + j0 + ql, blockIdx.x, o.n_sseg) + w] = hist[ql][w];
@@ -299,7 +301,7 @@ hipError_t launch_score(const Dims& d, const SelectPlan& pl, int batch, int n_q,
                        static_cast<const uint16_t*>(k_cmp), cap_blocks, (int)pl.sseg, o);
   } else if (pl.kernel == 2) {
     dim3 grid(segs, (unsigned)((n_q + 3) / 4), (unsigned)batch);
-    hipLaunchKernelGGL(score_mfma_decode_kernel, grid, dim3(256), 0, st,
+    hipLaunchKernelGGL(score_mfma_decode_kernel, grid, dim3(64 * kDecWaves), 0, st,
                        static_cast<const uint16_t*>(q_idx), q_pos0, n_q,
                        static_cast<const uint16_t*>(k_cmp), cap_blocks, o);
   } else {

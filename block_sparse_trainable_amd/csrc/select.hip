@@ -12,18 +12,20 @@
 //   1. sum the row's segment histograms; the threshold bin d* is the highest
 //      bin whose suffix count reaches k_B.  Every key in a bin above d* is
 //      kept (A of them, A < k_B); need = k_B - A keys of bin d* are kept.
-//   2. one sweep over the row in index order keeps the candidates (bin >= d*,
-//      typically k_B plus a few hundred) in LDS, still in index order (a
-//      workgroup scan gives each its slot).
+//   2. the same histograms give every segment's exact number of candidates
+//      (keys with bin >= d*, typically k_B plus a few hundred per row), hence
+//      its exact output offset; each wave then sweeps whole segments with all
+//      loads in flight and a ballot compaction, so the candidates land in
+//      index order without any workgroup-wide barrier.
 //   3. an MSB-first radix select (11/11/9-bit digits) over the bin-d*
 //      candidates only finds the need-th largest key; a final ordered pass
 //      writes the kept ids, ascending, ties to the lower index.
-// Long rows (decode) are split into filter segments handled by separate
-// workgroups; each hands its candidates over in a global slot and the last
-// one to finish (device-scope counter, zeroed by the scoring kernel of the
-// same call) gathers the slots in segment order and finishes the row.  If the
-// candidates ever exceed the LDS capacity, the row falls back to an exact
-// radix select over the whole row in global memory.
+// Long rows (decode) are split over several filter workgroups, which write
+// their candidates at their exact offsets into a row-wide array; the last one
+// to finish (device-scope counter, zeroed by the scoring kernel of the same
+// call) loads them and finishes the row.  If a row ever has more candidates
+// than the LDS capacity, it falls back to an exact radix select over the
+// whole row in global memory.
 #include "qsa_common.h"
 
 namespace qsa {
@@ -32,7 +34,6 @@ namespace {
 constexpr int kThreads = 512;
 constexpr int kWaves = kThreads / 64;
 constexpr int kRadixBins = 2048;
-constexpr int kCandCap = 4096;       // candidates finished in LDS
 constexpr int64_t kFilterSeg = 8192; // scores per filter segment of a long row
 constexpr uint32_t kOverflow = 0xFFFFFFFFu;
 
@@ -174,11 +175,11 @@ struct FilterArgs {
   const float* scores;
   int64_t W;
   const uint32_t* hist;     // per-score-segment histograms
-  int64_t sseg, n_sseg;
-  uint2* slots;             // [rows][n_fseg][kSlotCap]  (n_fseg > 1 only)
-  uint32_t* slotcnt;        // [rows][n_fseg]
-  uint32_t* done;           // [rows]
-  int64_t fseg, n_fseg;
+  int64_t sseg, n_sseg;     // blocks per score segment, segments per row (max)
+  uint2* cand;              // [rows][kCandCap] candidates of split rows
+  uint32_t* done;           // [rows] completion counters of split rows
+  int64_t spw;              // score segments per filter workgroup
+  int64_t n_fseg;           // filter workgroups per row
   int n_q;
   const int32_t* q_pos0;
   int64_t cap_blocks;
@@ -188,13 +189,18 @@ struct FilterArgs {
   float* sel_scores;
 };
 
+constexpr int kMaxSeg = 2048;  // score segments per row the offsets table holds
+
 __global__ __launch_bounds__(kThreads) void filter_select_kernel(FilterArgs a) {
   __shared__ uint32_t ckey[kCandCap];
   __shared__ uint32_t cidx[kCandCap];
   __shared__ uint32_t hist[kRadixBins];
+  __shared__ uint32_t segoff[kMaxSeg];
   __shared__ uint32_t scratch[64];
 
   const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
   const int64_t row = blockIdx.x;
   const int64_t fs = blockIdx.y;
   const int s = (int)(row / a.n_q);
@@ -215,17 +221,32 @@ __global__ __launch_bounds__(kThreads) void filter_select_kernel(FilterArgs a) {
     if (tid == 0) a.cnt[row] = (int32_t)c;
     return;
   }
+  const int64_t nseg = (c + a.sseg - 1) / a.sseg;
+  const uint32_t* hrow = a.hist + hist_offset(row, 0, a.n_sseg);
 
-  // ---- 1. row histogram and threshold bin --------------------------------
+  // ---- 1. row histogram and threshold bin ---------------------------------
   {
-    const int64_t nseg = (c + a.sseg - 1) / a.sseg;
-    uint32_t lo = 0, hi = 0;
-    if (tid < kHistWords) {
-      const int w = kHistWords - 1 - tid;  // thread 0 owns the top bins
-      for (int64_t g = 0; g < nseg; ++g) {
-        const uint32_t v = a.hist[hist_offset(row, g, a.n_sseg) + w];
+    // 512 threads: word w = 127 - (tid & 127) of every 4th segment
+    uint32_t* part = hist;  // [4][128][2] partial sums (lo, hi)
+    {
+      const int w = kHistWords - 1 - (tid & 127);
+      uint32_t lo = 0, hi = 0;
+#pragma unroll 8
+      for (int64_t g = tid >> 7; g < nseg; g += 4) {
+        const uint32_t v = hrow[g * kHistWords + w];
         lo += v & 0xFFFFu;
         hi += v >> 16;
+      }
+      part[(tid >> 7) * 256 + 2 * (tid & 127)] = lo;
+      part[(tid >> 7) * 256 + 2 * (tid & 127) + 1] = hi;
+    }
+    __syncthreads();
+    uint32_t lo = 0, hi = 0;
+    if (tid < kHistWords) {
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        lo += part[q4 * 256 + 2 * tid];
+        hi += part[q4 * 256 + 2 * tid + 1];
       }
     }
     uint32_t tot;
@@ -248,87 +269,128 @@ __global__ __launch_bounds__(kThreads) void filter_select_kernel(FilterArgs a) {
   const uint32_t n_sure = scratch[kWaves + 1];
   const uint32_t n_maybe = scratch[kWaves + 2];
   const uint32_t need = (uint32_t)kB - n_sure;
+  const uint32_t total = n_sure + n_maybe;
   __syncthreads();
 
-  // ---- 2. ordered sweep of this filter segment --------------------------
-  const int64_t lo_i = fs * a.fseg;
-  const int64_t hi_i = min(lo_i + a.fseg, c);
-  const uint32_t cap = a.n_fseg == 1 ? (uint32_t)kCandCap : (uint32_t)kSlotCap;
-  uint32_t ncand = 0;
-  bool overflow = false;
-  for (int64_t base = lo_i; base < hi_i; base += 4 * kThreads) {
-    const int64_t i0 = base + 4 * tid;   // lo_i, base multiples of 4: aligned loads
-    uint32_t k[4] = {0, 0, 0, 0};
-    uint32_t m = 0;
-    if (i0 < hi_i) {
-      const u32x4 v = *reinterpret_cast<const u32x4*>(bits + i0);
+  // ---- 2. exact candidate offset of every score segment -------------------
+  // candidates of segment g = its keys with bin >= d*, read off its histogram
+  const bool fits = total <= (uint32_t)kCandCap && nseg <= kMaxSeg;
+  if (fits) {
+    const int w0 = (int)(dstar >> 1);
+    const int nw = kHistWords - w0;  // words holding bins >= d*
+    for (int64_t g = tid; g < nseg; g += kThreads) segoff[g] = 0u;
+    __syncthreads();
+    const int64_t pairs = nseg * nw;
+#pragma unroll 4
+    for (int64_t i = tid; i < pairs; i += kThreads) {
+      const int64_t g = i / nw;
+      const int w = w0 + (int)(i % nw);
+      const uint32_t v = hrow[g * kHistWords + w];
+      const uint32_t n = (v >> 16) + ((w == w0 && (dstar & 1u)) ? 0u : (v & 0xFFFFu));
+      if (n) atomicAdd(&segoff[g], n);
+    }
+    __syncthreads();
+    // exclusive scan of segoff[0..nseg): thread t owns entries 4t..4t+3
+    uint32_t v[4], sum = 0;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        k[e] = key_of(v[e]);
-        if (i0 + e < hi_i && score_bin(k[e]) >= dstar) m |= 1u << e;
-      }
+    for (int e = 0; e < 4; ++e) {
+      const int64_t g = 4 * tid + e;
+      v[e] = g < nseg ? segoff[g] : 0u;
+      sum += v[e];
     }
     uint32_t tot;
-    const uint32_t ex = block_excl_scan((uint32_t)__popc(m), scratch, &tot);
-    if (ncand + tot > cap) overflow = true;
-    if (!overflow) {
-      uint32_t pos = ncand + ex;
+    uint32_t run = block_excl_scan(sum, scratch, &tot);
 #pragma unroll
-      for (int e = 0; e < 4; ++e)
-        if (m & (1u << e)) {
-          ckey[pos] = k[e];
-          cidx[pos] = (uint32_t)(i0 + e);
-          ++pos;
-        }
+    for (int e = 0; e < 4; ++e) {
+      const int64_t g = 4 * tid + e;
+      if (g < nseg) segoff[g] = run;
+      run += v[e];
     }
-    ncand += tot;
+    __syncthreads();
+  }
+
+  // ---- 3. sweep this workgroup's segments; waves take whole segments ------
+  const bool split = a.n_fseg > 1;
+  uint2* gcand = split ? a.cand + row * kCandCap : nullptr;
+  if (fits) {
+    const int64_t g_lo = fs * a.spw;
+    const int64_t g_hi = min(g_lo + a.spw, nseg);
+    const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    for (int64_t g = g_lo + wave; g < g_hi; g += kWaves) {
+      const int64_t i_lo = g * a.sseg;
+      const int64_t i_hi = min(i_lo + a.sseg, c);
+      uint32_t pos = segoff[g];
+      for (int64_t base = i_lo; base < i_hi; base += 256 * 8) {
+        u32x4 v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {   // all of this stretch's loads in flight
+          const int64_t i0 = base + 256 * u + 4 * lane;
+          v[u] = i0 < i_hi ? *reinterpret_cast<const u32x4*>(bits + i0) : u32x4{0, 0, 0, 0};
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const int64_t i0 = base + 256 * u + 4 * lane;
+          uint32_t m = 0;
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (i0 + e < i_hi && score_bin(key_of(v[u][e])) >= dstar) m |= 1u << e;
+          // order within the stretch: lane-major, then element
+          uint32_t before = 0, all = 0;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const uint64_t b = __ballot((m >> e) & 1u);
+            before += (uint32_t)__popcll(b & lt);
+            all += (uint32_t)__popcll(b);
+          }
+          uint32_t at = pos + before;
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if ((m >> e) & 1u) {
+              const uint32_t k = key_of(v[u][e]);
+              const uint32_t idx = (uint32_t)(i0 + e);
+              if (at < (uint32_t)kCandCap) {
+                if (split) {
+                  coherent_store(reinterpret_cast<unsigned long long*>(gcand + at),
+                                 (unsigned long long)k | ((unsigned long long)idx << 32));
+                } else {
+                  ckey[at] = k;
+                  cidx[at] = idx;
+                }
+              }
+              ++at;
+            }
+          pos += all;
+        }
+      }
+    }
+  }
+
+  if (split) {
+    // the last filter workgroup of the row finishes it
+    stores_complete();
+    __syncthreads();
+    if (tid == 0) scratch[kWaves + 3] = arrive_last(&a.done[row], (uint32_t)a.n_fseg) ? 1u : 0u;
+    __syncthreads();
+    if (scratch[kWaves + 3] == 0u) return;
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+    if (tid == 0) coherent_store(&a.done[row], 0u);  // leave the counter zeroed
+    if (fits)
+      for (uint32_t i = tid; i < total; i += kThreads) {
+        const unsigned long long v =
+            coherent_load(reinterpret_cast<const unsigned long long*>(gcand + i));
+        ckey[i] = (uint32_t)v;
+        cidx[i] = (uint32_t)(v >> 32);
+      }
   }
   __syncthreads();
 
-  uint32_t total = ncand;
-  if (a.n_fseg > 1) {
-    // hand the candidates over, then the last segment to finish gathers all
-    uint2* slot = a.slots + (row * a.n_fseg + fs) * kSlotCap;
-    if (!overflow)
-      for (uint32_t i = tid; i < ncand; i += kThreads) slot[i] = make_uint2(ckey[i], cidx[i]);
-    if (tid == 0) a.slotcnt[row * a.n_fseg + fs] = overflow ? kOverflow : ncand;
-    __threadfence();
-    __syncthreads();
-    if (tid == 0) {
-      const uint32_t old = atomicAdd(&a.done[row], 1u);
-      scratch[kWaves + 3] = (old == (uint32_t)a.n_fseg - 1u) ? 1u : 0u;
-    }
-    __syncthreads();
-    if (scratch[kWaves + 3] == 0u) return;
-    __threadfence();
-    if (tid == 0) a.done[row] = 0u;  // leave the counter zeroed
-    // gather slots in segment order
-    total = 0;
-    overflow = false;
-    for (int64_t g = 0; g < a.n_fseg; ++g) {
-      const uint32_t n = a.slotcnt[row * a.n_fseg + g];
-      if (n == kOverflow || total + n > (uint32_t)kCandCap) {
-        overflow = true;
-        break;
-      }
-      const uint2* src = a.slots + (row * a.n_fseg + g) * kSlotCap;
-      for (uint32_t i = tid; i < n; i += kThreads) {
-        const uint2 v = src[i];
-        ckey[total + i] = v.x;
-        cidx[total + i] = v.y;
-      }
-      total += n;
-    }
-    __syncthreads();
-  }
-
-  if (overflow || total != n_sure + n_maybe) {
+  if (!fits) {
     select_row_global(bits, c, kB, out, outs, hist, scratch);
     if (tid == 0) a.cnt[row] = kB;
     return;
   }
 
-  // ---- 3. exact choice among the threshold-bin candidates ---------------
+  // ---- 4. exact choice among the threshold-bin candidates ---------------
   Radix r{0u, 0u, need};
   if (need < n_maybe) {
     auto key = [&](int64_t i) { return ckey[i]; };
@@ -387,24 +449,23 @@ SelectPlan select_plan(const Dims& d, int batch, int n_q, int32_t max_pos_end) {
   p.kernel = !mfma ? 0 : (n_q >= 16 ? 1 : 2);
   p.W = score_row_width(d.r, max_pos_end);
   const int64_t c_max = max((int64_t)1, (int64_t)(max_pos_end - 1) / d.r);
-  p.sseg = p.kernel == 0 ? 256 : 2048;
+  p.sseg = p.kernel == 0 ? 256 : (p.kernel == 1 ? 2048 : 1024);
   p.n_sseg = (c_max + p.sseg - 1) / p.sseg;
   const int64_t rows = (int64_t)batch * n_q;
   if (rows >= 256 || c_max <= kFilterSeg) {
-    p.fseg = (c_max + 3) / 4 * 4;
+    p.fseg = p.n_sseg;          // score segments per filter workgroup
     p.n_fseg = 1;
   } else {
-    p.fseg = kFilterSeg;
-    p.n_fseg = (c_max + kFilterSeg - 1) / kFilterSeg;
+    p.fseg = max((int64_t)1, kFilterSeg / p.sseg);
+    p.n_fseg = (p.n_sseg + p.fseg - 1) / p.fseg;
   }
   auto align = [](size_t v) { return (v + 255) / 256 * 256; };
   size_t off = align(sizeof(float) * (size_t)rows * (size_t)p.W);
   p.off_hist = off;
   off = align(off + sizeof(uint32_t) * (size_t)rows * p.n_sseg * kHistWords);
   p.off_slots = off;
-  if (p.n_fseg > 1) off = align(off + sizeof(uint2) * (size_t)rows * p.n_fseg * kSlotCap);
+  if (p.n_fseg > 1) off = align(off + sizeof(uint2) * (size_t)rows * kCandCap);
   p.off_slotcnt = off;
-  off = align(off + sizeof(uint32_t) * (size_t)rows * p.n_fseg);
   p.off_done = off;
   off = align(off + sizeof(uint32_t) * (size_t)rows);
   p.bytes = off;
@@ -421,10 +482,9 @@ hipError_t launch_select(const Dims& d, const SelectPlan& pl, int batch, int n_q
   a.hist = reinterpret_cast<const uint32_t*>(ws + pl.off_hist);
   a.sseg = pl.sseg;
   a.n_sseg = pl.n_sseg;
-  a.slots = reinterpret_cast<uint2*>(ws + pl.off_slots);
-  a.slotcnt = reinterpret_cast<uint32_t*>(ws + pl.off_slotcnt);
+  a.cand = reinterpret_cast<uint2*>(ws + pl.off_slots);
   a.done = reinterpret_cast<uint32_t*>(ws + pl.off_done);
-  a.fseg = pl.fseg;
+  a.spw = pl.fseg;
   a.n_fseg = pl.n_fseg;
   a.n_q = n_q;
   a.q_pos0 = q_pos0;

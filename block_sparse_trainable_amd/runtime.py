@@ -63,10 +63,8 @@ class DeviceLayer:
         return torch.tensor(np.asarray(values, dtype=np.int32), device=self.device)
 
     def workspace(self, op: int, batch: int, n_q: int, max_pos_end: int) -> torch.Tensor:
-        """One workspace per op, grown on demand.  Zero-filled when allocated:
-        the decode attention keeps its completion counters at the head of its
-        workspace and needs them zero before the first call (every call
-        leaves them zero)."""
+        """One workspace per op, grown on demand (no state is kept in it
+        between calls)."""
         n = B.qsa_workspace_size(self.cfg, op, batch, n_q, max_pos_end)
         key = (op,)
         ws = self._ws.get(key)

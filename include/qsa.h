@@ -171,11 +171,6 @@ qsa_status qsa_sparse_attn_prefill(const qsa_config* cfg, int32_t batch, int32_t
  * [concept] (B); the concept page's "Why it matters" reports decode-phase
  * kernel speed-ups at 1M context.
  *
- * Workspace state: the first 256 KiB of the decode workspace hold per-row
- * completion counters that must be zero before the FIRST call using that
- * buffer (e.g. one hipMemset after allocation); every call leaves them zero
- * again.  batch <= 65536.
- *
  *   q          (dtype) [batch][q_heads][head_dim].
  *   q_pos      int32 [batch] device: position of the new token, whose K/V
  *              rows are already written.  max_pos_end > every q_pos[s].

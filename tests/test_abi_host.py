@@ -76,25 +76,23 @@ def test_workspace_sizes(lib):
     nseg = -(-34815 // 2048)
     want = _al(4 * rows * W)
     want = _al(want + 4 * rows * nseg * 128)
-    want = _al(want + 4 * rows)          # one filter segment per row
-    want = _al(want + 4 * rows)
+    want = _al(want + 4 * rows)          # completion counters
     assert qsa.qsa_workspace_size(c, B.QSA_OP_SELECT, 2, 8192, 139264) == want
-    # select, few long rows: candidate hand-over slots of 8192-score segments
+    # select, few long rows: 1024-block score segments and a row-wide
+    # candidate array (4096 key/index pairs) for rows split over workgroups
     rows, c_max = 8, (262211 - 1) // 4
     W = -(-c_max // 4) * 4
-    nseg, nf = -(-c_max // 2048), -(-c_max // 8192)
+    nseg = -(-c_max // 1024)
     want = _al(4 * rows * W)
     want = _al(want + 4 * rows * nseg * 128)
-    want = _al(want + 8 * rows * nf * 1024)
-    want = _al(want + 4 * rows * nf)
+    want = _al(want + 8 * rows * 4096)
     want = _al(want + 4 * rows)
     assert qsa.qsa_workspace_size(c, B.QSA_OP_SELECT, 8, 1, 262211) == want
     assert qsa.qsa_workspace_size(c, B.QSA_OP_INDEX_BUILD, 1, 1, 10) == 0
     assert qsa.qsa_workspace_size(c, B.QSA_OP_PREFILL, 1, 100, 100) == 0
-    # decode: 256 KiB of counters, then 17 splits of 32 pseudo-blocks, each
-    # 16 heads x (128 + 2) floats
+    # decode: 17 splits of 32 pseudo-blocks, each 16 heads x (128 + 2) floats
     assert (qsa.qsa_workspace_size(c, B.QSA_OP_DECODE, 8, 1, 300000)
-            == 4 * 65536 + 4 * 8 * 17 * (16 * 128 + 32))
+            == 4 * 8 * 17 * (16 * 128 + 32))
     assert qsa.qsa_workspace_size(cfg(dtype=B.QSA_F32), B.QSA_OP_DECODE, 8, 1, 300000) == 0
 
 
