@@ -35,6 +35,7 @@ __global__ __launch_bounds__(256) void compress_kernel(
   const int64_t b_end = min(la / 4, cap_blocks);
 
   const int d0 = 2 * lane;  // this lane's dims: d0, d0 + 1
+  if (b_begin + (int64_t)blockIdx.x * kWaves >= b_end) return;  // nothing to build here
   const int half = rope_dims / 2;
   // role: 0 = not rotated, 1 = first member of a pair, 2 = second member
   int role = 0, partner = lane;

@@ -133,6 +133,14 @@ struct SelectPlan {
   size_t off_hist, off_slots, off_slotcnt, off_done, bytes;
 };
 constexpr int kCandCap = 4096;      // candidates a row may have (else fallback)
+// blocks per score segment of the decode scoring kernel (waves x chunks x 64)
+#ifndef QSA_DEC_WAVES
+#define QSA_DEC_WAVES 8
+#endif
+#ifndef QSA_DEC_CPW
+#define QSA_DEC_CPW 2
+#endif
+constexpr int64_t kDecodeScoreSeg = (int64_t)QSA_DEC_WAVES * QSA_DEC_CPW * 64;
 SelectPlan select_plan(const struct Dims& d, int batch, int n_q, int32_t max_pos_end);
 
 // ------------------------------------------------------------ launchers ----

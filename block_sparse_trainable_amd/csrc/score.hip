@@ -208,16 +208,15 @@ __global__ __launch_bounds__(256) void score_mfma_prefill_kernel(
 }
 
 // ------------------------------------------------------- MFMA, decode ------
-// Few queries, long rows: workgroup = (segment of 1024 blocks, 4 queries).
-// Each of the eight waves takes 128 blocks of the segment and issues all of
-// their B-tile loads (32 KiB) straight from HBM before the MFMAs (no reuse to
+// Few queries, long rows: workgroup = (segment of WAVES*CPW*64 blocks, 4
+// queries).  Each wave takes CPW 64-block chunks of the segment and issues
+// all of their B-tile loads straight from HBM before its MFMAs (no reuse to
 // stage through LDS); rows are 4 queries x 4 heads.
-constexpr int kDecSeg = 1024;
-constexpr int kDecWaves = 8;
-
-__global__ __launch_bounds__(512) void score_mfma_decode_kernel(
+template <int WAVES, int CPW>
+__global__ __launch_bounds__(64 * WAVES) void score_mfma_decode_kernel(
     const uint16_t* __restrict__ q_idx, const int32_t* __restrict__ q_pos0, int n_q,
     const uint16_t* __restrict__ k_cmp, int64_t cap_blocks, ScoreOut o) {
+  constexpr int SEG = WAVES * CPW * 64;
   __shared__ uint32_t hist[4][kHistWords];
   float* __restrict__ scores = o.scores;
   const int64_t W = o.W;
@@ -232,10 +231,10 @@ __global__ __launch_bounds__(512) void score_mfma_decode_kernel(
   if (blockIdx.x == 0 && threadIdx.x < 4 && j0 + (int)threadIdx.x < n_q)
     coherent_store(&o.done[(int64_t)s * n_q + j0 + threadIdx.x], 0u);
   const int64_t c_tile = min(min((pos0 + j_last) / 4, cap_blocks), W);
-  const int64_t seg_lo = (int64_t)blockIdx.x * kDecSeg;
-  const int64_t seg_hi = min(seg_lo + kDecSeg, c_tile);
+  const int64_t seg_lo = (int64_t)blockIdx.x * SEG;
+  const int64_t seg_hi = min(seg_lo + SEG, c_tile);
   if (seg_lo >= seg_hi) return;  // no query of the tile reaches this segment
-  for (int i = threadIdx.x; i < 4 * kHistWords; i += 64 * kDecWaves) (&hist[0][0])[i] = 0u;
+  for (int i = threadIdx.x; i < 4 * kHistWords; i += 64 * WAVES) (&hist[0][0])[i] = 0u;
   __syncthreads();
 
   u32x4 qa[4];
@@ -251,38 +250,52 @@ __global__ __launch_bounds__(512) void score_mfma_decode_kernel(
   float* dst = scores + ((int64_t)s * n_q + (jq_o < n_q ? jq_o : 0)) * W;
   const uint16_t* kbase = k_cmp + (int64_t)s * cap_blocks * 128 + 8 * gq;
 
-  for (int64_t cb = seg_lo + 128 * wave; cb < seg_hi; cb += 128 * kDecWaves) {
-    u32x4 kb[8][4];
+  // chunk c of this wave: blocks seg_lo + 64 * (c * WAVES + wave) .. +63
+  // (adjacent waves stream adjacent memory)
+  u32x4 kb[CPW][4][4];
 #pragma unroll
-    for (int ct = 0; ct < 8; ++ct) {
-      const int64_t b = cb + 16 * ct + l16;
+  for (int c = 0; c < CPW; ++c)
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct) {
+      const int64_t b = seg_lo + 64 * (c * WAVES + wave) + 16 * ct + l16;
       const bool ok = b < seg_hi;
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk)
-        kb[ct][kk] = ok ? ld16(kbase + b * 128 + 32 * kk) : u32x4{0, 0, 0, 0};
+        kb[c][ct][kk] = ok ? ld16(kbase + b * 128 + 32 * kk) : u32x4{0, 0, 0, 0};
     }
 #pragma unroll
-    for (int ct = 0; ct < 8; ++ct) {
+  for (int c = 0; c < CPW; ++c)
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct) {
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk)
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(qa[kk]), as_bf16x8(kb[ct][kk]),
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(qa[kk]), as_bf16x8(kb[c][ct][kk]),
                                                       acc, 0, 0, 0);
-      const int64_t b = cb + 16 * ct + l16;
+      const int64_t b = seg_lo + 64 * (c * WAVES + wave) + 16 * ct + l16;
       const float v = relu(acc[0]) + relu(acc[1]) + relu(acc[2]) + relu(acc[3]);
       if (b < cq) {
         dst[b] = v;
         hist_add(hist[gq], v);
       }
     }
-  }
   __syncthreads();
-  for (int i = threadIdx.x; i < 4 * kHistWords; i += 64 * kDecWaves) {
+  for (int i = threadIdx.x; i < 4 * kHistWords; i += 64 * WAVES) {
     const int ql = i / kHistWords, w = i % kHistWords;
     if (j0 + ql < n_q)
       o.hist[hist_offset((int64_t)s * n_q + j0 + ql, blockIdx.x, o.n_sseg) + w] = hist[ql][w];
   }
 }
+
+// Decode scoring shape: QSA_DEC_WAVES waves x QSA_DEC_CPW chunks per workgroup.
+#ifndef QSA_DEC_WAVES
+#define QSA_DEC_WAVES 8
+#endif
+#ifndef QSA_DEC_CPW
+#define QSA_DEC_CPW 2
+#endif
+constexpr int kDecWaves = QSA_DEC_WAVES;
+constexpr int kDecCpw = QSA_DEC_CPW;
 
 }  // namespace
 
@@ -301,7 +314,7 @@ hipError_t launch_score(const Dims& d, const SelectPlan& pl, int batch, int n_q,
                        static_cast<const uint16_t*>(k_cmp), cap_blocks, (int)pl.sseg, o);
   } else if (pl.kernel == 2) {
     dim3 grid(segs, (unsigned)((n_q + 3) / 4), (unsigned)batch);
-    hipLaunchKernelGGL(score_mfma_decode_kernel, grid, dim3(64 * kDecWaves), 0, st,
+    hipLaunchKernelGGL((score_mfma_decode_kernel<kDecWaves, kDecCpw>), grid, dim3(64 * kDecWaves), 0, st,
                        static_cast<const uint16_t*>(q_idx), q_pos0, n_q,
                        static_cast<const uint16_t*>(k_cmp), cap_blocks, o);
   } else {

@@ -77,12 +77,13 @@ struct Radix {
 // eligible keys with (k & mask) == prefix complete the top need_in.
 template <class KeyFn, class EligFn>
 __device__ Radix radix_select(KeyFn key, EligFn elig, int64_t n, uint32_t need_in,
-                              uint32_t* hist, uint32_t* scratch) {
+                              uint32_t* hist, uint32_t* scratch, int first_pass = 0,
+                              uint32_t prefix0 = 0u, uint32_t mask0 = 0u) {
   const int tid = threadIdx.x;
-  Radix r{0u, 0u, need_in};
+  Radix r{prefix0, mask0, need_in};
   const int shifts[3] = {20, 9, 0};
   const int widths[3] = {11, 11, 9};
-  for (int pass = 0; pass < 3; ++pass) {
+  for (int pass = first_pass; pass < 3; ++pass) {
     const int sh = shifts[pass];
     const int nb = 1 << widths[pass];
     const uint32_t dmask = (uint32_t)nb - 1u;
@@ -191,6 +192,9 @@ struct FilterArgs {
 
 constexpr int kMaxSeg = 2048;  // score segments per row the offsets table holds
 
+// PRE: split rows whose workgroup sweeps one segment per wave load those
+// scores up front (only the decode shape; it costs registers).
+template <bool PRE>
 __global__ __launch_bounds__(kThreads) void filter_select_kernel(FilterArgs a) {
   __shared__ uint32_t ckey[kCandCap];
   __shared__ uint32_t cidx[kCandCap];
@@ -225,6 +229,23 @@ __global__ __launch_bounds__(kThreads) void filter_select_kernel(FilterArgs a) {
   const uint32_t* hrow = a.hist + hist_offset(row, 0, a.n_sseg);
 
   // ---- 1. row histogram and threshold bin ---------------------------------
+  // A split workgroup (long decode rows) also issues its own segment's score
+  // loads here, so they overlap the histogram work (one segment of <= 1024
+  // scores per wave).
+  const bool split = a.n_fseg > 1;
+  const bool pre_sweep = PRE && split && a.sseg <= 1024 && a.spw <= kWaves;
+  u32x4 pv[4];
+  if constexpr (PRE) {
+    const int64_t g = fs * a.spw + wave;
+    const int64_t i_lo = g * a.sseg;
+    const int64_t i_hi = min(i_lo + a.sseg, c);
+    const bool mine = g < min(fs * a.spw + a.spw, nseg);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int64_t i0 = i_lo + 256 * u + 4 * lane;
+      pv[u] = (mine && i0 < i_hi) ? *reinterpret_cast<const u32x4*>(bits + i0) : u32x4{0, 0, 0, 0};
+    }
+  }
   {
     // 512 threads: word w = 127 - (tid & 127) of every 4th segment
     uint32_t* part = hist;  // [4][128][2] partial sums (lo, hi)
@@ -310,56 +331,67 @@ __global__ __launch_bounds__(kThreads) void filter_select_kernel(FilterArgs a) {
   }
 
   // ---- 3. sweep this workgroup's segments; waves take whole segments ------
-  const bool split = a.n_fseg > 1;
   uint2* gcand = split ? a.cand + row * kCandCap : nullptr;
   if (fits) {
     const int64_t g_lo = fs * a.spw;
     const int64_t g_hi = min(g_lo + a.spw, nseg);
     const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-    for (int64_t g = g_lo + wave; g < g_hi; g += kWaves) {
-      const int64_t i_lo = g * a.sseg;
-      const int64_t i_hi = min(i_lo + a.sseg, c);
-      uint32_t pos = segoff[g];
-      for (int64_t base = i_lo; base < i_hi; base += 256 * 8) {
-        u32x4 v[8];
+    // keys i0..i0+3 (lane-ordered stretch of 256): keep those with bin >= d*
+    auto take4 = [&](int64_t i0, int64_t i_hi, const u32x4& v, uint32_t& pos) {
+      uint32_t m = 0;
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {   // all of this stretch's loads in flight
-          const int64_t i0 = base + 256 * u + 4 * lane;
-          v[u] = i0 < i_hi ? *reinterpret_cast<const u32x4*>(bits + i0) : u32x4{0, 0, 0, 0};
-        }
+      for (int e = 0; e < 4; ++e)
+        if (i0 + e < i_hi && score_bin(key_of(v[e])) >= dstar) m |= 1u << e;
+      // order within the stretch: lane-major, then element
+      uint32_t before = 0, all = 0;
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {
-          const int64_t i0 = base + 256 * u + 4 * lane;
-          uint32_t m = 0;
+      for (int e = 0; e < 4; ++e) {
+        const uint64_t b = __ballot((m >> e) & 1u);
+        before += (uint32_t)__popcll(b & lt);
+        all += (uint32_t)__popcll(b);
+      }
+      uint32_t at = pos + before;
 #pragma unroll
-          for (int e = 0; e < 4; ++e)
-            if (i0 + e < i_hi && score_bin(key_of(v[u][e])) >= dstar) m |= 1u << e;
-          // order within the stretch: lane-major, then element
-          uint32_t before = 0, all = 0;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const uint64_t b = __ballot((m >> e) & 1u);
-            before += (uint32_t)__popcll(b & lt);
-            all += (uint32_t)__popcll(b);
-          }
-          uint32_t at = pos + before;
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            if ((m >> e) & 1u) {
-              const uint32_t k = key_of(v[u][e]);
-              const uint32_t idx = (uint32_t)(i0 + e);
-              if (at < (uint32_t)kCandCap) {
-                if (split) {
-                  coherent_store(reinterpret_cast<unsigned long long*>(gcand + at),
-                                 (unsigned long long)k | ((unsigned long long)idx << 32));
-                } else {
-                  ckey[at] = k;
-                  cidx[at] = idx;
-                }
-              }
-              ++at;
+      for (int e = 0; e < 4; ++e)
+        if ((m >> e) & 1u) {
+          const uint32_t k = key_of(v[e]);
+          const uint32_t idx = (uint32_t)(i0 + e);
+          if (at < (uint32_t)kCandCap) {
+            if (split) {
+              coherent_store(reinterpret_cast<unsigned long long*>(gcand + at),
+                             (unsigned long long)k | ((unsigned long long)idx << 32));
+            } else {
+              ckey[at] = k;
+              cidx[at] = idx;
             }
-          pos += all;
+          }
+          ++at;
+        }
+      pos += all;
+    };
+    if (PRE && pre_sweep) {
+      const int64_t g = g_lo + wave;   // this wave's one segment, already loaded
+      if (g < g_hi) {
+        const int64_t i_lo = g * a.sseg;
+        const int64_t i_hi = min(i_lo + a.sseg, c);
+        uint32_t pos = segoff[g];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) take4(i_lo + 256 * u + 4 * lane, i_hi, pv[u], pos);
+      }
+    } else {
+      for (int64_t g = g_lo + wave; g < g_hi; g += kWaves) {
+        const int64_t i_lo = g * a.sseg;
+        const int64_t i_hi = min(i_lo + a.sseg, c);
+        uint32_t pos = segoff[g];
+        for (int64_t base = i_lo; base < i_hi; base += 256 * 8) {
+          u32x4 v[8];
+#pragma unroll
+          for (int u = 0; u < 8; ++u) {   // all of this stretch's loads in flight
+            const int64_t i0 = base + 256 * u + 4 * lane;
+            v[u] = i0 < i_hi ? *reinterpret_cast<const u32x4*>(bits + i0) : u32x4{0, 0, 0, 0};
+          }
+#pragma unroll
+          for (int u = 0; u < 8; ++u) take4(base + 256 * u + 4 * lane, i_hi, v[u], pos);
         }
       }
     }
@@ -395,7 +427,13 @@ __global__ __launch_bounds__(kThreads) void filter_select_kernel(FilterArgs a) {
   if (need < n_maybe) {
     auto key = [&](int64_t i) { return ckey[i]; };
     auto elig = [&](int64_t i) { return score_bin(ckey[i]) == dstar; };
-    r = radix_select(key, elig, (int64_t)total, need, hist, scratch);
+    if (dstar > 0u && dstar < (uint32_t)kHistBins - 1u) {
+      // an unclamped bin fixes bits 30..20 of its keys: start at the second digit
+      r = radix_select(key, elig, (int64_t)total, need, hist, scratch, 1, (dstar + 888u) << 20,
+                       0x7FFu << 20);
+    } else {
+      r = radix_select(key, elig, (int64_t)total, need, hist, scratch);
+    }
   }
   // ordered output: bin > d* always; bin == d* by (k & mask) vs prefix
   uint32_t written = 0, eq_seen = 0;
@@ -449,7 +487,7 @@ SelectPlan select_plan(const Dims& d, int batch, int n_q, int32_t max_pos_end) {
   p.kernel = !mfma ? 0 : (n_q >= 16 ? 1 : 2);
   p.W = score_row_width(d.r, max_pos_end);
   const int64_t c_max = max((int64_t)1, (int64_t)(max_pos_end - 1) / d.r);
-  p.sseg = p.kernel == 0 ? 256 : (p.kernel == 1 ? 2048 : 1024);
+  p.sseg = p.kernel == 0 ? 256 : (p.kernel == 1 ? 2048 : kDecodeScoreSeg);
   p.n_sseg = (c_max + p.sseg - 1) / p.sseg;
   const int64_t rows = (int64_t)batch * n_q;
   if (rows >= 256 || c_max <= kFilterSeg) {
@@ -494,7 +532,10 @@ hipError_t launch_select(const Dims& d, const SelectPlan& pl, int batch, int n_q
   a.cnt = cnt;
   a.sel_scores = sel_scores;
   dim3 grid((unsigned)((int64_t)batch * n_q), (unsigned)pl.n_fseg);
-  hipLaunchKernelGGL(filter_select_kernel, grid, dim3(kThreads), 0, st, a);
+  if (pl.n_fseg > 1 && pl.sseg <= 1024 && pl.fseg <= kWaves)
+    hipLaunchKernelGGL(filter_select_kernel<true>, grid, dim3(kThreads), 0, st, a);
+  else
+    hipLaunchKernelGGL(filter_select_kernel<false>, grid, dim3(kThreads), 0, st, a);
   return hipGetLastError();
 }
 

@@ -161,39 +161,68 @@ class DeviceLayer:
         self.attend_decode(q_s[t], pos_t[t], max_pos_end, sel, cnt, out, lse)
         return outputs
 
-    def capture_decode(self, plan, steps: int, outputs, overlap_build: bool = True):
+    def capture_decode(self, plan, steps: int, outputs, overlap_build: bool = False,
+                       branches: int = 1):
         """Capture `steps` decode steps into one HIP graph (torch.cuda.CUDAGraph).
 
-        With overlap_build, step t's index_build runs on a side stream: the
-        block it may complete is first a candidate at step t+1, so it only has
-        to finish before step t+1's selection, not before step t's.
+        overlap_build: step t's index_build runs on a side stream (the block it
+        may complete is first a candidate at step t+1), joined before step
+        t+1's selection.
+        branches: the batch is split into this many contiguous sequence groups,
+        each driven on its own stream (its own workspaces), so one group's
+        latency-bound selection/attention overlaps another's HBM-bound scan.
         """
         q_idx_s, q_s, pos_t, pos1_t, max_pos_end = plan
         sel, cnt, scs, out, lse = outputs
-        # allocate workspaces outside the capture
-        self.workspace(B.QSA_OP_SELECT, self.batch, 1, max_pos_end)
-        self.workspace(B.QSA_OP_DECODE, self.batch, 1, max_pos_end)
+        B_ = self.batch
+        bounds = [round(i * B_ / branches) for i in range(branches + 1)]
+        groups = [(a, b) for a, b in zip(bounds[:-1], bounds[1:]) if b > a]
+        # per-group workspaces allocated outside the capture
+        ws = []
+        for a, b in groups:
+            nsel = B.qsa_workspace_size(self.cfg, B.QSA_OP_SELECT, b - a, 1, max_pos_end)
+            ndec = B.qsa_workspace_size(self.cfg, B.QSA_OP_DECODE, b - a, 1, max_pos_end)
+            ws.append((torch.zeros(max(nsel, 16), dtype=torch.uint8, device=self.device),
+                       torch.zeros(max(ndec, 16), dtype=torch.uint8, device=self.device)))
         g = torch.cuda.CUDAGraph()
-        side = torch.cuda.Stream(device=self.device)
-        main = torch.cuda.current_stream(self.device)
-        side.wait_stream(main)
-        main.synchronize()
+        streams = [torch.cuda.Stream(device=self.device) for _ in range(len(groups) + 1)]
+        torch.cuda.synchronize(self.device)
         with torch.cuda.graph(g):
-            cap_stream = torch.cuda.current_stream(self.device)
-            built = None
+            cap = torch.cuda.current_stream(self.device)
             for t in range(steps):
+                if overlap_build and t > 0:
+                    cap.wait_event(built)
                 if overlap_build:
-                    side.wait_stream(cap_stream)
-                    with torch.cuda.stream(side):
+                    streams[-1].wait_stream(cap)
+                    with torch.cuda.stream(streams[-1]):
                         self.index_build(pos_t[t], pos1_t[t], 1)
-                    if built is not None:
-                        cap_stream.wait_event(built)
                     built = torch.cuda.Event()
-                    built.record(side)
+                    built.record(streams[-1])
                 else:
                     self.index_build(pos_t[t], pos1_t[t], 1)
-                self.select(q_idx_s[t].unsqueeze(1), pos_t[t], max_pos_end, sel, cnt, scs, n_q=1)
-                self.attend_decode(q_s[t], pos_t[t], max_pos_end, sel, cnt, out, lse)
-            if built is not None:
-                cap_stream.wait_event(built)
+                for gi, (a, b) in enumerate(groups):
+                    st = streams[gi] if len(groups) > 1 else cap
+                    if st is not cap:
+                        st.wait_stream(cap)
+                    with torch.cuda.stream(st):
+                        self._decode_group(plan, t, outputs, a, b, ws[gi])
+                for gi in range(len(groups)):
+                    if len(groups) > 1:
+                        cap.wait_stream(streams[gi])
+            if overlap_build:
+                cap.wait_event(built)
         return g
+
+    def _decode_group(self, plan, t, outputs, a, b, ws):
+        """select_topk + sparse_attn_decode for sequences [a, b) of step t."""
+        q_idx_s, q_s, pos_t, pos1_t, max_pos_end = plan
+        sel, cnt, scs, out, lse = outputs
+        nb = b - a
+        wsel, wdec = ws
+        k_cmp = self.k_cmp[a:b]
+        B.qsa_select_topk(self.cfg, nb, 1, q_idx_s[t, a:b].unsqueeze(1), pos_t[t, a:b],
+                          int(max_pos_end), k_cmp, self.cap, sel[a:b], cnt[a:b], scs[a:b],
+                          wsel, wsel.numel())
+        B.qsa_sparse_attn_decode(self.cfg, nb, q_s[t, a:b], self.k[a:b], self.v[a:b], self.cap,
+                                 pos_t[t, a:b], int(max_pos_end), sel[a:b], cnt[a:b], out[a:b],
+                                 lse[a:b], wdec, wdec.numel())

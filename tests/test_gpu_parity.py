@@ -307,15 +307,15 @@ def test_decode_graph_replay_matches_eager():
         dl.decode_step(plan, t, outs)
     torch.cuda.synchronize()
     ref = [o.clone() for o in outs]
-    for overlap in (True, False):
-        g = dl.capture_decode(plan, 9, outs, overlap_build=overlap)
+    for kw in ({}, {"overlap_build": True}, {"branches": 2}, {"branches": 3}):
+        g = dl.capture_decode(plan, 9, outs, **kw)
         for rep in range(3):
             for o in outs:
                 o.zero_()
             g.replay()
             torch.cuda.synchronize()
             for a, b in zip(ref, outs):
-                assert torch.equal(a, b), f"replay {rep} (overlap={overlap}) differs"
+                assert torch.equal(a, b), f"replay {rep} ({kw}) differs"
             dl.decode_step(plan, 2, outs)       # eager work between replays
             torch.cuda.synchronize()
 
