@@ -37,6 +37,30 @@ METRIC = "QSA prefill tok/s + decode µs/step at 128K–1M ctx; % of HBM/MFMA ro
 HBM_PEAK_GBS = 8000.0
 BF16_MFMA_PEAK_TFLOPS = 2500.0
 
+# HBM traffic of one sparse_attn_prefill launch on the 128K chunked workload,
+# from two rocprofv3 --pmc runs of `bench.py --only prefill` (FETCH_SIZE, then
+# WRITE_SIZE, KiB per dispatch), each scaled by what the same counter reads for
+# a plain 1 GiB device copy (`bench.py --calibrate-copy`: FETCH_SIZE reads
+# 524,302 KiB for 1 GiB read -> x2.0; WRITE_SIZE reads 1 GiB -> x1.0).  The
+# figures belong to the attention source with this SHA-1; for any other source
+# `traffic` is reported as null until the counters are taken again.
+ATTN_COUNTERS = {
+    "source_sha1": "fc8637675e81b8b7f40827b1131b244a63a5caaa",
+    "fetch_kib": 14366804.6, "write_kib": 66566.6,
+    "fetch_scale": 2.0, "write_scale": 1.0,
+}
+
+
+def attn_traffic_bytes():
+    import hashlib
+    src = os.path.join(ROOT, "block_sparse_trainable_amd", "csrc", "attn.hip")
+    with open(src, "rb") as f:
+        sha = hashlib.sha1(f.read()).hexdigest()
+    c = ATTN_COUNTERS
+    if sha != c["source_sha1"]:
+        return None
+    return (c["fetch_kib"] * c["fetch_scale"] + c["write_kib"] * c["write_scale"]) * 1024.0
+
 
 def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
@@ -56,7 +80,7 @@ def parse():
                          "known-size reference for scaling HBM byte counters")
     ap.add_argument("--decode-steps", type=int, default=64)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-rows", type=int, default=768,
+    ap.add_argument("--cpu-rows", type=int, default=2304,
                     help="query rows in the oracle's timed sample")
     return ap.parse_args()
 
@@ -313,7 +337,7 @@ def main():
     achieved = pre["attn_bytes"] / (attn_ms * 1e-3) / 1e9
     roofline = {"kernel": "sparse_attn_prefill (attn_mfma_kernel<2,128>)", "bound": "hbm",
                 "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                "frac": achieved / HBM_PEAK_GBS, "traffic": attn_traffic_bytes(),
                 "algorithmic_bytes_per_launch": pre["attn_bytes"],
                 "avg_launch_ms": attn_ms}
     score_tflops = pre["score_flops"] / (pre["stages_ms"]["score_select"] * 1e-3) / 1e12
