@@ -186,9 +186,10 @@ def bench_prefill(args, torch):
 # ----------------------------------------------------------------- decode --
 def bench_decode(args, torch):
     """Decode loop: `steps` steps of index_build + select_topk + attention for
-    8 sequences at 256K context, captured in one HIP graph (the step's
-    index_build overlapped on a side stream) and replayed; eager per-step
-    times are reported beside it."""
+    8 sequences at 256K context, as one fused launch per step
+    (qsa_decode_step) and as the three separate calls (several scheduling
+    variants), each captured in one HIP graph and replayed; the best is
+    reported, eager per-step times beside it."""
     from block_sparse_trainable_amd import synth
     from block_sparse_trainable_amd.runtime import DeviceLayer
     steps = args.decode_steps
@@ -212,11 +213,25 @@ def bench_decode(args, torch):
     torch.cuda.synchronize()
     per = np.array([evs[t].elapsed_time(evs[t + 1]) for t in range(steps)]) * 1e3
     eager_us = evs[0].elapsed_time(evs[-1]) * 1e3 / steps
+    # the same steps through the fused entry point (one launch per step)
+    for t in range(min(8, steps)):
+        dl.decode_step_fused(plan, t, outs)
+    torch.cuda.synchronize()
+    evs[0].record()
+    for t in range(steps):
+        dl.decode_step_fused(plan, t, outs)
+        evs[t + 1].record()
+    torch.cuda.synchronize()
+    per_f = np.array([evs[t].elapsed_time(evs[t + 1]) for t in range(steps)]) * 1e3
+    fused_eager_us = evs[0].elapsed_time(evs[-1]) * 1e3 / steps
     # graph replay, for each scheduling variant; the best one is reported
     variants = {}
-    for name, kw in (("inline-build", {}), ("side-build", {"overlap_build": True}),
+    for name, kw in (("fused", None), ("inline-build", {}), ("side-build", {"overlap_build": True}),
                      ("2-branch", {"branches": 2}), ("4-branch", {"branches": 4})):
-        g = dl.capture_decode(plan, steps, outs, **kw)
+        if kw is None:
+            g = dl.capture_decode_fused(plan, steps, outs)
+        else:
+            g = dl.capture_decode(plan, steps, outs, **kw)
         g.replay()
         torch.cuda.synchronize()
         reps = 5
@@ -241,6 +256,9 @@ def bench_decode(args, torch):
            "eager_us_per_step": eager_us,
            "eager_p50_us": float(np.percentile(per, 50)),
            "eager_p99_us": float(np.percentile(per, 99)),
+           "fused_eager_us_per_step": fused_eager_us,
+           "fused_eager_p50_us": float(np.percentile(per_f, 50)),
+           "fused_eager_p99_us": float(np.percentile(per_f, 99)),
            "algorithmic_bytes_per_step": scan_bytes + gather,
            "hbm_frac": (scan_bytes + gather) / (graph_us * 1e-6) / (HBM_PEAK_GBS * 1e9)}
     del dl, outs

@@ -17,11 +17,11 @@ _lib = None
 
 QSA_OK, QSA_ERR_INVALID_ARGUMENT, QSA_ERR_UNSUPPORTED, QSA_ERR_WORKSPACE, QSA_ERR_DEVICE = range(5)
 QSA_F32, QSA_BF16 = 0, 1
-QSA_OP_INDEX_BUILD, QSA_OP_SELECT, QSA_OP_PREFILL, QSA_OP_DECODE = range(4)
+QSA_OP_INDEX_BUILD, QSA_OP_SELECT, QSA_OP_PREFILL, QSA_OP_DECODE, QSA_OP_DECODE_STEP = range(5)
 
 EXPORTED = (
     "qsa_index_build", "qsa_select_topk", "qsa_sparse_attn_prefill", "qsa_sparse_attn_decode",
-    "qsa_workspace_size", "qsa_status_string", "qsa_last_error", "qsa_abi_version",
+    "qsa_decode_step", "qsa_workspace_size", "qsa_status_string", "qsa_last_error", "qsa_abi_version",
 )
 
 
@@ -85,6 +85,7 @@ def load(path: str | None = None):
         "qsa_select_topk": [CFG, I32, I32, P, P, I32, P, I64, P, P, P, P, SZ, P],
         "qsa_sparse_attn_prefill": [CFG, I32, I32, P, P, P, I64, P, I32, P, P, P, P, P, SZ, P],
         "qsa_sparse_attn_decode": [CFG, I32, P, P, P, I64, P, I32, P, P, P, P, P, SZ, P],
+        "qsa_decode_step": [CFG, I32, P, P, P, P, P, P, P, I64, P, I32, P, P, P, P, P, P, SZ, P],
         "qsa_workspace_size": [CFG, I32, I32, I32, I32, ctypes.POINTER(SZ)],
     }
     for name, args in sig.items():
@@ -170,3 +171,14 @@ def qsa_sparse_attn_decode(cfg, batch, q, k_cache, v_cache, cap_tokens, q_pos, m
                                            _ptr(sel_blocks), _ptr(sel_count), _ptr(out),
                                            _ptr(lse), _ptr(workspace), workspace_bytes,
                                            _stream(stream)))
+
+
+def qsa_decode_step(cfg, batch, q_idx, q, k_idx, k_cmp, rms_gain, k_cache, v_cache, cap_tokens,
+                    q_pos, max_pos_end, sel_blocks, sel_count, sel_scores, out, lse, workspace,
+                    workspace_bytes, stream=None) -> None:
+    lib = load()
+    _check(lib, lib.qsa_decode_step(ctypes.byref(cfg), batch, _ptr(q_idx), _ptr(q), _ptr(k_idx),
+                                    _ptr(k_cmp), _ptr(rms_gain), _ptr(k_cache), _ptr(v_cache),
+                                    cap_tokens, _ptr(q_pos), max_pos_end, _ptr(sel_blocks),
+                                    _ptr(sel_count), _ptr(sel_scores), _ptr(out), _ptr(lse),
+                                    _ptr(workspace), workspace_bytes, _stream(stream)))

@@ -1,0 +1,357 @@
+// One work item of the MFMA sparse-attention path: a query's token set, or
+// one split of it, attended by a 256-thread workgroup.  Shared by the
+// stand-alone attention kernels and the fused decode step.
+//
+// "QSA (Qwen Sparse Attention)", Key math / How it works: (B) full
+// scaled-dot-product attention restricted to the selected blocks' tokens;
+// (A) the selected blocks are expanded back to tokens and the tail of the
+// current block is always included.
+//
+// Token set of the query at p (c = floor(p/4)): pseudo-blocks 0..count-1 are
+// the selected blocks, pseudo-block `count` is the tail block c, whose
+// tokens 4c+t count only while 4c+t <= p.
+//
+// Layout (16 query heads, Hkv in {1,2}, head_dim in {64,128}, bf16):
+//   * Work unit: one wave, one tile of 8 pseudo-blocks = 32 tokens.  The 16
+//     heads are the 16 MFMA columns; the contraction dim is the KV rows of
+//     all Hkv heads concatenated (Hkv*D values, contiguous in the cache), and
+//     the query operand is block-diagonal (head h is non-zero only on its
+//     own KV head's dims), so one pass serves every GQA group.
+//   * S^T = K_tile * Qbd: K rows are gathered from HBM straight into A-operand
+//     registers (16 tokens x 64 contiguous bytes per load).  Lane l's result
+//     holds 4 consecutive tokens of one pseudo-block for head l%16.
+//   * Online softmax per head in the log2 domain.  Masked tokens read a safe
+//     row (position p) and get weight 0.
+//   * O^T += V_tile^T * P^T: P^T is already in the B-operand layout (each
+//     lane's 8 probabilities fill its 8 k-slots, the k<->token map chosen to
+//     match).  V rows go from HBM straight into a per-wave LDS tile
+//     (global_load_lds_dwordx4, 16-byte chunks XOR-swizzled so four token
+//     rows read together fall in distinct banks) and are read transposed,
+//     two dims per 4-byte read feeding two MFMAs.  No V staging registers.
+//   * The item's selected-block list is loaded into LDS once, so the K/V
+//     addresses of a tile never wait on a dependent global load.
+//   * The 4 waves interleave tiles and merge their (m, l, O) states in LDS.
+//     A single-split item writes the bf16 output and the log-sum-exp; a split
+//     writes its (m, l, O) state for a log-sum-exp merge of the splits.
+#pragma once
+
+#include <math.h>
+
+#include "qsa_common.h"
+
+namespace qsa {
+
+template <int HKV, int D>
+struct MfmaShape {
+  static constexpr int HQ = 16;
+  static constexpr int G = HQ / HKV;        // query heads per KV head
+  static constexpr int KD = HKV * D;        // concatenated KV row (elements)
+  static constexpr int NK = KD / 32;        // k-steps of S, dim pairs-of-16 of PV
+  static constexpr int ROWB = KD * 2;       // bytes per staged V row
+  static constexpr int CH = KD / 8;         // 16-byte chunks per V row
+  static constexpr int RPI = 64 / CH;       // V rows per wave-wide load
+  static constexpr int TILE_LDS = 32 * ROWB;
+  static constexpr int DP = D + 4;                       // padded head row of the merge area
+  static constexpr int MERGE_FLOATS = 2 * HQ + HQ * DP;  // per wave
+  // the four V tiles, or the wave merge: 4 states + per-head factors, Z, M
+  static constexpr int MERGE_BYTES = 4 * MERGE_FLOATS * 4 + (4 * HQ + 2 * HQ) * 4;
+  static constexpr int LDS_BYTES = (4 * TILE_LDS > MERGE_BYTES) ? 4 * TILE_LDS : MERGE_BYTES;
+  static_assert(CH == 16 || CH == 32, "the V swizzle needs 16 or 32 chunks per row");
+};
+
+constexpr int kMaxPB = 4 * 512 / 4 + 1;   // pseudo-blocks of one query (k_B + tail)
+constexpr int kMaxSplits = 17;            // decode splits: ceil((k_B + 1) / 32)
+constexpr int kDecodeSplitPB = 32;        // pseudo-blocks per decode split
+
+// Floats of one split's state [m 16][l 16][O 16 x D].
+constexpr int part_floats(int D) { return 32 + 16 * D; }
+
+// XOR swizzle of a V row's 16-byte chunks: rows 4 apart start their chunks
+// at different 64-byte offsets, so the transposed 4-byte reads of one wave
+// (four token rows at a time) hit distinct banks.
+__device__ __forceinline__ int vswz(int tk) { return 4 * ((tk >> 2) & 3); }
+
+// Block-diagonal query operand of query row `row` (16 heads): head l16 is
+// non-zero only on its KV head's dims of the concatenated KV row.
+template <int HKV, int D>
+__device__ __forceinline__ void load_qbd(const uint16_t* __restrict__ q, int64_t row,
+                                         u32x4 (&qb)[MfmaShape<HKV, D>::NK]) {
+  using S = MfmaShape<HKV, D>;
+  const int lane = threadIdx.x & 63;
+  const int l16 = lane & 15;
+  const int gq = lane >> 4;
+  const int gn = l16 / S::G;
+#pragma unroll
+  for (int kk = 0; kk < S::NK; ++kk) {
+    const int dim0 = 32 * kk + 8 * gq;
+    const int grp = dim0 / D;
+    qb[kk] = (grp == gn) ? ld16(q + (row * 16 + l16) * D + (dim0 - grp * D))
+                         : u32x4{0, 0, 0, 0};
+  }
+}
+
+// Attends query row `row` (sequence s, position p) over pseudo-blocks
+// [pb_lo, pb_hi) whose block ids the caller has put in sbid[0 ..) (the tail
+// block c = floor(p/4) included as an ordinary id), for work item `item` =
+// row * n_split + split.  n_split == 1 writes the bf16 output and the
+// log-sum-exp; otherwise the split's (m, l, O) state goes to part (with
+// coherent stores when COHERENT: another workgroup of the same kernel reads
+// it).  lds: MfmaShape::LDS_BYTES bytes.  Called by all 256 threads after a
+// barrier that publishes sbid.
+template <int HKV, int D, bool COHERENT>
+__device__ __forceinline__ void attn_mfma_tiles(
+    const u32x4 (&qb)[MfmaShape<HKV, D>::NK], const uint16_t* __restrict__ kc,
+    const uint16_t* __restrict__ vc, int64_t cap, int s, int64_t p, int64_t row, int64_t item,
+    int pb_lo, int pb_hi, const int32_t* sbid, float scale_log2, uint16_t* __restrict__ out,
+    float* __restrict__ lse, float* __restrict__ part, int n_split, unsigned char* lds) {
+  using S = MfmaShape<HKV, D>;
+  constexpr int KD = S::KD, NK = S::NK, ROWB = S::ROWB, G = S::G, CH = S::CH, RPI = S::RPI;
+  constexpr int MF = S::MERGE_FLOATS;
+  static_assert(S::MERGE_BYTES <= S::LDS_BYTES, "merge area must fit");
+
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int l16 = lane & 15;
+  const int gq = lane >> 4;
+  const uint16_t* kbase = kc + (int64_t)s * cap * KD;
+  const uint16_t* vbase = vc + (int64_t)s * cap * KD;
+  // block id of pseudo-block pb, -1 outside this work item
+  auto bid = [&](int pb) -> int64_t { return (pb < pb_hi) ? (int64_t)sbid[pb - pb_lo] : -1; };
+
+  float m_run = -INFINITY, l_run = 0.0f;
+  f32x4 oacc[NK][2];
+#pragma unroll
+  for (int pp = 0; pp < NK; ++pp) oacc[pp][0] = oacc[pp][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+  unsigned char* vt = lds + wave * S::TILE_LDS;
+
+  for (int pb0 = pb_lo + 8 * wave; pb0 < pb_hi; pb0 += 32) {
+    // ---- K rows straight into A-operand registers (needed first)
+    u32x4 kreg[2][NK];
+#pragma unroll
+    for (int st = 0; st < 2; ++st) {
+      const int tk = 16 * st + l16;
+      const int64_t b = bid(pb0 + (tk >> 2));
+      const int64_t tp = 4 * b + (tk & 3);
+      const int64_t rp = (b >= 0 && tp <= p) ? tp : p;
+      const uint16_t* kp = kbase + rp * KD + 8 * gq;
+#pragma unroll
+      for (int kk = 0; kk < NK; ++kk) kreg[st][kk] = ld16(kp + 32 * kk);
+    }
+    // ---- V rows of the tile's 32 tokens: straight from HBM into this wave's
+    // LDS tile (lane-ordered 1 KiB per instruction, chunk-swizzled)
+#pragma unroll
+    for (int u = 0; u < 32 / RPI; ++u) {
+      const int tk = RPI * u + lane / CH;
+      const int chunk = (lane % CH) ^ vswz(tk);
+      const int64_t b = bid(pb0 + (tk >> 2));
+      const int64_t tp = 4 * b + (tk & 3);
+      const int64_t rp = (b >= 0 && tp <= p) ? tp : p;
+      __builtin_amdgcn_global_load_lds(
+          (const __attribute__((address_space(1))) void*)(vbase + rp * KD + chunk * 8),
+          (__attribute__((address_space(3))) void*)(vt + u * 1024), 16, 0, 0);
+    }
+    // ---- S^T = K * Qbd: lane holds tokens 16st + 4gq + i for head l16
+    f32x4 sacc[2];
+#pragma unroll
+    for (int st = 0; st < 2; ++st) {
+      sacc[st] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kk = 0; kk < NK; ++kk)
+        sacc[st] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kreg[st][kk]),
+                                                           as_bf16x8(qb[kk]), sacc[st], 0, 0, 0);
+    }
+    float x[2][4];
+    float mt = -INFINITY;
+#pragma unroll
+    for (int st = 0; st < 2; ++st) {
+      const int64_t b = bid(pb0 + 4 * st + gq);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const bool ok = b >= 0 && 4 * b + i <= p;
+        x[st][i] = ok ? sacc[st][i] * scale_log2 : -INFINITY;
+        mt = fmaxf(mt, x[st][i]);
+      }
+    }
+    mt = fmaxf(mt, __shfl_xor(mt, 16));
+    mt = fmaxf(mt, __shfl_xor(mt, 32));
+    const float m_new = fmaxf(m_run, mt);
+    const bool any = m_new != -INFINITY;
+    const float alpha = any ? exp2f(m_run - m_new) : 1.0f;
+    float pr[2][4];
+    float psum = 0.0f;
+#pragma unroll
+    for (int st = 0; st < 2; ++st)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        pr[st][i] = any ? exp2f(x[st][i] - m_new) : 0.0f;
+        psum += pr[st][i];
+      }
+    l_run = l_run * alpha + psum;
+    m_run = m_new;
+#pragma unroll
+    for (int pp = 0; pp < NK; ++pp) {
+      oacc[pp][0] *= alpha;
+      oacc[pp][1] *= alpha;
+    }
+    u32x4 pv;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int st = e >> 1, i0 = 2 * (e & 1);
+      pv[e] = f32_to_bf16(pr[st][i0]) | (f32_to_bf16(pr[st][i0 + 1]) << 16);
+    }
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's V tile has landed in LDS
+    wave_sync();
+    // ---- O^T += V^T * P^T; k-slot (gq, e) <-> token (e<4 ? 4gq+e : 16+4gq+e-4)
+#pragma unroll
+    for (int pp = 0; pp < NK; ++pp) {
+      uint32_t w[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int tr = (e < 4) ? (4 * gq + e) : (16 + 4 * gq + e - 4);
+        const int chunk = (4 * pp + (l16 >> 2)) ^ vswz(tr);
+        w[e] = *reinterpret_cast<const uint32_t*>(vt + tr * ROWB + chunk * 16 + 4 * (l16 & 3));
+      }
+      u32x4 a0, a1;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        a0[e] = (w[2 * e] & 0xFFFFu) | (w[2 * e + 1] << 16);
+        a1[e] = (w[2 * e] >> 16) | (w[2 * e + 1] & 0xFFFF0000u);
+      }
+      oacc[pp][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a0), as_bf16x8(pv),
+                                                            oacc[pp][0], 0, 0, 0);
+      oacc[pp][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a1), as_bf16x8(pv),
+                                                            oacc[pp][1], 0, 0, 0);
+    }
+    wave_sync();  // all reads of this tile issued before the next tile's loads
+  }
+
+  // ---- merge the four waves' states: per head, M = max_w m_w,
+  // f_w = 2^(m_w - M) (waves without tokens skipped), Z = sum_w f_w l_w,
+  // O = sum_w f_w O_w, in wave order
+  l_run += __shfl_xor(l_run, 16);
+  l_run += __shfl_xor(l_run, 32);
+  __syncthreads();
+  float* mg = reinterpret_cast<float*>(lds);
+  float* my = mg + wave * MF;  // [m 16][l 16][o 16 x DP] (rows padded: no bank conflicts)
+  float* fac = mg + 4 * MF;    // [4 waves][16 heads]: f_w, or -1 when skipped
+  float* hz = fac + 4 * 16;    // [16] Z
+  float* hm = hz + 16;         // [16] M
+  if (gq == 0) {
+    my[l16] = m_run;
+    my[16 + l16] = l_run;
+  }
+  {
+    const int gn = l16 / G;
+#pragma unroll
+    for (int pp = 0; pp < NK; ++pp) {
+      if (pp / (D / 32) != gn) continue;
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int rel = 32 * pp + 8 * gq + 2 * i + h - gn * D;
+          my[32 + l16 * S::DP + rel] = oacc[pp][h][i];
+        }
+    }
+  }
+  __syncthreads();
+  // (all LDS reads hoisted out of the conditionals: they issue together)
+  if (threadIdx.x < 16) {
+    const int n = threadIdx.x;
+    float mw[4], lw[4], mx = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      mw[w] = mg[w * MF + n];
+      lw[w] = mg[w * MF + 16 + n];
+    }
+#pragma unroll
+    for (int w = 0; w < 4; ++w) mx = fmaxf(mx, mw[w]);
+    float z = 0.0f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      float f = -1.0f;
+      if (mw[w] != -INFINITY) {
+        f = exp2f(mw[w] - mx);
+        z += f * lw[w];
+      }
+      fac[w * 16 + n] = f;
+    }
+    hz[n] = z;
+    hm[n] = mx;
+  }
+  __syncthreads();
+  // four consecutive outputs (one head) per thread and pass
+  for (int q4 = threadIdx.x; q4 < 4 * D; q4 += 256) {
+    const int n = q4 / (D / 4);
+    const int dd = 4 * (q4 % (D / 4));
+    float fw[4];
+    f32x4 vw[4];
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      fw[w] = fac[w * 16 + n];
+      vw[w] = *reinterpret_cast<const f32x4*>(mg + w * MF + 32 + n * S::DP + dd);
+    }
+    f32x4 o = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      if (fw[w] < 0.0f) continue;
+      o[0] += fw[w] * vw[w][0];
+      o[1] += fw[w] * vw[w][1];
+      o[2] += fw[w] * vw[w][2];
+      o[3] += fw[w] * vw[w][3];
+    }
+    const float z = hz[n];
+    if (n_split == 1) {
+      const uint32_t lo = f32_to_bf16(o[0] / z) | (f32_to_bf16(o[1] / z) << 16);
+      const uint32_t hi = f32_to_bf16(o[2] / z) | (f32_to_bf16(o[3] / z) << 16);
+      *reinterpret_cast<uint2*>(out + (row * 16 + n) * D + dd) = make_uint2(lo, hi);
+      if (lse && dd == 0) lse[row * 16 + n] = (hm[n] + log2f(z)) * kLn2;
+    } else {
+      float* po = part + item * part_floats(D);
+      if constexpr (COHERENT) {
+        coherent_store(reinterpret_cast<unsigned long long*>(po + 32 + n * D + dd),
+                       (unsigned long long)__float_as_uint(o[0]) |
+                           ((unsigned long long)__float_as_uint(o[1]) << 32));
+        coherent_store(reinterpret_cast<unsigned long long*>(po + 32 + n * D + dd + 2),
+                       (unsigned long long)__float_as_uint(o[2]) |
+                           ((unsigned long long)__float_as_uint(o[3]) << 32));
+        if (dd == 0) {
+          coherent_store(&po[n], hm[n]);
+          coherent_store(&po[16 + n], z);
+        }
+      } else {
+        *reinterpret_cast<f32x4*>(po + 32 + n * D + dd) = o;
+        if (dd == 0) {
+          po[n] = hm[n];
+          po[16 + n] = z;
+        }
+      }
+    }
+  }
+}
+
+// Log-sum-exp merge of one (row, head, dim) over a row's split states, in
+// split order: M = max_k m_k, Z = sum_k 2^(m_k - M) l_k,
+// A = sum_k 2^(m_k - M) O_k (splits with m_k = -inf hold no token).
+// out = A / Z, lse = (M + log2 Z) ln 2.  The caller loads the states.
+__device__ __forceinline__ void lse_merge(const float (&m)[kMaxSplits],
+                                          const float (&z)[kMaxSplits],
+                                          const float (&o)[kMaxSplits], int n_split,
+                                          float& mx, float& zs, float& acc) {
+  mx = -INFINITY;
+#pragma unroll
+  for (int k = 0; k < kMaxSplits; ++k)
+    if (k < n_split) mx = fmaxf(mx, m[k]);
+  zs = 0.0f;
+  acc = 0.0f;
+#pragma unroll
+  for (int k = 0; k < kMaxSplits; ++k) {
+    if (k < n_split && m[k] != -INFINITY) {
+      const float f = exp2f(m[k] - mx);
+      zs += f * z[k];
+      acc += f * o[k];
+    }
+  }
+}
+
+}  // namespace qsa

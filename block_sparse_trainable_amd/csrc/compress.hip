@@ -6,14 +6,10 @@
 // Attention" gallery page, How block selection works: only complete blocks
 // are pooled, and the rotation uses the first position of each block.
 //
-// One wavefront builds one block: lane l owns dims 2l and 2l+1 of the
-// 128-dim key, reads its 4 B (bf16) or 8 B (fp32) of each of the block's 4
-// rows (a row is one coalesced 256 B / 512 B wave access), and the sum of
-// squares is a wave reduction.  All arithmetic is fp64 -- the work is a few
-// hundred flops per 1 KiB block and HBM-bound -- so the stored row is the
-// exact result rounded once.  Rotate-half pairs (j, j + rope_dims/2) live in
-// lanes l and l + rope_dims/4 and meet through one lane shuffle.
-#include "qsa_common.h"
+// Launcher: one wavefront per block (the per-wave arithmetic, fp64, is
+// compress_wave in compress_block.h); 4 waves per workgroup, a grid-stride
+// loop past 65535 workgroups.
+#include "compress_block.h"
 
 namespace qsa {
 namespace {
@@ -26,83 +22,15 @@ __global__ __launch_bounds__(256) void compress_kernel(
     const int32_t* __restrict__ len_after, const float* __restrict__ gain, double base,
     double eps, int rope_dims, void* __restrict__ k_cmp_v) {
   const int s = blockIdx.y;
-  const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int64_t cap_blocks = cap / 4;
   const int64_t lb = max(len_before[s], 0);
   const int64_t la = min((int64_t)max(len_after[s], 0), cap);
   const int64_t b_begin = lb / 4;
   const int64_t b_end = min(la / 4, cap_blocks);
-
-  const int d0 = 2 * lane;  // this lane's dims: d0, d0 + 1
   if (b_begin + (int64_t)blockIdx.x * kWaves >= b_end) return;  // nothing to build here
-  const int half = rope_dims / 2;
-  // role: 0 = not rotated, 1 = first member of a pair, 2 = second member
-  int role = 0, partner = lane;
-  double theta0 = 0.0, theta1 = 0.0;
-  if (d0 < half) {
-    role = 1;
-    partner = lane + rope_dims / 4;
-    theta0 = pow(base, -2.0 * (double)d0 / (double)rope_dims);
-    theta1 = pow(base, -2.0 * (double)(d0 + 1) / (double)rope_dims);
-  } else if (d0 < rope_dims) {
-    role = 2;
-    partner = lane - rope_dims / 4;
-    theta0 = pow(base, -2.0 * (double)(d0 - half) / (double)rope_dims);
-    theta1 = pow(base, -2.0 * (double)(d0 + 1 - half) / (double)rope_dims);
-  }
-  const double g0 = gain ? (double)gain[d0] : 1.0;
-  const double g1 = gain ? (double)gain[d0 + 1] : 1.0;
-
-  for (int64_t b = b_begin + (int64_t)blockIdx.x * kWaves + wave; b < b_end;
-       b += (int64_t)gridDim.x * kWaves) {
-    double p0 = 0.0, p1 = 0.0;
-    const int64_t row0 = ((int64_t)s * cap + 4 * b) * 128 + d0;
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      if constexpr (BF16) {
-        const uint32_t w =
-            *reinterpret_cast<const uint32_t*>(static_cast<const uint16_t*>(k_idx_v) + row0 + t * 128);
-        p0 += (double)bf16_to_f32(w & 0xFFFFu);
-        p1 += (double)bf16_to_f32(w >> 16);
-      } else {
-        const float2 w = *reinterpret_cast<const float2*>(static_cast<const float*>(k_idx_v) + row0 + t * 128);
-        p0 += (double)w.x;
-        p1 += (double)w.y;
-      }
-    }
-    p0 *= 0.25;
-    p1 *= 0.25;
-    double ss = p0 * p0 + p1 * p1;
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) ss += __shfl_xor(ss, off);
-    const double rms = sqrt(ss / 128.0 + eps);
-    const double n0 = p0 / rms * g0;
-    const double n1 = p1 / rms * g1;
-    const double o0 = __shfl(n0, partner);
-    const double o1 = __shfl(n1, partner);
-    double y0 = n0, y1 = n1;
-    if (role != 0) {
-      const double pos = (double)(4 * b);
-      double s0, c0, s1, c1;
-      sincos(pos * theta0, &s0, &c0);
-      sincos(pos * theta1, &s1, &c1);
-      if (role == 1) {
-        y0 = n0 * c0 - o0 * s0;
-        y1 = n1 * c1 - o1 * s1;
-      } else {
-        y0 = n0 * c0 + o0 * s0;
-        y1 = n1 * c1 + o1 * s1;
-      }
-    }
-    const int64_t orow = ((int64_t)s * cap_blocks + b) * 128 + d0;
-    if constexpr (BF16) {
-      const uint32_t w = f64_to_bf16(y0) | (f64_to_bf16(y1) << 16);
-      *reinterpret_cast<uint32_t*>(static_cast<uint16_t*>(k_cmp_v) + orow) = w;
-    } else {
-      *reinterpret_cast<float2*>(static_cast<float*>(k_cmp_v) + orow) = make_float2((float)y0, (float)y1);
-    }
-  }
+  compress_wave<BF16>(k_idx_v, cap, s, b_begin + (int64_t)blockIdx.x * kWaves + wave, b_end,
+                      (int64_t)gridDim.x * kWaves, gain, base, eps, rope_dims, k_cmp_v);
 }
 
 }  // namespace

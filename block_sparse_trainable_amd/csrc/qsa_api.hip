@@ -145,6 +145,7 @@ qsa_status qsa_workspace_size(const qsa_config* cfg, int32_t op, int32_t batch, 
     case QSA_OP_SELECT: *bytes = select_ws(d, batch, n_q, max_pos_end); break;
     case QSA_OP_PREFILL: *bytes = qsa::attn_workspace_bytes(d, batch * n_q, false); break;
     case QSA_OP_DECODE: *bytes = qsa::attn_workspace_bytes(d, batch, true); break;
+    case QSA_OP_DECODE_STEP: *bytes = qsa::step_plan(d, batch, max_pos_end).bytes; break;
     default: return fail(QSA_ERR_INVALID_ARGUMENT, "%s: unknown op %d", fn, op);
   }
   return ok();
@@ -259,6 +260,57 @@ qsa_status qsa_sparse_attn_decode(const qsa_config* cfg, int32_t batch, const vo
   return attn_common("qsa_sparse_attn_decode", cfg, batch, 1, q, k_cache, v_cache, cap_tokens,
                      q_pos, max_pos_end, sel_blocks, sel_count, out, lse, workspace,
                      workspace_bytes, true, stream);
+}
+
+qsa_status qsa_decode_step(const qsa_config* cfg, int32_t batch, const void* q_idx,
+                           const void* q, const void* k_idx, void* k_cmp,
+                           const float* rms_gain, const void* k_cache, const void* v_cache,
+                           int64_t cap_tokens, const int32_t* q_pos, int32_t max_pos_end,
+                           int32_t* sel_blocks, int32_t* sel_count, float* sel_scores,
+                           void* out, float* lse, void* workspace, size_t workspace_bytes,
+                           hipStream_t stream) {
+  const char* fn = "qsa_decode_step";
+  qsa::Dims d;
+  qsa_status st = check_config(fn, cfg, &d);
+  if (st != QSA_OK) return st;
+  st = check_sizes(fn, batch, 1, cap_tokens, max_pos_end);
+  if (st != QSA_OK) return st;
+  if (!qsa::decode_step_layout_ok(d))
+    return fail(QSA_ERR_UNSUPPORTED,
+                "%s: needs bf16, idx_heads 4 and 16 query heads with (kv_heads, head_dim) in "
+                "{(2,128), (2,64), (1,128)}",
+                fn);
+  if (batch > qsa::kStepMaxBatch)
+    return fail(QSA_ERR_UNSUPPORTED, "%s: batch %d (at most %d)", fn, batch, qsa::kStepMaxBatch);
+  if ((int64_t)(max_pos_end - 1) / d.r > qsa::kStepMaxBlocks)
+    return fail(QSA_ERR_UNSUPPORTED, "%s: max_pos_end %d (at most %lld candidate blocks)", fn,
+                max_pos_end, (long long)qsa::kStepMaxBlocks);
+  QSA_REQUIRE_PTR(q_idx, 16);
+  QSA_REQUIRE_PTR(q, 16);
+  QSA_REQUIRE_PTR(k_idx, 8);
+  QSA_REQUIRE_PTR(k_cmp, 16);
+  QSA_REQUIRE_PTR(k_cache, 16);
+  QSA_REQUIRE_PTR(v_cache, 16);
+  QSA_REQUIRE_PTR(q_pos, 4);
+  QSA_REQUIRE_PTR(sel_blocks, 4);
+  QSA_REQUIRE_PTR(sel_count, 4);
+  QSA_REQUIRE_PTR(out, 4);
+  if (rms_gain && !aligned(rms_gain, 8))
+    return fail(QSA_ERR_INVALID_ARGUMENT, "%s: rms_gain must be 8-byte aligned", fn);
+  if (sel_scores && !aligned(sel_scores, 4))
+    return fail(QSA_ERR_INVALID_ARGUMENT, "%s: sel_scores must be 4-byte aligned", fn);
+  if (lse && !aligned(lse, 4))
+    return fail(QSA_ERR_INVALID_ARGUMENT, "%s: lse must be 4-byte aligned", fn);
+  const qsa::StepPlan pl = qsa::step_plan(d, batch, max_pos_end);
+  if (!workspace || workspace_bytes < pl.bytes)
+    return fail(QSA_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn, pl.bytes,
+                workspace ? workspace_bytes : (size_t)0);
+  if (!aligned16(workspace))
+    return fail(QSA_ERR_INVALID_ARGUMENT, "%s: workspace must be 16-byte aligned", fn);
+  return launched(fn, qsa::launch_decode_step(d, pl, batch, q_idx, q, k_idx, k_cmp, rms_gain,
+                                              k_cache, v_cache, cap_tokens, q_pos, sel_blocks,
+                                              sel_count, sel_scores, out, lse, workspace,
+                                              stream));
 }
 
 }  // extern "C"

@@ -158,6 +158,50 @@ hipError_t launch_select(const Dims& d, const SelectPlan& pl, int batch, int n_q
                          const int32_t* q_pos0, int64_t cap, void* workspace, int32_t* sel,
                          int32_t* cnt, float* sel_scores, hipStream_t st);
 
+// ------------------------------------------------------ fused decode step ----
+// Score segments of 1024 blocks (a row's last segment also takes a remainder
+// of up to 512 blocks); an id bitmap sized for rows of up to kStepBmWords * 32
+// candidate blocks; a fixed control area at the start of the workspace holds
+// the completion counters, the error word and the per-row selection records
+// of up to kStepMaxBatch rows.
+constexpr int kStepSeg = 1024;
+constexpr int kStepSegMax = kStepSeg + kStepSeg / 2;
+constexpr int kStepBmWords = 8256;
+constexpr int64_t kStepMaxBlocks = (int64_t)kStepBmWords * 32;       // 264,192
+constexpr int kStepMaxBatch = 1024;
+constexpr int kStepRecStride = 528;      // record words per row (>= k_B + 1)
+constexpr int kStepOffAttn = 1024;       // control-area word offsets
+constexpr int kStepOffErr = 2048;
+constexpr int kStepOffRec = 4096;
+constexpr size_t kStepCtlBytes = 4 * ((size_t)kStepOffRec + (size_t)kStepMaxBatch * kStepRecStride);
+// Sequences per launch: keeps the attention workgroups that may wait for a
+// selection to at most 256, half of the device's resident capacity.
+constexpr int kStepMaxWaiting = 256;
+
+// Score segments of a row with c candidate blocks: 1024 each, the last one
+// also holding a remainder of up to 512 (non-decreasing in c).
+__host__ __device__ inline int step_nseg(int64_t c) {
+  const int64_t full = c / kStepSeg, rem = c % kStepSeg;
+  if (full == 0) return 1;
+  return (int)((rem <= kStepSeg / 2) ? full : full + 1);
+}
+constexpr int kStepMaxSegs = (int)(kStepMaxBlocks / kStepSeg);        // 258
+
+struct StepPlan {
+  int64_t c_max;     // largest candidate count, floor((max_pos_end - 1) / r)
+  int n_seg;         // score segments per row
+  int n_split;       // attention splits per row
+  size_t off_pairs, off_cum, off_part, bytes;
+};
+StepPlan step_plan(const Dims& d, int batch, int32_t max_pos_end);
+bool decode_step_layout_ok(const Dims& d);
+hipError_t launch_decode_step(const Dims& d, const StepPlan& pl, int batch, const void* q_idx,
+                              const void* q, const void* k_idx, void* k_cmp, const float* gain,
+                              const void* k_cache, const void* v_cache, int64_t cap,
+                              const int32_t* q_pos, int32_t* sel, int32_t* cnt,
+                              float* sel_scores, void* out, float* lse, void* workspace,
+                              hipStream_t st);
+
 // Decode attention workspace: the per-split partial states.
 size_t attn_workspace_bytes(const Dims& d, int rows, bool decode);
 

@@ -27,13 +27,13 @@
 // than the LDS capacity, it falls back to an exact radix select over the
 // whole row in global memory.
 #include "qsa_common.h"
+#include "select_common.h"
 
 namespace qsa {
 namespace {
 
 constexpr int kThreads = 512;
 constexpr int kWaves = kThreads / 64;
-constexpr int kRadixBins = 2048;
 constexpr int64_t kFilterSeg = 8192; // scores per filter segment of a long row
 constexpr uint32_t kOverflow = 0xFFFFFFFFu;
 
@@ -41,97 +41,12 @@ __device__ __forceinline__ uint32_t key_of(uint32_t bits) {
   return (bits & 0x80000000u) ? 0u : bits;  // scores are >= 0; guard anyway
 }
 
-// Exclusive prefix sum over the workgroup in thread order; total in *total.
-// Contains two barriers.
-__device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* scratch,
-                                                    uint32_t* total) {
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  uint32_t incl = v;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const uint32_t t = __shfl_up(incl, off);
-    if (lane >= off) incl += t;
-  }
-  if (lane == 63) scratch[wave] = incl;
-  __syncthreads();
-  uint32_t before = 0, all = 0;
-#pragma unroll
-  for (int w = 0; w < kWaves; ++w) {
-    const uint32_t t = scratch[w];
-    before += (w < wave) ? t : 0u;
-    all += t;
-  }
-  __syncthreads();
-  *total = all;
-  return before + incl - v;
-}
-
-struct Radix {
-  uint32_t prefix, mask, need;
-};
-
-// MSB-first radix select over n keys (key(i)), counting only keys with
-// elig(i).  Returns (prefix, mask, need): among eligible keys, those with
-// (k & mask) > prefix number need_in - need, and the `need` lowest-index
-// eligible keys with (k & mask) == prefix complete the top need_in.
-template <class KeyFn, class EligFn>
-__device__ Radix radix_select(KeyFn key, EligFn elig, int64_t n, uint32_t need_in,
-                              uint32_t* hist, uint32_t* scratch, int first_pass = 0,
-                              uint32_t prefix0 = 0u, uint32_t mask0 = 0u) {
-  const int tid = threadIdx.x;
-  Radix r{prefix0, mask0, need_in};
-  const int shifts[3] = {20, 9, 0};
-  const int widths[3] = {11, 11, 9};
-  for (int pass = first_pass; pass < 3; ++pass) {
-    const int sh = shifts[pass];
-    const int nb = 1 << widths[pass];
-    const uint32_t dmask = (uint32_t)nb - 1u;
-    for (int i = tid; i < nb; i += kThreads) hist[i] = 0;
-    __syncthreads();
-    for (int64_t i = tid; i < n; i += kThreads) {
-      if (!elig(i)) continue;
-      const uint32_t k = key(i);
-      if ((k & r.mask) == r.prefix) atomicAdd(&hist[(k >> sh) & dmask], 1u);
-    }
-    __syncthreads();
-    const int per = nb / kThreads;  // thread t owns the bins just below nb - t*per
-    const int hi = nb - tid * per;
-    uint32_t local = 0;
-    for (int e = hi - 1; e >= hi - per; --e) local += hist[e];
-    uint32_t tot;
-    const uint32_t above = block_excl_scan(local, scratch, &tot);
-    if (above < r.need && r.need <= above + local) {
-      uint32_t acc = above;
-      for (int e = hi - 1; e >= hi - per; --e) {
-        if (acc + hist[e] >= r.need) {
-          scratch[kWaves] = (uint32_t)e;
-          scratch[kWaves + 1] = acc;
-          scratch[kWaves + 2] = hist[e];
-          break;
-        }
-        acc += hist[e];
-      }
-    }
-    __syncthreads();
-    const uint32_t d = scratch[kWaves];
-    const uint32_t above_d = scratch[kWaves + 1];
-    const uint32_t in_d = scratch[kWaves + 2];
-    __syncthreads();
-    r.need -= above_d;
-    r.prefix |= d << sh;
-    r.mask |= dmask << sh;
-    if (in_d == r.need) break;  // every eligible key with this prefix is kept
-  }
-  return r;
-}
-
 // Exact selection over a whole row of c keys in global memory (fallback).
-__device__ void select_row_global(const uint32_t* bits, int64_t c, int kB, int32_t* out,
+__device__ __forceinline__ void select_row_global(const uint32_t* bits, int64_t c, int kB, int32_t* out,
                                   float* outs, uint32_t* hist, uint32_t* scratch) {
   auto key = [&](int64_t i) { return key_of(bits[i]); };
   auto all = [&](int64_t) { return true; };
-  const Radix r = radix_select(key, all, c, (uint32_t)kB, hist, scratch);
+  const Radix r = radix_select<kThreads>(key, all, c, (uint32_t)kB, hist, scratch);
   uint32_t gt_seen = 0, eq_seen = 0;
   const int tid = threadIdx.x;
   for (int64_t base = 0; base < c; base += 4 * kThreads) {
@@ -146,7 +61,7 @@ __device__ void select_row_global(const uint32_t* bits, int64_t c, int kB, int32
       neq += (i0 + e < c && m == r.prefix) ? 1u : 0u;
     }
     uint32_t tot;
-    const uint32_t ex = block_excl_scan((ngt << 16) | neq, scratch, &tot);
+    const uint32_t ex = block_excl_scan<kThreads>((ngt << 16) | neq, scratch, &tot);
     uint32_t gt_before = gt_seen + (ex >> 16);
     uint32_t eq_before = eq_seen + (ex & 0xFFFFu);
 #pragma unroll
@@ -271,7 +186,7 @@ __global__ __launch_bounds__(kThreads) void filter_select_kernel(FilterArgs a) {
       }
     }
     uint32_t tot;
-    const uint32_t above = block_excl_scan(lo + hi, scratch, &tot);
+    const uint32_t above = block_excl_scan<kThreads>(lo + hi, scratch, &tot);
     if (tid < kHistWords && above < (uint32_t)kB && (uint32_t)kB <= above + lo + hi) {
       const int w = kHistWords - 1 - tid;
       if (above + hi >= (uint32_t)kB) {      // bin 2w+1 holds the k_B-th key
@@ -320,7 +235,7 @@ __global__ __launch_bounds__(kThreads) void filter_select_kernel(FilterArgs a) {
       sum += v[e];
     }
     uint32_t tot;
-    uint32_t run = block_excl_scan(sum, scratch, &tot);
+    uint32_t run = block_excl_scan<kThreads>(sum, scratch, &tot);
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int64_t g = 4 * tid + e;
@@ -429,10 +344,10 @@ __global__ __launch_bounds__(kThreads) void filter_select_kernel(FilterArgs a) {
     auto elig = [&](int64_t i) { return score_bin(ckey[i]) == dstar; };
     if (dstar > 0u && dstar < (uint32_t)kHistBins - 1u) {
       // an unclamped bin fixes bits 30..20 of its keys: start at the second digit
-      r = radix_select(key, elig, (int64_t)total, need, hist, scratch, 1, (dstar + 888u) << 20,
+      r = radix_select<kThreads>(key, elig, (int64_t)total, need, hist, scratch, 1, (dstar + 888u) << 20,
                        0x7FFu << 20);
     } else {
-      r = radix_select(key, elig, (int64_t)total, need, hist, scratch);
+      r = radix_select<kThreads>(key, elig, (int64_t)total, need, hist, scratch);
     }
   }
   // ordered output: bin > d* always; bin == d* by (k & mask) vs prefix
@@ -455,7 +370,7 @@ __global__ __launch_bounds__(kThreads) void filter_select_kernel(FilterArgs a) {
     }
     // ties: the first r.need equal keys (index order) are kept
     uint32_t tot_eq;
-    const uint32_t ex_eq = block_excl_scan((uint32_t)__popc(eqm), scratch, &tot_eq);
+    const uint32_t ex_eq = block_excl_scan<kThreads>((uint32_t)__popc(eqm), scratch, &tot_eq);
     uint32_t eq_rank = eq_seen + ex_eq;
 #pragma unroll
     for (int e = 0; e < 8; ++e)
@@ -464,7 +379,7 @@ __global__ __launch_bounds__(kThreads) void filter_select_kernel(FilterArgs a) {
         ++eq_rank;
       }
     uint32_t tot;
-    const uint32_t ex = block_excl_scan((uint32_t)__popc(take), scratch, &tot);
+    const uint32_t ex = block_excl_scan<kThreads>((uint32_t)__popc(take), scratch, &tot);
     uint32_t pos = written + ex;
 #pragma unroll
     for (int e = 0; e < 8; ++e)

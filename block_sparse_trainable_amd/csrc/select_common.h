@@ -1,0 +1,104 @@
+// Workgroup-wide scan and MSB-first radix select used by the selection
+// kernels ("QSA (Qwen Sparse Attention)", Key math / How it works, (A): the
+// top-k_B blocks by importance).  Templated on the workgroup size NT (a
+// multiple of 64, at most 512).
+#pragma once
+
+#include "qsa_common.h"
+
+namespace qsa {
+
+constexpr int kRadixBins = 2048;
+
+// Exclusive prefix sum over the workgroup in thread order; total in *total.
+// scratch holds NT/64 words.  Contains two barriers.
+template <int NT>
+__device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* scratch,
+                                                    uint32_t* total) {
+  constexpr int NW = NT / 64;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  uint32_t incl = v;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const uint32_t t = __shfl_up(incl, off);
+    if (lane >= off) incl += t;
+  }
+  if (lane == 63) scratch[wave] = incl;
+  __syncthreads();
+  uint32_t before = 0, all = 0;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    const uint32_t t = scratch[w];
+    before += (w < wave) ? t : 0u;
+    all += t;
+  }
+  __syncthreads();
+  *total = all;
+  return before + incl - v;
+}
+
+// Result of a radix select: among eligible keys, those with
+// (k & mask) > prefix number need_in - need; `avail` keys have
+// (k & mask) == prefix, and `need` of them (need <= avail) complete the top
+// need_in.  avail == need means every key with the prefix is kept.
+struct Radix {
+  uint32_t prefix, mask, need, avail;
+};
+
+// MSB-first radix select (11/11/9-bit digits over key bits 30..0) over n keys
+// key(i), counting only keys with elig(i).  first_pass > 0 starts at a later
+// digit with the bits above it already fixed to prefix0/mask0.  hist holds
+// kRadixBins words, scratch NT/64 + 3.
+template <int NT, class KeyFn, class EligFn>
+__device__ Radix radix_select(KeyFn key, EligFn elig, int64_t n, uint32_t need_in,
+                              uint32_t* hist, uint32_t* scratch, int first_pass = 0,
+                              uint32_t prefix0 = 0u, uint32_t mask0 = 0u) {
+  constexpr int NW = NT / 64;
+  const int tid = threadIdx.x;
+  Radix r{prefix0, mask0, need_in, 0xFFFFFFFFu};
+  for (int pass = first_pass; pass < 3; ++pass) {
+    const int sh = pass == 0 ? 20 : (pass == 1 ? 9 : 0);  // digits: bits 30..20, 19..9, 8..0
+    const int nb = pass == 2 ? 512 : 2048;
+    const uint32_t dmask = (uint32_t)nb - 1u;
+    for (int i = tid; i < nb; i += NT) hist[i] = 0;
+    __syncthreads();
+    for (int64_t i = tid; i < n; i += NT) {
+      if (!elig(i)) continue;
+      const uint32_t k = key(i);
+      if ((k & r.mask) == r.prefix) atomicAdd(&hist[(k >> sh) & dmask], 1u);
+    }
+    __syncthreads();
+    const int per = nb / NT;  // thread t owns the bins just below nb - t*per
+    const int hi = nb - tid * per;
+    uint32_t local = 0;
+    for (int e = hi - 1; e >= hi - per; --e) local += hist[e];
+    uint32_t tot;
+    const uint32_t above = block_excl_scan<NT>(local, scratch, &tot);
+    if (above < r.need && r.need <= above + local) {
+      uint32_t acc = above;
+      for (int e = hi - 1; e >= hi - per; --e) {
+        if (acc + hist[e] >= r.need) {
+          scratch[NW] = (uint32_t)e;
+          scratch[NW + 1] = acc;
+          scratch[NW + 2] = hist[e];
+          break;
+        }
+        acc += hist[e];
+      }
+    }
+    __syncthreads();
+    const uint32_t d = scratch[NW];
+    const uint32_t above_d = scratch[NW + 1];
+    const uint32_t in_d = scratch[NW + 2];
+    __syncthreads();
+    r.need -= above_d;
+    r.prefix |= d << sh;
+    r.mask |= dmask << sh;
+    r.avail = in_d;
+    if (in_d == r.need) break;  // every eligible key with this prefix is kept
+  }
+  return r;
+}
+
+}  // namespace qsa

@@ -161,6 +161,36 @@ class DeviceLayer:
         self.attend_decode(q_s[t], pos_t[t], max_pos_end, sel, cnt, out, lse)
         return outputs
 
+    def step_workspace(self, max_pos_end: int) -> torch.Tensor:
+        """Zero-filled workspace of the fused decode step (its counters must
+        start at zero; every completed call leaves them zero)."""
+        n = B.qsa_workspace_size(self.cfg, B.QSA_OP_DECODE_STEP, self.batch, 1, max_pos_end)
+        ws = self._ws.get("step")
+        if ws is None or ws.numel() < n:
+            ws = torch.zeros(n, dtype=torch.uint8, device=self.device)
+            self._ws["step"] = ws
+        return ws
+
+    def decode_step_fused(self, plan, t: int, outputs, ws=None):
+        """The same decode step as decode_step, in one launch (qsa_decode_step)."""
+        q_idx_s, q_s, pos_t, pos1_t, max_pos_end = plan
+        sel, cnt, scs, out, lse = outputs
+        ws = self.step_workspace(max_pos_end) if ws is None else ws
+        B.qsa_decode_step(self.cfg, self.batch, q_idx_s[t], q_s[t], self.k_idx, self.k_cmp,
+                          self.gain, self.k, self.v, self.cap, pos_t[t], int(max_pos_end),
+                          sel[:, 0], cnt[:, 0], scs[:, 0], out, lse, ws, ws.numel())
+        return outputs
+
+    def capture_decode_fused(self, plan, steps: int, outputs):
+        """Capture `steps` fused decode steps into one HIP graph."""
+        ws = self.step_workspace(plan[4])
+        g = torch.cuda.CUDAGraph()
+        torch.cuda.synchronize(self.device)
+        with torch.cuda.graph(g):
+            for t in range(steps):
+                self.decode_step_fused(plan, t, outputs, ws)
+        return g
+
     def capture_decode(self, plan, steps: int, outputs, overlap_build: bool = False,
                        branches: int = 1):
         """Capture `steps` decode steps into one HIP graph (torch.cuda.CUDAGraph).

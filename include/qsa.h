@@ -56,7 +56,8 @@ typedef enum {
   QSA_OP_INDEX_BUILD = 0,
   QSA_OP_SELECT = 1,
   QSA_OP_PREFILL = 2,
-  QSA_OP_DECODE = 3
+  QSA_OP_DECODE = 3,
+  QSA_OP_DECODE_STEP = 4
 } qsa_op;
 
 /* Layer configuration.  Supported values are listed per field; anything
@@ -186,11 +187,50 @@ qsa_status qsa_sparse_attn_decode(const qsa_config* cfg, int32_t batch, const vo
                                   void* out, float* lse, void* workspace,
                                   size_t workspace_bytes, hipStream_t stream);
 
+/* qsa_decode_step -- one whole decode step in a single launch:
+ * qsa_index_build of the block the new token may complete (len_before =
+ * q_pos, len_after = q_pos + 1), qsa_select_topk for the new token (n_q = 1)
+ * and qsa_sparse_attn_decode, with results bit-identical to those three
+ * calls.  [concept] (A) and (B), and the decode-phase report under "Why it
+ * matters"; [gallery] "How block selection works".  The stages hand their
+ * data to each other inside the launch (score -> selection -> attention ->
+ * split merge) instead of across kernel boundaries.
+ *
+ *   q_idx      (dtype) [batch][idx_heads][idx_dim] indexer query of the new
+ *              token of each sequence.
+ *   q          (dtype) [batch][q_heads][head_dim] its main query.
+ *   k_idx, k_cmp, rms_gain   as in qsa_index_build; k_idx row q_pos[s] holds
+ *              the new token's raw indexer key.  Only the completed block's
+ *              row of k_cmp is written (it is not a candidate of this step).
+ *   k_cache, v_cache, cap_tokens, q_pos, max_pos_end   as in
+ *              qsa_sparse_attn_decode (the new token's K/V rows written).
+ *   sel_blocks, sel_count, sel_scores   as in qsa_select_topk with n_q = 1.
+ *   out, lse   as in qsa_sparse_attn_decode.
+ *   workspace  >= qsa_workspace_size(QSA_OP_DECODE_STEP, batch, 1,
+ *              max_pos_end) bytes.  Its first 2,179,072 bytes are a control
+ *              area (completion counters, per-row selection records, an error
+ *              word) that must be ZERO-FILLED BEFORE ITS FIRST USE; every
+ *              completed call leaves it zero again.  Word 2048 (byte 8192) is
+ *              the error word: 1 if a wait for a selection ever gave up
+ *              (never expected; the outputs of that call are then invalid).
+ * Supported: dtype bf16, idx_heads 4, q_heads 16 with (kv_heads, head_dim)
+ * in {(2,128), (2,64), (1,128)}, batch <= 1024 and floor((max_pos_end-1)/r)
+ * <= 264192 (contexts up to 1,056,768 tokens); anything else returns
+ * QSA_ERR_UNSUPPORTED and the three separate calls apply.                  */
+qsa_status qsa_decode_step(const qsa_config* cfg, int32_t batch, const void* q_idx,
+                           const void* q, const void* k_idx, void* k_cmp,
+                           const float* rms_gain, const void* k_cache, const void* v_cache,
+                           int64_t cap_tokens, const int32_t* q_pos, int32_t max_pos_end,
+                           int32_t* sel_blocks, int32_t* sel_count, float* sel_scores,
+                           void* out, float* lse, void* workspace, size_t workspace_bytes,
+                           hipStream_t stream);
+
 /* Workspace bytes needed by op (a qsa_op) for these sizes.  n_q is 1 for
- * QSA_OP_DECODE; QSA_OP_INDEX_BUILD needs none.  The select workspace
- * holds the materialised score rows, per-segment score histograms and the
- * candidate hand-over area of long rows; it carries no state between
- * calls.  Alignment: tensors read with 16-byte vector loads (q_idx, k_cmp
+ * QSA_OP_DECODE and QSA_OP_DECODE_STEP; QSA_OP_INDEX_BUILD needs none.  The
+ * select workspace holds the materialised score rows, per-segment score
+ * histograms and the candidate hand-over area of long rows; it carries no
+ * state between calls (the decode-step workspace does: see above).
+ * Alignment: tensors read with 16-byte vector loads (q_idx, k_cmp
  * in select, q, k_cache, v_cache, workspaces) must be 16-byte aligned, the
  * others 4- or 8-byte aligned as the validation messages state.           */
 qsa_status qsa_workspace_size(const qsa_config* cfg, int32_t op, int32_t batch, int32_t n_q,

@@ -167,3 +167,50 @@ def test_product_has_no_oracle_dependency():
         for f in files:
             if f.endswith((".py", ".hip", ".h", ".cpp")):
                 assert not pat.search(open(os.path.join(dirpath, f)).read()), f
+
+
+def test_decode_step_workspace_size(lib):
+    c = cfg()
+    # 2,179,072-byte control area, then (score, id) pairs of the score
+    # segments (room for 1536 each: 1024 plus a remainder of up to 512),
+    # per-segment suffix counts (128 words), 17 split states of 16 x (128 + 2)
+    batch, mpe = 8, 262211
+    c_max = (mpe - 1) // 4
+    full, rem = divmod(c_max, 1024)
+    nseg = full if rem <= 512 else full + 1
+    want = _al(4 * (4096 + 1024 * 528))
+    want = _al(want + 8 * batch * nseg * 1536)
+    want = _al(want + 4 * batch * nseg * 128)
+    want = _al(want + 4 * batch * 17 * (16 * 128 + 32))
+    assert nseg == 64
+    assert qsa.qsa_workspace_size(c, B.QSA_OP_DECODE_STEP, batch, 1, mpe) == want
+
+
+def _step(c, batch=2, mpe=64, ws_bytes=1 << 24, **ptr):
+    p = dict(q_idx=FAKE, q=FAKE, k_idx=FAKE, k_cmp=FAKE, gain=None, k=FAKE, v=FAKE, pos=FAKE,
+             sel=FAKE, cnt=FAKE, scs=None, out=FAKE, lse=None, ws=FAKE)
+    p.update(ptr)
+    qsa.qsa_decode_step(c, batch, p["q_idx"], p["q"], p["k_idx"], p["k_cmp"], p["gain"], p["k"],
+                        p["v"], 1 << 21, p["pos"], mpe, p["sel"], p["cnt"], p["scs"], p["out"],
+                        p["lse"], p["ws"], ws_bytes, stream=0)
+
+
+@pytest.mark.parametrize("kw,args,status,word", [
+    (dict(dtype=B.QSA_F32), {}, B.QSA_ERR_UNSUPPORTED, "bf16"),
+    (dict(idx_heads=2), {}, B.QSA_ERR_UNSUPPORTED, "idx_heads"),
+    (dict(q_heads=32, kv_heads=2), {}, B.QSA_ERR_UNSUPPORTED, "16 query heads"),
+    ({}, dict(batch=1025), B.QSA_ERR_UNSUPPORTED, "batch"),
+    ({}, dict(mpe=4 * 264192 + 5), B.QSA_ERR_UNSUPPORTED, "candidate blocks"),
+    ({}, dict(ws_bytes=100), B.QSA_ERR_WORKSPACE, "workspace"),
+    ({}, dict(q_idx=FAKE + 8), B.QSA_ERR_INVALID_ARGUMENT, "q_idx"),
+    ({}, dict(k_cmp=None), B.QSA_ERR_INVALID_ARGUMENT, "k_cmp"),
+    ({}, dict(pos=FAKE + 2), B.QSA_ERR_INVALID_ARGUMENT, "q_pos"),
+])
+def test_decode_step_rejects_before_launch(lib, kw, args, status, word):
+    c = cfg(**kw)
+    ptr = {k: v for k, v in args.items() if k not in ("batch", "mpe", "ws_bytes")}
+    size = {k: v for k, v in args.items() if k in ("batch", "mpe", "ws_bytes")}
+    with pytest.raises(B.QsaError) as e:
+        _step(c, **size, **ptr)
+    assert e.value.status == status
+    assert word in str(e.value)

@@ -333,3 +333,29 @@ def test_long_rows_split_filter_matches_oracle():
     for s in range(2):
         for j in range(3):
             assert int(x.target_block[s, j]) in set(sel[s, j].tolist())
+
+
+def test_decode_single_split_budget_matches_oracle():
+    say("decode with k_B = 16 (one attention split, no merge pass)")
+    lay = synth.Layout(token_budget=64)
+    x = synth.decode(context=3000, batch=2, steps=3, n_needles=4, layout=lay)
+    dl = DeviceLayer(x)
+    dl.build_prefix(x.cache_len)
+    plan = dl.decode_plan(3)
+    outs = dl.alloc_decode_outputs()
+    scale = 1.0 / math.sqrt(lay.head_dim)
+    for t in range(3):
+        dl.decode_step(plan, t, outs)
+        torch.cuda.synchronize()
+        sel, cnt, scs, out, lse = outs
+        for s in range(2):
+            p = int(x.q_pos0[s]) + t
+            kh = C.oracle_khat(x, s, p // 4 + 1)
+            K, V = C.f64(x.k[s], "bf16"), C.f64(x.v[s], "bf16")
+            q_idx, q = C.f64(x.q_idx[s, t], "bf16"), C.f64(x.q[s, t], "bf16")
+            res = O.qsa_row(p, q_idx, q, kh, K, V, k_B=lay.k_blocks, attend=False)
+            n = int(cnt[s, 0])
+            C.check_selection(res, sel[s, 0].cpu().numpy(), n, scs[s, 0].cpu().numpy(),
+                              lay.k_blocks)
+            C.check_attention(p, sel[s, 0, :n].cpu().numpy(), q, K, V, to_f32(out[s]),
+                              lse[s].cpu().numpy(), scale, "bf16")
