@@ -51,13 +51,19 @@ ATTN_COUNTERS = {
 }
 
 
-def attn_traffic_bytes():
+def attn_source_digest() -> str:
+    """sha1 over the sources the prefill attention kernel is compiled from."""
     import hashlib
-    src = os.path.join(ROOT, "block_sparse_trainable_amd", "csrc", "attn.hip")
-    with open(src, "rb") as f:
-        sha = hashlib.sha1(f.read()).hexdigest()
+    h = hashlib.sha1()
+    for f in ("attn.hip", "attn_tile.h", "qsa_common.h"):
+        with open(os.path.join(ROOT, "block_sparse_trainable_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def attn_traffic_bytes():
     c = ATTN_COUNTERS
-    if sha != c["source_sha1"]:
+    if attn_source_digest() != c["source_sha1"]:
         return None
     return (c["fetch_kib"] * c["fetch_scale"] + c["write_kib"] * c["write_scale"]) * 1024.0
 

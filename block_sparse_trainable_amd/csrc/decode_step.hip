@@ -42,15 +42,17 @@
 //       finish clears the record and merges the states (log-sum-exp).
 //
 // Forward progress: a score workgroup never waits, and a launch holds at most
-// kStepMaxWaiting attention workgroups (larger batches are split over
-// several launches), half of what the device keeps resident at 2 workgroups
-// per CU, so they cannot crowd out the score workgroups: every score
+// as many attention workgroups (which wait) as the device keeps resident
+// minus 64 (measured occupancy x CUs; larger batches are split over several
+// launches), so they cannot crowd out the score workgroups: every score
 // workgroup is eventually resident and every record is eventually written.
 // The spin is bounded all the same; on expiry the workgroup records an error
 // word in the workspace and proceeds (wrong values, no hang).
 //
 // The control area at the start of the workspace must be zero-filled before
 // its first use; every completed call leaves it zero.
+#include <atomic>
+
 #include "attn_tile.h"
 #include "compress_block.h"
 #include "select_common.h"
@@ -758,6 +760,25 @@ bool decode_step_layout_ok(const Dims& d) {
           (d.kv_heads == 1 && d.head_dim == 128));
 }
 
+// Workgroups of the fused kernel the current device keeps resident
+// (occupancy x CUs), cached per device.
+template <int HKV, int D>
+int step_capacity() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+  int cap = cache[dev].load(std::memory_order_relaxed);
+  if (cap > 0) return cap;
+  int per_cu = 0, cus = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_step_kernel<HKV, D>, kNT, 0) !=
+          hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return 0;
+  cap = per_cu * cus;
+  cache[dev].store(cap, std::memory_order_relaxed);
+  return cap;
+}
+
 hipError_t launch_decode_step(const Dims& d, const StepPlan& pl, int batch, const void* q_idx,
                               const void* q, const void* k_idx, void* k_cmp, const float* gain,
                               const void* k_cache, const void* v_cache, int64_t cap,
@@ -768,7 +789,12 @@ hipError_t launch_decode_step(const Dims& d, const StepPlan& pl, int batch, cons
   const int D = d.head_dim;
   const int64_t KD = (int64_t)d.kv_heads * D;
   const int64_t cap_blocks = cap / d.r;
-  const int per_launch = max(1, kStepMaxWaiting / pl.n_split);
+  int capacity = 0;
+  if (d.kv_heads == 2 && D == 128) capacity = step_capacity<2, 128>();
+  else if (d.kv_heads == 1 && D == 128) capacity = step_capacity<1, 128>();
+  else if (d.kv_heads == 2 && D == 64) capacity = step_capacity<2, 64>();
+  if (capacity - 64 < pl.n_split) return hipErrorInvalidConfiguration;
+  const int per_launch = max(1, (capacity - 64) / pl.n_split);
   for (int r0 = 0; r0 < batch; r0 += per_launch) {
     const int nb = min(per_launch, batch - r0);
     StepArgs a;

@@ -174,9 +174,6 @@ constexpr int kStepOffAttn = 1024;       // control-area word offsets
 constexpr int kStepOffErr = 2048;
 constexpr int kStepOffRec = 4096;
 constexpr size_t kStepCtlBytes = 4 * ((size_t)kStepOffRec + (size_t)kStepMaxBatch * kStepRecStride);
-// Sequences per launch: keeps the attention workgroups that may wait for a
-// selection to at most 256, half of the device's resident capacity.
-constexpr int kStepMaxWaiting = 256;
 
 // Score segments of a row with c candidate blocks: 1024 each, the last one
 // also holding a remainder of up to 512 (non-decreasing in c).

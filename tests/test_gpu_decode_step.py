@@ -120,8 +120,8 @@ def test_fused_step_other_head_layouts(kv_heads, head_dim):
 
 
 def test_fused_step_batch_over_several_launches():
-    say("fused step: batch 17 (split over two launches)")
-    x = synth.decode(context=2600, batch=17, steps=4, n_needles=2)
+    say("fused step: batch 40 (split over several launches)")
+    x = synth.decode(context=2600, batch=40, steps=4, n_needles=2)
     _fused_vs_unfused(x, 4, check_oracle_steps=(3,))
 
 
