@@ -77,8 +77,11 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", choices=["chunked", "prefill"], default="chunked")
-    ap.add_argument("--decode", choices=["decode", "none"], default="decode")
+    ap.add_argument("--workload", choices=["chunked", "prefill", "companion"], default="chunked",
+                    help="prefill workload: 2 x 8K over 128K (default), 32K from empty, or "
+                         "the last 4K queries of a 1M context")
+    ap.add_argument("--decode", choices=["decode", "stack", "none"], default="decode",
+                    help="decode workload: 8 x 256K (default) or the 12-layer 1M-context stack")
     ap.add_argument("--only", choices=["prefill", "decode"], default=None,
                     help="profile one leg only (the JSON line then carries that leg)")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -97,6 +100,10 @@ def make_prefill_inputs(name):
     if name == "chunked":
         return synth.chunked(), {"workload": "chunked-prefill-128k", "batch": 2,
                                  "cached_tokens": 131072, "chunk_tokens": 8192}
+    if name == "companion":
+        return synth.stack_layer(0, companion=4096), {
+            "workload": "companion-prefill-1m", "batch": 1, "cached_tokens": 1048576 - 4096,
+            "chunk_tokens": 4096}
     return synth.prefill(), {"workload": "prefill-32k", "batch": 1, "cached_tokens": 0,
                              "chunk_tokens": 32768}
 
@@ -272,6 +279,73 @@ def bench_decode(args, torch):
     return res
 
 
+def bench_stack_decode(args, torch):
+    """Decode through a stack of 12 independent QSA layers at a 1M-token
+    context, batch 1: each step runs the fused decode step of every layer in
+    turn (a layer's input depends on the previous layer's output in a model,
+    so the layers are not overlapped).  `steps` steps in one HIP graph."""
+    from block_sparse_trainable_amd import synth
+    from block_sparse_trainable_amd.runtime import DeviceLayer
+    steps = args.decode_steps
+    n_layers = 12
+    layers = []
+    t0 = time.time()
+    for l in range(n_layers):
+        x = synth.stack_layer(l, steps=steps)
+        dl = DeviceLayer(x, "cuda:0")
+        dl.build_prefix(x.cache_len)
+        plan = dl.decode_plan(steps)
+        outs = dl.alloc_decode_outputs()
+        ws = dl.step_workspace(plan[4])
+        scan = int(sum((int(x.q_pos0[0]) + t) // 4 for t in range(steps))) * 256 // steps
+        kB = x.layout.k_blocks
+        gather = int((4 * kB + 4) * x.layout.kv_heads * x.layout.head_dim * 4)
+        dl.x = None  # host copies are no longer needed
+        layers.append((dl, plan, outs, ws, scan + gather))
+        del x
+        torch.cuda.synchronize()
+        log(f"stack layer {l} ready ({time.time() - t0:.0f}s)")
+    for t in range(min(4, steps)):
+        for dl, plan, outs, ws, _ in layers:
+            dl.decode_step_fused(plan, t, outs, ws)
+    torch.cuda.synchronize()
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    evs[0].record()
+    for t in range(steps):
+        for dl, plan, outs, ws, _ in layers:
+            dl.decode_step_fused(plan, t, outs, ws)
+        evs[t + 1].record()
+    torch.cuda.synchronize()
+    per = np.array([evs[t].elapsed_time(evs[t + 1]) for t in range(steps)]) * 1e3
+    g = torch.cuda.CUDAGraph()
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        for t in range(steps):
+            for dl, plan, outs, ws, _ in layers:
+                dl.decode_step_fused(plan, t, outs, ws)
+    g.replay()
+    torch.cuda.synchronize()
+    reps = 3
+    s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s0.record()
+    for _ in range(reps):
+        g.replay()
+    s1.record()
+    torch.cuda.synchronize()
+    graph_us = s0.elapsed_time(s1) * 1e3 / (reps * steps)
+    bytes_step = sum(b for *_, b in layers)
+    res = {"workload": "stack-12x1m-decode", "layers": n_layers, "batch": 1,
+           "context": 1048576, "steps": steps, "us_per_step": graph_us,
+           "mode": "hip-graph (fused, layers in sequence)",
+           "eager_us_per_step": float(per.mean()), "eager_p50_us": float(np.percentile(per, 50)),
+           "eager_p99_us": float(np.percentile(per, 99)),
+           "algorithmic_bytes_per_step": bytes_step,
+           "hbm_frac": bytes_step / (graph_us * 1e-6) / (HBM_PEAK_GBS * 1e9)}
+    del g, layers
+    torch.cuda.empty_cache()
+    return res
+
+
 # ------------------------------------------------------------ cpu oracle --
 def cpu_baseline(x, rows: int):
     """The fp64 oracle on a bounded sample of the same chunk: compression of
@@ -345,15 +419,16 @@ def main():
         print(json.dumps({"calibration": "copy", "bytes_read_per_launch": n,
                           "bytes_written_per_launch": n, "launches": 3}), flush=True)
         return
+    run_decode = bench_stack_decode if args.decode == "stack" else bench_decode
     if args.only == "decode":
-        dec = bench_decode(args, torch)
+        dec = run_decode(args, torch)
         print(json.dumps({"metric": METRIC, "value": None, "unit": "tok/s", "n_gpus": 1,
                           "decode": dec, "note": "decode leg only"}), flush=True)
         return
     x, cfg, pre = bench_prefill(args, torch)
     log(f"prefill {pre['tok_s']:.0f} tok/s, {pre['ms_per_step']:.3f} ms/step, "
         f"stages {pre['stages_ms']}")
-    dec = bench_decode(args, torch) if (args.decode != "none" and args.only is None) else None
+    dec = run_decode(args, torch) if (args.decode != "none" and args.only is None) else None
     if dec:
         log(f"decode {dec['us_per_step']:.1f} us/step")
 

@@ -226,10 +226,17 @@ __device__ __forceinline__ void select_row(const StepArgs& a, int s, int64_t c, 
 #pragma unroll
     for (int e = 0; e < 4; ++e) acc4[e] += cum_field(held[i], e);
   }
-  for (int g = gs + 64; g < nseg_row; g += 4) {
-    const unsigned long long v = coherent_load(&crow[(int64_t)g * 64 + pw]);
+  for (int g0 = 64; g0 < nseg_row; g0 += 64) {  // long rows: 16 more segments per pass
+    unsigned long long w[16];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) acc4[e] += cum_field(v, e);
+    for (int i = 0; i < 16; ++i) {
+      const int g = g0 + gs + 4 * i;
+      w[i] = g < nseg_row ? coherent_load(&crow[(int64_t)g * 64 + pw]) : 0ull;
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc4[e] += cum_field(w[i], e);
   }
 #pragma unroll
   for (int e = 0; e < 4; ++e) rh[gs * 256 + 4 * pw + e] = acc4[e];
@@ -283,37 +290,64 @@ __device__ __forceinline__ void select_row(const StepArgs& a, int s, int64_t c, 
   for (int w = tid; w < nwords; w += kNT) bm[w] = 0u;
 
   if (total <= (uint32_t)kFCap) {
-    // ---- 3. gather the candidates: wave w takes segments w, w + 4, ...,
-    // lane j their j-th candidate; the first 64 entries of the first 64
-    // segments in one batch of independent loads, the rest (longer or later
-    // segments) by a plain loop
+    // ---- 3. gather the candidates.  Slot i (< total <= 4096) belongs to the
+    // last segment starting at or before it: mark each non-empty segment at
+    // its first slot, take a running max over the slots (16 consecutive per
+    // thread, then across threads), then issue every slot's load at once.
     {
-      const int lane = tid & 63, wave = tid >> 6;
-      uint32_t len[16], off[16];
-      unsigned long long v[16];
+      uint32_t* tab = cidx;  // slot -> segment, overwritten by the ids below
+      for (int i = 4 * tid; i < kFCap; i += 4 * kNT)  // every slot: segments stay in range
+        *reinterpret_cast<u32x4*>(tab + i) = u32x4{0u, 0u, 0u, 0u};
+      __syncthreads();
+      for (int g = tid; g < nseg_row; g += kNT)
+        if (seglen[g] != 0u) tab[segoff[g]] = (uint32_t)g;
+      __syncthreads();
+      uint32_t run[kGatherPT];
+      uint32_t mx = 0u;
 #pragma unroll
-      for (int k = 0; k < 16; ++k) {
-        const int g = wave + 4 * k;
-        len[k] = g < nseg_row ? seglen[g] : 0u;
-        off[k] = g < nseg_row ? segoff[g] : 0u;
+      for (int u = 0; u < kGatherPT; u += 4) {
+        const u32x4 t4 = *reinterpret_cast<const u32x4*>(tab + kGatherPT * tid + u);
+        run[u] = t4[0];
+        run[u + 1] = t4[1];
+        run[u + 2] = t4[2];
+        run[u + 3] = t4[3];
       }
 #pragma unroll
-      for (int k = 0; k < 16; ++k)
-        v[k] = (uint32_t)lane < len[k]
-                   ? coherent_load(&prow[(int64_t)(wave + 4 * k) * kStepSegMax + lane])
-                   : 0ull;
+      for (int u = 0; u < kGatherPT; ++u) run[u] = mx = max(mx, run[u]);
+      // exclusive max over the threads before this one (segments only grow)
+      {
+        const int lane = tid & 63, wave = tid >> 6;
+        uint32_t incl = mx;
 #pragma unroll
-      for (int k = 0; k < 16; ++k)
-        if ((uint32_t)lane < len[k]) {
-          ckey[off[k] + lane] = (uint32_t)v[k];
-          cidx[off[k] + lane] = (uint32_t)(v[k] >> 32);
+        for (int off = 1; off < 64; off <<= 1) {
+          const uint32_t t = __shfl_up(incl, off);
+          if (lane >= off) incl = max(incl, t);
         }
-      for (int g = wave; g < nseg_row; g += kNW)
-        for (uint32_t j = (uint32_t)lane + (g < 64 ? 64u : 0u); j < seglen[g]; j += 64) {
-          const unsigned long long x = coherent_load(&prow[(int64_t)g * kStepSegMax + j]);
-          ckey[segoff[g] + j] = (uint32_t)x;
-          cidx[segoff[g] + j] = (uint32_t)(x >> 32);
+        if (lane == 63) scr[20 + wave] = incl;
+        __syncthreads();
+        uint32_t before = __shfl_up(incl, 1);
+        if (lane == 0) before = 0u;
+#pragma unroll
+        for (int w = 0; w < kNW; ++w)
+          if (w < wave) before = max(before, scr[20 + w]);
+#pragma unroll
+        for (int u = 0; u < kGatherPT; ++u) run[u] = max(run[u], before);
+      }
+      unsigned long long v[kGatherPT];
+#pragma unroll
+      for (int u = 0; u < kGatherPT; ++u) {
+        const uint32_t i = (uint32_t)(kGatherPT * tid + u);
+        const uint32_t g = run[u];
+        v[u] = i < total ? coherent_load(&prow[(int64_t)g * kStepSegMax + (i - segoff[g])]) : 0ull;
+      }
+#pragma unroll
+      for (int u = 0; u < kGatherPT; ++u) {
+        const uint32_t i = (uint32_t)(kGatherPT * tid + u);
+        if (i < total) {
+          ckey[i] = (uint32_t)v[u];
+          cidx[i] = (uint32_t)(v[u] >> 32);
         }
+      }
     }
     __syncthreads();
     // ---- 4. exact choice among the bin-d* candidates -------------------------

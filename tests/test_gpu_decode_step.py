@@ -92,6 +92,12 @@ def test_fused_step_multi_segment_rows():
     _fused_vs_unfused(x, 9, check_oracle_steps=(0, 3, 8))
 
 
+def test_fused_step_long_rows_over_64_segments():
+    say("fused step: ~300K-token rows (73 score segments: the long-row passes)")
+    x = synth.decode(context=300000, batch=1, steps=3, n_needles=8)
+    _fused_vs_unfused(x, 3, check_oracle_steps=(2,))
+
+
 def test_fused_step_rows_crossing_the_budget():
     say("fused step: candidate counts crossing k_B = 512 (c <= k_B rows)")
     x = synth.decode(context=2040, batch=2, steps=16, n_needles=4)

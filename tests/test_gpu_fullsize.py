@@ -140,18 +140,26 @@ def test_decode_256k_full_size_eager_and_graph():
 
 
 def test_stack_layer_1m_decode_and_companion():
-    say("1M-context layer: decode steps")
+    say("1M-context layer: decode steps (three calls and fused, compared bitwise)")
     x = synth.stack_layer(0, steps=8)
     dl = DeviceLayer(x)
     dl.build_prefix(x.cache_len)
     plan = dl.decode_plan(8)
     outs = dl.alloc_decode_outputs()
+    fz = DeviceLayer(x)
+    fz.build_prefix(x.cache_len)
+    fplan = fz.decode_plan(8)
+    fouts = fz.alloc_decode_outputs()
     got = {}
     for t in range(8):
         dl.decode_step(plan, t, outs)
+        fz.decode_step_fused(fplan, t, fouts)
+        torch.cuda.synchronize()
+        for u, v in zip(outs, fouts):
+            assert torch.equal(u, v), f"fused step {t} differs from the three calls"
         if t in (0, 3, 7):
-            torch.cuda.synchronize()
             got[t] = [o.clone() for o in outs]
+    del fz, fouts
     kmp_rows = to_f32(dl.k_cmp[0, -(64 + 8):])  # the newest blocks only
     del dl, outs
     torch.cuda.empty_cache()
