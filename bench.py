@@ -45,8 +45,8 @@ BF16_MFMA_PEAK_TFLOPS = 2500.0
 # figures belong to the attention source with this SHA-1; for any other source
 # `traffic` is reported as null until the counters are taken again.
 ATTN_COUNTERS = {
-    "source_sha1": "fc8637675e81b8b7f40827b1131b244a63a5caaa",
-    "fetch_kib": 14366804.6, "write_kib": 66566.6,
+    "source_sha1": "30f6e01428459e659a42c3d185082f2ed7f7b22c",
+    "fetch_kib": 14945643.9, "write_kib": 66561.3,
     "fetch_scale": 2.0, "write_scale": 1.0,
 }
 
