@@ -34,13 +34,21 @@ CFLAGS = [
 ]
 
 
+# Per-source extra flags.  The scoring kernels keep their MFMA accumulators in
+# ordinary VGPRs: the epilogue reads every accumulator, and AGPR-held ones
+# would each cost a copy instruction.
+EXTRA = {
+    "score.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+}
+
+
 def sources():
     return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip"))
 
 
 def _compile(src: str, verbose: bool) -> str:
     obj = os.path.join(OBJDIR, os.path.basename(src) + ".o")
-    cmd = [HIPCC, *CFLAGS, "-c", src, "-o", obj]
+    cmd = [HIPCC, *CFLAGS, *EXTRA.get(os.path.basename(src), []), "-c", src, "-o", obj]
     if verbose:
         cmd.insert(1, "-Rpass-analysis=kernel-resource-usage")
     res = subprocess.run(cmd, capture_output=True, text=True)

@@ -199,6 +199,9 @@ qsa_status qsa_select_topk(const qsa_config* cfg, int32_t batch, int32_t n_q,
   if (!aligned16(workspace))
     return fail(QSA_ERR_INVALID_ARGUMENT, "%s: workspace must be 16-byte aligned", fn);
   const qsa::SelectPlan pl = qsa::select_plan(d, batch, n_q, max_pos_end);
+  if (pl.kernel == 1 && pl.W >= (int64_t{1} << 26))  // 32-bit offsets within a 64-row tile
+    return fail(QSA_ERR_UNSUPPORTED, "%s: max_pos_end %d is beyond the scoring kernel's range", fn,
+                max_pos_end);
   hipError_t e = qsa::launch_score(d, pl, batch, n_q, q_idx, q_pos0, k_cmp, cap_tokens,
                                    workspace, stream);
   if (e == hipSuccess)

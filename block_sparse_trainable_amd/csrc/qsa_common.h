@@ -119,13 +119,15 @@ inline int64_t score_row_width(int r, int32_t max_pos_end) {
 }
 
 // Layout of the select workspace, derived from the call's sizes only.
-//   scores  [rows][W] f32          block-importance rows
+//   scores  [batch][nq_pad][W] f32 block-importance rows (nq_pad >= n_q)
 //   hist    [rows][n_sseg][128] u32 per-score-segment histograms (u16 pairs)
 //   cand    [rows][kCandCap] u32x2 candidates of rows split over workgroups
 //   done    [rows] u32             completion counters of split rows
 struct SelectPlan {
   int kernel;        // 0 = VALU, 1 = MFMA prefill, 2 = MFMA decode
   int64_t W;         // score row width
+  int64_t nq_pad;    // score rows per sequence
+  bool resident;     // rows selected by one streaming pass: no histograms
   int64_t sseg;      // blocks per score segment
   int64_t n_sseg;
   int64_t fseg;      // score segments per filter workgroup

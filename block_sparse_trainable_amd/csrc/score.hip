@@ -27,9 +27,27 @@ __device__ __forceinline__ void hist_add(uint32_t* h, float v) {
   atomicAdd(&h[b >> 1], 1u << ((b & 1u) << 4));
 }
 
+// The same for a score known to be >= +0.0 (sign bit clear), as every MFMA
+// score is: its accumulation starts from +0.0, so a ReLU sum is never -0.0.
+__device__ __forceinline__ void hist_add_nonneg(uint32_t* h, float v) {
+  const int k = min(max((int)(__float_as_uint(v) >> 20) - 888, 0), kHistBins - 1);
+  atomicAdd(&h[k >> 1], 1u + (uint32_t)(k & 1) * 65535u);
+}
+
+// Sum over a lane's four accumulator rows (the four indexer heads) of ReLU.
+// ReLU as one integer max on the bit pattern: a float with the sign bit set
+// is a negative int and becomes +0.0; every other value passes unchanged.
+__device__ __forceinline__ float relu1(float x) {
+  return __int_as_float(max(__float_as_int(x), 0));
+}
+__device__ __forceinline__ float relu_sum4(f32x4 a) {
+  return relu1(a[0]) + relu1(a[1]) + relu1(a[2]) + relu1(a[3]);
+}
+
 struct ScoreOut {
-  float* scores;      // [rows][W]
+  float* scores;      // [batch][nq_pad][W]
   int64_t W;
+  int64_t nq_pad;     // score rows per sequence (n_q rounded up for the prefill tiles)
   uint32_t* hist;     // [rows][n_sseg][kHistWords]
   int64_t n_sseg;
   uint32_t* done;     // [rows]
@@ -70,7 +88,7 @@ __global__ __launch_bounds__(256) void score_valu_kernel(
       }
       acc += relu(dot);
     }
-    o.scores[row * o.W + b] = acc;
+    o.scores[((int64_t)s * o.nq_pad + j) * o.W + b] = acc;
     hist_add(hist, acc);
   }
   __syncthreads();
@@ -89,11 +107,14 @@ constexpr int kPQ = 64;       // queries per workgroup
 constexpr int kChunk = 64;    // blocks per LDS chunk
 constexpr int kRowB = 272;    // LDS bytes per block row (256 + 16 pad)
 
-__global__ __launch_bounds__(256) void score_mfma_prefill_kernel(
+// HIST: also build the per-segment histograms (rows selected by the
+// histogram-guided filter).  Without them the kernel fits three waves per SIMD.
+template <bool HIST>
+__global__ __launch_bounds__(256, HIST ? 2 : 3) void score_mfma_prefill_kernel(
     const uint16_t* __restrict__ q_idx, const int32_t* __restrict__ q_pos0, int n_q,
     const uint16_t* __restrict__ k_cmp, int64_t cap_blocks, int seg_blocks, ScoreOut o) {
   __shared__ __attribute__((aligned(16))) unsigned char lds[2][kChunk * kRowB];
-  __shared__ uint32_t hist[kPQ][kHistWords];
+  __shared__ uint32_t hist[HIST ? kPQ : 1][kHistWords];
   float* __restrict__ scores = o.scores;
   const int64_t W = o.W;
   const int s = blockIdx.z;
@@ -113,11 +134,13 @@ __global__ __launch_bounds__(256) void score_mfma_prefill_kernel(
   const int64_t b_lo = (int64_t)blockIdx.y * seg_blocks;
   const int64_t b_hi = min(b_lo + seg_blocks, c_tile);
   if (b_lo >= b_hi) return;  // no query of the tile reaches this segment
-  for (int i = threadIdx.x; i < kPQ * kHistWords; i += 256) (&hist[0][0])[i] = 0u;
+  if constexpr (HIST)
+    for (int i = threadIdx.x; i < kPQ * kHistWords; i += 256) (&hist[0][0])[i] = 0u;
 
   // A operands: row tile rt covers queries j0 + 16w + 4rt + (0..3)
   u32x4 qa[4][4];
-  int64_t cq[4];  // candidate count of this lane's output query in each row tile
+  int cq[4];        // candidate count of this lane's output query in each row tile
+  uint32_t drow[4]; // that query's score row, at column l16 (offset into scores)
 #pragma unroll
   for (int rt = 0; rt < 4; ++rt) {
     const int jq_a = j0 + 16 * wave + 4 * rt + (l16 >> 2);  // query of A row l16
@@ -127,8 +150,17 @@ __global__ __launch_bounds__(256) void score_mfma_prefill_kernel(
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) qa[rt][kk] = ok ? ld16(src + 32 * kk) : u32x4{0, 0, 0, 0};
     const int jq_o = j0 + 16 * wave + 4 * rt + gq;            // query of output rows 4gq..
-    cq[rt] = jq_o < n_q ? min(min((pos0 + jq_o) / 4, cap_blocks), W) : 0;
+    cq[rt] = jq_o < n_q ? (int)min(min((pos0 + jq_o) / 4, cap_blocks), W) : 0;
+    drow[rt] = (uint32_t)((jq_o - j0) * W + l16);
   }
+  // The tile's rows (queries past n_q have padding rows of their own), so
+  // every score store below is unconditional: a lane past its query's
+  // candidates writes a slot the selection never reads.
+  float* __restrict__ tile = scores + ((int64_t)s * o.nq_pad + j0) * W;
+  // Smallest candidate count among the wave's 16 queries (0 if any is past
+  // n_q): chunks below it need no per-score mask.
+  const int jw = j0 + 16 * wave;
+  const int64_t c_wave = jw + 15 < n_q ? min(min((pos0 + jw) / 4, cap_blocks), W) : 0;
 
   // cooperative chunk load: 1024 pieces of 16 B, four per thread
   const uint16_t* kbase = k_cmp + (int64_t)s * cap_blocks * 128;
@@ -137,8 +169,8 @@ __global__ __launch_bounds__(256) void score_mfma_prefill_kernel(
     for (int u = 0; u < 4; ++u) {
       const int piece = threadIdx.x + 256 * u;
       const int blk = piece >> 4, col = piece & 15;
-      const int64_t b = cb + blk;
-      r[u] = b < b_hi ? ld16(kbase + b * 128 + col * 8) : u32x4{0, 0, 0, 0};
+      const int64_t b = min(cb + blk, b_hi - 1);   // blocks past b_hi score no query
+      r[u] = ld16(kbase + b * 128 + col * 8);
     }
   };
   auto store_chunk = [&](int buf, const u32x4 (&r)[4]) {
@@ -149,6 +181,9 @@ __global__ __launch_bounds__(256) void score_mfma_prefill_kernel(
       *reinterpret_cast<u32x4*>(&lds[buf][blk * kRowB + col * 16]) = r[u];
     }
   };
+  uint32_t* hq[4];
+#pragma unroll
+  for (int rt = 0; rt < 4; ++rt) hq[rt] = hist[HIST ? 16 * wave + 4 * rt + gq : 0];
 
   u32x4 pre[4];
   load_chunk(b_lo, pre);
@@ -159,39 +194,35 @@ __global__ __launch_bounds__(256) void score_mfma_prefill_kernel(
     const bool more = cb + kChunk < b_hi;
     if (more) load_chunk(cb + kChunk, pre);
 
-    f32x4 acc[4][4];
+    // two halves of 32 blocks: 8 accumulator tiles live at a time
+    const bool full = !HIST || cb + kChunk <= c_wave;
 #pragma unroll
-    for (int rt = 0; rt < 4; ++rt)
+    for (int half = 0; half < 2; ++half) {
+      f32x4 acc[4][2];
 #pragma unroll
-      for (int ct = 0; ct < 4; ++ct) acc[rt][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int c2 = 0; c2 < 2; ++c2)
 #pragma unroll
-    for (int ct = 0; ct < 4; ++ct) {
+        for (int kk = 0; kk < 4; ++kk) {
+          const u32x4 bv = *reinterpret_cast<const u32x4*>(
+              &lds[buf][(32 * half + 16 * c2 + l16) * kRowB + 64 * kk + 16 * gq]);
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        const u32x4 bv = *reinterpret_cast<const u32x4*>(
-            &lds[buf][(16 * ct + l16) * kRowB + 64 * kk + 16 * gq]);
-#pragma unroll
-        for (int rt = 0; rt < 4; ++rt)
-          acc[rt][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(qa[rt][kk]),
-                                                                as_bf16x8(bv), acc[rt][ct], 0, 0, 0);
-      }
-    }
-    // epilogue: lane holds 4 heads of query (4rt + gq) for block 16ct + l16
-#pragma unroll
-    for (int rt = 0; rt < 4; ++rt) {
-      const int ql = 16 * wave + 4 * rt + gq;
-      const int jq = j0 + ql;
-      float* dst = scores + ((int64_t)s * n_q + jq) * W;
-#pragma unroll
-      for (int ct = 0; ct < 4; ++ct) {
-        const int64_t b = cb + 16 * ct + l16;
-        const f32x4 a = acc[rt][ct];
-        const float v = relu(a[0]) + relu(a[1]) + relu(a[2]) + relu(a[3]);
-        if (b < cq[rt]) {
-          dst[b] = v;
-          hist_add(hist[ql], v);
+          for (int rt = 0; rt < 4; ++rt)
+            acc[rt][c2] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                as_bf16x8(qa[rt][kk]), as_bf16x8(bv),
+                kk == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : acc[rt][c2], 0, 0, 0);
         }
-      }
+
+      // epilogue: lane holds 4 heads of query (4rt + gq) for block 16ct + l16
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+        for (int c2 = 0; c2 < 2; ++c2) {
+          const int ct = 2 * half + c2;
+          const float v = relu_sum4(acc[rt][c2]);
+          tile[drow[rt] + (uint32_t)cb + 16 * ct] = v;
+          if constexpr (HIST)
+            if (full || cb + 16 * ct + l16 < cq[rt]) hist_add_nonneg(hq[rt], v);
+        }
     }
     if (more) {
       store_chunk(buf ^ 1, pre);
@@ -199,11 +230,13 @@ __global__ __launch_bounds__(256) void score_mfma_prefill_kernel(
       buf ^= 1;
     }
   }
-  __syncthreads();
-  for (int i = threadIdx.x; i < kPQ * kHistWords; i += 256) {
-    const int ql = i / kHistWords, w = i % kHistWords;
-    if (j0 + ql < n_q)
-      o.hist[hist_offset((int64_t)s * n_q + j0 + ql, blockIdx.y, o.n_sseg) + w] = hist[ql][w];
+  if constexpr (HIST) {
+    __syncthreads();
+    for (int i = threadIdx.x; i < kPQ * kHistWords; i += 256) {
+      const int ql = i / kHistWords, w = i % kHistWords;
+      if (j0 + ql < n_q)
+        o.hist[hist_offset((int64_t)s * n_q + j0 + ql, blockIdx.y, o.n_sseg) + w] = hist[ql][w];
+    }
   }
 }
 
@@ -247,7 +280,7 @@ __global__ __launch_bounds__(64 * WAVES) void score_mfma_decode_kernel(
   }
   const int jq_o = j0 + gq;
   const int64_t cq = jq_o < n_q ? min(min((pos0 + jq_o) / 4, cap_blocks), W) : 0;
-  float* dst = scores + ((int64_t)s * n_q + (jq_o < n_q ? jq_o : 0)) * W;
+  float* dst = scores + ((int64_t)s * o.nq_pad + (jq_o < n_q ? jq_o : 0)) * W;
   const uint16_t* kbase = k_cmp + (int64_t)s * cap_blocks * 128 + 8 * gq;
 
   // chunk c of this wave: blocks seg_lo + 64 * (c * WAVES + wave) .. +63
@@ -304,14 +337,19 @@ hipError_t launch_score(const Dims& d, const SelectPlan& pl, int batch, int n_q,
                         int64_t cap, void* workspace, hipStream_t st) {
   const int64_t cap_blocks = cap / d.r;
   char* ws = static_cast<char*>(workspace);
-  ScoreOut o{reinterpret_cast<float*>(ws), pl.W, reinterpret_cast<uint32_t*>(ws + pl.off_hist),
+  ScoreOut o{reinterpret_cast<float*>(ws), pl.W, pl.nq_pad, reinterpret_cast<uint32_t*>(ws + pl.off_hist),
              pl.n_sseg, reinterpret_cast<uint32_t*>(ws + pl.off_done)};
   const unsigned segs = (unsigned)pl.n_sseg;
   if (pl.kernel == 1) {
     dim3 grid((unsigned)((n_q + kPQ - 1) / kPQ), segs, (unsigned)batch);
-    hipLaunchKernelGGL(score_mfma_prefill_kernel, grid, dim3(256), 0, st,
-                       static_cast<const uint16_t*>(q_idx), q_pos0, n_q,
-                       static_cast<const uint16_t*>(k_cmp), cap_blocks, (int)pl.sseg, o);
+    if (pl.resident)
+      hipLaunchKernelGGL(score_mfma_prefill_kernel<false>, grid, dim3(256), 0, st,
+                         static_cast<const uint16_t*>(q_idx), q_pos0, n_q,
+                         static_cast<const uint16_t*>(k_cmp), cap_blocks, (int)pl.sseg, o);
+    else
+      hipLaunchKernelGGL(score_mfma_prefill_kernel<true>, grid, dim3(256), 0, st,
+                         static_cast<const uint16_t*>(q_idx), q_pos0, n_q,
+                         static_cast<const uint16_t*>(k_cmp), cap_blocks, (int)pl.sseg, o);
   } else if (pl.kernel == 2) {
     dim3 grid(segs, (unsigned)((n_q + 3) / 4), (unsigned)batch);
     hipLaunchKernelGGL((score_mfma_decode_kernel<kDecWaves, kDecCpw>), grid, dim3(64 * kDecWaves), 0, st,

@@ -97,6 +97,7 @@ struct FilterArgs {
   int64_t spw;              // score segments per filter workgroup
   int64_t n_fseg;           // filter workgroups per row
   int n_q;
+  int64_t nq_pad;           // score rows per sequence
   const int32_t* q_pos0;
   int64_t cap_blocks;
   int kB;
@@ -126,7 +127,7 @@ __global__ __launch_bounds__(kThreads) void filter_select_kernel(FilterArgs a) {
   const int j = (int)(row % a.n_q);
   const int64_t p = max((int64_t)a.q_pos0[s] + j, (int64_t)0);
   const int64_t c = min(p / 4, min(a.cap_blocks, a.W));
-  const uint32_t* bits = reinterpret_cast<const uint32_t*>(a.scores + row * a.W);
+  const uint32_t* bits = reinterpret_cast<const uint32_t*>(a.scores + (s * a.nq_pad + j) * a.W);
   int32_t* out = a.sel + row * a.kB;
   float* outs = a.sel_scores ? a.sel_scores + row * a.kB : nullptr;
   const int kB = a.kB;
@@ -394,6 +395,219 @@ __global__ __launch_bounds__(kThreads) void filter_select_kernel(FilterArgs a) {
   if (tid == 0) a.cnt[row] = kB;
 }
 
+// ---------------------------------------------------------------------------
+// Rows selected without histograms (the prefill shape: many rows of at most
+// kStreamMax candidates), in two kernels.
+// select_compact_kernel, one wave per row, no LDS and no barriers:
+//   1. a strided sample of the row (one 16-byte piece per lane) gives its
+//      mean and spread, hence a floor F with, for a roughly normal row, about
+//      2 k_B keys at or above it (normal upper-tail quantile);
+//   2. the wave streams the row and appends the keys >= F with their indices,
+//      in index order, to the row's candidate list (ballot compaction);
+//   3. unless k_B <= count <= kCandCap, F moves and the row is streamed again
+//      (a few tries; then the row is marked for the exact fallback).  Every
+//      accepted F is correct: the k_B largest keys are all >= F.
+// select_finish_kernel, one workgroup per row: a radix select over the
+// candidates finds the k_B-th largest key and the ordered pass writes the
+// kept ids ascending, ties to the lower index.
+// The scores of this path are MFMA ReLU sums, never negative: their bits are
+// the keys as they are.  F is at least the smallest positive float, so zero
+// scores never count (a row that needs them takes the fallback).
+constexpr int kStreamBatch = 8;                    // 16-byte loads in flight per lane
+constexpr int64_t kStreamMax = int64_t{1} << 20;   // candidates per row this path takes
+constexpr uint32_t kCompactFailed = 0xFFFFFFFFu;
+
+// z with P(Z > z) = p for a standard normal Z and 0 < p < 0.5: Abramowitz &
+// Stegun 26.2.23 (absolute error below 4.5e-4).
+__device__ __forceinline__ float normal_upper_quantile(float p) {
+  const float t = sqrtf(-2.0f * __logf(p));
+  return t - (2.515517f + t * (0.802853f + t * 0.010328f)) /
+                 (1.0f + t * (1.432788f + t * (0.189269f + t * 0.001308f)));
+}
+
+struct RowOf {
+  int s, j;
+  int64_t c;
+  const uint32_t* bits;
+};
+__device__ __forceinline__ RowOf row_of(const FilterArgs& a, int64_t row) {
+  RowOf r;
+  r.s = (int)(row / a.n_q);
+  r.j = (int)(row % a.n_q);
+  const int64_t p = max((int64_t)a.q_pos0[r.s] + r.j, (int64_t)0);
+  r.c = min(p / 4, min(a.cap_blocks, a.W));
+  r.bits = reinterpret_cast<const uint32_t*>(a.scores + (r.s * a.nq_pad + r.j) * a.W);
+  return r;
+}
+
+__global__ __launch_bounds__(256) void select_compact_kernel(FilterArgs a, int64_t rows) {
+  const int lane = threadIdx.x & 63;
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= rows) return;
+  const RowOf ro = row_of(a, row);
+  const int kB = a.kB;
+  if (ro.c <= kB) return;               // the finishing kernel keeps them all
+  const int ci = (int)ro.c;
+  const uint32_t* bits = ro.bits;
+  unsigned long long* cand = reinterpret_cast<unsigned long long*>(a.cand) + row * kCandCap;
+
+  // ---- 1. sampled mean and spread ----------------------------------------
+  float sm = 0.0f, sq = 0.0f, sn = 0.0f;
+  {
+    const int n4 = (ci + 3) / 4;
+    const int k = (int)((int64_t)lane * n4 / 64);
+    const u32x4 w = *reinterpret_cast<const u32x4*>(bits + 4 * k);
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      if (4 * k + e < ci) {
+        const float x = __uint_as_float(w[e]);
+        sm += x;
+        sq = fmaf(x, x, sq);
+        sn += 1.0f;
+      }
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    sm += __shfl_xor(sm, off);
+    sq += __shfl_xor(sq, off);
+    sn += __shfl_xor(sn, off);
+  }
+  const float mu = sm / sn;
+  const float sd = sqrtf(fmaxf(sq / sn - mu * mu, 0.0f));
+  const float pfrac = 2.0f * (float)kB / (float)ci;
+  float z = pfrac < 0.5f ? normal_upper_quantile(pfrac) : -INFINITY;
+
+  // ---- 2./3. stream, compact, accept or move the floor -------------------
+  const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  uint32_t result = kCompactFailed;
+  for (int attempt = 0; attempt < 3; ++attempt) {
+    const float f = z == -INFINITY ? 0.0f : fmaxf(mu + z * sd, 0.0f);
+    const uint32_t fbits = max(__float_as_uint(f), 1u);
+    uint32_t pos = 0u;
+    for (int base = 0; base < ci; base += 256 * kStreamBatch) {
+      u32x4 v[kStreamBatch];
+#pragma unroll
+      for (int b = 0; b < kStreamBatch; ++b) {
+        const int i0 = base + 256 * b + 4 * lane;
+        v[b] = i0 < ci ? *reinterpret_cast<const u32x4*>(bits + i0) : u32x4{0, 0, 0, 0};
+      }
+#pragma unroll
+      for (int b = 0; b < kStreamBatch; ++b) {
+        const int i0 = base + 256 * b + 4 * lane;
+        uint32_t m = 0;
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (i0 + e < ci && v[b][e] >= fbits) m |= 1u << e;
+        uint32_t before = 0, all = 0;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const uint64_t bal = __ballot((m >> e) & 1u);
+          before += (uint32_t)__popcll(bal & lt);
+          all += (uint32_t)__popcll(bal);
+        }
+        if (m) {
+          uint32_t at = pos + before;
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if ((m >> e) & 1u) {
+              if (at < (uint32_t)kCandCap)
+                cand[at] = (unsigned long long)v[b][e] | ((unsigned long long)(i0 + e) << 32);
+              ++at;
+            }
+        }
+        pos += all;
+      }
+    }
+    if (pos < (uint32_t)kB) {
+      if (fbits == 1u) break;              // too few positive scores
+      z = z - 1.0f < -3.0f ? -INFINITY : z - 1.0f;
+    } else if (pos > (uint32_t)kCandCap) {
+      z = z == -INFINITY ? 0.0f : z + 0.5f;
+    } else {
+      result = pos;
+      break;
+    }
+  }
+  if (lane == 0) a.done[row] = result;
+}
+
+__global__ __launch_bounds__(kThreads) void select_finish_kernel(FilterArgs a) {
+  __shared__ uint32_t ckey[kCandCap];
+  __shared__ uint32_t cidx[kCandCap];
+  __shared__ uint32_t hist[kRadixBins];
+  __shared__ uint32_t scratch[64];
+  const int tid = threadIdx.x;
+  const int64_t row = blockIdx.x;
+  const RowOf ro = row_of(a, row);
+  const int64_t c = ro.c;
+  const uint32_t* bits = ro.bits;
+  int32_t* out = a.sel + row * a.kB;
+  float* outs = a.sel_scores ? a.sel_scores + row * a.kB : nullptr;
+  const int kB = a.kB;
+
+  if (c <= kB) {  // every candidate is kept
+    for (int i = tid; i < kB; i += kThreads) {
+      out[i] = i < c ? i : -1;
+      if (outs) outs[i] = i < c ? __uint_as_float(bits[i]) : 0.0f;
+    }
+    if (tid == 0) a.cnt[row] = (int32_t)c;
+    return;
+  }
+  const uint32_t n_f = a.done[row];
+  if (n_f == kCompactFailed) {
+    select_row_global(bits, c, kB, out, outs, hist, scratch);
+    if (tid == 0) a.cnt[row] = kB;
+    return;
+  }
+  const unsigned long long* cand = reinterpret_cast<const unsigned long long*>(a.cand) + row * kCandCap;
+  for (uint32_t i = tid; i < n_f; i += kThreads) {
+    const unsigned long long v = cand[i];
+    ckey[i] = (uint32_t)v;
+    cidx[i] = (uint32_t)(v >> 32);
+  }
+  __syncthreads();
+
+  auto key = [&](int64_t i) { return ckey[i]; };
+  auto all = [&](int64_t) { return true; };
+  const Radix r = radix_select<kThreads>(key, all, (int64_t)n_f, (uint32_t)kB, hist, scratch);
+  uint32_t written = 0, eq_seen = 0;
+  for (uint32_t base = 0; base < n_f; base += 8 * kThreads) {
+    const uint32_t i0 = base + 8 * tid;
+    uint32_t take = 0, eqm = 0;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const uint32_t i = i0 + e;
+      if (i < n_f) {
+        const uint32_t m = ckey[i] & r.mask;
+        if (m > r.prefix) take |= 1u << e;
+        else if (m == r.prefix) eqm |= 1u << e;
+      }
+    }
+    uint32_t tot_eq;
+    const uint32_t ex_eq = block_excl_scan<kThreads>((uint32_t)__popc(eqm), scratch, &tot_eq);
+    uint32_t eq_rank = eq_seen + ex_eq;
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      if (eqm & (1u << e)) {
+        if (eq_rank < r.need) take |= 1u << e;
+        ++eq_rank;
+      }
+    uint32_t tot;
+    const uint32_t ex = block_excl_scan<kThreads>((uint32_t)__popc(take), scratch, &tot);
+    uint32_t pos = written + ex;
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      if (take & (1u << e)) {
+        out[pos] = (int32_t)cidx[i0 + e];
+        if (outs) outs[pos] = __uint_as_float(ckey[i0 + e]);
+        ++pos;
+      }
+    written += tot;
+    eq_seen += tot_eq;
+  }
+  if (tid == 0) a.cnt[row] = kB;
+}
+
 }  // namespace
 
 SelectPlan select_plan(const Dims& d, int batch, int n_q, int32_t max_pos_end) {
@@ -405,6 +619,12 @@ SelectPlan select_plan(const Dims& d, int batch, int n_q, int32_t max_pos_end) {
   p.sseg = p.kernel == 0 ? 256 : (p.kernel == 1 ? 2048 : kDecodeScoreSeg);
   p.n_sseg = (c_max + p.sseg - 1) / p.sseg;
   const int64_t rows = (int64_t)batch * n_q;
+  // The prefill tiles write whole 64-query x 64-block chunks: pad each
+  // sequence's rows to 64 queries and each row to 64 blocks.
+  p.nq_pad = p.kernel == 1 ? ((int64_t)n_q + 63) / 64 * 64 : n_q;
+  if (p.kernel == 1) p.W = (p.W + 63) / 64 * 64;
+  // Prefill rows are selected by streaming them once: no histograms.
+  p.resident = p.kernel == 1 && c_max <= kStreamMax;
   if (rows >= 256 || c_max <= kFilterSeg) {
     p.fseg = p.n_sseg;          // score segments per filter workgroup
     p.n_fseg = 1;
@@ -413,11 +633,11 @@ SelectPlan select_plan(const Dims& d, int batch, int n_q, int32_t max_pos_end) {
     p.n_fseg = (p.n_sseg + p.fseg - 1) / p.fseg;
   }
   auto align = [](size_t v) { return (v + 255) / 256 * 256; };
-  size_t off = align(sizeof(float) * (size_t)rows * (size_t)p.W);
+  size_t off = align(sizeof(float) * (size_t)batch * (size_t)p.nq_pad * (size_t)p.W);
   p.off_hist = off;
-  off = align(off + sizeof(uint32_t) * (size_t)rows * p.n_sseg * kHistWords);
+  if (!p.resident) off = align(off + sizeof(uint32_t) * (size_t)rows * p.n_sseg * kHistWords);
   p.off_slots = off;
-  if (p.n_fseg > 1) off = align(off + sizeof(uint2) * (size_t)rows * kCandCap);
+  if (p.n_fseg > 1 || p.resident) off = align(off + sizeof(uint2) * (size_t)rows * kCandCap);
   p.off_slotcnt = off;
   p.off_done = off;
   off = align(off + sizeof(uint32_t) * (size_t)rows);
@@ -440,6 +660,7 @@ hipError_t launch_select(const Dims& d, const SelectPlan& pl, int batch, int n_q
   a.spw = pl.fseg;
   a.n_fseg = pl.n_fseg;
   a.n_q = n_q;
+  a.nq_pad = pl.nq_pad;
   a.q_pos0 = q_pos0;
   a.cap_blocks = cap / d.r;
   a.kB = d.kB;
@@ -447,7 +668,12 @@ hipError_t launch_select(const Dims& d, const SelectPlan& pl, int batch, int n_q
   a.cnt = cnt;
   a.sel_scores = sel_scores;
   dim3 grid((unsigned)((int64_t)batch * n_q), (unsigned)pl.n_fseg);
-  if (pl.n_fseg > 1 && pl.sseg <= 1024 && pl.fseg <= kWaves)
+  if (pl.resident) {
+    const int64_t rows = (int64_t)batch * n_q;
+    hipLaunchKernelGGL(select_compact_kernel, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, st, a,
+                       rows);
+    hipLaunchKernelGGL(select_finish_kernel, dim3((unsigned)rows), dim3(kThreads), 0, st, a);
+  } else if (pl.n_fseg > 1 && pl.sseg <= 1024 && pl.fseg <= kWaves)
     hipLaunchKernelGGL(filter_select_kernel<true>, grid, dim3(kThreads), 0, st, a);
   else
     hipLaunchKernelGGL(filter_select_kernel<false>, grid, dim3(kThreads), 0, st, a);

@@ -17,8 +17,8 @@ HIPCC = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
 
 
 def _report(src):
-    from block_sparse_trainable_amd.build import CFLAGS
-    cmd = [HIPCC, *CFLAGS, "--cuda-device-only", "-Rpass-analysis=kernel-resource-usage",
+    from block_sparse_trainable_amd.build import CFLAGS, EXTRA
+    cmd = [HIPCC, *CFLAGS, *EXTRA.get(os.path.basename(src), []), "--cuda-device-only", "-Rpass-analysis=kernel-resource-usage",
            "-c", src, "-o", os.devnull]
     return subprocess.run(cmd, capture_output=True, text=True).stderr
 
