@@ -41,15 +41,18 @@ __device__ __forceinline__ uint32_t key_of(uint32_t bits) {
   return (bits & 0x80000000u) ? 0u : bits;  // scores are >= 0; guard anyway
 }
 
-// Exact selection over a whole row of c keys in global memory (fallback).
-__device__ __forceinline__ void select_row_global(const uint32_t* bits, int64_t c, int kB, int32_t* out,
-                                  float* outs, uint32_t* hist, uint32_t* scratch) {
+// Exact selection over a whole row of c keys in global memory (fallback),
+// by a workgroup of NT threads.
+template <int NT>
+__device__ __forceinline__ void select_row_global_nt(const uint32_t* bits, int64_t c, int kB,
+                                                     int32_t* out, float* outs, uint32_t* hist,
+                                                     uint32_t* scratch) {
   auto key = [&](int64_t i) { return key_of(bits[i]); };
   auto all = [&](int64_t) { return true; };
-  const Radix r = radix_select<kThreads>(key, all, c, (uint32_t)kB, hist, scratch);
+  const Radix r = radix_select<NT>(key, all, c, (uint32_t)kB, hist, scratch);
   uint32_t gt_seen = 0, eq_seen = 0;
   const int tid = threadIdx.x;
-  for (int64_t base = 0; base < c; base += 4 * kThreads) {
+  for (int64_t base = 0; base < c; base += 4 * NT) {
     const int64_t i0 = base + 4 * tid;
     uint32_t k[4];
     uint32_t ngt = 0, neq = 0;
@@ -61,7 +64,7 @@ __device__ __forceinline__ void select_row_global(const uint32_t* bits, int64_t 
       neq += (i0 + e < c && m == r.prefix) ? 1u : 0u;
     }
     uint32_t tot;
-    const uint32_t ex = block_excl_scan<kThreads>((ngt << 16) | neq, scratch, &tot);
+    const uint32_t ex = block_excl_scan<NT>((ngt << 16) | neq, scratch, &tot);
     uint32_t gt_before = gt_seen + (ex >> 16);
     uint32_t eq_before = eq_seen + (ex & 0xFFFFu);
 #pragma unroll
@@ -333,7 +336,7 @@ __global__ __launch_bounds__(kThreads) void filter_select_kernel(FilterArgs a) {
   __syncthreads();
 
   if (!fits) {
-    select_row_global(bits, c, kB, out, outs, hist, scratch);
+    select_row_global_nt<kThreads>(bits, c, kB, out, outs, hist, scratch);
     if (tid == 0) a.cnt[row] = kB;
     return;
   }
@@ -413,9 +416,7 @@ __global__ __launch_bounds__(kThreads) void filter_select_kernel(FilterArgs a) {
 // The scores of this path are MFMA ReLU sums, never negative: their bits are
 // the keys as they are.  F is at least the smallest positive float, so zero
 // scores never count (a row that needs them takes the fallback).
-constexpr int kStreamBatch = 8;                    // 16-byte loads in flight per lane
 constexpr int64_t kStreamMax = int64_t{1} << 20;   // candidates per row this path takes
-constexpr uint32_t kCompactFailed = 0xFFFFFFFFu;
 
 // z with P(Z > z) = p for a standard normal Z and 0 < p < 0.5: Abramowitz &
 // Stegun 26.2.23 (absolute error below 4.5e-4).
@@ -440,22 +441,56 @@ __device__ __forceinline__ RowOf row_of(const FilterArgs& a, int64_t row) {
   return r;
 }
 
-__global__ __launch_bounds__(256) void select_compact_kernel(FilterArgs a, int64_t rows) {
-  const int lane = threadIdx.x & 63;
-  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (row >= rows) return;
+// One workgroup of NT threads per row: sample, stream in batches of BATCH
+// 16-byte pieces per thread compacting into the LDS pool in index order,
+// then the radix select and the ordered output.  PRUNE (long rows) lets the
+// floor rise during the pass instead of streaming the row again.
+constexpr int kRowCap = 3072;                  // pool capacity (candidates)
+// pool slot i lives at i + i / 16: the ordered pass reads 16 consecutive
+// slots per thread, which would otherwise all fall in two banks
+__device__ __forceinline__ uint32_t pslot(uint32_t i) { return i + (i >> 4); }
+constexpr int64_t kRowShortMax = 40960;        // candidates of a "short" row
+constexpr int kPrune = 256;                    // keys kept above k_B when the pool is pruned
+
+template <int NT, int BATCH, bool PRUNE>
+__global__ __launch_bounds__(NT) void select_row_kernel(FilterArgs a) {
+  constexpr int kRowThreads = NT;
+  constexpr int kRowWaves = NT / 64;
+  constexpr int kRowBatch = BATCH;
+  constexpr int kRowSlots = kRowCap + kRowCap / 16 + NT;  // + one trash slot per thread
+  static_assert(kRowWaves % 4 == 0, "batch offsets read 4-wave groups of counts");
+  __shared__ uint32_t ckey[kRowSlots];
+  __shared__ uint32_t cidx[kRowSlots];
+  __shared__ uint32_t hist[kRadixBins];
+  __shared__ __attribute__((aligned(16))) uint32_t wt[kRowBatch * kRowWaves];
+  __shared__ float fred[3 * kRowWaves];
+  __shared__ uint32_t scratch[64];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int64_t row = blockIdx.x;
   const RowOf ro = row_of(a, row);
-  const int kB = a.kB;
-  if (ro.c <= kB) return;               // the finishing kernel keeps them all
-  const int ci = (int)ro.c;
+  const int64_t c = ro.c;
   const uint32_t* bits = ro.bits;
-  unsigned long long* cand = reinterpret_cast<unsigned long long*>(a.cand) + row * kCandCap;
+  int32_t* out = a.sel + row * a.kB;
+  float* outs = a.sel_scores ? a.sel_scores + row * a.kB : nullptr;
+  const int kB = a.kB;
+
+  if (c <= kB) {  // every candidate is kept
+    for (int i = tid; i < kB; i += kRowThreads) {
+      out[i] = i < c ? i : -1;
+      if (outs) outs[i] = i < c ? __uint_as_float(bits[i]) : 0.0f;
+    }
+    if (tid == 0) a.cnt[row] = (int32_t)c;
+    return;
+  }
+  const int ci = (int)c;
 
   // ---- 1. sampled mean and spread ----------------------------------------
   float sm = 0.0f, sq = 0.0f, sn = 0.0f;
   {
     const int n4 = (ci + 3) / 4;
-    const int k = (int)((int64_t)lane * n4 / 64);
+    const int k = (int)((int64_t)tid * n4 / kRowThreads);
     const u32x4 w = *reinterpret_cast<const u32x4*>(bits + 4 * k);
 #pragma unroll
     for (int e = 0; e < 4; ++e)
@@ -472,134 +507,231 @@ __global__ __launch_bounds__(256) void select_compact_kernel(FilterArgs a, int64
     sq += __shfl_xor(sq, off);
     sn += __shfl_xor(sn, off);
   }
+  if (lane == 0) {
+    fred[wave] = sm;
+    fred[kRowWaves + wave] = sq;
+    fred[2 * kRowWaves + wave] = sn;
+  }
+  __syncthreads();
+  sm = sq = sn = 0.0f;
+#pragma unroll
+  for (int w = 0; w < kRowWaves; ++w) {
+    sm += fred[w];
+    sq += fred[kRowWaves + w];
+    sn += fred[2 * kRowWaves + w];
+  }
   const float mu = sm / sn;
   const float sd = sqrtf(fmaxf(sq / sn - mu * mu, 0.0f));
   const float pfrac = 2.0f * (float)kB / (float)ci;
   float z = pfrac < 0.5f ? normal_upper_quantile(pfrac) : -INFINITY;
 
-  // ---- 2./3. stream, compact, accept or move the floor -------------------
-  const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  uint32_t result = kCompactFailed;
-  for (int attempt = 0; attempt < 3; ++attempt) {
+  // ---- 2./3. stream the row into the pool; accept or move the floor ------
+  uint32_t n_f = 0u;
+  bool ok = false;
+  for (int attempt = 0; attempt < 4 && !ok; ++attempt) {
     const float f = z == -INFINITY ? 0.0f : fmaxf(mu + z * sd, 0.0f);
-    const uint32_t fbits = max(__float_as_uint(f), 1u);
-    uint32_t pos = 0u;
-    for (int base = 0; base < ci; base += 256 * kStreamBatch) {
-      u32x4 v[kStreamBatch];
+    uint32_t fbits = max(__float_as_uint(f), 1u);
+    uint32_t total = 0u;   // uniform: candidates before this batch
+    bool overflow = false;
+    constexpr int kStep = 4 * kRowThreads * kRowBatch;
+    // batches double-buffered in registers: the next one's loads are in
+    // flight while this one is compacted
+    // Loads are unconditional (addresses clamped to the row's last piece;
+    // keys past c are masked by index below), so the compiler can count
+    // them and wait for this batch only.
+    const int last4 = (ci - 1) & ~3;
+    u32x4 nx[kRowBatch];
 #pragma unroll
-      for (int b = 0; b < kStreamBatch; ++b) {
-        const int i0 = base + 256 * b + 4 * lane;
-        v[b] = i0 < ci ? *reinterpret_cast<const u32x4*>(bits + i0) : u32x4{0, 0, 0, 0};
+    for (int b = 0; b < kRowBatch; ++b) {
+      const int i0 = 4 * (tid + kRowThreads * b);
+      nx[b] = *reinterpret_cast<const u32x4*>(bits + min(i0, last4));
+    }
+    for (int base = 0; base < ci; base += kStep) {
+      u32x4 v[kRowBatch];
+#pragma unroll
+      for (int b = 0; b < kRowBatch; ++b) v[b] = nx[b];
+#pragma unroll
+      for (int b = 0; b < kRowBatch; ++b) {
+        const int i0 = base + kStep + 4 * (tid + kRowThreads * b);
+        nx[b] = *reinterpret_cast<const u32x4*>(bits + min(i0, last4));
       }
+      // Index order within the batch is (b, wave, lane, e).  Each lane's
+      // count per piece b (0..4) is scanned across the wave three pieces at
+      // a time in 10-bit fields; the wave totals per b go through LDS.  If
+      // the pool cannot take the batch, the floor first rises to the
+      // (k_B + kPrune)-th largest key kept so far (still a valid floor: at
+      // least k_B keys of the row are at or above it), the pool keeps only
+      // the keys at or above it, and the batch is counted again.
+      const bool full = base + kStep <= ci;
+      uint32_t excl[kRowBatch];
+      for (int pass = 0;; ++pass) {
+        uint32_t cnt[kRowBatch];
 #pragma unroll
-      for (int b = 0; b < kStreamBatch; ++b) {
-        const int i0 = base + 256 * b + 4 * lane;
-        uint32_t m = 0;
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          if (i0 + e < ci && v[b][e] >= fbits) m |= 1u << e;
-        uint32_t before = 0, all = 0;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const uint64_t bal = __ballot((m >> e) & 1u);
-          before += (uint32_t)__popcll(bal & lt);
-          all += (uint32_t)__popcll(bal);
-        }
-        if (m) {
-          uint32_t at = pos + before;
+        for (int b = 0; b < kRowBatch; ++b) {
+          const int i0 = base + 4 * (tid + kRowThreads * b);
+          uint32_t n = 0;
 #pragma unroll
           for (int e = 0; e < 4; ++e)
-            if ((m >> e) & 1u) {
-              if (at < (uint32_t)kCandCap)
-                cand[at] = (unsigned long long)v[b][e] | ((unsigned long long)(i0 + e) << 32);
-              ++at;
+            n += (v[b][e] >= fbits && (full || i0 + e < ci)) ? 1u : 0u;
+          cnt[b] = n;
+        }
+#pragma unroll
+        for (int g = 0; g < kRowBatch; g += 3) {
+          uint32_t x = 0;
+#pragma unroll
+          for (int q = 0; q < 3; ++q)
+            if (g + q < kRowBatch) x |= cnt[g + q] << (10 * q);
+          uint32_t incl = x;
+#pragma unroll
+          for (int off = 1; off < 64; off <<= 1) {
+            const uint32_t t = __shfl_up(incl, off);
+            if (lane >= off) incl += t;
+          }
+          const uint32_t ex = incl - x;
+          const uint32_t tot = __shfl(incl, 63);
+#pragma unroll
+          for (int q = 0; q < 3; ++q)
+            if (g + q < kRowBatch) {
+              excl[g + q] = (ex >> (10 * q)) & 1023u;
+              if (lane == 0) wt[(g + q) * kRowWaves + wave] = (tot >> (10 * q)) & 1023u;
             }
         }
-        pos += all;
+        __syncthreads();
+        uint32_t btot = 0u;
+#pragma unroll
+        for (int q = 0; q < kRowBatch * kRowWaves; q += 4) {
+          const u32x4 r4 = *reinterpret_cast<const u32x4*>(&wt[q]);
+          btot += r4[0] + r4[1] + r4[2] + r4[3];
+        }
+        if (total + btot <= (uint32_t)kRowCap) break;
+        if (!PRUNE || pass > 0 || total < (uint32_t)(kB + kPrune)) {   // no room for the batch
+          overflow = true;
+          break;
+        }
+        if constexpr (!PRUNE) break;
+        // raise the floor and prune the pool (stable, in place)
+        auto pkey = [&](int64_t i) { return ckey[pslot((uint32_t)i)]; };
+        auto pall = [&](int64_t) { return true; };
+        const Radix rp = radix_select<kRowThreads>(pkey, pall, (int64_t)total,
+                                                   (uint32_t)(kB + kPrune), hist, scratch);
+        fbits = max(fbits, rp.prefix);
+        // kept entries staged in the (now idle) radix histogram, then copied
+        // back in order
+        constexpr int E = kRowCap / kRowThreads;
+        constexpr uint32_t kStage = kRadixBins / 2;
+        uint32_t keep = 0;
+#pragma unroll
+        for (int q = 0; q < E; ++q) {
+          const uint32_t i = (uint32_t)(E * tid + q);
+          keep += (i < total && ckey[pslot(i)] >= fbits) ? 1u : 0u;
+        }
+        uint32_t kept;
+        uint32_t at = block_excl_scan<kRowThreads>(keep, scratch, &kept);
+        if (kept > kStage) {   // ties at the new floor: cannot happen short of
+          overflow = true;     // hundreds of equal keys; take the retry path
+          break;
+        }
+#pragma unroll
+        for (int q = 0; q < E; ++q) {
+          const uint32_t i = (uint32_t)(E * tid + q);
+          if (i < total) {
+            const uint32_t k = ckey[pslot(i)];
+            if (k >= fbits) {
+              hist[2 * at] = k;
+              hist[2 * at + 1] = cidx[pslot(i)];
+              ++at;
+            }
+          }
+        }
+        __syncthreads();
+        for (uint32_t i = tid; i < kept; i += kRowThreads) {
+          ckey[pslot(i)] = hist[2 * i];
+          cidx[pslot(i)] = hist[2 * i + 1];
+        }
+        total = kept;
+        __syncthreads();
       }
+      if (overflow) break;
+      // wave-uniform offsets: (b, wave) order over the 4-wave rows of wt
+      uint32_t run = total;
+      // non-candidates write to this lane's trash slot past the pool
+      const uint32_t trash = (uint32_t)(kRowCap + kRowCap / 16) + (uint32_t)tid;
+#pragma unroll
+      for (int b = 0; b < kRowBatch; ++b) {
+        uint32_t off = run;
+#pragma unroll
+        for (int w4 = 0; w4 < kRowWaves; w4 += 4) {
+          const u32x4 r4 = *reinterpret_cast<const u32x4*>(&wt[b * kRowWaves + w4]);
+#pragma unroll
+          for (int w = 0; w < 4; ++w) off += w4 + w < wave ? r4[w] : 0u;
+          run += r4[0] + r4[1] + r4[2] + r4[3];
+        }
+        uint32_t at = off + excl[b];
+        const int i0 = base + 4 * (tid + kRowThreads * b);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const bool take = v[b][e] >= fbits && (full || i0 + e < ci);
+          const uint32_t slot = take && at < (uint32_t)kRowCap ? pslot(at) : trash;
+          ckey[slot] = v[b][e];
+          cidx[slot] = (uint32_t)(i0 + e);
+          at += take ? 1u : 0u;
+        }
+      }
+      total = run;
+      __syncthreads();
     }
-    if (pos < (uint32_t)kB) {
+    n_f = total;
+    if (overflow) {
+      z = z == -INFINITY ? 0.0f : z + 0.5f;
+    } else if (total < (uint32_t)kB) {
       if (fbits == 1u) break;              // too few positive scores
       z = z - 1.0f < -3.0f ? -INFINITY : z - 1.0f;
-    } else if (pos > (uint32_t)kCandCap) {
+    } else if (total > (uint32_t)kRowCap) {
       z = z == -INFINITY ? 0.0f : z + 0.5f;
     } else {
-      result = pos;
-      break;
+      ok = true;
     }
   }
-  if (lane == 0) a.done[row] = result;
-}
-
-__global__ __launch_bounds__(kThreads) void select_finish_kernel(FilterArgs a) {
-  __shared__ uint32_t ckey[kCandCap];
-  __shared__ uint32_t cidx[kCandCap];
-  __shared__ uint32_t hist[kRadixBins];
-  __shared__ uint32_t scratch[64];
-  const int tid = threadIdx.x;
-  const int64_t row = blockIdx.x;
-  const RowOf ro = row_of(a, row);
-  const int64_t c = ro.c;
-  const uint32_t* bits = ro.bits;
-  int32_t* out = a.sel + row * a.kB;
-  float* outs = a.sel_scores ? a.sel_scores + row * a.kB : nullptr;
-  const int kB = a.kB;
-
-  if (c <= kB) {  // every candidate is kept
-    for (int i = tid; i < kB; i += kThreads) {
-      out[i] = i < c ? i : -1;
-      if (outs) outs[i] = i < c ? __uint_as_float(bits[i]) : 0.0f;
-    }
-    if (tid == 0) a.cnt[row] = (int32_t)c;
-    return;
-  }
-  const uint32_t n_f = a.done[row];
-  if (n_f == kCompactFailed) {
-    select_row_global(bits, c, kB, out, outs, hist, scratch);
+  if (__builtin_expect(!ok, 0)) {
+    select_row_global_nt<kRowThreads>(bits, c, kB, out, outs, hist, scratch);
     if (tid == 0) a.cnt[row] = kB;
     return;
   }
-  const unsigned long long* cand = reinterpret_cast<const unsigned long long*>(a.cand) + row * kCandCap;
-  for (uint32_t i = tid; i < n_f; i += kThreads) {
-    const unsigned long long v = cand[i];
-    ckey[i] = (uint32_t)v;
-    cidx[i] = (uint32_t)(v >> 32);
-  }
-  __syncthreads();
 
-  auto key = [&](int64_t i) { return ckey[i]; };
+  // ---- 4. the k_B-th largest key, then the ordered output -----------------
+  auto key = [&](int64_t i) { return ckey[pslot((uint32_t)i)]; };
   auto all = [&](int64_t) { return true; };
-  const Radix r = radix_select<kThreads>(key, all, (int64_t)n_f, (uint32_t)kB, hist, scratch);
+  const Radix r = radix_select<kRowThreads>(key, all, (int64_t)n_f, (uint32_t)kB, hist, scratch);
   uint32_t written = 0, eq_seen = 0;
-  for (uint32_t base = 0; base < n_f; base += 8 * kThreads) {
-    const uint32_t i0 = base + 8 * tid;
+  for (uint32_t base = 0; base < n_f; base += 16 * kRowThreads) {
+    const uint32_t i0 = base + 16 * tid;
     uint32_t take = 0, eqm = 0;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
+    for (int e = 0; e < 16; ++e) {
       const uint32_t i = i0 + e;
       if (i < n_f) {
-        const uint32_t m = ckey[i] & r.mask;
+        const uint32_t m = ckey[pslot(i)] & r.mask;
         if (m > r.prefix) take |= 1u << e;
         else if (m == r.prefix) eqm |= 1u << e;
       }
     }
     uint32_t tot_eq;
-    const uint32_t ex_eq = block_excl_scan<kThreads>((uint32_t)__popc(eqm), scratch, &tot_eq);
+    const uint32_t ex_eq = block_excl_scan<kRowThreads>((uint32_t)__popc(eqm), scratch, &tot_eq);
     uint32_t eq_rank = eq_seen + ex_eq;
 #pragma unroll
-    for (int e = 0; e < 8; ++e)
+    for (int e = 0; e < 16; ++e)
       if (eqm & (1u << e)) {
         if (eq_rank < r.need) take |= 1u << e;
         ++eq_rank;
       }
     uint32_t tot;
-    const uint32_t ex = block_excl_scan<kThreads>((uint32_t)__popc(take), scratch, &tot);
+    const uint32_t ex = block_excl_scan<kRowThreads>((uint32_t)__popc(take), scratch, &tot);
     uint32_t pos = written + ex;
 #pragma unroll
-    for (int e = 0; e < 8; ++e)
+    for (int e = 0; e < 16; ++e)
       if (take & (1u << e)) {
-        out[pos] = (int32_t)cidx[i0 + e];
-        if (outs) outs[pos] = __uint_as_float(ckey[i0 + e]);
+        out[pos] = (int32_t)cidx[pslot(i0 + e)];
+        if (outs) outs[pos] = __uint_as_float(ckey[pslot(i0 + e)]);
         ++pos;
       }
     written += tot;
@@ -637,7 +769,7 @@ SelectPlan select_plan(const Dims& d, int batch, int n_q, int32_t max_pos_end) {
   p.off_hist = off;
   if (!p.resident) off = align(off + sizeof(uint32_t) * (size_t)rows * p.n_sseg * kHistWords);
   p.off_slots = off;
-  if (p.n_fseg > 1 || p.resident) off = align(off + sizeof(uint2) * (size_t)rows * kCandCap);
+  if (p.n_fseg > 1) off = align(off + sizeof(uint2) * (size_t)rows * kCandCap);
   p.off_slotcnt = off;
   p.off_done = off;
   off = align(off + sizeof(uint32_t) * (size_t)rows);
@@ -669,10 +801,11 @@ hipError_t launch_select(const Dims& d, const SelectPlan& pl, int batch, int n_q
   a.sel_scores = sel_scores;
   dim3 grid((unsigned)((int64_t)batch * n_q), (unsigned)pl.n_fseg);
   if (pl.resident) {
-    const int64_t rows = (int64_t)batch * n_q;
-    hipLaunchKernelGGL(select_compact_kernel, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, st, a,
-                       rows);
-    hipLaunchKernelGGL(select_finish_kernel, dim3((unsigned)rows), dim3(kThreads), 0, st, a);
+    const dim3 g((unsigned)((int64_t)batch * n_q));
+    if (pl.W <= kRowShortMax)
+      hipLaunchKernelGGL((select_row_kernel<256, 4, false>), g, dim3(256), 0, st, a);
+    else
+      hipLaunchKernelGGL((select_row_kernel<256, 4, true>), g, dim3(256), 0, st, a);
   } else if (pl.n_fseg > 1 && pl.sseg <= 1024 && pl.fseg <= kWaves)
     hipLaunchKernelGGL(filter_select_kernel<true>, grid, dim3(kThreads), 0, st, a);
   else

@@ -180,6 +180,15 @@ def test_chunked_prefill_small_ragged():
     _check_rows(x, dl, outs, {s: list(range(0, 701, 2)) for s in range(2)})
 
 
+def test_prefill_long_rows_match_oracle():
+    say("chunked prefill bf16: 64 queries over a 200K-token cache (long-row streaming select)")
+    # c ~ 50K blocks per row: past the short-row shape, so the selection
+    # streams each row with the rising floor
+    x = synth.chunked(cache=200000, chunk=64, batch=1, window=2048, n_far=10)
+    dl, outs = _run_prefill(x)
+    _check_rows(x, dl, outs, {0: list(range(64))}, check_attn=False)
+
+
 def test_chunked_equals_monolithic_bitwise():
     say("chunked == monolithic")
     x = synth.prefill(n=2600, needle_frac=0.02)
