@@ -206,7 +206,7 @@ qsa_status qsa_select_topk(const qsa_config* cfg, int32_t batch, int32_t n_q,
                                    workspace, stream);
   if (e == hipSuccess)
     e = qsa::launch_select(d, pl, batch, n_q, q_pos0, cap_tokens, workspace, sel_blocks,
-                           sel_count, sel_scores, stream);
+                           sel_count, sel_scores, q_idx, k_cmp, stream);
   return launched(fn, e);
 }
 

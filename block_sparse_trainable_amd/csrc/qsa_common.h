@@ -158,7 +158,8 @@ hipError_t launch_score(const Dims& d, const SelectPlan& pl, int batch, int n_q,
 
 hipError_t launch_select(const Dims& d, const SelectPlan& pl, int batch, int n_q,
                          const int32_t* q_pos0, int64_t cap, void* workspace, int32_t* sel,
-                         int32_t* cnt, float* sel_scores, hipStream_t st);
+                         int32_t* cnt, float* sel_scores, const void* q_idx, const void* k_cmp,
+                         hipStream_t st);
 
 // ------------------------------------------------------ fused decode step ----
 // Score segments of 1024 blocks (a row's last segment also takes a remainder

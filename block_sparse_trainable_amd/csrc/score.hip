@@ -45,7 +45,7 @@ __device__ __forceinline__ float relu_sum4(f32x4 a) {
 }
 
 struct ScoreOut {
-  float* scores;      // [batch][nq_pad][W]
+  float* scores;      // [batch][nq_pad][W] f32 (16-bit keys for the streamed prefill rows)
   int64_t W;
   int64_t nq_pad;     // score rows per sequence (n_q rounded up for the prefill tiles)
   uint32_t* hist;     // [rows][n_sseg][kHistWords]
@@ -155,8 +155,13 @@ __global__ __launch_bounds__(256, HIST ? 2 : 3) void score_mfma_prefill_kernel(
   }
   // The tile's rows (queries past n_q have padding rows of their own), so
   // every score store below is unconditional: a lane past its query's
-  // candidates writes a slot the selection never reads.
+  // candidates writes a slot the selection never reads.  Without HIST the
+  // rows hold 16-bit keys: the top half of each score's bits, which orders
+  // like the score (the selection resolves keys equal at its threshold from
+  // exact recomputed scores).
   float* __restrict__ tile = scores + ((int64_t)s * o.nq_pad + j0) * W;
+  uint16_t* __restrict__ tile16 =
+      reinterpret_cast<uint16_t*>(scores) + ((int64_t)s * o.nq_pad + j0) * W;
   // Smallest candidate count among the wave's 16 queries (0 if any is past
   // n_q): chunks below it need no per-score mask.
   const int jw = j0 + 16 * wave;
@@ -219,7 +224,10 @@ __global__ __launch_bounds__(256, HIST ? 2 : 3) void score_mfma_prefill_kernel(
         for (int c2 = 0; c2 < 2; ++c2) {
           const int ct = 2 * half + c2;
           const float v = relu_sum4(acc[rt][c2]);
-          tile[drow[rt] + (uint32_t)cb + 16 * ct] = v;
+          if constexpr (HIST)
+            tile[drow[rt] + (uint32_t)cb + 16 * ct] = v;
+          else
+            tile16[drow[rt] + (uint32_t)cb + 16 * ct] = (uint16_t)(__float_as_uint(v) >> 16);
           if constexpr (HIST)
             if (full || cb + 16 * ct + l16 < cq[rt]) hist_add_nonneg(hq[rt], v);
         }

@@ -91,7 +91,9 @@ __device__ __forceinline__ void select_row_global_nt(const uint32_t* bits, int64
 }
 
 struct FilterArgs {
-  const float* scores;
+  const float* scores;      // f32 rows (16-bit keys on the streamed prefill path)
+  const uint16_t* q_idx;    // indexer queries and compressed keys (bf16): exact
+  const uint16_t* k_cmp;    //   scores of keys tied at a 16-bit threshold
   int64_t W;
   const uint32_t* hist;     // per-score-segment histograms
   int64_t sseg, n_sseg;     // blocks per score segment, segments per row (max)
@@ -400,23 +402,39 @@ __global__ __launch_bounds__(kThreads) void filter_select_kernel(FilterArgs a) {
 
 // ---------------------------------------------------------------------------
 // Rows selected without histograms (the prefill shape: many rows of at most
-// kStreamMax candidates), in two kernels.
-// select_compact_kernel, one wave per row, no LDS and no barriers:
-//   1. a strided sample of the row (one 16-byte piece per lane) gives its
-//      mean and spread, hence a floor F with, for a roughly normal row, about
-//      2 k_B keys at or above it (normal upper-tail quantile);
-//   2. the wave streams the row and appends the keys >= F with their indices,
-//      in index order, to the row's candidate list (ballot compaction);
-//   3. unless k_B <= count <= kCandCap, F moves and the row is streamed again
-//      (a few tries; then the row is marked for the exact fallback).  Every
-//      accepted F is correct: the k_B largest keys are all >= F.
-// select_finish_kernel, one workgroup per row: a radix select over the
-// candidates finds the k_B-th largest key and the ordered pass writes the
-// kept ids ascending, ties to the lower index.
-// The scores of this path are MFMA ReLU sums, never negative: their bits are
-// the keys as they are.  F is at least the smallest positive float, so zero
-// scores never count (a row that needs them takes the fallback).
+// kStreamMax candidates).  The scoring kernel leaves 16-bit keys for these
+// rows: the top half of each score's bits, which orders like the score.  One
+// workgroup per row:
+//   1. a strided sample of the row gives its mean and spread, hence a floor F
+//      with, for a roughly normal row, about 2 k_B keys at or above it
+//      (normal upper-tail quantile);
+//   2. the row is streamed once; the keys >= F are compacted, in index order,
+//      into an LDS pool.  Long rows let F rise when the pool fills: it moves
+//      to the (k_B + kPrune)-th largest key kept so far, still a valid floor
+//      since at least k_B keys of the row are at or above it.  Unless
+//      k_B <= pool size, F moves down and the row is streamed again (a few
+//      tries, then the exact whole-row fallback);
+//   3. a radix select over the pool finds the 16-bit threshold key T.  Keys
+//      above T are kept.  If the keys equal to T are more than the places
+//      left, their exact scores are recomputed in fp32 from the indexer
+//      query and the compressed keys, and the largest are kept, equal exact
+//      scores going to the lower index;
+//   4. the ordered pass writes the kept ids ascending.  The reported score is
+//      the exact one for keys equal to T, else the key's value (its top 16
+//      bits: at most 2^-8 below the score).
+// In the pool a key is stored as key << 15 (bits 30..15), so the generic
+// radix select resolves it in two digits.
 constexpr int64_t kStreamMax = int64_t{1} << 20;   // candidates per row this path takes
+constexpr int kRowCap = 3072;                      // pool capacity (candidates)
+// pool slot i lives at i + i / 16: the ordered pass reads 16 consecutive
+// slots per thread, which would otherwise all fall in two banks
+__device__ __forceinline__ uint32_t pslot(uint32_t i) { return i + (i >> 4); }
+constexpr int64_t kRowShortMax = 40960;            // candidates of a "short" row
+constexpr int kPrune = 256;                        // keys kept above k_B when the pool is pruned
+constexpr uint32_t kBand = 0x80000000u;            // cidx flag: key equal to the threshold
+constexpr uint32_t kBandKept = 0x40000000u;        // cidx flag: ... and kept
+constexpr uint32_t kIdxMask = 0x3FFFFFFFu;
+constexpr int kBandMax = 256;                      // band keys resolved in the pool
 
 // z with P(Z > z) = p for a standard normal Z and 0 < p < 0.5: Abramowitz &
 // Stegun 26.2.23 (absolute error below 4.5e-4).
@@ -426,76 +444,145 @@ __device__ __forceinline__ float normal_upper_quantile(float p) {
                  (1.0f + t * (1.432788f + t * (0.189269f + t * 0.001308f)));
 }
 
-struct RowOf {
-  int s, j;
-  int64_t c;
-  const uint32_t* bits;
-};
-__device__ __forceinline__ RowOf row_of(const FilterArgs& a, int64_t row) {
-  RowOf r;
-  r.s = (int)(row / a.n_q);
-  r.j = (int)(row % a.n_q);
-  const int64_t p = max((int64_t)a.q_pos0[r.s] + r.j, (int64_t)0);
-  r.c = min(p / 4, min(a.cap_blocks, a.W));
-  r.bits = reinterpret_cast<const uint32_t*>(a.scores + (r.s * a.nq_pad + r.j) * a.W);
-  return r;
+// Block importance of one block in fp32 ("QSA (Qwen Sparse Attention)", Key
+// math / How it works, (A)): qs holds the row's 4 x 128 indexer query in fp32
+// (LDS, read as a broadcast), kb the block's 128 bf16 compressed-key values.
+// Returns the bits of the non-negative result.
+__device__ __forceinline__ uint32_t exact_score_bits(const float* qs, const uint16_t* kb) {
+  float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll 4
+  for (int c16 = 0; c16 < 16; ++c16) {
+    const u32x4 w = ld16(kb + 8 * c16);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float kv = bf16_to_f32((e & 1) ? (w[e >> 1] >> 16) : (w[e >> 1] & 0xFFFFu));
+#pragma unroll
+      for (int h = 0; h < 4; ++h) acc[h] = fmaf(qs[h * 128 + 8 * c16 + e], kv, acc[h]);
+    }
+  }
+  return __float_as_uint(relu(acc[0]) + relu(acc[1]) + relu(acc[2]) + relu(acc[3]));
+}
+
+__device__ __forceinline__ float key16_value(uint32_t pool_key) {
+  return __uint_as_float((pool_key >> 15) << 16);
+}
+
+// Exact selection over a whole row of 16-bit keys in global memory (the
+// fallback), with keys tied at the threshold resolved from exact scores.
+template <int NT, class ExactFn>
+__device__ __forceinline__ void select_row_global16(const uint16_t* keys, int64_t c, int kB, int32_t* out,
+                                    float* outs, uint32_t* hist, uint32_t* scratch, ExactFn exact) {
+  auto key = [&](int64_t i) { return (uint32_t)keys[i] << 15; };
+  auto all = [&](int64_t) { return true; };
+  const Radix r = radix_select<NT>(key, all, c, (uint32_t)kB, hist, scratch, 0, 0u, 0u, 1);
+  const bool band = r.need < r.avail;
+  Radix r2{0u, 0u, 0u, 0u}, r3{0u, 0u, 0u, 0u};
+  bool ties = false;
+  auto in_band = [&](int64_t i) { return (key(i) & r.mask) == r.prefix; };
+  if (band) {
+    auto ex = [&](int64_t i) { return exact((uint32_t)i); };
+    r2 = radix_select<NT>(ex, in_band, c, r.need, hist, scratch);
+    ties = r2.need < r2.avail;
+    if (ties) {
+      auto ik = [&](int64_t i) { return 0x7FFFFFFFu - (uint32_t)i; };
+      auto eq = [&](int64_t i) { return in_band(i) && (exact((uint32_t)i) & r2.mask) == r2.prefix; };
+      r3 = radix_select<NT>(ik, eq, c, r2.need, hist, scratch);
+    }
+  }
+  uint32_t written = 0;
+  const int tid = threadIdx.x;
+  for (int64_t base = 0; base < c; base += 4 * NT) {
+    const int64_t i0 = base + 4 * tid;
+    uint32_t take = 0;
+    float val[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      val[e] = 0.0f;
+      const int64_t i = i0 + e;
+      if (i >= c) continue;
+      const uint32_t k = key(i) & r.mask;
+      if (k > r.prefix || (!band && k == r.prefix)) {
+        take |= 1u << e;
+        val[e] = key16_value(key(i));
+      } else if (band && k == r.prefix) {
+        const uint32_t x = exact((uint32_t)i);
+        const uint32_t m = x & r2.mask;
+        if (m > r2.prefix ||
+            (m == r2.prefix && (!ties || ((0x7FFFFFFFu - (uint32_t)i) & r3.mask) >= r3.prefix))) {
+          take |= 1u << e;
+          val[e] = __uint_as_float(x);
+        }
+      }
+    }
+    uint32_t tot;
+    uint32_t pos = written + block_excl_scan<NT>((uint32_t)__popc(take), scratch, &tot);
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      if (take & (1u << e)) {
+        out[pos] = (int32_t)(i0 + e);
+        if (outs) outs[pos] = val[e];
+        ++pos;
+      }
+    written += tot;
+  }
 }
 
 // One workgroup of NT threads per row: sample, stream in batches of BATCH
-// 16-byte pieces per thread compacting into the LDS pool in index order,
-// then the radix select and the ordered output.  PRUNE (long rows) lets the
-// floor rise during the pass instead of streaming the row again.
-constexpr int kRowCap = 3072;                  // pool capacity (candidates)
-// pool slot i lives at i + i / 16: the ordered pass reads 16 consecutive
-// slots per thread, which would otherwise all fall in two banks
-__device__ __forceinline__ uint32_t pslot(uint32_t i) { return i + (i >> 4); }
-constexpr int64_t kRowShortMax = 40960;        // candidates of a "short" row
-constexpr int kPrune = 256;                    // keys kept above k_B when the pool is pruned
-
+// 16-byte pieces (8 keys each) per thread, compacting into the LDS pool in
+// index order, then the threshold and the ordered output.  PRUNE (long rows)
+// lets the floor rise during the pass instead of streaming the row again.
 template <int NT, int BATCH, bool PRUNE>
 __global__ __launch_bounds__(NT) void select_row_kernel(FilterArgs a) {
-  constexpr int kRowThreads = NT;
-  constexpr int kRowWaves = NT / 64;
-  constexpr int kRowBatch = BATCH;
-  constexpr int kRowSlots = kRowCap + kRowCap / 16 + NT;  // + one trash slot per thread
-  static_assert(kRowWaves % 4 == 0, "batch offsets read 4-wave groups of counts");
-  __shared__ uint32_t ckey[kRowSlots];
-  __shared__ uint32_t cidx[kRowSlots];
+  constexpr int NW = NT / 64;
+  constexpr int kSlots = kRowCap + kRowCap / 16 + NT;  // + one trash slot per thread
+  static_assert(NW % 4 == 0, "batch offsets read 4-wave groups of counts");
+  __shared__ uint32_t ckey[kSlots];
+  __shared__ uint32_t cidx[kSlots];
   __shared__ uint32_t hist[kRadixBins];
-  __shared__ __attribute__((aligned(16))) uint32_t wt[kRowBatch * kRowWaves];
-  __shared__ float fred[3 * kRowWaves];
+  __shared__ __attribute__((aligned(16))) uint32_t wt[BATCH * NW];
+  __shared__ float fred[3 * NW];
+  __shared__ float qs[512];
   __shared__ uint32_t scratch[64];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int64_t row = blockIdx.x;
-  const RowOf ro = row_of(a, row);
-  const int64_t c = ro.c;
-  const uint32_t* bits = ro.bits;
+  const int s = (int)(row / a.n_q);
+  const int j = (int)(row % a.n_q);
+  const int64_t p = max((int64_t)a.q_pos0[s] + j, (int64_t)0);
+  const int64_t c = min(p / 4, min(a.cap_blocks, a.W));
+  const uint16_t* keys = reinterpret_cast<const uint16_t*>(a.scores) + (s * a.nq_pad + j) * a.W;
   int32_t* out = a.sel + row * a.kB;
   float* outs = a.sel_scores ? a.sel_scores + row * a.kB : nullptr;
   const int kB = a.kB;
 
   if (c <= kB) {  // every candidate is kept
-    for (int i = tid; i < kB; i += kRowThreads) {
+    for (int i = tid; i < kB; i += NT) {
       out[i] = i < c ? i : -1;
-      if (outs) outs[i] = i < c ? __uint_as_float(bits[i]) : 0.0f;
+      if (outs) outs[i] = i < c ? key16_value((uint32_t)keys[i] << 15) : 0.0f;
     }
     if (tid == 0) a.cnt[row] = (int32_t)c;
     return;
   }
   const int ci = (int)c;
+  // the row's indexer query in fp32, for exact scores of tied keys
+  {
+    const uint16_t* qrow = a.q_idx + ((int64_t)s * a.n_q + j) * 512;
+    for (int i = tid; i < 512; i += NT) qs[i] = bf16_to_f32(qrow[i]);
+  }
+  const uint16_t* kseq = a.k_cmp + (int64_t)s * a.cap_blocks * 128;
+  auto exact = [&](uint32_t b) { return exact_score_bits(qs, kseq + (int64_t)b * 128); };
 
-  // ---- 1. sampled mean and spread ----------------------------------------
+  // ---- 1. sampled mean and spread (the barrier also publishes qs) --------
   float sm = 0.0f, sq = 0.0f, sn = 0.0f;
   {
-    const int n4 = (ci + 3) / 4;
-    const int k = (int)((int64_t)tid * n4 / kRowThreads);
-    const u32x4 w = *reinterpret_cast<const u32x4*>(bits + 4 * k);
+    const int n8 = (ci + 7) / 8;
+    const int k = (int)((int64_t)tid * n8 / NT);
+    const u32x4 w = *reinterpret_cast<const u32x4*>(keys + 8 * k);
 #pragma unroll
-    for (int e = 0; e < 4; ++e)
-      if (4 * k + e < ci) {
-        const float x = __uint_as_float(w[e]);
+    for (int e = 0; e < 8; ++e)
+      if (8 * k + e < ci) {
+        const float x = __uint_as_float(((e & 1) ? (w[e >> 1] >> 16) : (w[e >> 1] & 0xFFFFu)) << 16);
         sm += x;
         sq = fmaf(x, x, sq);
         sn += 1.0f;
@@ -509,78 +596,72 @@ __global__ __launch_bounds__(NT) void select_row_kernel(FilterArgs a) {
   }
   if (lane == 0) {
     fred[wave] = sm;
-    fred[kRowWaves + wave] = sq;
-    fred[2 * kRowWaves + wave] = sn;
+    fred[NW + wave] = sq;
+    fred[2 * NW + wave] = sn;
   }
   __syncthreads();
   sm = sq = sn = 0.0f;
 #pragma unroll
-  for (int w = 0; w < kRowWaves; ++w) {
+  for (int w = 0; w < NW; ++w) {
     sm += fred[w];
-    sq += fred[kRowWaves + w];
-    sn += fred[2 * kRowWaves + w];
+    sq += fred[NW + w];
+    sn += fred[2 * NW + w];
   }
   const float mu = sm / sn;
   const float sd = sqrtf(fmaxf(sq / sn - mu * mu, 0.0f));
   const float pfrac = 2.0f * (float)kB / (float)ci;
   float z = pfrac < 0.5f ? normal_upper_quantile(pfrac) : -INFINITY;
 
-  // ---- 2./3. stream the row into the pool; accept or move the floor ------
+  // ---- 2. stream the row into the pool; accept or move the floor ---------
+  constexpr int kStep = 8 * NT * BATCH;
+  const int last8 = (ci - 1) & ~7;
   uint32_t n_f = 0u;
   bool ok = false;
   for (int attempt = 0; attempt < 4 && !ok; ++attempt) {
+    // F as a pool key, at least the smallest positive one: zero keys never
+    // count (a row that needs them takes the fallback)
     const float f = z == -INFINITY ? 0.0f : fmaxf(mu + z * sd, 0.0f);
-    uint32_t fbits = max(__float_as_uint(f), 1u);
+    uint32_t fkey = max(__float_as_uint(f) >> 16, 1u) << 15;
     uint32_t total = 0u;   // uniform: candidates before this batch
     bool overflow = false;
-    constexpr int kStep = 4 * kRowThreads * kRowBatch;
-    // batches double-buffered in registers: the next one's loads are in
-    // flight while this one is compacted
-    // Loads are unconditional (addresses clamped to the row's last piece;
-    // keys past c are masked by index below), so the compiler can count
-    // them and wait for this batch only.
-    const int last4 = (ci - 1) & ~3;
-    u32x4 nx[kRowBatch];
+    // batches double-buffered in registers; loads are unconditional
+    // (addresses clamped to the row's last piece, keys past c masked by
+    // index) so the compiler waits for the current batch only
+    u32x4 nx[BATCH];
 #pragma unroll
-    for (int b = 0; b < kRowBatch; ++b) {
-      const int i0 = 4 * (tid + kRowThreads * b);
-      nx[b] = *reinterpret_cast<const u32x4*>(bits + min(i0, last4));
-    }
+    for (int b = 0; b < BATCH; ++b)
+      nx[b] = *reinterpret_cast<const u32x4*>(keys + min(8 * (tid + NT * b), last8));
     for (int base = 0; base < ci; base += kStep) {
-      u32x4 v[kRowBatch];
+      u32x4 v[BATCH];
 #pragma unroll
-      for (int b = 0; b < kRowBatch; ++b) v[b] = nx[b];
+      for (int b = 0; b < BATCH; ++b) v[b] = nx[b];
 #pragma unroll
-      for (int b = 0; b < kRowBatch; ++b) {
-        const int i0 = base + kStep + 4 * (tid + kRowThreads * b);
-        nx[b] = *reinterpret_cast<const u32x4*>(bits + min(i0, last4));
-      }
+      for (int b = 0; b < BATCH; ++b)
+        nx[b] = *reinterpret_cast<const u32x4*>(keys + min(base + kStep + 8 * (tid + NT * b), last8));
+      auto k16 = [&](int b, int e) {
+        return ((e & 1) ? (v[b][e >> 1] >> 16) : (v[b][e >> 1] & 0xFFFFu)) << 15;
+      };
       // Index order within the batch is (b, wave, lane, e).  Each lane's
-      // count per piece b (0..4) is scanned across the wave three pieces at
-      // a time in 10-bit fields; the wave totals per b go through LDS.  If
-      // the pool cannot take the batch, the floor first rises to the
-      // (k_B + kPrune)-th largest key kept so far (still a valid floor: at
-      // least k_B keys of the row are at or above it), the pool keeps only
-      // the keys at or above it, and the batch is counted again.
+      // count per piece (0..8) is scanned across the wave three pieces at a
+      // time in 10-bit fields; the wave totals per piece go through LDS.
       const bool full = base + kStep <= ci;
-      uint32_t excl[kRowBatch];
+      uint32_t excl[BATCH];
       for (int pass = 0;; ++pass) {
-        uint32_t cnt[kRowBatch];
+        uint32_t cnt[BATCH];
 #pragma unroll
-        for (int b = 0; b < kRowBatch; ++b) {
-          const int i0 = base + 4 * (tid + kRowThreads * b);
+        for (int b = 0; b < BATCH; ++b) {
+          const int i0 = base + 8 * (tid + NT * b);
           uint32_t n = 0;
 #pragma unroll
-          for (int e = 0; e < 4; ++e)
-            n += (v[b][e] >= fbits && (full || i0 + e < ci)) ? 1u : 0u;
+          for (int e = 0; e < 8; ++e) n += (k16(b, e) >= fkey && (full || i0 + e < ci)) ? 1u : 0u;
           cnt[b] = n;
         }
 #pragma unroll
-        for (int g = 0; g < kRowBatch; g += 3) {
+        for (int g = 0; g < BATCH; g += 3) {
           uint32_t x = 0;
 #pragma unroll
           for (int q = 0; q < 3; ++q)
-            if (g + q < kRowBatch) x |= cnt[g + q] << (10 * q);
+            if (g + q < BATCH) x |= cnt[g + q] << (10 * q);
           uint32_t incl = x;
 #pragma unroll
           for (int off = 1; off < 64; off <<= 1) {
@@ -591,15 +672,15 @@ __global__ __launch_bounds__(NT) void select_row_kernel(FilterArgs a) {
           const uint32_t tot = __shfl(incl, 63);
 #pragma unroll
           for (int q = 0; q < 3; ++q)
-            if (g + q < kRowBatch) {
+            if (g + q < BATCH) {
               excl[g + q] = (ex >> (10 * q)) & 1023u;
-              if (lane == 0) wt[(g + q) * kRowWaves + wave] = (tot >> (10 * q)) & 1023u;
+              if (lane == 0) wt[(g + q) * NW + wave] = (tot >> (10 * q)) & 1023u;
             }
         }
         __syncthreads();
         uint32_t btot = 0u;
 #pragma unroll
-        for (int q = 0; q < kRowBatch * kRowWaves; q += 4) {
+        for (int q = 0; q < BATCH * NW; q += 4) {
           const u32x4 r4 = *reinterpret_cast<const u32x4*>(&wt[q]);
           btot += r4[0] + r4[1] + r4[2] + r4[3];
         }
@@ -608,71 +689,73 @@ __global__ __launch_bounds__(NT) void select_row_kernel(FilterArgs a) {
           overflow = true;
           break;
         }
-        if constexpr (!PRUNE) break;
-        // raise the floor and prune the pool (stable, in place)
-        auto pkey = [&](int64_t i) { return ckey[pslot((uint32_t)i)]; };
-        auto pall = [&](int64_t) { return true; };
-        const Radix rp = radix_select<kRowThreads>(pkey, pall, (int64_t)total,
-                                                   (uint32_t)(kB + kPrune), hist, scratch);
-        fbits = max(fbits, rp.prefix);
-        // kept entries staged in the (now idle) radix histogram, then copied
-        // back in order
-        constexpr int E = kRowCap / kRowThreads;
-        constexpr uint32_t kStage = kRadixBins / 2;
-        uint32_t keep = 0;
+        if constexpr (PRUNE) {
+          // raise the floor to the (k_B + kPrune)-th largest pool key and keep
+          // only the keys at or above it (staged through the idle radix
+          // histogram, then copied back in order)
+          auto pkey = [&](int64_t i) { return ckey[pslot((uint32_t)i)]; };
+          auto pall = [&](int64_t) { return true; };
+          const Radix rp = radix_select<NT>(pkey, pall, (int64_t)total, (uint32_t)(kB + kPrune), hist,
+                                            scratch, 0, 0u, 0u, 1);
+          fkey = max(fkey, rp.prefix);
+          constexpr int E = kRowCap / NT;
+          constexpr uint32_t kStage = kRadixBins / 2;
+          uint32_t keep = 0;
 #pragma unroll
-        for (int q = 0; q < E; ++q) {
-          const uint32_t i = (uint32_t)(E * tid + q);
-          keep += (i < total && ckey[pslot(i)] >= fbits) ? 1u : 0u;
-        }
-        uint32_t kept;
-        uint32_t at = block_excl_scan<kRowThreads>(keep, scratch, &kept);
-        if (kept > kStage) {   // ties at the new floor: cannot happen short of
-          overflow = true;     // hundreds of equal keys; take the retry path
-          break;
-        }
+          for (int q = 0; q < E; ++q) {
+            const uint32_t i = (uint32_t)(E * tid + q);
+            keep += (i < total && ckey[pslot(i)] >= fkey) ? 1u : 0u;
+          }
+          uint32_t kept;
+          uint32_t at = block_excl_scan<NT>(keep, scratch, &kept);
+          if (kept > kStage) {   // hundreds of equal keys at the new floor
+            overflow = true;
+            break;
+          }
 #pragma unroll
-        for (int q = 0; q < E; ++q) {
-          const uint32_t i = (uint32_t)(E * tid + q);
-          if (i < total) {
-            const uint32_t k = ckey[pslot(i)];
-            if (k >= fbits) {
-              hist[2 * at] = k;
-              hist[2 * at + 1] = cidx[pslot(i)];
-              ++at;
+          for (int q = 0; q < E; ++q) {
+            const uint32_t i = (uint32_t)(E * tid + q);
+            if (i < total) {
+              const uint32_t k = ckey[pslot(i)];
+              if (k >= fkey) {
+                hist[2 * at] = k;
+                hist[2 * at + 1] = cidx[pslot(i)];
+                ++at;
+              }
             }
           }
+          __syncthreads();
+          for (uint32_t i = tid; i < kept; i += NT) {
+            ckey[pslot(i)] = hist[2 * i];
+            cidx[pslot(i)] = hist[2 * i + 1];
+          }
+          total = kept;
+          __syncthreads();
         }
-        __syncthreads();
-        for (uint32_t i = tid; i < kept; i += kRowThreads) {
-          ckey[pslot(i)] = hist[2 * i];
-          cidx[pslot(i)] = hist[2 * i + 1];
-        }
-        total = kept;
-        __syncthreads();
       }
       if (overflow) break;
-      // wave-uniform offsets: (b, wave) order over the 4-wave rows of wt
+      // wave-uniform offsets in (b, wave) order; non-candidates write to this
+      // lane's trash slot past the pool
       uint32_t run = total;
-      // non-candidates write to this lane's trash slot past the pool
       const uint32_t trash = (uint32_t)(kRowCap + kRowCap / 16) + (uint32_t)tid;
 #pragma unroll
-      for (int b = 0; b < kRowBatch; ++b) {
+      for (int b = 0; b < BATCH; ++b) {
         uint32_t off = run;
 #pragma unroll
-        for (int w4 = 0; w4 < kRowWaves; w4 += 4) {
-          const u32x4 r4 = *reinterpret_cast<const u32x4*>(&wt[b * kRowWaves + w4]);
+        for (int w4 = 0; w4 < NW; w4 += 4) {
+          const u32x4 r4 = *reinterpret_cast<const u32x4*>(&wt[b * NW + w4]);
 #pragma unroll
           for (int w = 0; w < 4; ++w) off += w4 + w < wave ? r4[w] : 0u;
           run += r4[0] + r4[1] + r4[2] + r4[3];
         }
         uint32_t at = off + excl[b];
-        const int i0 = base + 4 * (tid + kRowThreads * b);
+        const int i0 = base + 8 * (tid + NT * b);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const bool take = v[b][e] >= fbits && (full || i0 + e < ci);
+        for (int e = 0; e < 8; ++e) {
+          const uint32_t kk = k16(b, e);
+          const bool take = kk >= fkey && (full || i0 + e < ci);
           const uint32_t slot = take && at < (uint32_t)kRowCap ? pslot(at) : trash;
-          ckey[slot] = v[b][e];
+          ckey[slot] = kk;
           cidx[slot] = (uint32_t)(i0 + e);
           at += take ? 1u : 0u;
         }
@@ -684,58 +767,127 @@ __global__ __launch_bounds__(NT) void select_row_kernel(FilterArgs a) {
     if (overflow) {
       z = z == -INFINITY ? 0.0f : z + 0.5f;
     } else if (total < (uint32_t)kB) {
-      if (fbits == 1u) break;              // too few positive scores
+      if (fkey == (1u << 15)) break;        // too few positive scores
       z = z - 1.0f < -3.0f ? -INFINITY : z - 1.0f;
-    } else if (total > (uint32_t)kRowCap) {
-      z = z == -INFINITY ? 0.0f : z + 0.5f;
     } else {
       ok = true;
     }
   }
   if (__builtin_expect(!ok, 0)) {
-    select_row_global_nt<kRowThreads>(bits, c, kB, out, outs, hist, scratch);
+    select_row_global16<NT>(keys, c, kB, out, outs, hist, scratch, exact);
     if (tid == 0) a.cnt[row] = kB;
     return;
   }
 
-  // ---- 4. the k_B-th largest key, then the ordered output -----------------
+  // ---- 3. the 16-bit threshold, then exact scores for the keys equal to it
   auto key = [&](int64_t i) { return ckey[pslot((uint32_t)i)]; };
   auto all = [&](int64_t) { return true; };
-  const Radix r = radix_select<kRowThreads>(key, all, (int64_t)n_f, (uint32_t)kB, hist, scratch);
-  uint32_t written = 0, eq_seen = 0;
-  for (uint32_t base = 0; base < n_f; base += 16 * kRowThreads) {
+  const Radix r = radix_select<NT>(key, all, (int64_t)n_f, (uint32_t)kB, hist, scratch, 0, 0u, 0u, 1);
+  const bool band = r.need < r.avail;
+  if (band) {
+    // the band (keys equal to T) listed in hist: [0, nb) pool indices, then
+    // [kBandMax, +nb) exact score bits
+    uint32_t* blist = hist;
+    uint32_t* bval = hist + kBandMax;
+    uint32_t* bcount = &scratch[48];
+    if (tid == 0) *bcount = 0u;
+    __syncthreads();
+    for (uint32_t i = tid; i < n_f; i += NT)
+      if ((ckey[pslot(i)] & r.mask) == r.prefix) {
+        const uint32_t at = atomicAdd(bcount, 1u);
+        if (at < (uint32_t)kBandMax) blist[at] = i;
+      }
+    __syncthreads();
+    const uint32_t nb = *bcount;
+    if (__builtin_expect(nb > (uint32_t)kBandMax, 0)) {
+      select_row_global16<NT>(keys, c, kB, out, outs, hist, scratch, exact);
+      if (tid == 0) a.cnt[row] = kB;
+      return;
+    }
+    // exact scores, one 16-lane group per band key: lane g16 takes dims
+    // 8 g16 .. 8 g16 + 7 of the four heads; partial sums meet by shuffles
+    {
+      const int grp = tid >> 4, g16 = tid & 15;
+      constexpr int NG = NT / 16;
+      for (uint32_t e0 = 0; e0 < nb; e0 += 4 * NG) {
+        u32x4 kw[4];
+        uint32_t ent[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const uint32_t e = e0 + (uint32_t)(grp + NG * q);
+          ent[q] = e;
+          const uint32_t b = e < nb ? cidx[pslot(blist[e])] : 0u;
+          kw[q] = ld16(kseq + (int64_t)b * 128 + 8 * g16);
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const float kv = bf16_to_f32((e & 1) ? (kw[q][e >> 1] >> 16) : (kw[q][e >> 1] & 0xFFFFu));
+#pragma unroll
+            for (int h = 0; h < 4; ++h) acc[h] = fmaf(qs[h * 128 + 8 * g16 + e], kv, acc[h]);
+          }
+#pragma unroll
+          for (int off = 8; off > 0; off >>= 1)
+#pragma unroll
+            for (int h = 0; h < 4; ++h) acc[h] += __shfl_xor(acc[h], off);
+          if (g16 == 0 && ent[q] < nb)
+            bval[ent[q]] = __float_as_uint(relu(acc[0]) + relu(acc[1]) + relu(acc[2]) + relu(acc[3]));
+        }
+      }
+    }
+    __syncthreads();
+    // rank inside the band: larger exact score first, then the lower index;
+    // the r.need best are kept
+    for (uint32_t e = tid; e < nb; e += NT) {
+      const uint32_t ve = bval[e];
+      const uint32_t ie = cidx[pslot(blist[e])];
+      uint32_t rank = 0;
+      for (uint32_t f = 0; f < nb; ++f) {
+        const uint32_t vf = bval[f];
+        const uint32_t iff = cidx[pslot(blist[f])];
+        rank += (vf > ve || (vf == ve && iff < ie)) ? 1u : 0u;
+      }
+      bval[kBandMax + e] = rank;
+    }
+    __syncthreads();
+    for (uint32_t e = tid; e < nb; e += NT) {
+      const uint32_t sl = pslot(blist[e]);
+      ckey[sl] = bval[e];
+      cidx[sl] |= kBand | (bval[kBandMax + e] < r.need ? kBandKept : 0u);
+    }
+    __syncthreads();
+  }
+
+  // ---- 4. the ordered output ---------------------------------------------
+  uint32_t written = 0;
+  for (uint32_t base = 0; base < n_f; base += 16 * NT) {
     const uint32_t i0 = base + 16 * tid;
-    uint32_t take = 0, eqm = 0;
+    uint32_t take = 0;
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
       const uint32_t i = i0 + e;
       if (i < n_f) {
-        const uint32_t m = ckey[pslot(i)] & r.mask;
-        if (m > r.prefix) take |= 1u << e;
-        else if (m == r.prefix) eqm |= 1u << e;
+        const uint32_t sl = pslot(i);
+        const uint32_t k = ckey[sl], x = cidx[sl];
+        const uint32_t m = k & r.mask;
+        const bool keep = (x & kBand) ? (x & kBandKept) != 0u : (m > r.prefix || (!band && m == r.prefix));
+        if (keep) take |= 1u << e;
       }
     }
-    uint32_t tot_eq;
-    const uint32_t ex_eq = block_excl_scan<kRowThreads>((uint32_t)__popc(eqm), scratch, &tot_eq);
-    uint32_t eq_rank = eq_seen + ex_eq;
-#pragma unroll
-    for (int e = 0; e < 16; ++e)
-      if (eqm & (1u << e)) {
-        if (eq_rank < r.need) take |= 1u << e;
-        ++eq_rank;
-      }
     uint32_t tot;
-    const uint32_t ex = block_excl_scan<kRowThreads>((uint32_t)__popc(take), scratch, &tot);
-    uint32_t pos = written + ex;
+    uint32_t pos = written + block_excl_scan<NT>((uint32_t)__popc(take), scratch, &tot);
 #pragma unroll
     for (int e = 0; e < 16; ++e)
       if (take & (1u << e)) {
-        out[pos] = (int32_t)cidx[pslot(i0 + e)];
-        if (outs) outs[pos] = __uint_as_float(ckey[pslot(i0 + e)]);
+        const uint32_t sl = pslot(i0 + e);
+        const uint32_t x = cidx[sl];
+        out[pos] = (int32_t)(x & kIdxMask);
+        if (outs) outs[pos] = (x & kBand) ? __uint_as_float(ckey[sl]) : key16_value(ckey[sl]);
         ++pos;
       }
     written += tot;
-    eq_seen += tot_eq;
   }
   if (tid == 0) a.cnt[row] = kB;
 }
@@ -765,7 +917,8 @@ SelectPlan select_plan(const Dims& d, int batch, int n_q, int32_t max_pos_end) {
     p.n_fseg = (p.n_sseg + p.fseg - 1) / p.fseg;
   }
   auto align = [](size_t v) { return (v + 255) / 256 * 256; };
-  size_t off = align(sizeof(float) * (size_t)batch * (size_t)p.nq_pad * (size_t)p.W);
+  const size_t key_bytes = p.resident ? sizeof(uint16_t) : sizeof(float);
+  size_t off = align(key_bytes * (size_t)batch * (size_t)p.nq_pad * (size_t)p.W);
   p.off_hist = off;
   if (!p.resident) off = align(off + sizeof(uint32_t) * (size_t)rows * p.n_sseg * kHistWords);
   p.off_slots = off;
@@ -779,10 +932,13 @@ SelectPlan select_plan(const Dims& d, int batch, int n_q, int32_t max_pos_end) {
 
 hipError_t launch_select(const Dims& d, const SelectPlan& pl, int batch, int n_q,
                          const int32_t* q_pos0, int64_t cap, void* workspace, int32_t* sel,
-                         int32_t* cnt, float* sel_scores, hipStream_t st) {
+                         int32_t* cnt, float* sel_scores, const void* q_idx, const void* k_cmp,
+                         hipStream_t st) {
   char* ws = static_cast<char*>(workspace);
   FilterArgs a;
   a.scores = reinterpret_cast<const float*>(ws);
+  a.q_idx = static_cast<const uint16_t*>(q_idx);
+  a.k_cmp = static_cast<const uint16_t*>(k_cmp);
   a.W = pl.W;
   a.hist = reinterpret_cast<const uint32_t*>(ws + pl.off_hist);
   a.sseg = pl.sseg;
@@ -803,9 +959,9 @@ hipError_t launch_select(const Dims& d, const SelectPlan& pl, int batch, int n_q
   if (pl.resident) {
     const dim3 g((unsigned)((int64_t)batch * n_q));
     if (pl.W <= kRowShortMax)
-      hipLaunchKernelGGL((select_row_kernel<256, 4, false>), g, dim3(256), 0, st, a);
+      hipLaunchKernelGGL((select_row_kernel<256, 2, false>), g, dim3(256), 0, st, a);
     else
-      hipLaunchKernelGGL((select_row_kernel<256, 4, true>), g, dim3(256), 0, st, a);
+      hipLaunchKernelGGL((select_row_kernel<256, 2, true>), g, dim3(256), 0, st, a);
   } else if (pl.n_fseg > 1 && pl.sseg <= 1024 && pl.fseg <= kWaves)
     hipLaunchKernelGGL(filter_select_kernel<true>, grid, dim3(kThreads), 0, st, a);
   else

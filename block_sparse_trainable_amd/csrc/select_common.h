@@ -48,16 +48,17 @@ struct Radix {
 
 // MSB-first radix select (11/11/9-bit digits over key bits 30..0) over n keys
 // key(i), counting only keys with elig(i).  first_pass > 0 starts at a later
-// digit with the bits above it already fixed to prefix0/mask0.  hist holds
-// kRadixBins words, scratch NT/64 + 3.
+// digit with the bits above it already fixed to prefix0/mask0; last_pass < 2
+// stops early for keys whose low bits are all zero.  hist holds kRadixBins
+// words, scratch NT/64 + 3.
 template <int NT, class KeyFn, class EligFn>
-__device__ Radix radix_select(KeyFn key, EligFn elig, int64_t n, uint32_t need_in,
+__device__ __forceinline__ Radix radix_select(KeyFn key, EligFn elig, int64_t n, uint32_t need_in,
                               uint32_t* hist, uint32_t* scratch, int first_pass = 0,
-                              uint32_t prefix0 = 0u, uint32_t mask0 = 0u) {
+                              uint32_t prefix0 = 0u, uint32_t mask0 = 0u, int last_pass = 2) {
   constexpr int NW = NT / 64;
   const int tid = threadIdx.x;
   Radix r{prefix0, mask0, need_in, 0xFFFFFFFFu};
-  for (int pass = first_pass; pass < 3; ++pass) {
+  for (int pass = first_pass; pass <= last_pass; ++pass) {
     const int sh = pass == 0 ? 20 : (pass == 1 ? 9 : 0);  // digits: bits 30..20, 19..9, 8..0
     const int nb = pass == 2 ? 512 : 2048;
     const uint32_t dmask = (uint32_t)nb - 1u;

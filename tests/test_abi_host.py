@@ -70,16 +70,16 @@ def _al(v):
 
 def test_workspace_sizes(lib):
     c = cfg()
-    # select, many rows of at most 2^20 candidates: fp32 score rows (64-row
+    # select, many rows of at most 2^20 candidates: 16-bit score keys (64-row
     # tiles per sequence, rows padded to 64 blocks) and completion counters;
     # the rows are selected by streaming them, so no histograms
     rows, W = 2 * 8192, 34816
-    want = _al(4 * rows * W)
+    want = _al(2 * rows * W)
     want = _al(want + 4 * rows)          # completion counters
     assert qsa.qsa_workspace_size(c, B.QSA_OP_SELECT, 2, 8192, 139264) == want
     # a ragged query count: each sequence's rows padded to a multiple of 64
     W = -(-((3000 - 1) // 4) // 64) * 64
-    want = _al(4 * 2 * 3008 * W)
+    want = _al(2 * 2 * 3008 * W)
     want = _al(want + 4 * 2 * 3000)
     assert qsa.qsa_workspace_size(c, B.QSA_OP_SELECT, 2, 3000, 3000) == want
     # prefill rows of more than 2^20 candidates keep per-2048-block-segment
