@@ -23,7 +23,8 @@
 //     - MFMA scores of the segment (the decode scoring kernel's layout), then
 //       a counting sort of the segment's (score, id) pairs by histogram bin,
 //       highest bin first, staged in LDS and stored whole, with the
-//       segment's suffix counts cum[b] = #scores with bin >= b;
+//       segment's suffix counts cum[b] = #scores with bin >= b, which are
+//       also added (atomically) into the row's suffix counts;
 //     - the last workgroup of a row to finish (completion counter) selects:
 //       the row's suffix counts give the threshold bin d*, each segment's
 //       candidates (bin >= d*) are a prefix of its sorted list (all fetched
@@ -118,6 +119,7 @@ struct StepArgs {
   uint32_t* rec;      // [B][kStepRecStride] selection records
   uint2* pairs;       // [B][n_seg][kStepSegMax]
   uint32_t* cum;      // [B][n_seg][128]  (u16 pairs: bins 2w, 2w+1)
+  uint32_t* acc;      // [B][256] row suffix counts, summed by the segments (control area)
   float* part;        // [B][n_split][part_floats(D)]
   int n_seg, n_split, n_score_wg;
 };
@@ -193,10 +195,10 @@ __device__ __forceinline__ void select_row(const StepArgs& a, int s, int64_t c, 
   uint32_t* rec = a.rec + (int64_t)s * kStepRecStride;
   const unsigned long long* prow =
       reinterpret_cast<const unsigned long long*>(a.pairs) + (int64_t)s * a.n_seg * kStepSegMax;
-  const unsigned long long* crow =
-      reinterpret_cast<const unsigned long long*>(a.cum) + (int64_t)s * a.n_seg * 64;
 
+  uint32_t* racc = a.acc + (int64_t)s * 256;
   if (c <= kB) {  // every candidate is kept; they all sit in segment 0
+    coherent_store(&racc[tid], 0u);  // leave the row's counts zeroed
     for (int i = tid; i < c; i += kNT) {
       const unsigned long long v = coherent_load(&prow[i]);
       o_key[(uint32_t)(v >> 32)] = (uint32_t)v;
@@ -213,37 +215,10 @@ __device__ __forceinline__ void select_row(const StepArgs& a, int s, int64_t c, 
     return;
   }
 
-  // ---- 1. row suffix counts S(b) = sum over segments of cum[g][b] -----------
-  const int pw = tid & 63;  // u64 word of a segment: bins 4pw .. 4pw+3
-  const int gs = tid >> 6;  // segments gs, gs + 4, ...
-  const bool hold = nseg_row <= 64;
-  unsigned long long held[16];
-  uint32_t acc4[4] = {0u, 0u, 0u, 0u};
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const int g = gs + 4 * i;
-    held[i] = g < nseg_row ? coherent_load(&crow[(int64_t)g * 64 + pw]) : 0ull;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) acc4[e] += cum_field(held[i], e);
-  }
-  for (int g0 = 64; g0 < nseg_row; g0 += 64) {  // long rows: 16 more segments per pass
-    unsigned long long w[16];
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int g = g0 + gs + 4 * i;
-      w[i] = g < nseg_row ? coherent_load(&crow[(int64_t)g * 64 + pw]) : 0ull;
-    }
-#pragma unroll
-    for (int i = 0; i < 16; ++i)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) acc4[e] += cum_field(w[i], e);
-  }
-#pragma unroll
-  for (int e = 0; e < 4; ++e) rh[gs * 256 + 4 * pw + e] = acc4[e];
-  __syncthreads();
+  // ---- 1. row suffix counts S(b), summed by the segments as they finished --
   {
-    const uint32_t S_t = rh[tid] + rh[256 + tid] + rh[512 + tid] + rh[768 + tid];
-    __syncthreads();
+    const uint32_t S_t = coherent_load(&racc[tid]);  // thread t: bin t
+    coherent_store(&racc[tid], 0u);                   // leave the row's counts zeroed
     rh[1024 + tid] = S_t;
     __syncthreads();
     const uint32_t S_next = tid < 255 ? rh[1024 + tid + 1] : 0u;
@@ -261,13 +236,7 @@ __device__ __forceinline__ void select_row(const StepArgs& a, int s, int64_t c, 
   const uint32_t need = (uint32_t)kB - n_sure;
 
   // ---- 2. candidates of segment g: the first cum[g][d*] entries of its list -
-  if (hold) {
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int g = gs + 4 * i;
-      if (g < nseg_row && pw == (int)(dstar >> 2)) seglen[g] = cum_field(held[i], dstar & 3);
-    }
-  } else {
+  {
     const uint32_t* crow32 = a.cum + (int64_t)s * a.n_seg * 128;
     for (int g = tid; g < nseg_row; g += kNT) {
       const uint32_t w = coherent_load(&crow32[(int64_t)g * 128 + (dstar >> 1)]);
@@ -564,6 +533,10 @@ __device__ __forceinline__ void score_segment(const StepArgs& a, int64_t wg, uns
     const uint32_t start = block_excl_scan<kNT>(nb, scr, &tot);
     curs[255 - tid] = start;
     bins[255 - tid] = start + nb;  // suffix count: scores with bin >= 255 - t
+    // the row's suffix counts accumulate as the segments finish
+    if (start + nb)
+      __hip_atomic_fetch_add(&a.acc[(int64_t)s * 256 + 255 - tid], start + nb, __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
     __syncthreads();
   }
 #pragma unroll
@@ -860,6 +833,7 @@ hipError_t launch_decode_step(const Dims& d, const StepPlan& pl, int batch, cons
     a.rec = ctl + kStepOffRec + (int64_t)r0 * kStepRecStride;
     a.pairs = reinterpret_cast<uint2*>(ws + pl.off_pairs) + (int64_t)r0 * pl.n_seg * kStepSegMax;
     a.cum = reinterpret_cast<uint32_t*>(ws + pl.off_cum) + (int64_t)r0 * pl.n_seg * 128;
+    a.acc = ctl + kStepOffAcc + (int64_t)r0 * 256;
     a.part = reinterpret_cast<float*>(ws + pl.off_part) + (int64_t)r0 * pl.n_split * part_floats(D);
     a.n_seg = pl.n_seg;
     a.n_split = pl.n_split;

@@ -165,8 +165,8 @@ hipError_t launch_select(const Dims& d, const SelectPlan& pl, int batch, int n_q
 // Score segments of 1024 blocks (a row's last segment also takes a remainder
 // of up to 512 blocks); an id bitmap sized for rows of up to kStepBmWords * 32
 // candidate blocks; a fixed control area at the start of the workspace holds
-// the completion counters, the error word and the per-row selection records
-// of up to kStepMaxBatch rows.
+// the completion counters, the error word, the per-row selection records and
+// the per-row score-bin suffix counts of up to kStepMaxBatch rows.
 constexpr int kStepSeg = 1024;
 constexpr int kStepSegMax = kStepSeg + kStepSeg / 2;
 constexpr int kStepBmWords = 8256;
@@ -176,7 +176,8 @@ constexpr int kStepRecStride = 528;      // record words per row (>= k_B + 1)
 constexpr int kStepOffAttn = 1024;       // control-area word offsets
 constexpr int kStepOffErr = 2048;
 constexpr int kStepOffRec = 4096;
-constexpr size_t kStepCtlBytes = 4 * ((size_t)kStepOffRec + (size_t)kStepMaxBatch * kStepRecStride);
+constexpr int kStepOffAcc = kStepOffRec + kStepMaxBatch * kStepRecStride;  // [row][256] counts
+constexpr size_t kStepCtlBytes = 4 * ((size_t)kStepOffAcc + (size_t)kStepMaxBatch * 256);
 
 // Score segments of a row with c candidate blocks: 1024 each, the last one
 // also holding a remainder of up to 512 (non-decreasing in c).

@@ -207,9 +207,10 @@ qsa_status qsa_sparse_attn_decode(const qsa_config* cfg, int32_t batch, const vo
  *   sel_blocks, sel_count, sel_scores   as in qsa_select_topk with n_q = 1.
  *   out, lse   as in qsa_sparse_attn_decode.
  *   workspace  >= qsa_workspace_size(QSA_OP_DECODE_STEP, batch, 1,
- *              max_pos_end) bytes.  Its first 2,179,072 bytes are a control
- *              area (completion counters, per-row selection records, an error
- *              word) that must be ZERO-FILLED BEFORE ITS FIRST USE; every
+ *              max_pos_end) bytes.  Its first 3,227,648 bytes are a control
+ *              area (completion counters, per-row selection records, per-row
+ *              score-bin counts, an error word) that must be ZERO-FILLED
+ *              BEFORE ITS FIRST USE; every
  *              completed call leaves it zero again.  Word 2048 (byte 8192) is
  *              the error word: 1 if a wait for a selection ever gave up
  *              (never expected; the outputs of that call are then invalid).

@@ -184,14 +184,15 @@ def test_product_has_no_oracle_dependency():
 
 def test_decode_step_workspace_size(lib):
     c = cfg()
-    # 2,179,072-byte control area, then (score, id) pairs of the score
+    # 3,227,648-byte control area, then (score, id) pairs of the score
     # segments (room for 1536 each: 1024 plus a remainder of up to 512),
     # per-segment suffix counts (128 words), 17 split states of 16 x (128 + 2)
     batch, mpe = 8, 262211
     c_max = (mpe - 1) // 4
     full, rem = divmod(c_max, 1024)
     nseg = full if rem <= 512 else full + 1
-    want = _al(4 * (4096 + 1024 * 528))
+    want = _al(4 * (4096 + 1024 * 528 + 1024 * 256))
+    assert want == 3227648
     want = _al(want + 8 * batch * nseg * 1536)
     want = _al(want + 4 * batch * nseg * 128)
     want = _al(want + 4 * batch * 17 * (16 * 128 + 32))

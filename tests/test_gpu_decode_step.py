@@ -24,7 +24,7 @@ from tests import _compare as C
 
 pytestmark = pytest.mark.gpu
 
-CTL_WORDS = 4096 + 1024 * 528   # counters, error word (word 2048), selection records
+CTL_WORDS = 4096 + 1024 * 528 + 1024 * 256   # counters, error word (word 2048), records, bin counts
 ERR_WORD = 2048
 
 
