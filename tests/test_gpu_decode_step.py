@@ -93,8 +93,14 @@ def test_fused_step_multi_segment_rows():
 
 
 def test_fused_step_long_rows_over_64_segments():
-    say("fused step: ~300K-token rows (73 score segments: the long-row passes)")
+    say("fused step: ~300K-token rows (73 score segments)")
     x = synth.decode(context=300000, batch=1, steps=3, n_needles=8)
+    _fused_vs_unfused(x, 3, check_oracle_steps=(2,))
+
+
+def test_fused_step_many_rows_and_segments():
+    say("fused step: 20 seqs at ~60K tokens (15 segments each, 300 score workgroups)")
+    x = synth.decode(context=60000, batch=20, steps=3, n_needles=8)
     _fused_vs_unfused(x, 3, check_oracle_steps=(2,))
 
 
