@@ -131,7 +131,12 @@ qsa_status qsa_index_build(const qsa_config* cfg, int32_t batch, const void* k_i
  *   sel_blocks int32 [batch][n_q][k_B]: ascending ids, then -1 padding.
  *   sel_count  int32 [batch][n_q].
  *   sel_scores float [batch][n_q][k_B] or NULL: I of each selected block
- *              (same order as sel_blocks; 0 in padding).
+ *              (same order as sel_blocks; 0 in padding).  With bf16 data
+ *              and n_q >= 16 the scores are kept as 16-bit keys (the top
+ *              half of the fp32 bits, truncated: relative error below
+ *              2^-7); blocks whose keys tie at the selection threshold are
+ *              rescored in fp32 to decide the selection, and report that
+ *              fp32 value.  The selection itself follows the fp32 scores.
  *   workspace  >= qsa_workspace_size(QSA_OP_SELECT, batch, n_q, max_pos_end).
  */
 qsa_status qsa_select_topk(const qsa_config* cfg, int32_t batch, int32_t n_q,
