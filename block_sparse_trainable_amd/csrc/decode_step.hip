@@ -215,9 +215,22 @@ __device__ __forceinline__ void select_row(const StepArgs& a, int s, int64_t c, 
     return;
   }
 
-  // ---- 1. row suffix counts S(b), summed by the segments as they finished --
+  // ---- 1. row suffix counts S(b), summed by the segments as they finished,
+  // and in the same round trip the first P entries of every segment's list
+  // (P = 64, 32 or 16 as the segments number up to 64, 128 or 256): a
+  // segment's candidates lead its list, and there are rarely more than P.
+  const int lp = nseg_row <= 64 ? 6 : (nseg_row <= 128 ? 5 : 4);
+  const bool pre_ok = nseg_row <= kFCap / 16;
+  const uint32_t nslot = pre_ok ? (uint32_t)nseg_row << lp : 0u;
+  const uint32_t S_t = coherent_load(&racc[tid]);  // thread t: bin t
+  unsigned long long pv[kGatherPT];
+#pragma unroll
+  for (int u = 0; u < kGatherPT; ++u) {  // unconditional: past the slots, slot 0 again
+    const uint32_t i = (uint32_t)tid + (uint32_t)kNT * u;
+    const uint32_t ic = i < nslot ? i : 0u;
+    pv[u] = coherent_load(&prow[(int64_t)(ic >> lp) * kStepSegMax + (ic & ((1u << lp) - 1u))]);
+  }
   {
-    const uint32_t S_t = coherent_load(&racc[tid]);  // thread t: bin t
     coherent_store(&racc[tid], 0u);                   // leave the row's counts zeroed
     rh[1024 + tid] = S_t;
     __syncthreads();
@@ -234,36 +247,52 @@ __device__ __forceinline__ void select_row(const StepArgs& a, int s, int64_t c, 
   const uint32_t total = scr[10];
   const uint32_t n_maybe = total - n_sure;
   const uint32_t need = (uint32_t)kB - n_sure;
-
-  // ---- 2. candidates of segment g: the first cum[g][d*] entries of its list -
-  {
-    const uint32_t* crow32 = a.cum + (int64_t)s * a.n_seg * 128;
-    for (int g = tid; g < nseg_row; g += kNT) {
-      const uint32_t w = coherent_load(&crow32[(int64_t)g * 128 + (dstar >> 1)]);
-      seglen[g] = (dstar & 1u) ? (w >> 16) : (w & 0xFFFFu);
+  // ---- 2. the candidates (bin >= d*) in LDS, slots [0, N) of ckey/cidx --
+  // fast: the loaded prefixes, when they hold all S(d*) candidates (each
+  // segment's candidates lead its prefix; the other slots hold entries below
+  // d*); else gathered: the first cum[g][d*] entries of every segment's list,
+  // packed.
+  bool fast = false, gathered = false;
+  uint32_t N = 0;
+  if (pre_ok) {
+    uint32_t ncand = 0;
+#pragma unroll
+    for (int u = 0; u < kGatherPT; ++u) {
+      const uint32_t i = (uint32_t)tid + (uint32_t)kNT * u;
+      ckey[i] = (uint32_t)pv[u];
+      cidx[i] = (uint32_t)(pv[u] >> 32);
+      ncand += (i < nslot && score_bin((uint32_t)pv[u]) >= dstar) ? 1u : 0u;
     }
+    uint32_t nloaded;
+    (void)block_excl_scan<kNT>(ncand, scr, &nloaded);
+    fast = nloaded == total;
+    N = nslot;
   }
-  __syncthreads();
-  {
-    const uint32_t v0 = 2 * tid < nseg_row ? seglen[2 * tid] : 0u;
-    const uint32_t v1 = 2 * tid + 1 < nseg_row ? seglen[2 * tid + 1] : 0u;
-    uint32_t tot;
-    const uint32_t ex = block_excl_scan<kNT>(v0 + v1, scr, &tot);
-    segoff[2 * tid] = ex;
-    segoff[2 * tid + 1] = ex + v0;
-    __syncthreads();
-  }
-
   const int nwords = (int)((c + 127) / 128) * 4;          // whole groups of 4 words
   const int wpt = (nwords + 4 * kNT - 1) / (4 * kNT) * 4;  // contiguous words per thread
-  for (int w = tid; w < nwords; w += kNT) bm[w] = 0u;
-
-  if (total <= (uint32_t)kFCap) {
-    // ---- 3. gather the candidates.  Slot i (< total <= 4096) belongs to the
-    // last segment starting at or before it: mark each non-empty segment at
-    // its first slot, take a running max over the slots (16 consecutive per
-    // thread, then across threads), then issue every slot's load at once.
+  if (!fast) {
     {
+      const uint32_t* crow32 = a.cum + (int64_t)s * a.n_seg * 128;
+      for (int g = tid; g < nseg_row; g += kNT) {
+        const uint32_t w = coherent_load(&crow32[(int64_t)g * 128 + (dstar >> 1)]);
+        seglen[g] = (dstar & 1u) ? (w >> 16) : (w & 0xFFFFu);
+      }
+    }
+    __syncthreads();
+    {
+      const uint32_t v0 = 2 * tid < nseg_row ? seglen[2 * tid] : 0u;
+      const uint32_t v1 = 2 * tid + 1 < nseg_row ? seglen[2 * tid + 1] : 0u;
+      uint32_t tot;
+      const uint32_t ex = block_excl_scan<kNT>(v0 + v1, scr, &tot);
+      segoff[2 * tid] = ex;
+      segoff[2 * tid + 1] = ex + v0;
+      __syncthreads();
+    }
+    if (total <= (uint32_t)kFCap) {
+      // Slot i (< total <= 4096) belongs to the last segment starting at or
+      // before it: mark each non-empty segment at its first slot, take a
+      // running max over the slots (16 consecutive per thread, then across
+      // threads), then issue every slot's load at once.
       uint32_t* tab = cidx;  // slot -> segment, overwritten by the ids below
       for (int i = 4 * tid; i < kFCap; i += 4 * kNT)  // every slot: segments stay in range
         *reinterpret_cast<u32x4*>(tab + i) = u32x4{0u, 0u, 0u, 0u};
@@ -317,43 +346,62 @@ __device__ __forceinline__ void select_row(const StepArgs& a, int s, int64_t c, 
           cidx[i] = (uint32_t)(v[u] >> 32);
         }
       }
+      gathered = true;
+      N = total;
     }
+  }
+
+  if (fast || gathered) {
+    for (int w = 4 * tid; w < nwords; w += 4 * kNT)  // nwords: a multiple of 4
+      *reinterpret_cast<u32x4*>(bm + w) = u32x4{0u, 0u, 0u, 0u};
     __syncthreads();
-    // ---- 4. exact choice among the bin-d* candidates -------------------------
+    // ---- 3. exact choice among the bin-d* candidates -------------------------
     // need of the n_maybe candidates in bin d* are kept: the largest scores,
     // equal scores to the lower id.  Packed as (key << 32 | ~id), that order
     // is the integer order of distinct 64-bit values.  Up to kDirect of them
     // are ranked directly (rank = number of larger packed values); larger
     // sets go through an MSB radix select, then one over the ids for ties.
+    // Slots below d* (fast path only) are never eligible.
     const bool some = need < n_maybe;  // else every bin-d* candidate is kept
     const bool direct = some && n_maybe <= (uint32_t)kDirect;
     Radix r{0u, 0u, need, need}, r2{0u, 0u, 0u, 0u};
     if (direct) {
-      unsigned long long* mk = reinterpret_cast<unsigned long long*>(rh);  // [kDirect]
-      uint32_t* mslot = rh + 2 * kDirect;                                  // [kDirect]
+      unsigned long long* mk = reinterpret_cast<unsigned long long*>(rh);  // [kDirect + 16]
+      uint32_t* mslot = rh + 2 * (kDirect + 16);                           // [kDirect]
       uint32_t cm = 0;
 #pragma unroll
       for (int u = 0; u < kGatherPT; ++u) {
         const uint32_t i = (uint32_t)tid + (uint32_t)kNT * u;
-        cm += (i < total && score_bin(ckey[i]) == dstar) ? 1u : 0u;
+        cm += (i < N && score_bin(ckey[i]) == dstar) ? 1u : 0u;
       }
       uint32_t tot;
       uint32_t pos = block_excl_scan<kNT>(cm, scr, &tot);
 #pragma unroll
       for (int u = 0; u < kGatherPT; ++u) {
         const uint32_t i = (uint32_t)tid + (uint32_t)kNT * u;
-        if (i < total && score_bin(ckey[i]) == dstar) {
+        if (i < N && score_bin(ckey[i]) == dstar) {
           mk[pos] = ((unsigned long long)ckey[i] << 32) | (0x7FFFFFFFu - cidx[i]);
           mslot[pos] = i;
           ++pos;
         }
       }
+      // pad to a multiple of 16 with values below every member
+      if (tid < 16) mk[n_maybe + tid] = 0ull;
       __syncthreads();
       if (tid < (int)n_maybe) {
         const unsigned long long me = mk[tid];
         uint32_t rank = 0;
-#pragma unroll 8
-        for (uint32_t j = 0; j < n_maybe; ++j) rank += mk[j] > me ? 1u : 0u;
+        for (uint32_t j = 0; j < n_maybe; j += 16) {  // 16 broadcast reads in flight
+          unsigned long long w[16];
+#pragma unroll
+          for (int e = 0; e < 16; e += 2) {
+            const u32x4 q = *reinterpret_cast<const u32x4*>(mk + j + e);
+            w[e] = (unsigned long long)q[0] | ((unsigned long long)q[1] << 32);
+            w[e + 1] = (unsigned long long)q[2] | ((unsigned long long)q[3] << 32);
+          }
+#pragma unroll
+          for (int e = 0; e < 16; ++e) rank += w[e] > me ? 1u : 0u;
+        }
         if (rank < need) cidx[mslot[tid]] |= 0x80000000u;  // kept
       }
       __syncthreads();
@@ -361,10 +409,10 @@ __device__ __forceinline__ void select_row(const StepArgs& a, int s, int64_t c, 
       auto key = [&](int64_t i) { return ckey[i]; };
       auto elig = [&](int64_t i) { return score_bin(ckey[i]) == dstar; };
       if (dstar > 0u && dstar < (uint32_t)kHistBins - 1u)
-        r = radix_select<kNT>(key, elig, (int64_t)total, need, rh, scr, 1, (dstar + 888u) << 20,
+        r = radix_select<kNT, true>(key, elig, (int64_t)N, need, rh, scr, 1, (dstar + 888u) << 20,
                               0x7FFu << 20);
       else
-        r = radix_select<kNT>(key, elig, (int64_t)total, need, rh, scr);
+        r = radix_select<kNT, true>(key, elig, (int64_t)N, need, rh, scr);
     }
     const bool tie = some && !direct && r.avail > r.need;
     if (tie) {  // equal scores at the threshold: the lowest ids win
@@ -372,38 +420,73 @@ __device__ __forceinline__ void select_row(const StepArgs& a, int s, int64_t c, 
       auto elig2 = [&](int64_t i) {
         return score_bin(ckey[i]) == dstar && (ckey[i] & r.mask) == r.prefix;
       };
-      r2 = radix_select<kNT>(key2, elig2, (int64_t)total, r.need, rh, scr);
+      r2 = radix_select<kNT, true>(key2, elig2, (int64_t)N, r.need, rh, scr);
     }
-    auto keep = [&](uint32_t i) {
-      const uint32_t k = ckey[i];
-      if (score_bin(k) != dstar || !some) return true;
-      if (direct) return (cidx[i] >> 31) != 0u;
-      const uint32_t m = k & r.mask;
-      if (m != r.prefix) return m > r.prefix;
-      return !tie || ((0x7FFFFFFFu - cidx[i]) & r2.mask) >= r2.prefix;
-    };
-    // ---- 5. ascending order through an id bitmap ----------------------------
     __syncthreads();
-    for (uint32_t i = tid; i < total; i += kNT)
-      if (keep(i)) {
-        const uint32_t id = cidx[i] & 0x7FFFFFFFu;
+    // ---- 4. the kept entries, packed into slots [0, k_B) (all reads first,
+    // then the branch-free choice), then in ascending order via an id bitmap
+    {
+      uint32_t kk[kGatherPT], kx[kGatherPT];
+#pragma unroll
+      for (int u = 0; u < kGatherPT; ++u) {
+        const uint32_t i = (uint32_t)tid + (uint32_t)kNT * u;
+        kk[u] = ckey[i];
+        kx[u] = cidx[i];
+      }
+      uint32_t kmask = 0, nk = 0;
+#pragma unroll
+      for (int u = 0; u < kGatherPT; ++u) {
+        const uint32_t i = (uint32_t)tid + (uint32_t)kNT * u;
+        const uint32_t b = score_bin(kk[u]);
+        const uint32_t m = kk[u] & r.mask;
+        const bool won = direct ? (kx[u] >> 31) != 0u
+                                : (m > r.prefix ||
+                                   (m == r.prefix &&
+                                    (!tie || ((0x7FFFFFFFu - kx[u]) & r2.mask) >= r2.prefix)));
+        const bool kp = i < N && (b > dstar || (b == dstar && (!some || won)));
+        kmask |= kp ? 1u << u : 0u;
+        nk += kp ? 1u : 0u;
+      }
+      uint32_t nkept;
+      uint32_t pos = block_excl_scan<kNT>(nk, scr, &nkept);  // reads above precede its barriers
+#pragma unroll
+      for (int u = 0; u < kGatherPT; ++u)
+        if ((kmask >> u) & 1u) {
+          ckey[pos] = kk[u];
+          cidx[pos] = kx[u] & 0x7FFFFFFFu;
+          ++pos;
+        }
+    }
+    __syncthreads();
+    constexpr int kPerT = 512 / kNT;  // kept entries per thread (k_B <= 512)
+#pragma unroll
+    for (int e = 0; e < kPerT; ++e) {
+      const int i = tid + kNT * e;
+      if (i < kB) {
+        const uint32_t id = cidx[i];
         atomicOr(&bm[id >> 5], 1u << (id & 31u));
       }
+    }
     __syncthreads();
     bitmap_prefix(bm, pre, scr, nwords, wpt);
-    for (uint32_t i = tid; i < total; i += kNT) {
-      if (!keep(i)) continue;
-      const uint32_t id = cidx[i] & 0x7FFFFFFFu;
-      const uint32_t rank = bitmap_rank(bm, pre, id);
-      if (rank < (uint32_t)kB) {
-        o_id[rank] = id;
-        o_key[rank] = ckey[i];
+#pragma unroll
+    for (int e = 0; e < kPerT; ++e) {
+      const int i = tid + kNT * e;
+      if (i < kB) {
+        const uint32_t id = cidx[i];
+        const uint32_t rank = bitmap_rank(bm, pre, id);
+        if (rank < (uint32_t)kB) {
+          o_id[rank] = id;
+          o_key[rank] = ckey[i];
+        }
       }
     }
   } else {
     // ---- fallback: exact selection over the whole row ---------------------
     // Entry i of the row's c entries: segment min(i / 1024, last), whose
     // list holds that segment's entries at stride kStepSegMax.
+    for (int w = 4 * tid; w < nwords; w += 4 * kNT)  // (published by the barriers below)
+      *reinterpret_cast<u32x4*>(bm + w) = u32x4{0u, 0u, 0u, 0u};
     auto at = [&](int64_t i) {
       const int64_t g = min(i / kStepSeg, (int64_t)nseg_row - 1);
       return coherent_load(&prow[g * kStepSegMax + (i - g * kStepSeg)]);
@@ -442,7 +525,7 @@ __device__ __forceinline__ void select_row(const StepArgs& a, int s, int64_t c, 
     }
   }
   __syncthreads();
-  // ---- 6. outputs and the record (coalesced) -------------------------------
+  // ---- 5. outputs and the record (coalesced) -------------------------------
   for (int i = tid; i <= kB; i += kNT) {
     if (i < kB) {
       out[i] = (int32_t)o_id[i];

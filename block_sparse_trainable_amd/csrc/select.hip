@@ -350,10 +350,10 @@ __global__ __launch_bounds__(kThreads) void filter_select_kernel(FilterArgs a) {
     auto elig = [&](int64_t i) { return score_bin(ckey[i]) == dstar; };
     if (dstar > 0u && dstar < (uint32_t)kHistBins - 1u) {
       // an unclamped bin fixes bits 30..20 of its keys: start at the second digit
-      r = radix_select<kThreads>(key, elig, (int64_t)total, need, hist, scratch, 1, (dstar + 888u) << 20,
+      r = radix_select<kThreads, true>(key, elig, (int64_t)total, need, hist, scratch, 1, (dstar + 888u) << 20,
                        0x7FFu << 20);
     } else {
-      r = radix_select<kThreads>(key, elig, (int64_t)total, need, hist, scratch);
+      r = radix_select<kThreads, true>(key, elig, (int64_t)total, need, hist, scratch);
     }
   }
   // ordered output: bin > d* always; bin == d* by (k & mask) vs prefix
@@ -695,7 +695,7 @@ __global__ __launch_bounds__(NT) void select_row_kernel(FilterArgs a) {
           // histogram, then copied back in order)
           auto pkey = [&](int64_t i) { return ckey[pslot((uint32_t)i)]; };
           auto pall = [&](int64_t) { return true; };
-          const Radix rp = radix_select<NT>(pkey, pall, (int64_t)total, (uint32_t)(kB + kPrune), hist,
+          const Radix rp = radix_select<NT, true>(pkey, pall, (int64_t)total, (uint32_t)(kB + kPrune), hist,
                                             scratch, 0, 0u, 0u, 1);
           fkey = max(fkey, rp.prefix);
           constexpr int E = kRowCap / NT;
@@ -782,7 +782,7 @@ __global__ __launch_bounds__(NT) void select_row_kernel(FilterArgs a) {
   // ---- 3. the 16-bit threshold, then exact scores for the keys equal to it
   auto key = [&](int64_t i) { return ckey[pslot((uint32_t)i)]; };
   auto all = [&](int64_t) { return true; };
-  const Radix r = radix_select<NT>(key, all, (int64_t)n_f, (uint32_t)kB, hist, scratch, 0, 0u, 0u, 1);
+  const Radix r = radix_select<NT, true>(key, all, (int64_t)n_f, (uint32_t)kB, hist, scratch, 0, 0u, 0u, 1);
   const bool band = r.need < r.avail;
   if (band) {
     // the band (keys equal to T) listed in hist: [0, nb) pool indices, then

@@ -50,8 +50,11 @@ struct Radix {
 // key(i), counting only keys with elig(i).  first_pass > 0 starts at a later
 // digit with the bits above it already fixed to prefix0/mask0; last_pass < 2
 // stops early for keys whose low bits are all zero.  hist holds kRadixBins
-// words, scratch NT/64 + 3.
-template <int NT, class KeyFn, class EligFn>
+// words, scratch NT/64 + 3.  CHEAP: key(i) and elig(i) are cheap reads of
+// any index below n (LDS): they are evaluated four elements at a time,
+// unconditionally, so their latencies overlap; otherwise key(i) is only
+// evaluated for eligible elements.
+template <int NT, bool CHEAP = false, class KeyFn, class EligFn>
 __device__ __forceinline__ Radix radix_select(KeyFn key, EligFn elig, int64_t n, uint32_t need_in,
                               uint32_t* hist, uint32_t* scratch, int first_pass = 0,
                               uint32_t prefix0 = 0u, uint32_t mask0 = 0u, int last_pass = 2) {
@@ -64,28 +67,57 @@ __device__ __forceinline__ Radix radix_select(KeyFn key, EligFn elig, int64_t n,
     const uint32_t dmask = (uint32_t)nb - 1u;
     for (int i = tid; i < nb; i += NT) hist[i] = 0;
     __syncthreads();
-    for (int64_t i = tid; i < n; i += NT) {
-      if (!elig(i)) continue;
-      const uint32_t k = key(i);
-      if ((k & r.mask) == r.prefix) atomicAdd(&hist[(k >> sh) & dmask], 1u);
+    if constexpr (CHEAP) {
+      constexpr int U = 4;
+      for (int64_t i0 = tid; i0 < n; i0 += (int64_t)U * NT) {
+        uint32_t kv[U];
+        bool ok[U];
+#pragma unroll
+        for (int e = 0; e < U; ++e) {
+          const int64_t i = i0 + (int64_t)e * NT;
+          const int64_t ic = i < n ? i : 0;
+          const bool el = elig(ic);
+          kv[e] = key(ic);
+          ok[e] = (i < n) & el;
+        }
+#pragma unroll
+        for (int e = 0; e < U; ++e)
+          if (ok[e] && (kv[e] & r.mask) == r.prefix) atomicAdd(&hist[(kv[e] >> sh) & dmask], 1u);
+      }
+    } else {
+      for (int64_t i = tid; i < n; i += NT) {
+        if (!elig(i)) continue;
+        const uint32_t k = key(i);
+        if ((k & r.mask) == r.prefix) atomicAdd(&hist[(k >> sh) & dmask], 1u);
+      }
     }
     __syncthreads();
-    const int per = nb / NT;  // thread t owns the bins just below nb - t*per
+    // thread t owns the per = nb / NT (8 or 2) bins just below nb - t*per,
+    // read at once, highest first
+    constexpr int kMaxPer = 2048 / NT;
+    const int per = nb / NT;
     const int hi = nb - tid * per;
+    uint32_t hv[kMaxPer];
     uint32_t local = 0;
-    for (int e = hi - 1; e >= hi - per; --e) local += hist[e];
+#pragma unroll
+    for (int e = 0; e < kMaxPer; ++e) {
+      hv[e] = e < per ? hist[hi - 1 - e] : 0u;
+      local += hv[e];
+    }
     uint32_t tot;
     const uint32_t above = block_excl_scan<NT>(local, scratch, &tot);
     if (above < r.need && r.need <= above + local) {
       uint32_t acc = above;
-      for (int e = hi - 1; e >= hi - per; --e) {
-        if (acc + hist[e] >= r.need) {
-          scratch[NW] = (uint32_t)e;
+      bool found = false;
+#pragma unroll
+      for (int e = 0; e < kMaxPer; ++e) {
+        if (!found && e < per && acc + hv[e] >= r.need) {
+          scratch[NW] = (uint32_t)(hi - 1 - e);
           scratch[NW + 1] = acc;
-          scratch[NW + 2] = hist[e];
-          break;
+          scratch[NW + 2] = hv[e];
+          found = true;
         }
-        acc += hist[e];
+        acc += hv[e];
       }
     }
     __syncthreads();
