@@ -5,8 +5,9 @@ The fused step must reproduce, bit for bit, the three-call decode step
 checked against the fp64 oracle; a few steps are also checked against the
 oracle directly.  Cases: multi-segment rows, rows with fewer candidates than
 k_B and rows crossing k_B, a budget small enough for a single attention
-split, the other head layouts, exact score ties at the threshold, the
-all-equal fallback, batches split over several launches, graph replay.
+split, the other head layouts, exact score ties at the threshold, many
+candidates inside one score segment, the all-equal fallback, batches split
+over several launches, graph replay.
 After every call the workspace's counters must be back at zero and its
 error word clear.
 """
@@ -151,6 +152,27 @@ def test_fused_step_exact_ties_at_threshold():
     x.q_idx[:] = synth.f32_to_bf16(qf)
     x.k_idx[:] = synth.f32_to_bf16(kf)
     _fused_vs_unfused(x, 4, check_oracle_steps=(0, 3))
+
+
+def test_fused_step_clustered_candidates():
+    say("fused step: 150 high-scoring blocks inside one of 17 score segments")
+    x = synth.decode(context=70000, batch=2, steps=3, n_needles=2)
+    kf = synth.bf16_to_f32(x.k_idx)
+    qf = synth.bf16_to_f32(x.q_idx)
+    for s in range(x.batch):
+        d = qf[s, :, :, 64:].mean(axis=(0, 1))          # the steps' shared direction
+        d = d / np.linalg.norm(d)
+        kf[s, 4 * 5200:4 * 5350, 64:] += 4.0 * d         # blocks 5200..5349, one segment
+    x.k_idx[:] = synth.f32_to_bf16(kf)
+    a, b = _fused_vs_unfused(x, 3, check_oracle_steps=(0, 2))
+    plan = b.decode_plan(3)
+    outs = b.alloc_decode_outputs()
+    b.decode_step_fused(plan, 0, outs)
+    torch.cuda.synchronize()
+    sel = outs[0][:, 0].cpu().numpy()
+    for s in range(x.batch):   # the cluster must really crowd one segment
+        assert ((sel[s] >= 5200) & (sel[s] < 5350)).sum() >= 100
+    _ctl_clear(b, plan[4])
 
 
 def test_fused_step_all_equal_scores_fallback():
