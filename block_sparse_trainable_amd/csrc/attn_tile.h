@@ -172,8 +172,7 @@ __device__ __forceinline__ void attn_mfma_tiles(
         mt = fmaxf(mt, x[st][i]);
       }
     }
-    mt = fmaxf(mt, __shfl_xor(mt, 16));
-    mt = fmaxf(mt, __shfl_xor(mt, 32));
+    mt = wave_max_xor32(wave_max_xor16(mt));
     const float m_new = fmaxf(m_run, mt);
     const bool any = m_new != -INFINITY;
     const float alpha = any ? exp2f(m_run - m_new) : 1.0f;
@@ -228,8 +227,7 @@ __device__ __forceinline__ void attn_mfma_tiles(
   // ---- merge the four waves' states: per head, M = max_w m_w,
   // f_w = 2^(m_w - M) (waves without tokens skipped), Z = sum_w f_w l_w,
   // O = sum_w f_w O_w, in wave order
-  l_run += __shfl_xor(l_run, 16);
-  l_run += __shfl_xor(l_run, 32);
+  l_run = wave_add_xor32(wave_add_xor16(l_run));
   __syncthreads();
   float* mg = reinterpret_cast<float*>(lds);
   float* my = mg + wave * MF;  // [m 16][l 16][o 16 x DP] (rows padded: no bank conflicts)

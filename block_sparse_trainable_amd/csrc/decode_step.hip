@@ -315,12 +315,7 @@ __device__ __forceinline__ void select_row(const StepArgs& a, int s, int64_t c, 
       // exclusive max over the threads before this one (segments only grow)
       {
         const int lane = tid & 63, wave = tid >> 6;
-        uint32_t incl = mx;
-#pragma unroll
-        for (int off = 1; off < 64; off <<= 1) {
-          const uint32_t t = __shfl_up(incl, off);
-          if (lane >= off) incl = max(incl, t);
-        }
+        const uint32_t incl = wave_incl_max(mx);
         if (lane == 63) scr[20 + wave] = incl;
         __syncthreads();
         uint32_t before = __shfl_up(incl, 1);

@@ -588,11 +588,17 @@ __global__ __launch_bounds__(NT) void select_row_kernel(FilterArgs a) {
         sn += 1.0f;
       }
   }
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) {
-    sm += __shfl_xor(sm, off);
-    sq += __shfl_xor(sq, off);
-    sn += __shfl_xor(sn, off);
+  {  // wave sums: per row of 16 lanes, then the four rows' last lanes
+    auto wsum = [](float v) {
+      v = row16_sum_to_last(v);
+      return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 15)) +
+             __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 31)) +
+             __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 47)) +
+             __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+    };
+    sm = wsum(sm);
+    sq = wsum(sq);
+    sn = wsum(sn);
   }
   if (lane == 0) {
     fred[wave] = sm;
@@ -662,14 +668,9 @@ __global__ __launch_bounds__(NT) void select_row_kernel(FilterArgs a) {
 #pragma unroll
           for (int q = 0; q < 3; ++q)
             if (g + q < BATCH) x |= cnt[g + q] << (10 * q);
-          uint32_t incl = x;
-#pragma unroll
-          for (int off = 1; off < 64; off <<= 1) {
-            const uint32_t t = __shfl_up(incl, off);
-            if (lane >= off) incl += t;
-          }
+          const uint32_t incl = wave_incl_add(x);
           const uint32_t ex = incl - x;
-          const uint32_t tot = __shfl(incl, 63);
+          const uint32_t tot = (uint32_t)__builtin_amdgcn_readlane((int)incl, 63);
 #pragma unroll
           for (int q = 0; q < 3; ++q)
             if (g + q < BATCH) {
@@ -805,7 +806,7 @@ __global__ __launch_bounds__(NT) void select_row_kernel(FilterArgs a) {
       return;
     }
     // exact scores, one 16-lane group per band key: lane g16 takes dims
-    // 8 g16 .. 8 g16 + 7 of the four heads; partial sums meet by shuffles
+    // 8 g16 .. 8 g16 + 7 of the four heads; partial sums meet in lane 15
     {
       const int grp = tid >> 4, g16 = tid & 15;
       constexpr int NG = NT / 16;
@@ -829,10 +830,8 @@ __global__ __launch_bounds__(NT) void select_row_kernel(FilterArgs a) {
             for (int h = 0; h < 4; ++h) acc[h] = fmaf(qs[h * 128 + 8 * g16 + e], kv, acc[h]);
           }
 #pragma unroll
-          for (int off = 8; off > 0; off >>= 1)
-#pragma unroll
-            for (int h = 0; h < 4; ++h) acc[h] += __shfl_xor(acc[h], off);
-          if (g16 == 0 && ent[q] < nb)
+          for (int h = 0; h < 4; ++h) acc[h] = row16_sum_to_last(acc[h]);  // the group's lane 15
+          if (g16 == 15 && ent[q] < nb)
             bval[ent[q]] = __float_as_uint(relu(acc[0]) + relu(acc[1]) + relu(acc[2]) + relu(acc[3]));
         }
       }
