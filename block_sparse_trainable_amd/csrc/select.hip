@@ -528,10 +528,11 @@ __device__ __forceinline__ void select_row_global16(const uint16_t* keys, int64_
 }
 
 // One workgroup of NT threads per row: sample, stream in batches of BATCH
-// 16-byte pieces (8 keys each) per thread, compacting into the LDS pool in
-// index order, then the threshold and the ordered output.  PRUNE (long rows)
-// lets the floor rise during the pass instead of streaming the row again.
-template <int NT, int BATCH, bool PRUNE>
+// 16-byte pieces (8 keys each) per thread, DEPTH batches in flight,
+// compacting into the LDS pool in index order, then the threshold and the
+// ordered output.  PRUNE (long rows) lets the floor rise during the pass
+// instead of streaming the row again.
+template <int NT, int BATCH, bool PRUNE, int DEPTH>
 __global__ __launch_bounds__(NT) void select_row_kernel(FilterArgs a) {
   constexpr int NW = NT / 64;
   constexpr int kSlots = kRowCap + kRowCap / 16 + NT;  // + one trash slot per thread
@@ -630,36 +631,51 @@ __global__ __launch_bounds__(NT) void select_row_kernel(FilterArgs a) {
     uint32_t fkey = max(__float_as_uint(f) >> 16, 1u) << 15;
     uint32_t total = 0u;   // uniform: candidates before this batch
     bool overflow = false;
-    // batches double-buffered in registers; loads are unconditional
+    // batches prefetched DEPTH deep in registers; loads are unconditional
     // (addresses clamped to the row's last piece, keys past c masked by
     // index) so the compiler waits for the current batch only
-    u32x4 nx[BATCH];
+    u32x4 nx[DEPTH][BATCH];
 #pragma unroll
-    for (int b = 0; b < BATCH; ++b)
-      nx[b] = *reinterpret_cast<const u32x4*>(keys + min(8 * (tid + NT * b), last8));
+    for (int d = 0; d < DEPTH; ++d)
+#pragma unroll
+      for (int b = 0; b < BATCH; ++b)
+        nx[d][b] = *reinterpret_cast<const u32x4*>(keys + min(d * kStep + 8 * (tid + NT * b), last8));
     for (int base = 0; base < ci; base += kStep) {
       u32x4 v[BATCH];
 #pragma unroll
-      for (int b = 0; b < BATCH; ++b) v[b] = nx[b];
+      for (int b = 0; b < BATCH; ++b) v[b] = nx[0][b];
+#pragma unroll
+      for (int d = 0; d + 1 < DEPTH; ++d)
+#pragma unroll
+        for (int b = 0; b < BATCH; ++b) nx[d][b] = nx[d + 1][b];
 #pragma unroll
       for (int b = 0; b < BATCH; ++b)
-        nx[b] = *reinterpret_cast<const u32x4*>(keys + min(base + kStep + 8 * (tid + NT * b), last8));
+        nx[DEPTH - 1][b] =
+            *reinterpret_cast<const u32x4*>(keys + min(base + DEPTH * kStep + 8 * (tid + NT * b), last8));
+      // the row's last batch: keys at or past c read as 0 (never taken)
+      if (base + kStep > ci) {
+#pragma unroll
+        for (int b = 0; b < BATCH; ++b) {
+          const int lim = min(max(ci - (base + 8 * (tid + NT * b)), 0), 8);
+#pragma unroll
+          for (int w = 0; w < 4; ++w)
+            v[b][w] &= (2 * w < lim ? 0xFFFFu : 0u) | (2 * w + 1 < lim ? 0xFFFF0000u : 0u);
+        }
+      }
       auto k16 = [&](int b, int e) {
         return ((e & 1) ? (v[b][e >> 1] >> 16) : (v[b][e >> 1] & 0xFFFFu)) << 15;
       };
       // Index order within the batch is (b, wave, lane, e).  Each lane's
       // count per piece (0..8) is scanned across the wave three pieces at a
       // time in 10-bit fields; the wave totals per piece go through LDS.
-      const bool full = base + kStep <= ci;
       uint32_t excl[BATCH];
       for (int pass = 0;; ++pass) {
         uint32_t cnt[BATCH];
 #pragma unroll
         for (int b = 0; b < BATCH; ++b) {
-          const int i0 = base + 8 * (tid + NT * b);
           uint32_t n = 0;
 #pragma unroll
-          for (int e = 0; e < 8; ++e) n += (k16(b, e) >= fkey && (full || i0 + e < ci)) ? 1u : 0u;
+          for (int e = 0; e < 8; ++e) n += k16(b, e) >= fkey ? 1u : 0u;
           cnt[b] = n;
         }
 #pragma unroll
@@ -736,7 +752,8 @@ __global__ __launch_bounds__(NT) void select_row_kernel(FilterArgs a) {
       }
       if (overflow) break;
       // wave-uniform offsets in (b, wave) order; non-candidates write to this
-      // lane's trash slot past the pool
+      // lane's trash slot past the pool (every candidate fits: total + btot
+      // <= kRowCap)
       uint32_t run = total;
       const uint32_t trash = (uint32_t)(kRowCap + kRowCap / 16) + (uint32_t)tid;
 #pragma unroll
@@ -754,8 +771,8 @@ __global__ __launch_bounds__(NT) void select_row_kernel(FilterArgs a) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const uint32_t kk = k16(b, e);
-          const bool take = kk >= fkey && (full || i0 + e < ci);
-          const uint32_t slot = take && at < (uint32_t)kRowCap ? pslot(at) : trash;
+          const bool take = kk >= fkey;
+          const uint32_t slot = take ? pslot(at) : trash;
           ckey[slot] = kk;
           cidx[slot] = (uint32_t)(i0 + e);
           at += take ? 1u : 0u;
@@ -958,9 +975,9 @@ hipError_t launch_select(const Dims& d, const SelectPlan& pl, int batch, int n_q
   if (pl.resident) {
     const dim3 g((unsigned)((int64_t)batch * n_q));
     if (pl.W <= kRowShortMax)
-      hipLaunchKernelGGL((select_row_kernel<256, 2, false>), g, dim3(256), 0, st, a);
+      hipLaunchKernelGGL((select_row_kernel<256, 2, false, 1>), g, dim3(256), 0, st, a);
     else
-      hipLaunchKernelGGL((select_row_kernel<256, 2, true>), g, dim3(256), 0, st, a);
+      hipLaunchKernelGGL((select_row_kernel<256, 2, true, 1>), g, dim3(256), 0, st, a);
   } else if (pl.n_fseg > 1 && pl.sseg <= 1024 && pl.fseg <= kWaves)
     hipLaunchKernelGGL(filter_select_kernel<true>, grid, dim3(kThreads), 0, st, a);
   else
