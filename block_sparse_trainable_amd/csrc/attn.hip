@@ -117,7 +117,15 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(
   using S = MfmaShape<HKV, D>;
   __shared__ __attribute__((aligned(16))) unsigned char lds[S::LDS_BYTES];
   __shared__ int32_t sbid[kMaxPB];
-  const int64_t item = blockIdx.x;
+  // Workgroups are handed to the 8 XCDs in turn (workgroup b to XCD b % 8):
+  // give each XCD one contiguous run of items, so that neighbouring queries,
+  // whose selections overlap, share an L2.  A bijection for any grid size.
+  int64_t item;
+  {
+    const uint32_t n = gridDim.x, b = blockIdx.x;
+    const uint32_t q = n / 8u, r = n % 8u, x = b % 8u;
+    item = (int64_t)(x * q + min(x, r) + b / 8u);
+  }
   const int64_t row = item / n_split;
   const int split = (int)(item % n_split);
   const int s = (int)(row / n_q);
