@@ -45,8 +45,8 @@ BF16_MFMA_PEAK_TFLOPS = 2500.0
 # figures belong to the attention source with this SHA-1; for any other source
 # `traffic` is reported as null until the counters are taken again.
 ATTN_COUNTERS = {
-    "source_sha1": "b2a58b960128e6f762de7312d3f76d0ac045ae7f",
-    "fetch_kib": 14926940.6, "write_kib": 66561.4,
+    "source_sha1": "8617706e1cc5be4d73e9eab0b00a2c8e4495622a",
+    "fetch_kib": 15033180.7, "write_kib": 66675.1,
     "fetch_scale": 2.0, "write_scale": 1.0,
 }
 
