@@ -259,6 +259,30 @@ def bench_decode(args, torch):
     log(f"decode graph variants (us/step): {variants}")
     best = min(variants, key=variants.get)
     graph_us = variants[best]
+    # cold: the fused graph with step t on replica t % 4 of the caches (equal
+    # values, other addresses), so the ~600 MB working set cannot stay in the
+    # 256 MB Infinity Cache; every replica holds every block the steps touch
+    reps = [dl] + [dl.replica() for _ in range(3)]
+    ws = dl.step_workspace(plan[4])
+    for r in reps:
+        for t in range(min(8, steps)):
+            r.decode_step_fused(plan, t, outs, ws)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for t in range(steps):
+            reps[t % 4].decode_step_fused(plan, t, outs, ws)
+    g.replay()
+    torch.cuda.synchronize()
+    s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s0.record()
+    for _ in range(5):
+        g.replay()
+    s1.record()
+    torch.cuda.synchronize()
+    cold_us = s0.elapsed_time(s1) * 1e3 / (5 * steps)
+    del g, reps
+    log(f"decode fused, 4 rotating cache replicas: {cold_us:.1f} us/step")
     kB = x.layout.k_blocks
     ctx = x.q_pos0.astype(np.int64)
     scan_bytes = int(sum((ctx[s] + t) // 4 for s in range(x.batch) for t in range(steps))) * 256 // steps
@@ -273,7 +297,9 @@ def bench_decode(args, torch):
            "fused_eager_p50_us": float(np.percentile(per_f, 50)),
            "fused_eager_p99_us": float(np.percentile(per_f, 99)),
            "algorithmic_bytes_per_step": scan_bytes + gather,
-           "hbm_frac": (scan_bytes + gather) / (graph_us * 1e-6) / (HBM_PEAK_GBS * 1e9)}
+           "hbm_frac": (scan_bytes + gather) / (graph_us * 1e-6) / (HBM_PEAK_GBS * 1e9),
+           "cold_4_replicas_us_per_step": cold_us,
+           "cold_hbm_frac": (scan_bytes + gather) / (cold_us * 1e-6) / (HBM_PEAK_GBS * 1e9)}
     del dl, outs
     torch.cuda.empty_cache()
     return res
@@ -438,7 +464,12 @@ def main():
                 "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": achieved / HBM_PEAK_GBS, "traffic": attn_traffic_bytes(),
                 "algorithmic_bytes_per_launch": pre["attn_bytes"],
-                "avg_launch_ms": attn_ms}
+                "avg_launch_ms": attn_ms,
+                # the gather kernel's own contraction (QK^T and PV: 8,192 flop
+                # per token visit at 16 heads x 128 dims) against the dense
+                # bf16 MFMA peak, for reference: it runs at 8 flop per byte
+                "mfma_frac": pre["token_visits"] * 4 * x.layout.q_heads * x.layout.head_dim
+                             / (attn_ms * 1e-3) / (BF16_MFMA_PEAK_TFLOPS * 1e12)}
     score_tflops = pre["score_flops"] / (pre["stages_ms"]["score_select"] * 1e-3) / 1e12
 
     cpu = None

@@ -9,6 +9,7 @@ query per sequence) -> sparse_attn_decode.
 """
 from __future__ import annotations
 
+import copy
 import numpy as np
 import torch
 
@@ -57,6 +58,16 @@ class DeviceLayer:
                                   self.layout.idx_dim), dtype=self.tdtype, device=self.device)
         self.kB = self.cfg.k_blocks
         self._ws = {}
+
+    def replica(self) -> "DeviceLayer":
+        """The same layer with its caches (raw and compressed index, K, V)
+        copied to new device memory: equal values at other addresses, for
+        runs whose working set must not stay in the on-chip caches.  Queries
+        and workspaces are shared."""
+        r = copy.copy(self)
+        r.k_idx, r.k, r.v = self.k_idx.clone(), self.k.clone(), self.v.clone()
+        r.k_cmp = self.k_cmp.clone()
+        return r
 
     # ------------------------------------------------------------ helpers --
     def i32(self, values) -> torch.Tensor:
