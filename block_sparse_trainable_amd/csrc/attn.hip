@@ -24,7 +24,7 @@
 namespace qsa {
 namespace {
 
-constexpr int kMaxTokens = 4 * 512 + 4;
+constexpr int kMaxTokens = 2048 + 128;  // r * k_B <= 2048 selected, tail <= r <= 128
 
 // ------------------------------------------------------------- generic ----
 template <bool BF16>
@@ -54,7 +54,7 @@ __global__ __launch_bounds__(256) void attn_generic_kernel(
     const void* __restrict__ q, const void* __restrict__ kc, const void* __restrict__ vc,
     int64_t cap, int n_q, const int32_t* __restrict__ q_pos0, const int32_t* __restrict__ sel,
     const int32_t* __restrict__ cnt, int kB, int Hq, int Hkv, int D, float scale,
-    void* __restrict__ out, float* __restrict__ lse) {
+    void* __restrict__ out, float* __restrict__ lse, int lr) {
   __shared__ int32_t tok[kMaxTokens];
   __shared__ float wts[kMaxTokens];
   __shared__ float red[8];
@@ -62,16 +62,17 @@ __global__ __launch_bounds__(256) void attn_generic_kernel(
   const int s = (int)(row / n_q);
   const int j = (int)(row % n_q);
   const int64_t p = min(max((int64_t)q_pos0[s] + j, (int64_t)0), cap - 1);
-  const int64_t c = p / 4;
+  const int64_t c = p >> lr;
   const int count = (int)min((int64_t)max(cnt[row], 0), min((int64_t)kB, c));
-  for (int i = threadIdx.x; i < 4 * count; i += blockDim.x) {
-    int64_t b = sel[row * kB + i / 4];
+  for (int i = threadIdx.x; i < (count << lr); i += blockDim.x) {
+    int64_t b = sel[row * kB + (i >> lr)];
     b = min(max(b, (int64_t)0), c - 1);
-    tok[i] = (int32_t)(4 * b + (i & 3));
+    tok[i] = (int32_t)((b << lr) + (i & ((1 << lr) - 1)));
   }
-  const int ntail = (int)(p - 4 * c + 1);
-  for (int i = threadIdx.x; i < ntail; i += blockDim.x) tok[4 * count + i] = (int32_t)(4 * c + i);
-  const int n = 4 * count + ntail;
+  const int ntail = (int)(p - (c << lr) + 1);
+  for (int i = threadIdx.x; i < ntail; i += blockDim.x)
+    tok[(count << lr) + i] = (int32_t)((c << lr) + i);
+  const int n = (count << lr) + ntail;
   __syncthreads();
   for (int h = 0; h < Hq; ++h) {
     const int g = (h * Hkv) / Hq;
@@ -113,7 +114,7 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(
     const uint16_t* __restrict__ vc, int64_t cap, int n_q, const int32_t* __restrict__ q_pos0,
     const int32_t* __restrict__ sel, const int32_t* __restrict__ cnt, int kB, float scale_log2,
     uint16_t* __restrict__ out, float* __restrict__ lse, float* __restrict__ part,
-    int n_split, int pb_per_split) {
+    int n_split, int pb_per_split, int lr) {
   using S = MfmaShape<HKV, D>;
   __shared__ __attribute__((aligned(16))) unsigned char lds[S::LDS_BYTES];
   __shared__ int32_t sbid[kMaxPB];
@@ -131,15 +132,21 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(
   const int s = (int)(row / n_q);
   const int j = (int)(row % n_q);
   const int64_t p = min(max((int64_t)q_pos0[s] + j, (int64_t)0), cap - 1);
-  const int64_t c = p / 4;
+  const int64_t c = p >> lr;
   const int count = (int)min((int64_t)max(cnt[row], 0), min((int64_t)kB, c));
+  // 4-token pseudo-blocks: selected block b is m = r/4 of them (b*m .. b*m+m-1),
+  // then the tail block c up to the one holding p
+  const int lm = lr - 2;
+  const int nsel = count << lm;
+  const int npb = nsel + (int)((p - (c << lr)) >> 2) + 1;
   const int pb_lo = split * pb_per_split;
-  const int pb_hi = min(pb_lo + pb_per_split, count + 1);
-  // block ids of this item's pseudo-blocks (the last one is the tail block c)
+  const int pb_hi = min(pb_lo + pb_per_split, npb);
   const int32_t* srow = sel + row * kB;
   for (int i = pb_lo + (int)threadIdx.x; i < pb_hi; i += 256)
-    sbid[i - pb_lo] = i < count ? (int32_t)min(max((int64_t)srow[i], (int64_t)0), c - 1)
-                                : (int32_t)c;
+    sbid[i - pb_lo] =
+        i < nsel ? (int32_t)((min(max((int64_t)srow[i >> lm], (int64_t)0), c - 1) << lm) +
+                             (i & ((1 << lm) - 1)))
+                 : (int32_t)((c << lm) + (i - nsel));
   u32x4 qb[S::NK];
   load_qbd<HKV, D>(q, row, qb);
   __syncthreads();
@@ -182,7 +189,12 @@ bool use_mfma(const Dims& d) {
           (d.kv_heads == 1 && d.head_dim == 128));
 }
 
-int decode_splits(const Dims& d) { return (d.kB + 1 + kDecodeSplitPB - 1) / kDecodeSplitPB; }
+// 4-token pseudo-blocks of a largest token set: k_B + 1 blocks of r / 4
+int max_pseudo_blocks(const Dims& d) { return (d.kB + 1) << (d.lr - 2); }
+
+int decode_splits(const Dims& d) {
+  return (max_pseudo_blocks(d) + kDecodeSplitPB - 1) / kDecodeSplitPB;
+}
 
 template <int HKV, int D>
 hipError_t launch_mfma(const Dims& d, int rows, int n_q, const void* q, const void* kc,
@@ -196,7 +208,7 @@ hipError_t launch_mfma(const Dims& d, int rows, int n_q, const void* q, const vo
                      static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(kc),
                      static_cast<const uint16_t*>(vc), cap, n_q, q_pos0, sel, cnt, d.kB, sl2,
                      static_cast<uint16_t*>(out), lse, part, ns,
-                     decode ? kDecodeSplitPB : d.kB + 1);
+                     decode ? kDecodeSplitPB : max_pseudo_blocks(d), d.lr);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || !decode || ns == 1) return e;  // one split wrote the output itself
   hipLaunchKernelGGL((attn_merge_kernel<D>), dim3((unsigned)(rows * 16)), dim3(D), 0, st, part,
@@ -229,11 +241,11 @@ hipError_t launch_attn(const Dims& d, int batch, int n_q, const void* q, const v
   if (d.bf16)
     hipLaunchKernelGGL(attn_generic_kernel<true>, dim3(rows), dim3(256), 0, st, q, k_cache,
                        v_cache, cap, n_q, q_pos0, sel, cnt, d.kB, d.q_heads, d.kv_heads,
-                       d.head_dim, d.scale, out, lse);
+                       d.head_dim, d.scale, out, lse, d.lr);
   else
     hipLaunchKernelGGL(attn_generic_kernel<false>, dim3(rows), dim3(256), 0, st, q, k_cache,
                        v_cache, cap, n_q, q_pos0, sel, cnt, d.kB, d.q_heads, d.kv_heads,
-                       d.head_dim, d.scale, out, lse);
+                       d.head_dim, d.scale, out, lse, d.lr);
   return hipGetLastError();
 }
 

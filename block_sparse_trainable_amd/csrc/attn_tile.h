@@ -59,8 +59,11 @@ struct MfmaShape {
   static_assert(CH == 16 || CH == 32, "the V swizzle needs 16 or 32 chunks per row");
 };
 
-constexpr int kMaxPB = 4 * 512 / 4 + 1;   // pseudo-blocks of one query (k_B + tail)
-constexpr int kMaxSplits = 17;            // decode splits: ceil((k_B + 1) / 32)
+// Pseudo-blocks are 4-token units: a block of r = 4m tokens is m of them.
+// A token set holds at most 2048 selected tokens (r * k_B <= 2048) plus a
+// tail of at most r <= 128 tokens.
+constexpr int kMaxPB = (2048 + 128) / 4;  // pseudo-blocks of one query
+constexpr int kMaxSplits = 17;            // decode splits of 32 pseudo-blocks
 constexpr int kDecodeSplitPB = 32;        // pseudo-blocks per decode split
 
 // Floats of one split's state [m 16][l 16][O 16 x D].

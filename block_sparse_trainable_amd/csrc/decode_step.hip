@@ -668,7 +668,7 @@ __device__ __forceinline__ void attend_split(const StepArgs& a, int64_t item, un
     const int64_t b_end = min(la / 4, a.cap_blocks);
     if (b_begin < b_end)
       compress_wave<true>(a.k_idx, a.cap, (int)row, b_begin, b_end, 1, a.gain, a.base, a.eps,
-                          a.rope_dims, a.k_cmp);
+                          a.rope_dims, a.k_cmp, 2);  // blocks of 4 tokens
   }
   u32x4 qb[S::NK];
   load_qbd<HKV, D>(a.q, row, qb);  // in flight while the selection is made
@@ -840,7 +840,7 @@ StepPlan step_plan(const Dims& d, int batch, int32_t max_pos_end) {
 }
 
 bool decode_step_layout_ok(const Dims& d) {
-  return d.bf16 && d.idx_heads == 4 && d.idx_dim == 128 && d.q_heads == 16 &&
+  return d.bf16 && d.r == 4 && d.idx_heads == 4 && d.idx_dim == 128 && d.q_heads == 16 &&
          ((d.kv_heads == 2 && (d.head_dim == 64 || d.head_dim == 128)) ||
           (d.kv_heads == 1 && d.head_dim == 128));
 }

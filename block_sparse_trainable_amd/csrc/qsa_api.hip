@@ -55,8 +55,9 @@ qsa_status check_config(const char* fn, const qsa_config* cfg, qsa::Dims* d) {
     return fail(QSA_ERR_INVALID_ARGUMENT, "%s: rope_base must be positive", fn);
   if (!(cfg->rms_eps >= 0.0f))
     return fail(QSA_ERR_INVALID_ARGUMENT, "%s: rms_eps must be >= 0", fn);
-  if (cfg->block_size != 4)
-    return fail(QSA_ERR_UNSUPPORTED, "%s: block_size %d (only 4 is built)", fn, cfg->block_size);
+  if (cfg->block_size < 4 || cfg->block_size > 128 || (cfg->block_size & (cfg->block_size - 1)))
+    return fail(QSA_ERR_UNSUPPORTED, "%s: block_size %d (a power of two from 4 to 128)", fn,
+                cfg->block_size);
   if (cfg->idx_dim != 128)
     return fail(QSA_ERR_UNSUPPORTED, "%s: idx_dim %d (only 128 is built)", fn, cfg->idx_dim);
   if (cfg->idx_heads > 16)
@@ -71,7 +72,11 @@ qsa_status check_config(const char* fn, const qsa_config* cfg, qsa::Dims* d) {
   const int kB = (cfg->token_budget + cfg->block_size - 1) / cfg->block_size;
   if (kB > 512)
     return fail(QSA_ERR_UNSUPPORTED, "%s: k_B = ceil(K/r) = %d (at most 512)", fn, kB);
+  if ((int64_t)kB * cfg->block_size > 2048)
+    return fail(QSA_ERR_UNSUPPORTED, "%s: k_B * r = %lld selected tokens (at most 2048)", fn,
+                (long long)kB * cfg->block_size);
   d->r = cfg->block_size;
+  d->lr = __builtin_ctz((unsigned)cfg->block_size);
   d->kB = kB;
   d->idx_heads = cfg->idx_heads;
   d->idx_dim = cfg->idx_dim;
@@ -280,8 +285,8 @@ qsa_status qsa_decode_step(const qsa_config* cfg, int32_t batch, const void* q_i
   if (st != QSA_OK) return st;
   if (!qsa::decode_step_layout_ok(d))
     return fail(QSA_ERR_UNSUPPORTED,
-                "%s: needs bf16, idx_heads 4 and 16 query heads with (kv_heads, head_dim) in "
-                "{(2,128), (2,64), (1,128)}",
+                "%s: needs bf16, block_size 4, idx_heads 4 and 16 query heads with (kv_heads, "
+                "head_dim) in {(2,128), (2,64), (1,128)}",
                 fn);
   if (batch > qsa::kStepMaxBatch)
     return fail(QSA_ERR_UNSUPPORTED, "%s: batch %d (at most %d)", fn, batch, qsa::kStepMaxBatch);

@@ -152,7 +152,7 @@ __host__ __device__ inline int64_t hist_offset(int64_t row, int64_t seg, int64_t
 
 // --------------------------------------------------------- launch params ----
 struct Dims {
-  int r, kB, idx_heads, idx_dim, rope_dims, q_heads, kv_heads, head_dim;
+  int r, lr, kB, idx_heads, idx_dim, rope_dims, q_heads, kv_heads, head_dim;  // r = 1 << lr
   bool bf16;
   float eps, scale;
   double base;

@@ -51,6 +51,7 @@ struct ScoreOut {
   uint32_t* hist;     // [rows][n_sseg][kHistWords]
   int64_t n_sseg;
   uint32_t* done;     // [rows]
+  int lr;             // log2 of the block size r
 };
 
 // ----------------------------------------------------------------- VALU ----
@@ -66,7 +67,7 @@ __global__ __launch_bounds__(256) void score_valu_kernel(
   const int s = (int)(row / n_q);
   const int j = (int)(row % n_q);
   const int64_t p = (int64_t)q_pos0[s] + j;
-  const int64_t c = min(min(p / 4, cap_blocks), o.W);
+  const int64_t c = min(min(p >> o.lr, cap_blocks), o.W);
   if (blockIdx.y == 0 && threadIdx.x == 0) coherent_store(&o.done[row], 0u);
   for (int i = threadIdx.x; i < kHistWords; i += blockDim.x) hist[i] = 0u;
   for (int i = threadIdx.x; i < H * D; i += blockDim.x) {
@@ -130,7 +131,7 @@ __global__ __launch_bounds__(256, HIST ? 2 : 3) void score_mfma_prefill_kernel(
   const int64_t pos0 = q_pos0[s];
   if (blockIdx.y == 0 && threadIdx.x < kPQ && j0 + (int)threadIdx.x < n_q)
     coherent_store(&o.done[(int64_t)s * n_q + j0 + threadIdx.x], 0u);
-  const int64_t c_tile = min(min((pos0 + j_last) / 4, cap_blocks), W);
+  const int64_t c_tile = min(min((pos0 + j_last) >> o.lr, cap_blocks), W);
   const int64_t b_lo = (int64_t)blockIdx.y * seg_blocks;
   const int64_t b_hi = min(b_lo + seg_blocks, c_tile);
   if (b_lo >= b_hi) return;  // no query of the tile reaches this segment
@@ -150,7 +151,7 @@ __global__ __launch_bounds__(256, HIST ? 2 : 3) void score_mfma_prefill_kernel(
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) qa[rt][kk] = ok ? ld16(src + 32 * kk) : u32x4{0, 0, 0, 0};
     const int jq_o = j0 + 16 * wave + 4 * rt + gq;            // query of output rows 4gq..
-    cq[rt] = jq_o < n_q ? (int)min(min((pos0 + jq_o) / 4, cap_blocks), W) : 0;
+    cq[rt] = jq_o < n_q ? (int)min(min((pos0 + jq_o) >> o.lr, cap_blocks), W) : 0;
     drow[rt] = (uint32_t)((jq_o - j0) * W + l16);
   }
   // The tile's rows (queries past n_q have padding rows of their own), so
@@ -165,7 +166,7 @@ __global__ __launch_bounds__(256, HIST ? 2 : 3) void score_mfma_prefill_kernel(
   // Smallest candidate count among the wave's 16 queries (0 if any is past
   // n_q): chunks below it need no per-score mask.
   const int jw = j0 + 16 * wave;
-  const int64_t c_wave = jw + 15 < n_q ? min(min((pos0 + jw) / 4, cap_blocks), W) : 0;
+  const int64_t c_wave = jw + 15 < n_q ? min(min((pos0 + jw) >> o.lr, cap_blocks), W) : 0;
 
   // cooperative chunk load: 1024 pieces of 16 B, four per thread
   const uint16_t* kbase = k_cmp + (int64_t)s * cap_blocks * 128;
@@ -271,7 +272,7 @@ __global__ __launch_bounds__(64 * WAVES) void score_mfma_decode_kernel(
   const int j_last = min(j0 + 4, n_q) - 1;
   if (blockIdx.x == 0 && threadIdx.x < 4 && j0 + (int)threadIdx.x < n_q)
     coherent_store(&o.done[(int64_t)s * n_q + j0 + threadIdx.x], 0u);
-  const int64_t c_tile = min(min((pos0 + j_last) / 4, cap_blocks), W);
+  const int64_t c_tile = min(min((pos0 + j_last) >> o.lr, cap_blocks), W);
   const int64_t seg_lo = (int64_t)blockIdx.x * SEG;
   const int64_t seg_hi = min(seg_lo + SEG, c_tile);
   if (seg_lo >= seg_hi) return;  // no query of the tile reaches this segment
@@ -287,7 +288,7 @@ __global__ __launch_bounds__(64 * WAVES) void score_mfma_decode_kernel(
     for (int kk = 0; kk < 4; ++kk) qa[kk] = ok ? ld16(src + 32 * kk) : u32x4{0, 0, 0, 0};
   }
   const int jq_o = j0 + gq;
-  const int64_t cq = jq_o < n_q ? min(min((pos0 + jq_o) / 4, cap_blocks), W) : 0;
+  const int64_t cq = jq_o < n_q ? min(min((pos0 + jq_o) >> o.lr, cap_blocks), W) : 0;
   float* dst = scores + ((int64_t)s * o.nq_pad + (jq_o < n_q ? jq_o : 0)) * W;
   const uint16_t* kbase = k_cmp + (int64_t)s * cap_blocks * 128 + 8 * gq;
 
@@ -346,7 +347,7 @@ hipError_t launch_score(const Dims& d, const SelectPlan& pl, int batch, int n_q,
   const int64_t cap_blocks = cap / d.r;
   char* ws = static_cast<char*>(workspace);
   ScoreOut o{reinterpret_cast<float*>(ws), pl.W, pl.nq_pad, reinterpret_cast<uint32_t*>(ws + pl.off_hist),
-             pl.n_sseg, reinterpret_cast<uint32_t*>(ws + pl.off_done)};
+             pl.n_sseg, reinterpret_cast<uint32_t*>(ws + pl.off_done), d.lr};
   const unsigned segs = (unsigned)pl.n_sseg;
   if (pl.kernel == 1) {
     dim3 grid((unsigned)((n_q + kPQ - 1) / kPQ), segs, (unsigned)batch);

@@ -105,6 +105,7 @@ struct FilterArgs {
   int64_t nq_pad;           // score rows per sequence
   const int32_t* q_pos0;
   int64_t cap_blocks;
+  int lr;             // log2 of the block size r
   int kB;
   int32_t* sel;
   int32_t* cnt;
@@ -131,7 +132,7 @@ __global__ __launch_bounds__(kThreads) void filter_select_kernel(FilterArgs a) {
   const int s = (int)(row / a.n_q);
   const int j = (int)(row % a.n_q);
   const int64_t p = max((int64_t)a.q_pos0[s] + j, (int64_t)0);
-  const int64_t c = min(p / 4, min(a.cap_blocks, a.W));
+  const int64_t c = min(p >> a.lr, min(a.cap_blocks, a.W));
   const uint32_t* bits = reinterpret_cast<const uint32_t*>(a.scores + (s * a.nq_pad + j) * a.W);
   int32_t* out = a.sel + row * a.kB;
   float* outs = a.sel_scores ? a.sel_scores + row * a.kB : nullptr;
@@ -551,7 +552,7 @@ __global__ __launch_bounds__(NT) void select_row_kernel(FilterArgs a) {
   const int s = (int)(row / a.n_q);
   const int j = (int)(row % a.n_q);
   const int64_t p = max((int64_t)a.q_pos0[s] + j, (int64_t)0);
-  const int64_t c = min(p / 4, min(a.cap_blocks, a.W));
+  const int64_t c = min(p >> a.lr, min(a.cap_blocks, a.W));
   const uint16_t* keys = reinterpret_cast<const uint16_t*>(a.scores) + (s * a.nq_pad + j) * a.W;
   int32_t* out = a.sel + row * a.kB;
   float* outs = a.sel_scores ? a.sel_scores + row * a.kB : nullptr;
@@ -967,6 +968,7 @@ hipError_t launch_select(const Dims& d, const SelectPlan& pl, int batch, int n_q
   a.nq_pad = pl.nq_pad;
   a.q_pos0 = q_pos0;
   a.cap_blocks = cap / d.r;
+  a.lr = d.lr;
   a.kB = d.kB;
   a.sel = sel;
   a.cnt = cnt;

@@ -63,11 +63,14 @@ typedef enum {
 /* Layer configuration.  Supported values are listed per field; anything
  * else returns QSA_ERR_UNSUPPORTED (or INVALID_ARGUMENT when meaningless). */
 typedef struct {
-  int32_t block_size;    /* r: tokens per micro-block.  4 ([concept] Config;
-                            [gallery] selection-unit table).                */
+  int32_t block_size;    /* r: tokens per micro-block: 4 in the pages'
+                            configuration ([concept] Config; [gallery]
+                            selection-unit table).  Supported: a power of
+                            two from 4 to 128 (qsa_decode_step: 4 only).   */
   int32_t token_budget;  /* K: selected tokens; k_B = ceil(K / r) blocks are
                             kept ([concept] (A) top-k_B; Config K = 2048).
-                            Supported: 1 <= k_B <= 512.                     */
+                            Supported: 1 <= k_B <= 512 and k_B * r <= 2048.
+                                                                            */
   int32_t idx_heads;     /* indexer query heads sharing one key head: 4
                             ([concept] (A) MQA head layout).                */
   int32_t idx_dim;       /* indexer head dim: 128 ([concept] (A)).          */
@@ -219,8 +222,9 @@ qsa_status qsa_sparse_attn_decode(const qsa_config* cfg, int32_t batch, const vo
  *              completed call leaves it zero again.  Word 2048 (byte 8192) is
  *              the error word: 1 if a wait for a selection ever gave up
  *              (never expected; the outputs of that call are then invalid).
- * Supported: dtype bf16, idx_heads 4, q_heads 16 with (kv_heads, head_dim)
- * in {(2,128), (2,64), (1,128)}, batch <= 1024 and floor((max_pos_end-1)/r)
+ * Supported: dtype bf16, block_size 4, idx_heads 4, q_heads 16 with
+ * (kv_heads, head_dim) in {(2,128), (2,64), (1,128)}, batch <= 1024 and
+ * floor((max_pos_end-1)/r)
  * <= 264192 (contexts up to 1,056,768 tokens); anything else returns
  * QSA_ERR_UNSUPPORTED and the three separate calls apply.                  */
 qsa_status qsa_decode_step(const qsa_config* cfg, int32_t batch, const void* q_idx,

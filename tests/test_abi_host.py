@@ -110,7 +110,9 @@ def test_workspace_sizes(lib):
 
 
 @pytest.mark.parametrize("field,value,status,word", [
-    ("block_size", 8, B.QSA_ERR_UNSUPPORTED, "block_size"),
+    ("block_size", 6, B.QSA_ERR_UNSUPPORTED, "block_size"),     # not a power of two
+    ("block_size", 2, B.QSA_ERR_UNSUPPORTED, "block_size"),
+    ("block_size", 256, B.QSA_ERR_UNSUPPORTED, "block_size"),
     ("block_size", 0, B.QSA_ERR_INVALID_ARGUMENT, "positive"),
     ("idx_dim", 64, B.QSA_ERR_UNSUPPORTED, "idx_dim"),
     ("rope_dims", 62, B.QSA_ERR_UNSUPPORTED, "rope_dims"),
@@ -130,6 +132,25 @@ def test_config_validation(lib, field, value, status, word):
 
 
 FAKE = 1 << 20  # a 16-byte-aligned non-null address; never dereferenced
+
+
+def test_block_sizes(lib):
+    """r a power of two from 4 to 128 with k_B * r <= 2048 selected tokens."""
+    for r in (4, 8, 16, 32, 64, 128):
+        qsa.qsa_workspace_size(cfg(block_size=r), B.QSA_OP_SELECT, 1, 16, 4096)
+    with pytest.raises(B.QsaError) as e:          # k_B = 17 blocks of 128 = 2176 tokens
+        qsa.qsa_workspace_size(cfg(block_size=128, token_budget=2049), B.QSA_OP_SELECT, 1, 1, 8)
+    assert e.value.status == B.QSA_ERR_UNSUPPORTED and "2048" in str(e.value)
+    # decode splits count 4-token pseudo-blocks: r = 16, k_B = 128 -> 129 * 4 = 516 -> 17 splits
+    assert (qsa.qsa_workspace_size(cfg(block_size=16), B.QSA_OP_DECODE, 2, 1, 300000)
+            == 4 * 2 * 17 * (16 * 128 + 32))
+    # r = 64, k_B = 32 -> 33 * 16 = 528 -> 17 splits; K = 512 -> k_B = 8 -> 9 * 16 = 144 -> 5
+    assert (qsa.qsa_workspace_size(cfg(block_size=64, token_budget=512), B.QSA_OP_DECODE, 1, 1,
+                                   300000) == 4 * 5 * (16 * 128 + 32))
+    with pytest.raises(B.QsaError) as e:          # the fused step is built for r = 4 only
+        qsa.qsa_decode_step(cfg(block_size=8), 1, FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, 4096,
+                            FAKE, 4096, FAKE, FAKE, None, FAKE, None, FAKE, 1 << 30, stream=0)
+    assert e.value.status == B.QSA_ERR_UNSUPPORTED and "block_size" in str(e.value)
 
 
 def test_null_and_alignment_rejected_before_launch(lib):
