@@ -88,6 +88,8 @@ def parse():
                     help="run only a plain 1 GiB device-to-device copy (3 times), the "
                          "known-size reference for scaling HBM byte counters")
     ap.add_argument("--decode-steps", type=int, default=64)
+    ap.add_argument("--block-size", type=int, default=4,
+                    help="r of the chunked prefill workload (4 = the pages' configuration)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=2304,
                     help="query rows in the oracle's timed sample")
@@ -95,9 +97,13 @@ def parse():
 
 
 # ------------------------------------------------------------ workloads ----
-def make_prefill_inputs(name):
+def make_prefill_inputs(name, block_size=4):
     from block_sparse_trainable_amd import synth
     if name == "chunked":
+        if block_size != 4:
+            return synth.chunked(layout=synth.Layout(block_size=block_size)), {
+                "workload": f"chunked-prefill-128k-r{block_size}", "batch": 2,
+                "cached_tokens": 131072, "chunk_tokens": 8192}
         return synth.chunked(), {"workload": "chunked-prefill-128k", "batch": 2,
                                  "cached_tokens": 131072, "chunk_tokens": 8192}
     if name == "companion":
@@ -109,22 +115,23 @@ def make_prefill_inputs(name):
 
 
 def token_visits(x) -> int:
-    """sum over queries of |S_i| = 4*min(k_B, c_i) + (p_i mod 4) + 1."""
-    kB = x.layout.k_blocks
+    """sum over queries of |S_i| = r*min(k_B, c_i) + (p_i mod r) + 1."""
+    kB, r = x.layout.k_blocks, x.layout.block_size
     tot = 0
     for s in range(x.batch):
         p = x.q_pos0[s] + np.arange(x.n_q, dtype=np.int64)
-        c = p // 4
-        tot += int((4 * np.minimum(kB, c) + (p % 4) + 1).sum())
+        c = p // r
+        tot += int((r * np.minimum(kB, c) + (p % r) + 1).sum())
     return tot
 
 
 def score_pairs(x) -> int:
     """sum over queries of c_i (visible candidate blocks)."""
+    r = x.layout.block_size
     tot = 0
     for s in range(x.batch):
         p = x.q_pos0[s] + np.arange(x.n_q, dtype=np.int64)
-        tot += int((p // 4).sum())
+        tot += int((p // r).sum())
     return tot
 
 
@@ -132,7 +139,7 @@ def score_pairs(x) -> int:
 def bench_prefill(args, torch):
     from block_sparse_trainable_amd.runtime import DeviceLayer
     t0 = time.time()
-    x, cfg = make_prefill_inputs(args.workload)
+    x, cfg = make_prefill_inputs(args.workload, args.block_size)
     log(f"generated {x.name} in {time.time() - t0:.1f}s")
     dl = DeviceLayer(x, "cuda:0")
     dl.build_prefix(x.cache_len)
@@ -392,10 +399,12 @@ def cpu_baseline(x, rows: int):
             nb_all = (int(x.q_pos0[s]) + x.n_q) // lay.block_size
             nb_old = int(x.cache_len[s]) // lay.block_size
             k_idx = f64(x.k_idx[s, :nb_all * lay.block_size])
-            kh_old = O.compress_index(k_idx[:nb_old * 4], nb_old, gain=x.gain.astype(np.float64),
+            r = lay.block_size
+            kh_old = O.compress_index(k_idx[:nb_old * r], nb_old, r=r,
+                                      gain=x.gain.astype(np.float64),
                                       eps=float(np.float32(lay.rms_eps)), storage=lay.dtype)
             t = time.perf_counter()
-            kh_all = O.compress_index(k_idx, nb_all, gain=x.gain.astype(np.float64),
+            kh_all = O.compress_index(k_idx, nb_all, r=r, gain=x.gain.astype(np.float64),
                                       eps=float(np.float32(lay.rms_eps)), storage=lay.dtype)
             t_comp += (time.perf_counter() - t) * (nb_all - nb_old) / max(nb_all, 1)
             khat.append(kh_all)
@@ -409,7 +418,7 @@ def cpu_baseline(x, rows: int):
             for j in rng.choice(x.n_q, size=min(per_seq, x.n_q), replace=False):
                 p = int(x.q_pos0[s]) + int(j)
                 t = time.perf_counter()
-                O.qsa_row(p, q_idx[j], q[j], khat[s], K, V, k_B=lay.k_blocks)
+                O.qsa_row(p, q_idx[j], q[j], khat[s], K, V, k_B=lay.k_blocks, r=lay.block_size)
                 t_rows += time.perf_counter() - t
                 n_rows += 1
     total = x.batch * x.n_q
