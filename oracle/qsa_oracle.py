@@ -1,4 +1,5 @@
-"""fp64 CPU oracle of the QSA layer forward pass.
+"""fp64 CPU oracle of the QSA layer forward pass (and of the sparse attention's
+backward, the next step the pages point to).
 
 TEST INFRASTRUCTURE.  Only the tests, the package's smoke check and the CPU
 baseline leg of the benchmark may import this module.  The product path (the
@@ -41,6 +42,9 @@ Readings where the pages are silent (each is listed in the design doc):
     floor(h * Hkv / Hq); one selection per query is shared by every main head.
   * Index rows are stored in the layer's storage dtype (bf16 or fp32),
     rounded to nearest-even, before scoring ("storage" argument).
+  * Backward (the pages give none): the exact derivative of the sparse
+    attention with each query's token set held fixed; no gradient reaches
+    the indexer through the top-k_B choice.
 """
 from __future__ import annotations
 
@@ -52,7 +56,8 @@ import numpy as np
 __all__ = [
     "round_to_bf16", "round_to_f32", "avg_pool_blocks", "rms_norm", "rope_angles",
     "partial_rope", "compress_index", "block_importance", "top_k_blocks",
-    "expand_with_tail", "sparse_attention", "RowResult", "qsa_row",
+    "expand_with_tail", "sparse_attention", "sparse_attention_backward", "RowResult",
+    "qsa_row",
 ]
 
 
@@ -229,6 +234,43 @@ def sparse_attention(q_row: np.ndarray, K: np.ndarray, V: np.ndarray, S: np.ndar
         o[h] = (w @ Vs[:, g, :]) / z
         lse[h] = m + math.log(z)
     return o, lse
+
+
+def sparse_attention_backward(q_row: np.ndarray, K: np.ndarray, V: np.ndarray,
+                              S: np.ndarray, dout_row: np.ndarray, scale: float,
+                              dK: np.ndarray, dV: np.ndarray) -> np.ndarray:
+    """Gradient of sparse_attention for one query, given dL/do = dout_row.
+
+    The pages define the forward only ([concept] (B)); this is its exact
+    derivative with the token set S held fixed (the top-k_B choice is
+    piecewise constant in its inputs, so the attention loss sends no gradient
+    through it).  Per head h with KV head g:
+        P_j  = softmax_j(scale * <q_h, K_j>)          over j in S
+        dP_j = <dO_h, V_j>
+        dS_j = P_j * (dP_j - sum_k P_k dP_k)
+        dq_h = scale * sum_j dS_j K_j
+        dK_j += scale * dS_j q_h,   dV_j += P_j dO_h.
+    Returns dq [Hq, d]; adds into dK, dV [T, Hkv, d] (fp64) at the rows of S.
+    """
+    q = np.asarray(q_row, dtype=np.float64)
+    do = np.asarray(dout_row, dtype=np.float64)
+    Hq, d = q.shape
+    Hkv = K.shape[1]
+    S = np.asarray(S, dtype=np.int64)
+    Ks = np.asarray(K[S], dtype=np.float64)
+    Vs = np.asarray(V[S], dtype=np.float64)
+    dq = np.empty((Hq, d))
+    for h in range(Hq):
+        g = (h * Hkv) // Hq
+        logits = scale * (Ks[:, g, :] @ q[h])
+        w = np.exp(logits - logits.max())
+        P = w / w.sum()
+        dP = Vs[:, g, :] @ do[h]
+        dS = P * (dP - P @ dP)
+        dq[h] = scale * (dS @ Ks[:, g, :])
+        np.add.at(dK[:, g, :], S, scale * dS[:, None] * q[h][None, :])
+        np.add.at(dV[:, g, :], S, P[:, None] * do[h][None, :])
+    return dq
 
 
 # ---------------------------------------------------------------------------

@@ -370,3 +370,79 @@ def test_tiny_margins_are_mostly_clear():
         res = O.qsa_row(p, q_idx[p], q[p], kh, K, V, k_B=16, attend=False)
         ms.append(res.sel.margin)
     assert np.mean(np.array(ms) > 1e-3) > 0.8
+
+
+# ------------------------------------------------- attention backward ----
+# The pages define the forward only; the backward is its exact derivative
+# with each query's token set held fixed.  Pinned by finite differences, by
+# the reduction to autograd of dense causal attention when every block is
+# selected, and by the one-token closed form.
+def _bwd_tiny(seed=3, Hq=4, Hkv=2, d=8, T=30):
+    rng = np.random.default_rng(seed)
+    q = rng.standard_normal((Hq, d))
+    K = rng.standard_normal((T, Hkv, d))
+    V = rng.standard_normal((T, Hkv, d))
+    dO = rng.standard_normal((Hq, d))
+    S = np.array([2, 3, 7, 8, 9, 10, 11, 20, 21, 22, 23, 27], np.int64)
+    return q, K, V, dO, S
+
+
+def test_attention_backward_matches_finite_differences():
+    q, K, V, dO, S = _bwd_tiny()
+    scale = 0.37
+    loss = lambda q_, K_, V_: float((O.sparse_attention(q_, K_, V_, S, scale)[0] * dO).sum())
+    dK, dV = np.zeros_like(K), np.zeros_like(V)
+    dq = O.sparse_attention_backward(q, K, V, S, dO, scale, dK, dV)
+    eps = 1e-6
+
+    def num(arr, idx, f):
+        a, b = arr.copy(), arr.copy()
+        a[idx] += eps
+        b[idx] -= eps
+        return (f(a) - f(b)) / (2 * eps)
+
+    for idx in np.ndindex(q.shape):
+        assert abs(num(q, idx, lambda a: loss(a, K, V)) - dq[idx]) < 1e-7
+    for t in [2, 9, 23, 27, 0, 15]:            # rows in S, and rows outside it (gradient 0)
+        for g in range(2):
+            for j in range(0, 8, 3):
+                idx = (t, g, j)
+                assert abs(num(K, idx, lambda a: loss(q, a, V)) - dK[idx]) < 1e-7
+                assert abs(num(V, idx, lambda a: loss(q, K, a)) - dV[idx]) < 1e-7
+    assert not dK[[0, 15]].any() and not dV[[0, 15]].any()
+
+
+def test_attention_backward_one_token_closed_form():
+    # |S| = 1: P = 1, so dq = 0, dK = 0 and dV = sum of dO over the heads of each KV head
+    q, K, V, dO, _ = _bwd_tiny()
+    dK, dV = np.zeros_like(K), np.zeros_like(V)
+    dq = O.sparse_attention_backward(q, K, V, np.array([5]), dO, 0.5, dK, dV)
+    assert np.abs(dq).max() < 1e-15 and np.abs(dK).max() < 1e-15
+    np.testing.assert_allclose(dV[5, 0], dO[0] + dO[1], atol=1e-15)
+    np.testing.assert_allclose(dV[5, 1], dO[2] + dO[3], atol=1e-15)
+
+
+def test_full_budget_backward_equals_dense_causal_autograd():
+    # every block selected: the summed per-row backward equals autograd of
+    # dense causal attention (torch CPU fp64, GQA by repeating KV heads)
+    x, lay, k_idx, q_idx, q, K, V, kh = _tiny_full(n=96, token_budget=256)
+    n = q.shape[0]
+    rng = np.random.default_rng(11)
+    dO = rng.standard_normal(q.shape)
+    scale = 1.0 / math.sqrt(lay.head_dim)
+    dK, dV = np.zeros_like(K), np.zeros_like(V)
+    dq = np.empty_like(q)
+    for p in range(n):
+        res = O.qsa_row(p, q_idx[p], q[p], kh, K, V, k_B=lay.k_blocks, attend=False)
+        dq[p] = O.sparse_attention_backward(q[p], K, V, res.S, dO[p], scale, dK, dV)
+    rep = lay.q_heads // lay.kv_heads
+    qt = torch.tensor(q).permute(1, 0, 2).requires_grad_()            # [Hq, n, d]
+    kt = torch.tensor(K[:n]).permute(1, 0, 2).requires_grad_()        # [Hkv, n, d]
+    vt = torch.tensor(V[:n]).permute(1, 0, 2).requires_grad_()
+    o = torch.nn.functional.scaled_dot_product_attention(
+        qt, kt.repeat_interleave(rep, 0), vt.repeat_interleave(rep, 0), is_causal=True)
+    (o * torch.tensor(dO).permute(1, 0, 2)).sum().backward()
+    np.testing.assert_allclose(dq, qt.grad.permute(1, 0, 2).numpy(), atol=1e-11)
+    np.testing.assert_allclose(dK[:n], kt.grad.permute(1, 0, 2).numpy(), atol=1e-11)
+    np.testing.assert_allclose(dV[:n], vt.grad.permute(1, 0, 2).numpy(), atol=1e-11)
+    assert not dK[n:].any() and not dV[n:].any()
