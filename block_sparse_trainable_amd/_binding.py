@@ -17,11 +17,13 @@ _lib = None
 
 QSA_OK, QSA_ERR_INVALID_ARGUMENT, QSA_ERR_UNSUPPORTED, QSA_ERR_WORKSPACE, QSA_ERR_DEVICE = range(5)
 QSA_F32, QSA_BF16 = 0, 1
-QSA_OP_INDEX_BUILD, QSA_OP_SELECT, QSA_OP_PREFILL, QSA_OP_DECODE, QSA_OP_DECODE_STEP = range(5)
+(QSA_OP_INDEX_BUILD, QSA_OP_SELECT, QSA_OP_PREFILL, QSA_OP_DECODE, QSA_OP_DECODE_STEP,
+ QSA_OP_BACKWARD) = range(6)
 
 EXPORTED = (
     "qsa_index_build", "qsa_select_topk", "qsa_sparse_attn_prefill", "qsa_sparse_attn_decode",
-    "qsa_decode_step", "qsa_workspace_size", "qsa_status_string", "qsa_last_error", "qsa_abi_version",
+    "qsa_decode_step", "qsa_sparse_attn_backward", "qsa_workspace_size", "qsa_status_string",
+    "qsa_last_error", "qsa_abi_version",
 )
 
 
@@ -86,6 +88,8 @@ def load(path: str | None = None):
         "qsa_sparse_attn_prefill": [CFG, I32, I32, P, P, P, I64, P, I32, P, P, P, P, P, SZ, P],
         "qsa_sparse_attn_decode": [CFG, I32, P, P, P, I64, P, I32, P, P, P, P, P, SZ, P],
         "qsa_decode_step": [CFG, I32, P, P, P, P, P, P, P, I64, P, I32, P, P, P, P, P, P, SZ, P],
+        "qsa_sparse_attn_backward": [CFG, I32, I32, P, P, P, I64, P, I32, P, P, P, P, P, P, P,
+                                     P, P, SZ, P],
         "qsa_workspace_size": [CFG, I32, I32, I32, I32, ctypes.POINTER(SZ)],
     }
     for name, args in sig.items():
@@ -182,3 +186,15 @@ def qsa_decode_step(cfg, batch, q_idx, q, k_idx, k_cmp, rms_gain, k_cache, v_cac
                                     cap_tokens, _ptr(q_pos), max_pos_end, _ptr(sel_blocks),
                                     _ptr(sel_count), _ptr(sel_scores), _ptr(out), _ptr(lse),
                                     _ptr(workspace), workspace_bytes, _stream(stream)))
+
+
+def qsa_sparse_attn_backward(cfg, batch, n_q, q, k_cache, v_cache, cap_tokens, q_pos0,
+                             max_pos_end, sel_blocks, sel_count, out, lse, dout, dq, dk, dv,
+                             workspace, workspace_bytes, stream=None) -> None:
+    lib = load()
+    _check(lib, lib.qsa_sparse_attn_backward(ctypes.byref(cfg), batch, n_q, _ptr(q),
+                                             _ptr(k_cache), _ptr(v_cache), cap_tokens,
+                                             _ptr(q_pos0), max_pos_end, _ptr(sel_blocks),
+                                             _ptr(sel_count), _ptr(out), _ptr(lse), _ptr(dout),
+                                             _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace),
+                                             workspace_bytes, _stream(stream)))

@@ -151,6 +151,7 @@ qsa_status qsa_workspace_size(const qsa_config* cfg, int32_t op, int32_t batch, 
     case QSA_OP_PREFILL: *bytes = qsa::attn_workspace_bytes(d, batch * n_q, false); break;
     case QSA_OP_DECODE: *bytes = qsa::attn_workspace_bytes(d, batch, true); break;
     case QSA_OP_DECODE_STEP: *bytes = qsa::step_plan(d, batch, max_pos_end).bytes; break;
+    case QSA_OP_BACKWARD: *bytes = qsa::bwd_workspace_bytes(d, batch, n_q, max_pos_end); break;
     default: return fail(QSA_ERR_INVALID_ARGUMENT, "%s: unknown op %d", fn, op);
   }
   return ok();
@@ -268,6 +269,45 @@ qsa_status qsa_sparse_attn_decode(const qsa_config* cfg, int32_t batch, const vo
   return attn_common("qsa_sparse_attn_decode", cfg, batch, 1, q, k_cache, v_cache, cap_tokens,
                      q_pos, max_pos_end, sel_blocks, sel_count, out, lse, workspace,
                      workspace_bytes, true, stream);
+}
+
+qsa_status qsa_sparse_attn_backward(const qsa_config* cfg, int32_t batch, int32_t n_q,
+                                    const void* q, const void* k_cache, const void* v_cache,
+                                    int64_t cap_tokens, const int32_t* q_pos0,
+                                    int32_t max_pos_end, const int32_t* sel_blocks,
+                                    const int32_t* sel_count, const void* out, const float* lse,
+                                    const void* dout, void* dq, float* dk, float* dv,
+                                    void* workspace, size_t workspace_bytes,
+                                    hipStream_t stream) {
+  const char* fn = "qsa_sparse_attn_backward";
+  qsa::Dims d;
+  qsa_status st = check_config(fn, cfg, &d);
+  if (st != QSA_OK) return st;
+  st = check_sizes(fn, batch, n_q, cap_tokens, max_pos_end);
+  if (st != QSA_OK) return st;
+  if (d.kv_heads > 2)
+    return fail(QSA_ERR_UNSUPPORTED, "%s: kv_heads %d (at most 2)", fn, d.kv_heads);
+  QSA_REQUIRE_PTR(q, 16);
+  QSA_REQUIRE_PTR(k_cache, 16);
+  QSA_REQUIRE_PTR(v_cache, 16);
+  QSA_REQUIRE_PTR(q_pos0, 4);
+  QSA_REQUIRE_PTR(sel_blocks, 4);
+  QSA_REQUIRE_PTR(sel_count, 4);
+  QSA_REQUIRE_PTR(out, 4);
+  QSA_REQUIRE_PTR(lse, 4);
+  QSA_REQUIRE_PTR(dout, 4);
+  QSA_REQUIRE_PTR(dq, 4);
+  QSA_REQUIRE_PTR(dk, 4);
+  QSA_REQUIRE_PTR(dv, 4);
+  const size_t need = qsa::bwd_workspace_bytes(d, batch, n_q, max_pos_end);
+  if (!workspace || workspace_bytes < need)
+    return fail(QSA_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn, need,
+                workspace ? workspace_bytes : (size_t)0);
+  if (!aligned16(workspace))
+    return fail(QSA_ERR_INVALID_ARGUMENT, "%s: workspace must be 16-byte aligned", fn);
+  return launched(fn, qsa::launch_attn_backward(d, batch, n_q, q, k_cache, v_cache, cap_tokens,
+                                                q_pos0, max_pos_end, sel_blocks, sel_count, out,
+                                                lse, dout, dq, dk, dv, workspace, stream));
 }
 
 qsa_status qsa_decode_step(const qsa_config* cfg, int32_t batch, const void* q_idx,

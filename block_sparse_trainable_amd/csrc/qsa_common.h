@@ -254,6 +254,15 @@ hipError_t launch_decode_step(const Dims& d, const StepPlan& pl, int batch, cons
 // Decode attention workspace: the per-split partial states.
 size_t attn_workspace_bytes(const Dims& d, int rows, bool decode);
 
+// Attention backward: transposed index (per-block query lists) and per-head D.
+size_t bwd_workspace_bytes(const Dims& d, int batch, int n_q, int32_t max_pos_end);
+hipError_t launch_attn_backward(const Dims& d, int batch, int n_q, const void* q,
+                                const void* k_cache, const void* v_cache, int64_t cap,
+                                const int32_t* q_pos0, int32_t max_pos_end, const int32_t* sel,
+                                const int32_t* cnt, const void* out, const float* lse,
+                                const void* dout, void* dq, float* dk, float* dv,
+                                void* workspace, hipStream_t st);
+
 hipError_t launch_attn(const Dims& d, int batch, int n_q, const void* q, const void* k_cache,
                        const void* v_cache, int64_t cap, const int32_t* q_pos0,
                        const int32_t* sel, const int32_t* cnt, void* out, float* lse,

@@ -114,6 +114,15 @@ class DeviceLayer:
         B.qsa_sparse_attn_prefill(self.cfg, self.batch, n_q, q, self.k, self.v, self.cap, q_pos0,
                                   int(max_pos_end), sel, cnt, out, lse, ws, ws.numel())
 
+    def attend_backward(self, q, q_pos0, max_pos_end: int, sel, cnt, out, lse, dout, dq, dk,
+                        dv):
+        """Gradients of attend_prefill: dq written, dk/dv (fp32, [B][cap][Hkv][d]) added."""
+        n_q = q.shape[1]
+        ws = self.workspace(B.QSA_OP_BACKWARD, self.batch, n_q, max_pos_end)
+        B.qsa_sparse_attn_backward(self.cfg, self.batch, n_q, q, self.k, self.v, self.cap, q_pos0,
+                                   int(max_pos_end), sel, cnt, out, lse, dout, dq, dk, dv, ws,
+                                   ws.numel())
+
     def attend_decode(self, q, q_pos, max_pos_end: int, sel, cnt, out, lse):
         ws = self.workspace(B.QSA_OP_DECODE, self.batch, 1, max_pos_end)
         B.qsa_sparse_attn_decode(self.cfg, self.batch, q, self.k, self.v, self.cap, q_pos,

@@ -57,7 +57,8 @@ typedef enum {
   QSA_OP_SELECT = 1,
   QSA_OP_PREFILL = 2,
   QSA_OP_DECODE = 3,
-  QSA_OP_DECODE_STEP = 4
+  QSA_OP_DECODE_STEP = 4,
+  QSA_OP_BACKWARD = 5
 } qsa_op;
 
 /* Layer configuration.  Supported values are listed per field; anything
@@ -248,6 +249,39 @@ qsa_status qsa_workspace_size(const qsa_config* cfg, int32_t op, int32_t batch, 
 
 const char* qsa_status_string(qsa_status status);
 const char* qsa_last_error(void);  /* thread-local text of the last failure */
+/* qsa_sparse_attn_backward -- gradients of qsa_sparse_attn_prefill.
+ * The pages define the forward only ([concept] (B) over the token sets of
+ * (A)); this is its exact derivative with every query's token set held
+ * fixed: the selection is piecewise constant, so no gradient reaches the
+ * indexer through it.  Per query, head h (KV head g) and token j of S:
+ *   P_j = exp(scale <q_h, K_j> - lse_h),  dP_j = <dO_h, V_j>,
+ *   D_h = sum_j P_j dP_j,  dS_j = P_j (dP_j - D_h),
+ *   dq_h = scale sum_j dS_j K_j,  dK_j += scale dS_j q_h,  dV_j += P_j dO_h.
+ *
+ *   q, k_cache, v_cache, q_pos0, max_pos_end, sel_blocks, sel_count
+ *              as given to the forward call.
+ *   out        (dtype) [batch][n_q][q_heads][head_dim]: the forward output
+ *              (validated, not read: D is recomputed exactly).
+ *   lse        float [batch][n_q][q_heads]: the forward's log-sum-exp.
+ *   dout       (dtype) [batch][n_q][q_heads][head_dim]: dL/dout.
+ *   dq         (dtype) [batch][n_q][q_heads][head_dim]: written.
+ *   dk, dv     float [batch][cap_tokens][kv_heads][head_dim]: the gradients
+ *              of this call are ADDED (zero them first, or accumulate the
+ *              chunks of a sequence); rows no query attends are untouched.
+ *   workspace  >= qsa_workspace_size(QSA_OP_BACKWARD, batch, n_q,
+ *              max_pos_end): the per-block query lists and D.
+ * Supported: kv_heads <= 2 (any dtype, head_dim, block size the forward
+ * takes).  dq is deterministic; dk/dv sum each block's queries in an order
+ * that can change from run to run (the last bits can differ).             */
+qsa_status qsa_sparse_attn_backward(const qsa_config* cfg, int32_t batch, int32_t n_q,
+                                    const void* q, const void* k_cache, const void* v_cache,
+                                    int64_t cap_tokens, const int32_t* q_pos0,
+                                    int32_t max_pos_end, const int32_t* sel_blocks,
+                                    const int32_t* sel_count, const void* out, const float* lse,
+                                    const void* dout, void* dq, float* dk, float* dv,
+                                    void* workspace, size_t workspace_bytes,
+                                    hipStream_t stream);
+
 int32_t qsa_abi_version(void);     /* 1 */
 
 #ifdef __cplusplus

@@ -249,3 +249,28 @@ def test_decode_step_rejects_before_launch(lib, kw, args, status, word):
         _step(c, **size, **ptr)
     assert e.value.status == status
     assert word in str(e.value)
+
+
+def test_backward_validation_and_workspace(lib):
+    c = cfg(token_budget=256)                         # k_B = 64
+    # lists of (k_B + 1) rows per query, per-block counters, per-head D
+    nb = (1000 + 3) // 4
+    want = _al(4 * 2 * nb)
+    want = _al(want + 4 * 2 * nb)
+    want = _al(want + 4 * (2 * nb + 1))
+    want = _al(want + 4 * 2 * 500 * 65)
+    want = _al(want + 4 * 2 * 500 * 16)
+    assert qsa.qsa_workspace_size(c, B.QSA_OP_BACKWARD, 2, 500, 1000) == want
+    args = [FAKE] * 3 + [1024, FAKE, 1000, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                         FAKE, 1 << 30]
+    with pytest.raises(B.QsaError) as e:              # kv_heads > 2
+        qsa.qsa_sparse_attn_backward(cfg(kv_heads=4), 1, 16, *args, stream=0)
+    assert e.value.status == B.QSA_ERR_UNSUPPORTED and "kv_heads" in str(e.value)
+    bad = list(args)
+    bad[10] = None                                    # dout
+    with pytest.raises(B.QsaError) as e:
+        qsa.qsa_sparse_attn_backward(c, 1, 16, *bad, stream=0)
+    assert e.value.status == B.QSA_ERR_INVALID_ARGUMENT and "dout" in str(e.value)
+    with pytest.raises(B.QsaError) as e:              # workspace too small
+        qsa.qsa_sparse_attn_backward(c, 1, 16, *args[:-1], 64, stream=0)
+    assert e.value.status == B.QSA_ERR_WORKSPACE
