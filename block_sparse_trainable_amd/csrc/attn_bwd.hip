@@ -22,6 +22,7 @@
 // run to run; dq is deterministic.
 #include <math.h>
 
+#include "attn_tile.h"
 #include "qsa_common.h"
 #include "select_common.h"
 
@@ -125,6 +126,304 @@ __global__ __launch_bounds__(kNT) void bwd_query_kernel(
     }
     if (threadIdx.x == 0) dsum[row * Hq + h] = Dh;
     __syncthreads();
+  }
+}
+
+// ------------------------------------------------------ query side, MFMA --
+// bf16 layers of 16 query heads, Hkv in {1, 2}, head_dim in {64, 128} (the
+// forward's MFMA shapes).  One workgroup per query row; its 4 waves take
+// 32-token tiles in turn, as the forward does.  Per tile:
+//   * V rows go from HBM into A-operand registers: dP^T = V_tile * dObd
+//     (dO block-diagonal over the KV heads, like the forward's query operand);
+//   * K rows go from HBM into the wave's LDS tile, read twice: as the A
+//     operand of S^T = K_tile * Qbd, and transposed for the dq contraction;
+//   * P = 2^(S scale log2e - lse log2e) from the forward's log-sum-exp.
+// D_h = sum_j P_j dP_j is only known after the last tile, so the weights fed
+// to the dq MFMAs use a reference D~_h = <dO_h, O_h> from the forward's
+// (rounded) output and the kernel also sums B_h = sum_j P_j K_j:
+//     dq_h = scale (sum_j P_j (dP_j - D~_h) K_j - (D_h - D~_h) B_h),
+// which is the exact derivative for any D~; D~ only keeps the weights
+// P_j (dP_j - D~_h) close to the true dS_j (they enter as bf16 hi + lo).  With two KV heads each
+// group's dims need only its own 8 heads, so the 16 MFMA columns carry the 8
+// heads' weights and their P (no extra MFMAs for B); with one KV head B has
+// accumulators of its own.  The waves' sums meet in LDS once per row.
+
+// 16-byte chunk c of token row tk sits at slot c ^ (tk & 15) of the K tile:
+// the S operand reads (16 rows, one chunk each) and the transposed reads
+// (4 rows x 64 contiguous bytes) both fall in distinct banks.
+__device__ __forceinline__ int kswz(int tk) { return tk & 15; }
+
+// Value of lane l ^ 8 (the other half of each 16-lane row).
+__device__ __forceinline__ uint32_t swap8(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x128, 0xF, 0xF, false);  // row_ror:8
+}
+__device__ __forceinline__ float swap8f(float v) { return __uint_as_float(swap8(__float_as_uint(v))); }
+
+// (the two-KV-head, 128-dim shape needs about 300 registers: one workgroup
+// per CU, the others two)
+template <int HKV, int D>
+__global__ __launch_bounds__(256, (HKV == 2 && D == 128) ? 1 : 2) void bwd_query_mfma_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ kc,
+    const uint16_t* __restrict__ vc, int64_t cap, int n_q, const int32_t* __restrict__ q_pos0,
+    const int32_t* __restrict__ sel, const int32_t* __restrict__ cnt, int kB, float scale,
+    const uint16_t* __restrict__ out, const float* __restrict__ lse,
+    const uint16_t* __restrict__ dout, uint16_t* __restrict__ dq, float* __restrict__ dsum,
+    int lr) {
+  using S = MfmaShape<HKV, D>;
+  constexpr int KD = S::KD, NK = S::NK, ROWB = S::ROWB, CH = S::CH, RPI = S::RPI;
+  constexpr int MF = S::MERGE_FLOATS, DP = S::DP;
+  constexpr int NACC = HKV == 2 ? 1 : 2;   // accumulator sets (A and B share one with 2 KV heads)
+  static_assert(16 * DP <= MF, "a wave's dq part must fit its merge slot");
+  __shared__ __attribute__((aligned(16))) unsigned char lds[S::LDS_BYTES];
+  __shared__ int32_t sbid[kMaxPB];
+  __shared__ float dref[16], dpart[4][16];
+  __shared__ u32x4 dbs[NK * 64];   // dObd in lane order (kept out of registers)
+  int64_t row;
+  {  // contiguous runs of rows per XCD (workgroup b goes to XCD b % 8)
+    const uint32_t n = gridDim.x, b = blockIdx.x;
+    const uint32_t qn = n / 8u, rn = n % 8u, x = b % 8u;
+    row = (int64_t)(x * qn + min(x, rn) + b / 8u);
+  }
+  const int s = (int)(row / n_q);
+  const int j = (int)(row % n_q);
+  const int64_t p = min(max((int64_t)q_pos0[s] + j, (int64_t)0), cap - 1);
+  const int64_t c = p >> lr;
+  const int count = (int)min((int64_t)max(cnt[row], 0), min((int64_t)kB, c));
+  const int lm = lr - 2;
+  const int nsel = count << lm;
+  const int npb = nsel + (int)((p - (c << lr)) >> 2) + 1;
+  const int32_t* srow = sel + row * kB;
+  for (int i = (int)threadIdx.x; i < npb; i += 256)
+    sbid[i] = i < nsel ? (int32_t)((min(max((int64_t)srow[i >> lm], (int64_t)0), c - 1) << lm) +
+                                   (i & ((1 << lm) - 1)))
+                       : (int32_t)((c << lm) + (i - nsel));
+  {  // D~_h = <dO_h, O_h>: 16 threads per head, D/16 dims each
+    constexpr int E = D / 16;
+    const int h = (int)threadIdx.x >> 4;
+    const int64_t o = (row * 16 + h) * D + (threadIdx.x & 15) * E;
+    float a = 0.0f;
+#pragma unroll
+    for (int e = 0; e < E; ++e) a = fmaf(bf16_to_f32(out[o + e]), bf16_to_f32(dout[o + e]), a);
+    a = row16_sum_to_last(a);
+    if ((threadIdx.x & 15) == 15) dref[h] = a;
+  }
+  u32x4 qb[NK];
+  load_qbd<HKV, D>(q, row, qb);
+  if (threadIdx.x < 64) {
+    u32x4 db[NK];
+    load_qbd<HKV, D>(dout, row, db);
+#pragma unroll
+    for (int kk = 0; kk < NK; ++kk) dbs[kk * 64 + threadIdx.x] = db[kk];
+  }
+  __syncthreads();
+
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int l16 = lane & 15;
+  const int gq = lane >> 4;
+  const float sl2 = scale * kLog2e;
+  const float lse2 = lse[row * 16 + l16] * kLog2e;
+  const float dt = dref[l16];
+  const uint16_t* kbase = kc + (int64_t)s * cap * KD;
+  const uint16_t* vbase = vc + (int64_t)s * cap * KD;
+  auto bid = [&](int pb) -> int64_t { return (pb < npb) ? (int64_t)sbid[pb] : -1; };
+  // token tk of the tile at pb0 reads row rp (a masked token reads row p)
+  auto trow = [&](int pb0, int tk) -> int64_t {
+    const int64_t b = bid(pb0 + (tk >> 2));
+    const int64_t tp = 4 * b + (tk & 3);
+    return (b >= 0 && tp <= p) ? tp : p;
+  };
+
+  f32x4 acc[NACC][NK][2];
+#pragma unroll
+  for (int a = 0; a < NACC; ++a)
+#pragma unroll
+    for (int pp = 0; pp < NK; ++pp) acc[a][pp][0] = acc[a][pp][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float dacc = 0.0f;
+  unsigned char* kt = lds + wave * S::TILE_LDS;
+
+  for (int pb0 = 8 * wave; pb0 < npb; pb0 += 32) {
+    // ---- V rows into A-operand registers
+    u32x4 vreg[2][NK];
+#pragma unroll
+    for (int st = 0; st < 2; ++st) {
+      const uint16_t* vp = vbase + trow(pb0, 16 * st + l16) * KD + 8 * gq;
+#pragma unroll
+      for (int kk = 0; kk < NK; ++kk) vreg[st][kk] = ld16(vp + 32 * kk);
+    }
+    // ---- K rows into this wave's LDS tile (lane-ordered 1 KiB per load)
+#pragma unroll
+    for (int u = 0; u < 32 / RPI; ++u) {
+      const int tk = RPI * u + lane / CH;
+      const int chunk = (lane % CH) ^ kswz(tk);
+      __builtin_amdgcn_global_load_lds(
+          (const __attribute__((address_space(1))) void*)(kbase + trow(pb0, tk) * KD + chunk * 8),
+          (__attribute__((address_space(3))) void*)(kt + u * 1024), 16, 0, 0);
+    }
+    // ---- dP^T = V * dObd: lane holds tokens 16st + 4gq + i for head l16
+    f32x4 dpa[2];
+#pragma unroll
+    for (int st = 0; st < 2; ++st) {
+      dpa[st] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kk = 0; kk < NK; ++kk)
+        dpa[st] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+            as_bf16x8(vreg[st][kk]), as_bf16x8(dbs[kk * 64 + lane]), dpa[st], 0, 0, 0);
+    }
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's K tile has landed in LDS
+    wave_sync();
+    // ---- S^T = K * Qbd from the tile
+    f32x4 sa[2];
+#pragma unroll
+    for (int st = 0; st < 2; ++st) {
+      const int tk = 16 * st + l16;
+      sa[st] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kk = 0; kk < NK; ++kk) {
+        const u32x4 a = *reinterpret_cast<const u32x4*>(kt + tk * ROWB +
+                                                        (((4 * kk + gq) ^ kswz(tk)) * 16));
+        sa[st] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(qb[kk]),
+                                                         sa[st], 0, 0, 0);
+      }
+    }
+    // ---- P, D partial, weights P (dP - D~) and P
+    float w1[2][4], w2[2][4];
+#pragma unroll
+    for (int st = 0; st < 2; ++st) {
+      const int64_t b = bid(pb0 + 4 * st + gq);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const bool ok = b >= 0 && 4 * b + i <= p;
+        const float P = ok ? exp2f(fmaf(sa[st][i], sl2, -lse2)) : 0.0f;
+        dacc = fmaf(P, dpa[st][i], dacc);
+        w1[st][i] = P * (dpa[st][i] - dt);
+        w2[st][i] = P;
+      }
+    }
+    // B-operand layout of the forward's P^T: k-slot (gq, e) <-> token
+    // (e < 4 ? 4gq + e : 16 + 4gq + e - 4)
+    // The weights go in as bf16 hi + lo pairs (about 16 significant bits):
+    // a single bf16 rounding of P (dP - D~) costs up to 2^-9 of each term,
+    // which rows of few, sharply weighted tokens turn into percent-level
+    // errors in dq.  P (for B, scaled by the small D - D~) needs only hi.
+    u32x4 p1, p1l, p2;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int st = e >> 1, i0 = 2 * (e & 1);
+      const uint32_t h0 = f32_to_bf16(w1[st][i0]), h1 = f32_to_bf16(w1[st][i0 + 1]);
+      p1[e] = h0 | (h1 << 16);
+      p1l[e] = f32_to_bf16(w1[st][i0] - bf16_to_f32(h0)) |
+               (f32_to_bf16(w1[st][i0 + 1] - bf16_to_f32(h1)) << 16);
+      p2[e] = f32_to_bf16(w2[st][i0]) | (f32_to_bf16(w2[st][i0 + 1]) << 16);
+    }
+    u32x4 bop[2], bol[2];
+    if constexpr (HKV == 2) {
+      // group g's columns: 0..7 the weights of heads 8g .. 8g+7, 8..15 their
+      // P (the lo operand carries 0 there)
+      u32x4 x1, x1l, x2;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        x1[e] = swap8(p1[e]);
+        x1l[e] = swap8(p1l[e]);
+        x2[e] = swap8(p2[e]);
+      }
+      const u32x4 zero = {0u, 0u, 0u, 0u};
+      bop[0] = l16 < 8 ? p1 : x2;
+      bop[1] = l16 < 8 ? x1 : p2;
+      bol[0] = l16 < 8 ? p1l : zero;
+      bol[1] = l16 < 8 ? x1l : zero;
+    } else {
+      bop[0] = p1;
+      bop[1] = p2;
+      bol[0] = p1l;
+    }
+    // ---- dq^T (and B^T) += K^T * weights, K read transposed from the tile
+#pragma unroll
+    for (int pp = 0; pp < NK; ++pp) {
+      uint32_t w[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int tr = (e < 4) ? (4 * gq + e) : (16 + 4 * gq + e - 4);
+        const int chunk = (4 * pp + (l16 >> 2)) ^ kswz(tr);
+        w[e] = *reinterpret_cast<const uint32_t*>(kt + tr * ROWB + chunk * 16 + 4 * (l16 & 3));
+      }
+      u32x4 a0, a1;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        a0[e] = (w[2 * e] & 0xFFFFu) | (w[2 * e + 1] << 16);
+        a1[e] = (w[2 * e] >> 16) | (w[2 * e + 1] & 0xFFFF0000u);
+      }
+      const u32x4 bw = bop[HKV == 2 ? pp / (D / 32) : 0];
+      const u32x4 bl = bol[HKV == 2 ? pp / (D / 32) : 0];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const bf16x8 ah = as_bf16x8(h ? a1 : a0);
+        acc[0][pp][h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, as_bf16x8(bw), acc[0][pp][h],
+                                                                0, 0, 0);
+        acc[0][pp][h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, as_bf16x8(bl), acc[0][pp][h],
+                                                                0, 0, 0);
+        if constexpr (HKV == 1)
+          acc[1][pp][h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, as_bf16x8(bop[1]),
+                                                                  acc[1][pp][h], 0, 0, 0);
+      }
+    }
+    wave_sync();  // all reads of this tile issued before the next tile's loads
+  }
+
+  // ---- D_h over the four waves, then each wave's part of dq into LDS
+  const float dw = wave_add_xor32(wave_add_xor16(dacc));
+  if (gq == 0) dpart[wave][l16] = dw;
+  __syncthreads();  // also: every wave is done with its tile
+  const float dfull = dpart[0][l16] + dpart[1][l16] + dpart[2][l16] + dpart[3][l16];
+  const float delta = dfull - dt;
+  float* mg = reinterpret_cast<float*>(lds);
+  float* my = mg + wave * MF;  // [16 heads][DP]
+  if constexpr (HKV == 2) {
+    const float dx = swap8f(delta);  // delta of head l16 ^ 8
+#pragma unroll
+    for (int pp = 0; pp < NK; ++pp) {
+      const int gp = pp / (D / 32);
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float a = acc[0][pp][h][i];
+          const float bx = swap8f(a);  // column l16 + 8: P-weighted K of the same head
+          if (l16 < 8) {
+            const int head = 8 * gp + l16;
+            my[head * DP + 32 * pp + 8 * gq + 2 * i + h - gp * D] = a - (gp ? dx : delta) * bx;
+          }
+        }
+    }
+  } else {
+#pragma unroll
+    for (int pp = 0; pp < NK; ++pp)
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          my[l16 * DP + 32 * pp + 8 * gq + 2 * i + h] = acc[0][pp][h][i] - delta * acc[1][pp][h][i];
+  }
+  __syncthreads();
+  for (int q4 = threadIdx.x; q4 < 4 * D; q4 += 256) {
+    const int n = q4 / (D / 4);
+    const int dd = 4 * (q4 % (D / 4));
+    f32x4 o = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const f32x4 v = *reinterpret_cast<const f32x4*>(mg + w * MF + n * DP + dd);
+      o[0] += v[0];
+      o[1] += v[1];
+      o[2] += v[2];
+      o[3] += v[3];
+    }
+    const uint32_t lo = f32_to_bf16(o[0] * scale) | (f32_to_bf16(o[1] * scale) << 16);
+    const uint32_t hi = f32_to_bf16(o[2] * scale) | (f32_to_bf16(o[3] * scale) << 16);
+    *reinterpret_cast<uint2*>(dq + (row * 16 + n) * D + dd) = make_uint2(lo, hi);
+  }
+  if (threadIdx.x < 16) {
+    const int h = threadIdx.x;
+    dsum[row * 16 + h] = dpart[0][h] + dpart[1][h] + dpart[2][h] + dpart[3][h];
   }
 }
 
@@ -350,10 +649,24 @@ hipError_t launch_attn_backward(const Dims& d, int batch, int n_q, const void* q
   hipLaunchKernelGGL((bwd_list_kernel<true>), dim3((unsigned)rows), dim3(kNT), 0, st, ix, cap,
                      n_q, q_pos0, sel, cnt, d.kB, d.lr);
   const int64_t units = (pl.nb << d.lr) / 4;   // 4-token units of the covered blocks
+  const bool mfma = d.bf16 && d.q_heads == 16 &&
+                    ((d.kv_heads == 2 && (d.head_dim == 64 || d.head_dim == 128)) ||
+                     (d.kv_heads == 1 && d.head_dim == 128));
+#define QSA_BWD_MFMA(HKV, DD)                                                                  \
+  else if (d.kv_heads == HKV && d.head_dim == DD)                                              \
+    hipLaunchKernelGGL((bwd_query_mfma_kernel<HKV, DD>), dim3((unsigned)rows), dim3(256), 0, st, \
+                       static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k_cache), \
+                       static_cast<const uint16_t*>(v_cache), cap, n_q, q_pos0, sel, cnt, d.kB, \
+                       d.scale, static_cast<const uint16_t*>(out), lse,                       \
+                       static_cast<const uint16_t*>(dout), static_cast<uint16_t*>(dq), dsum, d.lr);
 #define QSA_BWD(BF)                                                                            \
-  hipLaunchKernelGGL((bwd_query_kernel<BF>), dim3((unsigned)rows), dim3(kNT), 0, st, q, k_cache, \
-                     v_cache, cap, n_q, q_pos0, sel, cnt, d.kB, d.q_heads, d.kv_heads,         \
-                     d.head_dim, d.scale, out, lse, dout, dq, dsum, d.lr);                     \
+  if (!mfma)                                                                                   \
+    hipLaunchKernelGGL((bwd_query_kernel<BF>), dim3((unsigned)rows), dim3(kNT), 0, st, q, k_cache, \
+                       v_cache, cap, n_q, q_pos0, sel, cnt, d.kB, d.q_heads, d.kv_heads,       \
+                       d.head_dim, d.scale, out, lse, dout, dq, dsum, d.lr);                   \
+  QSA_BWD_MFMA(2, 128)                                                                         \
+  QSA_BWD_MFMA(1, 128)                                                                         \
+  QSA_BWD_MFMA(2, 64)                                                                          \
   hipLaunchKernelGGL((bwd_key_kernel<BF>), dim3((unsigned)(batch * units)), dim3(kNT), 0, st, ix, \
                      q, k_cache, v_cache, cap, n_q, q_pos0, d.q_heads, d.kv_heads, d.head_dim, \
                      d.scale, lse, dout, dsum, dk, dv, units, d.lr);
@@ -363,6 +676,7 @@ hipError_t launch_attn_backward(const Dims& d, int batch, int n_q, const void* q
     QSA_BWD(false)
   }
 #undef QSA_BWD
+#undef QSA_BWD_MFMA
   return hipGetLastError();
 }
 

@@ -3,7 +3,8 @@ against the fp64 oracle's exact derivative, on the GPU's own selections.
 
 Tolerance (the pages fix none for a backward): every element within
 1e-2 * max(|ref|, RMS of the checked tensor) in bf16 layers (dq is rounded
-to bf16; the forward's log-sum-exp is fp32), 1e-4 in fp32 layers.  Cases: bf16 prefill (r = 4 and r = 16), a chunk over a cache
+to bf16; the forward's log-sum-exp is fp32), 1e-4 in fp32 layers.  Cases: bf16 prefill (r = 4 and r = 16; the three head shapes of the MFMA
+path), a chunk over a cache
 (gradients reach cached rows), an fp32 layer on the generic path, and the
 accumulating contract of dk/dv.
 """
@@ -111,6 +112,15 @@ def test_backward_bf16_prefill(r):
     x = synth.prefill(n=1100, layout=lay, needle_frac=0.05)
     dl, res, dO = _run(x)
     _check(x, res, dO, 1e-2, {0: set(range(0, 1100, 5)) | {1099}})
+
+
+@pytest.mark.parametrize("kv_heads,head_dim", [(1, 128), (2, 64)])
+def test_backward_bf16_head_shapes(kv_heads, head_dim):
+    say(f"backward bf16 prefill n=900, {kv_heads} KV heads, d={head_dim}")
+    lay = synth.Layout(token_budget=256, kv_heads=kv_heads, head_dim=head_dim)
+    x = synth.prefill(n=900, layout=lay, needle_frac=0.05)
+    dl, res, dO = _run(x)
+    _check(x, res, dO, 1e-2, {0: set(range(0, 900, 4)) | {899}})
 
 
 def test_backward_chunk_over_cache():
