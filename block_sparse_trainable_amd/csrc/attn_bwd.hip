@@ -167,7 +167,8 @@ __global__ __launch_bounds__(256, (HKV == 2 && D == 128) ? 1 : 2) void bwd_query
     const uint16_t* __restrict__ vc, int64_t cap, int n_q, const int32_t* __restrict__ q_pos0,
     const int32_t* __restrict__ sel, const int32_t* __restrict__ cnt, int kB, float scale,
     const uint16_t* __restrict__ out, const float* __restrict__ lse,
-    const uint16_t* __restrict__ dout, uint16_t* __restrict__ dq, float* __restrict__ dsum,
+    const uint16_t* __restrict__ dout, uint16_t* __restrict__ dq, float* __restrict__ dlt,
+    float2* __restrict__ pw, int max_pb, uint16_t* __restrict__ qt, uint16_t* __restrict__ dot,
     int lr) {
   using S = MfmaShape<HKV, D>;
   constexpr int KD = S::KD, NK = S::NK, ROWB = S::ROWB, CH = S::CH, RPI = S::RPI;
@@ -214,6 +215,22 @@ __global__ __launch_bounds__(256, (HKV == 2 && D == 128) ? 1 : 2) void bwd_query
     load_qbd<HKV, D>(dout, row, db);
 #pragma unroll
     for (int kk = 0; kk < NK; ++kk) dbs[kk * 64 + threadIdx.x] = db[kk];
+    // q and dO transposed ([row][dim][head], bf16) for the key side's
+    // contraction over heads: lane (head l, dims dim0 .. dim0 + 7)
+    const int l = threadIdx.x & 15, g4 = threadIdx.x >> 4, gn = l / S::G;
+#pragma unroll
+    for (int kk = 0; kk < NK; ++kk) {
+      const int dim0 = 32 * kk + 8 * g4;
+      const int grp = dim0 / D;
+      if (grp != gn) continue;
+      const int64_t base = (row * D + (dim0 - grp * D)) * 16 + l;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int sh = 16 * (e & 1);
+        qt[base + 16 * e] = (uint16_t)(qb[kk][e >> 1] >> sh);
+        dot[base + 16 * e] = (uint16_t)(db[kk][e >> 1] >> sh);
+      }
+    }
   }
   __syncthreads();
 
@@ -298,6 +315,16 @@ __global__ __launch_bounds__(256, (HKV == 2 && D == 128) ? 1 : 2) void bwd_query
         dacc = fmaf(P, dpa[st][i], dacc);
         w1[st][i] = P * (dpa[st][i] - dt);
         w2[st][i] = P;
+      }
+    }
+    // the key side's inputs: {P, P (dP - D~)} per token of the row's set
+    // ([row][token][head]; tokens past p hold zeros)
+#pragma unroll
+    for (int st = 0; st < 2; ++st) {
+      if (pb0 + 4 * st + gq < npb) {
+        float2* dst = pw + ((row * max_pb + pb0 + 4 * st + gq) * 4) * 16 + l16;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) dst[16 * i] = make_float2(w2[st][i], w1[st][i]);
       }
     }
     // B-operand layout of the forward's P^T: k-slot (gq, e) <-> token
@@ -421,9 +448,9 @@ __global__ __launch_bounds__(256, (HKV == 2 && D == 128) ? 1 : 2) void bwd_query
     const uint32_t hi = f32_to_bf16(o[2] * scale) | (f32_to_bf16(o[3] * scale) << 16);
     *reinterpret_cast<uint2*>(dq + (row * 16 + n) * D + dd) = make_uint2(lo, hi);
   }
-  if (threadIdx.x < 16) {
+  if (threadIdx.x < 16) {  // D_h - D~_h: the key side's dS = P (dP - D~) - (D - D~) P
     const int h = threadIdx.x;
-    dsum[row * 16 + h] = dpart[0][h] + dpart[1][h] + dpart[2][h] + dpart[3][h];
+    dlt[row * 16 + h] = dpart[0][h] + dpart[1][h] + dpart[2][h] + dpart[3][h] - dref[h];
   }
 }
 
@@ -601,22 +628,200 @@ __global__ __launch_bounds__(kNT) void bwd_key_kernel(
   }
 }
 
+// ------------------------------------------------- key side, MFMA shapes --
+// Transposed index over 16-token groups (four 4-token units): an entry
+// {row << 4 | unit mask, i0} says that row's token set holds the group's
+// units in `mask`, the first of them at position i0 of the row's unit list
+// (the units of one group are adjacent there: the list ascends).  Rows stay
+// below 2^27 (the entry points bound batch * n_q), so row << 4 fits.
+template <bool FILL>
+__global__ __launch_bounds__(kNT) void bwd_group_list_kernel(
+    BwdIndex ix, uint2* __restrict__ glist, int64_t cap, int n_q,
+    const int32_t* __restrict__ q_pos0, const int32_t* __restrict__ sel,
+    const int32_t* __restrict__ cnt, int kB, int lr) {
+  const int64_t row = blockIdx.x;
+  const int s = (int)(row / n_q);
+  const int j = (int)(row % n_q);
+  const int64_t p = min(max((int64_t)q_pos0[s] + j, (int64_t)0), cap - 1);
+  const int64_t c = p >> lr;
+  const int count = (int)min((int64_t)max(cnt[row], 0), min((int64_t)kB, c));
+  const int lm = lr - 2;
+  const int nsel = count << lm;
+  const int npb = nsel + (int)((p - (c << lr)) >> 2) + 1;
+  const int32_t* srow = sel + row * kB;
+  auto unit = [&](int i) -> int64_t {
+    return i < nsel ? (min(max((int64_t)srow[i >> lm], (int64_t)0), c - 1) << lm) +
+                          (i & ((1 << lm) - 1))
+                    : (c << lm) + (i - nsel);
+  };
+  for (int i = threadIdx.x; i < npb; i += kNT) {
+    const int64_t u = unit(i), g = u >> 2;
+    if (g >= ix.nb || (i > 0 && (unit(i - 1) >> 2) == g)) continue;  // not its group's first
+    uint32_t mask = 1u << (u & 3);
+    for (int k = 1; k < 4 && i + k < npb; ++k) {
+      const int64_t v = unit(i + k);
+      if ((v >> 2) != g) break;
+      mask |= 1u << (v & 3);
+    }
+    const int64_t e = (int64_t)s * ix.nb + g;
+    if constexpr (FILL) {
+      const uint32_t at = atomicAdd(&ix.cur[e], 1u);
+      glist[ix.off[e] + at] = make_uint2(((uint32_t)row << 4) | mask, (uint32_t)i);
+    } else {
+      atomicAdd(&ix.cnt[e], 1u);
+    }
+  }
+}
+
+typedef short bf16x4s __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ bf16x4s pack4(uint32_t a, uint32_t b) {
+  return __builtin_bit_cast(bf16x4s, make_uint2(a, b));
+}
+
+// One workgroup per (sequence, 16-token group); its waves take the group's
+// entries in turn.  Per entry, lane (token l16, heads 4gq .. 4gq+3) forms
+// dS = P (dP - D~) - (D - D~) P and P from the query side's export, as
+// bf16 hi + lo A operands; the B operands are the row's transposed q / dO
+// (a 16-dim block, 4 heads per lane, zero where the head's KV group is not
+// the block's).  16x16x16 MFMAs contract over the 16 heads:
+//     dK[token][dim] += sum_h dS[h][token] q[h][dim],
+//     dV[token][dim] += sum_h  P[h][token] dO[h][dim].
+// The waves' sums meet in LDS and are added to dK (times scale) and dV once.
+template <int HKV, int D>
+__global__ __launch_bounds__(256, 2) void bwd_key_mfma_kernel(
+    BwdIndex gx, const uint2* __restrict__ glist, const float2* __restrict__ pw, int max_pb,
+    const uint16_t* __restrict__ qt, const uint16_t* __restrict__ dot,
+    const float* __restrict__ dlt, int64_t cap, float scale, float* __restrict__ dk,
+    float* __restrict__ dv) {
+  constexpr int KD = HKV * D, NB = KD / 16, G = 16 / HKV;
+  __shared__ float sk[16 * KD], sv[16 * KD];
+  int64_t item;
+  {  // contiguous runs of groups per XCD: neighbouring groups share queries
+    const uint32_t n = gridDim.x, b = blockIdx.x;
+    const uint32_t qn = n / 8u, rn = n % 8u, x = b % 8u;
+    item = (int64_t)(x * qn + min(x, rn) + b / 8u);
+  }
+  const uint32_t nq = gx.cnt[item];
+  if (nq == 0u) return;
+  const int s = (int)(item / gx.nb);
+  const int64_t t0 = (item % gx.nb) * 16;
+  for (int i = threadIdx.x; i < 16 * KD; i += 256) sk[i] = sv[i] = 0.0f;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int l16 = lane & 15, gq = lane >> 4;
+  const int u = l16 >> 2, t = l16 & 3;
+  f32x4 ak[NB], av[NB];
+#pragma unroll
+  for (int b = 0; b < NB; ++b) ak[b] = av[b] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const uint2* lst = glist + gx.off[item];
+  for (uint32_t qi = wave; qi < nq; qi += 4) {
+    const uint2 en = lst[qi];
+    const int64_t row = en.x >> 4;
+    const uint32_t mask = en.x & 15u;
+    float4 a = {0.f, 0.f, 0.f, 0.f}, b = {0.f, 0.f, 0.f, 0.f};   // {P, weight} x 4 heads
+    if ((mask >> u) & 1u) {
+      const int idx = (int)en.y + __popc(mask & ((1u << u) - 1u));
+      const float4* src =
+          reinterpret_cast<const float4*>(pw + ((row * max_pb + idx) * 4 + t) * 16 + 4 * gq);
+      a = src[0];
+      b = src[1];
+    }
+    const float4 dl = *reinterpret_cast<const float4*>(dlt + row * 16 + 4 * gq);
+    uint32_t sh[4], sl[4], ph[4], pl[4];
+    auto split = [&](int k, float P, float w, float dlk) {
+      const float dS = fmaf(-dlk, P, w);
+      sh[k] = f32_to_bf16(dS);
+      sl[k] = f32_to_bf16(dS - bf16_to_f32(sh[k]));
+      ph[k] = f32_to_bf16(P);
+      pl[k] = f32_to_bf16(P - bf16_to_f32(ph[k]));
+    };
+    split(0, a.x, a.y, dl.x);
+    split(1, a.z, a.w, dl.y);
+    split(2, b.x, b.y, dl.z);
+    split(3, b.z, b.w, dl.w);
+    const bf16x4s aSh = pack4(sh[0] | (sh[1] << 16), sh[2] | (sh[3] << 16));
+    const bf16x4s aSl = pack4(sl[0] | (sl[1] << 16), sl[2] | (sl[3] << 16));
+    const bf16x4s aPh = pack4(ph[0] | (ph[1] << 16), ph[2] | (ph[3] << 16));
+    const bf16x4s aPl = pack4(pl[0] | (pl[1] << 16), pl[2] | (pl[3] << 16));
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      const int grp = (16 * b) / D;
+      const bool mine = (4 * gq) / G == grp;
+      // lanes whose heads are not the block's load a neighbour's address (no
+      // extra traffic) and zero the value
+      const int gqe = mine ? gq : (G / 4) * grp + (gq % (G / 4));
+      const int64_t o = (row * D + (16 * b - grp * D + l16)) * 16 + 4 * gqe;
+      const uint2 z = make_uint2(0u, 0u);
+      uint2 q4 = *reinterpret_cast<const uint2*>(qt + o);
+      uint2 d4 = *reinterpret_cast<const uint2*>(dot + o);
+      q4 = mine ? q4 : z;
+      d4 = mine ? d4 : z;
+      const bf16x4s bq = __builtin_bit_cast(bf16x4s, q4);
+      const bf16x4s bd = __builtin_bit_cast(bf16x4s, d4);
+      ak[b] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(aSh, bq, ak[b], 0, 0, 0);
+      ak[b] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(aSl, bq, ak[b], 0, 0, 0);
+      av[b] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(aPh, bd, av[b], 0, 0, 0);
+      av[b] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(aPl, bd, av[b], 0, 0, 0);
+    }
+  }
+  __syncthreads();  // LDS cleared
+  // lane (dim 16b + l16) holds tokens 4gq + i
+#pragma unroll
+  for (int b = 0; b < NB; ++b)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      atomicAdd(&sk[(4 * gq + i) * KD + 16 * b + l16], ak[b][i]);
+      atomicAdd(&sv[(4 * gq + i) * KD + 16 * b + l16], av[b][i]);
+    }
+  __syncthreads();
+  for (int i = threadIdx.x; i < 16 * KD; i += 256) {
+    const int64_t pos = t0 + i / KD;
+    if (pos >= cap) continue;
+    const int64_t o = ((int64_t)s * cap + pos) * KD + (i % KD);
+    dk[o] += scale * sk[i];
+    dv[o] += sv[i];
+  }
+}
+
+bool bwd_mfma(const Dims& d) {
+  return d.bf16 && d.q_heads == 16 &&
+         ((d.kv_heads == 2 && (d.head_dim == 64 || d.head_dim == 128)) ||
+          (d.kv_heads == 1 && d.head_dim == 128));
+}
+
+// Workspace: the transposed index, then per path
+//   generic: per-block lists (rows x (k_B + 1)), D per (row, head);
+//   MFMA:    per-group lists of uint2 (rows x max units), D - D~ per (row,
+//            head), q / dO transposed (rows x 16 x head_dim bf16 each), and
+//            {P, P (dP - D~)} per (row, token of the set, head) as fp32.
 struct BwdPlan {
-  int64_t nb;
-  size_t off_cnt, off_cur, off_off, off_list, off_dsum, bytes;
+  bool mfma;
+  int64_t nb;   // blocks (generic) or 16-token groups (MFMA) per sequence
+  int max_pb;   // 4-token units of a largest token set
+  size_t off_cnt, off_cur, off_off, off_list, off_dsum, off_qt, off_dot, off_pw, bytes;
 };
 
 BwdPlan bwd_plan(const Dims& d, int batch, int n_q, int32_t max_pos_end) {
   BwdPlan p{};
-  p.nb = ((int64_t)max_pos_end + d.r - 1) >> d.lr;
+  p.mfma = bwd_mfma(d);
+  p.max_pb = (d.kB + 1) << (d.lr - 2);
+  p.nb = p.mfma ? ((int64_t)max_pos_end + 15) >> 4 : ((int64_t)max_pos_end + d.r - 1) >> d.lr;
   auto al = [](size_t v) { return (v + 255) / 256 * 256; };
   const size_t rows = (size_t)batch * n_q;
+  const size_t hd = (size_t)d.q_heads;
   size_t o = 0;
   p.off_cnt = o;  o = al(o + 4 * (size_t)batch * p.nb);
   p.off_cur = o;  o = al(o + 4 * (size_t)batch * p.nb);
   p.off_off = o;  o = al(o + 4 * ((size_t)batch * p.nb + 1));
-  p.off_list = o; o = al(o + 4 * rows * (size_t)(d.kB + 1));
-  p.off_dsum = o; o = al(o + 4 * rows * (size_t)d.q_heads);
+  p.off_list = o;
+  o = al(o + (p.mfma ? 8 * rows * (size_t)p.max_pb : 4 * rows * (size_t)(d.kB + 1)));
+  p.off_dsum = o; o = al(o + 4 * rows * hd);
+  p.off_qt = p.off_dot = p.off_pw = o;
+  if (p.mfma) {
+    p.off_qt = o;  o = al(o + 2 * rows * hd * (size_t)d.head_dim);
+    p.off_dot = o; o = al(o + 2 * rows * hd * (size_t)d.head_dim);
+    p.off_pw = o;  o = al(o + 8 * rows * (size_t)p.max_pb * 4 * hd);
+  }
   p.bytes = o;
   return p;
 }
@@ -643,30 +848,43 @@ hipError_t launch_attn_backward(const Dims& d, int batch, int n_q, const void* q
   const int64_t nblk = (int64_t)batch * pl.nb;
   hipLaunchKernelGGL(bwd_clear_kernel, dim3((unsigned)min((nblk + kNT - 1) / kNT, (int64_t)65535)),
                      dim3(kNT), 0, st, ix, nblk);
+  if (pl.mfma) {
+    uint2* glist = reinterpret_cast<uint2*>(ws + pl.off_list);
+    uint16_t* qt = reinterpret_cast<uint16_t*>(ws + pl.off_qt);
+    uint16_t* dot = reinterpret_cast<uint16_t*>(ws + pl.off_dot);
+    float2* pw = reinterpret_cast<float2*>(ws + pl.off_pw);
+    hipLaunchKernelGGL((bwd_group_list_kernel<false>), dim3((unsigned)rows), dim3(kNT), 0, st, ix,
+                       glist, cap, n_q, q_pos0, sel, cnt, d.kB, d.lr);
+    hipLaunchKernelGGL(bwd_scan_kernel, dim3(1), dim3(kNT), 0, st, ix, nblk);
+    hipLaunchKernelGGL((bwd_group_list_kernel<true>), dim3((unsigned)rows), dim3(kNT), 0, st, ix,
+                       glist, cap, n_q, q_pos0, sel, cnt, d.kB, d.lr);
+#define QSA_BWD_MFMA(HKV, DD)                                                                  \
+  if (d.kv_heads == HKV && d.head_dim == DD) {                                                 \
+    hipLaunchKernelGGL((bwd_query_mfma_kernel<HKV, DD>), dim3((unsigned)rows), dim3(256), 0, st, \
+                       static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k_cache), \
+                       static_cast<const uint16_t*>(v_cache), cap, n_q, q_pos0, sel, cnt, d.kB, \
+                       d.scale, static_cast<const uint16_t*>(out), lse,                       \
+                       static_cast<const uint16_t*>(dout), static_cast<uint16_t*>(dq), dsum, pw, \
+                       pl.max_pb, qt, dot, d.lr);                                              \
+    hipLaunchKernelGGL((bwd_key_mfma_kernel<HKV, DD>), dim3((unsigned)nblk), dim3(256), 0, st, ix, \
+                       glist, pw, pl.max_pb, qt, dot, dsum, cap, d.scale, dk, dv);             \
+  }
+    QSA_BWD_MFMA(2, 128)
+    QSA_BWD_MFMA(1, 128)
+    QSA_BWD_MFMA(2, 64)
+#undef QSA_BWD_MFMA
+    return hipGetLastError();
+  }
   hipLaunchKernelGGL((bwd_list_kernel<false>), dim3((unsigned)rows), dim3(kNT), 0, st, ix, cap,
                      n_q, q_pos0, sel, cnt, d.kB, d.lr);
   hipLaunchKernelGGL(bwd_scan_kernel, dim3(1), dim3(kNT), 0, st, ix, nblk);
   hipLaunchKernelGGL((bwd_list_kernel<true>), dim3((unsigned)rows), dim3(kNT), 0, st, ix, cap,
                      n_q, q_pos0, sel, cnt, d.kB, d.lr);
   const int64_t units = (pl.nb << d.lr) / 4;   // 4-token units of the covered blocks
-  const bool mfma = d.bf16 && d.q_heads == 16 &&
-                    ((d.kv_heads == 2 && (d.head_dim == 64 || d.head_dim == 128)) ||
-                     (d.kv_heads == 1 && d.head_dim == 128));
-#define QSA_BWD_MFMA(HKV, DD)                                                                  \
-  else if (d.kv_heads == HKV && d.head_dim == DD)                                              \
-    hipLaunchKernelGGL((bwd_query_mfma_kernel<HKV, DD>), dim3((unsigned)rows), dim3(256), 0, st, \
-                       static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k_cache), \
-                       static_cast<const uint16_t*>(v_cache), cap, n_q, q_pos0, sel, cnt, d.kB, \
-                       d.scale, static_cast<const uint16_t*>(out), lse,                       \
-                       static_cast<const uint16_t*>(dout), static_cast<uint16_t*>(dq), dsum, d.lr);
 #define QSA_BWD(BF)                                                                            \
-  if (!mfma)                                                                                   \
-    hipLaunchKernelGGL((bwd_query_kernel<BF>), dim3((unsigned)rows), dim3(kNT), 0, st, q, k_cache, \
-                       v_cache, cap, n_q, q_pos0, sel, cnt, d.kB, d.q_heads, d.kv_heads,       \
-                       d.head_dim, d.scale, out, lse, dout, dq, dsum, d.lr);                   \
-  QSA_BWD_MFMA(2, 128)                                                                         \
-  QSA_BWD_MFMA(1, 128)                                                                         \
-  QSA_BWD_MFMA(2, 64)                                                                          \
+  hipLaunchKernelGGL((bwd_query_kernel<BF>), dim3((unsigned)rows), dim3(kNT), 0, st, q, k_cache, \
+                     v_cache, cap, n_q, q_pos0, sel, cnt, d.kB, d.q_heads, d.kv_heads,         \
+                     d.head_dim, d.scale, out, lse, dout, dq, dsum, d.lr);                     \
   hipLaunchKernelGGL((bwd_key_kernel<BF>), dim3((unsigned)(batch * units)), dim3(kNT), 0, st, ix, \
                      q, k_cache, v_cache, cap, n_q, q_pos0, d.q_heads, d.kv_heads, d.head_dim, \
                      d.scale, lse, dout, dsum, dk, dv, units, d.lr);
@@ -676,7 +894,6 @@ hipError_t launch_attn_backward(const Dims& d, int batch, int n_q, const void* q
     QSA_BWD(false)
   }
 #undef QSA_BWD
-#undef QSA_BWD_MFMA
   return hipGetLastError();
 }
 

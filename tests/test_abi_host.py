@@ -253,14 +253,28 @@ def test_decode_step_rejects_before_launch(lib, kw, args, status, word):
 
 def test_backward_validation_and_workspace(lib):
     c = cfg(token_budget=256)                         # k_B = 64
-    # lists of (k_B + 1) rows per query, per-block counters, per-head D
+    # MFMA shapes: counters per 16-token group, lists of uint2 (one per unit
+    # of a largest token set, k_B + 1 at r = 4), D - D~ per head, q and dO
+    # transposed, {P, weight} per (token of the set, head)
+    ng = (1000 + 15) // 16
+    want = _al(4 * 2 * ng)
+    want = _al(want + 4 * 2 * ng)
+    want = _al(want + 4 * (2 * ng + 1))
+    want = _al(want + 8 * 1000 * 65)
+    want = _al(want + 4 * 1000 * 16)
+    want = _al(want + 2 * 1000 * 16 * 128)
+    want = _al(want + 2 * 1000 * 16 * 128)
+    want = _al(want + 8 * 1000 * 65 * 4 * 16)
+    assert qsa.qsa_workspace_size(c, B.QSA_OP_BACKWARD, 2, 500, 1000) == want
+    # other shapes (fp32 here): per-block counters and lists, per-head D
+    c32 = cfg(token_budget=256, dtype=B.QSA_F32, q_heads=4, kv_heads=1, head_dim=64)
     nb = (1000 + 3) // 4
     want = _al(4 * 2 * nb)
     want = _al(want + 4 * 2 * nb)
     want = _al(want + 4 * (2 * nb + 1))
     want = _al(want + 4 * 2 * 500 * 65)
-    want = _al(want + 4 * 2 * 500 * 16)
-    assert qsa.qsa_workspace_size(c, B.QSA_OP_BACKWARD, 2, 500, 1000) == want
+    want = _al(want + 4 * 2 * 500 * 4)
+    assert qsa.qsa_workspace_size(c32, B.QSA_OP_BACKWARD, 2, 500, 1000) == want
     args = [FAKE] * 3 + [1024, FAKE, 1000, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
                          FAKE, 1 << 30]
     with pytest.raises(B.QsaError) as e:              # kv_heads > 2
