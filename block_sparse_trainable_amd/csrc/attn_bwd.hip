@@ -31,6 +31,7 @@ namespace {
 
 constexpr int kBwdMaxTokens = 2048 + 128;   // r * k_B <= 2048 selected, tail <= r
 constexpr int kNT = 256;
+constexpr int kKeyPF = 2;   // key side: the next entry's loads issued before this one is consumed
 
 template <bool BF16>
 __device__ __forceinline__ float ldx(const void* p, int64_t i) {
@@ -148,6 +149,19 @@ __global__ __launch_bounds__(kNT) void bwd_query_kernel(
 // heads' weights and their P (no extra MFMAs for B); with one KV head B has
 // accumulators of its own.  The waves' sums meet in LDS once per row.
 
+// Element (row, KV head grp, dim d of that head, query head hl of its group)
+// of the transposed q / dO.  Lane (l16, gq) of the key side reads 16 bytes
+// at index(row, grp, 32 bp + l16, 4 gql): heads 4 gql .. 4 gql + 3 of dims
+// 32 bp + l16 and 32 bp + 16 + l16, i.e. the B operands of two 16-dim
+// blocks; the 64 lanes of one read cover 512 (or, with 8 heads per group and
+// half the lanes repeating, 256 x 2) contiguous bytes.
+template <int HKV, int D>
+__device__ __forceinline__ int64_t qt_index(int64_t row, int grp, int d, int hl) {
+  constexpr int GQ = 16 / HKV / 4;  // 4-head lane groups per KV head
+  const int bp = d >> 5, blk = (d >> 4) & 1, l16 = d & 15, gql = hl >> 2, i = hl & 3;
+  return (((((row * HKV + grp) * (D / 32) + bp) * GQ + gql) * 16 + l16) * 2 + blk) * 4 + i;
+}
+
 // 16-byte chunk c of token row tk sits at slot c ^ (tk & 15) of the K tile:
 // the S operand reads (16 rows, one chunk each) and the transposed reads
 // (4 rows x 64 contiguous bytes) both fall in distinct banks.
@@ -215,20 +229,21 @@ __global__ __launch_bounds__(256, (HKV == 2 && D == 128) ? 1 : 2) void bwd_query
     load_qbd<HKV, D>(dout, row, db);
 #pragma unroll
     for (int kk = 0; kk < NK; ++kk) dbs[kk * 64 + threadIdx.x] = db[kk];
-    // q and dO transposed ([row][dim][head], bf16) for the key side's
-    // contraction over heads: lane (head l, dims dim0 .. dim0 + 7)
+    // q and dO transposed for the key side's contraction over heads, in the
+    // order its MFMA operands are read (see qt_index): lane (head l, dims
+    // dim0 .. dim0 + 7 of the concatenated KV row)
     const int l = threadIdx.x & 15, g4 = threadIdx.x >> 4, gn = l / S::G;
 #pragma unroll
     for (int kk = 0; kk < NK; ++kk) {
       const int dim0 = 32 * kk + 8 * g4;
       const int grp = dim0 / D;
       if (grp != gn) continue;
-      const int64_t base = (row * D + (dim0 - grp * D)) * 16 + l;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const int sh = 16 * (e & 1);
-        qt[base + 16 * e] = (uint16_t)(qb[kk][e >> 1] >> sh);
-        dot[base + 16 * e] = (uint16_t)(db[kk][e >> 1] >> sh);
+        const int64_t o = qt_index<HKV, D>(row, grp, dim0 - grp * D + e, l - grp * S::G);
+        qt[o] = (uint16_t)(qb[kk][e >> 1] >> sh);
+        dot[o] = (uint16_t)(db[kk][e >> 1] >> sh);
       }
     }
   }
@@ -688,14 +703,20 @@ __device__ __forceinline__ bf16x4s pack4(uint32_t a, uint32_t b) {
 //     dK[token][dim] += sum_h dS[h][token] q[h][dim],
 //     dV[token][dim] += sum_h  P[h][token] dO[h][dim].
 // The waves' sums meet in LDS and are added to dK (times scale) and dV once.
-template <int HKV, int D>
+template <int HKV, int D, int PF>
 __global__ __launch_bounds__(256, 2) void bwd_key_mfma_kernel(
     BwdIndex gx, const uint2* __restrict__ glist, const float2* __restrict__ pw, int max_pb,
     const uint16_t* __restrict__ qt, const uint16_t* __restrict__ dot,
     const float* __restrict__ dlt, int64_t cap, float scale, float* __restrict__ dk,
     float* __restrict__ dv) {
   constexpr int KD = HKV * D, NB = KD / 16, G = 16 / HKV;
-  __shared__ float sk[16 * KD], sv[16 * KD];
+  // the group's list is staged here during the loop; the waves' dK / dV sums
+  // meet here after it
+  __shared__ __attribute__((aligned(16))) float sbuf[2 * 16 * KD];
+  constexpr uint32_t LCAP = 16 * KD;  // list entries (uint2) per staged chunk
+  float* sk = sbuf;
+  float* sv = sbuf + 16 * KD;
+  uint2* sl = reinterpret_cast<uint2*>(sbuf);
   int64_t item;
   {  // contiguous runs of groups per XCD: neighbouring groups share queries
     const uint32_t n = gridDim.x, b = blockIdx.x;
@@ -706,7 +727,6 @@ __global__ __launch_bounds__(256, 2) void bwd_key_mfma_kernel(
   if (nq == 0u) return;
   const int s = (int)(item / gx.nb);
   const int64_t t0 = (item % gx.nb) * 16;
-  for (int i = threadIdx.x; i < 16 * KD; i += 256) sk[i] = sv[i] = 0.0f;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int l16 = lane & 15, gq = lane >> 4;
   const int u = l16 >> 2, t = l16 & 3;
@@ -714,11 +734,12 @@ __global__ __launch_bounds__(256, 2) void bwd_key_mfma_kernel(
 #pragma unroll
   for (int b = 0; b < NB; ++b) ak[b] = av[b] = f32x4{0.f, 0.f, 0.f, 0.f};
   const uint2* lst = glist + gx.off[item];
-  for (uint32_t qi = wave; qi < nq; qi += 4) {
-    const uint2 en = lst[qi];
+
+  // {P, weight} of the lane's token for heads 4gq .. 4gq+3, and D - D~
+  auto fetch_pw = [&](uint2 en, float4& a, float4& b, float4& dl) {
     const int64_t row = en.x >> 4;
     const uint32_t mask = en.x & 15u;
-    float4 a = {0.f, 0.f, 0.f, 0.f}, b = {0.f, 0.f, 0.f, 0.f};   // {P, weight} x 4 heads
+    a = b = float4{0.f, 0.f, 0.f, 0.f};
     if ((mask >> u) & 1u) {
       const int idx = (int)en.y + __popc(mask & ((1u << u) - 1u));
       const float4* src =
@@ -726,12 +747,32 @@ __global__ __launch_bounds__(256, 2) void bwd_key_mfma_kernel(
       a = src[0];
       b = src[1];
     }
-    const float4 dl = *reinterpret_cast<const float4*>(dlt + row * 16 + 4 * gq);
-    uint32_t sh[4], sl[4], ph[4], pl[4];
+    dl = *reinterpret_cast<const float4*>(dlt + row * 16 + 4 * gq);
+  };
+  // transposed q / dO of two 16-dim blocks, 4 heads per lane; lanes whose
+  // heads are not the blocks' KV head read a neighbour's address (no extra
+  // traffic) and are zeroed when consumed
+  auto fetch_q = [&](uint2 en, uint2 (&q4)[NB], uint2 (&d4)[NB]) {
+    const int64_t row = en.x >> 4;
+#pragma unroll
+    for (int b = 0; b < NB; b += 2) {
+      const int grp = (16 * b) / D;
+      const int64_t o = qt_index<HKV, D>(row, grp, 16 * b - grp * D + l16, 4 * (gq % (G / 4)));
+      const u32x4 qq = *reinterpret_cast<const u32x4*>(qt + o);
+      const u32x4 dd = *reinterpret_cast<const u32x4*>(dot + o);
+      q4[b] = make_uint2(qq[0], qq[1]);
+      q4[b + 1] = make_uint2(qq[2], qq[3]);
+      d4[b] = make_uint2(dd[0], dd[1]);
+      d4[b + 1] = make_uint2(dd[2], dd[3]);
+    }
+  };
+  auto consume = [&](const float4& a, const float4& b, const float4& dl, const uint2 (&q4)[NB],
+                     const uint2 (&d4)[NB]) {
+    uint32_t sh[4], sl2[4], ph[4], pl[4];
     auto split = [&](int k, float P, float w, float dlk) {
       const float dS = fmaf(-dlk, P, w);
       sh[k] = f32_to_bf16(dS);
-      sl[k] = f32_to_bf16(dS - bf16_to_f32(sh[k]));
+      sl2[k] = f32_to_bf16(dS - bf16_to_f32(sh[k]));
       ph[k] = f32_to_bf16(P);
       pl[k] = f32_to_bf16(P - bf16_to_f32(ph[k]));
     };
@@ -740,31 +781,64 @@ __global__ __launch_bounds__(256, 2) void bwd_key_mfma_kernel(
     split(2, b.x, b.y, dl.z);
     split(3, b.z, b.w, dl.w);
     const bf16x4s aSh = pack4(sh[0] | (sh[1] << 16), sh[2] | (sh[3] << 16));
-    const bf16x4s aSl = pack4(sl[0] | (sl[1] << 16), sl[2] | (sl[3] << 16));
+    const bf16x4s aSl = pack4(sl2[0] | (sl2[1] << 16), sl2[2] | (sl2[3] << 16));
     const bf16x4s aPh = pack4(ph[0] | (ph[1] << 16), ph[2] | (ph[3] << 16));
     const bf16x4s aPl = pack4(pl[0] | (pl[1] << 16), pl[2] | (pl[3] << 16));
 #pragma unroll
-    for (int b = 0; b < NB; ++b) {
-      const int grp = (16 * b) / D;
-      const bool mine = (4 * gq) / G == grp;
-      // lanes whose heads are not the block's load a neighbour's address (no
-      // extra traffic) and zero the value
-      const int gqe = mine ? gq : (G / 4) * grp + (gq % (G / 4));
-      const int64_t o = (row * D + (16 * b - grp * D + l16)) * 16 + 4 * gqe;
+    for (int bb = 0; bb < NB; ++bb) {
+      const bool mine = (4 * gq) / G == (16 * bb) / D;
       const uint2 z = make_uint2(0u, 0u);
-      uint2 q4 = *reinterpret_cast<const uint2*>(qt + o);
-      uint2 d4 = *reinterpret_cast<const uint2*>(dot + o);
-      q4 = mine ? q4 : z;
-      d4 = mine ? d4 : z;
-      const bf16x4s bq = __builtin_bit_cast(bf16x4s, q4);
-      const bf16x4s bd = __builtin_bit_cast(bf16x4s, d4);
-      ak[b] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(aSh, bq, ak[b], 0, 0, 0);
-      ak[b] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(aSl, bq, ak[b], 0, 0, 0);
-      av[b] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(aPh, bd, av[b], 0, 0, 0);
-      av[b] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(aPl, bd, av[b], 0, 0, 0);
+      const bf16x4s bq = __builtin_bit_cast(bf16x4s, mine ? q4[bb] : z);
+      const bf16x4s bd = __builtin_bit_cast(bf16x4s, mine ? d4[bb] : z);
+      ak[bb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(aSh, bq, ak[bb], 0, 0, 0);
+      ak[bb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(aSl, bq, ak[bb], 0, 0, 0);
+      av[bb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(aPh, bd, av[bb], 0, 0, 0);
+      av[bb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(aPl, bd, av[bb], 0, 0, 0);
+    }
+  };
+
+  for (uint32_t base = 0; base < nq; base += LCAP) {
+    const uint32_t n = min(nq - base, LCAP);
+    __syncthreads();  // the previous chunk's entries are read
+    for (uint32_t i = threadIdx.x; i < n; i += 256) sl[i] = lst[base + i];
+    __syncthreads();
+    uint32_t k = wave;
+    if (k < n) {
+      // the next entry's loads are issued before this one is consumed
+      // (PF = 1: its {P, weight} and D - D~; PF = 2: everything)
+      uint2 en = sl[k];
+      float4 a, b, dl;
+      uint2 q4[NB], d4[NB];
+      fetch_pw(en, a, b, dl);
+      if constexpr (PF == 2) fetch_q(en, q4, d4);
+      for (; k < n; k += 4) {
+        const uint2 en2 = sl[k + 4 < n ? k + 4 : k];
+        float4 a2, b2, dl2;
+        uint2 q42[NB], d42[NB];
+        if constexpr (PF >= 1) fetch_pw(en2, a2, b2, dl2);
+        if constexpr (PF == 2) fetch_q(en2, q42, d42);
+        if constexpr (PF == 0) fetch_pw(en, a, b, dl);
+        if constexpr (PF <= 1) fetch_q(en, q4, d4);
+        consume(a, b, dl, q4, d4);
+        en = en2;
+        if constexpr (PF >= 1) {
+          a = a2;
+          b = b2;
+          dl = dl2;
+        }
+        if constexpr (PF == 2) {
+#pragma unroll
+          for (int bb = 0; bb < NB; ++bb) {
+            q4[bb] = q42[bb];
+            d4[bb] = d42[bb];
+          }
+        }
+      }
     }
   }
-  __syncthreads();  // LDS cleared
+  __syncthreads();
+  for (int i = threadIdx.x; i < 2 * 16 * KD; i += 256) sbuf[i] = 0.0f;
+  __syncthreads();
   // lane (dim 16b + l16) holds tokens 4gq + i
 #pragma unroll
   for (int b = 0; b < NB; ++b)
@@ -866,7 +940,7 @@ hipError_t launch_attn_backward(const Dims& d, int batch, int n_q, const void* q
                        d.scale, static_cast<const uint16_t*>(out), lse,                       \
                        static_cast<const uint16_t*>(dout), static_cast<uint16_t*>(dq), dsum, pw, \
                        pl.max_pb, qt, dot, d.lr);                                              \
-    hipLaunchKernelGGL((bwd_key_mfma_kernel<HKV, DD>), dim3((unsigned)nblk), dim3(256), 0, st, ix, \
+    hipLaunchKernelGGL((bwd_key_mfma_kernel<HKV, DD, kKeyPF>), dim3((unsigned)nblk), dim3(256), 0, st, ix, \
                        glist, pw, pl.max_pb, qt, dot, dsum, cap, d.scale, dk, dv);             \
   }
     QSA_BWD_MFMA(2, 128)
