@@ -91,6 +91,8 @@ def parse():
     ap.add_argument("--block-size", type=int, default=4,
                     help="r of the chunked prefill workload (4 = the pages' configuration)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--backward", action=argparse.BooleanOptionalAction, default=True,
+                    help="also time the sparse attention backward on the prefill workload")
     ap.add_argument("--cpu-rows", type=int, default=2304,
                     help="query rows in the oracle's timed sample")
     return ap.parse_args()
@@ -195,12 +197,78 @@ def bench_prefill(args, torch):
         "attn_bytes": attn_bytes, "token_visits": visits, "score_pairs": pairs,
         "score_flops": pairs * 2 * x.layout.idx_heads * x.layout.idx_dim,
     }
+    if args.backward:
+        res["backward"] = bench_backward(args, torch, x, dl, outs, q_pos0, max_pos_end)
     cfg.update({"q_heads": x.layout.q_heads, "kv_heads": x.layout.kv_heads,
                 "head_dim": x.layout.head_dim, "token_budget": x.layout.token_budget,
                 "block_size": r, "idx_heads": x.layout.idx_heads, "idx_dim": x.layout.idx_dim})
     del dl, outs
     torch.cuda.empty_cache()
     return x, cfg, res
+
+
+# --------------------------------------------------------------- backward --
+def group_entries(x, sel, cnt) -> int:
+    """(query, 16-token group) pairs of the token sets: the key side's work
+    items, each reading the query's transposed q and dO once."""
+    r, kB = x.layout.block_size, x.layout.k_blocks
+    m = r // 4
+    tot = 0
+    for s in range(x.batch):
+        for j in range(x.n_q):
+            p = int(x.q_pos0[s]) + j
+            c = p // r
+            n = min(max(int(cnt[s, j]), 0), kB, c)
+            b = np.clip(sel[s, j, :n].astype(np.int64), 0, max(c - 1, 0))
+            units = np.concatenate([(b[:, None] * m + np.arange(m)).ravel(),
+                                    c * m + np.arange((p - c * r) // 4 + 1)])
+            g = units >> 2
+            tot += 1 + int((g[1:] != g[:-1]).sum())
+    return tot
+
+
+def bench_backward(args, torch, x, dl, outs, q_pos0, max_pos_end):
+    """Gradients of the chunk's sparse attention (dq, dK, dV) for a seeded
+    dL/dout, on the forward's own selections."""
+    sel, cnt, scs, out, lse = outs
+    g = torch.Generator(device="cuda:0")
+    g.manual_seed(5)
+    dout = torch.randn(dl.q.shape, generator=g, device="cuda:0", dtype=torch.float32).to(dl.q.dtype)
+    dq = torch.empty_like(dl.q)
+    dk = torch.zeros(dl.k.shape, dtype=torch.float32, device="cuda:0")
+    dv = torch.zeros_like(dk)
+
+    def call():
+        dl.attend_backward(dl.q, q_pos0, max_pos_end, sel, cnt, out, lse, dout, dq, dk, dv)
+
+    for _ in range(2):
+        call()
+    torch.cuda.synchronize()
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(args.steps):
+        call()
+    stop.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(stop) / args.steps
+    lay = x.layout
+    visits = token_visits(x)
+    entries = group_entries(x, sel.cpu().numpy(), cnt.cpu().numpy())
+    rows = x.batch * x.n_q
+    row_bytes = lay.q_heads * lay.head_dim * 2          # one bf16 row of q, dO, out or dq
+    kd = lay.kv_heads * lay.head_dim
+    parts = {
+        "kv_gather": visits * kd * 2 * 2,               # K and V rows per token visit
+        "p_weight_export": visits * lay.q_heads * 8 * 2,  # written by the query side, read back
+        "rows": rows * row_bytes * 6 + rows * lay.q_heads * 4 * 2,  # q,dO,out,dq,qT,dOT; lse, D
+        "transposed_reads": entries * row_bytes * 2,    # qT and dO^T per group entry
+    }
+    tot = sum(parts.values())
+    log(f"backward {ms:.3f} ms/call, {entries} group entries")
+    return {"ms_per_call": ms, "tok_s": rows / (ms / 1e3), "token_visits": visits,
+            "group_entries": entries, "algorithmic_bytes": parts,
+            "achieved_gbs": tot / (ms * 1e-3) / 1e9,
+            "hbm_frac": tot / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
 
 
 # ----------------------------------------------------------------- decode --
@@ -495,6 +563,7 @@ def main():
         "stages_ms": pre["stages_ms"],
         "score_select_effective_tflops": score_tflops,
         "decode": dec,
+        "backward": pre.get("backward"),
     }
     print(json.dumps(line), flush=True)
 
