@@ -45,8 +45,8 @@ BF16_MFMA_PEAK_TFLOPS = 2500.0
 # figures belong to the attention source with this SHA-1; for any other source
 # `traffic` is reported as null until the counters are taken again.
 ATTN_COUNTERS = {
-    "source_sha1": "8617706e1cc5be4d73e9eab0b00a2c8e4495622a",
-    "fetch_kib": 15033180.7, "write_kib": 66675.1,
+    "source_sha1": "38e5ddb5601b98a9acf4f1ad2fcc2296dd7e3e68",
+    "fetch_kib": 15017750.0, "write_kib": 66673.4,
     "fetch_scale": 2.0, "write_scale": 1.0,
 }
 
