@@ -260,8 +260,12 @@ const char* qsa_last_error(void);  /* thread-local text of the last failure */
  *
  *   q, k_cache, v_cache, q_pos0, max_pos_end, sel_blocks, sel_count
  *              as given to the forward call.
- *   out        (dtype) [batch][n_q][q_heads][head_dim]: the forward output
- *              (validated, not read: D is recomputed exactly).
+ *   out        (dtype) [batch][n_q][q_heads][head_dim]: the forward output.
+ *              bf16 layers with 16 query heads read it for a reference
+ *              D~ = <dO, out> that keeps the dq weights small; D itself is
+ *              always recomputed from the token set, so the result is exact
+ *              (up to rounding) for any out, most accurate for the forward's.
+ *              Other layouts validate it only.
  *   lse        float [batch][n_q][q_heads]: the forward's log-sum-exp.
  *   dout       (dtype) [batch][n_q][q_heads][head_dim]: dL/dout.
  *   dq         (dtype) [batch][n_q][q_heads][head_dim]: written.
@@ -269,9 +273,14 @@ const char* qsa_last_error(void);  /* thread-local text of the last failure */
  *              of this call are ADDED (zero them first, or accumulate the
  *              chunks of a sequence); rows no query attends are untouched.
  *   workspace  >= qsa_workspace_size(QSA_OP_BACKWARD, batch, n_q,
- *              max_pos_end): the per-block query lists and D.
+ *              max_pos_end): transposed query lists and per-head sums; for
+ *              bf16 layers with 16 query heads also q/dO transposed and
+ *              8 bytes per (query, token of its set, head) of softmax
+ *              values -- about 4.3 GB for 16,384 queries at k_B = 512.
+ *              Nothing is kept in it between calls.
  * Supported: kv_heads <= 2 (any dtype, head_dim, block size the forward
- * takes).  dq is deterministic; dk/dv sum each block's queries in an order
+ * takes); sel_blocks ascending without repeats, as qsa_select_topk writes
+ * them.  dq is deterministic; dk/dv sum each token's queries in an order
  * that can change from run to run (the last bits can differ).             */
 qsa_status qsa_sparse_attn_backward(const qsa_config* cfg, int32_t batch, int32_t n_q,
                                     const void* q, const void* k_cache, const void* v_cache,
