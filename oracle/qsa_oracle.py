@@ -45,6 +45,18 @@ Readings where the pages are silent (each is listed in the design doc):
   * Backward (the pages give none): the exact derivative of the sparse
     attention with each query's token set held fixed; no gradient reaches
     the indexer through the top-k_B choice.
+  * Stage-1 indexer distillation ([concept] "Native trainability": an
+    indexer-only warm-up fits the indexer scores to a block-maxpooled dense
+    teacher attention distribution with a KL loss while the model runs dense
+    attention).  Unstated, read as: the teacher is the dense causal
+    attention of the query at p over tokens 0..p, averaged over the main
+    heads; its max over each candidate block's r tokens (b < floor(p/r)),
+    renormalised over the candidates, is the target t; the indexer
+    distribution is softmax over the candidates of I_b (no temperature); the
+    loss of a query is KL(t || softmax(I)), 0 when it has no candidate.  The
+    teacher sends no gradient.  ReLU'(0) = 0.  Gradients reach the stored
+    index rows k_hat (its storage rounding passed straight through) and,
+    through RMSNorm, RoPE and the block mean, the raw indexer keys.
 """
 from __future__ import annotations
 
@@ -57,7 +69,8 @@ __all__ = [
     "round_to_bf16", "round_to_f32", "avg_pool_blocks", "rms_norm", "rope_angles",
     "partial_rope", "compress_index", "block_importance", "top_k_blocks",
     "expand_with_tail", "sparse_attention", "sparse_attention_backward", "RowResult",
-    "qsa_row",
+    "qsa_row", "teacher_block_target", "distill_row", "distill_grads",
+    "compress_index_backward",
 ]
 
 
@@ -271,6 +284,91 @@ def sparse_attention_backward(q_row: np.ndarray, K: np.ndarray, V: np.ndarray,
         np.add.at(dK[:, g, :], S, scale * dS[:, None] * q[h][None, :])
         np.add.at(dV[:, g, :], S, P[:, None] * do[h][None, :])
     return dq
+
+
+# ---------------------------------------------------------------------------
+# stage-1 indexer distillation (loss and its gradients)
+# ---------------------------------------------------------------------------
+def teacher_block_target(q_row: np.ndarray, K: np.ndarray, p: int, r: int,
+                         scale: float) -> np.ndarray:
+    """Target distribution over the candidate blocks b < floor(p/r) of the
+    query at p: the dense causal attention of every main head over tokens
+    0..p, averaged over the heads, max-pooled over each block's r tokens,
+    renormalised over the candidates.
+
+    [concept] "Native trainability" (stage-1: a block-maxpooled version of
+    the dense teacher attention distribution).  Head h reads KV head
+    floor(h*Hkv/Hq), scale as in (B).  Empty when there is no candidate.
+    """
+    c = p // r
+    if c == 0:
+        return np.zeros(0)
+    q = np.asarray(q_row, dtype=np.float64)
+    Hq, d = q.shape
+    Hkv = K.shape[1]
+    Kp = np.asarray(K[: p + 1], dtype=np.float64)
+    mean = np.zeros(p + 1)
+    for h in range(Hq):
+        g = (h * Hkv) // Hq
+        logits = scale * (Kp[:, g, :] @ q[h])
+        w = np.exp(logits - logits.max())
+        mean += w / w.sum()
+    mean /= Hq
+    t = mean[: c * r].reshape(c, r).max(axis=1)
+    return t / t.sum()
+
+
+def distill_row(t: np.ndarray, I: np.ndarray):
+    """KL(t || softmax(I)) over one query's candidates and its gradient with
+    respect to I: dL/dI_b = softmax(I)_b - t_b.
+
+    Terms with t_b = 0 contribute 0 to the loss.  Returns (loss, dI).
+    """
+    t = np.asarray(t, dtype=np.float64)
+    I = np.asarray(I, dtype=np.float64)
+    if t.size == 0:
+        return 0.0, np.zeros(0)
+    m = I.max()
+    lse = m + math.log(np.exp(I - m).sum())
+    logQ = I - lse
+    nz = t > 0
+    loss = float(np.sum(t[nz] * (np.log(t[nz]) - logQ[nz])))
+    return loss, np.exp(logQ) - t
+
+
+def distill_grads(q_idx_row: np.ndarray, k_hat: np.ndarray, dI: np.ndarray):
+    """Back through I_b = sum_h ReLU(<q^h, k_hat_b>) for b < c = len(dI):
+        dq^h     = sum_b dI_b [<q^h, k_hat_b> > 0] k_hat_b
+        dk_hat_b = dI_b sum_h [<q^h, k_hat_b> > 0] q^h
+    Returns (dq_idx [H, D], dk_hat [c, D]); ReLU'(0) = 0.
+    """
+    q = np.asarray(q_idx_row, dtype=np.float64)
+    c = len(dI)
+    kh = np.asarray(k_hat, dtype=np.float64)[:c]
+    on = (kh @ q.T) > 0                      # [c, H]
+    w = on * np.asarray(dI, dtype=np.float64)[:, None]
+    return w.T @ kh, w @ q
+
+
+def compress_index_backward(k_idx: np.ndarray, n_blocks: int, dk_hat: np.ndarray, *,
+                            r: int = 4, gain=None, eps: float = 1e-6, rope_dims: int = 64,
+                            base: float = 10000.0) -> np.ndarray:
+    """dL/dk_idx for rows 0 .. n_blocks*r - 1 given dL/dk_hat of blocks
+    0 .. n_blocks-1, back through compress_index (the storage rounding passed
+    straight through): RoPE's rotation transposed (the same rotation at minus
+    the angle), then RMSNorm's Jacobian
+        dx = (g*dy)/rms - x * sum(g*dy*x) / (D rms^3),  rms = sqrt(mean(x^2)+eps),
+    then 1/r to each of the block's r rows.
+    """
+    d = np.asarray(k_idx).shape[-1]
+    g = np.ones(d) if gain is None else np.asarray(gain, dtype=np.float64)
+    x = avg_pool_blocks(k_idx, r, n_blocks)
+    dy = partial_rope(np.asarray(dk_hat, dtype=np.float64)[:n_blocks],
+                      -r * np.arange(n_blocks), rope_dims, base)
+    rms = np.sqrt(np.mean(x * x, axis=-1, keepdims=True) + eps)
+    gdy = g * dy
+    dx = gdy / rms - x * np.sum(gdy * x, axis=-1, keepdims=True) / (d * rms ** 3)
+    return np.repeat(dx / r, r, axis=0)
 
 
 # ---------------------------------------------------------------------------

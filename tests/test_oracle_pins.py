@@ -446,3 +446,151 @@ def test_full_budget_backward_equals_dense_causal_autograd():
     np.testing.assert_allclose(dK[:n], kt.grad.permute(1, 0, 2).numpy(), atol=1e-11)
     np.testing.assert_allclose(dV[:n], vt.grad.permute(1, 0, 2).numpy(), atol=1e-11)
     assert not dK[n:].any() and not dV[n:].any()
+
+
+# --------------------------------------------------------------------------
+# stage-1 indexer distillation ([concept] "Native trainability", stage 1)
+# --------------------------------------------------------------------------
+def test_teacher_target_is_block_max_of_library_softmax():
+    """One head, one KV head: the target is the block max of torch's causal
+    softmax row, renormalised over the complete blocks before the query's."""
+    rng = np.random.default_rng(41)
+    K = rng.standard_normal((61, 1, 16))
+    q = rng.standard_normal((1, 16))
+    for p, r in ((60, 4), (37, 4), (47, 8), (3, 4)):
+        t = O.teacher_block_target(q, K, p, r, 0.25)
+        c = p // r
+        assert t.shape == (c,)
+        if c == 0:
+            continue
+        logits = torch.tensor(K[: p + 1, 0] @ q[0] * 0.25)
+        a = torch.softmax(logits, 0).numpy()
+        want = a[: c * r].reshape(c, r).max(axis=1)
+        np.testing.assert_allclose(t, want / want.sum(), rtol=1e-12)
+
+
+def test_teacher_target_averages_heads_and_follows_gqa():
+    """Two heads reading two KV heads: the target is built from the mean of
+    the two heads' rows, each against its own KV head."""
+    rng = np.random.default_rng(42)
+    K = rng.standard_normal((40, 2, 8))
+    q = rng.standard_normal((2, 8))
+    p, r = 39, 4
+    rows = []
+    for h in range(2):
+        lg = torch.tensor(K[: p + 1, h] @ q[h] * 0.5)
+        rows.append(torch.softmax(lg, 0).numpy())
+    mean = (rows[0] + rows[1]) / 2
+    want = mean[:36].reshape(9, 4).max(axis=1)
+    np.testing.assert_allclose(O.teacher_block_target(q, K, p, r, 0.5), want / want.sum(),
+                               rtol=1e-12)
+
+
+def test_distill_loss_properties():
+    rng = np.random.default_rng(43)
+    for _ in range(20):
+        c = int(rng.integers(1, 30))
+        t = rng.random(c)
+        t /= t.sum()
+        I = rng.standard_normal(c) * 3
+        loss, dI = O.distill_row(t, I)
+        assert loss >= 0
+        assert abs(dI.sum()) < 1e-12                    # softmax and t both sum to 1
+        # matched distribution: I = log t + const gives zero loss and gradient
+        loss0, dI0 = O.distill_row(t, np.log(t) + 1.7)
+        assert abs(loss0) < 1e-12 and np.abs(dI0).max() < 1e-12
+        # the library KL on the same pair
+        kl = torch.nn.functional.kl_div(torch.log_softmax(torch.tensor(I), 0), torch.tensor(t),
+                                        reduction="sum").item()
+        assert abs(loss - kl) < 1e-10
+    assert O.distill_row(np.zeros(0), np.zeros(0))[0] == 0.0
+
+
+def test_distill_loss_zero_target_terms():
+    """Blocks whose target is 0 add nothing to the loss but still get dI = Q_b."""
+    t = np.array([0.0, 0.25, 0.75])
+    I = np.array([1.0, 0.0, 2.0])
+    loss, dI = O.distill_row(t, I)
+    Q = np.exp(I) / np.exp(I).sum()
+    assert abs(loss - (0.25 * math.log(0.25 / Q[1]) + 0.75 * math.log(0.75 / Q[2]))) < 1e-14
+    np.testing.assert_allclose(dI, Q - t, rtol=1e-14)
+
+
+def _distill_loss_of(q_idx, k_hat, t):
+    I = O.block_importance(q_idx, k_hat, len(t))
+    return O.distill_row(t, I)[0]
+
+
+def test_distill_grads_match_finite_differences():
+    rng = np.random.default_rng(44)
+    H, D, c = 4, 12, 9
+    q = rng.standard_normal((H, D))
+    kh = rng.standard_normal((c, D))
+    t = rng.random(c)
+    t /= t.sum()
+    dots = kh @ q.T
+    assert np.abs(dots).min() > 1e-3                    # away from the ReLU kink
+    _, dI = O.distill_row(t, O.block_importance(q, kh, c))
+    dq, dk = O.distill_grads(q, kh, dI)
+    eps = 1e-6
+    for (arr, grad) in ((q, dq), (kh, dk)):
+        for idx in [(0, 0), (1, 5), (3, 11), (2, 7)]:
+            a = arr.copy(); a[idx] += eps
+            b = arr.copy(); b[idx] -= eps
+            fp = _distill_loss_of(a if arr is q else q, a if arr is kh else kh, t)
+            fm = _distill_loss_of(b if arr is q else q, b if arr is kh else kh, t)
+            assert abs((fp - fm) / (2 * eps) - grad[idx]) < 1e-6
+
+
+def test_compress_backward_matches_finite_differences():
+    """The chain k_idx -> k_hat (fp64 storage) -> weighted sum, differentiated
+    by compress_index_backward, against central differences."""
+    rng = np.random.default_rng(45)
+    r, nb, D = 4, 5, 128
+    k_idx = rng.standard_normal((nb * r, D))
+    gain = rng.uniform(0.5, 1.5, D)
+    W = rng.standard_normal((nb, D))
+
+    def f(k):
+        kh = O.compress_index(k, nb, r=r, gain=gain, eps=1e-6, rope_dims=64, base=10000.0,
+                              storage="f64")
+        return float((W * kh).sum())
+
+    g = O.compress_index_backward(k_idx, nb, W, r=r, gain=gain, eps=1e-6, rope_dims=64,
+                                  base=10000.0)
+    assert g.shape == k_idx.shape
+    eps = 1e-6
+    for idx in [(0, 0), (3, 31), (5, 32), (9, 63), (12, 64), (19, 127)]:
+        a = k_idx.copy(); a[idx] += eps
+        b = k_idx.copy(); b[idx] -= eps
+        assert abs((f(a) - f(b)) / (2 * eps) - g[idx]) < 1e-6
+
+
+def test_distill_chain_to_raw_keys_matches_finite_differences():
+    """Loss of one query as a function of the raw indexer keys and q_idx:
+    compression, scoring, softmax and KL end to end."""
+    rng = np.random.default_rng(46)
+    r, nb, D, H = 4, 6, 128, 4
+    k_idx = rng.standard_normal((nb * r + 2, D))
+    q = rng.standard_normal((H, D)) * 0.3
+    t = rng.random(nb)
+    t /= t.sum()
+
+    def loss(k, qq):
+        kh = O.compress_index(k, nb, r=r, storage="f64")
+        return _distill_loss_of(qq, kh, t)
+
+    kh = O.compress_index(k_idx, nb, r=r, storage="f64")
+    assert np.abs(kh @ q.T).min() > 1e-4
+    _, dI = O.distill_row(t, O.block_importance(q, kh, nb))
+    dq, dkh = O.distill_grads(q, kh, dI)
+    dk = O.compress_index_backward(k_idx, nb, dkh, r=r)
+    eps = 1e-6
+    for idx in [(0, 3), (7, 40), (23, 100)]:
+        a = k_idx.copy(); a[idx] += eps
+        b = k_idx.copy(); b[idx] -= eps
+        assert abs((loss(a, q) - loss(b, q)) / (2 * eps) - dk[idx]) < 1e-6
+    for idx in [(0, 0), (3, 77)]:
+        a = q.copy(); a[idx] += eps
+        b = q.copy(); b[idx] -= eps
+        assert abs((loss(k_idx, a) - loss(k_idx, b)) / (2 * eps) - dq[idx]) < 1e-6
