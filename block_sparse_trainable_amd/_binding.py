@@ -18,11 +18,12 @@ _lib = None
 QSA_OK, QSA_ERR_INVALID_ARGUMENT, QSA_ERR_UNSUPPORTED, QSA_ERR_WORKSPACE, QSA_ERR_DEVICE = range(5)
 QSA_F32, QSA_BF16 = 0, 1
 (QSA_OP_INDEX_BUILD, QSA_OP_SELECT, QSA_OP_PREFILL, QSA_OP_DECODE, QSA_OP_DECODE_STEP,
- QSA_OP_BACKWARD) = range(6)
+ QSA_OP_BACKWARD, QSA_OP_DISTILL) = range(7)
 
 EXPORTED = (
     "qsa_index_build", "qsa_select_topk", "qsa_sparse_attn_prefill", "qsa_sparse_attn_decode",
-    "qsa_decode_step", "qsa_sparse_attn_backward", "qsa_workspace_size", "qsa_status_string",
+    "qsa_decode_step", "qsa_sparse_attn_backward", "qsa_index_build_backward",
+    "qsa_indexer_distill", "qsa_workspace_size", "qsa_status_string",
     "qsa_last_error", "qsa_abi_version",
 )
 
@@ -90,6 +91,8 @@ def load(path: str | None = None):
         "qsa_decode_step": [CFG, I32, P, P, P, P, P, P, P, I64, P, I32, P, P, P, P, P, P, SZ, P],
         "qsa_sparse_attn_backward": [CFG, I32, I32, P, P, P, I64, P, I32, P, P, P, P, P, P, P,
                                      P, P, SZ, P],
+        "qsa_index_build_backward": [CFG, I32, P, I64, P, P, I32, P, P, P, P],
+        "qsa_indexer_distill": [CFG, I32, I32, P, P, I64, P, I32, P, P, P, P, P, P, SZ, P],
         "qsa_workspace_size": [CFG, I32, I32, I32, I32, ctypes.POINTER(SZ)],
     }
     for name, args in sig.items():
@@ -198,3 +201,22 @@ def qsa_sparse_attn_backward(cfg, batch, n_q, q, k_cache, v_cache, cap_tokens, q
                                              _ptr(sel_count), _ptr(out), _ptr(lse), _ptr(dout),
                                              _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace),
                                              workspace_bytes, _stream(stream)))
+
+
+def qsa_index_build_backward(cfg, batch, k_idx, cap_tokens, len_before, len_after,
+                             max_new_blocks, rms_gain, dk_cmp, dk_idx, stream=None) -> None:
+    lib = load()
+    _check(lib, lib.qsa_index_build_backward(ctypes.byref(cfg), batch, _ptr(k_idx), cap_tokens,
+                                             _ptr(len_before), _ptr(len_after), max_new_blocks,
+                                             _ptr(rms_gain), _ptr(dk_cmp), _ptr(dk_idx),
+                                             _stream(stream)))
+
+
+def qsa_indexer_distill(cfg, batch, n_q, q, k_cache, cap_tokens, q_pos0, max_pos_end, q_idx,
+                        k_cmp, loss, dq_idx, dk_cmp, workspace, workspace_bytes,
+                        stream=None) -> None:
+    lib = load()
+    _check(lib, lib.qsa_indexer_distill(ctypes.byref(cfg), batch, n_q, _ptr(q), _ptr(k_cache),
+                                        cap_tokens, _ptr(q_pos0), max_pos_end, _ptr(q_idx),
+                                        _ptr(k_cmp), _ptr(loss), _ptr(dq_idx), _ptr(dk_cmp),
+                                        _ptr(workspace), workspace_bytes, _stream(stream)))

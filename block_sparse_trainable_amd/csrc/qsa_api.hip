@@ -152,6 +152,7 @@ qsa_status qsa_workspace_size(const qsa_config* cfg, int32_t op, int32_t batch, 
     case QSA_OP_DECODE: *bytes = qsa::attn_workspace_bytes(d, batch, true); break;
     case QSA_OP_DECODE_STEP: *bytes = qsa::step_plan(d, batch, max_pos_end).bytes; break;
     case QSA_OP_BACKWARD: *bytes = qsa::bwd_workspace_bytes(d, batch, n_q, max_pos_end); break;
+    case QSA_OP_DISTILL: *bytes = qsa::distill_workspace_bytes(d, batch, n_q, max_pos_end); break;
     default: return fail(QSA_ERR_INVALID_ARGUMENT, "%s: unknown op %d", fn, op);
   }
   return ok();
@@ -178,6 +179,33 @@ qsa_status qsa_index_build(const qsa_config* cfg, int32_t batch, const void* k_i
     return fail(QSA_ERR_INVALID_ARGUMENT, "%s: rms_gain must be 8-byte aligned", fn);
   return launched(fn, qsa::launch_compress(d, batch, k_idx, cap_tokens, len_before, len_after,
                                            max_new_blocks, rms_gain, k_cmp, stream));
+}
+
+qsa_status qsa_index_build_backward(const qsa_config* cfg, int32_t batch, const void* k_idx,
+                                    int64_t cap_tokens, const int32_t* len_before,
+                                    const int32_t* len_after, int32_t max_new_blocks,
+                                    const float* rms_gain, const float* dk_cmp, float* dk_idx,
+                                    hipStream_t stream) {
+  const char* fn = "qsa_index_build_backward";
+  qsa::Dims d;
+  qsa_status st = check_config(fn, cfg, &d);
+  if (st != QSA_OK) return st;
+  if (batch <= 0 || batch > 65535)
+    return fail(QSA_ERR_INVALID_ARGUMENT, "%s: batch must be in [1, 65535]", fn);
+  if (cap_tokens < d.r)
+    return fail(QSA_ERR_INVALID_ARGUMENT, "%s: cap_tokens must be >= block_size", fn);
+  if (max_new_blocks < 0)
+    return fail(QSA_ERR_INVALID_ARGUMENT, "%s: max_new_blocks must be >= 0", fn);
+  QSA_REQUIRE_PTR(k_idx, 8);
+  QSA_REQUIRE_PTR(len_before, 4);
+  QSA_REQUIRE_PTR(len_after, 4);
+  QSA_REQUIRE_PTR(dk_cmp, 8);
+  QSA_REQUIRE_PTR(dk_idx, 8);
+  if (rms_gain && !aligned(rms_gain, 8))
+    return fail(QSA_ERR_INVALID_ARGUMENT, "%s: rms_gain must be 8-byte aligned", fn);
+  return launched(fn, qsa::launch_compress_backward(d, batch, k_idx, cap_tokens, len_before,
+                                                    len_after, max_new_blocks, rms_gain, dk_cmp,
+                                                    dk_idx, stream));
 }
 
 qsa_status qsa_select_topk(const qsa_config* cfg, int32_t batch, int32_t n_q,
@@ -359,6 +387,42 @@ qsa_status qsa_decode_step(const qsa_config* cfg, int32_t batch, const void* q_i
                                               k_cache, v_cache, cap_tokens, q_pos, sel_blocks,
                                               sel_count, sel_scores, out, lse, workspace,
                                               stream));
+}
+
+qsa_status qsa_indexer_distill(const qsa_config* cfg, int32_t batch, int32_t n_q, const void* q,
+                               const void* k_cache, int64_t cap_tokens, const int32_t* q_pos0,
+                               int32_t max_pos_end, const void* q_idx, const void* k_cmp,
+                               float* loss, float* dq_idx, float* dk_cmp, void* workspace,
+                               size_t workspace_bytes, hipStream_t stream) {
+  const char* fn = "qsa_indexer_distill";
+  qsa::Dims d;
+  qsa_status st = check_config(fn, cfg, &d);
+  if (st != QSA_OK) return st;
+  st = check_sizes(fn, batch, n_q, cap_tokens, max_pos_end);
+  if (st != QSA_OK) return st;
+  if (d.kv_heads > 2 || d.q_heads > 16 || d.head_dim > 128 || d.head_dim % 8 != 0)
+    return fail(QSA_ERR_UNSUPPORTED,
+                "%s: q_heads <= 16, kv_heads <= 2 and head_dim a multiple of 8 up to 128 are "
+                "built (got %d, %d, %d)", fn, d.q_heads, d.kv_heads, d.head_dim);
+  if (d.idx_heads > 8)
+    return fail(QSA_ERR_UNSUPPORTED, "%s: idx_heads %d (at most 8)", fn, d.idx_heads);
+  QSA_REQUIRE_PTR(q, 16);
+  QSA_REQUIRE_PTR(k_cache, 16);
+  QSA_REQUIRE_PTR(q_pos0, 4);
+  QSA_REQUIRE_PTR(q_idx, 16);
+  QSA_REQUIRE_PTR(k_cmp, 16);
+  QSA_REQUIRE_PTR(loss, 4);
+  QSA_REQUIRE_PTR(dq_idx, 8);
+  QSA_REQUIRE_PTR(dk_cmp, 8);
+  const size_t need = qsa::distill_workspace_bytes(d, batch, n_q, max_pos_end);
+  if (!workspace || workspace_bytes < need)
+    return fail(QSA_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn, need,
+                workspace_bytes);
+  if (!aligned16(workspace))
+    return fail(QSA_ERR_INVALID_ARGUMENT, "%s: workspace must be 16-byte aligned", fn);
+  return launched(fn, qsa::launch_distill(d, batch, n_q, q, k_cache, cap_tokens, q_pos0,
+                                          max_pos_end, q_idx, k_cmp, loss, dq_idx, dk_cmp,
+                                          workspace, stream));
 }
 
 }  // extern "C"

@@ -255,6 +255,16 @@ hipError_t launch_decode_step(const Dims& d, const StepPlan& pl, int batch, cons
 size_t attn_workspace_bytes(const Dims& d, int rows, bool decode);
 
 // Attention backward: transposed index (per-block query lists) and per-head D.
+size_t distill_workspace_bytes(const Dims& d, int batch, int n_q, int32_t max_pos_end);
+hipError_t launch_distill(const Dims& d, int batch, int n_q, const void* q, const void* k_cache,
+                          int64_t cap, const int32_t* q_pos0, int32_t max_pos_end,
+                          const void* q_idx, const void* k_cmp, float* loss, float* dq_idx,
+                          float* dk_cmp, void* workspace, hipStream_t st);
+hipError_t launch_compress_backward(const Dims& d, int batch, const void* k_idx, int64_t cap,
+                                    const int32_t* len_before, const int32_t* len_after,
+                                    int max_new_blocks, const float* gain, const float* dk_cmp,
+                                    float* dk_idx, hipStream_t st);
+
 size_t bwd_workspace_bytes(const Dims& d, int batch, int n_q, int32_t max_pos_end);
 hipError_t launch_attn_backward(const Dims& d, int batch, int n_q, const void* q,
                                 const void* k_cache, const void* v_cache, int64_t cap,

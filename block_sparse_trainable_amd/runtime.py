@@ -123,6 +123,20 @@ class DeviceLayer:
                                    int(max_pos_end), sel, cnt, out, lse, dout, dq, dk, dv, ws,
                                    ws.numel())
 
+    def distill(self, q_pos0, max_pos_end: int, loss, dq_idx, dk_cmp):
+        """Stage-1 distillation loss of the chunk's queries (per row) with
+        dq_idx written and dk_cmp (fp32, [B][cap/r][128]) added."""
+        n_q = self.q.shape[1]
+        ws = self.workspace(B.QSA_OP_DISTILL, self.batch, n_q, max_pos_end)
+        B.qsa_indexer_distill(self.cfg, self.batch, n_q, self.q, self.k, self.cap, q_pos0,
+                              int(max_pos_end), self.q_idx, self.k_cmp, loss, dq_idx, dk_cmp,
+                              ws, ws.numel())
+
+    def index_build_backward(self, len_before, len_after, max_new_blocks: int, dk_cmp,
+                             dk_idx) -> None:
+        B.qsa_index_build_backward(self.cfg, self.batch, self.k_idx, self.cap, len_before,
+                                   len_after, int(max_new_blocks), self.gain, dk_cmp, dk_idx)
+
     def attend_decode(self, q, q_pos, max_pos_end: int, sel, cnt, out, lse):
         ws = self.workspace(B.QSA_OP_DECODE, self.batch, 1, max_pos_end)
         B.qsa_sparse_attn_decode(self.cfg, self.batch, q, self.k, self.v, self.cap, q_pos,

@@ -58,7 +58,8 @@ typedef enum {
   QSA_OP_PREFILL = 2,
   QSA_OP_DECODE = 3,
   QSA_OP_DECODE_STEP = 4,
-  QSA_OP_BACKWARD = 5
+  QSA_OP_BACKWARD = 5,
+  QSA_OP_DISTILL = 6
 } qsa_op;
 
 /* Layer configuration.  Supported values are listed per field; anything
@@ -290,6 +291,60 @@ qsa_status qsa_sparse_attn_backward(const qsa_config* cfg, int32_t batch, int32_
                                     const void* dout, void* dq, float* dk, float* dv,
                                     void* workspace, size_t workspace_bytes,
                                     hipStream_t stream);
+
+/* qsa_index_build_backward -- gradient back through qsa_index_build.
+ * For the blocks qsa_index_build builds with the same (len_before,
+ * len_after), adds dL/dk_idx given dL/dk_cmp: the rotation transposed
+ * (RoPE at minus the block's angle), the RMSNorm Jacobian
+ *     dx = (g dy) / rms - x sum(g dy x) / (idx_dim rms^3),
+ *     rms = sqrt(mean(x^2) + eps),  x = the block mean,
+ * then dx / r to each of the block's r rows; the storage rounding of k_cmp
+ * is passed straight through.  fp64 arithmetic, as the forward.
+ *
+ *   k_idx, len_before, len_after, max_new_blocks, rms_gain
+ *              as given to qsa_index_build (batch <= 65535).
+ *   dk_cmp     float [batch][cap_tokens / r][idx_dim]: dL/dk_cmp.
+ *   dk_idx     float [batch][cap_tokens][idx_dim]: ADDED into at the rows of
+ *              the blocks in range.                                        */
+qsa_status qsa_index_build_backward(const qsa_config* cfg, int32_t batch, const void* k_idx,
+                                    int64_t cap_tokens, const int32_t* len_before,
+                                    const int32_t* len_after, int32_t max_new_blocks,
+                                    const float* rms_gain, const float* dk_cmp, float* dk_idx,
+                                    hipStream_t stream);
+
+/* qsa_indexer_distill -- stage-1 indexer distillation loss and gradients.
+ * [concept] "Native trainability", stage 1: the indexer scores are fitted to
+ * a block-maxpooled version of the dense teacher attention distribution
+ * with a KL loss while the model runs dense attention.  The pages leave the
+ * details open; taken here: for the query at p (c = floor(p/r) candidate
+ * blocks), the teacher is the dense causal attention over tokens 0..p
+ * averaged over the q_heads heads (head h reads KV head h*Hkv/Hq, the
+ * forward's scale); t_b is its max over block b's r tokens, renormalised over
+ * b < c; the student is softmax_b(I_b) over the same blocks, I as in
+ * qsa_select_topk; the loss of the query is KL(t || softmax(I)), 0 when
+ * c = 0.  The teacher sends no gradient; ReLU'(0) = 0.  With
+ * dI_b = softmax(I)_b - t_b:
+ *     dq_idx^h = sum_b dI_b [<q_idx^h, k_b> > 0] k_b,
+ *     dk_cmp_b += sum over the call's queries of dI_b sum_h [..] q_idx^h.
+ *
+ *   q, k_cache, cap_tokens, q_pos0, max_pos_end
+ *              as for qsa_sparse_attn_prefill (the teacher's query rows and
+ *              keys; values are not needed).
+ *   q_idx, k_cmp  as for qsa_select_topk (blocks below floor(p/r) built).
+ *   loss       float [batch][n_q]: each query's KL, written.
+ *   dq_idx     float [batch][n_q][idx_heads][idx_dim]: written.
+ *   dk_cmp     float [batch][cap_tokens / r][idx_dim]: ADDED into.
+ *   workspace  >= qsa_workspace_size(QSA_OP_DISTILL, batch, n_q,
+ *              max_pos_end): per-head teacher sums and, per (query,
+ *              candidate block), t_b / dI_b, I_b and the ReLU mask
+ *              (9 bytes each).  Nothing is kept between calls.
+ * Supported: q_heads <= 16, kv_heads <= 2, head_dim a multiple of 8 up to
+ * 128, idx_heads <= 8, every dtype and block size of the forward.       */
+qsa_status qsa_indexer_distill(const qsa_config* cfg, int32_t batch, int32_t n_q, const void* q,
+                               const void* k_cache, int64_t cap_tokens, const int32_t* q_pos0,
+                               int32_t max_pos_end, const void* q_idx, const void* k_cmp,
+                               float* loss, float* dq_idx, float* dk_cmp, void* workspace,
+                               size_t workspace_bytes, hipStream_t stream);
 
 int32_t qsa_abi_version(void);     /* 1 */
 
