@@ -25,6 +25,7 @@
 //   compress_bwd     one wave per block: back through RoPE, RMSNorm, mean.
 #include <math.h>
 
+#include "attn_tile.h"
 #include "qsa_common.h"
 
 namespace qsa {
@@ -79,10 +80,11 @@ __device__ float wg_max(float v, float* red) {
 
 struct DistillWs {
   float* lse;      // [rows][Hq]   teacher log-sum-exp per head
-  float* tb;       // [rows][W]    block maxima t_b, then dI_b
-  float* ib;       // [rows][W]    I_b
+  float* um;       // [rows][Wu]   teacher maximum over each 4-token unit
+  float* ib;       // [rows][W]    I_b, then dI_b
   uint8_t* mk;     // [rows][W]    bit h: <q_idx^h, k_b> > 0
   int64_t W;       // row stride (candidates of the longest row, rounded up)
+  int64_t Wu;      // row stride of um (4-token units below max_pos_end, rounded up)
 };
 
 // ------------------------------------------------------------------ teacher --
@@ -119,7 +121,6 @@ __global__ __launch_bounds__(kDT) void distill_teacher_kernel(
     m[h] = -INFINITY;
     l[h] = 0.0f;
   }
-  const int r = 1 << lr;
   const int64_t end = PASS == 1 ? p + 1 : (c << lr);   // pass 2: candidate blocks only
   for (int64_t base = 0; base < end; base += kDT) {
     const int64_t t = base + threadIdx.x;
@@ -159,14 +160,12 @@ __global__ __launch_bounds__(kDT) void distill_teacher_kernel(
     if constexpr (PASS == 2) {
       tt[threadIdx.x] = mean / (float)Hq;
       __syncthreads();
-      const int nb = kDT >> lr;   // blocks in this stretch (r <= 128 divides 256)
-      if ((int)threadIdx.x < nb) {
-        const int64_t b = (base >> lr) + threadIdx.x;
-        if (b < c) {
-          float mx = 0.0f;
-          for (int u = 0; u < r; ++u) mx = fmaxf(mx, tt[threadIdx.x * r + u]);
-          ws.tb[row * ws.W + b] = mx;
-        }
+      if ((int)threadIdx.x < kDT / 4) {
+        const int64_t u = (base >> 2) + threadIdx.x;
+        if (u < (c << (lr - 2)))
+          ws.um[row * ws.Wu + u] =
+              fmaxf(fmaxf(tt[4 * threadIdx.x], tt[4 * threadIdx.x + 1]),
+                    fmaxf(tt[4 * threadIdx.x + 2], tt[4 * threadIdx.x + 3]));
       }
       __syncthreads();
     }
@@ -178,6 +177,198 @@ __global__ __launch_bounds__(kDT) void distill_teacher_kernel(
       const float M = wg_max(m[h], red);
       const float L = wg_sum(m[h] == -INFINITY ? 0.0f : l[h] * expf(m[h] - M), red);
       if (threadIdx.x == 0) ws.lse[row * Hq + h] = M + logf(L);
+    }
+  }
+}
+
+// ------------------------------------------------------------ teacher, MFMA --
+// bf16 layers with 16 query heads (the forward's MFMA shapes).  One workgroup
+// of 8 waves per 32 consecutive query rows of a sequence; each wave owns 4 of
+// them, i.e. 64 (query, head) columns = 4 MFMA column groups of 16: with Hkv
+// KV heads a group holds Hkv queries x 16/Hkv heads of one KV head.  The queries sit in
+// B-operand registers for the whole token loop; all eight waves share each
+// 32-token K tile, staged in LDS (swizzled as the backward's K tile) and read
+// as A operands: S^T = K_tile * Q per column group (v_mfma_f32_16x16x32_bf16).
+// PASS 1 keeps an online (max, sum) per column in the log2 domain and writes
+// lse per (row, head); PASS 2 turns the logits into probabilities, sums each
+// (query, token)'s 16 heads across lanes, and writes the maximum of the head
+// mean over each 4-token unit below the query's candidate limit.
+__device__ __forceinline__ float swz_add(float v, int pattern_xor) {
+  // ds_swizzle in bit-mask mode: lane' = lane ^ x within each 32-lane half
+  int r;
+  switch (pattern_xor) {
+    case 1: r = __builtin_amdgcn_ds_swizzle(__float_as_int(v), 0x041F); break;
+    case 2: r = __builtin_amdgcn_ds_swizzle(__float_as_int(v), 0x081F); break;
+    case 4: r = __builtin_amdgcn_ds_swizzle(__float_as_int(v), 0x101F); break;
+    default: r = __builtin_amdgcn_ds_swizzle(__float_as_int(v), 0x201F); break;
+  }
+  return v + __int_as_float(r);
+}
+
+constexpr int kTW = 8;   // waves per teacher workgroup
+
+template <int HKV, int D, int PASS>
+__global__ __launch_bounds__(64 * kTW) void distill_teacher_mfma_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ kc, int64_t cap, int n_q,
+    const int32_t* __restrict__ q_pos0, float scale, int lr, DistillWs ws) {
+  using S = MfmaShape<HKV, D>;
+  constexpr int KD = S::KD, ROWB = S::ROWB, CH = S::CH, RPI = S::RPI;
+  constexpr int G = 16 / HKV;          // heads per KV head
+  constexpr int QPC = HKV;             // queries per column group
+  constexpr int NKD = D / 32;          // k-steps over one KV head's dims
+  constexpr int NCG = 4;               // column groups per wave
+  __shared__ __attribute__((aligned(16))) unsigned char kbuf[2][32 * ROWB];   // double-buffered
+  constexpr int NL = (32 / RPI) / kTW;   // tile loads per lane
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int l16 = lane & 15, gq = lane >> 4;
+  const int tiles_per_seq = (n_q + 31) / 32;
+  const int s = blockIdx.x / tiles_per_seq;
+  const int j0 = (blockIdx.x % tiles_per_seq) * 32;
+  const int64_t pos0 = q_pos0[s];
+  auto qpos = [&](int j) -> int64_t { return min(max(pos0 + j, (int64_t)0), cap - 1); };
+  // token range of the tile
+  const int jl = min(j0 + 31, n_q - 1);
+  const int64_t pmax = qpos(jl);
+  const int64_t tok_end = PASS == 1 ? pmax + 1 : ((pmax >> lr) << lr);
+  if (tok_end <= 0) return;
+  // this lane's column in group cg: query qcol(cg), head hcol(cg); rows
+  // past n_q stand in for the last row and write nothing
+  auto qcol = [&](int cg) { return j0 + 4 * wave + (cg / HKV) * QPC + l16 / G; };
+  auto hcol = [&](int cg) { return (cg % HKV) * G + l16 % G; };
+  int32_t pq[NCG];   // positions (cap < 2^31)
+  u32x4 qb[NCG][NKD];
+  float lse2[NCG];
+#pragma unroll
+  for (int cg = 0; cg < NCG; ++cg) {
+    const int jj = min(qcol(cg), jl);
+    pq[cg] = (int32_t)qpos(jj);
+    const int64_t row = (int64_t)s * n_q + jj;
+#pragma unroll
+    for (int kk = 0; kk < NKD; ++kk)
+      qb[cg][kk] = ld16(q + (row * 16 + hcol(cg)) * D + 32 * kk + 8 * gq);
+    if constexpr (PASS == 2) lse2[cg] = ws.lse[row * 16 + hcol(cg)] * kLog2e;
+  }
+  const float sl2 = scale * kLog2e;
+  float m[NCG], l[NCG];
+#pragma unroll
+  for (int cg = 0; cg < NCG; ++cg) {
+    m[cg] = -INFINITY;
+    l[cg] = 0.0f;
+  }
+  static_assert(NL >= 1 && NL * kTW * RPI == 32, "tile loads must split evenly over the waves");
+  const uint16_t* kbase = kc + (int64_t)s * cap * KD;
+  // K rows of the tile at t0 into buffer bf (rows past tok_end read row 0, unused)
+  auto load_tile = [&](int64_t t0, int bf) {
+#pragma unroll
+    for (int v = 0; v < NL; ++v) {
+      const int u = wave + kTW * v;
+      const int tk = RPI * u + lane / CH;
+      const int chunk = (lane % CH) ^ (tk & 15);
+      const int64_t tp = t0 + tk < tok_end ? t0 + tk : 0;
+      __builtin_amdgcn_global_load_lds(
+          (const __attribute__((address_space(1))) void*)(kbase + tp * KD + chunk * 8),
+          (__attribute__((address_space(3))) void*)(kbuf[bf] + u * 1024), 16, 0, 0);
+    }
+  };
+  load_tile(0, 0);
+  int bf = 0;
+  for (int64_t t0 = 0; t0 < tok_end; t0 += 32, bf ^= 1) {
+    // the next tile's loads go out first; then wait for this tile's (the
+    // in-order count leaves only the NL loads just issued outstanding)
+    if (t0 + 32 < tok_end) {
+      load_tile(t0 + 32, bf ^ 1);
+      __builtin_amdgcn_s_waitcnt(NL | 0x70 | 0xF00);   // vmcnt(NL), expcnt/lgkmcnt any
+    } else {
+      __builtin_amdgcn_s_waitcnt(0);
+    }
+    __syncthreads();
+    const unsigned char* kt = kbuf[bf];
+    // S^T per column group and 16-token half
+    f32x4 sa[NCG][2];
+#pragma unroll
+    for (int cg = 0; cg < NCG; ++cg) sa[cg][0] = sa[cg][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int st = 0; st < 2; ++st) {
+      const int tk = 16 * st + l16;
+#pragma unroll
+      for (int g = 0; g < HKV; ++g)
+#pragma unroll
+        for (int kk = 0; kk < NKD; ++kk) {
+          const int c0 = (g * D + 32 * kk + 8 * gq) / 8;
+          const u32x4 a = *reinterpret_cast<const u32x4*>(kt + tk * ROWB + ((c0 ^ (tk & 15)) * 16));
+#pragma unroll
+          for (int cg = g; cg < NCG; cg += HKV)
+            sa[cg][st] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(qb[cg][kk]),
+                                                                 sa[cg][st], 0, 0, 0);
+        }
+    }
+    if constexpr (PASS == 1) {
+#pragma unroll
+      for (int cg = 0; cg < NCG; ++cg) {
+        float x[2][4], mt = -INFINITY;
+#pragma unroll
+        for (int st = 0; st < 2; ++st)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int64_t tp = t0 + 16 * st + 4 * gq + i;
+            x[st][i] = tp <= (int64_t)pq[cg] ? sa[cg][st][i] * sl2 : -INFINITY;
+            mt = fmaxf(mt, x[st][i]);
+          }
+        mt = wave_max_xor32(wave_max_xor16(mt));
+        const float mn = fmaxf(m[cg], mt);
+        if (mn != -INFINITY) {
+          float ps = 0.0f;
+#pragma unroll
+          for (int st = 0; st < 2; ++st)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) ps += exp2f(x[st][i] - mn);
+          l[cg] = l[cg] * exp2f(m[cg] - mn) + ps;
+          m[cg] = mn;
+        }
+      }
+    } else {
+#pragma unroll
+      for (int qs = 0; qs < NCG / HKV; ++qs) {
+        float v[2][4];
+#pragma unroll
+        for (int st = 0; st < 2; ++st)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            float a = 0.0f;
+#pragma unroll
+            for (int g = 0; g < HKV; ++g) {
+              const int cg = qs * HKV + g;
+              a += exp2f(fmaf(sa[cg][st][i], sl2, -lse2[cg]));
+            }
+            // sum over the query's heads held by the lanes of this group
+            a = swz_add(a, 1);
+            a = swz_add(a, 2);
+            a = swz_add(a, 4);
+            if constexpr (HKV == 1) a = swz_add(a, 8);
+            v[st][i] = a * (1.0f / 16.0f);
+          }
+        const int cg0 = qs * HKV;
+        if (l16 % G == 0 && qcol(cg0) < n_q) {
+          const int64_t row = (int64_t)s * n_q + qcol(cg0);
+          const int64_t nu = ((int64_t)pq[cg0] >> lr) << (lr - 2);   // candidate units
+#pragma unroll
+          for (int st = 0; st < 2; ++st) {
+            const int64_t u = (t0 + 16 * st + 4 * gq) >> 2;
+            if (u < nu)
+              ws.um[row * ws.Wu + u] =
+                  fmaxf(fmaxf(v[st][0], v[st][1]), fmaxf(v[st][2], v[st][3]));
+          }
+        }
+      }
+    }
+    __syncthreads();  // every wave is done with this buffer before it is refilled
+  }
+  if constexpr (PASS == 1) {
+#pragma unroll
+    for (int cg = 0; cg < NCG; ++cg) {
+      const float lt = wave_add_xor32(wave_add_xor16(l[cg]));
+      if (gq == 0 && qcol(cg) < n_q)
+        ws.lse[((int64_t)s * n_q + qcol(cg)) * 16 + hcol(cg)] = (m[cg] + log2f(lt)) * kLn2;
     }
   }
 }
@@ -197,8 +388,9 @@ __global__ __launch_bounds__(kDT) void distill_student_kernel(
   const int64_t c = p >> lr;
   for (int i = threadIdx.x; i < H * 128; i += kDT) qs[i] = ldv<BF16>(q_idx, row * H * 128 + i);
   __syncthreads();
-  float* tb = ws.tb + row * ws.W;
+  const float* um = ws.um + row * ws.Wu;
   float* ib = ws.ib + row * ws.W;
+  const int m4 = 1 << (lr - 2);   // 4-token units per block
   uint8_t* mk = ws.mk + row * ws.W;
   // pass 1: I_b, masks; online logsumexp of I; Z, sum t log t, sum t I
   float m = -INFINITY, l = 0.0f, z = 0.0f, a = 0.0f, bI = 0.0f;
@@ -233,7 +425,8 @@ __global__ __launch_bounds__(kDT) void distill_student_kernel(
     const float mn = fmaxf(m, I);
     l = l * expf(m - mn) + expf(I - mn);
     m = mn;
-    const float t = tb[b];
+    float t = um[b * m4];
+    for (int u = 1; u < m4; ++u) t = fmaxf(t, um[b * m4 + u]);
     z += t;
     if (t > 0.0f) a += t * logf(t);
     bI += t * I;
@@ -245,16 +438,20 @@ __global__ __launch_bounds__(kDT) void distill_student_kernel(
   const float BI = wg_sum(bI, red);
   const float lseI = M + logf(L);
   if (threadIdx.x == 0) loss[row] = c > 0 ? A / Z - logf(Z) - BI / Z + lseI : 0.0f;
-  // pass 2: dI_b over t_b in place
+  // pass 2: dI_b over I_b in place
   const float invZ = c > 0 ? 1.0f / Z : 0.0f;
-  for (int64_t b = threadIdx.x; b < c; b += kDT) tb[b] = expf(ib[b] - lseI) - tb[b] * invZ;
+  for (int64_t b = threadIdx.x; b < c; b += kDT) {
+    float t = um[b * m4];
+    for (int u = 1; u < m4; ++u) t = fmaxf(t, um[b * m4 + u]);
+    ib[b] = expf(ib[b] - lseI) - t * invZ;
+  }
   __syncthreads();
   // dq_idx^h: thread (h, dims 2e, 2e+1), blocks in order
   const int h = threadIdx.x >> 6, e = threadIdx.x & 63;
   for (int hh = h; hh < H; hh += 4) {
     float d0 = 0.0f, d1 = 0.0f;
     for (int64_t b = 0; b < c; ++b) {
-      const float w = ((mk[b] >> hh) & 1u) ? tb[b] : 0.0f;
+      const float w = ((mk[b] >> hh) & 1u) ? ib[b] : 0.0f;
       const int64_t ko = ((int64_t)s * cap_blocks + b) * 128 + 2 * e;
       d0 = fmaf(w, ldv<BF16>(k_cmp, ko), d0);
       d1 = fmaf(w, ldv<BF16>(k_cmp, ko + 1), d1);
@@ -285,7 +482,7 @@ __global__ __launch_bounds__(kDT) void distill_dk_kernel(
   float d0 = 0.0f, d1 = 0.0f;
   for (int64_t jj = j0 + rl; jj < n_q; jj += 4) {
     const int64_t row = (int64_t)s * n_q + jj;
-    const float dI = ws.tb[row * ws.W + b];
+    const float dI = ws.ib[row * ws.W + b];
     const uint32_t bits = ws.mk[row * ws.W + b];
     for (int h = 0; h < H; ++h) {
       if (!((bits >> h) & 1u)) continue;
@@ -388,18 +585,19 @@ DistillWs distill_layout(const Dims& d, int batch, int n_q, int32_t max_pos_end,
                          size_t* bytes) {
   DistillWs w{};
   w.W = score_row_width(d.r, max_pos_end);
+  w.Wu = ((int64_t)max_pos_end / 4 + 3) / 4 * 4;
   const size_t rows = (size_t)batch * n_q;
   auto al = [](size_t v) { return (v + 255) / 256 * 256; };
   size_t o = 0;
   const size_t o_lse = o; o = al(o + 4 * rows * (size_t)d.q_heads);
-  const size_t o_tb = o;  o = al(o + 4 * rows * (size_t)w.W);
+  const size_t o_um = o;  o = al(o + 4 * rows * (size_t)w.Wu);
   const size_t o_ib = o;  o = al(o + 4 * rows * (size_t)w.W);
   const size_t o_mk = o;  o = al(o + rows * (size_t)w.W);
   if (bytes) *bytes = o;
   char* c = static_cast<char*>(base);
   if (c) {
     w.lse = reinterpret_cast<float*>(c + o_lse);
-    w.tb = reinterpret_cast<float*>(c + o_tb);
+    w.um = reinterpret_cast<float*>(c + o_um);
     w.ib = reinterpret_cast<float*>(c + o_ib);
     w.mk = reinterpret_cast<uint8_t*>(c + o_mk);
   }
@@ -422,11 +620,29 @@ hipError_t launch_distill(const Dims& d, int batch, int n_q, const void* q, cons
   const unsigned rows = (unsigned)(batch * n_q);
   const int64_t cap_blocks = cap >> d.lr;
   const int64_t nblk = max((int64_t)(max_pos_end - 1) >> d.lr, (int64_t)1);
+  const bool mfma = d.bf16 && d.q_heads == 16 &&
+                    ((d.kv_heads == 2 && (d.head_dim == 64 || d.head_dim == 128)) ||
+                     (d.kv_heads == 1 && d.head_dim == 128));
+  const unsigned qtiles = (unsigned)(batch * ((n_q + 31) / 32));
+#define QSA_TEACHER_MFMA(HKV, DD)                                                              \
+  else if (d.kv_heads == HKV && d.head_dim == DD) {                                            \
+    hipLaunchKernelGGL((distill_teacher_mfma_kernel<HKV, DD, 1>), dim3(qtiles), dim3(64 * kTW), 0, st, \
+                       static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k_cache), \
+                       cap, n_q, q_pos0, d.scale, d.lr, ws);                                  \
+    hipLaunchKernelGGL((distill_teacher_mfma_kernel<HKV, DD, 2>), dim3(qtiles), dim3(64 * kTW), 0, st, \
+                       static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k_cache), \
+                       cap, n_q, q_pos0, d.scale, d.lr, ws);                                  \
+  }
 #define QSA_DISTILL(BF)                                                                        \
-  hipLaunchKernelGGL((distill_teacher_kernel<BF, 1>), dim3(rows), dim3(kDT), 0, st, q, k_cache, \
-                     cap, n_q, q_pos0, d.q_heads, d.kv_heads, d.head_dim, d.scale, d.lr, ws);  \
-  hipLaunchKernelGGL((distill_teacher_kernel<BF, 2>), dim3(rows), dim3(kDT), 0, st, q, k_cache, \
-                     cap, n_q, q_pos0, d.q_heads, d.kv_heads, d.head_dim, d.scale, d.lr, ws);  \
+  if (!mfma) {                                                                                 \
+    hipLaunchKernelGGL((distill_teacher_kernel<BF, 1>), dim3(rows), dim3(kDT), 0, st, q, k_cache, \
+                       cap, n_q, q_pos0, d.q_heads, d.kv_heads, d.head_dim, d.scale, d.lr, ws); \
+    hipLaunchKernelGGL((distill_teacher_kernel<BF, 2>), dim3(rows), dim3(kDT), 0, st, q, k_cache, \
+                       cap, n_q, q_pos0, d.q_heads, d.kv_heads, d.head_dim, d.scale, d.lr, ws); \
+  }                                                                                            \
+  QSA_TEACHER_MFMA(2, 128)                                                                     \
+  QSA_TEACHER_MFMA(1, 128)                                                                     \
+  QSA_TEACHER_MFMA(2, 64)                                                                      \
   hipLaunchKernelGGL((distill_student_kernel<BF>), dim3(rows), dim3(kDT), 0, st, q_idx, k_cmp,  \
                      cap_blocks, n_q, q_pos0, cap, d.idx_heads, d.lr, ws, loss, dq_idx);      \
   hipLaunchKernelGGL((distill_dk_kernel<BF>), dim3((unsigned)(batch * nblk)), dim3(kDT), 0, st, \
@@ -437,6 +653,7 @@ hipError_t launch_distill(const Dims& d, int batch, int n_q, const void* q, cons
     QSA_DISTILL(false)
   }
 #undef QSA_DISTILL
+#undef QSA_TEACHER_MFMA
   return hipGetLastError();
 }
 
