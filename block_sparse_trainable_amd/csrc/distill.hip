@@ -83,8 +83,11 @@ struct DistillWs {
   float* um;       // [rows][Wu]   teacher maximum over each 4-token unit
   float* ib;       // [rows][W]    I_b, then dI_b
   uint8_t* mk;     // [rows][W]    bit h: <q_idx^h, k_b> > 0
-  int64_t W;       // row stride (candidates of the longest row, rounded up)
+  int64_t W;       // row stride (candidates of the longest row, rounded up to 16)
   int64_t Wu;      // row stride of um (4-token units below max_pos_end, rounded up)
+  uint16_t* qT;    // [rows][128][4]  q_idx transposed (bf16, 4-head MFMA path)
+  uint16_t* kT;    // [batch][nbt/4][128][4]  k_cmp in groups of 4 blocks (same)
+  int64_t nbt;     // blocks per sequence covered by kT (a multiple of 16)
 };
 
 // ------------------------------------------------------------------ teacher --
@@ -461,6 +464,254 @@ __global__ __launch_bounds__(kDT) void distill_student_kernel(
   }
 }
 
+// --------------------------------------------------------- student, MFMA --
+// bf16 index rows, 4 indexer heads.  One wave per 4 consecutive query rows of
+// a sequence (16 (query, head) columns: lane l16 = 4 query + head); blocks in
+// tiles of 16.  Dots: C[block][column] = k_tile * q_idx^T
+// (v_mfma_f32_16x16x32_bf16 over the 128 dims), so lane (column, gq) holds
+// blocks 4gq .. 4gq+3 of its head; the head sum (I) and the mask bits meet
+// across each lane quad.  Pass 1: the query's statistics (online logsumexp
+// of I, Z, sum t log t, sum t I).  Pass 2 recomputes the dots, forms dI and
+// W = dI [dot > 0] -- already the A-operand layout of a 16x16x16 MFMA over
+// blocks -- and accumulates dq_idx = W * k (k in 4-block groups, kT), with W
+// as bf16 hi + lo.  dI and the mask bytes go to the workspace for the key
+// side; q_idx is also written transposed (qT) for it.
+__device__ __forceinline__ float quad_xor1(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float quad_xor2(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float quad_first(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x00, 0xF, 0xF, false));
+}
+
+typedef short bf16x4d __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ void split4(const float (&w)[4], bf16x4d& hi, bf16x4d& lo) {
+  uint32_t h[4], l[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    h[i] = f32_to_bf16(w[i]);
+    l[i] = f32_to_bf16(w[i] - bf16_to_f32(h[i]));
+  }
+  hi = __builtin_bit_cast(bf16x4d, make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16)));
+  lo = __builtin_bit_cast(bf16x4d, make_uint2(l[0] | (l[1] << 16), l[2] | (l[3] << 16)));
+}
+
+__global__ __launch_bounds__(256) void distill_kt_kernel(const uint16_t* __restrict__ k_cmp,
+                                                         int64_t cap_blocks, DistillWs ws) {
+  const int s = blockIdx.y;
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;   // (block, dim)
+  if (i >= ws.nbt * 128) return;
+  const int64_t b = i >> 7;
+  const int d = (int)(i & 127);
+  const uint16_t v = b < cap_blocks ? k_cmp[((int64_t)s * cap_blocks + b) * 128 + d] : (uint16_t)0;
+  ws.kT[(((int64_t)s * (ws.nbt / 4) + (b >> 2)) * 128 + d) * 4 + (b & 3)] = v;
+}
+
+__global__ __launch_bounds__(256) void distill_student_mfma_kernel(
+    const uint16_t* __restrict__ q_idx, const uint16_t* __restrict__ k_cmp, int64_t cap_blocks,
+    int batch, int n_q, const int32_t* __restrict__ q_pos0, int64_t cap, int lr, DistillWs ws,
+    float* __restrict__ loss, float* __restrict__ dq_idx) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int l16 = lane & 15, gq = lane >> 4;
+  const int qn = l16 >> 2, h = l16 & 3;
+  const int wps = (n_q + 3) / 4;                 // waves per sequence
+  const int64_t wg = (int64_t)blockIdx.x * 4 + wave;
+  const int s = (int)(wg / wps);
+  if (s >= batch) return;                        // whole wave
+  const int jb = (int)(wg % wps) * 4;
+  const int j = jb + qn;
+  const bool valid = j < n_q;
+  const int64_t row = (int64_t)s * n_q + (valid ? j : n_q - 1);
+  const int64_t p = min(max((int64_t)q_pos0[s] + (valid ? j : n_q - 1), (int64_t)0), cap - 1);
+  const int64_t c = valid ? p >> lr : 0;
+  const int m4 = 1 << (lr - 2);
+  u32x4 qb[4];
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) qb[kk] = ld16(q_idx + (row * 4 + h) * 128 + 32 * kk + 8 * gq);
+  if (valid) {   // q_idx transposed for the key side: qT[row][dim][head]
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        ws.qT[(row * 128 + 32 * kk + 8 * gq + e) * 4 + h] =
+            (uint16_t)(qb[kk][e >> 1] >> (16 * (e & 1)));
+  }
+  int64_t cmax = c;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1)
+    cmax = max(cmax, (int64_t)__shfl_xor((long long)cmax, off));
+  const uint16_t* kbase = k_cmp + (int64_t)s * cap_blocks * 128;
+  const float* um = ws.um + row * ws.Wu;
+  // dots of the tile at b0: lane holds blocks b0 + 4gq + i for (qn, h)
+  auto dots = [&](int64_t b0, f32x4& acc) {
+    const int64_t kb = min(b0 + l16, cap_blocks - 1);
+    acc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      const u32x4 a = ld16(kbase + kb * 128 + 32 * kk + 8 * gq);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(qb[kk]), acc, 0, 0, 0);
+    }
+  };
+  auto target = [&](int64_t b) {
+    float t = um[b * m4];
+    for (int u = 1; u < m4; ++u) t = fmaxf(t, um[b * m4 + u]);
+    return t;
+  };
+  // ---- pass 1: statistics (lanes h == 0 count each (query, block) once)
+  float m = -INFINITY, l = 0.0f, z = 0.0f, a = 0.0f, bI = 0.0f;
+  for (int64_t b0 = 0; b0 < cmax; b0 += 16) {
+    f32x4 acc;
+    dots(b0, acc);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float I = fmaxf(acc[i], 0.0f);
+      I += quad_xor1(I);
+      I += quad_xor2(I);
+      const int64_t b = b0 + 4 * gq + i;
+      if (h == 0 && b < c) {
+        const float mn = fmaxf(m, I);
+        l = l * exp2f((m - mn) * kLog2e) + exp2f((I - mn) * kLog2e);
+        m = mn;
+        const float t = target(b);
+        z += t;
+        if (t > 0.0f) a += t * logf(t);
+        bI += t * I;
+      }
+    }
+  }
+  // combine the four gq lanes of each (query, head 0) column, then share
+  // the query's figures with its quad
+  {
+    const float M = wave_max_xor32(wave_max_xor16(m));
+    l = (m == -INFINITY) ? 0.0f : l * exp2f((m - M) * kLog2e);
+    m = M;
+  }
+  l = wave_add_xor32(wave_add_xor16(l));
+  z = wave_add_xor32(wave_add_xor16(z));
+  a = wave_add_xor32(wave_add_xor16(a));
+  bI = wave_add_xor32(wave_add_xor16(bI));
+  m = quad_first(m);
+  l = quad_first(l);
+  z = quad_first(z);
+  a = quad_first(a);
+  bI = quad_first(bI);
+  const float lseI = m + logf(l);
+  if (valid && h == 0 && gq == 0) loss[row] = c > 0 ? a / z - logf(z) - bI / z + lseI : 0.0f;
+  const float invZ = c > 0 ? 1.0f / z : 0.0f;
+  // ---- pass 2: dI, masks, dq_idx
+  f32x4 dq[8];
+#pragma unroll
+  for (int db = 0; db < 8; ++db) dq[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const uint16_t* kT = ws.kT + (int64_t)s * (ws.nbt / 4) * 512;
+  for (int64_t b0 = 0; b0 < cmax; b0 += 16) {
+    f32x4 acc;
+    dots(b0, acc);
+    float w[4], dIv[4];
+    uint32_t bits4 = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float I = fmaxf(acc[i], 0.0f);
+      I += quad_xor1(I);
+      I += quad_xor2(I);
+      const int64_t b = b0 + 4 * gq + i;
+      const bool in = b < c;
+      dIv[i] = in ? exp2f((I - lseI) * kLog2e) - target(b) * invZ : 0.0f;
+      const bool on = acc[i] > 0.0f;
+      w[i] = on ? dIv[i] : 0.0f;
+      float bit = on ? (float)(1 << h) : 0.0f;
+      bit += quad_xor1(bit);
+      bit += quad_xor2(bit);
+      bits4 |= (uint32_t)bit << (8 * i);
+    }
+    if (valid && h == 0) {
+      const int64_t o = row * ws.W + b0 + 4 * gq;   // W is a multiple of 16
+      *reinterpret_cast<float4*>(ws.ib + o) = make_float4(dIv[0], dIv[1], dIv[2], dIv[3]);
+      *reinterpret_cast<uint32_t*>(ws.mk + o) = bits4;
+    }
+    bf16x4d whi, wlo;
+    split4(w, whi, wlo);
+    const uint16_t* kt = kT + ((b0 >> 2) + gq) * 512;
+#pragma unroll
+    for (int db = 0; db < 8; ++db) {
+      const bf16x4d bk = __builtin_bit_cast(bf16x4d, *reinterpret_cast<const uint2*>(kt + (16 * db + l16) * 4));
+      dq[db] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(whi, bk, dq[db], 0, 0, 0);
+      dq[db] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(wlo, bk, dq[db], 0, 0, 0);
+    }
+  }
+  // lane (dim 16db + l16, gq) holds (query gq, head i)
+  if (jb + gq < n_q) {
+    const int64_t orow = (int64_t)s * n_q + jb + gq;
+#pragma unroll
+    for (int db = 0; db < 8; ++db)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) dq_idx[(orow * 4 + i) * 128 + 16 * db + l16] = dq[db][i];
+  }
+}
+
+// ------------------------------------------------------------ dk, MFMA --
+// One workgroup per (sequence, 16-block tile); its waves take 4 query rows at
+// a time from the rows that see the tile's first block.  A operand: lane
+// (block, gq) holds W of query gq's 4 heads (dI and mask bytes from the
+// student); B: q_idx transposed (qT), query gq's 4 heads at one dim; 16x16x16
+// MFMAs contract over the 16 (query, head) pairs.  The waves meet in LDS.
+__global__ __launch_bounds__(256) void distill_dk_mfma_kernel(
+    int n_q, const int32_t* __restrict__ q_pos0, int64_t cap, int lr, int64_t ntile,
+    DistillWs ws, float* __restrict__ dk_cmp, int64_t cap_blocks) {
+  __shared__ float sd[16 * 128];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int l16 = lane & 15, gq = lane >> 4;
+  const int s = (int)(blockIdx.x / ntile);
+  const int64_t b0 = (blockIdx.x % ntile) * 16;
+  const int64_t pos0 = q_pos0[s];
+  const int64_t need = (b0 + 1) << lr;
+  if (need > cap - 1) return;
+  const int64_t j0 = max(need - pos0, (int64_t)0);
+  if (j0 >= n_q) return;
+  for (int i = threadIdx.x; i < 16 * 128; i += 256) sd[i] = 0.0f;
+  f32x4 acc[8];
+#pragma unroll
+  for (int db = 0; db < 8; ++db) acc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const int64_t b = b0 + l16;
+  for (int64_t jg = j0 + 4 * wave; jg < n_q; jg += 16) {
+    const int64_t jq = jg + gq;
+    const bool vq = jq < n_q;
+    const int64_t row = (int64_t)s * n_q + (vq ? jq : n_q - 1);
+    const int64_t p = min(max(pos0 + (vq ? jq : n_q - 1), (int64_t)0), cap - 1);
+    float w[4] = {0.f, 0.f, 0.f, 0.f};
+    if (vq && b < (p >> lr)) {
+      const float dI = ws.ib[row * ws.W + b];
+      const uint32_t bits = ws.mk[row * ws.W + b];
+#pragma unroll
+      for (int hh = 0; hh < 4; ++hh) w[hh] = ((bits >> hh) & 1u) ? dI : 0.0f;
+    }
+    bf16x4d whi, wlo;
+    split4(w, whi, wlo);
+    const uint16_t* qt = ws.qT + row * 512;
+#pragma unroll
+    for (int db = 0; db < 8; ++db) {
+      uint2 qv = *reinterpret_cast<const uint2*>(qt + (16 * db + l16) * 4);
+      if (!vq) qv = make_uint2(0u, 0u);
+      const bf16x4d bq = __builtin_bit_cast(bf16x4d, qv);
+      acc[db] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(whi, bq, acc[db], 0, 0, 0);
+      acc[db] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(wlo, bq, acc[db], 0, 0, 0);
+    }
+  }
+  __syncthreads();   // LDS cleared
+  // lane (dim 16db + l16, gq) holds blocks b0 + 4gq + i
+#pragma unroll
+  for (int db = 0; db < 8; ++db)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) atomicAdd(&sd[(4 * gq + i) * 128 + 16 * db + l16], acc[db][i]);
+  __syncthreads();
+  for (int i = threadIdx.x; i < 16 * 128; i += 256) {
+    const int64_t bb = b0 + (i >> 7);
+    if (bb < cap_blocks) dk_cmp[((int64_t)s * cap_blocks + bb) * 128 + (i & 127)] += sd[i];
+  }
+}
+
 // ----------------------------------------------------------------------- dk --
 // One workgroup per (sequence, block b): the rows of the call whose query
 // sees b (p >= r (b + 1)) are a contiguous range j >= j0.  Thread (row lane
@@ -581,10 +832,14 @@ __global__ __launch_bounds__(kDT) void compress_bwd_kernel(
   }
 }
 
+bool distill_student_mfma(const Dims& d) { return d.bf16 && d.idx_heads == 4 && d.idx_dim == 128; }
+
 DistillWs distill_layout(const Dims& d, int batch, int n_q, int32_t max_pos_end, void* base,
                          size_t* bytes) {
   DistillWs w{};
-  w.W = score_row_width(d.r, max_pos_end);
+  const int64_t cmax = max((int64_t)(max_pos_end - 1) >> d.lr, (int64_t)1);
+  w.W = (cmax + 15) / 16 * 16;
+  w.nbt = w.W;
   w.Wu = ((int64_t)max_pos_end / 4 + 3) / 4 * 4;
   const size_t rows = (size_t)batch * n_q;
   auto al = [](size_t v) { return (v + 255) / 256 * 256; };
@@ -593,6 +848,9 @@ DistillWs distill_layout(const Dims& d, int batch, int n_q, int32_t max_pos_end,
   const size_t o_um = o;  o = al(o + 4 * rows * (size_t)w.Wu);
   const size_t o_ib = o;  o = al(o + 4 * rows * (size_t)w.W);
   const size_t o_mk = o;  o = al(o + rows * (size_t)w.W);
+  const bool m4 = distill_student_mfma(d);
+  const size_t o_qt = o;  if (m4) o = al(o + rows * 128 * 4 * 2);
+  const size_t o_kt = o;  if (m4) o = al(o + (size_t)batch * w.nbt * 128 * 2);
   if (bytes) *bytes = o;
   char* c = static_cast<char*>(base);
   if (c) {
@@ -600,6 +858,8 @@ DistillWs distill_layout(const Dims& d, int batch, int n_q, int32_t max_pos_end,
     w.um = reinterpret_cast<float*>(c + o_um);
     w.ib = reinterpret_cast<float*>(c + o_ib);
     w.mk = reinterpret_cast<uint8_t*>(c + o_mk);
+    w.qT = reinterpret_cast<uint16_t*>(c + o_qt);
+    w.kT = reinterpret_cast<uint16_t*>(c + o_kt);
   }
   return w;
 }
@@ -643,14 +903,29 @@ hipError_t launch_distill(const Dims& d, int batch, int n_q, const void* q, cons
   QSA_TEACHER_MFMA(2, 128)                                                                     \
   QSA_TEACHER_MFMA(1, 128)                                                                     \
   QSA_TEACHER_MFMA(2, 64)                                                                      \
-  hipLaunchKernelGGL((distill_student_kernel<BF>), dim3(rows), dim3(kDT), 0, st, q_idx, k_cmp,  \
-                     cap_blocks, n_q, q_pos0, cap, d.idx_heads, d.lr, ws, loss, dq_idx);      \
-  hipLaunchKernelGGL((distill_dk_kernel<BF>), dim3((unsigned)(batch * nblk)), dim3(kDT), 0, st, \
-                     q_idx, n_q, q_pos0, cap, d.idx_heads, d.lr, nblk, ws, dk_cmp, cap_blocks);
+  if (!smfma) {                                                                                \
+    hipLaunchKernelGGL((distill_student_kernel<BF>), dim3(rows), dim3(kDT), 0, st, q_idx, k_cmp, \
+                       cap_blocks, n_q, q_pos0, cap, d.idx_heads, d.lr, ws, loss, dq_idx);    \
+    hipLaunchKernelGGL((distill_dk_kernel<BF>), dim3((unsigned)(batch * nblk)), dim3(kDT), 0, st, \
+                       q_idx, n_q, q_pos0, cap, d.idx_heads, d.lr, nblk, ws, dk_cmp, cap_blocks); \
+  }
+  const bool smfma = distill_student_mfma(d);
   if (d.bf16) {
     QSA_DISTILL(true)
   } else {
     QSA_DISTILL(false)
+  }
+  if (smfma) {
+    const int64_t ntile = ws.nbt / 16;
+    hipLaunchKernelGGL(distill_kt_kernel, dim3((unsigned)((ws.nbt * 128 + 255) / 256), (unsigned)batch),
+                       dim3(256), 0, st, static_cast<const uint16_t*>(k_cmp), cap_blocks, ws);
+    const int64_t waves = (int64_t)batch * ((n_q + 3) / 4);
+    hipLaunchKernelGGL(distill_student_mfma_kernel, dim3((unsigned)((waves + 3) / 4)), dim3(256),
+                       0, st, static_cast<const uint16_t*>(q_idx),
+                       static_cast<const uint16_t*>(k_cmp), cap_blocks, batch, n_q, q_pos0, cap,
+                       d.lr, ws, loss, dq_idx);
+    hipLaunchKernelGGL(distill_dk_mfma_kernel, dim3((unsigned)(batch * ntile)), dim3(256), 0, st,
+                       n_q, q_pos0, cap, d.lr, ntile, ws, dk_cmp, cap_blocks);
   }
 #undef QSA_DISTILL
 #undef QSA_TEACHER_MFMA
