@@ -93,6 +93,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--backward", action=argparse.BooleanOptionalAction, default=True,
                     help="also time the sparse attention backward on the prefill workload")
+    ap.add_argument("--distill", action=argparse.BooleanOptionalAction, default=True,
+                    help="also time the stage-1 indexer distillation on the prefill workload")
     ap.add_argument("--cpu-rows", type=int, default=2304,
                     help="query rows in the oracle's timed sample")
     return ap.parse_args()
@@ -199,6 +201,8 @@ def bench_prefill(args, torch):
     }
     if args.backward:
         res["backward"] = bench_backward(args, torch, x, dl, outs, q_pos0, max_pos_end)
+    if args.distill:
+        res["distill"] = bench_distill(args, torch, x, dl, q_pos0, max_pos_end)
     cfg.update({"q_heads": x.layout.q_heads, "kv_heads": x.layout.kv_heads,
                 "head_dim": x.layout.head_dim, "token_budget": x.layout.token_budget,
                 "block_size": r, "idx_heads": x.layout.idx_heads, "idx_dim": x.layout.idx_dim})
@@ -269,6 +273,47 @@ def bench_backward(args, torch, x, dl, outs, q_pos0, max_pos_end):
             "group_entries": entries, "algorithmic_bytes": parts,
             "achieved_gbs": tot / (ms * 1e-3) / 1e9,
             "hbm_frac": tot / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
+
+
+# ---------------------------------------------------------------- distill --
+def bench_distill(args, torch, x, dl, q_pos0, max_pos_end):
+    """Stage-1 indexer distillation on the chunk: the dense teacher over
+    tokens 0..p of every query (two passes), the student over its candidate
+    blocks, dq_idx and dk_cmp."""
+    lay = x.layout
+    loss = torch.empty((x.batch, x.n_q), dtype=torch.float32, device="cuda:0")
+    dq_idx = torch.empty((x.batch, x.n_q, lay.idx_heads, lay.idx_dim), dtype=torch.float32,
+                         device="cuda:0")
+    dk_cmp = torch.zeros(dl.k_cmp.shape, dtype=torch.float32, device="cuda:0")
+
+    def call():
+        dl.distill(q_pos0, max_pos_end, loss, dq_idx, dk_cmp)
+
+    call()
+    torch.cuda.synchronize()
+    n = max(1, min(args.steps, 3))
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(n):
+        call()
+    stop.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(stop) / n
+    r = lay.block_size
+    visits = cand = 0
+    for s in range(x.batch):
+        p = x.q_pos0[s] + np.arange(x.n_q, dtype=np.int64)
+        visits += int((p + 1).sum())                    # teacher tokens 0..p
+        cand += int((p // r).sum())                     # candidate blocks
+    per_tok = 2 * lay.q_heads * lay.head_dim            # one logit for every head
+    teacher = visits * per_tok + cand * r * per_tok     # pass 1 over 0..p, pass 2 over candidates
+    student = cand * 2 * lay.idx_heads * lay.idx_dim * 4   # dots twice, dq_idx, dk_cmp
+    log(f"distill {ms:.3f} ms/call")
+    return {"ms_per_call": ms, "rows_per_s": x.batch * x.n_q / (ms / 1e3),
+            "teacher_token_visits": visits, "candidate_pairs": cand,
+            "flops": {"teacher": teacher, "student": student},
+            "mfma_frac": (teacher + student) / (ms * 1e-3) / (BF16_MFMA_PEAK_TFLOPS * 1e12),
+            "mean_loss": float(loss.mean().item())}
 
 
 # ----------------------------------------------------------------- decode --
@@ -564,6 +609,7 @@ def main():
         "score_select_effective_tflops": score_tflops,
         "decode": dec,
         "backward": pre.get("backward"),
+        "distill": pre.get("distill"),
     }
     print(json.dumps(line), flush=True)
 

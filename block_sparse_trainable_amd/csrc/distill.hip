@@ -16,12 +16,16 @@
 //     dq_idx^h = sum_b dI_b [<q^h, k_b> > 0] k_b,
 //     dk_b    += dI_b sum_h [<q^h, k_b> > 0] q^h        (ReLU'(0) = 0).
 //
-// Kernels (one workgroup of 256 threads per query row unless noted):
+// Kernels.  bf16 layers with 16 query heads (teacher) and 4 indexer heads
+// (student, key side) take the MFMA kernels; other layouts the VALU ones
+// (one workgroup of 256 threads per query row unless noted):
 //   teacher<PASS 1>  per head, the dense log-sum-exp over tokens 0..p;
-//   teacher<PASS 2>  the head-averaged probabilities, max-pooled per block;
+//   teacher<PASS 2>  the head-averaged probabilities, max-pooled per 4-token
+//                    unit (a block's target is the max over its units);
 //   student          I_b, the loss terms, dI_b and dq_idx;
-//   dk               one workgroup per (sequence, block): the rows whose
-//                    candidates include the block form a contiguous range;
+//   dk               one workgroup per (sequence, block) -- MFMA: per
+//                    16-block tile: the rows whose candidates include the
+//                    block form a contiguous range;
 //   compress_bwd     one wave per block: back through RoPE, RMSNorm, mean.
 #include <math.h>
 

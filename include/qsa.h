@@ -335,9 +335,12 @@ qsa_status qsa_index_build_backward(const qsa_config* cfg, int32_t batch, const 
  *   dq_idx     float [batch][n_q][idx_heads][idx_dim]: written.
  *   dk_cmp     float [batch][cap_tokens / r][idx_dim]: ADDED into.
  *   workspace  >= qsa_workspace_size(QSA_OP_DISTILL, batch, n_q,
- *              max_pos_end): per-head teacher sums and, per (query,
- *              candidate block), t_b / dI_b, I_b and the ReLU mask
- *              (9 bytes each).  Nothing is kept between calls.
+ *              max_pos_end): per-head teacher sums, the teacher's maximum
+ *              per (query, 4-token unit), and per (query, candidate block)
+ *              I_b / dI_b and the ReLU mask; with bf16 and 4 indexer heads
+ *              also q_idx and k_cmp regrouped for the MFMA operands
+ *              (about 5 GB for 16,384 queries over 135K tokens).  Nothing is
+ *              kept between calls.
  * Supported: q_heads <= 16, kv_heads <= 2, head_dim a multiple of 8 up to
  * 128, idx_heads <= 8, every dtype and block size of the forward.       */
 qsa_status qsa_indexer_distill(const qsa_config* cfg, int32_t batch, int32_t n_q, const void* q,
