@@ -16,6 +16,6 @@ from ._binding import (  # noqa: F401
     EXPORTED, QSA_BF16, QSA_F32, QSA_OP_BACKWARD, QSA_OP_DECODE, QSA_OP_DECODE_STEP,
     QSA_OP_DISTILL, QSA_OP_INDEX_BUILD, QSA_OP_PREFILL, QSA_OP_SELECT, QsaConfig, QsaError,
     library_path, load, qsa_decode_step, qsa_index_build, qsa_index_build_backward,
-    qsa_indexer_distill, qsa_select_topk, qsa_sparse_attn_backward, qsa_sparse_attn_decode,
-    qsa_sparse_attn_prefill, qsa_workspace_size,
+    qsa_indexer_distill, qsa_offload_stage, qsa_select_topk, qsa_sparse_attn_backward,
+    qsa_sparse_attn_decode, qsa_sparse_attn_prefill, qsa_workspace_size,
 )

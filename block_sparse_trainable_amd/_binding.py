@@ -23,7 +23,7 @@ QSA_F32, QSA_BF16 = 0, 1
 EXPORTED = (
     "qsa_index_build", "qsa_select_topk", "qsa_sparse_attn_prefill", "qsa_sparse_attn_decode",
     "qsa_decode_step", "qsa_sparse_attn_backward", "qsa_index_build_backward",
-    "qsa_indexer_distill", "qsa_workspace_size", "qsa_status_string",
+    "qsa_indexer_distill", "qsa_offload_stage", "qsa_workspace_size", "qsa_status_string",
     "qsa_last_error", "qsa_abi_version",
 )
 
@@ -93,6 +93,8 @@ def load(path: str | None = None):
                                      P, P, SZ, P],
         "qsa_index_build_backward": [CFG, I32, P, I64, P, P, I32, P, P, P, P],
         "qsa_indexer_distill": [CFG, I32, I32, P, P, I64, P, I32, P, P, P, P, P, P, SZ, P],
+        "qsa_offload_stage": [CFG, I32, P, P, P, P, P, I64, P, P, P, I32, P, P, I64, P, P, P, P,
+                              P],
         "qsa_workspace_size": [CFG, I32, I32, I32, I32, ctypes.POINTER(SZ)],
     }
     for name, args in sig.items():
@@ -220,3 +222,15 @@ def qsa_indexer_distill(cfg, batch, n_q, q, k_cache, cap_tokens, q_pos0, max_pos
                                         cap_tokens, _ptr(q_pos0), max_pos_end, _ptr(q_idx),
                                         _ptr(k_cmp), _ptr(loss), _ptr(dq_idx), _ptr(dk_cmp),
                                         _ptr(workspace), workspace_bytes, _stream(stream)))
+
+
+def qsa_offload_stage(cfg, batch, q_pos, sel_blocks, sel_count, k_host, v_host, cap_tokens,
+                      hot_k, hot_v, hot_tag, hot_units, stage_k, stage_v, stage_tokens, stage_sel,
+                      stage_cnt, stage_pos, stats, stream=None) -> None:
+    lib = load()
+    _check(lib, lib.qsa_offload_stage(ctypes.byref(cfg), batch, _ptr(q_pos), _ptr(sel_blocks),
+                                      _ptr(sel_count), _ptr(k_host), _ptr(v_host), cap_tokens,
+                                      _ptr(hot_k), _ptr(hot_v), _ptr(hot_tag), hot_units,
+                                      _ptr(stage_k), _ptr(stage_v), stage_tokens, _ptr(stage_sel),
+                                      _ptr(stage_cnt), _ptr(stage_pos), _ptr(stats),
+                                      _stream(stream)))

@@ -1,0 +1,127 @@
+// Selection-driven host-offloaded KV for decode (qsa_offload_stage).
+//
+// "Qwen Sparse Attention" gallery page and the serving-port page: the full
+// KV history can stay in host memory while the GPU keeps a hot cache and a
+// staging area, fetching on demand only the blocks each step selects (every
+// layer selects independently).  The pages describe another party's port,
+// not an algorithm; taken here: the KV rows of every token live in pinned
+// host memory ([batch][cap][Hkv][d], read by the kernel over the host link);
+// the compressed index stays in HBM, so scoring and top-k run as usual; per
+// decode step this call gathers the query's token set -- the selected blocks
+// in ascending order, then the tail -- into a contiguous staging buffer in
+// HBM, reading each 4-token unit from a direct-mapped HBM hot cache when it
+// is there and from host memory otherwise, then promotes the missed units
+// into the hot cache.  It also writes the selection in staged coordinates
+// (blocks 0 .. count-1, the tail after them), so qsa_sparse_attn_decode on
+// the staging buffer attends over exactly the query's token set.
+#include "qsa_common.h"
+
+namespace qsa {
+namespace {
+
+constexpr int kOT = 256;
+constexpr int kClaim = 2048;   // promotion claims per step (a hash of the slot)
+
+// One workgroup per sequence (decode: one query each).  Waves take units in
+// turn; a unit's K (and V) rows are 4 x KD bf16 = 4 KD / 8 chunks of 16 B.
+__global__ __launch_bounds__(kOT) void offload_stage_kernel(
+    int kB, int lr, int KD, const int32_t* __restrict__ q_pos, const int32_t* __restrict__ sel,
+    const int32_t* __restrict__ cnt, const uint16_t* __restrict__ kh,
+    const uint16_t* __restrict__ vh, int64_t cap, uint16_t* __restrict__ hk,
+    uint16_t* __restrict__ hv, int32_t* __restrict__ htag, int hot_units,
+    uint16_t* __restrict__ sk, uint16_t* __restrict__ sv, int64_t stage_tokens,
+    int32_t* __restrict__ ssel, int32_t* __restrict__ scnt, int32_t* __restrict__ spos,
+    int32_t* __restrict__ stats) {
+  __shared__ int claim[kClaim];
+  __shared__ int n_hit, n_miss;
+  const int s = blockIdx.x;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t p = min(max((int64_t)q_pos[s], (int64_t)0), cap - 1);
+  const int64_t c = p >> lr;
+  const int count = (int)min((int64_t)max(cnt[s], 0), min((int64_t)kB, c));
+  const int lm = lr - 2;
+  const int nsel = count << lm;
+  const int npb = nsel + (int)((p - (c << lr)) >> 2) + 1;
+  const int32_t* srow = sel + (int64_t)s * kB;
+  auto unit = [&](int i) -> int64_t {
+    return i < nsel ? (min(max((int64_t)srow[i >> lm], (int64_t)0), c - 1) << lm) +
+                          (i & ((1 << lm) - 1))
+                    : (c << lm) + (i - nsel);
+  };
+  for (int i = threadIdx.x; i < kClaim; i += kOT) claim[i] = -1;
+  if (threadIdx.x == 0) n_hit = n_miss = 0;
+  __syncthreads();
+  const int CH = 4 * KD / 8;   // 16-byte chunks of one unit's K (or V) rows
+  int32_t* tags = htag + (int64_t)s * hot_units;
+  // ---- phase 1: every unit of the set into the staging buffer
+  for (int i = wave; i < npb; i += kOT / 64) {
+    const int64_t u = unit(i);
+    const int slot = (int)(u % hot_units);
+    const bool hit = tags[slot] == (int32_t)u;
+    uint16_t* dk = sk + ((int64_t)s * stage_tokens + 4 * (int64_t)i) * KD;
+    uint16_t* dv = sv + ((int64_t)s * stage_tokens + 4 * (int64_t)i) * KD;
+    for (int ch = lane; ch < CH; ch += 64) {
+      // token t of the unit; rows past the cache end (a last, partial unit:
+      // tokens after p, never attended) repeat the last row
+      const int t = ch / (KD / 8), e = ch % (KD / 8);
+      const int64_t src = hit ? (((int64_t)s * hot_units + slot) * 4 + t) * KD + 8 * e
+                              : ((int64_t)s * cap + min(4 * u + t, cap - 1)) * KD + 8 * e;
+      const u32x4 a = *reinterpret_cast<const u32x4*>((hit ? hk : kh) + src);
+      const u32x4 b = *reinterpret_cast<const u32x4*>((hit ? hv : vh) + src);
+      *reinterpret_cast<u32x4*>(dk + 8 * ch) = a;
+      *reinterpret_cast<u32x4*>(dv + 8 * ch) = b;
+    }
+    if (lane == 0) atomicAdd(hit ? &n_hit : &n_miss, 1);
+  }
+  __syncthreads();   // staging written; no unit reads the hot cache any more
+  // ---- phase 2: promote missed units (one per hash bucket of the slot)
+  for (int i = wave; i < npb; i += kOT / 64) {
+    const int64_t u = unit(i);
+    const int slot = (int)(u % hot_units);
+    if (tags[slot] == (int32_t)u) continue;          // was a hit
+    int owner = 0;
+    if (lane == 0) owner = atomicCAS(&claim[slot & (kClaim - 1)], -1, slot) == -1;
+    owner = __shfl(owner, 0);
+    if (!owner) continue;                            // the bucket went to another unit
+    const uint16_t* srck = sk + ((int64_t)s * stage_tokens + 4 * (int64_t)i) * KD;
+    const uint16_t* srcv = sv + ((int64_t)s * stage_tokens + 4 * (int64_t)i) * KD;
+    uint16_t* dk = hk + ((int64_t)s * hot_units + slot) * 4 * KD;
+    uint16_t* dv = hv + ((int64_t)s * hot_units + slot) * 4 * KD;
+    for (int ch = lane; ch < CH; ch += 64) {
+      *reinterpret_cast<u32x4*>(dk + 8 * ch) = *reinterpret_cast<const u32x4*>(srck + 8 * ch);
+      *reinterpret_cast<u32x4*>(dv + 8 * ch) = *reinterpret_cast<const u32x4*>(srcv + 8 * ch);
+    }
+    if (lane == 0) tags[slot] = (int32_t)u;           // read by later calls only
+  }
+  // ---- the selection in staged coordinates
+  for (int k = threadIdx.x; k < kB; k += kOT) ssel[(int64_t)s * kB + k] = k < count ? k : -1;
+  if (threadIdx.x == 0) {
+    scnt[s] = count;
+    spos[s] = (int32_t)(((int64_t)count << lr) + (p - (c << lr)));
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    stats[2 * s] = n_hit;
+    stats[2 * s + 1] = n_miss;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_offload_stage(const Dims& d, int batch, const int32_t* q_pos,
+                                const int32_t* sel, const int32_t* cnt, const void* k_host_dev,
+                                const void* v_host_dev, int64_t cap, void* hot_k, void* hot_v,
+                                int32_t* hot_tag, int hot_units, void* stage_k, void* stage_v,
+                                int64_t stage_tokens, int32_t* stage_sel, int32_t* stage_cnt,
+                                int32_t* stage_pos, int32_t* stats, hipStream_t st) {
+  hipLaunchKernelGGL(offload_stage_kernel, dim3((unsigned)batch), dim3(kOT), 0, st, d.kB, d.lr,
+                     d.kv_heads * d.head_dim, q_pos, sel, cnt,
+                     static_cast<const uint16_t*>(k_host_dev),
+                     static_cast<const uint16_t*>(v_host_dev), cap,
+                     static_cast<uint16_t*>(hot_k), static_cast<uint16_t*>(hot_v), hot_tag,
+                     hot_units, static_cast<uint16_t*>(stage_k), static_cast<uint16_t*>(stage_v),
+                     stage_tokens, stage_sel, stage_cnt, stage_pos, stats);
+  return hipGetLastError();
+}
+
+}  // namespace qsa

@@ -425,4 +425,55 @@ qsa_status qsa_indexer_distill(const qsa_config* cfg, int32_t batch, int32_t n_q
                                           workspace, stream));
 }
 
+qsa_status qsa_offload_stage(const qsa_config* cfg, int32_t batch, const int32_t* q_pos,
+                             const int32_t* sel_blocks, const int32_t* sel_count,
+                             const void* k_host, const void* v_host, int64_t cap_tokens,
+                             void* hot_k, void* hot_v, int32_t* hot_tag, int32_t hot_units,
+                             void* stage_k, void* stage_v, int64_t stage_tokens,
+                             int32_t* stage_sel, int32_t* stage_cnt, int32_t* stage_pos,
+                             int32_t* stats, hipStream_t stream) {
+  const char* fn = "qsa_offload_stage";
+  qsa::Dims d;
+  qsa_status st = check_config(fn, cfg, &d);
+  if (st != QSA_OK) return st;
+  if (!d.bf16) return fail(QSA_ERR_UNSUPPORTED, "%s: bf16 caches only", fn);
+  if (batch <= 0 || batch > 65535)
+    return fail(QSA_ERR_INVALID_ARGUMENT, "%s: batch must be in [1, 65535]", fn);
+  if (cap_tokens < d.r || cap_tokens > INT32_MAX)
+    return fail(QSA_ERR_INVALID_ARGUMENT, "%s: cap_tokens must be in [block_size, 2^31)", fn);
+  if (hot_units <= 0) return fail(QSA_ERR_INVALID_ARGUMENT, "%s: hot_units must be > 0", fn);
+  if (stage_tokens < (int64_t)(d.kB + 1) * d.r)
+    return fail(QSA_ERR_INVALID_ARGUMENT, "%s: stage_tokens %lld < (k_B + 1) * block_size = %lld",
+                fn, (long long)stage_tokens, (long long)(d.kB + 1) * d.r);
+  if ((d.kv_heads * d.head_dim) % 8 != 0)
+    return fail(QSA_ERR_UNSUPPORTED, "%s: kv_heads * head_dim must be a multiple of 8", fn);
+  QSA_REQUIRE_PTR(q_pos, 4);
+  QSA_REQUIRE_PTR(sel_blocks, 4);
+  QSA_REQUIRE_PTR(sel_count, 4);
+  QSA_REQUIRE_PTR(k_host, 16);
+  QSA_REQUIRE_PTR(v_host, 16);
+  QSA_REQUIRE_PTR(hot_k, 16);
+  QSA_REQUIRE_PTR(hot_v, 16);
+  QSA_REQUIRE_PTR(hot_tag, 4);
+  QSA_REQUIRE_PTR(stage_k, 16);
+  QSA_REQUIRE_PTR(stage_v, 16);
+  QSA_REQUIRE_PTR(stage_sel, 4);
+  QSA_REQUIRE_PTR(stage_cnt, 4);
+  QSA_REQUIRE_PTR(stage_pos, 4);
+  QSA_REQUIRE_PTR(stats, 4);
+  // the host caches must be pinned, device-mapped host memory
+  void* kd = nullptr;
+  void* vd = nullptr;
+  if (hipHostGetDevicePointer(&kd, const_cast<void*>(k_host), 0) != hipSuccess || !kd ||
+      hipHostGetDevicePointer(&vd, const_cast<void*>(v_host), 0) != hipSuccess || !vd) {
+    (void)hipGetLastError();
+    return fail(QSA_ERR_INVALID_ARGUMENT,
+                "%s: k_host / v_host must be pinned host memory (hipHostMalloc)", fn);
+  }
+  return launched(fn, qsa::launch_offload_stage(d, batch, q_pos, sel_blocks, sel_count, kd, vd,
+                                                cap_tokens, hot_k, hot_v, hot_tag, hot_units,
+                                                stage_k, stage_v, stage_tokens, stage_sel,
+                                                stage_cnt, stage_pos, stats, stream));
+}
+
 }  // extern "C"

@@ -255,6 +255,12 @@ hipError_t launch_decode_step(const Dims& d, const StepPlan& pl, int batch, cons
 size_t attn_workspace_bytes(const Dims& d, int rows, bool decode);
 
 // Attention backward: transposed index (per-block query lists) and per-head D.
+hipError_t launch_offload_stage(const Dims& d, int batch, const int32_t* q_pos,
+                                const int32_t* sel, const int32_t* cnt, const void* k_host_dev,
+                                const void* v_host_dev, int64_t cap, void* hot_k, void* hot_v,
+                                int32_t* hot_tag, int hot_units, void* stage_k, void* stage_v,
+                                int64_t stage_tokens, int32_t* stage_sel, int32_t* stage_cnt,
+                                int32_t* stage_pos, int32_t* stats, hipStream_t st);
 size_t distill_workspace_bytes(const Dims& d, int batch, int n_q, int32_t max_pos_end);
 hipError_t launch_distill(const Dims& d, int batch, int n_q, const void* q, const void* k_cache,
                           int64_t cap, const int32_t* q_pos0, int32_t max_pos_end,

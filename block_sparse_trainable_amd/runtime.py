@@ -290,3 +290,55 @@ class DeviceLayer:
         B.qsa_sparse_attn_decode(self.cfg, nb, q_s[t, a:b], self.k[a:b], self.v[a:b], self.cap,
                                  pos_t[t, a:b], int(max_pos_end), sel[a:b], cnt[a:b], out[a:b],
                                  lse[a:b], wdec, wdec.numel())
+
+
+class OffloadedKV:
+    """Decode with a layer's KV history in pinned host memory: a hot cache of
+    `hot_units` 4-token units per sequence and a staging buffer in GPU
+    memory, filled per step by qsa_offload_stage (plumbing only)."""
+
+    def __init__(self, dl: "DeviceLayer", hot_units: int):
+        lay = dl.layout
+        self.dl = dl
+        self.hot_units = int(hot_units)
+        # pinned host copies of the caches (the history the GPU no longer holds)
+        self.k_host = torch.empty(dl.k.shape, dtype=dl.k.dtype, pin_memory=True)
+        self.v_host = torch.empty(dl.v.shape, dtype=dl.v.dtype, pin_memory=True)
+        self.k_host.copy_(dl.k.cpu())
+        self.v_host.copy_(dl.v.cpu())
+        kd = (lay.kv_heads, lay.head_dim)
+        self.hot_k = torch.zeros((dl.batch, self.hot_units, 4) + kd, dtype=dl.k.dtype,
+                                 device=dl.device)
+        self.hot_v = torch.zeros_like(self.hot_k)
+        self.hot_tag = torch.full((dl.batch, self.hot_units), -1, dtype=torch.int32,
+                                  device=dl.device)
+        self.stage_tokens = (dl.kB + 1) * lay.block_size
+        self.stage_k = torch.zeros((dl.batch, self.stage_tokens) + kd, dtype=dl.k.dtype,
+                                   device=dl.device)
+        self.stage_v = torch.zeros_like(self.stage_k)
+        self.stage_sel = torch.empty((dl.batch, dl.kB), dtype=torch.int32, device=dl.device)
+        self.stage_cnt = torch.empty((dl.batch,), dtype=torch.int32, device=dl.device)
+        self.stage_pos = torch.empty((dl.batch,), dtype=torch.int32, device=dl.device)
+        self.stats = torch.zeros((dl.batch, 2), dtype=torch.int32, device=dl.device)
+
+    def stage(self, q_pos, sel, cnt) -> None:
+        dl = self.dl
+        B.qsa_offload_stage(dl.cfg, dl.batch, q_pos, sel, cnt, self.k_host.data_ptr(),
+                            self.v_host.data_ptr(), dl.cap, self.hot_k, self.hot_v, self.hot_tag,
+                            self.hot_units, self.stage_k, self.stage_v, self.stage_tokens,
+                            self.stage_sel, self.stage_cnt, self.stage_pos, self.stats)
+
+    def decode_step(self, plan, t: int, outputs):
+        """index build + select on the GPU-resident index, staging, attention
+        over the staging buffer."""
+        dl = self.dl
+        q_idx_s, q_s, pos_t, pos1_t, max_pos_end = plan
+        sel, cnt, scs, out, lse = outputs
+        dl.index_build(pos_t[t], pos1_t[t], 1)
+        dl.select(q_idx_s[t].unsqueeze(1), pos_t[t], max_pos_end, sel, cnt, scs, n_q=1)
+        self.stage(pos_t[t], sel[:, 0], cnt[:, 0])
+        ws = dl.workspace(B.QSA_OP_DECODE, dl.batch, 1, self.stage_tokens)
+        B.qsa_sparse_attn_decode(dl.cfg, dl.batch, q_s[t], self.stage_k, self.stage_v,
+                                 self.stage_tokens, self.stage_pos, self.stage_tokens,
+                                 self.stage_sel, self.stage_cnt, out, lse, ws, ws.numel())
+        return outputs

@@ -349,6 +349,46 @@ qsa_status qsa_indexer_distill(const qsa_config* cfg, int32_t batch, int32_t n_q
                                float* loss, float* dq_idx, float* dk_cmp, void* workspace,
                                size_t workspace_bytes, hipStream_t stream);
 
+/* qsa_offload_stage -- decode with the KV history in host memory.
+ * The pages describe a serving port that keeps the full history in host
+ * memory with a hot cache and a staging area in GPU memory, fetching the
+ * blocks each step selects ([gallery] Where QSA sits; the port page).
+ * Taken here: for each sequence's decode query at q_pos[s], with the
+ * selection of qsa_select_topk (made on the compressed index, which stays in
+ * GPU memory), gathers the query's token set -- the selected blocks in
+ * ascending order, then the tail -- into stage_k / stage_v, 4-token unit by
+ * unit: from the hot cache when the unit's slot (unit id mod hot_units)
+ * holds it, else from host memory; then writes the missed units into their
+ * slots (one per slot when several miss to it).  It also writes the
+ * selection in staging coordinates, so that
+ *     qsa_sparse_attn_decode(cfg, batch, q, stage_k, stage_v, stage_tokens,
+ *                            stage_pos, stage_tokens, stage_sel, stage_cnt, ...)
+ * attends over exactly the query's token set (in another order: equal up to
+ * the rounding of the softmax sums).
+ *
+ *   q_pos, sel_blocks, sel_count  as for qsa_sparse_attn_decode.
+ *   k_host, v_host  bf16 [batch][cap_tokens][kv_heads][head_dim] in pinned,
+ *              device-mapped host memory (hipHostMalloc); read only.
+ *   hot_k, hot_v    bf16 [batch][hot_units][4][kv_heads][head_dim] GPU memory.
+ *   hot_tag    int32 [batch][hot_units]: the unit each slot holds, -1 for
+ *              none; the caller fills it with -1 once; every call keeps it
+ *              consistent with hot_k / hot_v.
+ *   stage_k, stage_v  bf16 [batch][stage_tokens][kv_heads][head_dim] GPU
+ *              memory, stage_tokens >= (k_B + 1) * block_size.
+ *   stage_sel int32 [batch][k_B], stage_cnt int32 [batch],
+ *   stage_pos int32 [batch]: written (blocks 0 .. count-1, -1 padding; the
+ *              query's position in the staging buffer).
+ *   stats      int32 [batch][2]: units read from the hot cache, from host.
+ * Calls on one stream are ordered; concurrent calls must not share a hot
+ * cache.                                                                  */
+qsa_status qsa_offload_stage(const qsa_config* cfg, int32_t batch, const int32_t* q_pos,
+                             const int32_t* sel_blocks, const int32_t* sel_count,
+                             const void* k_host, const void* v_host, int64_t cap_tokens,
+                             void* hot_k, void* hot_v, int32_t* hot_tag, int32_t hot_units,
+                             void* stage_k, void* stage_v, int64_t stage_tokens,
+                             int32_t* stage_sel, int32_t* stage_cnt, int32_t* stage_pos,
+                             int32_t* stats, hipStream_t stream);
+
 int32_t qsa_abi_version(void);     /* 1 */
 
 #ifdef __cplusplus

@@ -288,3 +288,20 @@ def test_backward_validation_and_workspace(lib):
     with pytest.raises(B.QsaError) as e:              # workspace too small
         qsa.qsa_sparse_attn_backward(c, 1, 16, *args[:-1], 64, stream=0)
     assert e.value.status == B.QSA_ERR_WORKSPACE
+
+
+def test_offload_stage_validation(lib):
+    c = cfg(token_budget=256)                           # k_B = 64: staging needs 65 * 4 tokens
+    args = [FAKE, FAKE, FAKE, FAKE, FAKE, 1024, FAKE, FAKE, FAKE, 128, FAKE, FAKE]
+    with pytest.raises(B.QsaError) as e:
+        qsa.qsa_offload_stage(c, 2, *args, 259, FAKE, FAKE, FAKE, FAKE, stream=0)
+    assert e.value.status == B.QSA_ERR_INVALID_ARGUMENT and "stage_tokens" in str(e.value)
+    with pytest.raises(B.QsaError) as e:
+        qsa.qsa_offload_stage(cfg(token_budget=256, dtype=B.QSA_F32), 2, *args, 260, FAKE, FAKE,
+                              FAKE, FAKE, stream=0)
+    assert e.value.status == B.QSA_ERR_UNSUPPORTED and "bf16" in str(e.value)
+    with pytest.raises(B.QsaError) as e:                # hot_units
+        bad = list(args)
+        bad[9] = 0
+        qsa.qsa_offload_stage(c, 2, *bad, 260, FAKE, FAKE, FAKE, FAKE, stream=0)
+    assert e.value.status == B.QSA_ERR_INVALID_ARGUMENT and "hot_units" in str(e.value)
