@@ -93,6 +93,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--backward", action=argparse.BooleanOptionalAction, default=True,
                     help="also time the sparse attention backward on the prefill workload")
+    ap.add_argument("--offload", action=argparse.BooleanOptionalAction, default=True,
+                    help="also time decode with the KV history in pinned host memory")
     ap.add_argument("--distill", action=argparse.BooleanOptionalAction, default=True,
                     help="also time the stage-1 indexer distillation on the prefill workload")
     ap.add_argument("--cpu-rows", type=int, default=2304,
@@ -420,9 +422,46 @@ def bench_decode(args, torch):
            "hbm_frac": (scan_bytes + gather) / (graph_us * 1e-6) / (HBM_PEAK_GBS * 1e9),
            "cold_4_replicas_us_per_step": cold_us,
            "cold_hbm_frac": (scan_bytes + gather) / (cold_us * 1e-6) / (HBM_PEAK_GBS * 1e9)}
+    if args.offload:
+        res["offload"] = bench_offload(args, torch, x, dl, plan, steps)
     del dl, outs
     torch.cuda.empty_cache()
     return res
+
+
+def bench_offload(args, torch, x, dl, plan, steps):
+    """The same decode steps with the K/V history in pinned host memory:
+    index build + top-k on the GPU-resident index, staging of each step's
+    token set (hot cache of 65,536 4-token units per sequence, the rest from
+    host), attention over the staging buffer."""
+    from block_sparse_trainable_amd.runtime import OffloadedKV
+    off = OffloadedKV(dl, 65536)
+    outs = dl.alloc_decode_outputs()
+    for t in range(min(4, steps)):
+        off.decode_step(plan, t, outs)
+    torch.cuda.synchronize()
+    off.hot_tag.fill_(-1)
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+    recs = []
+    start, stop = ev(), ev()
+    start.record()
+    for t in range(steps):
+        off.decode_step(plan, t, outs)
+        st = off.stats.sum(0)
+        recs.append(st)
+    stop.record()
+    torch.cuda.synchronize()
+    us = start.elapsed_time(stop) * 1e3 / steps
+    tot = torch.stack(recs).sum(0).cpu().numpy()
+    hits, miss = int(tot[0]), int(tot[1])
+    unit_bytes = 4 * x.layout.kv_heads * x.layout.head_dim * 2 * 2   # K and V of 4 tokens
+    host_bytes = miss * unit_bytes / steps
+    log(f"decode offloaded: {us:.1f} us/step, hit rate {hits / max(1, hits + miss):.3f}")
+    del off
+    return {"us_per_step": us, "mode": "eager (index build, top-k, staging, attention)",
+            "hot_units_per_sequence": 65536, "hit_rate": hits / max(1, hits + miss),
+            "host_bytes_per_step": host_bytes,
+            "host_gbs": host_bytes / (us * 1e-6) / 1e9}
 
 
 def bench_stack_decode(args, torch):

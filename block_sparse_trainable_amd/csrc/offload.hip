@@ -21,40 +21,50 @@ namespace {
 
 constexpr int kOT = 256;
 constexpr int kClaim = 2048;   // promotion claims per step (a hash of the slot)
+constexpr int kGatherSplit = 32;   // gathering workgroups per sequence
+constexpr int kPT = 1024;          // threads of the promoting workgroup
 
-// One workgroup per sequence (decode: one query each).  Waves take units in
-// turn; a unit's K (and V) rows are 4 x KD bf16 = 4 KD / 8 chunks of 16 B.
-__global__ __launch_bounds__(kOT) void offload_stage_kernel(
-    int kB, int lr, int KD, const int32_t* __restrict__ q_pos, const int32_t* __restrict__ sel,
-    const int32_t* __restrict__ cnt, const uint16_t* __restrict__ kh,
-    const uint16_t* __restrict__ vh, int64_t cap, uint16_t* __restrict__ hk,
-    uint16_t* __restrict__ hv, int32_t* __restrict__ htag, int hot_units,
-    uint16_t* __restrict__ sk, uint16_t* __restrict__ sv, int64_t stage_tokens,
-    int32_t* __restrict__ ssel, int32_t* __restrict__ scnt, int32_t* __restrict__ spos,
-    int32_t* __restrict__ stats) {
-  __shared__ int claim[kClaim];
-  __shared__ int n_hit, n_miss;
-  const int s = blockIdx.x;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int64_t p = min(max((int64_t)q_pos[s], (int64_t)0), cap - 1);
-  const int64_t c = p >> lr;
-  const int count = (int)min((int64_t)max(cnt[s], 0), min((int64_t)kB, c));
-  const int lm = lr - 2;
-  const int nsel = count << lm;
-  const int npb = nsel + (int)((p - (c << lr)) >> 2) + 1;
-  const int32_t* srow = sel + (int64_t)s * kB;
-  auto unit = [&](int i) -> int64_t {
+// The query's token set in 4-token units: the selected blocks' units in
+// ascending order, then the tail's.
+struct UnitList {
+  const int32_t* srow;
+  int64_t p, c;
+  int count, lm, nsel, npb;
+  __device__ UnitList(const int32_t* sel, const int32_t* cnt, const int32_t* q_pos, int s, int kB,
+                      int lr, int64_t cap) {
+    p = min(max((int64_t)q_pos[s], (int64_t)0), cap - 1);
+    c = p >> lr;
+    count = (int)min((int64_t)max(cnt[s], 0), min((int64_t)kB, c));
+    lm = lr - 2;
+    nsel = count << lm;
+    npb = nsel + (int)((p - (c << lr)) >> 2) + 1;
+    srow = sel + (int64_t)s * kB;
+  }
+  __device__ int64_t operator()(int i) const {
     return i < nsel ? (min(max((int64_t)srow[i >> lm], (int64_t)0), c - 1) << lm) +
                           (i & ((1 << lm) - 1))
                     : (c << lm) + (i - nsel);
-  };
-  for (int i = threadIdx.x; i < kClaim; i += kOT) claim[i] = -1;
-  if (threadIdx.x == 0) n_hit = n_miss = 0;
-  __syncthreads();
+  }
+};
+
+// Gathering: kGatherSplit workgroups per sequence, each a contiguous share of
+// the units; a wave moves one unit at a time (4 x KD bf16 of K and of V, in
+// 16-byte chunks), from the hot cache when the unit's slot holds it, else
+// from host memory.  The hot cache is only read here.
+__global__ __launch_bounds__(kOT) void offload_gather_kernel(
+    int kB, int lr, int KD, const int32_t* __restrict__ q_pos, const int32_t* __restrict__ sel,
+    const int32_t* __restrict__ cnt, const uint16_t* __restrict__ kh,
+    const uint16_t* __restrict__ vh, int64_t cap, const uint16_t* __restrict__ hk,
+    const uint16_t* __restrict__ hv, const int32_t* __restrict__ htag, int hot_units,
+    uint16_t* __restrict__ sk, uint16_t* __restrict__ sv, int64_t stage_tokens) {
+  const int s = blockIdx.y;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const UnitList unit(sel, cnt, q_pos, s, kB, lr, cap);
+  const int per = (unit.npb + kGatherSplit - 1) / kGatherSplit;
+  const int i0 = blockIdx.x * per, i1 = min(i0 + per, unit.npb);
   const int CH = 4 * KD / 8;   // 16-byte chunks of one unit's K (or V) rows
-  int32_t* tags = htag + (int64_t)s * hot_units;
-  // ---- phase 1: every unit of the set into the staging buffer
-  for (int i = wave; i < npb; i += kOT / 64) {
+  const int32_t* tags = htag + (int64_t)s * hot_units;
+  for (int i = i0 + wave; i < i1; i += kOT / 64) {
     const int64_t u = unit(i);
     const int slot = (int)(u % hot_units);
     const bool hit = tags[slot] == (int32_t)u;
@@ -71,14 +81,43 @@ __global__ __launch_bounds__(kOT) void offload_stage_kernel(
       *reinterpret_cast<u32x4*>(dk + 8 * ch) = a;
       *reinterpret_cast<u32x4*>(dv + 8 * ch) = b;
     }
-    if (lane == 0) atomicAdd(hit ? &n_hit : &n_miss, 1);
   }
-  __syncthreads();   // staging written; no unit reads the hot cache any more
-  // ---- phase 2: promote missed units (one per hash bucket of the slot)
-  for (int i = wave; i < npb; i += kOT / 64) {
+}
+
+// Promotion, one workgroup per sequence, after the gathering: counts the hits
+// and misses against the tags the gathering saw, then writes each missed unit
+// from the staging buffer into its slot -- one unit per hash bucket of the
+// slot, so a slot gets data and tag from a single unit -- and writes the
+// selection in staging coordinates.
+__global__ __launch_bounds__(kPT) void offload_promote_kernel(
+    int kB, int lr, int KD, const int32_t* __restrict__ q_pos, const int32_t* __restrict__ sel,
+    const int32_t* __restrict__ cnt, int64_t cap, uint16_t* __restrict__ hk,
+    uint16_t* __restrict__ hv, int32_t* __restrict__ htag, int hot_units,
+    const uint16_t* __restrict__ sk, const uint16_t* __restrict__ sv, int64_t stage_tokens,
+    int32_t* __restrict__ ssel, int32_t* __restrict__ scnt, int32_t* __restrict__ spos,
+    int32_t* __restrict__ stats) {
+  __shared__ int claim[kClaim];
+  __shared__ int n_hit, n_miss;
+  const int s = blockIdx.x;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const UnitList unit(sel, cnt, q_pos, s, kB, lr, cap);
+  for (int i = threadIdx.x; i < kClaim; i += kPT) claim[i] = -1;
+  if (threadIdx.x == 0) n_hit = n_miss = 0;
+  __syncthreads();
+  int32_t* tags = htag + (int64_t)s * hot_units;
+  int h = 0, m = 0;
+  for (int i = threadIdx.x; i < unit.npb; i += kPT) {
+    const int64_t u = unit(i);
+    if (tags[u % hot_units] == (int32_t)u) ++h; else ++m;
+  }
+  atomicAdd(&n_hit, h);
+  atomicAdd(&n_miss, m);
+  __syncthreads();   // every tag read before any is rewritten
+  const int CH = 4 * KD / 8;
+  for (int i = wave; i < unit.npb; i += kPT / 64) {
     const int64_t u = unit(i);
     const int slot = (int)(u % hot_units);
-    if (tags[slot] == (int32_t)u) continue;          // was a hit
+    if (tags[slot] == (int32_t)u) continue;          // a hit (or already promoted)
     int owner = 0;
     if (lane == 0) owner = atomicCAS(&claim[slot & (kClaim - 1)], -1, slot) == -1;
     owner = __shfl(owner, 0);
@@ -93,14 +132,10 @@ __global__ __launch_bounds__(kOT) void offload_stage_kernel(
     }
     if (lane == 0) tags[slot] = (int32_t)u;           // read by later calls only
   }
-  // ---- the selection in staged coordinates
-  for (int k = threadIdx.x; k < kB; k += kOT) ssel[(int64_t)s * kB + k] = k < count ? k : -1;
+  for (int k = threadIdx.x; k < kB; k += kPT) ssel[(int64_t)s * kB + k] = k < unit.count ? k : -1;
   if (threadIdx.x == 0) {
-    scnt[s] = count;
-    spos[s] = (int32_t)(((int64_t)count << lr) + (p - (c << lr)));
-  }
-  __syncthreads();
-  if (threadIdx.x == 0) {
+    scnt[s] = unit.count;
+    spos[s] = (int32_t)(((int64_t)unit.count << lr) + (unit.p - (unit.c << lr)));
     stats[2 * s] = n_hit;
     stats[2 * s + 1] = n_miss;
   }
@@ -114,12 +149,17 @@ hipError_t launch_offload_stage(const Dims& d, int batch, const int32_t* q_pos,
                                 int32_t* hot_tag, int hot_units, void* stage_k, void* stage_v,
                                 int64_t stage_tokens, int32_t* stage_sel, int32_t* stage_cnt,
                                 int32_t* stage_pos, int32_t* stats, hipStream_t st) {
-  hipLaunchKernelGGL(offload_stage_kernel, dim3((unsigned)batch), dim3(kOT), 0, st, d.kB, d.lr,
-                     d.kv_heads * d.head_dim, q_pos, sel, cnt,
-                     static_cast<const uint16_t*>(k_host_dev),
+  const int KD = d.kv_heads * d.head_dim;
+  hipLaunchKernelGGL(offload_gather_kernel, dim3(kGatherSplit, (unsigned)batch), dim3(kOT), 0, st,
+                     d.kB, d.lr, KD, q_pos, sel, cnt, static_cast<const uint16_t*>(k_host_dev),
                      static_cast<const uint16_t*>(v_host_dev), cap,
-                     static_cast<uint16_t*>(hot_k), static_cast<uint16_t*>(hot_v), hot_tag,
-                     hot_units, static_cast<uint16_t*>(stage_k), static_cast<uint16_t*>(stage_v),
+                     static_cast<const uint16_t*>(hot_k), static_cast<const uint16_t*>(hot_v),
+                     hot_tag, hot_units, static_cast<uint16_t*>(stage_k),
+                     static_cast<uint16_t*>(stage_v), stage_tokens);
+  hipLaunchKernelGGL(offload_promote_kernel, dim3((unsigned)batch), dim3(kPT), 0, st, d.kB, d.lr,
+                     KD, q_pos, sel, cnt, cap, static_cast<uint16_t*>(hot_k),
+                     static_cast<uint16_t*>(hot_v), hot_tag, hot_units,
+                     static_cast<const uint16_t*>(stage_k), static_cast<const uint16_t*>(stage_v),
                      stage_tokens, stage_sel, stage_cnt, stage_pos, stats);
   return hipGetLastError();
 }
