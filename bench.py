@@ -271,7 +271,10 @@ def bench_backward(args, torch, x, dl, outs, q_pos0, max_pos_end):
     }
     tot = sum(parts.values())
     log(f"backward {ms:.3f} ms/call, {entries} group entries")
+    cpu = None if args.no_cpu_baseline else cpu_baseline_backward(
+        x, sel.cpu().numpy(), cnt.cpu().numpy(), dout.float().cpu().numpy(), 96)
     return {"ms_per_call": ms, "tok_s": rows / (ms / 1e3), "token_visits": visits,
+            "cpu_baseline": cpu,
             "group_entries": entries, "algorithmic_bytes": parts,
             "achieved_gbs": tot / (ms * 1e-3) / 1e9,
             "hbm_frac": tot / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
@@ -311,7 +314,9 @@ def bench_distill(args, torch, x, dl, q_pos0, max_pos_end):
     teacher = visits * per_tok + cand * r * per_tok     # pass 1 over 0..p, pass 2 over candidates
     student = cand * 2 * lay.idx_heads * lay.idx_dim * 4   # dots twice, dq_idx, dk_cmp
     log(f"distill {ms:.3f} ms/call")
+    cpu = None if args.no_cpu_baseline else cpu_baseline_distill(x, 8)
     return {"ms_per_call": ms, "rows_per_s": x.batch * x.n_q / (ms / 1e3),
+            "cpu_baseline": cpu,
             "teacher_token_visits": visits, "candidate_pairs": cand,
             "flops": {"teacher": teacher, "student": student},
             "mfma_frac": (teacher + student) / (ms * 1e-3) / (BF16_MFMA_PEAK_TFLOPS * 1e12),
@@ -580,6 +585,78 @@ def cpu_baseline(x, rows: int):
                        f"compression of the chunk's new blocks, single thread; extrapolated "
                        f"to the full chunk"),
             "measured_s": t_comp + t_rows}
+
+
+def _sample_rows(x, rows, seed):
+    rng = np.random.default_rng(seed)
+    per = max(1, rows // x.batch)
+    return [(s, int(j)) for s in range(x.batch)
+            for j in rng.choice(x.n_q, size=min(per, x.n_q), replace=False)]
+
+
+def cpu_baseline_backward(x, sel, cnt, dout, rows: int):
+    """The oracle's attention backward on a seeded sample of query rows (the
+    GPU's selections), single-threaded; extrapolated to every row."""
+    from threadpoolctl import threadpool_limits
+    from oracle import qsa_oracle as O
+    from block_sparse_trainable_amd import synth
+    lay = x.layout
+    f64 = lambda a: synth.as_f32(a, lay.dtype).astype(np.float64)
+    scale = 1.0 / math.sqrt(lay.head_dim)
+    sample = _sample_rows(x, rows, 11)
+    t_rows = 0.0
+    with threadpool_limits(limits=1):
+        for s in range(x.batch):
+            K, V, q = f64(x.k[s]), f64(x.v[s]), f64(x.q[s])
+            dK = np.zeros_like(K)
+            dV = np.zeros_like(V)
+            for (ss, j) in sample:
+                if ss != s:
+                    continue
+                p = int(x.q_pos0[s]) + j
+                S = O.expand_with_tail(np.sort(sel[s, j, :int(cnt[s, j])]), p, lay.block_size)
+                t = time.perf_counter()
+                O.sparse_attention_backward(q[j], K, V, S, dout[s, j], scale, dK, dV)
+                t_rows += time.perf_counter() - t
+    total = x.batch * x.n_q
+    return {"value": len(sample) / t_rows, "unit": "query rows/s", "cores": 1, "kind": "oracle",
+            "sample": f"{len(sample)} of {total} query rows (uniform seeded sample), single "
+                      f"thread, on the GPU's selections", "measured_s": t_rows}
+
+
+def cpu_baseline_distill(x, rows: int):
+    """The oracle's distillation (dense teacher target, KL, gradients) on a
+    seeded sample of query rows, single-threaded; extrapolated."""
+    from threadpoolctl import threadpool_limits
+    from oracle import qsa_oracle as O
+    from block_sparse_trainable_amd import synth
+    lay = x.layout
+    f64 = lambda a: synth.as_f32(a, lay.dtype).astype(np.float64)
+    scale = 1.0 / math.sqrt(lay.head_dim)
+    r = lay.block_size
+    sample = _sample_rows(x, rows, 12)
+    t_rows = 0.0
+    with threadpool_limits(limits=1):
+        for s in range(x.batch):
+            end = int(x.q_pos0[s]) + x.n_q
+            kh = O.compress_index(f64(x.k_idx[s, :(end // r) * r]), end // r, r=r,
+                                  gain=x.gain.astype(np.float64),
+                                  eps=float(np.float32(lay.rms_eps)), storage=lay.dtype)
+            K, q, qi = f64(x.k[s]), f64(x.q[s]), f64(x.q_idx[s])
+            for (ss, j) in sample:
+                if ss != s:
+                    continue
+                p = int(x.q_pos0[s]) + j
+                t = time.perf_counter()
+                tb = O.teacher_block_target(q[j], K, p, r, scale)
+                I = O.block_importance(qi[j], kh, p // r)
+                _, dI = O.distill_row(tb, I)
+                O.distill_grads(qi[j], kh, dI)
+                t_rows += time.perf_counter() - t
+    total = x.batch * x.n_q
+    return {"value": len(sample) / t_rows, "unit": "query rows/s", "cores": 1, "kind": "oracle",
+            "sample": f"{len(sample)} of {total} query rows (uniform seeded sample), single "
+                      f"thread", "measured_s": t_rows}
 
 
 def main():
