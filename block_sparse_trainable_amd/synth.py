@@ -6,8 +6,8 @@ random numbers, rounds those draws to the storage dtype, and plants the
 structure (needle blocks, positional locality) that the workloads describe.
 Both sides receive the exact same arrays.
 
-Workloads (sizes follow the five layer configurations of the task; the
-planted-structure recipes are this project's readings):
+Workloads (the sizes of the five layer configurations measured here; the
+planted structure is a reading of the pages' workloads):
 
 * ``tiny``      -- fp32, 1 x 256 tokens, 4Q/1KV heads, d=64, K=64 (k_B=16).
 * ``prefill``   -- bf16, 1 x 32,768 tokens, 16Q/2KV, d=128, K=2048.

@@ -45,7 +45,7 @@ extern "C" {
 typedef enum {
   QSA_OK = 0,
   QSA_ERR_INVALID_ARGUMENT = 1, /* null pointer, bad size, misalignment    */
-  QSA_ERR_UNSUPPORTED = 2,      /* a setting this build does not implement */
+  QSA_ERR_UNSUPPORTED = 2,      /* a setting the library does not implement */
   QSA_ERR_WORKSPACE = 3,        /* workspace missing or too small          */
   QSA_ERR_DEVICE = 4            /* HIP reported an error at launch         */
 } qsa_status;

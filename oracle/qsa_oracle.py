@@ -26,7 +26,7 @@ plain NumPy fp64, one query row at a time.  Sources:
     positions plus the current incomplete block); the QSA-vs-DSA table (the
     current incomplete block is included directly).
 
-Readings where the pages are silent (each is listed in the design doc):
+Readings where the pages are silent:
   * k_hat_b and k_bar_b are one vector: AvgPool -> RMSNorm -> partial RoPE.
   * RMSNorm(x) = x / sqrt(mean(x^2) + eps) * g, over all idx_dim dims.
   * RoPE rotates dims [0, rope_dims) in rotate-half pairs (j, j + rope_dims/2)
