@@ -107,3 +107,34 @@ def test_offloaded_decode_matches_resident(r, hot_units, steps):
             u = int(tags[s, slot])
             assert u % hot_units == slot
             assert torch.equal(hk[s, slot], off.k_host[s, 4 * u:4 * u + 4])
+
+
+def test_offloaded_decode_graph_replays():
+    """The offloaded steps captured in one HIP graph (the hot cache emptied by
+    a fill kernel at its start) replay bit for bit as the eager run, with
+    eager work between the replays."""
+    say("offloaded decode: 4 steps in a graph, 3 replays vs eager")
+    x = synth.decode(context=30000, batch=2, steps=4, n_needles=8)
+    dl = DeviceLayer(x)
+    dl.build_prefix(x.cache_len)
+    plan = dl.decode_plan(4)
+    off = OffloadedKV(dl, 2048)
+    outs = dl.alloc_decode_outputs()
+    off.hot_tag.fill_(-1)
+    eager = []
+    for t in range(4):
+        off.decode_step(plan, t, outs)
+        eager.append((outs[3].clone(), outs[4].clone(), off.stats.clone()))
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        off.hot_tag.fill_(-1)
+        for t in range(4):
+            off.decode_step(plan, t, outs)
+    for rep in range(3):
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(outs[3], eager[-1][0]) and torch.equal(outs[4], eager[-1][1])
+        assert torch.equal(off.stats, eager[-1][2])
+        dl.decode_step(plan, rep, dl.alloc_decode_outputs())   # eager work between replays
+        torch.cuda.synchronize()
