@@ -474,11 +474,13 @@ __global__ __launch_bounds__(kDT) void distill_student_kernel(
 // tiles of 16.  Dots: C[block][column] = k_tile * q_idx^T
 // (v_mfma_f32_16x16x32_bf16 over the 128 dims), so lane (column, gq) holds
 // blocks 4gq .. 4gq+3 of its head; the head sum (I) and the mask bits meet
-// across each lane quad.  Pass 1: the query's statistics (online logsumexp
-// of I, Z, sum t log t, sum t I).  Pass 2 recomputes the dots, forms dI and
-// W = dI [dot > 0] -- already the A-operand layout of a 16x16x16 MFMA over
-// blocks -- and accumulates dq_idx = W * k (k in 4-block groups, kT), with W
-// as bf16 hi + lo.  dI and the mask bytes go to the workspace for the key
+// across each lane quad, after which lane h of a quad takes the quad's block
+// h, so each (query, block) pair is one lane's work.  Pass 1: the query's
+// statistics (online logsumexp of I, Z, sum t log t, sum t I).  Pass 2
+// recomputes the dots, forms dI, gathers the quad's four dI back to every
+// lane and forms W = dI [dot > 0] -- the A-operand layout of a 16x16x16 MFMA
+// over blocks -- and accumulates dq_idx = W * k (k in 4-block groups, kT),
+// with W as bf16 hi + lo.  dI and the mask bytes go to the workspace for the key
 // side; q_idx is also written transposed (qT) for it.
 __device__ __forceinline__ float quad_xor1(float v) {
   return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false));
@@ -564,48 +566,61 @@ __global__ __launch_bounds__(256) void distill_student_mfma_kernel(
     for (int u = 1; u < m4; ++u) t = fmaxf(t, um[b * m4 + u]);
     return t;
   };
-  // ---- pass 1: statistics (lanes h == 0 count each (query, block) once)
-  float m = -INFINITY, l = 0.0f, z = 0.0f, a = 0.0f, bI = 0.0f;
-  for (int64_t b0 = 0; b0 < cmax; b0 += 16) {
-    f32x4 acc;
-    dots(b0, acc);
+  // After the head sum the 4 lanes of a quad hold the same I for the tile's
+  // blocks 4gq .. 4gq+3; lane h takes block 4gq + h, so each (query, block)
+  // pair is handled by one lane.
+  auto quad_sum4 = [&](const f32x4& acc, float (&Iq)[4]) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       float I = fmaxf(acc[i], 0.0f);
       I += quad_xor1(I);
       I += quad_xor2(I);
-      const int64_t b = b0 + 4 * gq + i;
-      if (h == 0 && b < c) {
-        const float mn = fmaxf(m, I);
-        l = l * exp2f((m - mn) * kLog2e) + exp2f((I - mn) * kLog2e);
-        m = mn;
-        const float t = target(b);
-        z += t;
-        if (t > 0.0f) a += t * logf(t);
-        bI += t * I;
-      }
+      Iq[i] = I;
+    }
+  };
+  auto pick = [&](const float (&v)[4]) {
+    return h == 0 ? v[0] : h == 1 ? v[1] : h == 2 ? v[2] : v[3];
+  };
+  // ---- pass 1: statistics
+  float m = -INFINITY, l = 0.0f, z = 0.0f, a = 0.0f, bI = 0.0f;
+  for (int64_t b0 = 0; b0 < cmax; b0 += 16) {
+    f32x4 acc;
+    dots(b0, acc);
+    float Iq[4];
+    quad_sum4(acc, Iq);
+    const float I = pick(Iq);
+    const int64_t b = b0 + 4 * gq + h;
+    if (b < c) {
+      const float mn = fmaxf(m, I);
+      l = l * exp2f((m - mn) * kLog2e) + exp2f((I - mn) * kLog2e);
+      m = mn;
+      const float t = target(b);
+      z += t;
+      if (t > 0.0f) a += t * logf(t);
+      bI += t * I;
     }
   }
-  // combine the four gq lanes of each (query, head 0) column, then share
-  // the query's figures with its quad
+  // combine the 16 lanes of each query (its quad, and the four gq rows)
   {
-    const float M = wave_max_xor32(wave_max_xor16(m));
+    float M = fmaxf(m, quad_xor1(m));
+    M = fmaxf(M, quad_xor2(M));
+    M = wave_max_xor32(wave_max_xor16(M));
     l = (m == -INFINITY) ? 0.0f : l * exp2f((m - M) * kLog2e);
     m = M;
   }
-  l = wave_add_xor32(wave_add_xor16(l));
-  z = wave_add_xor32(wave_add_xor16(z));
-  a = wave_add_xor32(wave_add_xor16(a));
-  bI = wave_add_xor32(wave_add_xor16(bI));
-  m = quad_first(m);
-  l = quad_first(l);
-  z = quad_first(z);
-  a = quad_first(a);
-  bI = quad_first(bI);
+  auto sum16 = [&](float v) {
+    v += quad_xor1(v);
+    v += quad_xor2(v);
+    return wave_add_xor32(wave_add_xor16(v));
+  };
+  l = sum16(l);
+  z = sum16(z);
+  a = sum16(a);
+  bI = sum16(bI);
   const float lseI = m + logf(l);
   if (valid && h == 0 && gq == 0) loss[row] = c > 0 ? a / z - logf(z) - bI / z + lseI : 0.0f;
   const float invZ = c > 0 ? 1.0f / z : 0.0f;
-  // ---- pass 2: dI, masks, dq_idx
+  // ---- pass 2: dI (one lane per pair), masks, dq_idx
   f32x4 dq[8];
 #pragma unroll
   for (int db = 0; db < 8; ++db) dq[db] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -613,28 +628,31 @@ __global__ __launch_bounds__(256) void distill_student_mfma_kernel(
   for (int64_t b0 = 0; b0 < cmax; b0 += 16) {
     f32x4 acc;
     dots(b0, acc);
-    float w[4], dIv[4];
-    uint32_t bits4 = 0;
+    float Iq[4], bitq[4];
+    quad_sum4(acc, Iq);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      float I = fmaxf(acc[i], 0.0f);
-      I += quad_xor1(I);
-      I += quad_xor2(I);
-      const int64_t b = b0 + 4 * gq + i;
-      const bool in = b < c;
-      dIv[i] = in ? exp2f((I - lseI) * kLog2e) - target(b) * invZ : 0.0f;
-      const bool on = acc[i] > 0.0f;
-      w[i] = on ? dIv[i] : 0.0f;
-      float bit = on ? (float)(1 << h) : 0.0f;
+    for (int i = 0; i < 4; ++i) {   // the heads' mask bits of block 4gq + i, on every lane
+      float bit = acc[i] > 0.0f ? (float)(1 << h) : 0.0f;
       bit += quad_xor1(bit);
       bit += quad_xor2(bit);
-      bits4 |= (uint32_t)bit << (8 * i);
+      bitq[i] = bit;
     }
-    if (valid && h == 0) {
-      const int64_t o = row * ws.W + b0 + 4 * gq;   // W is a multiple of 16
-      *reinterpret_cast<float4*>(ws.ib + o) = make_float4(dIv[0], dIv[1], dIv[2], dIv[3]);
-      *reinterpret_cast<uint32_t*>(ws.mk + o) = bits4;
+    const int64_t b = b0 + 4 * gq + h;
+    const float dI = b < c ? exp2f((pick(Iq) - lseI) * kLog2e) - target(b) * invZ : 0.0f;
+    if (valid) {
+      const int64_t o = row * ws.W + b;   // W is a multiple of 16
+      ws.ib[o] = dI;
+      ws.mk[o] = (uint8_t)pick(bitq);
     }
+    // this lane's head over the quad's four blocks: W = dI [dot > 0]
+    const float dIq[4] = {
+        __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(dI), 0x00, 0xF, 0xF, false)),
+        __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(dI), 0x55, 0xF, 0xF, false)),
+        __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(dI), 0xAA, 0xF, 0xF, false)),
+        __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(dI), 0xFF, 0xF, 0xF, false))};
+    float w[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) w[i] = acc[i] > 0.0f ? dIq[i] : 0.0f;
     bf16x4d whi, wlo;
     split4(w, whi, wlo);
     const uint16_t* kt = kT + ((b0 >> 2) + gq) * 512;
