@@ -190,9 +190,11 @@ __global__ __launch_bounds__(kDT) void distill_teacher_kernel(
 
 // ------------------------------------------------------------ teacher, MFMA --
 // bf16 layers with 16 query heads (the forward's MFMA shapes).  One workgroup
-// of 8 waves per 32 consecutive query rows of a sequence; each wave owns 4 of
-// them, i.e. 64 (query, head) columns = 4 MFMA column groups of 16: with Hkv
-// KV heads a group holds Hkv queries x 16/Hkv heads of one KV head.  The queries sit in
+// of 8 waves per 16 consecutive query rows of a sequence; each wave owns 2 of
+// them, i.e. 32 (query, head) columns = 2 MFMA column groups of 16: with Hkv
+// KV heads a group holds Hkv queries x 16/Hkv heads of one KV head.  (Fewer
+// queries per wave than 4 leave registers for two workgroups per CU, which
+// hides more of each tile's latency than the halved K reuse costs.)  The queries sit in
 // B-operand registers for the whole token loop; all eight waves share each
 // 32-token K tile, staged in LDS (swizzled as the backward's K tile) and read
 // as A operands: S^T = K_tile * Q per column group (v_mfma_f32_16x16x32_bf16).
@@ -212,7 +214,8 @@ __device__ __forceinline__ float swz_add(float v, int pattern_xor) {
   return v + __int_as_float(r);
 }
 
-constexpr int kTW = 8;   // waves per teacher workgroup
+constexpr int kTW = 8;    // waves per teacher workgroup
+constexpr int kTCG = 2;   // column groups (= query rows) per teacher wave
 
 template <int HKV, int D, int PASS>
 __global__ __launch_bounds__(64 * kTW) void distill_teacher_mfma_kernel(
@@ -223,24 +226,26 @@ __global__ __launch_bounds__(64 * kTW) void distill_teacher_mfma_kernel(
   constexpr int G = 16 / HKV;          // heads per KV head
   constexpr int QPC = HKV;             // queries per column group
   constexpr int NKD = D / 32;          // k-steps over one KV head's dims
-  constexpr int NCG = 4;               // column groups per wave
+  constexpr int NCG = kTCG;            // column groups (= queries) per wave
+  constexpr int QT = kTW * NCG;        // query rows per workgroup
+  static_assert(NCG % HKV == 0, "a wave's columns must cover every KV head of its queries");
   __shared__ __attribute__((aligned(16))) unsigned char kbuf[2][32 * ROWB];   // double-buffered
   constexpr int NL = (32 / RPI) / kTW;   // tile loads per lane
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int l16 = lane & 15, gq = lane >> 4;
-  const int tiles_per_seq = (n_q + 31) / 32;
+  const int tiles_per_seq = (n_q + QT - 1) / QT;
   const int s = blockIdx.x / tiles_per_seq;
-  const int j0 = (blockIdx.x % tiles_per_seq) * 32;
+  const int j0 = (blockIdx.x % tiles_per_seq) * QT;
   const int64_t pos0 = q_pos0[s];
   auto qpos = [&](int j) -> int64_t { return min(max(pos0 + j, (int64_t)0), cap - 1); };
   // token range of the tile
-  const int jl = min(j0 + 31, n_q - 1);
+  const int jl = min(j0 + QT - 1, n_q - 1);
   const int64_t pmax = qpos(jl);
   const int64_t tok_end = PASS == 1 ? pmax + 1 : ((pmax >> lr) << lr);
   if (tok_end <= 0) return;
   // this lane's column in group cg: query qcol(cg), head hcol(cg); rows
   // past n_q stand in for the last row and write nothing
-  auto qcol = [&](int cg) { return j0 + 4 * wave + (cg / HKV) * QPC + l16 / G; };
+  auto qcol = [&](int cg) { return j0 + NCG * wave + (cg / HKV) * QPC + l16 / G; };
   auto hcol = [&](int cg) { return (cg % HKV) * G + l16 % G; };
   int32_t pq[NCG];   // positions (cap < 2^31)
   u32x4 qb[NCG][NKD];
@@ -905,7 +910,7 @@ hipError_t launch_distill(const Dims& d, int batch, int n_q, const void* q, cons
   const bool mfma = d.bf16 && d.q_heads == 16 &&
                     ((d.kv_heads == 2 && (d.head_dim == 64 || d.head_dim == 128)) ||
                      (d.kv_heads == 1 && d.head_dim == 128));
-  const unsigned qtiles = (unsigned)(batch * ((n_q + 31) / 32));
+  const unsigned qtiles = (unsigned)(batch * ((n_q + kTW * kTCG - 1) / (kTW * kTCG)));
 #define QSA_TEACHER_MFMA(HKV, DD)                                                              \
   else if (d.kv_heads == HKV && d.head_dim == DD) {                                            \
     hipLaunchKernelGGL((distill_teacher_mfma_kernel<HKV, DD, 1>), dim3(qtiles), dim3(64 * kTW), 0, st, \
