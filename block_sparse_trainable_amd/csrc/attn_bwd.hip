@@ -31,6 +31,7 @@ namespace {
 
 constexpr int kBwdMaxTokens = 2048 + 128;   // r * k_B <= 2048 selected, tail <= r
 constexpr int kNT = 256;
+constexpr int kKeySplit = 2;   // key side: dim groups of waves (1, 2 or 4)
 constexpr int kKeyPF = 2;   // key side: the next entry's loads issued before this one is consumed
 
 template <bool BF16>
@@ -694,8 +695,9 @@ __device__ __forceinline__ bf16x4s pack4(uint32_t a, uint32_t b) {
   return __builtin_bit_cast(bf16x4s, make_uint2(a, b));
 }
 
-// One workgroup per (sequence, 16-token group); its waves take the group's
-// entries in turn.  Per entry, lane (token l16, heads 4gq .. 4gq+3) forms
+// One workgroup per (sequence, 16-token group); its waves, in kKeySplit
+// groups that each own a share of the Hkv*d dims, take the group's entries in
+// turn.  Per entry, lane (token l16, heads 4gq .. 4gq+3) forms
 // dS = P (dP - D~) - (D - D~) P and P from the query side's export, as
 // bf16 hi + lo A operands; the B operands are the row's transposed q / dO
 // (a 16-dim block, 4 heads per lane, zero where the head's KV group is not
@@ -710,6 +712,10 @@ __global__ __launch_bounds__(256, 2) void bwd_key_mfma_kernel(
     const float* __restrict__ dlt, int64_t cap, float scale, float* __restrict__ dk,
     float* __restrict__ dv) {
   constexpr int KD = HKV * D, NB = KD / 16, G = 16 / HKV;
+  // the dims are split over kKeySplit groups of waves: wave w takes the
+  // 16-dim blocks of part w % kKeySplit and every (4 / kKeySplit)-th entry
+  constexpr int NS = kKeySplit, NBW = NB / NS, STEP = 4 / NS;
+  static_assert(NBW % 2 == 0 && 4 % NS == 0, "dim split must leave pairs of blocks");
   // the group's list is staged here during the loop; the waves' dK / dV sums
   // meet here after it
   __shared__ __attribute__((aligned(16))) float sbuf[2 * 16 * KD];
@@ -730,9 +736,10 @@ __global__ __launch_bounds__(256, 2) void bwd_key_mfma_kernel(
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int l16 = lane & 15, gq = lane >> 4;
   const int u = l16 >> 2, t = l16 & 3;
-  f32x4 ak[NB], av[NB];
+  const int bbase = (wave % NS) * NBW;   // this wave's first 16-dim block
+  f32x4 ak[NBW], av[NBW];
 #pragma unroll
-  for (int b = 0; b < NB; ++b) ak[b] = av[b] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int b = 0; b < NBW; ++b) ak[b] = av[b] = f32x4{0.f, 0.f, 0.f, 0.f};
   const uint2* lst = glist + gx.off[item];
 
   // {P, weight} of the lane's token for heads 4gq .. 4gq+3, and D - D~
@@ -752,12 +759,13 @@ __global__ __launch_bounds__(256, 2) void bwd_key_mfma_kernel(
   // transposed q / dO of two 16-dim blocks, 4 heads per lane; lanes whose
   // heads are not the blocks' KV head read a neighbour's address (no extra
   // traffic) and are zeroed when consumed
-  auto fetch_q = [&](uint2 en, uint2 (&q4)[NB], uint2 (&d4)[NB]) {
+  auto fetch_q = [&](uint2 en, uint2 (&q4)[NBW], uint2 (&d4)[NBW]) {
     const int64_t row = en.x >> 4;
 #pragma unroll
-    for (int b = 0; b < NB; b += 2) {
-      const int grp = (16 * b) / D;
-      const int64_t o = qt_index<HKV, D>(row, grp, 16 * b - grp * D + l16, 4 * (gq % (G / 4)));
+    for (int b = 0; b < NBW; b += 2) {
+      const int grp = (16 * (bbase + b)) / D;
+      const int64_t o =
+          qt_index<HKV, D>(row, grp, 16 * (bbase + b) - grp * D + l16, 4 * (gq % (G / 4)));
       const u32x4 qq = *reinterpret_cast<const u32x4*>(qt + o);
       const u32x4 dd = *reinterpret_cast<const u32x4*>(dot + o);
       q4[b] = make_uint2(qq[0], qq[1]);
@@ -766,8 +774,8 @@ __global__ __launch_bounds__(256, 2) void bwd_key_mfma_kernel(
       d4[b + 1] = make_uint2(dd[2], dd[3]);
     }
   };
-  auto consume = [&](const float4& a, const float4& b, const float4& dl, const uint2 (&q4)[NB],
-                     const uint2 (&d4)[NB]) {
+  auto consume = [&](const float4& a, const float4& b, const float4& dl, const uint2 (&q4)[NBW],
+                     const uint2 (&d4)[NBW]) {
     uint32_t sh[4], sl2[4], ph[4], pl[4];
     auto split = [&](int k, float P, float w, float dlk) {
       const float dS = fmaf(-dlk, P, w);
@@ -785,8 +793,8 @@ __global__ __launch_bounds__(256, 2) void bwd_key_mfma_kernel(
     const bf16x4s aPh = pack4(ph[0] | (ph[1] << 16), ph[2] | (ph[3] << 16));
     const bf16x4s aPl = pack4(pl[0] | (pl[1] << 16), pl[2] | (pl[3] << 16));
 #pragma unroll
-    for (int bb = 0; bb < NB; ++bb) {
-      const bool mine = (4 * gq) / G == (16 * bb) / D;
+    for (int bb = 0; bb < NBW; ++bb) {
+      const bool mine = (4 * gq) / G == (16 * (bbase + bb)) / D;
       const uint2 z = make_uint2(0u, 0u);
       const bf16x4s bq = __builtin_bit_cast(bf16x4s, mine ? q4[bb] : z);
       const bf16x4s bd = __builtin_bit_cast(bf16x4s, mine ? d4[bb] : z);
@@ -802,19 +810,19 @@ __global__ __launch_bounds__(256, 2) void bwd_key_mfma_kernel(
     __syncthreads();  // the previous chunk's entries are read
     for (uint32_t i = threadIdx.x; i < n; i += 256) sl[i] = lst[base + i];
     __syncthreads();
-    uint32_t k = wave;
+    uint32_t k = wave / NS;
     if (k < n) {
       // the next entry's loads are issued before this one is consumed
       // (PF = 1: its {P, weight} and D - D~; PF = 2: everything)
       uint2 en = sl[k];
       float4 a, b, dl;
-      uint2 q4[NB], d4[NB];
+      uint2 q4[NBW], d4[NBW];
       fetch_pw(en, a, b, dl);
       if constexpr (PF == 2) fetch_q(en, q4, d4);
-      for (; k < n; k += 4) {
-        const uint2 en2 = sl[k + 4 < n ? k + 4 : k];
+      for (; k < n; k += STEP) {
+        const uint2 en2 = sl[k + STEP < n ? k + STEP : k];
         float4 a2, b2, dl2;
-        uint2 q42[NB], d42[NB];
+        uint2 q42[NBW], d42[NBW];
         if constexpr (PF >= 1) fetch_pw(en2, a2, b2, dl2);
         if constexpr (PF == 2) fetch_q(en2, q42, d42);
         if constexpr (PF == 0) fetch_pw(en, a, b, dl);
@@ -828,7 +836,7 @@ __global__ __launch_bounds__(256, 2) void bwd_key_mfma_kernel(
         }
         if constexpr (PF == 2) {
 #pragma unroll
-          for (int bb = 0; bb < NB; ++bb) {
+          for (int bb = 0; bb < NBW; ++bb) {
             q4[bb] = q42[bb];
             d4[bb] = d42[bb];
           }
@@ -839,13 +847,13 @@ __global__ __launch_bounds__(256, 2) void bwd_key_mfma_kernel(
   __syncthreads();
   for (int i = threadIdx.x; i < 2 * 16 * KD; i += 256) sbuf[i] = 0.0f;
   __syncthreads();
-  // lane (dim 16b + l16) holds tokens 4gq + i
+  // lane (dim 16 (bbase + b) + l16) holds tokens 4gq + i
 #pragma unroll
-  for (int b = 0; b < NB; ++b)
+  for (int b = 0; b < NBW; ++b)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      atomicAdd(&sk[(4 * gq + i) * KD + 16 * b + l16], ak[b][i]);
-      atomicAdd(&sv[(4 * gq + i) * KD + 16 * b + l16], av[b][i]);
+      atomicAdd(&sk[(4 * gq + i) * KD + 16 * (bbase + b) + l16], ak[b][i]);
+      atomicAdd(&sv[(4 * gq + i) * KD + 16 * (bbase + b) + l16], av[b][i]);
     }
   __syncthreads();
   for (int i = threadIdx.x; i < 16 * KD; i += 256) {
