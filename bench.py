@@ -364,6 +364,7 @@ def bench_decode(args, torch):
     torch.cuda.synchronize()
     per_f = np.array([evs[t].elapsed_time(evs[t + 1]) for t in range(steps)]) * 1e3
     fused_eager_us = evs[0].elapsed_time(evs[-1]) * 1e3 / steps
+    dl.check_step()     # raises (the run fails) if a wait for a selection gave up
     # graph replay, for each scheduling variant; the best one is reported
     variants = {}
     for name, kw in (("fused", None), ("inline-build", {}), ("side-build", {"overlap_build": True}),
@@ -382,6 +383,8 @@ def bench_decode(args, torch):
         s1.record()
         torch.cuda.synchronize()
         variants[name] = s0.elapsed_time(s1) * 1e3 / (reps * steps)
+        if kw is None:
+            dl.check_step()
         del g
     log(f"decode graph variants (us/step): {variants}")
     best = min(variants, key=variants.get)
@@ -408,6 +411,7 @@ def bench_decode(args, torch):
     s1.record()
     torch.cuda.synchronize()
     cold_us = s0.elapsed_time(s1) * 1e3 / (5 * steps)
+    dl.check_step(ws)
     del g, reps
     log(f"decode fused, 4 rotating cache replicas: {cold_us:.1f} us/step")
     kB = x.layout.k_blocks
@@ -425,6 +429,7 @@ def bench_decode(args, torch):
            "fused_eager_p99_us": float(np.percentile(per_f, 99)),
            "algorithmic_bytes_per_step": scan_bytes + gather,
            "hbm_frac": (scan_bytes + gather) / (graph_us * 1e-6) / (HBM_PEAK_GBS * 1e9),
+           "step_error_word": dl.step_error_word(ws),
            "cold_4_replicas_us_per_step": cold_us,
            "cold_hbm_frac": (scan_bytes + gather) / (cold_us * 1e-6) / (HBM_PEAK_GBS * 1e9)}
     if args.offload:
@@ -540,10 +545,13 @@ def bench_stack_decode(args, torch):
     s1.record()
     torch.cuda.synchronize()
     graph_us = s0.elapsed_time(s1) * 1e3 / (reps * steps)
+    for dl, plan, outs, ws, _ in layers:
+        dl.check_step(ws)
+    err_words = sum(dl.step_error_word(ws) for dl, plan, outs, ws, _ in layers)
     bytes_step = sum(b for *_, b in layers)
     res = {"workload": "stack-12x1m-decode", "layers": n_layers, "batch": 1,
            "context": 1048576, "steps": steps, "us_per_step": graph_us,
-           "mode": "hip-graph (fused, layers in sequence)",
+           "mode": "hip-graph (fused, layers in sequence)", "step_error_word": err_words,
            "eager_us_per_step": float(per.mean()), "eager_p50_us": float(np.percentile(per, 50)),
            "eager_p99_us": float(np.percentile(per, 99)),
            "algorithmic_bytes_per_step": bytes_step,

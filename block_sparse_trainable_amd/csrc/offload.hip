@@ -1,19 +1,26 @@
 // Selection-driven host-offloaded KV for decode (qsa_offload_stage).
 //
-// "Qwen Sparse Attention" gallery page and the serving-port page: the full
-// KV history can stay in host memory while the GPU keeps a hot cache and a
-// staging area, fetching on demand only the blocks each step selects (every
-// layer selects independently).  The pages describe another party's port,
-// not an algorithm; taken here: the KV rows of every token live in pinned
-// host memory ([batch][cap][Hkv][d], read by the kernel over the host link);
-// the compressed index stays in HBM, so scoring and top-k run as usual; per
-// decode step this call gathers the query's token set -- the selected blocks
+// "QSA" knowledge-card page (kongchang.com), Timeline and All Facts: a
+// serving port keeps each request's full KV history in host memory and only
+// hot data in GPU memory, fetches what each step selects, and each of the
+// QSA layers keeps its own selection (so no index is shared across layers).
+// That page reports another party's port, not an algorithm; the reading
+// taken here: the K/V rows of every token live in pinned host memory
+// ([batch][cap][Hkv][d], read by the kernel over the host link); the
+// compressed index stays in HBM, so scoring and top-k run as usual; per
+// decode step this call copies the query's token set -- the selected blocks
 // in ascending order, then the tail -- into a contiguous staging buffer in
-// HBM, reading each 4-token unit from a direct-mapped HBM hot cache when it
-// is there and from host memory otherwise, then promotes the missed units
-// into the hot cache.  It also writes the selection in staged coordinates
-// (blocks 0 .. count-1, the tail after them), so qsa_sparse_attn_decode on
-// the staging buffer attends over exactly the query's token set.
+// HBM, taking each 4-token unit from a direct-mapped HBM hot cache when the
+// unit is there and from host memory otherwise, then promotes the missed
+// units into the hot cache.  It also writes the selection in staged
+// coordinates (blocks 0 .. count-1, the tail after them), so
+// qsa_sparse_attn_decode on the staging buffer attends over exactly the
+// query's token set.
+//
+// Only units that are complete at the step (every row at or before the
+// query's position p) are cached or read from the cache: the unit holding p
+// also covers rows p+1 .. that the caller has not written yet, so it always
+// comes from host memory, where the next steps will find their new rows.
 #include "qsa_common.h"
 
 namespace qsa {
@@ -67,7 +74,7 @@ __global__ __launch_bounds__(kOT) void offload_gather_kernel(
   for (int i = i0 + wave; i < i1; i += kOT / 64) {
     const int64_t u = unit(i);
     const int slot = (int)(u % hot_units);
-    const bool hit = tags[slot] == (int32_t)u;
+    const bool hit = 4 * u + 3 <= unit.p && tags[slot] == (int32_t)u;
     uint16_t* dk = sk + ((int64_t)s * stage_tokens + 4 * (int64_t)i) * KD;
     uint16_t* dv = sv + ((int64_t)s * stage_tokens + 4 * (int64_t)i) * KD;
     for (int ch = lane; ch < CH; ch += 64) {
@@ -85,10 +92,10 @@ __global__ __launch_bounds__(kOT) void offload_gather_kernel(
 }
 
 // Promotion, one workgroup per sequence, after the gathering: counts the hits
-// and misses against the tags the gathering saw, then writes each missed unit
-// from the staging buffer into its slot -- one unit per hash bucket of the
-// slot, so a slot gets data and tag from a single unit -- and writes the
-// selection in staging coordinates.
+// and misses against the tags the gathering saw, then writes each missed
+// complete unit from the staging buffer into its slot -- one unit per hash
+// bucket of the slot, so a slot gets data and tag from a single unit -- and
+// writes the selection in staging coordinates.
 __global__ __launch_bounds__(kPT) void offload_promote_kernel(
     int kB, int lr, int KD, const int32_t* __restrict__ q_pos, const int32_t* __restrict__ sel,
     const int32_t* __restrict__ cnt, int64_t cap, uint16_t* __restrict__ hk,
@@ -108,7 +115,7 @@ __global__ __launch_bounds__(kPT) void offload_promote_kernel(
   int h = 0, m = 0;
   for (int i = threadIdx.x; i < unit.npb; i += kPT) {
     const int64_t u = unit(i);
-    if (tags[u % hot_units] == (int32_t)u) ++h; else ++m;
+    if (4 * u + 3 <= unit.p && tags[u % hot_units] == (int32_t)u) ++h; else ++m;
   }
   atomicAdd(&n_hit, h);
   atomicAdd(&n_miss, m);
@@ -117,6 +124,7 @@ __global__ __launch_bounds__(kPT) void offload_promote_kernel(
   for (int i = wave; i < unit.npb; i += kPT / 64) {
     const int64_t u = unit(i);
     const int slot = (int)(u % hot_units);
+    if (4 * u + 3 > unit.p) continue;                // rows past p: not final yet
     if (tags[slot] == (int32_t)u) continue;          // a hit (or already promoted)
     int owner = 0;
     if (lane == 0) owner = atomicCAS(&claim[slot & (kClaim - 1)], -1, slot) == -1;

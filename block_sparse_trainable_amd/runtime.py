@@ -205,6 +205,28 @@ class DeviceLayer:
             self._ws["step"] = ws
         return ws
 
+    def step_error_word(self, ws=None) -> int:
+        """The fused step's error word (reads device memory: synchronises).
+        Non-zero means a wait for a selection gave up in some call since the
+        control area was last cleared, and those calls' outputs are invalid."""
+        ws = self._ws.get("step") if ws is None else ws
+        if ws is None:
+            return 0
+        e = B.QSA_STEP_ERROR_BYTE
+        return int(ws[e:e + 4].view(torch.int32).item())
+
+    def check_step(self, ws=None) -> None:
+        """Raises if the fused step's error word is set, after zero-filling
+        the control area again (a call that gave up can leave records
+        behind that the next call would take as published)."""
+        ws = self._ws.get("step") if ws is None else ws
+        err = self.step_error_word(ws)
+        if err:
+            ws[:B.QSA_STEP_CONTROL_BYTES].zero_()
+            torch.cuda.synchronize(self.device)
+            raise B.QsaError(B.QSA_ERR_DEVICE,
+                             f"qsa_decode_step: a wait for a selection gave up (error word {err})")
+
     def decode_step_fused(self, plan, t: int, outputs, ws=None):
         """The same decode step as decode_step, in one launch (qsa_decode_step)."""
         q_idx_s, q_s, pos_t, pos1_t, max_pos_end = plan

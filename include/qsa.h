@@ -350,17 +350,20 @@ qsa_status qsa_indexer_distill(const qsa_config* cfg, int32_t batch, int32_t n_q
                                size_t workspace_bytes, hipStream_t stream);
 
 /* qsa_offload_stage -- decode with the KV history in host memory.
- * The pages describe a serving port that keeps the full history in host
- * memory with a hot cache and a staging area in GPU memory, fetching the
- * blocks each step selects ([gallery] Where QSA sits; the port page).
- * Taken here: for each sequence's decode query at q_pos[s], with the
- * selection of qsa_select_topk (made on the compressed index, which stays in
- * GPU memory), gathers the query's token set -- the selected blocks in
- * ascending order, then the tail -- into stage_k / stage_v, 4-token unit by
- * unit: from the hot cache when the unit's slot (unit id mod hot_units)
- * holds it, else from host memory; then writes the missed units into their
- * slots (one per slot when several miss to it).  It also writes the
- * selection in staging coordinates, so that
+ * The "QSA" knowledge-card page (Timeline; All Facts) reports a serving
+ * port that keeps the full history in host memory, only hot data and a
+ * staging area in GPU memory, fetching on demand what each layer's own
+ * selection picks.  Taken here: for each sequence's decode query at
+ * q_pos[s], with the selection of qsa_select_topk (made on the compressed
+ * index, which stays in GPU memory), gathers the query's token set -- the
+ * selected blocks in ascending order, then the tail -- into stage_k /
+ * stage_v, 4-token unit by unit: from the hot cache when the unit's slot
+ * (unit id mod hot_units) holds it, else from host memory; then writes the
+ * missed units into their slots (one per slot when several miss to it).
+ * Only complete units (all four rows at or before q_pos[s]) are cached or
+ * read from the cache; the unit holding q_pos[s] always comes from host
+ * memory, since its later rows are written by later steps.  It also writes
+ * the selection in staging coordinates, so that
  *     qsa_sparse_attn_decode(cfg, batch, q, stage_k, stage_v, stage_tokens,
  *                            stage_pos, stage_tokens, stage_sel, stage_cnt, ...)
  * attends over exactly the query's token set (in another order: equal up to
@@ -368,7 +371,9 @@ qsa_status qsa_indexer_distill(const qsa_config* cfg, int32_t batch, int32_t n_q
  *
  *   q_pos, sel_blocks, sel_count  as for qsa_sparse_attn_decode.
  *   k_host, v_host  bf16 [batch][cap_tokens][kv_heads][head_dim] in pinned,
- *              device-mapped host memory (hipHostMalloc); read only.
+ *              device-mapped host memory (hipHostMalloc); read only.  Row t
+ *              must hold its final value from the step at position t on and
+ *              never change after (the hot cache keeps copies).
  *   hot_k, hot_v    bf16 [batch][hot_units][4][kv_heads][head_dim] GPU memory.
  *   hot_tag    int32 [batch][hot_units]: the unit each slot holds, -1 for
  *              none; the caller fills it with -1 once; every call keeps it
@@ -379,8 +384,8 @@ qsa_status qsa_indexer_distill(const qsa_config* cfg, int32_t batch, int32_t n_q
  *   stage_pos int32 [batch]: written (blocks 0 .. count-1, -1 padding; the
  *              query's position in the staging buffer).
  *   stats      int32 [batch][2]: units read from the hot cache, from host.
- * Calls on one stream are ordered; concurrent calls must not share a hot
- * cache.                                                                  */
+ * Supported: block_size >= 4 (units of 4 tokens).  Calls on one stream are
+ * ordered; concurrent calls must not share a hot cache.                   */
 qsa_status qsa_offload_stage(const qsa_config* cfg, int32_t batch, const int32_t* q_pos,
                              const int32_t* sel_blocks, const int32_t* sel_count,
                              const void* k_host, const void* v_host, int64_t cap_tokens,

@@ -145,6 +145,25 @@ def test_distill_chunk_over_cache():
     _check(x, _run(x), {s: set(range(0, 160, 2)) for s in range(2)})
 
 
+@pytest.mark.parametrize("kv_heads,head_dim", [(1, 128), (2, 64)])
+def test_distill_bf16_other_head_shapes(kv_heads, head_dim):
+    """The MFMA teacher's other two shapes (16 query heads over one KV head of
+    128 dims, or two of 64), with a query count that is not a multiple of
+    the 16 rows a teacher workgroup takes."""
+    say(f"distill bf16 kv_heads={kv_heads} head_dim={head_dim}, n=613")
+    lay = synth.Layout(token_budget=512, kv_heads=kv_heads, head_dim=head_dim)
+    x = synth.prefill(n=613, layout=lay, needle_frac=0.05)
+    _check(x, _run(x), {0: set(range(0, 613, 3)) | {612}})
+
+
+@pytest.mark.parametrize("kv_heads,head_dim", [(1, 128), (2, 64)])
+def test_distill_other_head_shapes_chunk_over_cache(kv_heads, head_dim):
+    say(f"distill bf16 kv_heads={kv_heads} head_dim={head_dim}: 75 queries over 1300 cached")
+    lay = synth.Layout(token_budget=256, kv_heads=kv_heads, head_dim=head_dim)
+    x = synth.chunked(cache=1300, chunk=75, batch=2, window=256, n_far=3, layout=lay)
+    _check(x, _run(x), {s: set(range(75)) for s in range(2)})
+
+
 def test_distill_fp32_small_heads():
     say("distill fp32, 4 heads / 1 KV head, d=64, r=8")
     lay = synth.Layout(block_size=8, token_budget=128, dtype="f32", q_heads=4, kv_heads=1,

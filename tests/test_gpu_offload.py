@@ -138,3 +138,47 @@ def test_offloaded_decode_graph_replays():
         assert torch.equal(off.stats, eager[-1][2])
         dl.decode_step(plan, rep, dl.alloc_decode_outputs())   # eager work between replays
         torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("r", [4, 16])
+def test_offloaded_decode_rows_written_step_by_step(r):
+    """Real decode writes row p into host memory only just before step p.
+    The unit holding p also spans rows p+1.. that are not written yet, so
+    it must never be served from the hot cache: with garbage in every host
+    row past the current position, each step must still match the
+    resident path."""
+    say(f"offloaded decode, host rows written step by step, r={r}")
+    steps = 9
+    lay = synth.Layout(block_size=r)
+    x = synth.decode(context=20000, batch=2, steps=steps, n_needles=4, layout=lay)
+    dl = DeviceLayer(x)
+    dl.build_prefix(x.cache_len)
+    plan = dl.decode_plan(steps)
+    off = OffloadedKV(dl, 4096)
+    garbage = torch.full(off.k_host.shape[2:], 7.5, dtype=off.k_host.dtype)
+    for s in range(2):
+        p0 = int(x.q_pos0[s])
+        off.k_host[s, p0:] = garbage
+        off.v_host[s, p0:] = -garbage
+    k_cpu, v_cpu = dl.k.cpu(), dl.v.cpu()
+    res = dl.alloc_decode_outputs()
+    ofs = dl.alloc_decode_outputs()
+    for t in range(steps):
+        torch.cuda.synchronize()
+        for s in range(2):                  # the new token's row arrives now
+            p = int(x.q_pos0[s]) + t
+            off.k_host[s, p] = k_cpu[s, p]
+            off.v_host[s, p] = v_cpu[s, p]
+        dl.decode_step(plan, t, res)
+        off.decode_step(plan, t, ofs)
+        torch.cuda.synchronize()
+        assert torch.equal(res[0], ofs[0]) and torch.equal(res[1], ofs[1])
+        err = np.abs(to_f32(res[3]) - to_f32(ofs[3])).max()
+        assert err <= C.ATOL["bf16"], f"step {t}: offloaded output off by {err:.3e}"
+        assert np.abs(res[4].cpu().numpy() - ofs[4].cpu().numpy()).max() <= 1e-3
+    # no cached unit reaches past the last position
+    tags = off.hot_tag.cpu().numpy()
+    for s in range(2):
+        p = int(x.q_pos0[s]) + steps - 1
+        u = tags[s][tags[s] >= 0].astype(np.int64)
+        assert (4 * u + 3 <= p).all()
