@@ -29,7 +29,7 @@ EXPORTED = (
     "qsa_index_build", "qsa_select_topk", "qsa_sparse_attn_prefill", "qsa_sparse_attn_decode",
     "qsa_decode_step", "qsa_sparse_attn_backward", "qsa_index_build_backward",
     "qsa_indexer_distill", "qsa_offload_stage", "qsa_workspace_size", "qsa_status_string",
-    "qsa_last_error", "qsa_abi_version",
+    "qsa_last_error", "qsa_abi_version", "qsa_decode_step_noalloc",
 )
 
 
@@ -94,6 +94,7 @@ def load(path: str | None = None):
         "qsa_sparse_attn_prefill": [CFG, I32, I32, P, P, P, I64, P, I32, P, P, P, P, P, SZ, P],
         "qsa_sparse_attn_decode": [CFG, I32, P, P, P, I64, P, I32, P, P, P, P, P, SZ, P],
         "qsa_decode_step": [CFG, I32, P, P, P, P, P, P, P, I64, P, I32, P, P, P, P, P, P, SZ, P],
+        "qsa_decode_step_noalloc": [CFG, I32, P, P, P, P, P, P, P, I64, P, I32, P, P, P, P, P, P],
         "qsa_sparse_attn_backward": [CFG, I32, I32, P, P, P, I64, P, I32, P, P, P, P, P, P, P,
                                      P, P, SZ, P],
         "qsa_index_build_backward": [CFG, I32, P, I64, P, P, I32, P, P, P, P],
@@ -196,6 +197,18 @@ def qsa_decode_step(cfg, batch, q_idx, q, k_idx, k_cmp, rms_gain, k_cache, v_cac
                                     cap_tokens, _ptr(q_pos), max_pos_end, _ptr(sel_blocks),
                                     _ptr(sel_count), _ptr(sel_scores), _ptr(out), _ptr(lse),
                                     _ptr(workspace), workspace_bytes, _stream(stream)))
+
+
+def qsa_decode_step_noalloc(cfg, batch, q_idx, q, k_idx, k_cmp, rms_gain, k_cache, v_cache,
+                            cap_tokens, q_pos, max_pos_end, sel_blocks, sel_count, sel_scores,
+                            out, lse, stream=None) -> None:
+    lib = load()
+    _check(lib, lib.qsa_decode_step_noalloc(ctypes.byref(cfg), batch, _ptr(q_idx), _ptr(q),
+                                            _ptr(k_idx), _ptr(k_cmp), _ptr(rms_gain),
+                                            _ptr(k_cache), _ptr(v_cache), cap_tokens, _ptr(q_pos),
+                                            max_pos_end, _ptr(sel_blocks), _ptr(sel_count),
+                                            _ptr(sel_scores), _ptr(out), _ptr(lse),
+                                            _stream(stream)))
 
 
 def qsa_sparse_attn_backward(cfg, batch, n_q, q, k_cache, v_cache, cap_tokens, q_pos0,

@@ -6,8 +6,15 @@
 #include <string.h>
 
 #include <cmath>
+#include <mutex>
 
 #include "qsa_common.h"
+
+// Step workspace of qsa_decode_step_noalloc: one copy per device, held
+// until the process ends.  In host code `scratch` names a host-side stand-in,
+// not device memory; the device address comes from hipGetSymbolAddress.
+static constexpr size_t kNoAllocScratchBytes = size_t{32} << 20;
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
 
 namespace {
 
@@ -115,6 +122,42 @@ qsa_status launched(const char* fn, hipError_t e) {
   if (e != hipSuccess)
     return fail(QSA_ERR_DEVICE, "%s: launch failed: %s", fn, hipGetErrorString(e));
   return ok();
+}
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];   // device address of scratch, per device
+bool g_scratch_cleared[kMaxDevices];
+
+__global__ __launch_bounds__(256) void zero_words_kernel(uint32_t* p, size_t n) {
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+       i += (size_t)gridDim.x * blockDim.x)
+    p[i] = 0u;
+}
+
+// The current device's scratch address; *first is true on the first call
+// for that device (the caller then clears the control area).
+qsa_status scratch_for_current_device(const char* fn, void** ptr, bool* first) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    (void)hipGetLastError();
+    return fail(QSA_ERR_DEVICE, "%s: no usable current device", fn);
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p) {
+      (void)hipGetLastError();
+      return fail(QSA_ERR_DEVICE, "%s: hipGetSymbolAddress(scratch) failed: %s", fn,
+                  hipGetErrorString(e));
+    }
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  *first = !g_scratch_cleared[dev];
+  g_scratch_cleared[dev] = true;
+  return QSA_OK;
 }
 
 }  // namespace
@@ -338,15 +381,17 @@ qsa_status qsa_sparse_attn_backward(const qsa_config* cfg, int32_t batch, int32_
                                                 lse, dout, dq, dk, dv, workspace, stream));
 }
 
-qsa_status qsa_decode_step(const qsa_config* cfg, int32_t batch, const void* q_idx,
-                           const void* q, const void* k_idx, void* k_cmp,
-                           const float* rms_gain, const void* k_cache, const void* v_cache,
-                           int64_t cap_tokens, const int32_t* q_pos, int32_t max_pos_end,
-                           int32_t* sel_blocks, int32_t* sel_count, float* sel_scores,
-                           void* out, float* lse, void* workspace, size_t workspace_bytes,
-                           hipStream_t stream) {
-  const char* fn = "qsa_decode_step";
-  qsa::Dims d;
+// Validation shared by qsa_decode_step and qsa_decode_step_noalloc: every
+// argument but the workspace.  Fills the kernel dimensions and the plan.
+static qsa_status step_validate(const char* fn, const qsa_config* cfg, int32_t batch,
+                                const void* q_idx, const void* q, const void* k_idx,
+                                const void* k_cmp, const float* rms_gain, const void* k_cache,
+                                const void* v_cache, int64_t cap_tokens, const int32_t* q_pos,
+                                int32_t max_pos_end, const int32_t* sel_blocks,
+                                const int32_t* sel_count, const float* sel_scores,
+                                const void* out, const float* lse, qsa::Dims* dp,
+                                qsa::StepPlan* plan) {
+  qsa::Dims& d = *dp;
   qsa_status st = check_config(fn, cfg, &d);
   if (st != QSA_OK) return st;
   st = check_sizes(fn, batch, 1, cap_tokens, max_pos_end);
@@ -377,7 +422,24 @@ qsa_status qsa_decode_step(const qsa_config* cfg, int32_t batch, const void* q_i
     return fail(QSA_ERR_INVALID_ARGUMENT, "%s: sel_scores must be 4-byte aligned", fn);
   if (lse && !aligned(lse, 4))
     return fail(QSA_ERR_INVALID_ARGUMENT, "%s: lse must be 4-byte aligned", fn);
-  const qsa::StepPlan pl = qsa::step_plan(d, batch, max_pos_end);
+  *plan = qsa::step_plan(d, batch, max_pos_end);
+  return QSA_OK;
+}
+
+qsa_status qsa_decode_step(const qsa_config* cfg, int32_t batch, const void* q_idx,
+                           const void* q, const void* k_idx, void* k_cmp,
+                           const float* rms_gain, const void* k_cache, const void* v_cache,
+                           int64_t cap_tokens, const int32_t* q_pos, int32_t max_pos_end,
+                           int32_t* sel_blocks, int32_t* sel_count, float* sel_scores,
+                           void* out, float* lse, void* workspace, size_t workspace_bytes,
+                           hipStream_t stream) {
+  const char* fn = "qsa_decode_step";
+  qsa::Dims d;
+  qsa::StepPlan pl;
+  qsa_status st = step_validate(fn, cfg, batch, q_idx, q, k_idx, k_cmp, rms_gain, k_cache,
+                                v_cache, cap_tokens, q_pos, max_pos_end, sel_blocks, sel_count,
+                                sel_scores, out, lse, &d, &pl);
+  if (st != QSA_OK) return st;
   if (!workspace || workspace_bytes < pl.bytes)
     return fail(QSA_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn, pl.bytes,
                 workspace ? workspace_bytes : (size_t)0);
@@ -474,6 +536,46 @@ qsa_status qsa_offload_stage(const qsa_config* cfg, int32_t batch, const int32_t
                                                 cap_tokens, hot_k, hot_v, hot_tag, hot_units,
                                                 stage_k, stage_v, stage_tokens, stage_sel,
                                                 stage_cnt, stage_pos, stats, stream));
+}
+
+// qsa_decode_step_noalloc: qsa_decode_step with its workspace in the
+// library's own device memory, for callers that cannot allocate.  The
+// workspace is `scratch`, a file-scope device array; its device address is
+// looked up once per device (hipGetSymbolAddress with that device current)
+// and only that address is handed to kernels.  The first call on a device
+// also enqueues, on its stream, a clear of the control area the fused step
+// expects to find zero; every completed call leaves it zero again.
+qsa_status qsa_decode_step_noalloc(const qsa_config* cfg, int32_t batch, const void* q_idx,
+                                   const void* q, const void* k_idx, void* k_cmp,
+                                   const float* rms_gain, const void* k_cache,
+                                   const void* v_cache, int64_t cap_tokens, const int32_t* q_pos,
+                                   int32_t max_pos_end, int32_t* sel_blocks, int32_t* sel_count,
+                                   float* sel_scores, void* out, float* lse, hipStream_t stream) {
+  const char* fn = "qsa_decode_step_noalloc";
+  qsa::Dims d;
+  qsa::StepPlan pl;
+  qsa_status st = step_validate(fn, cfg, batch, q_idx, q, k_idx, k_cmp, rms_gain, k_cache,
+                                v_cache, cap_tokens, q_pos, max_pos_end, sel_blocks, sel_count,
+                                sel_scores, out, lse, &d, &pl);
+  if (st != QSA_OK) return st;
+  if (pl.bytes > kNoAllocScratchBytes)
+    return fail(QSA_ERR_UNSUPPORTED,
+                "%s: these sizes need %zu bytes of step workspace, beyond the library's "
+                "%zu-byte scratch (use qsa_decode_step with a workspace)",
+                fn, pl.bytes, kNoAllocScratchBytes);
+  void* ws = nullptr;
+  bool first = false;
+  st = scratch_for_current_device(fn, &ws, &first);
+  if (st != QSA_OK) return st;
+  if (first) {
+    hipLaunchKernelGGL(zero_words_kernel, dim3(256), dim3(256), 0, stream,
+                       static_cast<uint32_t*>(ws), qsa::kStepCtlBytes / 4);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return launched(fn, e);
+  }
+  return launched(fn, qsa::launch_decode_step(d, pl, batch, q_idx, q, k_idx, k_cmp, rms_gain,
+                                              k_cache, v_cache, cap_tokens, q_pos, sel_blocks,
+                                              sel_count, sel_scores, out, lse, ws, stream));
 }
 
 }  // extern "C"

@@ -237,6 +237,16 @@ class DeviceLayer:
                           sel[:, 0], cnt[:, 0], scs[:, 0], out, lse, ws, ws.numel())
         return outputs
 
+    def decode_step_noalloc(self, plan, t: int, outputs):
+        """decode_step_fused through qsa_decode_step_noalloc (the library's
+        own per-device step workspace: nothing is allocated)."""
+        q_idx_s, q_s, pos_t, pos1_t, max_pos_end = plan
+        sel, cnt, scs, out, lse = outputs
+        B.qsa_decode_step_noalloc(self.cfg, self.batch, q_idx_s[t], q_s[t], self.k_idx,
+                                  self.k_cmp, self.gain, self.k, self.v, self.cap, pos_t[t],
+                                  int(max_pos_end), sel[:, 0], cnt[:, 0], scs[:, 0], out, lse)
+        return outputs
+
     def capture_decode_fused(self, plan, steps: int, outputs):
         """Capture `steps` fused decode steps into one HIP graph."""
         ws = self.step_workspace(plan[4])

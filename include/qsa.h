@@ -237,6 +237,30 @@ qsa_status qsa_decode_step(const qsa_config* cfg, int32_t batch, const void* q_i
                            void* out, float* lse, void* workspace, size_t workspace_bytes,
                            hipStream_t stream);
 
+/* qsa_decode_step_noalloc -- qsa_decode_step for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  Same arguments, semantics and results
+ * as qsa_decode_step, without the workspace: the step workspace is a 32 MiB
+ * array in the library's own device memory, one per GPU, held until the
+ * process ends.  The call allocates nothing.  The first call on a device
+ * also enqueues a clear of the array's control area on its stream; every
+ * completed call leaves the control area zero for the next.
+ *   Limits: sizes whose qsa_workspace_size(QSA_OP_DECODE_STEP, batch, 1,
+ *   max_pos_end) exceeds 32 MiB return QSA_ERR_UNSUPPORTED (batch 8 at
+ *   256K context needs about 11 MB).
+ *   Concurrency: every call on a GPU uses that GPU's one array, so calls
+ *   that overlap on one GPU (other streams, other threads) race and give
+ *   wrong results; order them on one stream.  If a call's wait ever gives
+ *   up (word 2048 of the control area, as in qsa_decode_step), the array is
+ *   not readable from the host: that call's outputs are invalid and later
+ *   calls may be too.                                                      */
+qsa_status qsa_decode_step_noalloc(const qsa_config* cfg, int32_t batch, const void* q_idx,
+                                   const void* q, const void* k_idx, void* k_cmp,
+                                   const float* rms_gain, const void* k_cache,
+                                   const void* v_cache, int64_t cap_tokens, const int32_t* q_pos,
+                                   int32_t max_pos_end, int32_t* sel_blocks, int32_t* sel_count,
+                                   float* sel_scores, void* out, float* lse, hipStream_t stream);
+
 /* Workspace bytes needed by op (a qsa_op) for these sizes.  n_q is 1 for
  * QSA_OP_DECODE and QSA_OP_DECODE_STEP; QSA_OP_INDEX_BUILD needs none.  The
  * select workspace holds the materialised score rows, per-segment score
