@@ -1,12 +1,12 @@
 // Sparse core attention (kernel d): prefill (one workgroup per query) and
 // decode (a query's token set split over several workgroups, then merged).
 //
-// "QSA (Qwen Sparse Attention)", Key math / How it works: (B) full
-// scaled-dot-product attention restricted to the selected blocks' tokens;
-// (A) the selected blocks are expanded back to tokens and the tail of the
-// current block is always included.  "Qwen Sparse Attention" gallery page:
-// the attention input is every token of the selected blocks plus the visible
-// tokens of the current incomplete block.
+// "QSA (Qwen Sparse Attention)", Key math / How it works: (B) each query
+// runs ordinary softmax attention (logits scaled by 1/sqrt(d)), but only over
+// the tokens of its chosen blocks; (A) a chosen block contributes all of its
+// tokens, and the already visible part of the query's own block is added.
+// "Qwen Sparse Attention" gallery page, How block selection works: the same
+// token set, as the pseudocode's attention input.
 //
 // Token set of the query at p (c = floor(p/4)): pseudo-blocks 0..count-1 are
 // the selected blocks, pseudo-block `count` is the tail block c, whose

@@ -1,8 +1,8 @@
 // Gradients of the sparse core attention (qsa_sparse_attn_backward).
 //
-// "QSA (Qwen Sparse Attention)", Key math / How it works: (B) full
-// scaled-dot-product attention restricted to each query's selected tokens,
-// (A) the selected blocks expanded to tokens plus the tail.  The pages give
+// "QSA (Qwen Sparse Attention)", Key math / How it works: (B) softmax
+// attention over each query's token set only, (A) that set being the chosen
+// blocks' tokens plus the visible part of the query's block.  The pages give
 // the forward only; these kernels compute its exact derivative with every
 // token set held fixed (no gradient reaches the indexer through the top-k_B
 // choice).  Per query i, head h, KV head g = floor(h * Hkv / Hq), token j in
@@ -12,14 +12,20 @@
 //     dq_h = scale sum_j dS_j K_j,  dK_j += scale dS_j q_h,  dV_j += P_j dO_h.
 //
 // Two sides, no atomics on the gradients:
-//   * query side (one workgroup per query row): D_h, then dq, heads in turn;
-//   * key side (one workgroup per 4-token unit of the cache): the unit's K/V
-//     rows stay in LDS while the workgroup walks the queries whose token set
-//     holds the unit's block -- a transposed index built by counting (per
-//     block), scanning and filling -- and adds the unit's dK/dV once.
+//   * query side (one workgroup per query row): dq.  MFMA path (bf16, 16
+//     query heads): one pass over the forward's 32-token tiles with a
+//     reference D~ from the forward output and an exact correction; it also
+//     exports what the key side needs.  VALU path: D_h, then dq, heads in
+//     turn;
+//   * key side, from a transposed index (the queries whose token set holds
+//     each piece of the cache, built by counting, scanning and filling).
+//     MFMA path: one workgroup per 16-token group, four waves in two pairs
+//     each owning half of the KV dims, 16x16x16 MFMAs contracting over the
+//     16 heads, dK/dV added once per group.  VALU path: one workgroup per
+//     4-token unit, the unit's K/V rows in LDS while it walks its queries.
 // The transposed lists are filled with atomics, so the order in which a
-// unit sums its queries, and with it the last bits of dK/dV, can change from
-// run to run; dq is deterministic.
+// group or unit sums its queries, and with it the last bits of dK/dV, can
+// change from run to run; dq is deterministic.
 #include <math.h>
 
 #include "attn_tile.h"

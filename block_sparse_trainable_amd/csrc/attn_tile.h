@@ -2,10 +2,10 @@
 // one split of it, attended by a 256-thread workgroup.  Shared by the
 // stand-alone attention kernels and the fused decode step.
 //
-// "QSA (Qwen Sparse Attention)", Key math / How it works: (B) full
-// scaled-dot-product attention restricted to the selected blocks' tokens;
-// (A) the selected blocks are expanded back to tokens and the tail of the
-// current block is always included.
+// "QSA (Qwen Sparse Attention)", Key math / How it works: (B) each query
+// runs ordinary softmax attention (logits scaled by 1/sqrt(d)), but only over
+// the tokens of its chosen blocks; (A) a chosen block contributes all of its
+// tokens, and the already visible part of the query's own block is added.
 //
 // Token set of the query at p (c = floor(p/4)): pseudo-blocks 0..count-1 are
 // the selected blocks, pseudo-block `count` is the tail block c, whose

@@ -1,10 +1,11 @@
 // Stage-1 indexer distillation: loss and gradients (qsa_indexer_distill), and
 // the gradient back through the block compression (qsa_index_build_backward).
 //
-// "QSA (Qwen Sparse Attention)", Native trainability, stage 1: an indexer-only
-// warm-up fits the indexer scores to a block-maxpooled version of the dense
-// teacher attention distribution with a KL loss, while the model still runs
-// dense attention.  The pages leave the details open; read as: for the query
+// "QSA (Qwen Sparse Attention)", Native trainability, stage 1: before sparse
+// training, only the indexer learns; its scores are pulled, by a KL
+// divergence, toward the dense model's attention after a max over each
+// block, and the model itself keeps attending densely meanwhile.  The pages
+// leave the details open; read as: for the query
 // at p, the teacher is the dense causal attention over tokens 0..p averaged
 // over the main heads; its max over each candidate block's r tokens
 // (b < c = floor(p/r)), renormalised over the candidates, is the target t;

@@ -337,10 +337,10 @@ qsa_status qsa_index_build_backward(const qsa_config* cfg, int32_t batch, const 
                                     hipStream_t stream);
 
 /* qsa_indexer_distill -- stage-1 indexer distillation loss and gradients.
- * [concept] "Native trainability", stage 1: the indexer scores are fitted to
- * a block-maxpooled version of the dense teacher attention distribution
- * with a KL loss while the model runs dense attention.  The pages leave the
- * details open; taken here: for the query at p (c = floor(p/r) candidate
+ * [concept] "Native trainability", stage 1: only the indexer trains, its
+ * scores pulled by a KL divergence toward the dense model's attention after
+ * a max over each block, while the model still attends densely.  The pages
+ * leave the details open; taken here: for the query at p (c = floor(p/r) candidate
  * blocks), the teacher is the dense causal attention over tokens 0..p
  * averaged over the q_heads heads (head h reads KV head h*Hkv/Hq, the
  * forward's scale); t_b is its max over block b's r tokens, renormalised over

@@ -16,8 +16,9 @@ plain NumPy fp64, one query row at a time.  Sources:
     partial RoPE on 64 of 128 dims, applied after compression; block
     importance I_ib = sum_h ReLU(<q_i^h, k_bar_b>) with block-causal masking;
     top-k_B selection, k_B = ceil(K/r), expanded to tokens plus the tail of
-    the current block.  (B) sparse core attention: full scaled-dot-product
-    attention restricted to the selected tokens.  "Config": K=2048, r=4.
+    the current block.  (B) sparse core attention: softmax attention with
+    the 1/sqrt(d) logit scale over the selected tokens only.  "Config":
+    K=2048, r=4.
 [gallery] "Qwen Sparse Attention" architecture-gallery page: the selection
     unit/budget table (complete four-token blocks, up to 512 blocks plus the
     current tail); "How block selection works" (blocks of keys preceding the
@@ -296,8 +297,8 @@ def teacher_block_target(q_row: np.ndarray, K: np.ndarray, p: int, r: int,
     0..p, averaged over the heads, max-pooled over each block's r tokens,
     renormalised over the candidates.
 
-    [concept] "Native trainability" (stage-1: a block-maxpooled version of
-    the dense teacher attention distribution).  Head h reads KV head
+    [concept] "Native trainability", stage 1 (the dense attention, maxed
+    over each block, as the indexer's target).  Head h reads KV head
     floor(h*Hkv/Hq), scale as in (B).  Empty when there is no candidate.
     """
     c = p // r
