@@ -1,21 +1,31 @@
 """QSA layer forward pass benchmark on one MI355X.
 
-    python bench.py [--steps K] [--warmup W] [--workload chunked|prefill]
-                    [--decode {decode,stack,none}] [--no-cpu-baseline]
+    python bench.py [--steps K] [--warmup W] [--legs LIST] [--block-size R]
 
 One step = one pass of the whole hot path over one batch of synthetic input:
 index build of the chunk's new blocks -> block scoring + top-k_B selection ->
 sparse attention.  The headline workload is chunked prefill at 128K context
 (2 sequences, 131,072 cached tokens, 8,192 new queries each, 16Q/2KV heads,
 d=128, K=2048, r=4, bf16); `value` is prefill tokens/s with every input
-resident in HBM.  Alongside, the decode loop (8 sequences at 256K context,
-one token per sequence per step: index build, selection, split attention)
-is timed over 64 steps and reported as microseconds per step.
+resident in HBM.  Beside it, one object per other workload:
+
+  prefill_32k   1 x 32,768 queries from an empty cache;
+  companion_1m  the last 4,096 queries of a 1,048,576-token context;
+  decode        8 sequences at 256K context, 64 decode steps (fused step in a
+                HIP graph, a cold variant on 4 rotating cache replicas, the
+                three-call variants, the KV history offloaded to host memory);
+  stack_1m      12 independent layers at 1M context, batch 1, 64 decode steps,
+                the layers strictly in sequence;
+  backward, distill   the attention backward and the stage-1 distillation on
+                the headline chunk.
 
 Timing: torch.cuda events on the stream every kernel is launched on (the
 binding launches on torch's current stream), a device synchronisation on
 both sides of the timed region.  The dominant kernel's average duration is
 taken from events around its launches inside the timed region.
+
+The oracle (fp64, CPU) is timed last, on the host's cores, one worker process
+per usable core (at most 16), on seeded row samples of the same workloads.
 
 Prints one JSON line.
 """
@@ -25,7 +35,9 @@ import argparse
 import json
 import math
 import os
+import shutil
 import sys
+import tempfile
 import time
 
 import numpy as np
@@ -36,18 +48,21 @@ sys.path.insert(0, ROOT)
 METRIC = "QSA prefill tok/s + decode µs/step at 128K–1M ctx; % of HBM/MFMA roofline"
 HBM_PEAK_GBS = 8000.0
 BF16_MFMA_PEAK_TFLOPS = 2500.0
+ALL_LEGS = ("chunked", "backward", "distill", "prefill32k", "companion", "decode", "offload",
+            "stack", "cpu")
 
-# HBM traffic of one sparse_attn_prefill launch on the 128K chunked workload,
-# from two rocprofv3 --pmc runs of `bench.py --only prefill` (FETCH_SIZE, then
-# WRITE_SIZE, KiB per dispatch), each scaled by what the same counter reads for
-# a plain 1 GiB device copy (`bench.py --calibrate-copy`: FETCH_SIZE reads
-# 524,302 KiB for 1 GiB read -> x2.0; WRITE_SIZE reads 1 GiB -> x1.0).  The
-# figures belong to the attention source with this SHA-1; for any other source
-# `traffic` is reported as null until the counters are taken again.
+# Bytes that went past the L2 (to the Infinity Cache or HBM) in one
+# sparse_attn_prefill launch on the 128K chunked workload, from rocprofv3
+# --pmc runs of `bench.py --legs chunked --steps 3 --warmup 1`:
+# 32*TCC_EA0_RDREQ_32B + 64*TCC_EA0_RDREQ_64B + 128*TCC_EA0_RDREQ_128B read,
+# 64*TCC_EA0_WRREQ_64B + 32*(TCC_EA0_WRREQ - TCC_EA0_WRREQ_64B) written, each
+# scaled by what the same counters give for a plain 1 GiB device copy
+# (`bench.py --calibrate-copy`).  They belong to the attention source with
+# this SHA-1; for any other source `traffic` is null until they are retaken.
 ATTN_COUNTERS = {
-    "source_sha1": "38e5ddb5601b98a9acf4f1ad2fcc2296dd7e3e68",
-    "fetch_kib": 15017750.0, "write_kib": 66673.4,
-    "fetch_scale": 2.0, "write_scale": 1.0,
+    "source_sha1": None,
+    "read_bytes": None, "write_bytes": None,
+    "read_scale": 1.0, "write_scale": 1.0,
 }
 
 
@@ -55,7 +70,7 @@ def attn_source_digest() -> str:
     """sha1 over the sources the prefill attention kernel is compiled from."""
     import hashlib
     h = hashlib.sha1()
-    for f in ("attn.hip", "attn_tile.h"):
+    for f in ("attn.hip", "attn_tile.h", "qsa_common.h"):
         with open(os.path.join(ROOT, "block_sparse_trainable_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()
@@ -63,43 +78,38 @@ def attn_source_digest() -> str:
 
 def attn_traffic_bytes():
     c = ATTN_COUNTERS
-    if attn_source_digest() != c["source_sha1"]:
+    if c["source_sha1"] is None or attn_source_digest() != c["source_sha1"]:
         return None
-    return (c["fetch_kib"] * c["fetch_scale"] + c["write_kib"] * c["write_scale"]) * 1024.0
+    return c["read_bytes"] * c["read_scale"] + c["write_bytes"] * c["write_scale"]
 
 
 def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-def parse():
+def parse(argv=None):
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", choices=["chunked", "prefill", "companion"], default="chunked",
-                    help="prefill workload: 2 x 8K over 128K (default), 32K from empty, or "
-                         "the last 4K queries of a 1M context")
-    ap.add_argument("--decode", choices=["decode", "stack", "none"], default="decode",
-                    help="decode workload: 8 x 256K (default) or the 12-layer 1M-context stack")
-    ap.add_argument("--only", choices=["prefill", "decode"], default=None,
-                    help="profile one leg only (the JSON line then carries that leg)")
+    ap.add_argument("--legs", default=",".join(ALL_LEGS),
+                    help="comma-separated subset of " + ",".join(ALL_LEGS))
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run only a plain 1 GiB device-to-device copy (3 times), the "
                          "known-size reference for scaling HBM byte counters")
     ap.add_argument("--decode-steps", type=int, default=64)
     ap.add_argument("--block-size", type=int, default=4,
                     help="r of the chunked prefill workload (4 = the pages' configuration)")
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--backward", action=argparse.BooleanOptionalAction, default=True,
-                    help="also time the sparse attention backward on the prefill workload")
-    ap.add_argument("--offload", action=argparse.BooleanOptionalAction, default=True,
-                    help="also time decode with the KV history in pinned host memory")
-    ap.add_argument("--distill", action=argparse.BooleanOptionalAction, default=True,
-                    help="also time the stage-1 indexer distillation on the prefill workload")
-    ap.add_argument("--cpu-rows", type=int, default=2304,
-                    help="query rows in the oracle's timed sample")
-    return ap.parse_args()
+    ap.add_argument("--cpu-rows", type=int, default=4096,
+                    help="query rows in the oracle's timed sample of the chunked workload")
+    ap.add_argument("--cpu-workers", type=int, default=0,
+                    help="oracle worker processes (0: one per usable core, at most 16)")
+    a = ap.parse_args(argv)
+    a.legs = [l for l in a.legs.split(",") if l]
+    bad = [l for l in a.legs if l not in ALL_LEGS]
+    if bad:
+        ap.error(f"unknown legs {bad}")
+    return a
 
 
 # ------------------------------------------------------------ workloads ----
@@ -141,82 +151,9 @@ def score_pairs(x) -> int:
     return tot
 
 
-# ---------------------------------------------------------------- prefill --
-def bench_prefill(args, torch):
-    from block_sparse_trainable_amd.runtime import DeviceLayer
-    t0 = time.time()
-    x, cfg = make_prefill_inputs(args.workload, args.block_size)
-    log(f"generated {x.name} in {time.time() - t0:.1f}s")
-    dl = DeviceLayer(x, "cuda:0")
-    dl.build_prefix(x.cache_len)
-    torch.cuda.synchronize()
-    outs = dl.alloc_prefill_outputs()
-    sel, cnt, scs, out, lse = outs
-    r = x.layout.block_size
-    q_pos0 = dl.i32(x.q_pos0)
-    cache_len = dl.i32(x.cache_len)
-    end_np = x.q_pos0.astype(np.int64) + x.n_q
-    end = dl.i32(end_np)
-    max_pos_end = int(end_np.max())
-    new_blocks = int((end_np // r - x.cache_len // r).max())
-    ev = lambda: torch.cuda.Event(enable_timing=True)
-
-    def step(rec=None):
-        e = [ev() for _ in range(4)] if rec is not None else None
-        if e: e[0].record()
-        dl.index_build(cache_len, end, new_blocks)
-        if e: e[1].record()
-        dl.select(dl.q_idx, q_pos0, max_pos_end, sel, cnt, scs)
-        if e: e[2].record()
-        dl.attend_prefill(dl.q, q_pos0, max_pos_end, sel, cnt, out, lse)
-        if e:
-            e[3].record()
-            rec.append(e)
-
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    log("prefill warm")
-    recs = []
-    start, stop = ev(), ev()
-    torch.cuda.synchronize()
-    start.record()
-    for _ in range(args.steps):
-        step(recs)
-    stop.record()
-    torch.cuda.synchronize()
-    total_ms = start.elapsed_time(stop)
-    ms = total_ms / args.steps
-    build_ms = np.mean([e[0].elapsed_time(e[1]) for e in recs])
-    select_ms = np.mean([e[1].elapsed_time(e[2]) for e in recs])
-    attn_ms = np.mean([e[2].elapsed_time(e[3]) for e in recs])
-    toks = x.batch * x.n_q
-    visits = token_visits(x)
-    pairs = score_pairs(x)
-    attn_bytes = visits * x.layout.kv_heads * x.layout.head_dim * 2 * 2
-    res = {
-        "ms_per_step": ms, "tok_s": toks / (ms / 1e3), "tokens": toks,
-        "stages_ms": {"index_build": build_ms, "score_select": select_ms,
-                      "sparse_attn_prefill": attn_ms},
-        "attn_bytes": attn_bytes, "token_visits": visits, "score_pairs": pairs,
-        "score_flops": pairs * 2 * x.layout.idx_heads * x.layout.idx_dim,
-    }
-    if args.backward:
-        res["backward"] = bench_backward(args, torch, x, dl, outs, q_pos0, max_pos_end)
-    if args.distill:
-        res["distill"] = bench_distill(args, torch, x, dl, q_pos0, max_pos_end)
-    cfg.update({"q_heads": x.layout.q_heads, "kv_heads": x.layout.kv_heads,
-                "head_dim": x.layout.head_dim, "token_budget": x.layout.token_budget,
-                "block_size": r, "idx_heads": x.layout.idx_heads, "idx_dim": x.layout.idx_dim})
-    del dl, outs
-    torch.cuda.empty_cache()
-    return x, cfg, res
-
-
-# --------------------------------------------------------------- backward --
 def group_entries(x, sel, cnt) -> int:
-    """(query, 16-token group) pairs of the token sets: the key side's work
-    items, each reading the query's transposed q and dO once."""
+    """(query, 16-token group) pairs of the token sets: the backward key
+    side's work items, each reading the query's transposed q and dO once."""
     r, kB = x.layout.block_size, x.layout.k_blocks
     m = r // 4
     tot = 0
@@ -233,9 +170,133 @@ def group_entries(x, sel, cnt) -> int:
     return tot
 
 
-def bench_backward(args, torch, x, dl, outs, q_pos0, max_pos_end):
+def _ev(torch):
+    return torch.cuda.Event(enable_timing=True)
+
+
+# ---------------------------------------------------------------- prefill --
+def bench_prefill(args, torch, name, keep=False):
+    """index_build + select_topk + sparse_attn_prefill over one chunk, timed
+    per stage.  keep: also return the device layer and outputs (for the
+    backward, distillation and cold-attention legs)."""
+    from block_sparse_trainable_amd.runtime import DeviceLayer
+    t0 = time.time()
+    x, cfg = make_prefill_inputs(name, args.block_size if name == "chunked" else 4)
+    log(f"generated {x.name} in {time.time() - t0:.1f}s")
+    dl = DeviceLayer(x, "cuda:0")
+    dl.build_prefix(x.cache_len)
+    torch.cuda.synchronize()
+    outs = dl.alloc_prefill_outputs()
+    sel, cnt, scs, out, lse = outs
+    r = x.layout.block_size
+    q_pos0 = dl.i32(x.q_pos0)
+    cache_len = dl.i32(x.cache_len)
+    end_np = x.q_pos0.astype(np.int64) + x.n_q
+    end = dl.i32(end_np)
+    max_pos_end = int(end_np.max())
+    new_blocks = int((end_np // r - x.cache_len // r).max())
+
+    def step(rec=None):
+        e = [_ev(torch) for _ in range(4)] if rec is not None else None
+        if e: e[0].record()
+        dl.index_build(cache_len, end, new_blocks)
+        if e: e[1].record()
+        dl.select(dl.q_idx, q_pos0, max_pos_end, sel, cnt, scs)
+        if e: e[2].record()
+        dl.attend_prefill(dl.q, q_pos0, max_pos_end, sel, cnt, out, lse)
+        if e:
+            e[3].record()
+            rec.append(e)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    recs = []
+    start, stop = _ev(torch), _ev(torch)
+    torch.cuda.synchronize()
+    start.record()
+    for _ in range(args.steps):
+        step(recs)
+    stop.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(stop) / args.steps
+    build_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in recs]))
+    select_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in recs]))
+    attn_ms = float(np.mean([e[2].elapsed_time(e[3]) for e in recs]))
+    lay = x.layout
+    toks = x.batch * x.n_q
+    visits = token_visits(x)
+    pairs = score_pairs(x)
+    gather = visits * lay.kv_heads * lay.head_dim * 2 * 2      # K and V rows, bf16
+    attn_flops = visits * 4 * lay.q_heads * lay.head_dim     # q.k and p.v per head
+    score_flops = pairs * 2 * lay.idx_heads * lay.idx_dim
+    res = {
+        "workload": cfg["workload"], "ms_per_step": ms, "tok_s": toks / (ms / 1e3),
+        "tokens": toks,
+        "stages_ms": {"index_build": build_ms, "score_select": select_ms,
+                      "sparse_attn_prefill": attn_ms},
+        "score_select": {
+            "flops": score_flops,
+            "tflops": score_flops / (select_ms * 1e-3) / 1e12,
+            "mfma_frac": score_flops / (select_ms * 1e-3) / (BF16_MFMA_PEAK_TFLOPS * 1e12),
+            "note": "scoring and top-k together (one call, two kernels); scoring's own "
+                    "fraction is in the kernel statistics"},
+        "attention": {
+            "token_visits": visits, "flops": attn_flops, "avg_launch_ms": attn_ms,
+            "mfma_frac": attn_flops / (attn_ms * 1e-3) / (BF16_MFMA_PEAK_TFLOPS * 1e12),
+            "gather_bytes": gather, "gather_gbs": gather / (attn_ms * 1e-3) / 1e9,
+            "note": "gather_gbs counts every token visit's K/V rows; rows gathered again "
+                    "by other queries are served from L2 or the Infinity Cache, so it can "
+                    "exceed the HBM peak"},
+    }
+    cfg.update({"q_heads": lay.q_heads, "kv_heads": lay.kv_heads, "head_dim": lay.head_dim,
+                "token_budget": lay.token_budget, "block_size": r, "idx_heads": lay.idx_heads,
+                "idx_dim": lay.idx_dim})
+    log(f"{cfg['workload']}: {res['tok_s']:.0f} tok/s, {ms:.3f} ms/step, stages "
+        f"{ {k: round(v, 4) for k, v in res['stages_ms'].items()} }")
+    if keep:
+        return x, cfg, res, (dl, outs, q_pos0, max_pos_end)
+    del dl, outs
+    torch.cuda.empty_cache()
+    return x, cfg, res, None
+
+
+def bench_attention_cold(args, torch, x, state):
+    """sparse_attn_prefill alone with launch i on replica i mod 4 of the KV
+    caches (equal values at other addresses): a launch finds nothing of its
+    caches left in the Infinity Cache by the previous one."""
+    from block_sparse_trainable_amd import _binding as B
+    dl, outs, q_pos0, max_pos_end = state
+    sel, cnt, scs, out, lse = outs
+    reps = [(dl.k, dl.v)] + [(dl.k.clone(), dl.v.clone()) for _ in range(3)]
+    ws = dl.workspace(B.QSA_OP_PREFILL, dl.batch, x.n_q, max_pos_end)
+
+    def call(i):
+        k, v = reps[i % 4]
+        B.qsa_sparse_attn_prefill(dl.cfg, dl.batch, x.n_q, dl.q, k, v, dl.cap, q_pos0,
+                                  max_pos_end, sel, cnt, out, lse, ws, ws.numel())
+
+    for i in range(4):
+        call(i)
+    torch.cuda.synchronize()
+    n = 4 * max(1, args.steps // 4)
+    start, stop = _ev(torch), _ev(torch)
+    start.record()
+    for i in range(n):
+        call(i)
+    stop.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(stop) / n
+    del reps
+    torch.cuda.empty_cache()
+    return ms
+
+
+# --------------------------------------------------------------- backward --
+def bench_backward(args, torch, x, state):
     """Gradients of the chunk's sparse attention (dq, dK, dV) for a seeded
     dL/dout, on the forward's own selections."""
+    dl, outs, q_pos0, max_pos_end = state
     sel, cnt, scs, out, lse = outs
     g = torch.Generator(device="cuda:0")
     g.manual_seed(5)
@@ -250,7 +311,7 @@ def bench_backward(args, torch, x, dl, outs, q_pos0, max_pos_end):
     for _ in range(2):
         call()
     torch.cuda.synchronize()
-    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start, stop = _ev(torch), _ev(torch)
     start.record()
     for _ in range(args.steps):
         call()
@@ -259,7 +320,8 @@ def bench_backward(args, torch, x, dl, outs, q_pos0, max_pos_end):
     ms = start.elapsed_time(stop) / args.steps
     lay = x.layout
     visits = token_visits(x)
-    entries = group_entries(x, sel.cpu().numpy(), cnt.cpu().numpy())
+    sel_np, cnt_np = sel.cpu().numpy(), cnt.cpu().numpy()
+    entries = group_entries(x, sel_np, cnt_np)
     rows = x.batch * x.n_q
     row_bytes = lay.q_heads * lay.head_dim * 2          # one bf16 row of q, dO, out or dq
     kd = lay.kv_heads * lay.head_dim
@@ -271,20 +333,23 @@ def bench_backward(args, torch, x, dl, outs, q_pos0, max_pos_end):
     }
     tot = sum(parts.values())
     log(f"backward {ms:.3f} ms/call, {entries} group entries")
-    cpu = None if args.no_cpu_baseline else cpu_baseline_backward(
-        x, sel.cpu().numpy(), cnt.cpu().numpy(), dout.float().cpu().numpy(), 96)
-    return {"ms_per_call": ms, "tok_s": rows / (ms / 1e3), "token_visits": visits,
-            "cpu_baseline": cpu,
+    flops = visits * lay.q_heads * lay.head_dim * 2 * 4   # S, dP, dq, dK/dV: four contractions
+    dout_np = dout.float().cpu().numpy()
+    return {"ms_per_call": ms, "rows_per_s": rows / (ms / 1e3), "token_visits": visits,
             "group_entries": entries, "algorithmic_bytes": parts,
             "achieved_gbs": tot / (ms * 1e-3) / 1e9,
-            "hbm_frac": tot / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
+            "mfma_frac": flops / (ms * 1e-3) / (BF16_MFMA_PEAK_TFLOPS * 1e12),
+            "note": "algorithmic bytes count every gather and re-read; most re-reads hit "
+                    "L2 or the Infinity Cache, so achieved_gbs is not an HBM rate"}, \
+        (sel_np, cnt_np, dout_np)
 
 
 # ---------------------------------------------------------------- distill --
-def bench_distill(args, torch, x, dl, q_pos0, max_pos_end):
+def bench_distill(args, torch, x, state):
     """Stage-1 indexer distillation on the chunk: the dense teacher over
     tokens 0..p of every query (two passes), the student over its candidate
     blocks, dq_idx and dk_cmp."""
+    dl, outs, q_pos0, max_pos_end = state
     lay = x.layout
     loss = torch.empty((x.batch, x.n_q), dtype=torch.float32, device="cuda:0")
     dq_idx = torch.empty((x.batch, x.n_q, lay.idx_heads, lay.idx_dim), dtype=torch.float32,
@@ -297,7 +362,7 @@ def bench_distill(args, torch, x, dl, q_pos0, max_pos_end):
     call()
     torch.cuda.synchronize()
     n = max(1, min(args.steps, 3))
-    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start, stop = _ev(torch), _ev(torch)
     start.record()
     for _ in range(n):
         call()
@@ -314,9 +379,7 @@ def bench_distill(args, torch, x, dl, q_pos0, max_pos_end):
     teacher = visits * per_tok + cand * r * per_tok     # pass 1 over 0..p, pass 2 over candidates
     student = cand * 2 * lay.idx_heads * lay.idx_dim * 4   # dots twice, dq_idx, dk_cmp
     log(f"distill {ms:.3f} ms/call")
-    cpu = None if args.no_cpu_baseline else cpu_baseline_distill(x, 8)
     return {"ms_per_call": ms, "rows_per_s": x.batch * x.n_q / (ms / 1e3),
-            "cpu_baseline": cpu,
             "teacher_token_visits": visits, "candidate_pairs": cand,
             "flops": {"teacher": teacher, "student": student},
             "mfma_frac": (teacher + student) / (ms * 1e-3) / (BF16_MFMA_PEAK_TFLOPS * 1e12),
@@ -324,12 +387,24 @@ def bench_distill(args, torch, x, dl, q_pos0, max_pos_end):
 
 
 # ----------------------------------------------------------------- decode --
-def bench_decode(args, torch):
+def _graph_us(torch, g, steps, reps=5):
+    g.replay()
+    torch.cuda.synchronize()
+    s0, s1 = _ev(torch), _ev(torch)
+    s0.record()
+    for _ in range(reps):
+        g.replay()
+    s1.record()
+    torch.cuda.synchronize()
+    return s0.elapsed_time(s1) * 1e3 / (reps * steps)
+
+
+def bench_decode(args, torch, with_offload):
     """Decode loop: `steps` steps of index_build + select_topk + attention for
     8 sequences at 256K context, as one fused launch per step
     (qsa_decode_step) and as the three separate calls (several scheduling
-    variants), each captured in one HIP graph and replayed; the best is
-    reported, eager per-step times beside it."""
+    variants), each captured in one HIP graph and replayed; the fused graph
+    is reported, the others and eager per-step times beside it."""
     from block_sparse_trainable_amd import synth
     from block_sparse_trainable_amd.runtime import DeviceLayer
     steps = args.decode_steps
@@ -345,7 +420,7 @@ def bench_decode(args, torch):
         dl.decode_step(plan, t, outs)
     torch.cuda.synchronize()
     # eager, per-step events
-    evs = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    evs = [_ev(torch) for _ in range(steps + 1)]
     evs[0].record()
     for t in range(steps):
         dl.decode_step(plan, t, outs)
@@ -365,61 +440,41 @@ def bench_decode(args, torch):
     per_f = np.array([evs[t].elapsed_time(evs[t + 1]) for t in range(steps)]) * 1e3
     fused_eager_us = evs[0].elapsed_time(evs[-1]) * 1e3 / steps
     dl.check_step()     # raises (the run fails) if a wait for a selection gave up
-    # graph replay, for each scheduling variant; the best one is reported
     variants = {}
     for name, kw in (("fused", None), ("inline-build", {}), ("side-build", {"overlap_build": True}),
                      ("2-branch", {"branches": 2}), ("4-branch", {"branches": 4})):
-        if kw is None:
-            g = dl.capture_decode_fused(plan, steps, outs)
-        else:
-            g = dl.capture_decode(plan, steps, outs, **kw)
-        g.replay()
-        torch.cuda.synchronize()
-        reps = 5
-        s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        s0.record()
-        for _ in range(reps):
-            g.replay()
-        s1.record()
-        torch.cuda.synchronize()
-        variants[name] = s0.elapsed_time(s1) * 1e3 / (reps * steps)
+        g = dl.capture_decode_fused(plan, steps, outs) if kw is None else \
+            dl.capture_decode(plan, steps, outs, **kw)
+        variants[name] = _graph_us(torch, g, steps)
         if kw is None:
             dl.check_step()
         del g
-    log(f"decode graph variants (us/step): {variants}")
-    best = min(variants, key=variants.get)
-    graph_us = variants[best]
+    log(f"decode graph variants (us/step): { {k: round(v, 2) for k, v in variants.items()} }")
+    graph_us = variants["fused"]
     # cold: the fused graph with step t on replica t % 4 of the caches (equal
     # values, other addresses), so the ~600 MB working set cannot stay in the
     # 256 MB Infinity Cache; every replica holds every block the steps touch
     reps = [dl] + [dl.replica() for _ in range(3)]
     ws = dl.step_workspace(plan[4])
-    for r in reps:
+    for rr in reps:
         for t in range(min(8, steps)):
-            r.decode_step_fused(plan, t, outs, ws)
+            rr.decode_step_fused(plan, t, outs, ws)
     torch.cuda.synchronize()
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
         for t in range(steps):
             reps[t % 4].decode_step_fused(plan, t, outs, ws)
-    g.replay()
-    torch.cuda.synchronize()
-    s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    s0.record()
-    for _ in range(5):
-        g.replay()
-    s1.record()
-    torch.cuda.synchronize()
-    cold_us = s0.elapsed_time(s1) * 1e3 / (5 * steps)
+    cold_us = _graph_us(torch, g, steps)
     dl.check_step(ws)
     del g, reps
-    log(f"decode fused, 4 rotating cache replicas: {cold_us:.1f} us/step")
+    log(f"decode fused {graph_us:.1f} us/step, cold (4 rotating cache replicas) {cold_us:.1f}")
     kB = x.layout.k_blocks
     ctx = x.q_pos0.astype(np.int64)
     scan_bytes = int(sum((ctx[s] + t) // 4 for s in range(x.batch) for t in range(steps))) * 256 // steps
     gather = int(x.batch * (4 * kB + 4) * x.layout.kv_heads * x.layout.head_dim * 4)
+    alg = scan_bytes + gather
     res = {"workload": "decode-256k", "batch": x.batch, "context": int(ctx.min()),
-           "steps": steps, "us_per_step": graph_us, "mode": f"hip-graph ({best})",
+           "steps": steps, "us_per_step": graph_us, "mode": "hip-graph (fused)",
            "graph_variants_us": variants,
            "eager_us_per_step": eager_us,
            "eager_p50_us": float(np.percentile(per, 50)),
@@ -427,12 +482,12 @@ def bench_decode(args, torch):
            "fused_eager_us_per_step": fused_eager_us,
            "fused_eager_p50_us": float(np.percentile(per_f, 50)),
            "fused_eager_p99_us": float(np.percentile(per_f, 99)),
-           "algorithmic_bytes_per_step": scan_bytes + gather,
-           "hbm_frac": (scan_bytes + gather) / (graph_us * 1e-6) / (HBM_PEAK_GBS * 1e9),
            "step_error_word": dl.step_error_word(ws),
+           "algorithmic_bytes_per_step": alg,
+           "hbm_frac": alg / (graph_us * 1e-6) / (HBM_PEAK_GBS * 1e9),
            "cold_4_replicas_us_per_step": cold_us,
-           "cold_hbm_frac": (scan_bytes + gather) / (cold_us * 1e-6) / (HBM_PEAK_GBS * 1e9)}
-    if args.offload:
+           "cold_hbm_frac": alg / (cold_us * 1e-6) / (HBM_PEAK_GBS * 1e9)}
+    if with_offload:
         res["offload"] = bench_offload(args, torch, x, dl, plan, steps)
     del dl, outs
     torch.cuda.empty_cache()
@@ -451,11 +506,9 @@ def bench_offload(args, torch, x, dl, plan, steps):
     for t in range(min(4, steps)):
         off.decode_step(plan, t, outs)
     torch.cuda.synchronize()
-    ev = lambda: torch.cuda.Event(enable_timing=True)
-    # eager, with the per-step hit and miss counts
     off.hot_tag.fill_(-1)
     recs = []
-    start, stop = ev(), ev()
+    start, stop = _ev(torch), _ev(torch)
     start.record()
     for t in range(steps):
         off.decode_step(plan, t, outs)
@@ -465,20 +518,12 @@ def bench_offload(args, torch, x, dl, plan, steps):
     eager_us = start.elapsed_time(stop) * 1e3 / steps
     tot = torch.stack(recs).sum(0).cpu().numpy()
     hits, miss = int(tot[0]), int(tot[1])
-    # the same run captured in one HIP graph
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
         off.hot_tag.fill_(-1)
         for t in range(steps):
             off.decode_step(plan, t, outs)
-    g.replay()
-    torch.cuda.synchronize()
-    start.record()
-    for _ in range(3):
-        g.replay()
-    stop.record()
-    torch.cuda.synchronize()
-    graph_us = start.elapsed_time(stop) * 1e3 / (3 * steps)
+    graph_us = _graph_us(torch, g, steps, reps=3)
     unit_bytes = 4 * x.layout.kv_heads * x.layout.head_dim * 2 * 2   # K and V of 4 tokens
     host_bytes = miss * unit_bytes / steps
     log(f"decode offloaded: {graph_us:.1f} us/step (graph), {eager_us:.1f} eager, "
@@ -496,32 +541,36 @@ def bench_stack_decode(args, torch):
     context, batch 1: each step runs the fused decode step of every layer in
     turn (a layer's input depends on the previous layer's output in a model,
     so the layers are not overlapped).  `steps` steps in one HIP graph."""
+    from concurrent.futures import ThreadPoolExecutor
     from block_sparse_trainable_amd import synth
     from block_sparse_trainable_amd.runtime import DeviceLayer
     steps = args.decode_steps
     n_layers = 12
-    layers = []
     t0 = time.time()
-    for l in range(n_layers):
-        x = synth.stack_layer(l, steps=steps)
-        dl = DeviceLayer(x, "cuda:0")
-        dl.build_prefix(x.cache_len)
-        plan = dl.decode_plan(steps)
-        outs = dl.alloc_decode_outputs()
-        ws = dl.step_workspace(plan[4])
-        scan = int(sum((int(x.q_pos0[0]) + t) // 4 for t in range(steps))) * 256 // steps
-        kB = x.layout.k_blocks
-        gather = int((4 * kB + 4) * x.layout.kv_heads * x.layout.head_dim * 4)
-        dl.x = None  # host copies are no longer needed
-        layers.append((dl, plan, outs, ws, scan + gather))
-        del x
-        torch.cuda.synchronize()
-        log(f"stack layer {l} ready ({time.time() - t0:.0f}s)")
+    layers = []
+    with ThreadPoolExecutor(min(n_layers, max(1, len(os.sched_getaffinity(0))))) as ex:
+        futs = [ex.submit(synth.stack_layer, l, steps=steps) for l in range(n_layers)]
+        for l in range(n_layers):
+            x = futs[l].result()
+            futs[l] = None
+            dl = DeviceLayer(x, "cuda:0")
+            dl.build_prefix(x.cache_len)
+            plan = dl.decode_plan(steps)
+            outs = dl.alloc_decode_outputs()
+            ws = dl.step_workspace(plan[4])
+            scan = int(sum((int(x.q_pos0[0]) + t) // 4 for t in range(steps))) * 256 // steps
+            kB = x.layout.k_blocks
+            gather = int((4 * kB + 4) * x.layout.kv_heads * x.layout.head_dim * 4)
+            dl.x = None  # host copies are no longer needed
+            layers.append((dl, plan, outs, ws, scan + gather))
+            del x
+    torch.cuda.synchronize()
+    log(f"stack: 12 layers generated and uploaded in {time.time() - t0:.0f}s")
     for t in range(min(4, steps)):
         for dl, plan, outs, ws, _ in layers:
             dl.decode_step_fused(plan, t, outs, ws)
     torch.cuda.synchronize()
-    evs = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    evs = [_ev(torch) for _ in range(steps + 1)]
     evs[0].record()
     for t in range(steps):
         for dl, plan, outs, ws, _ in layers:
@@ -535,20 +584,12 @@ def bench_stack_decode(args, torch):
         for t in range(steps):
             for dl, plan, outs, ws, _ in layers:
                 dl.decode_step_fused(plan, t, outs, ws)
-    g.replay()
-    torch.cuda.synchronize()
-    reps = 3
-    s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    s0.record()
-    for _ in range(reps):
-        g.replay()
-    s1.record()
-    torch.cuda.synchronize()
-    graph_us = s0.elapsed_time(s1) * 1e3 / (reps * steps)
+    graph_us = _graph_us(torch, g, steps, reps=3)
     for dl, plan, outs, ws, _ in layers:
         dl.check_step(ws)
     err_words = sum(dl.step_error_word(ws) for dl, plan, outs, ws, _ in layers)
     bytes_step = sum(b for *_, b in layers)
+    log(f"stack 12 x 1M: {graph_us:.1f} us/step")
     res = {"workload": "stack-12x1m-decode", "layers": n_layers, "batch": 1,
            "context": 1048576, "steps": steps, "us_per_step": graph_us,
            "mode": "hip-graph (fused, layers in sequence)", "step_error_word": err_words,
@@ -562,130 +603,160 @@ def bench_stack_decode(args, torch):
 
 
 # ------------------------------------------------------------ cpu oracle --
-def cpu_baseline(x, rows: int):
-    """The fp64 oracle on a bounded sample of the same chunk: compression of
-    every new block of the chunk, then `rows` query rows (scoring, top-k,
-    attention), single-threaded; extrapolated to the full chunk."""
+# The oracle runs in worker processes started fresh (spawn: they never touch
+# the GPU), one per usable core.  The parent writes each sequence's inputs as
+# .npy files that the workers memory-map; a task is one query row.
+_OW = None
+
+
+def _oracle_init(paths, meta):
+    global _OW
+    _OW = {"meta": meta}
+    for k, p in paths.items():
+        _OW[k] = np.load(p, mmap_mode="r")
+
+
+def _oracle_task(task):
+    from oracle import qsa_oracle as O
+    kind, s, j = task
+    W, meta = _OW, _OW["meta"]
+    p = int(meta["q_pos0"][s]) + j
+    r, kB, scale = meta["r"], meta["k_B"], meta["scale"]
+    t = time.perf_counter()
+    if kind == "fwd":
+        O.qsa_row(p, W[f"qi{s}"][j], W[f"q{s}"][j], W[f"kh{s}"], W[f"K{s}"], W[f"V{s}"],
+                  k_B=kB, r=r)
+    elif kind == "bwd":
+        n = int(W[f"cnt{s}"][j])
+        S = O.expand_with_tail(np.sort(np.asarray(W[f"sel{s}"][j, :n])), p, r)
+        key = f"dK{s}"
+        if key not in W:   # the accumulators of this worker
+            W[key] = np.zeros(W[f"K{s}"].shape)
+            W[f"dV{s}"] = np.zeros(W[f"V{s}"].shape)
+        O.sparse_attention_backward(W[f"q{s}"][j], W[f"K{s}"], W[f"V{s}"], S,
+                                    W[f"dout{s}"][j], scale, W[key], W[f"dV{s}"])
+    else:  # "distill"
+        tb = O.teacher_block_target(W[f"q{s}"][j], W[f"K{s}"], p, r, scale)
+        I = O.block_importance(W[f"qi{s}"][j], W[f"kh{s}"], p // r)
+        _, dI = O.distill_row(tb, I)
+        O.distill_grads(W[f"qi{s}"][j], W[f"kh{s}"], dI)
+    return time.perf_counter() - t
+
+
+def _pool_size(args):
+    n = len(os.sched_getaffinity(0))
+    return max(1, min(n, 16) if args.cpu_workers <= 0 else args.cpu_workers)
+
+
+def cpu_baselines(args, x, bwd_data):
+    """The fp64 oracle, as it stands, on bounded seeded samples of the
+    headline chunk: the forward (compression of the chunk's new blocks in
+    this process, then `cpu_rows` query rows: scoring, top-k, attention),
+    and, when their legs ran, the backward (on the GPU's selections) and the
+    distillation."""
+    import multiprocessing as mp
+    from concurrent.futures import ProcessPoolExecutor
     from threadpoolctl import threadpool_limits
     from oracle import qsa_oracle as O
     from block_sparse_trainable_amd import synth
     lay = x.layout
-    f64 = lambda a: synth.as_f32(a, lay.dtype).astype(np.float64)
-    rng = np.random.default_rng(7)
-    with threadpool_limits(limits=1):
-        t_comp = 0.0
-        khat = []
-        for s in range(x.batch):
-            # the cached prefix is setup work on both sides; only the chunk's
-            # new blocks are timed
-            nb_all = (int(x.q_pos0[s]) + x.n_q) // lay.block_size
-            nb_old = int(x.cache_len[s]) // lay.block_size
-            k_idx = f64(x.k_idx[s, :nb_all * lay.block_size])
-            r = lay.block_size
-            kh_old = O.compress_index(k_idx[:nb_old * r], nb_old, r=r,
-                                      gain=x.gain.astype(np.float64),
-                                      eps=float(np.float32(lay.rms_eps)), storage=lay.dtype)
-            t = time.perf_counter()
-            kh_all = O.compress_index(k_idx, nb_all, r=r, gain=x.gain.astype(np.float64),
-                                      eps=float(np.float32(lay.rms_eps)), storage=lay.dtype)
-            t_comp += (time.perf_counter() - t) * (nb_all - nb_old) / max(nb_all, 1)
-            khat.append(kh_all)
-            del kh_old
-        per_seq = max(1, rows // x.batch)
-        t_rows = 0.0
-        n_rows = 0
-        for s in range(x.batch):
-            K, V = f64(x.k[s]), f64(x.v[s])
-            q_idx, q = f64(x.q_idx[s]), f64(x.q[s])
-            for j in rng.choice(x.n_q, size=min(per_seq, x.n_q), replace=False):
-                p = int(x.q_pos0[s]) + int(j)
-                t = time.perf_counter()
-                O.qsa_row(p, q_idx[j], q[j], khat[s], K, V, k_B=lay.k_blocks, r=lay.block_size)
-                t_rows += time.perf_counter() - t
-                n_rows += 1
-    total = x.batch * x.n_q
-    est = t_comp + t_rows * total / n_rows
-    return {"value": total / est, "unit": "tok/s", "cores": 1, "kind": "oracle",
-            "sample": (f"{n_rows} of {total} query rows (uniform seeded sample) plus the "
-                       f"compression of the chunk's new blocks, single thread; extrapolated "
-                       f"to the full chunk"),
-            "measured_s": t_comp + t_rows}
-
-
-def _sample_rows(x, rows, seed):
-    rng = np.random.default_rng(seed)
-    per = max(1, rows // x.batch)
-    return [(s, int(j)) for s in range(x.batch)
-            for j in rng.choice(x.n_q, size=min(per, x.n_q), replace=False)]
-
-
-def cpu_baseline_backward(x, sel, cnt, dout, rows: int):
-    """The oracle's attention backward on a seeded sample of query rows (the
-    GPU's selections), single-threaded; extrapolated to every row."""
-    from threadpoolctl import threadpool_limits
-    from oracle import qsa_oracle as O
-    from block_sparse_trainable_amd import synth
-    lay = x.layout
-    f64 = lambda a: synth.as_f32(a, lay.dtype).astype(np.float64)
-    scale = 1.0 / math.sqrt(lay.head_dim)
-    sample = _sample_rows(x, rows, 11)
-    t_rows = 0.0
-    with threadpool_limits(limits=1):
-        for s in range(x.batch):
-            K, V, q = f64(x.k[s]), f64(x.v[s]), f64(x.q[s])
-            dK = np.zeros_like(K)
-            dV = np.zeros_like(V)
-            for (ss, j) in sample:
-                if ss != s:
-                    continue
-                p = int(x.q_pos0[s]) + j
-                S = O.expand_with_tail(np.sort(sel[s, j, :int(cnt[s, j])]), p, lay.block_size)
-                t = time.perf_counter()
-                O.sparse_attention_backward(q[j], K, V, S, dout[s, j], scale, dK, dV)
-                t_rows += time.perf_counter() - t
-    total = x.batch * x.n_q
-    return {"value": len(sample) / t_rows, "unit": "query rows/s", "cores": 1, "kind": "oracle",
-            "sample": f"{len(sample)} of {total} query rows (uniform seeded sample), single "
-                      f"thread, on the GPU's selections", "measured_s": t_rows}
-
-
-def cpu_baseline_distill(x, rows: int):
-    """The oracle's distillation (dense teacher target, KL, gradients) on a
-    seeded sample of query rows, single-threaded; extrapolated."""
-    from threadpoolctl import threadpool_limits
-    from oracle import qsa_oracle as O
-    from block_sparse_trainable_amd import synth
-    lay = x.layout
-    f64 = lambda a: synth.as_f32(a, lay.dtype).astype(np.float64)
-    scale = 1.0 / math.sqrt(lay.head_dim)
     r = lay.block_size
-    sample = _sample_rows(x, rows, 12)
-    t_rows = 0.0
-    with threadpool_limits(limits=1):
-        for s in range(x.batch):
-            end = int(x.q_pos0[s]) + x.n_q
-            kh = O.compress_index(f64(x.k_idx[s, :(end // r) * r]), end // r, r=r,
-                                  gain=x.gain.astype(np.float64),
-                                  eps=float(np.float32(lay.rms_eps)), storage=lay.dtype)
-            K, q, qi = f64(x.k[s]), f64(x.q[s]), f64(x.q_idx[s])
-            for (ss, j) in sample:
-                if ss != s:
-                    continue
-                p = int(x.q_pos0[s]) + j
+    f32 = lambda a: synth.as_f32(a, lay.dtype)
+    workers = _pool_size(args)
+    host = {"sched_getaffinity": len(os.sched_getaffinity(0)), "cpu_count": os.cpu_count()}
+    tmp = tempfile.mkdtemp(prefix="qsa_oracle_",
+                           dir="/dev/shm" if os.path.isdir("/dev/shm") else None)
+    try:
+        paths = {}
+
+        def put(name, arr):
+            paths[name] = os.path.join(tmp, name + ".npy")
+            np.save(paths[name], np.ascontiguousarray(arr))
+
+        t_comp = 0.0
+        with threadpool_limits(limits=1):
+            for s in range(x.batch):
+                nb_all = (int(x.q_pos0[s]) + x.n_q) // r
+                nb_old = int(x.cache_len[s]) // r
+                k_idx = f32(x.k_idx[s, :nb_all * r]).astype(np.float64)
                 t = time.perf_counter()
-                tb = O.teacher_block_target(q[j], K, p, r, scale)
-                I = O.block_importance(qi[j], kh, p // r)
-                _, dI = O.distill_row(tb, I)
-                O.distill_grads(qi[j], kh, dI)
-                t_rows += time.perf_counter() - t
-    total = x.batch * x.n_q
-    return {"value": len(sample) / t_rows, "unit": "query rows/s", "cores": 1, "kind": "oracle",
-            "sample": f"{len(sample)} of {total} query rows (uniform seeded sample), single "
-                      f"thread", "measured_s": t_rows}
+                kh = O.compress_index(k_idx, nb_all, r=r, gain=x.gain.astype(np.float64),
+                                      eps=float(np.float32(lay.rms_eps)), storage=lay.dtype)
+                # the cached prefix is setup work on both sides: only the
+                # chunk's new blocks are charged
+                t_comp += (time.perf_counter() - t) * (nb_all - nb_old) / max(nb_all, 1)
+                put(f"kh{s}", kh)
+                put(f"K{s}", f32(x.k[s]))
+                put(f"V{s}", f32(x.v[s]))
+                put(f"qi{s}", f32(x.q_idx[s]))
+                put(f"q{s}", f32(x.q[s]))
+                if bwd_data is not None:
+                    sel, cnt, dout = bwd_data
+                    put(f"sel{s}", sel[s])
+                    put(f"cnt{s}", cnt[s])
+                    put(f"dout{s}", dout[s])
+        meta = {"q_pos0": [int(v) for v in x.q_pos0], "r": r, "k_B": lay.k_blocks,
+                "scale": 1.0 / math.sqrt(lay.head_dim)}
+        total = x.batch * x.n_q
+
+        def sample(kind, rows, seed):
+            g = np.random.default_rng(seed)
+            per = max(1, rows // x.batch)
+            return [(kind, s, int(j)) for s in range(x.batch)
+                    for j in g.choice(x.n_q, size=min(per, x.n_q), replace=False)]
+
+        legs = {"fwd": sample("fwd", args.cpu_rows, 7)}
+        if bwd_data is not None:
+            legs["bwd"] = sample("bwd", 16 * workers, 11)
+        if "distill" in args.legs:
+            legs["distill"] = sample("distill", 4 * workers, 12)
+        saved = {k: os.environ.get(k) for k in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS",
+                                                "MKL_NUM_THREADS")}
+        for k in saved:
+            os.environ[k] = "1"
+        out = {}
+        try:
+            # a worker that dies raises BrokenProcessPool here (no silent respawn)
+            with ProcessPoolExecutor(workers, mp_context=mp.get_context("spawn"),
+                                     initializer=_oracle_init,
+                                     initargs=(paths, meta)) as pool:
+                list(pool.map(_oracle_task, [("fwd", 0, 0)] * (2 * workers)))   # warm
+                for kind, tasks in legs.items():
+                    t = time.perf_counter()
+                    busy = sum(pool.map(_oracle_task, tasks))
+                    out[kind] = (len(tasks), time.perf_counter() - t, busy)
+        finally:
+            for k, v in saved.items():
+                if v is None:
+                    os.environ.pop(k, None)
+                else:
+                    os.environ[k] = v
+    finally:
+        shutil.rmtree(tmp, ignore_errors=True)
+    n, wall, busy = out["fwd"]
+    est = t_comp + wall * total / n
+    res = {"cpu_baseline": {
+        "value": total / est, "unit": "tok/s", "cores": workers, "kind": "oracle",
+        "sample": (f"{n} of {total} query rows (uniform seeded sample) on {workers} worker "
+                   f"processes, plus the compression of the chunk's new blocks in one; "
+                   f"extrapolated to the full chunk"),
+        "measured_s": t_comp + wall, "cpu_seconds": t_comp + busy, "host_cores": host}}
+    if "bwd" in out:
+        n, wall, busy = out["bwd"]
+        res["backward"] = {"value": n / wall, "unit": "query rows/s", "cores": workers,
+                           "kind": "oracle", "sample": f"{n} of {total} query rows, on the "
+                           f"GPU's selections", "measured_s": wall, "cpu_seconds": busy}
+    if "distill" in out:
+        n, wall, busy = out["distill"]
+        res["distill"] = {"value": n / wall, "unit": "query rows/s", "cores": workers,
+                          "kind": "oracle", "sample": f"{n} of {total} query rows",
+                          "measured_s": wall, "cpu_seconds": busy}
+    return res
 
 
-def main():
-    args = parse()
+# -------------------------------------------------------------------- main --
+def main(argv=None):
+    args = parse(argv)
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py runs on exactly one GPU: the QSA forward path here is single-GPU "
               "(no sharding or collectives are built); use --gpus 1", file=sys.stderr)
@@ -708,50 +779,68 @@ def main():
         print(json.dumps({"calibration": "copy", "bytes_read_per_launch": n,
                           "bytes_written_per_launch": n, "launches": 3}), flush=True)
         return
-    run_decode = bench_stack_decode if args.decode == "stack" else bench_decode
-    if args.only == "decode":
-        dec = run_decode(args, torch)
-        print(json.dumps({"metric": METRIC, "value": None, "unit": "tok/s", "n_gpus": 1,
-                          "decode": dec, "note": "decode leg only"}), flush=True)
-        return
-    x, cfg, pre = bench_prefill(args, torch)
-    log(f"prefill {pre['tok_s']:.0f} tok/s, {pre['ms_per_step']:.3f} ms/step, "
-        f"stages {pre['stages_ms']}")
-    dec = run_decode(args, torch) if (args.decode != "none" and args.only is None) else None
-    if dec:
-        log(f"decode {dec['us_per_step']:.1f} us/step")
 
-    attn_ms = pre["stages_ms"]["sparse_attn_prefill"]
-    achieved = pre["attn_bytes"] / (attn_ms * 1e-3) / 1e9
-    roofline = {"kernel": "sparse_attn_prefill (attn_mfma_kernel<2,128>)", "bound": "hbm",
-                "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": achieved / HBM_PEAK_GBS, "traffic": attn_traffic_bytes(),
-                "algorithmic_bytes_per_launch": pre["attn_bytes"],
-                "avg_launch_ms": attn_ms,
-                # the gather kernel's own contraction (QK^T and PV: 8,192 flop
-                # per token visit at 16 heads x 128 dims) against the dense
-                # bf16 MFMA peak, for reference: it runs at 8 flop per byte
-                "mfma_frac": pre["token_visits"] * 4 * x.layout.q_heads * x.layout.head_dim
-                             / (attn_ms * 1e-3) / (BF16_MFMA_PEAK_TFLOPS * 1e12)}
-    score_tflops = pre["score_flops"] / (pre["stages_ms"]["score_select"] * 1e-3) / 1e12
-
-    cpu = None
-    if not args.no_cpu_baseline:
-        log("cpu baseline (oracle) ...")
-        cpu = cpu_baseline(x, args.cpu_rows)
-        log(f"cpu baseline {cpu['value']:.2f} tok/s over {cpu['measured_s']:.1f}s")
-
-    line = {
-        "metric": METRIC, "value": pre["tok_s"], "unit": "tok/s", "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": pre["ms_per_step"],
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
-        "data": "synthetic", "config": cfg, "roofline": roofline, "cpu_baseline": cpu,
-        "stages_ms": pre["stages_ms"],
-        "score_select_effective_tflops": score_tflops,
-        "decode": dec,
-        "backward": pre.get("backward"),
-        "distill": pre.get("distill"),
-    }
+    legs = args.legs
+    line = {"metric": METRIC, "value": None, "unit": "tok/s", "n_gpus": 1, "steps": args.steps,
+            "warmup": args.warmup, "ms_per_step": None, "higher_is_better": True,
+            "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+            "config": None, "roofline": None, "cpu_baseline": None}
+    x = bwd_data = None
+    if "chunked" in legs:
+        x, cfg, pre, state = bench_prefill(args, torch, "chunked", keep=True)
+        cold_ms = bench_attention_cold(args, torch, x, state)
+        att = pre["attention"]
+        att["cold_4_replicas_avg_launch_ms"] = cold_ms
+        att["cold_gather_gbs"] = att["gather_bytes"] / (cold_ms * 1e-3) / 1e9
+        achieved = att["flops"] / (att["avg_launch_ms"] * 1e-3) / 1e12
+        line.update({
+            "value": pre["tok_s"], "ms_per_step": pre["ms_per_step"], "config": cfg,
+            # The dominant kernel against its roofline.  Its minimum traffic (each
+            # distinct K/V row once, plus q and out) gives an arithmetic intensity
+            # far above the MFMA ridge, so the binding roof is the bf16 MFMA peak;
+            # the kernel re-gathers rows per query instead of sharing them, which
+            # is what keeps it below.  `traffic` is the counter-measured bytes
+            # past L2 per launch (null until retaken for the current source).
+            "roofline": {"kernel": "sparse_attn_prefill (attn_mfma_kernel<2,128>)",
+                         "bound": "mfma", "achieved": achieved,
+                         "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+                         "frac": achieved / BF16_MFMA_PEAK_TFLOPS,
+                         "traffic": attn_traffic_bytes(),
+                         "algorithmic_flops_per_launch": att["flops"],
+                         "avg_launch_ms": att["avg_launch_ms"],
+                         "gather_gbs": att["gather_gbs"],
+                         "cold_gather_gbs": att["cold_gather_gbs"]},
+            "stages_ms": pre["stages_ms"], "score_select": pre["score_select"],
+            "attention": att,
+        })
+        if "backward" in legs:
+            line["backward"], bwd_data = bench_backward(args, torch, x, state)
+        if "distill" in legs:
+            line["distill"] = bench_distill(args, torch, x, state)
+        del state
+        torch.cuda.empty_cache()
+    if "prefill32k" in legs:
+        _, cfg2, res, _ = bench_prefill(args, torch, "prefill32k")
+        res["config"] = cfg2
+        line["prefill_32k"] = res
+    if "companion" in legs:
+        _, cfg5, res, _ = bench_prefill(args, torch, "companion")
+        res["config"] = cfg5
+        line["companion_1m"] = res
+    if "decode" in legs:
+        line["decode"] = bench_decode(args, torch, "offload" in legs)
+    if "stack" in legs:
+        line["stack_1m"] = bench_stack_decode(args, torch)
+    if "cpu" in legs and x is not None:
+        log(f"cpu baseline (oracle), {_pool_size(args)} worker processes ...")
+        cpu = cpu_baselines(args, x, bwd_data if "backward" in legs else None)
+        line["cpu_baseline"] = cpu["cpu_baseline"]
+        if "backward" in cpu and "backward" in line:
+            line["backward"]["cpu_baseline"] = cpu["backward"]
+        if "distill" in cpu and "distill" in line:
+            line["distill"]["cpu_baseline"] = cpu["distill"]
+        log(f"cpu baseline {line['cpu_baseline']['value']:.1f} tok/s on "
+            f"{line['cpu_baseline']['cores']} workers")
     print(json.dumps(line), flush=True)
 
 

@@ -80,6 +80,23 @@ def _normal(rng: np.random.Generator, shape, chunk: int = 1 << 24) -> np.ndarray
     return out
 
 
+def _draws(st, shapes: dict) -> list:
+    """fp32 N(0,1) tensors, one per named stream, drawn concurrently: each
+    tensor has a stream of its own, so the values do not depend on the
+    order (numpy releases the GIL while it fills)."""
+    from concurrent.futures import ThreadPoolExecutor
+    with ThreadPoolExecutor(len(shapes)) as ex:
+        futs = [ex.submit(_normal, st[name], shape) for name, shape in shapes.items()]
+        return [f.result() for f in futs]
+
+
+def _stores(arrays, dtype: str) -> list:
+    """_store of each array, concurrently."""
+    from concurrent.futures import ThreadPoolExecutor
+    with ThreadPoolExecutor(len(arrays)) as ex:
+        return list(ex.map(lambda a: _store(a, dtype), arrays))
+
+
 # --------------------------------------------------------------------------
 # layer description
 # --------------------------------------------------------------------------
@@ -183,11 +200,10 @@ def tiny(n: int = 256, seed: int = SEEDS["tiny"], token_budget: int = 64) -> Lay
     lay = Layout(q_heads=4, kv_heads=1, head_dim=64, token_budget=token_budget, dtype="f32")
     st = _streams(seed)
     T = _cap(n, 4)
-    k_idx = _normal(st["k_idx"], (1, T, lay.idx_dim))
-    q_idx = _normal(st["q_idx"], (1, n, lay.idx_heads, lay.idx_dim))
-    q = _normal(st["q"], (1, n, lay.q_heads, lay.head_dim))
-    k = _normal(st["k"], (1, T, lay.kv_heads, lay.head_dim))
-    v = _normal(st["v"], (1, T, lay.kv_heads, lay.head_dim))
+    k_idx, q_idx, q, k, v = _draws(st, {
+        "k_idx": (1, T, lay.idx_dim), "q_idx": (1, n, lay.idx_heads, lay.idx_dim),
+        "q": (1, n, lay.q_heads, lay.head_dim), "k": (1, T, lay.kv_heads, lay.head_dim),
+        "v": (1, T, lay.kv_heads, lay.head_dim)})
     m = q_idx.reshape(-1, lay.idx_dim).mean(axis=0, dtype=np.float64).astype(np.float32)
     nb = n // lay.block_size
     needles = sorted(st["structure"].choice(nb, size=min(3, nb), replace=False).tolist())
@@ -214,11 +230,10 @@ def prefill(n: int = 32768, seed: int = SEEDS["prefill"], batch: int = 1,
     st = _streams(seed)
     T = _cap(n)
     r = lay.block_size
-    k_idx = _normal(st["k_idx"], (batch, T, lay.idx_dim))
-    q_idx = _normal(st["q_idx"], (batch, n, lay.idx_heads, lay.idx_dim))
-    q = _normal(st["q"], (batch, n, lay.q_heads, lay.head_dim))
-    k = _normal(st["k"], (batch, T, lay.kv_heads, lay.head_dim))
-    v = _normal(st["v"], (batch, T, lay.kv_heads, lay.head_dim))
+    k_idx, q_idx, q, k, v = _draws(st, {
+        "k_idx": (batch, T, lay.idx_dim), "q_idx": (batch, n, lay.idx_heads, lay.idx_dim),
+        "q": (batch, n, lay.q_heads, lay.head_dim), "k": (batch, T, lay.kv_heads, lay.head_dim),
+        "v": (batch, T, lay.kv_heads, lay.head_dim)})
     rs = st["structure"]
     nb = n // r
     n_needles = int(round(needle_frac * nb))
@@ -240,8 +255,7 @@ def prefill(n: int = 32768, seed: int = SEEDS["prefill"], batch: int = 1,
                 q_idx[s, i] += np.float32(0.5) * us[j][None, :]
         all_needles.append(blocks.tolist())
     g = np.ones(lay.idx_dim, np.float32) if gain is None else np.asarray(gain, np.float32)
-    return LayerInputs(lay, _store(k_idx, lay.dtype), _store(q_idx, lay.dtype),
-                       _store(q, lay.dtype), _store(k, lay.dtype), _store(v, lay.dtype),
+    return LayerInputs(lay, *_stores([k_idx, q_idx, q, k, v], lay.dtype),
                        q_pos0=np.zeros(batch, np.int32), cache_len=np.zeros(batch, np.int32),
                        gain=g, target_block=target, needles=all_needles,
                        name=f"prefill-n{n}-b{batch}")
@@ -263,11 +277,10 @@ def chunked(cache: int = 131072, chunk: int = 8192, batch: int = 2,
     r = lay.block_size
     total = cache + chunk
     T = _cap(total)
-    k_idx = _normal(st["k_idx"], (batch, T, lay.idx_dim))
-    q_idx = _normal(st["q_idx"], (batch, chunk, lay.idx_heads, lay.idx_dim))
-    q = _normal(st["q"], (batch, chunk, lay.q_heads, lay.head_dim))
-    k = _normal(st["k"], (batch, T, lay.kv_heads, lay.head_dim))
-    v = _normal(st["v"], (batch, T, lay.kv_heads, lay.head_dim))
+    k_idx, q_idx, q, k, v = _draws(st, {
+        "k_idx": (batch, T, lay.idx_dim), "q_idx": (batch, chunk, lay.idx_heads, lay.idx_dim),
+        "q": (batch, chunk, lay.q_heads, lay.head_dim), "k": (batch, T, lay.kv_heads, lay.head_dim),
+        "v": (batch, T, lay.kv_heads, lay.head_dim)})
     rs = st["structure"]
     n_win = T // window + 2
     target = np.full((batch, chunk), -1, np.int32)
@@ -291,8 +304,7 @@ def chunked(cache: int = 131072, chunk: int = 8192, batch: int = 2,
             q_idx[s, j] += np.float32(0.5) * us[pick[j]][None, :]
             target[s, j] = int(blocks[pick[j]])
         all_needles.append(blocks.tolist())
-    return LayerInputs(lay, _store(k_idx, lay.dtype), _store(q_idx, lay.dtype),
-                       _store(q, lay.dtype), _store(k, lay.dtype), _store(v, lay.dtype),
+    return LayerInputs(lay, *_stores([k_idx, q_idx, q, k, v], lay.dtype),
                        q_pos0=np.full(batch, cache, np.int32),
                        cache_len=np.full(batch, cache, np.int32),
                        gain=np.ones(lay.idx_dim, np.float32), target_block=target,
@@ -317,11 +329,10 @@ def decode(context: int = 262144, batch: int = 8, steps: int = 64,
     tails = rs.integers(0, r, size=batch).astype(np.int32)
     lens = (context + tails).astype(np.int32)
     T = _cap(int(lens.max()) + steps)
-    k_idx = _normal(st["k_idx"], (batch, T, lay.idx_dim))
-    q_idx = _normal(st["q_idx"], (batch, steps, lay.idx_heads, lay.idx_dim))
-    q = _normal(st["q"], (batch, steps, lay.q_heads, lay.head_dim))
-    k = _normal(st["k"], (batch, T, lay.kv_heads, lay.head_dim))
-    v = _normal(st["v"], (batch, T, lay.kv_heads, lay.head_dim))
+    k_idx, q_idx, q, k, v = _draws(st, {
+        "k_idx": (batch, T, lay.idx_dim), "q_idx": (batch, steps, lay.idx_heads, lay.idx_dim),
+        "q": (batch, steps, lay.q_heads, lay.head_dim), "k": (batch, T, lay.kv_heads, lay.head_dim),
+        "v": (batch, T, lay.kv_heads, lay.head_dim)})
     nb = context // r
     target = np.full((batch, steps), -1, np.int32)
     all_needles = []
@@ -335,8 +346,7 @@ def decode(context: int = 262144, batch: int = 8, steps: int = 64,
             q_idx[s, j] += np.float32(0.5) * us[pick[j]][None, :]
             target[s, j] = int(blocks[pick[j]])
         all_needles.append(blocks.tolist())
-    return LayerInputs(lay, _store(k_idx, lay.dtype), _store(q_idx, lay.dtype),
-                       _store(q, lay.dtype), _store(k, lay.dtype), _store(v, lay.dtype),
+    return LayerInputs(lay, *_stores([k_idx, q_idx, q, k, v], lay.dtype),
                        q_pos0=lens.copy(), cache_len=lens.copy(),
                        gain=np.ones(lay.idx_dim, np.float32), target_block=target,
                        needles=all_needles, name=f"decode-c{context}-b{batch}-s{steps}")
@@ -369,11 +379,10 @@ def stack_layer(layer: int, context: int = 1048576, steps: int = 64,
         n = steps
         start = context
         T = _cap(context + steps)
-    k_idx = _normal(st["k_idx"], (1, T, lay.idx_dim))
-    q_idx = _normal(st["q_idx"], (1, n, lay.idx_heads, lay.idx_dim))
-    q = _normal(st["q"], (1, n, lay.q_heads, lay.head_dim))
-    k = _normal(st["k"], (1, T, lay.kv_heads, lay.head_dim))
-    v = _normal(st["v"], (1, T, lay.kv_heads, lay.head_dim))
+    k_idx, q_idx, q, k, v = _draws(st, {
+        "k_idx": (1, T, lay.idx_dim), "q_idx": (1, n, lay.idx_heads, lay.idx_dim),
+        "q": (1, n, lay.q_heads, lay.head_dim), "k": (1, T, lay.kv_heads, lay.head_dim),
+        "v": (1, T, lay.kv_heads, lay.head_dim)})
     for b, u in zip(blocks, us):
         _plant_needle(k_idx[0], b, u, rs, r)
     target = np.full((1, n), -1, np.int32)
@@ -392,8 +401,7 @@ def stack_layer(layer: int, context: int = 1048576, steps: int = 64,
             m = (j + layer) % n_needles
             q_idx[0, j] += np.float32(0.5) * us[m][None, :]
             target[0, j] = blocks[m]
-    return LayerInputs(lay, _store(k_idx, lay.dtype), _store(q_idx, lay.dtype),
-                       _store(q, lay.dtype), _store(k, lay.dtype), _store(v, lay.dtype),
+    return LayerInputs(lay, *_stores([k_idx, q_idx, q, k, v], lay.dtype),
                        q_pos0=np.array([start], np.int32), cache_len=np.array([start], np.int32),
                        gain=np.ones(lay.idx_dim, np.float32), target_block=target,
                        needles=[blocks],
