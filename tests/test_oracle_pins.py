@@ -594,3 +594,61 @@ def test_distill_chain_to_raw_keys_matches_finite_differences():
         a = q.copy(); a[idx] += eps
         b = q.copy(); b[idx] -= eps
         assert abs((loss(k_idx, a) - loss(k_idx, b)) / (2 * eps) - dq[idx]) < 1e-6
+
+
+# ------------------------------------------- token level (r = 1, DSA-like) ---
+def test_token_level_pool_is_identity_and_rotates_at_own_position():
+    # one token per block: the "mean" is the token itself, and block b is
+    # rotated at position b.  Pair j = 16 has theta = 0.01, so a unit vector
+    # on dim 16 of token 100 turns by exactly 1 rad.
+    rng = np.random.default_rng(21)
+    k = rng.standard_normal((130, 128))
+    np.testing.assert_array_equal(O.avg_pool_blocks(k, 1, 130), k)
+    e = np.zeros((101, 128))
+    e[:, 16] = 1.0
+    e[:, 100] = 1.0                       # an unrotated dim: RMSNorm scale sqrt(64)
+    kh = O.compress_index(e, 101, r=1, eps=0.0, storage="f64")
+    s = math.sqrt(64.0)
+    assert kh[100, 16] == pytest.approx(s * math.cos(1.0), abs=1e-12)
+    assert kh[100, 48] == pytest.approx(s * math.sin(1.0), abs=1e-12)
+    assert kh[100, 100] == pytest.approx(s, abs=1e-12)
+    assert kh[0, 16] == pytest.approx(s, abs=1e-12) and kh[0, 48] == 0.0
+
+
+def test_token_level_selection_and_tail():
+    # r = 1, k_B = K = 8: the 8 best earlier tokens (brute-force rank count,
+    # ties to the lower index), then the query itself as the whole tail
+    rng = np.random.default_rng(22)
+    n = 40
+    kh = rng.standard_normal((n, 128))
+    for p in (0, 1, 5, 8, 9, 23, 39):
+        qi = rng.standard_normal((4, 128))
+        res = O.qsa_row(p, qi, np.zeros((2, 8)), kh, np.zeros((n, 1, 8)), np.zeros((n, 1, 8)),
+                        k_B=8, r=1, attend=False)
+        I = res.scores
+        assert I.shape == (p,)
+        rank = np.array([(I > I[b]).sum() + (I[:b] == I[b]).sum() for b in range(p)], int)
+        want = np.nonzero(rank < 8)[0]
+        assert res.sel.blocks.tolist() == want.tolist()
+        assert res.S.tolist() == want.tolist() + [p]
+
+
+def test_token_level_full_budget_equals_dense_causal_attention():
+    # r = 1 with K >= n: every earlier token is selected, so each row is
+    # dense causal attention (torch CPU fp64)
+    rng = np.random.default_rng(23)
+    n, Hq, Hkv, d = 90, 8, 2, 32
+    q = rng.standard_normal((n, Hq, d))
+    K = rng.standard_normal((n, Hkv, d))
+    V = rng.standard_normal((n, Hkv, d))
+    qi = rng.standard_normal((n, 4, 128))
+    kh = O.compress_index(rng.standard_normal((n, 128)), n, r=1, storage="f64")
+    qt = torch.tensor(q).permute(1, 0, 2)
+    kt = torch.tensor(K).permute(1, 0, 2).repeat_interleave(Hq // Hkv, 0)
+    vt = torch.tensor(V).permute(1, 0, 2).repeat_interleave(Hq // Hkv, 0)
+    dense = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, is_causal=True)
+    dense = dense.permute(1, 0, 2).numpy()
+    for p in range(0, n, 7):
+        res = O.qsa_row(p, qi[p], q[p], kh, K, V, k_B=128, r=1)
+        assert res.S.tolist() == list(range(p + 1))
+        np.testing.assert_allclose(res.o, dense[p], atol=1e-12)
