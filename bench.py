@@ -781,6 +781,8 @@ def main(argv=None):
         return
 
     legs = args.legs
+    if args.block_size < 4:   # the backward and the distillation work on 4-token units
+        legs = [l for l in legs if l not in ("backward", "distill")]
     line = {"metric": METRIC, "value": None, "unit": "tok/s", "n_gpus": 1, "steps": args.steps,
             "warmup": args.warmup, "ms_per_step": None, "higher_is_better": True,
             "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",

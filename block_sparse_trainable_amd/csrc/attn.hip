@@ -8,9 +8,13 @@
 // "Qwen Sparse Attention" gallery page, How block selection works: the same
 // token set, as the pseudocode's attention input.
 //
-// Token set of the query at p (c = floor(p/4)): pseudo-blocks 0..count-1 are
-// the selected blocks, pseudo-block `count` is the tail block c, whose
-// tokens 4c+t count only while 4c+t <= p.
+// Token set of the query at p (c = floor(p/r)): a selected block b is the
+// r/4 pseudo-blocks (4-token units) of its tokens, then come the tail's
+// pseudo-blocks up to the one holding p, whose tokens count only while they
+// are <= p.  Blocks of r < 4 tokens (down to single tokens, r = 1) take the
+// token mode: the set is written out as a list of positions -- the selected
+// blocks' tokens, then the tail r*c .. p -- and the tiles read it 32 slots
+// at a time.
 //
 // MFMA path (16 query heads, Hkv in {1,2}, head_dim in {64,128}, bf16): the
 // work item in attn_tile.h, one workgroup per query (prefill) or per split
@@ -108,7 +112,7 @@ __global__ __launch_bounds__(256) void attn_generic_kernel(
 }
 
 // ---------------------------------------------------------------- MFMA ----
-template <int HKV, int D>
+template <int HKV, int D, bool TOK>
 __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kc,
     const uint16_t* __restrict__ vc, int64_t cap, int n_q, const int32_t* __restrict__ q_pos0,
@@ -117,7 +121,7 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(
     int n_split, int pb_per_split, int lr) {
   using S = MfmaShape<HKV, D>;
   __shared__ __attribute__((aligned(16))) unsigned char lds[S::LDS_BYTES];
-  __shared__ int32_t sbid[kMaxPB];
+  __shared__ int32_t sbid[TOK ? kMaxTok : kMaxPB];
   // Workgroups are handed to the 8 XCDs in turn (workgroup b to XCD b % 8):
   // give each XCD one contiguous run of items, so that neighbouring queries,
   // whose selections overlap, share an L2.  A bijection for any grid size.
@@ -134,24 +138,42 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(
   const int64_t p = min(max((int64_t)q_pos0[s] + j, (int64_t)0), cap - 1);
   const int64_t c = p >> lr;
   const int count = (int)min((int64_t)max(cnt[row], 0), min((int64_t)kB, c));
-  // 4-token pseudo-blocks: selected block b is m = r/4 of them (b*m .. b*m+m-1),
-  // then the tail block c up to the one holding p
-  const int lm = lr - 2;
-  const int nsel = count << lm;
-  const int npb = nsel + (int)((p - (c << lr)) >> 2) + 1;
-  const int pb_lo = split * pb_per_split;
-  const int pb_hi = min(pb_lo + pb_per_split, npb);
   const int32_t* srow = sel + row * kB;
-  for (int i = pb_lo + (int)threadIdx.x; i < pb_hi; i += 256)
-    sbid[i - pb_lo] =
-        i < nsel ? (int32_t)((min(max((int64_t)srow[i >> lm], (int64_t)0), c - 1) << lm) +
-                             (i & ((1 << lm) - 1)))
-                 : (int32_t)((c << lm) + (i - nsel));
   u32x4 qb[S::NK];
-  load_qbd<HKV, D>(q, row, qb);
-  __syncthreads();
-  attn_mfma_tiles<HKV, D, false>(qb, kc, vc, cap, s, p, row, item, pb_lo, pb_hi, sbid,
-                                 scale_log2, out, lse, part, n_split, lds);
+  if constexpr (TOK) {
+    // the token list: count*r selected tokens, then the tail r*c .. p
+    const int nsel = count << lr;
+    const int ntok = nsel + (int)(p - (c << lr)) + 1;
+    const int pb_lo = split * pb_per_split;
+    const int pb_hi = min(pb_lo + pb_per_split, (ntok + 3) >> 2);
+    const int t_lo = 4 * pb_lo, t_hi = min(4 * pb_hi, ntok);
+    for (int i = t_lo + (int)threadIdx.x; i < t_hi; i += 256)
+      sbid[i - t_lo] =
+          i < nsel ? (int32_t)((min(max((int64_t)srow[i >> lr], (int64_t)0), c - 1) << lr) +
+                               (i & ((1 << lr) - 1)))
+                   : (int32_t)((c << lr) + (i - nsel));
+    load_qbd<HKV, D>(q, row, qb);
+    __syncthreads();
+    attn_mfma_tiles<HKV, D, false, true>(qb, kc, vc, cap, s, p, row, item, pb_lo, pb_hi, sbid,
+                                         scale_log2, out, lse, part, n_split, lds, t_hi);
+  } else {
+    // 4-token pseudo-blocks: selected block b is m = r/4 of them
+    // (b*m .. b*m+m-1), then the tail block c up to the one holding p
+    const int lm = lr - 2;
+    const int nsel = count << lm;
+    const int npb = nsel + (int)((p - (c << lr)) >> 2) + 1;
+    const int pb_lo = split * pb_per_split;
+    const int pb_hi = min(pb_lo + pb_per_split, npb);
+    for (int i = pb_lo + (int)threadIdx.x; i < pb_hi; i += 256)
+      sbid[i - pb_lo] =
+          i < nsel ? (int32_t)((min(max((int64_t)srow[i >> lm], (int64_t)0), c - 1) << lm) +
+                               (i & ((1 << lm) - 1)))
+                   : (int32_t)((c << lm) + (i - nsel));
+    load_qbd<HKV, D>(q, row, qb);
+    __syncthreads();
+    attn_mfma_tiles<HKV, D, false>(qb, kc, vc, cap, s, p, row, item, pb_lo, pb_hi, sbid,
+                                   scale_log2, out, lse, part, n_split, lds);
+  }
 }
 
 // Decode: log-sum-exp merge of a row's split states.  One workgroup per
@@ -189,8 +211,11 @@ bool use_mfma(const Dims& d) {
           (d.kv_heads == 1 && d.head_dim == 128));
 }
 
-// 4-token pseudo-blocks of a largest token set: k_B + 1 blocks of r / 4
-int max_pseudo_blocks(const Dims& d) { return (d.kB + 1) << (d.lr - 2); }
+// 4-token pseudo-blocks (token-list slots of 4 in token mode) of a largest
+// token set: k_B + 1 blocks of r tokens
+int max_pseudo_blocks(const Dims& d) {
+  return d.lr >= 2 ? (d.kB + 1) << (d.lr - 2) : (((d.kB + 1) << d.lr) + 3) / 4;
+}
 
 int decode_splits(const Dims& d) {
   return (max_pseudo_blocks(d) + kDecodeSplitPB - 1) / kDecodeSplitPB;
@@ -204,11 +229,19 @@ hipError_t launch_mfma(const Dims& d, int rows, int n_q, const void* q, const vo
   const float sl2 = d.scale * kLog2e;
   const int ns = decode ? decode_splits(d) : 1;
   float* part = decode ? static_cast<float*>(ws) : nullptr;
-  hipLaunchKernelGGL((attn_mfma_kernel<HKV, D>), dim3((unsigned)(rows * ns)), dim3(256), 0, st,
-                     static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(kc),
-                     static_cast<const uint16_t*>(vc), cap, n_q, q_pos0, sel, cnt, d.kB, sl2,
-                     static_cast<uint16_t*>(out), lse, part, ns,
-                     decode ? kDecodeSplitPB : max_pseudo_blocks(d), d.lr);
+  const dim3 grid((unsigned)(rows * ns));
+  if (d.lr < 2)
+    hipLaunchKernelGGL((attn_mfma_kernel<HKV, D, true>), grid, dim3(256), 0, st,
+                       static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(kc),
+                       static_cast<const uint16_t*>(vc), cap, n_q, q_pos0, sel, cnt, d.kB, sl2,
+                       static_cast<uint16_t*>(out), lse, part, ns,
+                       decode ? kDecodeSplitPB : max_pseudo_blocks(d), d.lr);
+  else
+    hipLaunchKernelGGL((attn_mfma_kernel<HKV, D, false>), grid, dim3(256), 0, st,
+                       static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(kc),
+                       static_cast<const uint16_t*>(vc), cap, n_q, q_pos0, sel, cnt, d.kB, sl2,
+                       static_cast<uint16_t*>(out), lse, part, ns,
+                       decode ? kDecodeSplitPB : max_pseudo_blocks(d), d.lr);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || !decode || ns == 1) return e;  // one split wrote the output itself
   hipLaunchKernelGGL((attn_merge_kernel<D>), dim3((unsigned)(rows * 16)), dim3(D), 0, st, part,

@@ -61,8 +61,11 @@ struct MfmaShape {
 
 // Pseudo-blocks are 4-token units: a block of r = 4m tokens is m of them.
 // A token set holds at most 2048 selected tokens (r * k_B <= 2048) plus a
-// tail of at most r <= 128 tokens.
+// tail of at most r <= 128 tokens.  Blocks of r < 4 tokens are attended from
+// an explicit token list instead (token mode): list slots 4i .. 4i+3 play
+// the part of pseudo-block i.
 constexpr int kMaxPB = (2048 + 128) / 4;  // pseudo-blocks of one query
+constexpr int kMaxTok = 2048 + 4;         // token-mode list: r*k_B <= 2048 plus a tail of r < 4
 constexpr int kMaxSplits = 17;            // decode splits of 32 pseudo-blocks
 constexpr int kDecodeSplitPB = 32;        // pseudo-blocks per decode split
 
@@ -96,17 +99,20 @@ __device__ __forceinline__ void load_qbd(const uint16_t* __restrict__ q, int64_t
 // Attends query row `row` (sequence s, position p) over pseudo-blocks
 // [pb_lo, pb_hi) whose block ids the caller has put in sbid[0 ..) (the tail
 // block c = floor(p/4) included as an ordinary id), for work item `item` =
-// row * n_split + split.  n_split == 1 writes the bf16 output and the
+// row * n_split + split.  TOK (token mode): sbid[i] is instead the position
+// of token slot 4*pb_lo + i, and slots at or past t_hi are empty.
+// n_split == 1 writes the bf16 output and the
 // log-sum-exp; otherwise the split's (m, l, O) state goes to part (with
 // coherent stores when COHERENT: another workgroup of the same kernel reads
 // it).  lds: MfmaShape::LDS_BYTES bytes.  Called by all 256 threads after a
 // barrier that publishes sbid.
-template <int HKV, int D, bool COHERENT>
+template <int HKV, int D, bool COHERENT, bool TOK = false>
 __device__ __forceinline__ void attn_mfma_tiles(
     const u32x4 (&qb)[MfmaShape<HKV, D>::NK], const uint16_t* __restrict__ kc,
     const uint16_t* __restrict__ vc, int64_t cap, int s, int64_t p, int64_t row, int64_t item,
     int pb_lo, int pb_hi, const int32_t* sbid, float scale_log2, uint16_t* __restrict__ out,
-    float* __restrict__ lse, float* __restrict__ part, int n_split, unsigned char* lds) {
+    float* __restrict__ lse, float* __restrict__ part, int n_split, unsigned char* lds,
+    int t_hi = 0) {
   using S = MfmaShape<HKV, D>;
   constexpr int KD = S::KD, NK = S::NK, ROWB = S::ROWB, G = S::G, CH = S::CH, RPI = S::RPI;
   constexpr int MF = S::MERGE_FLOATS;
@@ -120,6 +126,8 @@ __device__ __forceinline__ void attn_mfma_tiles(
   const uint16_t* vbase = vc + (int64_t)s * cap * KD;
   // block id of pseudo-block pb, -1 outside this work item
   auto bid = [&](int pb) -> int64_t { return (pb < pb_hi) ? (int64_t)sbid[pb - pb_lo] : -1; };
+  // token mode: position of list slot sl, -1 past the list
+  auto tok = [&](int sl) -> int64_t { return (sl < t_hi) ? (int64_t)sbid[sl - 4 * pb_lo] : -1; };
 
   float m_run = -INFINITY, l_run = 0.0f;
   f32x4 oacc[NK][2];
@@ -133,9 +141,15 @@ __device__ __forceinline__ void attn_mfma_tiles(
 #pragma unroll
     for (int st = 0; st < 2; ++st) {
       const int tk = 16 * st + l16;
-      const int64_t b = bid(pb0 + (tk >> 2));
-      const int64_t tp = 4 * b + (tk & 3);
-      const int64_t rp = (b >= 0 && tp <= p) ? tp : p;
+      int64_t rp;
+      if constexpr (TOK) {
+        const int64_t tp = tok(4 * pb0 + tk);
+        rp = tp >= 0 ? tp : p;
+      } else {
+        const int64_t b = bid(pb0 + (tk >> 2));
+        const int64_t tp = 4 * b + (tk & 3);
+        rp = (b >= 0 && tp <= p) ? tp : p;
+      }
       const uint16_t* kp = kbase + rp * KD + 8 * gq;
 #pragma unroll
       for (int kk = 0; kk < NK; ++kk) kreg[st][kk] = ld16(kp + 32 * kk);
@@ -146,9 +160,15 @@ __device__ __forceinline__ void attn_mfma_tiles(
     for (int u = 0; u < 32 / RPI; ++u) {
       const int tk = RPI * u + lane / CH;
       const int chunk = (lane % CH) ^ vswz(tk);
-      const int64_t b = bid(pb0 + (tk >> 2));
-      const int64_t tp = 4 * b + (tk & 3);
-      const int64_t rp = (b >= 0 && tp <= p) ? tp : p;
+      int64_t rp;
+      if constexpr (TOK) {
+        const int64_t tp = tok(4 * pb0 + tk);
+        rp = tp >= 0 ? tp : p;
+      } else {
+        const int64_t b = bid(pb0 + (tk >> 2));
+        const int64_t tp = 4 * b + (tk & 3);
+        rp = (b >= 0 && tp <= p) ? tp : p;
+      }
       __builtin_amdgcn_global_load_lds(
           (const __attribute__((address_space(1))) void*)(vbase + rp * KD + chunk * 8),
           (__attribute__((address_space(3))) void*)(vt + u * 1024), 16, 0, 0);
@@ -167,10 +187,10 @@ __device__ __forceinline__ void attn_mfma_tiles(
     float mt = -INFINITY;
 #pragma unroll
     for (int st = 0; st < 2; ++st) {
-      const int64_t b = bid(pb0 + 4 * st + gq);
+      const int64_t b = TOK ? 0 : bid(pb0 + 4 * st + gq);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const bool ok = b >= 0 && 4 * b + i <= p;
+        const bool ok = TOK ? 4 * (pb0 + 4 * st + gq) + i < t_hi : (b >= 0 && 4 * b + i <= p);
         x[st][i] = ok ? sacc[st][i] * scale_log2 : -INFINITY;
         mt = fmaxf(mt, x[st][i]);
       }

@@ -62,8 +62,8 @@ qsa_status check_config(const char* fn, const qsa_config* cfg, qsa::Dims* d) {
     return fail(QSA_ERR_INVALID_ARGUMENT, "%s: rope_base must be positive", fn);
   if (!(cfg->rms_eps >= 0.0f))
     return fail(QSA_ERR_INVALID_ARGUMENT, "%s: rms_eps must be >= 0", fn);
-  if (cfg->block_size < 4 || cfg->block_size > 128 || (cfg->block_size & (cfg->block_size - 1)))
-    return fail(QSA_ERR_UNSUPPORTED, "%s: block_size %d (a power of two from 4 to 128)", fn,
+  if (cfg->block_size > 128 || (cfg->block_size & (cfg->block_size - 1)))
+    return fail(QSA_ERR_UNSUPPORTED, "%s: block_size %d (a power of two from 1 to 128)", fn,
                 cfg->block_size);
   if (cfg->idx_dim != 128)
     return fail(QSA_ERR_UNSUPPORTED, "%s: idx_dim %d (only 128 is built)", fn, cfg->idx_dim);
@@ -77,8 +77,9 @@ qsa_status check_config(const char* fn, const qsa_config* cfg, qsa::Dims* d) {
   if (cfg->q_heads > 64)
     return fail(QSA_ERR_UNSUPPORTED, "%s: q_heads %d (at most 64)", fn, cfg->q_heads);
   const int kB = (cfg->token_budget + cfg->block_size - 1) / cfg->block_size;
-  if (kB > 512)
-    return fail(QSA_ERR_UNSUPPORTED, "%s: k_B = ceil(K/r) = %d (at most 512)", fn, kB);
+  if (kB > 512 && cfg->block_size >= 4)
+    return fail(QSA_ERR_UNSUPPORTED, "%s: k_B = ceil(K/r) = %d (at most 512 for r >= 4)", fn,
+                kB);
   if ((int64_t)kB * cfg->block_size > 2048)
     return fail(QSA_ERR_UNSUPPORTED, "%s: k_B * r = %lld selected tokens (at most 2048)", fn,
                 (long long)kB * cfg->block_size);
@@ -188,6 +189,8 @@ qsa_status qsa_workspace_size(const qsa_config* cfg, int32_t op, int32_t batch, 
   if (!bytes) return fail(QSA_ERR_INVALID_ARGUMENT, "%s: bytes must not be NULL", fn);
   if (batch <= 0 || n_q <= 0 || max_pos_end <= 0)
     return fail(QSA_ERR_INVALID_ARGUMENT, "%s: batch, n_q and max_pos_end must be > 0", fn);
+  if (d.r < 4 && (op == QSA_OP_BACKWARD || op == QSA_OP_DISTILL || op == QSA_OP_DECODE_STEP))
+    return fail(QSA_ERR_UNSUPPORTED, "%s: op %d needs block_size >= 4", fn, op);
   switch (op) {
     case QSA_OP_INDEX_BUILD: *bytes = 0; break;
     case QSA_OP_SELECT: *bytes = select_ws(d, batch, n_q, max_pos_end); break;
@@ -358,6 +361,9 @@ qsa_status qsa_sparse_attn_backward(const qsa_config* cfg, int32_t batch, int32_
   if (st != QSA_OK) return st;
   if (d.kv_heads > 2)
     return fail(QSA_ERR_UNSUPPORTED, "%s: kv_heads %d (at most 2)", fn, d.kv_heads);
+  if (d.r < 4)
+    return fail(QSA_ERR_UNSUPPORTED, "%s: block_size %d (the key side works on 4-token units: "
+                "r >= 4)", fn, d.r);
   QSA_REQUIRE_PTR(q, 16);
   QSA_REQUIRE_PTR(k_cache, 16);
   QSA_REQUIRE_PTR(v_cache, 16);
@@ -468,6 +474,9 @@ qsa_status qsa_indexer_distill(const qsa_config* cfg, int32_t batch, int32_t n_q
                 "built (got %d, %d, %d)", fn, d.q_heads, d.kv_heads, d.head_dim);
   if (d.idx_heads > 8)
     return fail(QSA_ERR_UNSUPPORTED, "%s: idx_heads %d (at most 8)", fn, d.idx_heads);
+  if (d.r < 4)
+    return fail(QSA_ERR_UNSUPPORTED, "%s: block_size %d (the teacher's maximum is kept per "
+                "4-token unit: r >= 4)", fn, d.r);
   QSA_REQUIRE_PTR(q, 16);
   QSA_REQUIRE_PTR(k_cache, 16);
   QSA_REQUIRE_PTR(q_pos0, 4);
@@ -499,6 +508,8 @@ qsa_status qsa_offload_stage(const qsa_config* cfg, int32_t batch, const int32_t
   qsa_status st = check_config(fn, cfg, &d);
   if (st != QSA_OK) return st;
   if (!d.bf16) return fail(QSA_ERR_UNSUPPORTED, "%s: bf16 caches only", fn);
+  if (d.r < 4)
+    return fail(QSA_ERR_UNSUPPORTED, "%s: block_size %d (4-token units: r >= 4)", fn, d.r);
   if (batch <= 0 || batch > 65535)
     return fail(QSA_ERR_INVALID_ARGUMENT, "%s: batch must be in [1, 65535]", fn);
   if (cap_tokens < d.r || cap_tokens > INT32_MAX)

@@ -1,8 +1,9 @@
 // Top-k_B block selection (kernel c).
 //
 // "QSA (Qwen Sparse Attention)", Key math / How it works, (A): keep the
-// k_B = ceil(K/r) highest-scoring blocks (at most 512 with K = 2048, r = 4,
-// per the "Config" line and the gallery page's budget table).  Equal scores
+// k_B = ceil(K/r) highest-scoring blocks (512 with K = 2048, r = 4, per the
+// "Config" line and the gallery page's budget table; up to 2,048 single
+// tokens at r = 1, the token-level end of the QSA-vs-DSA table).  Equal scores
 // go to the lower block index, and the kept ids are written in ascending
 // order, so the result is unique.
 //
@@ -426,7 +427,8 @@ __global__ __launch_bounds__(kThreads) void filter_select_kernel(FilterArgs a) {
 // In the pool a key is stored as key << 15 (bits 30..15), so the generic
 // radix select resolves it in two digits.
 constexpr int64_t kStreamMax = int64_t{1} << 20;   // candidates per row this path takes
-constexpr int kRowCap = 3072;                      // pool capacity (candidates)
+constexpr int kRowCap = 3072;                      // pool capacity (candidates), k_B <= 512
+constexpr int kRowCapBig = 6144;                   // ... for k_B up to 2048
 // pool slot i lives at i + i / 16: the ordered pass reads 16 consecutive
 // slots per thread, which would otherwise all fall in two banks
 __device__ __forceinline__ uint32_t pslot(uint32_t i) { return i + (i >> 4); }
@@ -496,24 +498,25 @@ __device__ __forceinline__ void select_row_global16(const uint16_t* keys, int64_
     const int64_t i0 = base + 4 * tid;
     uint32_t take = 0;
     float val[4];
+    // branch-free per element: the exact score is computed once (band keys
+    // only), then the kept value is chosen among the key's, the exact one
+    // and 0 (a nested conditional assignment of the exact value here was
+    // compiled to store 0)
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      val[e] = 0.0f;
       const int64_t i = i0 + e;
-      if (i >= c) continue;
-      const uint32_t k = key(i) & r.mask;
-      if (k > r.prefix || (!band && k == r.prefix)) {
-        take |= 1u << e;
-        val[e] = key16_value(key(i));
-      } else if (band && k == r.prefix) {
-        const uint32_t x = exact((uint32_t)i);
-        const uint32_t m = x & r2.mask;
-        if (m > r2.prefix ||
-            (m == r2.prefix && (!ties || ((0x7FFFFFFFu - (uint32_t)i) & r3.mask) >= r3.prefix))) {
-          take |= 1u << e;
-          val[e] = __uint_as_float(x);
-        }
-      }
+      const bool in = i < c;
+      const uint32_t kf = in ? key(i) : 0u;
+      const uint32_t k = kf & r.mask;
+      const bool at_t = in && band && k == r.prefix;
+      const uint32_t x = at_t ? exact((uint32_t)i) : 0u;
+      const uint32_t m = x & r2.mask;
+      const bool hi = in && (k > r.prefix || (!band && k == r.prefix));
+      const bool kb = at_t && (m > r2.prefix ||
+                               (m == r2.prefix &&
+                                (!ties || ((0x7FFFFFFFu - (uint32_t)i) & r3.mask) >= r3.prefix)));
+      take |= (hi || kb) ? 1u << e : 0u;
+      val[e] = hi ? key16_value(kf) : (kb ? __uint_as_float(x) : 0.0f);
     }
     uint32_t tot;
     uint32_t pos = written + block_excl_scan<NT>((uint32_t)__popc(take), scratch, &tot);
@@ -530,12 +533,13 @@ __device__ __forceinline__ void select_row_global16(const uint16_t* keys, int64_
 
 // One workgroup of NT threads per row: sample, stream in batches of BATCH
 // 16-byte pieces (8 keys each) per thread, DEPTH batches in flight,
-// compacting into the LDS pool in index order, then the threshold and the
-// ordered output.  PRUNE (long rows) lets the floor rise during the pass
-// instead of streaming the row again.
-template <int NT, int BATCH, bool PRUNE, int DEPTH>
+// compacting into the LDS pool of CAP candidates in index order, then the
+// threshold and the ordered output.  PRUNE (long rows) lets the floor rise
+// during the pass instead of streaming the row again.
+template <int NT, int BATCH, bool PRUNE, int DEPTH, int CAP>
 __global__ __launch_bounds__(NT) void select_row_kernel(FilterArgs a) {
   constexpr int NW = NT / 64;
+  constexpr int kRowCap = CAP;
   constexpr int kSlots = kRowCap + kRowCap / 16 + NT;  // + one trash slot per thread
   static_assert(NW % 4 == 0, "batch offsets read 4-wave groups of counts");
   __shared__ uint32_t ckey[kSlots];
@@ -709,44 +713,37 @@ __global__ __launch_bounds__(NT) void select_row_kernel(FilterArgs a) {
         }
         if constexpr (PRUNE) {
           // raise the floor to the (k_B + kPrune)-th largest pool key and keep
-          // only the keys at or above it (staged through the idle radix
-          // histogram, then copied back in order)
+          // only the keys at or above it, compacted in place: every thread
+          // holds its E consecutive entries in registers, and the scan's
+          // barriers separate all reads from the writes (an entry only moves
+          // down)
           auto pkey = [&](int64_t i) { return ckey[pslot((uint32_t)i)]; };
           auto pall = [&](int64_t) { return true; };
           const Radix rp = radix_select<NT, true>(pkey, pall, (int64_t)total, (uint32_t)(kB + kPrune), hist,
                                             scratch, 0, 0u, 0u, 1);
           fkey = max(fkey, rp.prefix);
           constexpr int E = kRowCap / NT;
-          constexpr uint32_t kStage = kRadixBins / 2;
-          uint32_t keep = 0;
+          uint32_t pk[E], px[E];
+          uint32_t keep = 0, kmask = 0;
 #pragma unroll
           for (int q = 0; q < E; ++q) {
             const uint32_t i = (uint32_t)(E * tid + q);
-            keep += (i < total && ckey[pslot(i)] >= fkey) ? 1u : 0u;
+            const uint32_t ic = i < total ? i : 0u;
+            pk[q] = ckey[pslot(ic)];
+            px[q] = cidx[pslot(ic)];
+            const bool kp = i < total && pk[q] >= fkey;
+            kmask |= kp ? 1u << q : 0u;
+            keep += kp ? 1u : 0u;
           }
           uint32_t kept;
           uint32_t at = block_excl_scan<NT>(keep, scratch, &kept);
-          if (kept > kStage) {   // hundreds of equal keys at the new floor
-            overflow = true;
-            break;
-          }
 #pragma unroll
-          for (int q = 0; q < E; ++q) {
-            const uint32_t i = (uint32_t)(E * tid + q);
-            if (i < total) {
-              const uint32_t k = ckey[pslot(i)];
-              if (k >= fkey) {
-                hist[2 * at] = k;
-                hist[2 * at + 1] = cidx[pslot(i)];
-                ++at;
-              }
+          for (int q = 0; q < E; ++q)
+            if ((kmask >> q) & 1u) {
+              ckey[pslot(at)] = pk[q];
+              cidx[pslot(at)] = px[q];
+              ++at;
             }
-          }
-          __syncthreads();
-          for (uint32_t i = tid; i < kept; i += NT) {
-            ckey[pslot(i)] = hist[2 * i];
-            cidx[pslot(i)] = hist[2 * i + 1];
-          }
           total = kept;
           __syncthreads();
         }
@@ -976,10 +973,15 @@ hipError_t launch_select(const Dims& d, const SelectPlan& pl, int batch, int n_q
   dim3 grid((unsigned)((int64_t)batch * n_q), (unsigned)pl.n_fseg);
   if (pl.resident) {
     const dim3 g((unsigned)((int64_t)batch * n_q));
-    if (pl.W <= kRowShortMax)
-      hipLaunchKernelGGL((select_row_kernel<256, 2, false, 1>), g, dim3(256), 0, st, a);
+    const bool big = d.kB > 512;   // the token-level budgets (r < 4)
+    if (pl.W <= kRowShortMax && !big)
+      hipLaunchKernelGGL((select_row_kernel<256, 2, false, 1, kRowCap>), g, dim3(256), 0, st, a);
+    else if (!big)
+      hipLaunchKernelGGL((select_row_kernel<256, 2, true, 1, kRowCap>), g, dim3(256), 0, st, a);
+    else if (pl.W <= kRowShortMax)
+      hipLaunchKernelGGL((select_row_kernel<256, 2, false, 1, kRowCapBig>), g, dim3(256), 0, st, a);
     else
-      hipLaunchKernelGGL((select_row_kernel<256, 2, true, 1>), g, dim3(256), 0, st, a);
+      hipLaunchKernelGGL((select_row_kernel<256, 2, true, 1, kRowCapBig>), g, dim3(256), 0, st, a);
   } else if (pl.n_fseg > 1 && pl.sseg <= 1024 && pl.fseg <= kWaves)
     hipLaunchKernelGGL(filter_select_kernel<true>, grid, dim3(kThreads), 0, st, a);
   else

@@ -67,12 +67,16 @@ typedef enum {
 typedef struct {
   int32_t block_size;    /* r: tokens per micro-block: 4 in the pages'
                             configuration ([concept] Config; [gallery]
-                            selection-unit table).  Supported: a power of
-                            two from 4 to 128 (qsa_decode_step: 4 only).   */
+                            selection-unit table); r = 1 selects single
+                            tokens, the token-level end of the [gallery]
+                            QSA-vs-DSA table.  Supported: a power of two
+                            from 1 to 128 (qsa_decode_step: 4 only; the
+                            backward, the distillation and the offload:
+                            r >= 4).                                        */
   int32_t token_budget;  /* K: selected tokens; k_B = ceil(K / r) blocks are
                             kept ([concept] (A) top-k_B; Config K = 2048).
-                            Supported: 1 <= k_B <= 512 and k_B * r <= 2048.
-                                                                            */
+                            Supported: k_B * r <= 2048, and k_B <= 512 when
+                            r >= 4 (so r = 1 keeps up to 2048 tokens).      */
   int32_t idx_heads;     /* indexer query heads sharing one key head: 4
                             ([concept] (A) MQA head layout).                */
   int32_t idx_dim;       /* indexer head dim: 128 ([concept] (A)).          */

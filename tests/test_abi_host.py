@@ -111,13 +111,13 @@ def test_workspace_sizes(lib):
 
 @pytest.mark.parametrize("field,value,status,word", [
     ("block_size", 6, B.QSA_ERR_UNSUPPORTED, "block_size"),     # not a power of two
-    ("block_size", 2, B.QSA_ERR_UNSUPPORTED, "block_size"),
+    ("block_size", 3, B.QSA_ERR_UNSUPPORTED, "block_size"),
     ("block_size", 256, B.QSA_ERR_UNSUPPORTED, "block_size"),
     ("block_size", 0, B.QSA_ERR_INVALID_ARGUMENT, "positive"),
     ("idx_dim", 64, B.QSA_ERR_UNSUPPORTED, "idx_dim"),
     ("rope_dims", 62, B.QSA_ERR_UNSUPPORTED, "rope_dims"),
     ("head_dim", 96, B.QSA_ERR_UNSUPPORTED, "head_dim"),
-    ("token_budget", 2052, B.QSA_ERR_UNSUPPORTED, "k_B"),      # k_B = 513
+    ("token_budget", 2052, B.QSA_ERR_UNSUPPORTED, "k_B"),      # k_B = 513 at r = 4
     ("kv_heads", 3, B.QSA_ERR_INVALID_ARGUMENT, "kv_heads"),
     ("dtype", 7, B.QSA_ERR_INVALID_ARGUMENT, "dtype"),
     ("rope_base", -1.0, B.QSA_ERR_INVALID_ARGUMENT, "rope_base"),
@@ -135,9 +135,20 @@ FAKE = 1 << 20  # a 16-byte-aligned non-null address; never dereferenced
 
 
 def test_block_sizes(lib):
-    """r a power of two from 4 to 128 with k_B * r <= 2048 selected tokens."""
-    for r in (4, 8, 16, 32, 64, 128):
+    """r a power of two from 1 to 128 with k_B * r <= 2048 selected tokens
+    (k_B <= 512 for r >= 4)."""
+    for r in (1, 2, 4, 8, 16, 32, 64, 128):
         qsa.qsa_workspace_size(cfg(block_size=r), B.QSA_OP_SELECT, 1, 16, 4096)
+    with pytest.raises(B.QsaError) as e:          # k_B = 2049 tokens
+        qsa.qsa_workspace_size(cfg(block_size=1, token_budget=2049), B.QSA_OP_SELECT, 1, 1, 8)
+    assert e.value.status == B.QSA_ERR_UNSUPPORTED and "2048" in str(e.value)
+    # token level: r = 1, k_B = 2048 -> 2049 tokens in slots of 4 -> 513 -> 17 splits
+    assert (qsa.qsa_workspace_size(cfg(block_size=1), B.QSA_OP_DECODE, 2, 1, 300000)
+            == 4 * 2 * 17 * (16 * 128 + 32))
+    for op in (B.QSA_OP_BACKWARD, B.QSA_OP_DISTILL, B.QSA_OP_DECODE_STEP):
+        with pytest.raises(B.QsaError) as e:      # built on 4-token units
+            qsa.qsa_workspace_size(cfg(block_size=2), op, 1, 16, 4096)
+        assert e.value.status == B.QSA_ERR_UNSUPPORTED
     with pytest.raises(B.QsaError) as e:          # k_B = 17 blocks of 128 = 2176 tokens
         qsa.qsa_workspace_size(cfg(block_size=128, token_budget=2049), B.QSA_OP_SELECT, 1, 1, 8)
     assert e.value.status == B.QSA_ERR_UNSUPPORTED and "2048" in str(e.value)

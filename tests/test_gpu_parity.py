@@ -256,6 +256,29 @@ def test_exact_ties_prefer_lower_block():
             assert got == tied[:16], got
 
 
+def test_many_exact_ties_report_exact_scores():
+    """More keys tie at the 16-bit threshold than the row selection resolves
+    in LDS (2,500 identical blocks, k_B = 512): the whole-row fallback picks
+    the lowest ids and reports their fp32 scores (not the 16-bit keys)."""
+    say("2500 identical blocks, nonzero scores: whole-row fallback")
+    x = synth.prefill(n=12800, needle_frac=0.0)
+    kf = synth.bf16_to_f32(x.k_idx)
+    kf[:, :, :64] = 0.0
+    rep = kf[0, 0:4].copy()
+    for b in range(2500):
+        kf[0, 4 * b:4 * b + 4] = rep
+    x.k_idx[:] = synth.f32_to_bf16(kf)
+    qf = synth.bf16_to_f32(x.q_idx)
+    qf[0, :, :, 64:] = rep.mean(0)[None, None, 64:]
+    x.q_idx[:] = synth.f32_to_bf16(qf)
+    dl, outs = _run_prefill(x)
+    _check_rows(x, dl, outs, {0: [10400, 12799]}, check_attn=False)
+    sel, cnt, scs, _, _ = _host(outs, "bf16")
+    for j in (10400, 12799):
+        assert sel[0, j].tolist() == list(range(512))
+        assert (scs[0, j] > 100.0).all()
+
+
 # ----------------------------------------------------------------- decode --
 def test_decode_steps_match_oracle_and_prefill_rows():
     say("decode small: 3 seqs x 9 steps")
