@@ -12,7 +12,10 @@ import math
 import os
 from dataclasses import dataclass
 
-_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libqsa.so")
+# QSA_LIBRARY names another build of the same library (the host-sanitized
+# one the sanitizer test loads); by default the in-tree libqsa.so.
+_LIB_PATH = os.environ.get("QSA_LIBRARY") or os.path.join(
+    os.path.dirname(os.path.abspath(__file__)), "libqsa.so")
 _lib = None
 
 QSA_OK, QSA_ERR_INVALID_ARGUMENT, QSA_ERR_UNSUPPORTED, QSA_ERR_WORKSPACE, QSA_ERR_DEVICE = range(5)

@@ -75,6 +75,49 @@ def build(verbose: bool = False) -> str:
     return LIB
 
 
+# Host-side sanitizers for the C-ABI layer: AddressSanitizer and UBSan on the
+# host pass only (device code is never instrumented), UB fatal.
+SAN_HOST = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+            "-Xarch_host", "-fno-sanitize-recover=all", "-Xarch_host", "-fno-omit-frame-pointer"]
+CLANGXX = "/opt/rocm/llvm/bin/clang++"
+
+
+def asan_runtime() -> str:
+    """Path of the AddressSanitizer runtime the sanitized library links to
+    (to be preloaded into an uninstrumented host process)."""
+    res = subprocess.run([CLANGXX, "-print-file-name=libclang_rt.asan-x86_64.so"],
+                         capture_output=True, text=True, check=True)
+    return res.stdout.strip()
+
+
+def build_sanitized(out: str) -> str:
+    """libqsa with the C-ABI source (qsa_api.hip: validation, workspace sizes,
+    dispatch) compiled with host ASan + UBSan, linked with the ordinary
+    objects of the kernel sources, into `out`."""
+    os.makedirs(OBJDIR, exist_ok=True)
+    objs = []
+    for src in sources():
+        if os.path.basename(src) == "qsa_api.hip":
+            obj = os.path.join(OBJDIR, "qsa_api.san.o")
+            cmd = [HIPCC, *CFLAGS, *SAN_HOST, "-c", src, "-o", obj]
+            res = subprocess.run(cmd, capture_output=True, text=True)
+            if res.returncode != 0:
+                raise RuntimeError(f"hipcc failed on {src}:\n{res.stdout}{res.stderr}")
+            objs.append(obj)
+        else:
+            obj = os.path.join(OBJDIR, os.path.basename(src) + ".o")
+            if not os.path.exists(obj) or os.path.getmtime(obj) < os.path.getmtime(src):
+                obj = _compile(src, False)
+            objs.append(obj)
+    # host link (the device code is already embedded in each object)
+    cmd = [CLANGXX, "-shared", "-fPIC", "-fsanitize=address,undefined", "-o", out, *objs,
+           "-L/opt/rocm/lib", "-lamdhip64", "-Wl,-rpath,/opt/rocm/lib"]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"sanitized link failed:\n{res.stdout}{res.stderr}")
+    return out
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--verbose", action="store_true", help="print kernel resource usage")
