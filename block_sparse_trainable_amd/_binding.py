@@ -23,9 +23,10 @@ QSA_F32, QSA_BF16 = 0, 1
 (QSA_OP_INDEX_BUILD, QSA_OP_SELECT, QSA_OP_PREFILL, QSA_OP_DECODE, QSA_OP_DECODE_STEP,
  QSA_OP_BACKWARD, QSA_OP_DISTILL) = range(7)
 # qsa_decode_step's workspace (qsa.h): a control area of this many bytes at
-# its start, zero between calls, whose int32 at this byte offset is the
-# error word (non-zero once a wait for a selection gave up).
-QSA_STEP_CONTROL_BYTES = 3227648
+# its start (zero-filled before the first call, the calls' state after),
+# whose int32 at this byte offset is the error word (non-zero once a wait
+# gave up).
+QSA_STEP_CONTROL_BYTES = 3325952
 QSA_STEP_ERROR_BYTE = 8192
 
 EXPORTED = (

@@ -181,25 +181,21 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(
 // by the previous kernel, so plain loads see them.
 template <int D>
 __global__ __launch_bounds__(D) void attn_merge_kernel(const float* __restrict__ part,
-                                                       int n_split, uint16_t* __restrict__ out,
+                                                       uint16_t* __restrict__ out,
                                                        float* __restrict__ lse) {
   constexpr int PF = part_floats(D);
+  __shared__ float ml[2 * kDecodeSplits];
   const int64_t row = blockIdx.x / 16;
   const int n = (int)(blockIdx.x % 16);
   const int dd = threadIdx.x;
-  const float* base = part + row * n_split * PF;
-  float m[kMaxSplits], z[kMaxSplits], o[kMaxSplits];
+  const float* base = part + row * kDecodeSplits * PF;
+  for (int i = dd; i < 2 * kDecodeSplits; i += D) ml[i] = base[(i >> 1) * PF + 16 * (i & 1) + n];
+  float o[kDecodeSplits];
 #pragma unroll
-  for (int k = 0; k < kMaxSplits; ++k) {  // every split's loads in flight at once
-    if (k < n_split) {
-      const float* pk = base + k * PF;
-      m[k] = pk[n];
-      z[k] = pk[16 + n];
-      o[k] = pk[32 + n * D + dd];
-    }
-  }
+  for (int k = 0; k < kDecodeSplits; ++k) o[k] = base[k * PF + 32 + n * D + dd];  // all in flight
+  __syncthreads();
   float mx, zs, acc;
-  lse_merge(m, z, o, n_split, mx, zs, acc);
+  lse_merge_splits(ml, o, mx, zs, acc);
   out[(row * 16 + n) * D + dd] = (uint16_t)f32_to_bf16(acc / zs);
   if (lse && dd == 0) lse[row * 16 + n] = (mx + log2f(zs)) * kLn2;
 }
@@ -217,9 +213,7 @@ int max_pseudo_blocks(const Dims& d) {
   return d.lr >= 2 ? (d.kB + 1) << (d.lr - 2) : (((d.kB + 1) << d.lr) + 3) / 4;
 }
 
-int decode_splits(const Dims& d) {
-  return (max_pseudo_blocks(d) + kDecodeSplitPB - 1) / kDecodeSplitPB;
-}
+int decode_splits(const Dims&) { return kDecodeSplits; }
 
 template <int HKV, int D>
 hipError_t launch_mfma(const Dims& d, int rows, int n_q, const void* q, const void* kc,
@@ -235,17 +229,17 @@ hipError_t launch_mfma(const Dims& d, int rows, int n_q, const void* q, const vo
                        static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(kc),
                        static_cast<const uint16_t*>(vc), cap, n_q, q_pos0, sel, cnt, d.kB, sl2,
                        static_cast<uint16_t*>(out), lse, part, ns,
-                       decode ? kDecodeSplitPB : max_pseudo_blocks(d), d.lr);
+                       decode ? decode_pb_per_split(max_pseudo_blocks(d)) : max_pseudo_blocks(d), d.lr);
   else
     hipLaunchKernelGGL((attn_mfma_kernel<HKV, D, false>), grid, dim3(256), 0, st,
                        static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(kc),
                        static_cast<const uint16_t*>(vc), cap, n_q, q_pos0, sel, cnt, d.kB, sl2,
                        static_cast<uint16_t*>(out), lse, part, ns,
-                       decode ? kDecodeSplitPB : max_pseudo_blocks(d), d.lr);
+                       decode ? decode_pb_per_split(max_pseudo_blocks(d)) : max_pseudo_blocks(d), d.lr);
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess || !decode || ns == 1) return e;  // one split wrote the output itself
+  if (e != hipSuccess || !decode) return e;
   hipLaunchKernelGGL((attn_merge_kernel<D>), dim3((unsigned)(rows * 16)), dim3(D), 0, st, part,
-                     ns, static_cast<uint16_t*>(out), lse);
+                     static_cast<uint16_t*>(out), lse);
   return hipGetLastError();
 }
 

@@ -66,8 +66,14 @@ struct MfmaShape {
 // the part of pseudo-block i.
 constexpr int kMaxPB = (2048 + 128) / 4;  // pseudo-blocks of one query
 constexpr int kMaxTok = 2048 + 4;         // token-mode list: r*k_B <= 2048 plus a tail of r < 4
-constexpr int kMaxSplits = 17;            // decode splits of 32 pseudo-blocks
-constexpr int kDecodeSplitPB = 32;        // pseudo-blocks per decode split
+constexpr int kDecodeSplits = 17;         // decode: splits of a query's token set
+
+// Pseudo-blocks per decode split: the largest token set (max_pb pseudo-
+// blocks) cut into kDecodeSplits equal runs (32 at k_B = 512, r = 4: one
+// 32-token tile for each of a workgroup's four waves).
+__host__ __device__ constexpr int decode_pb_per_split(int max_pb) {
+  return (max_pb + kDecodeSplits - 1) / kDecodeSplits;
+}
 
 // Floats of one split's state [m 16][l 16][O 16 x D].
 constexpr int part_floats(int D) { return 32 + 16 * D; }
@@ -351,25 +357,24 @@ __device__ __forceinline__ void attn_mfma_tiles(
   }
 }
 
-// Log-sum-exp merge of one (row, head, dim) over a row's split states, in
-// split order: M = max_k m_k, Z = sum_k 2^(m_k - M) l_k,
+// Log-sum-exp merge of one (row, head, dim) over a row's kDecodeSplits split
+// states, in split order: M = max_k m_k, Z = sum_k 2^(m_k - M) l_k,
 // A = sum_k 2^(m_k - M) O_k (splits with m_k = -inf hold no token).
-// out = A / Z, lse = (M + log2 Z) ln 2.  The caller loads the states.
-__device__ __forceinline__ void lse_merge(const float (&m)[kMaxSplits],
-                                          const float (&z)[kMaxSplits],
-                                          const float (&o)[kMaxSplits], int n_split,
-                                          float& mx, float& zs, float& acc) {
+// out = A / Z, lse = (M + log2 Z) ln 2.  ml[2k], ml[2k+1] hold m_k, l_k (the
+// caller loads them, and the O values o[k]).
+__device__ __forceinline__ void lse_merge_splits(const float* ml, const float (&o)[kDecodeSplits],
+                                                 float& mx, float& zs, float& acc) {
   mx = -INFINITY;
 #pragma unroll
-  for (int k = 0; k < kMaxSplits; ++k)
-    if (k < n_split) mx = fmaxf(mx, m[k]);
+  for (int k = 0; k < kDecodeSplits; ++k) mx = fmaxf(mx, ml[2 * k]);
   zs = 0.0f;
   acc = 0.0f;
 #pragma unroll
-  for (int k = 0; k < kMaxSplits; ++k) {
-    if (k < n_split && m[k] != -INFINITY) {
-      const float f = exp2f(m[k] - mx);
-      zs += f * z[k];
+  for (int k = 0; k < kDecodeSplits; ++k) {
+    const float mk = ml[2 * k];
+    if (mk != -INFINITY) {
+      const float f = exp2f(mk - mx);
+      zs += f * ml[2 * k + 1];
       acc += f * o[k];
     }
   }

@@ -2,56 +2,62 @@
 // the block the new token completes, block scoring, top-k_B selection and
 // sparse attention with its split merge.
 //
-// "QSA (Qwen Sparse Attention)", Key math / How it works: (A) compressed
-// lightweight indexer (block compression, I_ib = sum_h ReLU(<q^h, k_b>) over
-// complete earlier blocks, top-k_B blocks expanded to tokens plus the tail)
-// and (B) sparse core attention over those tokens; the concept page's "Why
-// it matters" reports the decode phase at long context.  "Qwen Sparse
+// "QSA (Qwen Sparse Attention)", Key math / How it works: (A) the compressed
+// indexer (block compression, I_ib = sum_h ReLU(<q^h, k_b>) over complete
+// earlier blocks, top-k_B blocks expanded to tokens plus the tail) and (B)
+// softmax attention over those tokens only; the concept page's "Why it
+// matters" reports the decode phase at long context.  "Qwen Sparse
 // Attention" gallery page, How block selection works.
 //
 // The arithmetic is that of qsa_index_build + qsa_select_topk (n_q = 1) +
 // qsa_sparse_attn_decode -- the same device code (compress_block.h, the
-// decode scoring MFMA layout, select_common.h, attn_tile.h) -- so the results
-// are bit-identical to those three calls.  What differs is the hand-off
-// between the stages: instead of kernel boundaries (each of which costs a
-// few microseconds and drains the GPU), workgroups hand data to each other
-// through the workspace with coherent (agent-scope) accesses, each hand-off
-// a single coalesced round trip:
+// decode scoring MFMA layout, select_common.h, attn_tile.h) and the same
+// split partition and merge order -- so the results are bit-identical to
+// those three calls.  What differs is the hand-off between the stages.
 //
-//   score workgroups (row, segment of 1024 blocks; a row's last segment also
-//   takes a remainder of up to 512, so 65,5xx-block rows need 64 of them)
-//     - MFMA scores of the segment (the decode scoring kernel's layout), then
-//       a counting sort of the segment's (score, id) pairs by histogram bin,
-//       highest bin first, staged in LDS and stored whole, with the
-//       segment's suffix counts cum[b] = #scores with bin >= b, which are
-//       also added (atomically) into the row's suffix counts;
-//     - the last workgroup of a row to finish (completion counter) selects:
-//       the row's suffix counts give the threshold bin d*, each segment's
-//       candidates (bin >= d*) are a prefix of its sorted list (all fetched
-//       at once), an MSB radix select finds the exact threshold among bin d*,
-//       equal scores go to the lower id (a second radix select over the
-//       ids), and an id bitmap with prefix popcounts ranks the kept ids in
-//       ascending order.  It writes the outputs and the row's selection
-//       record: entry i = id_i + 1 for i < count, NONE for count <= i <= k_B;
-//   attention workgroups (row, split of 32 pseudo-blocks), last in the grid
-//     - split 0 first compresses the block the new token completes (not a
-//       candidate of this step: the candidates are blocks < floor(p/4));
-//     - load the query, then poll the record entries of the split (and the
-//       one before it) until all are written -- the entries themselves are
-//       the ready signal; the first NONE marks the tail pseudo-block;
-//     - attend over the split, store the split state; the last split to
-//       finish clears the record and merges the states (log-sum-exp).
+// A row (one sequence's new token) is served by the workgroups of its score
+// segments (1024 blocks each; the last one also takes a remainder of up to
+// 512):
+//   P1 every workgroup scores its segment with MFMA, sorts the (score, id)
+//      pairs by score bin (256 monotone bins, highest first), stores them
+//      with the segment's suffix counts cum[b] = #scores with bin >= b, adds
+//      those counts into the row's, and raises its flag.  Workgroups past
+//      the first kDecodeSplits leave here.
+//   P2 the first min(n_seg, kDecodeSplits) workgroups wait for every flag of
+//      the row; then each derives the selection by itself: the threshold bin
+//      d* from the row's counts, every segment's number of entries above and
+//      at d* (its entries with bin >= d* head its sorted list), all of those
+//      entries at once, which bin-d* ones are kept -- the largest scores,
+//      equal scores to the lower id -- and each kept id's position (its rank
+//      among the kept ids).  It writes the positions its attention splits
+//      cover and the splits' block lists;
+//   P3 it attends that split (the token set cut into kDecodeSplits runs of
+//      pseudo-blocks), stores the split's (m, l, O) state and raises the
+//      split's flag;
+//   P4 up to 16 of them wait for every split flag and merge one head each
+//      (log-sum-exp, in split order) into the output.
+// So a row crosses two waits: one after scoring, one before the merge.  A
+// wait is a poll of the row's flags (one load per flag, all in flight), not
+// a shared counter: arrivals are plain stores and never queue on one address.
 //
-// Forward progress: a score workgroup never waits, and a launch holds at most
-// as many attention workgroups (which wait) as the device keeps resident
-// minus 64 (measured occupancy x CUs; larger batches are split over several
-// launches), so they cannot crowd out the score workgroups: every score
-// workgroup is eventually resident and every record is eventually written.
-// The spin is bounded all the same; on expiry the workgroup records an error
-// word in the workspace and proceeds (wrong values, no hang).
+// A flag holds the epoch of the call that raised it: the row's generation
+// word plus one.  Every workgroup of the row reads the generation word when
+// it starts; workgroup 0 advances it once all scoring flags are up (so every
+// reader has read it), and flags never need clearing.  The row's score-bin
+// counts alternate between two buffers by epoch parity; workgroup 0 clears
+// the one the row's next call will use.
+//
+// Forward progress: a row's workgroups are consecutive in the grid and the
+// dispatcher starts workgroups in grid order.  Only the row's first
+// kDecodeSplits workgroups wait, and only for workgroups of their own row,
+// which either run (scoring never waits) or are next to start once a slot
+// frees.  Every wait is bounded all the same; on expiry the workgroup sets
+// the error word in the workspace and proceeds (wrong values, no hang).
 //
 // The control area at the start of the workspace must be zero-filled before
-// its first use; every completed call leaves it zero.
+// the first call.  Between calls it holds the generation words, flags and
+// counts; zero-filling it again between calls is always allowed (and needed
+// after a call that set the error word).
 #include <atomic>
 
 #include "attn_tile.h"
@@ -67,32 +73,41 @@ constexpr int kCpw = 2;                          // 64-block chunks per wave per
 constexpr int kRoundBlocks = kNW * kCpw * 64;    // 512
 constexpr int kMaxRounds = kStepSegMax / kRoundBlocks;  // 3
 constexpr int kPerThread = kStepSegMax / kNT;    // 6 scores per thread in the sort
-constexpr int kFCap = 4096;                      // candidates held in LDS
-constexpr int kGatherPT = kFCap / kNT;           // 16 candidate loads per thread
-constexpr int kDirect = kNT;                     // bin-d* sets ranked directly (<= kNT)
+constexpr int kMaxKB = 512;                      // k_B of the fused step
+constexpr int kFlatCap = 2560;                   // entries with bin >= d* held by a workgroup
+constexpr int kFPT = kFlatCap / kNT;             // 10 per thread
+constexpr int kMkCap = kFlatCap;                 // boundary-group entries ranked in LDS
+constexpr int kGroupPT = kMkCap / kNT;           // 10 per thread
 constexpr int kSegArr = 2 * kNT;                 // per-segment arrays (>= kStepMaxSegs)
-constexpr uint32_t kNone = 0xFFFFFFFFu;          // record entry past the count
+constexpr int kMaxRunPB = 32;                    // pseudo-blocks of one split (>= P)
+constexpr int kFlagPerLane = (kStepFaStride + 63) / 64;
 constexpr uint32_t kSpinLimit = 1u << 22;
-static_assert(kStepMaxSegs <= kSegArr, "segment arrays");
+static_assert(kStepMaxSegs <= kSegArr && kStepMaxSegs <= kStepFaStride, "segment arrays");
+static_assert(kDecodeSplits <= kStepFcStride, "split flags");
 static_assert(kMaxRounds * kRoundBlocks == kStepSegMax, "segments are whole rounds");
-static_assert(kStepRecStride >= 512 + 1, "record holds k_B + 1 entries");
+static_assert(decode_pb_per_split(kMaxKB + 1) <= kMaxRunPB, "split size");
+static_assert(kFlatCap % kNT == 0 && kMkCap % kNT == 0, "per-thread shares");
 
-// LDS carve-up of the selection role (bytes)
-constexpr int kOffKey = 0;
-constexpr int kOffIdx = kOffKey + 4 * kFCap;
-constexpr int kOffBm = kOffIdx + 4 * kFCap;
-constexpr int kOffRh = kOffBm + 4 * kStepBmWords;
-constexpr int kOffSegLen = kOffRh + 4 * kRadixBins;
-constexpr int kOffSegOff = kOffSegLen + 4 * kSegArr;
-constexpr int kOffTbase = kOffSegOff + 4 * kSegArr;
-constexpr int kOffScr = kOffTbase + 4 * kNT;
+// LDS carve-up (bytes).  Scoring: scores, bin counts, sorted pairs.  The
+// selection reuses that room once scoring is over (a row with c <= k_B
+// keeps its scores for the outputs and never selects).
+constexpr int kOffSc = 0;                                // float [kStepSegMax] scores
+constexpr int kOffBins = kOffSc + 4 * kStepSegMax;       // u32 [256]: this segment's suffix counts
+constexpr int kOffCurs = kOffBins + 4 * 256;             // u32 [256]
+constexpr int kOffSorted = kOffCurs + 4 * 256;           // u64 [kStepSegMax] (key, id) by bin
+constexpr int kOffFseg = 0;                              // u32 [kFlatCap] list slot -> segment
+constexpr int kOffMk = kOffFseg + 4 * kFlatCap;          // u64 [kMkCap + 16] boundary group
+constexpr int kOffRh = kOffMk + 8 * (kMkCap + 16);       // u32 [kRadixBins] radix / sub-bins
+constexpr int kOffHi = kOffRh + 4 * kRadixBins;          // u32 [kSegArr] per segment: bin > d*
+constexpr int kOffEq = kOffHi + 4 * kSegArr;             // u32 [kSegArr] ... bin == d*
+constexpr int kOffFo = kOffEq + 4 * kSegArr;             // u32 [kSegArr] ... list offsets
+constexpr int kOffSFirst = kOffFo + 4 * kSegArr;         // u32 [kSegArr] ... first kept index
+constexpr int kOffSLast = kOffSFirst + 4 * kSegArr;      // u32 [kSegArr] ... last kept index
+constexpr int kOffKId = kOffSLast + 4 * kSegArr;         // u32 [kMaxKB] kept ids
+constexpr int kOffKKey = kOffKId + 4 * kMaxKB;           // u32 [kMaxKB] ... their keys
+constexpr int kOffKSeg = kOffKKey + 4 * kMaxKB;          // u32 [kMaxKB] ... their segments
+constexpr int kOffScr = kOffKSeg + 4 * kMaxKB;           // u32 [64] scratch
 constexpr int kSelLds = kOffScr + 4 * 64;
-// score role (aliases the start of the selection area)
-constexpr int kOffSc = 0;                           // float [kStepSegMax]
-constexpr int kOffBins = kOffSc + 4 * kStepSegMax;  // u32 [256]
-constexpr int kOffCurs = kOffBins + 4 * 256;        // u32 [256]
-constexpr int kOffSorted = kOffCurs + 4 * 256;      // u64 [kStepSegMax]
-static_assert(kOffSorted + 8 * kStepSegMax <= kOffRh, "score role fits below the radix area");
 
 struct StepArgs {
   const uint16_t* q_idx;  // [B][4][128]
@@ -113,15 +128,15 @@ struct StepArgs {
   float* sel_scores;
   uint16_t* out;
   float* lse;
-  uint32_t* rowcnt;   // [B] score arrivals
-  uint32_t* attncnt;  // [B] split arrivals
-  uint32_t* err;
-  uint32_t* rec;      // [B][kStepRecStride] selection records
+  uint32_t* gen;      // [kStepMaxBatch] per-row generation             (control area)
+  uint32_t* fa;       // [kStepMaxBatch][kStepFaStride] scoring flags   (control)
+  uint32_t* fc;       // [kStepMaxBatch][kStepFcStride] split flags     (control)
+  uint32_t* err;      //                                                (control)
+  uint32_t* acc;      // [kStepMaxBatch][2][256] row suffix counts      (control)
   uint2* pairs;       // [B][n_seg][kStepSegMax]
   uint32_t* cum;      // [B][n_seg][128]  (u16 pairs: bins 2w, 2w+1)
-  uint32_t* acc;      // [B][256] row suffix counts, summed by the segments (control area)
-  float* part;        // [B][n_split][part_floats(D)]
-  int n_seg, n_split, n_score_wg;
+  float* part;        // [B][kDecodeSplits][part_floats(D)]
+  int n_seg, pb_per_split;
 };
 
 __device__ __forceinline__ int64_t row_c(const StepArgs& a, int s) {
@@ -133,419 +148,55 @@ __device__ __forceinline__ unsigned long long pack_pair(uint32_t key, uint32_t i
   return (unsigned long long)key | ((unsigned long long)id << 32);
 }
 
-__device__ __forceinline__ uint32_t cum_field(unsigned long long v, int e) {
-  return (uint32_t)(v >> (16 * e)) & 0xFFFFu;
-}
-
-// ------------------------------------------------------------- selection ----
-// Ranks through the id bitmap bm (a set bit per kept id).  After
-// bitmap_prefix, pre[G] (u16) is the number of kept ids below word 4G, so the
-// rank of a kept id -- the number of kept ids below it -- takes the group
-// prefix, at most three whole words and one masked word, all independent
-// reads.  Each thread sums its contiguous run of wpt words (a multiple of 4,
-// read 16 bytes at a time; nwords is a multiple of 4, the bitmap cleared up
-// to it).
-__device__ __forceinline__ void bitmap_prefix(const uint32_t* bm, uint16_t* pre, uint32_t* scr,
-                                              int nwords, int wpt) {
-  const int w0 = (int)threadIdx.x * wpt, w1 = min(w0 + wpt, nwords);
-  uint32_t pc = 0;
-  for (int w = w0; w < w1; w += 4) {
-    const u32x4 q = *reinterpret_cast<const u32x4*>(bm + w);
-    pc += __popc(q[0]) + __popc(q[1]) + __popc(q[2]) + __popc(q[3]);
-  }
-  uint32_t tot;
-  uint32_t run = block_excl_scan<kNT>(pc, scr, &tot);
-  for (int w = w0; w < w1; w += 4) {
-    const u32x4 q = *reinterpret_cast<const u32x4*>(bm + w);
-    pre[w >> 2] = (uint16_t)run;
-    run += __popc(q[0]) + __popc(q[1]) + __popc(q[2]) + __popc(q[3]);
-  }
-  __syncthreads();
-}
-
-__device__ __forceinline__ uint32_t bitmap_rank(const uint32_t* bm, const uint16_t* pre,
-                                                uint32_t id) {
-  const int w = (int)(id >> 5);
-  const int g0 = w & ~3;
-  uint32_t rank = pre[w >> 2] + __popc(bm[w] & ((1u << (id & 31u)) - 1u));
-  rank += (g0 + 0 < w) ? __popc(bm[g0 + 0]) : 0u;
-  rank += (g0 + 1 < w) ? __popc(bm[g0 + 1]) : 0u;
-  rank += (g0 + 2 < w) ? __popc(bm[g0 + 2]) : 0u;
-  return rank;
-}
-
-// Selects row s (run by the row's last score workgroup); writes sel, cnt,
-// sel_scores and the row's record.
-__device__ __forceinline__ void select_row(const StepArgs& a, int s, int64_t c, int nseg_row,
-                           unsigned char* smem) {
-  const int tid = threadIdx.x;
-  uint32_t* ckey = reinterpret_cast<uint32_t*>(smem + kOffKey);
-  uint32_t* cidx = reinterpret_cast<uint32_t*>(smem + kOffIdx);
-  uint32_t* bm = reinterpret_cast<uint32_t*>(smem + kOffBm);
-  uint32_t* rh = reinterpret_cast<uint32_t*>(smem + kOffRh);
-  uint32_t* seglen = reinterpret_cast<uint32_t*>(smem + kOffSegLen);
-  uint32_t* segoff = reinterpret_cast<uint32_t*>(smem + kOffSegOff);
-  uint32_t* scr = reinterpret_cast<uint32_t*>(smem + kOffScr);
-  uint16_t* pre = reinterpret_cast<uint16_t*>(rh);  // bitmap group prefixes (after the radix)
-  uint32_t* o_id = seglen;     // staged output (after the gather)
-  uint32_t* o_key = segoff;
-  const int kB = a.kB;
-  int32_t* out = a.sel + (int64_t)s * kB;
-  float* outs = a.sel_scores ? a.sel_scores + (int64_t)s * kB : nullptr;
-  uint32_t* rec = a.rec + (int64_t)s * kStepRecStride;
-  const unsigned long long* prow =
-      reinterpret_cast<const unsigned long long*>(a.pairs) + (int64_t)s * a.n_seg * kStepSegMax;
-
-  uint32_t* racc = a.acc + (int64_t)s * 256;
-  if (c <= kB) {  // every candidate is kept; they all sit in segment 0
-    coherent_store(&racc[tid], 0u);  // leave the row's counts zeroed
-    for (int i = tid; i < c; i += kNT) {
-      const unsigned long long v = coherent_load(&prow[i]);
-      o_key[(uint32_t)(v >> 32)] = (uint32_t)v;
-    }
-    __syncthreads();
-    for (int i = tid; i <= kB; i += kNT) {
-      if (i < kB) {
-        out[i] = i < c ? i : -1;
-        if (outs) outs[i] = i < c ? __uint_as_float(o_key[i]) : 0.0f;
+// Wave 0 polls flags[0 .. n) (n <= kStepFaStride) until each holds epoch,
+// bounded (on expiry the error word is set); the barrier after it releases
+// the workgroup.
+__device__ __forceinline__ void wait_flags(const StepArgs& a, const uint32_t* flags, int n,
+                                           uint32_t epoch) {
+  if (threadIdx.x < 64) {
+    const int lane = threadIdx.x;
+    uint32_t spins = 0;
+    while (true) {
+      uint32_t v[kFlagPerLane];
+#pragma unroll
+      for (int u = 0; u < kFlagPerLane; ++u) {
+        const int i = lane + 64 * u;
+        v[u] = i < n ? coherent_load(&flags[i]) : epoch;
       }
-      coherent_store(&rec[i], i < c ? (uint32_t)i + 1u : kNone);
-    }
-    if (tid == 0) a.cnt[s] = (int32_t)c;
-    return;
-  }
-
-  // ---- 1. row suffix counts S(b), summed by the segments as they finished,
-  // and in the same round trip the first P entries of every segment's list
-  // (P = 64, 32 or 16 as the segments number up to 64, 128 or 256): a
-  // segment's candidates lead its list, and there are rarely more than P.
-  const int lp = nseg_row <= 64 ? 6 : (nseg_row <= 128 ? 5 : 4);
-  const bool pre_ok = nseg_row <= kFCap / 16;
-  const uint32_t nslot = pre_ok ? (uint32_t)nseg_row << lp : 0u;
-  const uint32_t S_t = coherent_load(&racc[tid]);  // thread t: bin t
-  unsigned long long pv[kGatherPT];
+      bool up = true;
 #pragma unroll
-  for (int u = 0; u < kGatherPT; ++u) {  // unconditional: past the slots, slot 0 again
-    const uint32_t i = (uint32_t)tid + (uint32_t)kNT * u;
-    const uint32_t ic = i < nslot ? i : 0u;
-    pv[u] = coherent_load(&prow[(int64_t)(ic >> lp) * kStepSegMax + (ic & ((1u << lp) - 1u))]);
-  }
-  {
-    coherent_store(&racc[tid], 0u);                   // leave the row's counts zeroed
-    rh[1024 + tid] = S_t;
-    __syncthreads();
-    const uint32_t S_next = tid < 255 ? rh[1024 + tid + 1] : 0u;
-    if (S_t >= (uint32_t)kB && S_next < (uint32_t)kB) {  // S(0) = c > k_B: one such bin
-      scr[8] = (uint32_t)tid;
-      scr[9] = S_next;
-      scr[10] = S_t;
-    }
-    __syncthreads();
-  }
-  const uint32_t dstar = scr[8];
-  const uint32_t n_sure = scr[9];
-  const uint32_t total = scr[10];
-  const uint32_t n_maybe = total - n_sure;
-  const uint32_t need = (uint32_t)kB - n_sure;
-  // ---- 2. the candidates (bin >= d*) in LDS, slots [0, N) of ckey/cidx --
-  // fast: the loaded prefixes, when they hold all S(d*) candidates (each
-  // segment's candidates lead its prefix; the other slots hold entries below
-  // d*); else gathered: the first cum[g][d*] entries of every segment's list,
-  // packed.
-  bool fast = false, gathered = false;
-  uint32_t N = 0;
-  if (pre_ok) {
-    uint32_t ncand = 0;
-#pragma unroll
-    for (int u = 0; u < kGatherPT; ++u) {
-      const uint32_t i = (uint32_t)tid + (uint32_t)kNT * u;
-      ckey[i] = (uint32_t)pv[u];
-      cidx[i] = (uint32_t)(pv[u] >> 32);
-      ncand += (i < nslot && score_bin((uint32_t)pv[u]) >= dstar) ? 1u : 0u;
-    }
-    uint32_t nloaded;
-    (void)block_excl_scan<kNT>(ncand, scr, &nloaded);
-    fast = nloaded == total;
-    N = nslot;
-  }
-  const int nwords = (int)((c + 127) / 128) * 4;          // whole groups of 4 words
-  const int wpt = (nwords + 4 * kNT - 1) / (4 * kNT) * 4;  // contiguous words per thread
-  if (!fast) {
-    {
-      const uint32_t* crow32 = a.cum + (int64_t)s * a.n_seg * 128;
-      for (int g = tid; g < nseg_row; g += kNT) {
-        const uint32_t w = coherent_load(&crow32[(int64_t)g * 128 + (dstar >> 1)]);
-        seglen[g] = (dstar & 1u) ? (w >> 16) : (w & 0xFFFFu);
+      for (int u = 0; u < kFlagPerLane; ++u) up = up && v[u] == epoch;
+      if (__ballot(!up) == 0ull) break;
+      if (++spins >= kSpinLimit) {
+        if (lane == 0) coherent_store(a.err, 1u);
+        break;
       }
-    }
-    __syncthreads();
-    {
-      const uint32_t v0 = 2 * tid < nseg_row ? seglen[2 * tid] : 0u;
-      const uint32_t v1 = 2 * tid + 1 < nseg_row ? seglen[2 * tid + 1] : 0u;
-      uint32_t tot;
-      const uint32_t ex = block_excl_scan<kNT>(v0 + v1, scr, &tot);
-      segoff[2 * tid] = ex;
-      segoff[2 * tid + 1] = ex + v0;
-      __syncthreads();
-    }
-    if (total <= (uint32_t)kFCap) {
-      // Slot i (< total <= 4096) belongs to the last segment starting at or
-      // before it: mark each non-empty segment at its first slot, take a
-      // running max over the slots (16 consecutive per thread, then across
-      // threads), then issue every slot's load at once.
-      uint32_t* tab = cidx;  // slot -> segment, overwritten by the ids below
-      for (int i = 4 * tid; i < kFCap; i += 4 * kNT)  // every slot: segments stay in range
-        *reinterpret_cast<u32x4*>(tab + i) = u32x4{0u, 0u, 0u, 0u};
-      __syncthreads();
-      for (int g = tid; g < nseg_row; g += kNT)
-        if (seglen[g] != 0u) tab[segoff[g]] = (uint32_t)g;
-      __syncthreads();
-      uint32_t run[kGatherPT];
-      uint32_t mx = 0u;
-#pragma unroll
-      for (int u = 0; u < kGatherPT; u += 4) {
-        const u32x4 t4 = *reinterpret_cast<const u32x4*>(tab + kGatherPT * tid + u);
-        run[u] = t4[0];
-        run[u + 1] = t4[1];
-        run[u + 2] = t4[2];
-        run[u + 3] = t4[3];
-      }
-#pragma unroll
-      for (int u = 0; u < kGatherPT; ++u) run[u] = mx = max(mx, run[u]);
-      // exclusive max over the threads before this one (segments only grow)
-      {
-        const int lane = tid & 63, wave = tid >> 6;
-        const uint32_t incl = wave_incl_max(mx);
-        if (lane == 63) scr[20 + wave] = incl;
-        __syncthreads();
-        uint32_t before = __shfl_up(incl, 1);
-        if (lane == 0) before = 0u;
-#pragma unroll
-        for (int w = 0; w < kNW; ++w)
-          if (w < wave) before = max(before, scr[20 + w]);
-#pragma unroll
-        for (int u = 0; u < kGatherPT; ++u) run[u] = max(run[u], before);
-      }
-      unsigned long long v[kGatherPT];
-#pragma unroll
-      for (int u = 0; u < kGatherPT; ++u) {
-        const uint32_t i = (uint32_t)(kGatherPT * tid + u);
-        const uint32_t g = run[u];
-        v[u] = i < total ? coherent_load(&prow[(int64_t)g * kStepSegMax + (i - segoff[g])]) : 0ull;
-      }
-#pragma unroll
-      for (int u = 0; u < kGatherPT; ++u) {
-        const uint32_t i = (uint32_t)(kGatherPT * tid + u);
-        if (i < total) {
-          ckey[i] = (uint32_t)v[u];
-          cidx[i] = (uint32_t)(v[u] >> 32);
-        }
-      }
-      gathered = true;
-      N = total;
-    }
-  }
-
-  if (fast || gathered) {
-    for (int w = 4 * tid; w < nwords; w += 4 * kNT)  // nwords: a multiple of 4
-      *reinterpret_cast<u32x4*>(bm + w) = u32x4{0u, 0u, 0u, 0u};
-    __syncthreads();
-    // ---- 3. exact choice among the bin-d* candidates -------------------------
-    // need of the n_maybe candidates in bin d* are kept: the largest scores,
-    // equal scores to the lower id.  Packed as (key << 32 | ~id), that order
-    // is the integer order of distinct 64-bit values.  Up to kDirect of them
-    // are ranked directly (rank = number of larger packed values); larger
-    // sets go through an MSB radix select, then one over the ids for ties.
-    // Slots below d* (fast path only) are never eligible.
-    const bool some = need < n_maybe;  // else every bin-d* candidate is kept
-    const bool direct = some && n_maybe <= (uint32_t)kDirect;
-    Radix r{0u, 0u, need, need}, r2{0u, 0u, 0u, 0u};
-    if (direct) {
-      unsigned long long* mk = reinterpret_cast<unsigned long long*>(rh);  // [kDirect + 16]
-      uint32_t* mslot = rh + 2 * (kDirect + 16);                           // [kDirect]
-      uint32_t cm = 0;
-#pragma unroll
-      for (int u = 0; u < kGatherPT; ++u) {
-        const uint32_t i = (uint32_t)tid + (uint32_t)kNT * u;
-        cm += (i < N && score_bin(ckey[i]) == dstar) ? 1u : 0u;
-      }
-      uint32_t tot;
-      uint32_t pos = block_excl_scan<kNT>(cm, scr, &tot);
-#pragma unroll
-      for (int u = 0; u < kGatherPT; ++u) {
-        const uint32_t i = (uint32_t)tid + (uint32_t)kNT * u;
-        if (i < N && score_bin(ckey[i]) == dstar) {
-          mk[pos] = ((unsigned long long)ckey[i] << 32) | (0x7FFFFFFFu - cidx[i]);
-          mslot[pos] = i;
-          ++pos;
-        }
-      }
-      // pad to a multiple of 16 with values below every member
-      if (tid < 16) mk[n_maybe + tid] = 0ull;
-      __syncthreads();
-      if (tid < (int)n_maybe) {
-        const unsigned long long me = mk[tid];
-        uint32_t rank = 0;
-        for (uint32_t j = 0; j < n_maybe; j += 16) {  // 16 broadcast reads in flight
-          unsigned long long w[16];
-#pragma unroll
-          for (int e = 0; e < 16; e += 2) {
-            const u32x4 q = *reinterpret_cast<const u32x4*>(mk + j + e);
-            w[e] = (unsigned long long)q[0] | ((unsigned long long)q[1] << 32);
-            w[e + 1] = (unsigned long long)q[2] | ((unsigned long long)q[3] << 32);
-          }
-#pragma unroll
-          for (int e = 0; e < 16; ++e) rank += w[e] > me ? 1u : 0u;
-        }
-        if (rank < need) cidx[mslot[tid]] |= 0x80000000u;  // kept
-      }
-      __syncthreads();
-    } else if (some) {
-      auto key = [&](int64_t i) { return ckey[i]; };
-      auto elig = [&](int64_t i) { return score_bin(ckey[i]) == dstar; };
-      if (dstar > 0u && dstar < (uint32_t)kHistBins - 1u)
-        r = radix_select<kNT, true>(key, elig, (int64_t)N, need, rh, scr, 1, (dstar + 888u) << 20,
-                              0x7FFu << 20);
-      else
-        r = radix_select<kNT, true>(key, elig, (int64_t)N, need, rh, scr);
-    }
-    const bool tie = some && !direct && r.avail > r.need;
-    if (tie) {  // equal scores at the threshold: the lowest ids win
-      auto key2 = [&](int64_t i) { return 0x7FFFFFFFu - cidx[i]; };
-      auto elig2 = [&](int64_t i) {
-        return score_bin(ckey[i]) == dstar && (ckey[i] & r.mask) == r.prefix;
-      };
-      r2 = radix_select<kNT, true>(key2, elig2, (int64_t)N, r.need, rh, scr);
-    }
-    __syncthreads();
-    // ---- 4. the kept entries, packed into slots [0, k_B) (all reads first,
-    // then the branch-free choice), then in ascending order via an id bitmap
-    {
-      uint32_t kk[kGatherPT], kx[kGatherPT];
-#pragma unroll
-      for (int u = 0; u < kGatherPT; ++u) {
-        const uint32_t i = (uint32_t)tid + (uint32_t)kNT * u;
-        kk[u] = ckey[i];
-        kx[u] = cidx[i];
-      }
-      uint32_t kmask = 0, nk = 0;
-#pragma unroll
-      for (int u = 0; u < kGatherPT; ++u) {
-        const uint32_t i = (uint32_t)tid + (uint32_t)kNT * u;
-        const uint32_t b = score_bin(kk[u]);
-        const uint32_t m = kk[u] & r.mask;
-        const bool won = direct ? (kx[u] >> 31) != 0u
-                                : (m > r.prefix ||
-                                   (m == r.prefix &&
-                                    (!tie || ((0x7FFFFFFFu - kx[u]) & r2.mask) >= r2.prefix)));
-        const bool kp = i < N && (b > dstar || (b == dstar && (!some || won)));
-        kmask |= kp ? 1u << u : 0u;
-        nk += kp ? 1u : 0u;
-      }
-      uint32_t nkept;
-      uint32_t pos = block_excl_scan<kNT>(nk, scr, &nkept);  // reads above precede its barriers
-#pragma unroll
-      for (int u = 0; u < kGatherPT; ++u)
-        if ((kmask >> u) & 1u) {
-          ckey[pos] = kk[u];
-          cidx[pos] = kx[u] & 0x7FFFFFFFu;
-          ++pos;
-        }
-    }
-    __syncthreads();
-    constexpr int kPerT = 512 / kNT;  // kept entries per thread (k_B <= 512)
-#pragma unroll
-    for (int e = 0; e < kPerT; ++e) {
-      const int i = tid + kNT * e;
-      if (i < kB) {
-        const uint32_t id = cidx[i];
-        atomicOr(&bm[id >> 5], 1u << (id & 31u));
-      }
-    }
-    __syncthreads();
-    bitmap_prefix(bm, pre, scr, nwords, wpt);
-#pragma unroll
-    for (int e = 0; e < kPerT; ++e) {
-      const int i = tid + kNT * e;
-      if (i < kB) {
-        const uint32_t id = cidx[i];
-        const uint32_t rank = bitmap_rank(bm, pre, id);
-        if (rank < (uint32_t)kB) {
-          o_id[rank] = id;
-          o_key[rank] = ckey[i];
-        }
-      }
-    }
-  } else {
-    // ---- fallback: exact selection over the whole row ---------------------
-    // Entry i of the row's c entries: segment min(i / 1024, last), whose
-    // list holds that segment's entries at stride kStepSegMax.
-    for (int w = 4 * tid; w < nwords; w += 4 * kNT)  // (published by the barriers below)
-      *reinterpret_cast<u32x4*>(bm + w) = u32x4{0u, 0u, 0u, 0u};
-    auto at = [&](int64_t i) {
-      const int64_t g = min(i / kStepSeg, (int64_t)nseg_row - 1);
-      return coherent_load(&prow[g * kStepSegMax + (i - g * kStepSeg)]);
-    };
-    auto key = [&](int64_t i) { return (uint32_t)at(i); };
-    auto all = [&](int64_t) { return true; };
-    const Radix r = radix_select<kNT>(key, all, c, (uint32_t)kB, rh, scr);
-    const bool tie = r.avail > r.need;
-    Radix r2{0u, 0u, 0u, 0u};
-    if (tie) {
-      auto key2 = [&](int64_t i) { return 0x7FFFFFFFu - (uint32_t)(at(i) >> 32); };
-      auto elig2 = [&](int64_t i) { return (key(i) & r.mask) == r.prefix; };
-      r2 = radix_select<kNT>(key2, elig2, c, r.need, rh, scr);
-    }
-    auto keep = [&](unsigned long long v) {
-      const uint32_t m = (uint32_t)v & r.mask;
-      if (m != r.prefix) return m > r.prefix;
-      return !tie || ((0x7FFFFFFFu - (uint32_t)(v >> 32)) & r2.mask) >= r2.prefix;
-    };
-    __syncthreads();
-    for (int64_t i = tid; i < c; i += kNT) {
-      const unsigned long long v = at(i);
-      const uint32_t id = (uint32_t)(v >> 32);
-      if (keep(v)) atomicOr(&bm[id >> 5], 1u << (id & 31u));
-    }
-    __syncthreads();
-    bitmap_prefix(bm, pre, scr, nwords, wpt);
-    for (int64_t i = tid; i < c; i += kNT) {
-      const unsigned long long v = at(i);
-      if (!keep(v)) continue;
-      const uint32_t rank = bitmap_rank(bm, pre, (uint32_t)(v >> 32));
-      if (rank < (uint32_t)kB) {
-        o_id[rank] = (uint32_t)(v >> 32);
-        o_key[rank] = (uint32_t)v;
-      }
+      __builtin_amdgcn_s_sleep(1);
     }
   }
   __syncthreads();
-  // ---- 5. outputs and the record (coalesced) -------------------------------
-  for (int i = tid; i <= kB; i += kNT) {
-    if (i < kB) {
-      out[i] = (int32_t)o_id[i];
-      if (outs) outs[i] = __uint_as_float(o_key[i]);
-    }
-    coherent_store(&rec[i], i < kB ? o_id[i] + 1u : kNone);
-  }
-  if (tid == 0) a.cnt[s] = (int32_t)kB;
 }
 
-// ---------------------------------------------------------------- scoring ----
-// Workgroup (row s, segment g): the scores of the segment's blocks, as the
-// decode scoring kernel computes them (rows of the A tile = 4 x query +
-// head; only query 0 is live), sorted by bin and stored.
-__device__ __forceinline__ void score_segment(const StepArgs& a, int64_t wg, unsigned char* smem) {
+// Suffix count of bin b (0..256) from a segment's packed cum words.
+__device__ __forceinline__ uint32_t cum_at(const uint32_t* words, uint32_t b) {
+  if (b >= 256u) return 0u;
+  const uint32_t w = coherent_load(&words[b >> 1]);
+  return (b & 1u) ? (w >> 16) : (w & 0xFFFFu);
+}
+
+// ---------------------------------------------------------------- P1 -------
+// Scores of the segment's blocks, as the decode scoring kernel computes them
+// (rows of the A tile = 4 x query + head; only query 0 is live), sorted by
+// bin, stored, their suffix counts added into the row's (acc_row), and the
+// segment's flag raised.  Leaves the scores in sc.
+__device__ __forceinline__ void score_segment(const StepArgs& a, int s, int g, int64_t c,
+                                              int nseg_row, uint32_t* acc_row, uint32_t epoch,
+                                              unsigned char* smem) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int l16 = lane & 15;
   const int gq = lane >> 4;
-  const int s = (int)(wg / a.n_seg);
-  const int g = (int)(wg % a.n_seg);
-  const int64_t c = row_c(a, s);
-  const int nseg_row = step_nseg(c);
-  if (g >= nseg_row) return;  // not part of this row
   const int64_t seg_lo = (int64_t)g * kStepSeg;
   const int64_t seg_hi = (g == nseg_row - 1) ? c : seg_lo + kStepSeg;
   const int n_here = (int)max(seg_hi - seg_lo, (int64_t)0);
@@ -613,7 +264,7 @@ __device__ __forceinline__ void score_segment(const StepArgs& a, int64_t wg, uns
     bins[255 - tid] = start + nb;  // suffix count: scores with bin >= 255 - t
     // the row's suffix counts accumulate as the segments finish
     if (start + nb)
-      __hip_atomic_fetch_add(&a.acc[(int64_t)s * 256 + 255 - tid], start + nb, __ATOMIC_RELAXED,
+      __hip_atomic_fetch_add(&acc_row[255 - tid], start + nb, __ATOMIC_RELAXED,
                              __HIP_MEMORY_SCOPE_AGENT);
     __syncthreads();
   }
@@ -636,188 +287,532 @@ __device__ __forceinline__ void score_segment(const StepArgs& a, int64_t wg, uns
                    bins[2 * tid] | (bins[2 * tid + 1] << 16));
   stores_complete();
   __syncthreads();
-  if (tid == 0) scr[12] = arrive_last(&a.rowcnt[s], (uint32_t)nseg_row) ? 1u : 0u;
-  __syncthreads();
-  if (scr[12] == 0u) return;
-  if (tid == 0) coherent_store(&a.rowcnt[s], 0u);  // leave the counter zeroed
-  select_row(a, s, c, nseg_row, smem);
+  if (tid == 0) coherent_store(&a.fa[(int64_t)s * kStepFaStride + g], epoch);
 }
 
-// -------------------------------------------------------------- attention ----
-template <int HKV, int D>
-__device__ __forceinline__ void attend_split(const StepArgs& a, int64_t item, unsigned char* smem) {
-  using S = MfmaShape<HKV, D>;
-  constexpr int PF = part_floats(D);
+// ---------------------------------------------------------------- P2 -------
+// The selection of a row with c > k_B candidates, derived by each waiting
+// workgroup from every segment's published counts and pairs:
+//   * d* from the row's suffix counts S(b): S(d*) >= k_B > S(d*+1);
+//   * per segment, hi (entries above d*) and eq (at d*) from its cum words;
+//     its entries with bin >= d* are the first hi + eq of its sorted list,
+//     and all of them (fewer than k_B + kGCap) are loaded at once, thread t
+//     holding kFPT consecutive ones of the row's list in segment order;
+//   * the need = k_B - S(d*+1) largest bin-d* entries are kept (equal
+//     scores to the lower id): a 256-bin histogram of the next 8 key bits
+//     finds the sub-bin t* that holds the boundary, and only t*'s entries
+//     are ranked one against another;
+//   * the kept entries, compacted in list order, are grouped by segment in
+//     ascending segment order, so a kept id's position in the selection is
+//     its segment's first index there plus its rank by id within the segment.
+// If the entries with bin >= d* do not fit (bin d* holds thousands of
+// equal scores), an exact radix select over the whole row decides instead.
+// Writes the selection outputs for the positions of this workgroup's splits
+// and their block lists (sball: split kl's list at kl * P).
+__device__ __forceinline__ void select_runs(const StepArgs& a, int s, int g, int64_t c,
+                                            int nseg_row, int nsw, const uint32_t* acc_row,
+                                            int32_t* sball, unsigned char* smem) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int64_t row = item / a.n_split;
-  const int split = (int)(item % a.n_split);
+  const int wave = tid >> 6;
   const int kB = a.kB;
-  const int64_t p = min(max((int64_t)a.q_pos[row], (int64_t)0), a.cap - 1);
-  const int64_t c = p / 4;
+  const int P = a.pb_per_split;
+  const int count = kB;  // c > k_B
+  uint32_t* fseg = reinterpret_cast<uint32_t*>(smem + kOffFseg);
+  unsigned long long* mk = reinterpret_cast<unsigned long long*>(smem + kOffMk);
+  uint32_t* rh = reinterpret_cast<uint32_t*>(smem + kOffRh);
+  uint32_t* hi = reinterpret_cast<uint32_t*>(smem + kOffHi);
+  uint32_t* eq = reinterpret_cast<uint32_t*>(smem + kOffEq);
+  uint32_t* fo = reinterpret_cast<uint32_t*>(smem + kOffFo);
+  uint32_t* kid = reinterpret_cast<uint32_t*>(smem + kOffKId);
+  uint32_t* kkey = reinterpret_cast<uint32_t*>(smem + kOffKKey);
+  uint32_t* kseg = reinterpret_cast<uint32_t*>(smem + kOffKSeg);
+  uint32_t* sfirst = reinterpret_cast<uint32_t*>(smem + kOffSFirst);
+  uint32_t* slast = reinterpret_cast<uint32_t*>(smem + kOffSLast);
   uint32_t* scr = reinterpret_cast<uint32_t*>(smem + kOffScr);
-  int32_t* sbid = reinterpret_cast<int32_t*>(smem + S::LDS_BYTES);
-  uint32_t* rec = a.rec + row * kStepRecStride;
-  const int pb_lo = split * kDecodeSplitPB;
+  const unsigned long long* prow =
+      reinterpret_cast<const unsigned long long*>(a.pairs) + (int64_t)s * a.n_seg * kStepSegMax;
 
-  if (split == 0 && tid < 64) {  // the block the new token completes, if any
-    const int64_t pr = a.q_pos[row];
-    const int64_t lb = max(pr, (int64_t)0);
-    const int64_t la = min(max(pr + 1, (int64_t)0), a.cap);
-    const int64_t b_begin = lb / 4;
-    const int64_t b_end = min(la / 4, a.cap_blocks);
-    if (b_begin < b_end)
-      compress_wave<true>(a.k_idx, a.cap, (int)row, b_begin, b_end, 1, a.gain, a.base, a.eps,
-                          a.rope_dims, a.k_cmp, 2);  // blocks of 4 tokens
+  // ---- the threshold bin from the row's suffix counts S(b) -------------------
+  if (tid == 0) {  // defaults, kept only if the counts are inconsistent
+    scr[8] = 0u;
+    scr[9] = 0u;
+    scr[10] = (uint32_t)c;
+    scr[12] = 0u;  // kept entries (fallback)
+    scr[13] = 0u;  // boundary entries
+    scr[16] = 0u;  // t*
+    scr[17] = 0u;  // entries above t*
+    scr[18] = 0u;  // entries in t*
   }
-  u32x4 qb[S::NK];
-  load_qbd<HKV, D>(a.q, row, qb);  // in flight while the selection is made
-
-  // wait for record entries pb_lo - 1 .. pb_lo + 31 (lane L <-> pb_lo - 1 + L);
-  // the split's pseudo-blocks are [pb_lo, pb_hi), the first NONE the tail
-  if (tid < 64) {
-    const int e = pb_lo - 1 + lane;
-    const bool mine = lane <= kDecodeSplitPB && e >= 0 && e <= kB;
-    uint32_t v = (e < 0) ? 1u : kNone;  // before the record: "an id"; past it: NONE
-    uint32_t n = 0;
-    while (true) {
-      if (mine) v = coherent_load(&rec[e]);
-      if (__ballot(mine && v == 0u) == 0ull) break;
-      if (++n >= kSpinLimit) {
-        if (lane == 0) coherent_store(a.err, 1u);
-        break;
-      }
-      __builtin_amdgcn_s_sleep(1);
+  {
+    const uint32_t S_t = coherent_load(&acc_row[tid]);  // thread t: bin t
+    rh[tid] = S_t;
+    __syncthreads();
+    const uint32_t S_next = tid < 255 ? rh[tid + 1] : 0u;
+    if (S_t >= (uint32_t)kB && S_next < (uint32_t)kB) {  // S(0) = c > k_B: one such bin
+      scr[8] = (uint32_t)tid;
+      scr[9] = S_next;
+      scr[10] = S_t;
     }
-    const unsigned long long none =
-        __ballot(lane >= 1 && lane <= kDecodeSplitPB && v == kNone);
-    int hi = pb_lo + kDecodeSplitPB;
-    if (__shfl(v, 0) == kNone) hi = pb_lo;         // the count ends before this split
-    else if (none) hi = pb_lo + (__ffsll(none) - 1);  // lane L holds the tail: pb_hi = pb_lo + L
-    if (lane >= 1 && lane <= hi - pb_lo)
-      sbid[lane - 1] = (v == kNone) ? (int32_t)c
-                                    : (int32_t)min(max((int64_t)v - 1, (int64_t)0), c - 1);
-    if (lane == 0) scr[13] = (uint32_t)hi;
+    __syncthreads();
+  }
+  const uint32_t dstar = scr[8];
+  const uint32_t n_sure = scr[9];
+  const uint32_t n_maybe = scr[10] - min(n_sure, scr[10]);
+  const uint32_t need = (uint32_t)kB - min(n_sure, (uint32_t)kB);
+  const bool all_eq = need >= n_maybe;
+
+  // ---- every segment's entries above and at d*, and their list offsets ------
+  const uint32_t* crow = a.cum + (int64_t)s * a.n_seg * 128;
+  for (int i = tid; i < nseg_row; i += kNT) {
+    const uint32_t* cw = crow + (int64_t)i * 128;
+    const uint32_t above = min(cum_at(cw, dstar + 1u), (uint32_t)kStepSegMax);
+    const uint32_t at = cum_at(cw, dstar);
+    hi[i] = above;
+    eq[i] = min(at - min(at, above), (uint32_t)kStepSegMax - above);
   }
   __syncthreads();
-  const int pb_hi = (int)scr[13];
-  attn_mfma_tiles<HKV, D, true>(qb, a.kc, a.vc, a.cap, (int)row, p, row, item, pb_lo, pb_hi,
-                                sbid, a.scale_log2, a.out, a.lse, a.part, a.n_split, smem);
-  if (a.n_split == 1) {  // the split wrote the output itself; clear the record
-    for (int i = tid; i <= kB; i += kNT) coherent_store(&rec[i], 0u);
-    return;
+  uint32_t total;
+  {  // two segments per thread
+    const uint32_t v0 = 2 * tid < nseg_row ? hi[2 * tid] + eq[2 * tid] : 0u;
+    const uint32_t v1 = 2 * tid + 1 < nseg_row ? hi[2 * tid + 1] + eq[2 * tid + 1] : 0u;
+    const uint32_t ex = block_excl_scan<kNT>(v0 + v1, scr, &total);
+    fo[2 * tid] = ex;
+    fo[2 * tid + 1] = ex + v0;
+    __syncthreads();
+  }
+  const bool fallback = total > (uint32_t)kFlatCap;
+
+  // this workgroup's block lists start valid, whatever happens below
+  for (int k = g, kl = 0; k < kDecodeSplits; k += nsw, ++kl)
+    for (int i = tid; i < P; i += kNT) sball[kl * P + i] = 0;
+  uint32_t nk;
+
+  if (!fallback) {
+    // ---- load the list: slot f belongs to the last segment starting at or
+    // before it (marks, then a running max over the slots, consecutive per
+    // thread), then every slot's load at once
+    for (int i = tid; i < kFlatCap; i += kNT) fseg[i] = 0u;
+    __syncthreads();
+    for (int i = tid; i < nseg_row; i += kNT)
+      if (hi[i] + eq[i] != 0u && fo[i] < (uint32_t)kFlatCap) fseg[fo[i]] = (uint32_t)i;
+    __syncthreads();
+    uint32_t run[kFPT];
+    uint32_t mx = 0u;
+#pragma unroll
+    for (int u = 0; u < kFPT; ++u) run[u] = mx = max(mx, fseg[kFPT * tid + u]);
+    {  // exclusive max over the threads before this one (segments only grow)
+      const uint32_t incl = wave_incl_max(mx);
+      if (lane == 63) scr[20 + wave] = incl;
+      __syncthreads();
+      uint32_t before = __shfl_up(incl, 1);
+      if (lane == 0) before = 0u;
+#pragma unroll
+      for (int w = 0; w < kNW; ++w)
+        if (w < wave) before = max(before, scr[20 + w]);
+#pragma unroll
+      for (int u = 0; u < kFPT; ++u) run[u] = max(run[u], before);
+    }
+    unsigned long long v[kFPT];
+#pragma unroll
+    for (int u = 0; u < kFPT; ++u) {
+      const uint32_t f = (uint32_t)(kFPT * tid + u);
+      const uint32_t sg = run[u];
+      const uint32_t at = min(f - min(f, fo[sg]), (uint32_t)kStepSegMax - 1u);
+      v[u] = f < total ? coherent_load(&prow[(int64_t)sg * kStepSegMax + at]) : 0ull;
+    }
+    // class of slot u: 2 kept for sure (bin > d*), 1 at d*, 0 empty
+    uint32_t cls[kFPT];
+#pragma unroll
+    for (int u = 0; u < kFPT; ++u) {
+      const uint32_t f = (uint32_t)(kFPT * tid + u);
+      const uint32_t b = score_bin((uint32_t)v[u]);
+      cls[u] = f >= total ? 0u : (b > dstar ? 2u : (b == dstar ? 1u : 0u));
+    }
+    if (!all_eq) {
+      // ---- the boundary sub-bin t* of bin d*: bits 19..12 of the key order
+      // the bin's entries (bits 30..20 are the bin); the end bins, which
+      // clamp, go whole to the ranking instead
+      const bool split_bin = dstar > 0u && dstar < (uint32_t)kHistBins - 1u;
+      uint32_t tstar = 0u, above = 0u, m = n_maybe;
+      if (split_bin) {
+        rh[tid] = 0u;
+        __syncthreads();
+#pragma unroll
+        for (int u = 0; u < kFPT; ++u)
+          if (cls[u] == 1u) atomicAdd(&rh[((uint32_t)v[u] >> 12) & 255u], 1u);
+        __syncthreads();
+        const uint32_t nb = rh[255 - tid];  // thread t: sub-bin 255 - t
+        uint32_t tot;
+        const uint32_t ex = block_excl_scan<kNT>(nb, scr, &tot);  // entries above it
+        if (ex + nb >= need && ex < need) {
+          scr[16] = 255u - (uint32_t)tid;
+          scr[17] = ex;
+          scr[18] = nb;
+        }
+        __syncthreads();
+        tstar = scr[16];
+        above = scr[17];
+        m = scr[18];
+      }
+      const uint32_t need2 = need - min(above, need);
+      // slot u is in the boundary group: at d*, and in t* when the bin splits
+      auto in_group = [&](int u) {
+        return cls[u] == 1u && (!split_bin || (((uint32_t)v[u] >> 12) & 255u) == tstar);
+      };
+      uint32_t qidx[kFPT];
+      const bool rank_group = m > need2;  // else every group entry is kept
+      if (rank_group) {
+        // gather the group, packed (key << 32 | ~id) so that the integer
+        // order of distinct entries is the selection order
+#pragma unroll
+        for (int u = 0; u < kFPT; ++u) {
+          const bool want = in_group(u);
+          const unsigned long long bal = __ballot(want);
+          uint32_t base = 0u;
+          if (lane == 0 && bal) base = atomicAdd(&scr[13], (uint32_t)__popcll(bal));
+          base = __shfl(base, 0);
+          qidx[u] = base + (uint32_t)__popcll(bal & ((1ull << lane) - 1ull));
+          if (want && qidx[u] < (uint32_t)kMkCap)
+            mk[qidx[u]] = (v[u] << 32) | (0x7FFFFFFFu - (uint32_t)(v[u] >> 32));
+        }
+        __syncthreads();
+        const uint32_t n = min(scr[13], (uint32_t)kMkCap);
+        if (n <= (uint32_t)kNT) {  // pairwise ranks
+          if (tid < 16) mk[n + tid] = 0ull;  // pad with values below every member
+          __syncthreads();
+          const unsigned long long me = tid < (int)n ? mk[tid] : ~0ull;
+          uint32_t rank = 0;
+          for (uint32_t j = 0; j < n; j += 16) {  // 16 broadcast reads in flight
+            unsigned long long w[16];
+#pragma unroll
+            for (int e = 0; e < 16; e += 2) {
+              const u32x4 q = *reinterpret_cast<const u32x4*>(mk + j + e);
+              w[e] = (unsigned long long)q[0] | ((unsigned long long)q[1] << 32);
+              w[e + 1] = (unsigned long long)q[2] | ((unsigned long long)q[3] << 32);
+            }
+#pragma unroll
+            for (int e = 0; e < 16; ++e) rank += w[e] > me ? 1u : 0u;
+          }
+          __syncthreads();
+          if (tid < (int)n && rank < need2) mk[tid] |= 0x80000000ull;  // kept mark
+        } else {
+          auto key = [&](int64_t i) { return (uint32_t)(mk[i] >> 32); };
+          auto all = [&](int64_t) { return true; };
+          Radix r;
+          if (split_bin)
+            r = radix_select<kNT, true>(key, all, (int64_t)n, need2, rh, scr, 1,
+                                        (dstar + 888u) << 20, 0x7FFu << 20);
+          else
+            r = radix_select<kNT, true>(key, all, (int64_t)n, need2, rh, scr);
+          const bool tie = r.avail > r.need;
+          Radix r2{0u, 0u, 0u, 0u};
+          if (tie) {  // equal scores at the threshold: the lowest ids win
+            auto key2 = [&](int64_t i) { return (uint32_t)mk[i] & 0x7FFFFFFFu; };
+            auto elig2 = [&](int64_t i) { return (key(i) & r.mask) == r.prefix; };
+            r2 = radix_select<kNT, true>(key2, elig2, (int64_t)n, r.need, rh, scr);
+          }
+          __syncthreads();
+          bool won[kGroupPT];
+#pragma unroll
+          for (int e = 0; e < kGroupPT; ++e) {
+            const uint32_t i = (uint32_t)(tid + kNT * e);
+            won[e] = false;
+            if (i < n) {
+              const uint32_t mm = key(i) & r.mask;
+              won[e] = mm > r.prefix ||
+                       (mm == r.prefix &&
+                        (!tie || (((uint32_t)mk[i] & 0x7FFFFFFFu) & r2.mask) >= r2.prefix));
+            }
+          }
+          __syncthreads();
+#pragma unroll
+          for (int e = 0; e < kGroupPT; ++e)
+            if (won[e]) mk[tid + kNT * e] |= 0x80000000ull;
+        }
+        __syncthreads();
+      }
+#pragma unroll
+      for (int u = 0; u < kFPT; ++u) {
+        if (cls[u] != 1u) continue;
+        const uint32_t sb = ((uint32_t)v[u] >> 12) & 255u;
+        bool keep;
+        if (split_bin && sb != tstar) keep = sb > tstar;
+        else keep = !rank_group || (qidx[u] < (uint32_t)kMkCap && (mk[qidx[u]] & 0x80000000ull));
+        cls[u] = keep ? 2u : 0u;
+      }
+    } else {
+#pragma unroll
+      for (int u = 0; u < kFPT; ++u)
+        if (cls[u] == 1u) cls[u] = 2u;
+    }
+    // ---- the kept entries in list order (grouped by segment, ascending)
+    uint32_t mine = 0;
+#pragma unroll
+    for (int u = 0; u < kFPT; ++u) mine += cls[u] == 2u ? 1u : 0u;
+    uint32_t tot;
+    uint32_t o = block_excl_scan<kNT>(mine, scr, &tot);
+#pragma unroll
+    for (int u = 0; u < kFPT; ++u)
+      if (cls[u] == 2u) {
+        if (o < (uint32_t)kMaxKB) {
+          kid[o] = (uint32_t)(v[u] >> 32);
+          kkey[o] = (uint32_t)v[u];
+          kseg[o] = run[u];
+        }
+        ++o;
+      }
+    nk = min(tot, (uint32_t)kMaxKB);
+  } else {
+    // ---- fallback: exact selection over the whole row ---------------------
+    // Entry i of the row's c entries: segment min(i / 1024, last), whose
+    // list holds that segment's entries at stride kStepSegMax.
+    auto seg_of = [&](int64_t i) { return min(i / kStepSeg, (int64_t)nseg_row - 1); };
+    auto at = [&](int64_t i) {
+      const int64_t sg = seg_of(i);
+      return coherent_load(&prow[sg * kStepSegMax + (i - sg * kStepSeg)]);
+    };
+    auto key = [&](int64_t i) { return (uint32_t)at(i); };
+    auto all = [&](int64_t) { return true; };
+    const Radix r = radix_select<kNT>(key, all, c, (uint32_t)kB, rh, scr);
+    const bool tie = r.avail > r.need;
+    Radix r2{0u, 0u, 0u, 0u};
+    if (tie) {
+      auto key2 = [&](int64_t i) { return 0x7FFFFFFFu - (uint32_t)(at(i) >> 32); };
+      auto elig2 = [&](int64_t i) { return (key(i) & r.mask) == r.prefix; };
+      r2 = radix_select<kNT>(key2, elig2, c, r.need, rh, scr);
+    }
+    __syncthreads();
+    // the kept entries all have bin >= d*: stream those (segment j's list
+    // range [fo[j], fo[j] + hi[j] + eq[j])), appended in any order
+    for (uint32_t f = tid; f < total; f += kNT) {
+      int lo = 0, up = nseg_row - 1;  // the last segment with fo <= f
+      while (lo < up) {
+        const int mid = (lo + up + 1) >> 1;
+        if (fo[mid] <= f) lo = mid;
+        else up = mid - 1;
+      }
+      const uint32_t at_ = min(f - fo[lo], (uint32_t)kStepSegMax - 1u);
+      const unsigned long long e = coherent_load(&prow[(int64_t)lo * kStepSegMax + at_]);
+      const uint32_t mm = (uint32_t)e & r.mask;
+      const bool k = mm != r.prefix
+                         ? mm > r.prefix
+                         : (!tie || ((0x7FFFFFFFu - (uint32_t)(e >> 32)) & r2.mask) >= r2.prefix);
+      if (k) {
+        const uint32_t q = atomicAdd(&scr[12], 1u);
+        if (q < (uint32_t)kMaxKB) {
+          kid[q] = (uint32_t)(e >> 32);
+          kkey[q] = (uint32_t)e;
+          kseg[q] = 0u;  // one group: ranked over all kept ids
+        }
+      }
+    }
+    __syncthreads();
+    nk = min(scr[12], (uint32_t)kMaxKB);
+  }
+  __syncthreads();
+
+  // ---- positions: first index of the id's segment group + rank within it ----
+  for (uint32_t i = tid; i < nk; i += kNT) {
+    const uint32_t sg = kseg[i];
+    if (i == 0u || kseg[i - 1] != sg) sfirst[sg] = i;
+    if (i + 1u == nk || kseg[i + 1] != sg) slast[sg] = i;
+  }
+  __syncthreads();
+  int32_t* outsel = a.sel + (int64_t)s * kB;
+  float* outsc = a.sel_scores ? a.sel_scores + (int64_t)s * kB : nullptr;
+  for (uint32_t i = tid; i < nk; i += kNT) {
+    const uint32_t id = kid[i];
+    const uint32_t sg = kseg[i];
+    const uint32_t lo = sfirst[sg], up = slast[sg];
+    uint32_t pos = lo;
+    for (uint32_t j = lo; j <= up; ++j) pos += kid[j] < id ? 1u : 0u;
+    if (pos >= (uint32_t)count) continue;
+    const int k = (int)pos / P;
+    if (k % nsw != g) continue;  // another workgroup's split
+    sball[(k / nsw) * P + ((int)pos - k * P)] = (int32_t)min((int64_t)id, c - 1);
+    outsel[pos] = (int32_t)id;
+    if (outsc) outsc[pos] = __uint_as_float(kkey[i]);
+  }
+  if (tid == 0)  // the tail block c ends the token set
+    for (int k = g, kl = 0; k < kDecodeSplits; k += nsw, ++kl)
+      if (k * P <= count && count < k * P + P) sball[kl * P + (count - k * P)] = (int32_t)c;
+  __syncthreads();
+}
+
+// ------------------------------------------------------------ P2 + P3 ------
+// LDS past the selection's (and the attention tiles') room: the block lists
+// of a workgroup's splits, then the row's main query (loaded at the start).
+template <int HKV, int D>
+constexpr int sbid_offset() {
+  return MfmaShape<HKV, D>::LDS_BYTES > kSelLds ? MfmaShape<HKV, D>::LDS_BYTES : kSelLds;
+}
+template <int HKV, int D>
+constexpr int q_offset() {
+  return sbid_offset<HKV, D>() + 4 * kDecodeSplits * kMaxRunPB;
+}
+
+// load_qbd from the query staged in LDS (16 heads x D).
+template <int HKV, int D>
+__device__ __forceinline__ void load_qbd_lds(const uint16_t* qs,
+                                             u32x4 (&qb)[MfmaShape<HKV, D>::NK]) {
+  using S = MfmaShape<HKV, D>;
+  const int lane = threadIdx.x & 63;
+  const int l16 = lane & 15;
+  const int gq = lane >> 4;
+  const int gn = l16 / S::G;
+#pragma unroll
+  for (int kk = 0; kk < S::NK; ++kk) {
+    const int dim0 = 32 * kk + 8 * gq;
+    const int grp = dim0 / D;
+    qb[kk] = (grp == gn) ? *reinterpret_cast<const u32x4*>(qs + l16 * D + (dim0 - grp * D))
+                         : u32x4{0, 0, 0, 0};
+  }
+}
+
+// Split k of the row's token set: pseudo-blocks [k P, min((k+1) P, npb)),
+// the selected blocks then the tail block c.  Workgroup g takes splits
+// g, g + nsw, ...; their block lists are all built before any attention
+// (the attention reuses the selection's LDS).
+template <int HKV, int D>
+__device__ __forceinline__ void select_and_attend(const StepArgs& a, int s, int g, int64_t c,
+                                                  int nseg_row, int nsw, const uint32_t* acc_row,
+                                                  uint32_t epoch, unsigned char* smem) {
+  using S = MfmaShape<HKV, D>;
+  const int tid = threadIdx.x;
+  const int kB = a.kB;
+  const int64_t p = min(max((int64_t)a.q_pos[s], (int64_t)0), a.cap - 1);
+  const int count = (int)min((int64_t)kB, c);
+  const int npb = count + 1;  // r = 4: the tail is one pseudo-block
+  const int P = a.pb_per_split;
+  int32_t* sball = reinterpret_cast<int32_t*>(smem + sbid_offset<HKV, D>());
+  const uint16_t* qs = reinterpret_cast<const uint16_t*>(smem + q_offset<HKV, D>());
+
+  wait_flags(a, a.fa + (int64_t)s * kStepFaStride, nseg_row, epoch);
+  if (g == 0 && tid == 0) {  // every workgroup of the row has read the generation
+    coherent_store(&a.gen[s], epoch);
+    a.cnt[s] = count;
+  }
+
+  if (c <= kB) {  // every candidate is kept: the row has one segment, its scores in sc
+    const float* sc = reinterpret_cast<const float*>(smem + kOffSc);
+    int32_t* outsel = a.sel + (int64_t)s * kB;
+    float* outsc = a.sel_scores ? a.sel_scores + (int64_t)s * kB : nullptr;
+    for (int i = tid; i < kB; i += kNT) {
+      outsel[i] = i < c ? i : -1;
+      if (outsc) outsc[i] = i < c ? sc[i] : 0.0f;
+    }
+    int kl = 0;
+    for (int k = g; k < kDecodeSplits; k += nsw, ++kl)
+      for (int pb = k * P + tid; pb < min(k * P + P, npb); pb += kNT)
+        sball[kl * P + (pb - k * P)] = pb < count ? pb : (int32_t)c;
+    __syncthreads();
+  } else {
+    select_runs(a, s, g, c, nseg_row, nsw, acc_row, sball, smem);
+  }
+
+  u32x4 qb[S::NK];
+  load_qbd_lds<HKV, D>(qs, qb);
+  int kl = 0;
+  for (int k = g; k < kDecodeSplits; k += nsw, ++kl) {
+    const int pb_lo = k * P;
+    const int pb_hi = min(pb_lo + P, npb);
+    if (pb_lo >= pb_hi) {  // an empty split: the state attn_mfma_tiles leaves for no token
+      float* po = a.part + ((int64_t)s * kDecodeSplits + k) * part_floats(D);
+      for (int i = tid; i < part_floats(D); i += kNT)
+        coherent_store(&po[i], i < 16 ? -INFINITY : 0.0f);
+      continue;
+    }
+    attn_mfma_tiles<HKV, D, true>(qb, a.kc, a.vc, a.cap, s, p, s,
+                                  (int64_t)s * kDecodeSplits + k, pb_lo, pb_hi, sball + kl * P,
+                                  a.scale_log2, a.out, a.lse, a.part, kDecodeSplits, smem);
+    __syncthreads();  // the tiles' LDS is reused by the next split
   }
   stores_complete();
   __syncthreads();
-  if (tid == 0) scr[12] = arrive_last(&a.attncnt[row], (uint32_t)a.n_split) ? 1u : 0u;
-  __syncthreads();
-  if (scr[12] == 0u) return;
-  if (tid == 0) coherent_store(&a.attncnt[row], 0u);
-  for (int i = tid; i <= kB; i += kNT) coherent_store(&rec[i], 0u);
+  if (tid == 0)
+    for (int k = g; k < kDecodeSplits; k += nsw)
+      coherent_store(&a.fc[(int64_t)s * kStepFcStride + k], epoch);
+}
 
-  // ---- log-sum-exp merge of the splits (all loads coalesced): per head
-  // M = max_k m_k, f_k = 2^(m_k - M), Z = sum_k f_k l_k once, then
-  // O = sum_k f_k O_k per output -- lse_merge's expressions, in split order
-  const float* base = a.part + row * a.n_split * PF;
-  float* msz = reinterpret_cast<float*>(smem);  // [split][m 16, l 16]
-  float* fac = msz + kMaxSplits * 32;           // [head][split]: f_k, or -1 when skipped
-  float* hz = fac + 16 * kMaxSplits;            // [head] Z
-  float* hm = hz + 16;                          // [head] M
-  // (m, l) pairs of every split first, then the O values: the loads return
-  // in order, so storing the pairs waits for them alone
-  const int nmz = a.n_split * 16;
-  unsigned long long mz[2];
+// ---------------------------------------------------------------- P4 -------
+// Head h of the output: the log-sum-exp merge of the row's splits, in split
+// order (lse_merge_splits, as the stand-alone merge kernel).
+template <int D>
+__device__ __forceinline__ void merge_heads(const StepArgs& a, int s, int g, int nsw,
+                                            uint32_t epoch, unsigned char* smem) {
+  constexpr int PF = part_floats(D);
+  const int nm = min(nsw, 16);
+  if (g >= nm) return;
+  const int tid = threadIdx.x;
+  wait_flags(a, a.fc + (int64_t)s * kStepFcStride, kDecodeSplits, epoch);
+  float* ml = reinterpret_cast<float*>(smem);  // [2 * kDecodeSplits] per pass
+  const float* base = a.part + (int64_t)s * kDecodeSplits * PF;
+  for (int h = g; h < 16; h += nm) {
+    for (int i = tid; i < 2 * kDecodeSplits; i += kNT)
+      ml[i] = coherent_load(&base[(i >> 1) * PF + 16 * (i & 1) + h]);
+    float o[kDecodeSplits];
+    const int dd = tid < D ? tid : 0;
 #pragma unroll
-  for (int r = 0; r < 2; ++r) {
-    const int i = tid + kNT * r;
-    mz[r] = i < nmz ? coherent_load(reinterpret_cast<const unsigned long long*>(base + (i >> 4) * PF) + (i & 15))
-                    : 0ull;
-  }
-  constexpr int NJ = 16 * D / 2 / kNT;  // float pairs per thread
-  unsigned long long ov[NJ][kMaxSplits];
-#pragma unroll
-  for (int jj = 0; jj < NJ; ++jj)
-#pragma unroll
-    for (int k = 0; k < kMaxSplits; ++k)
-      ov[jj][k] = k < a.n_split ? coherent_load(reinterpret_cast<const unsigned long long*>(
-                                      base + k * PF + 32) + tid + kNT * jj)
-                                : 0ull;
-#pragma unroll
-  for (int r = 0; r < 2; ++r) {
-    const int i = tid + kNT * r;  // splits past n_split read as zero (unused)
-    if (i < kMaxSplits * 16) {
-      const int k = i >> 4, w = i & 15;
-      msz[k * 32 + 2 * w] = __uint_as_float((uint32_t)mz[r]);
-      msz[k * 32 + 2 * w + 1] = __uint_as_float((uint32_t)(mz[r] >> 32));
+    for (int k = 0; k < kDecodeSplits; ++k) o[k] = coherent_load(&base[k * PF + 32 + h * D + dd]);
+    __syncthreads();
+    if (tid < D) {
+      float mx, zs, acc;
+      lse_merge_splits(ml, o, mx, zs, acc);
+      a.out[((int64_t)s * 16 + h) * D + tid] = (uint16_t)f32_to_bf16(acc / zs);
+      if (a.lse && tid == 0) a.lse[(int64_t)s * 16 + h] = (mx + log2f(zs)) * kLn2;
     }
-  }
-  __syncthreads();
-  if (tid < 16) {
-    const int n = tid;
-    float mk[kMaxSplits], lk[kMaxSplits];
-#pragma unroll
-    for (int k = 0; k < kMaxSplits; ++k) {  // (reads outside any condition)
-      mk[k] = msz[k * 32 + n];
-      lk[k] = msz[k * 32 + 16 + n];
-    }
-    float mx = -INFINITY;
-#pragma unroll
-    for (int k = 0; k < kMaxSplits; ++k)
-      if (k < a.n_split) mx = fmaxf(mx, mk[k]);
-    float zs = 0.0f;
-#pragma unroll
-    for (int k = 0; k < kMaxSplits; ++k) {
-      float f = -1.0f;
-      if (k < a.n_split && mk[k] != -INFINITY) {
-        f = exp2f(mk[k] - mx);
-        zs += f * lk[k];
-      }
-      fac[n * kMaxSplits + k] = f;
-    }
-    hz[n] = zs;
-    hm[n] = mx;
-  }
-  __syncthreads();
-#pragma unroll
-  for (int jj = 0; jj < NJ; ++jj) {
-    const int e2 = 2 * (tid + kNT * jj);  // first of the two floats
-    const int n = e2 / D, d = e2 % D;
-    float fk[kMaxSplits];
-#pragma unroll
-    for (int k = 0; k < kMaxSplits; ++k) fk[k] = fac[n * kMaxSplits + k];  // -1 past n_split
-    float acc0 = 0.0f, acc1 = 0.0f;
-#pragma unroll
-    for (int k = 0; k < kMaxSplits; ++k) {
-      const float f = fk[k];
-      if (f >= 0.0f) {
-        acc0 += f * __uint_as_float((uint32_t)ov[jj][k]);
-        acc1 += f * __uint_as_float((uint32_t)(ov[jj][k] >> 32));
-      }
-    }
-    const float zs = hz[n];
-    *reinterpret_cast<uint32_t*>(a.out + (row * 16 + n) * D + d) =
-        f32_to_bf16(acc0 / zs) | (f32_to_bf16(acc1 / zs) << 16);
-    if (a.lse && d == 0) a.lse[row * 16 + n] = (hm[n] + log2f(zs)) * kLn2;
+    __syncthreads();
   }
 }
 
 template <int HKV, int D>
 constexpr int step_lds_bytes() {
-  return (MfmaShape<HKV, D>::LDS_BYTES + 4 * kMaxPB > kSelLds)
-             ? MfmaShape<HKV, D>::LDS_BYTES + 4 * kMaxPB
-             : kSelLds;
+  return q_offset<HKV, D>() + 2 * 16 * D;
+}
+
+// The block the new token completes, if any: not a candidate of this step
+// (candidates are the blocks before the query's own), so it is built off the
+// critical path by the row's last workgroup.
+__device__ __forceinline__ void compress_new_block(const StepArgs& a, int s) {
+  if (threadIdx.x >= 64) return;
+  const int64_t pr = a.q_pos[s];
+  const int64_t lb = max(pr, (int64_t)0);
+  const int64_t la = min(max(pr + 1, (int64_t)0), a.cap);
+  const int64_t b_begin = lb / 4;
+  const int64_t b_end = min(la / 4, a.cap_blocks);
+  if (b_begin < b_end)
+    compress_wave<true>(a.k_idx, a.cap, s, b_begin, b_end, 1, a.gain, a.base, a.eps, a.rope_dims,
+                        a.k_cmp, 2);  // blocks of 4 tokens
 }
 
 template <int HKV, int D>
 __global__ __launch_bounds__(kNT, 2) void decode_step_kernel(StepArgs a) {
   __shared__ __attribute__((aligned(16))) unsigned char smem[step_lds_bytes<HKV, D>()];
-  static_assert(MfmaShape<HKV, D>::LDS_BYTES + 4 * kMaxPB <= kOffScr,
-                "attention LDS stays below the scratch words");
-  const int64_t wg = blockIdx.x;
-  if (wg < a.n_score_wg)
-    score_segment(a, wg, smem);
-  else
-    attend_split<HKV, D>(a, wg - a.n_score_wg, smem);
+  const int s = (int)(blockIdx.x / (unsigned)a.n_seg);
+  const int g = (int)(blockIdx.x % (unsigned)a.n_seg);
+  const int64_t c = row_c(a, s);
+  const int nseg_row = step_nseg(c);
+  if (g >= nseg_row) return;  // not part of this row
+  const int tid = threadIdx.x;
+  const int nsw = min(nseg_row, kDecodeSplits);  // the row's waiting workgroups
+  const uint32_t epoch = coherent_load(&a.gen[s]) + 1u;
+  uint32_t* acc_row = a.acc + ((int64_t)s * 2 + (epoch & 1u)) * 256;
+  if (g == 0)  // the counts the row's next call adds into
+    coherent_store(&a.acc[((int64_t)s * 2 + ((epoch & 1u) ^ 1u)) * 256 + tid], 0u);
+  if (g < nsw && tid < 2 * D) {  // the main query, for the attention at the end
+    uint16_t* qs = reinterpret_cast<uint16_t*>(smem + q_offset<HKV, D>());
+    *reinterpret_cast<u32x4*>(qs + 8 * tid) = ld16(a.q + (int64_t)s * 16 * D + 8 * tid);
+  }
+  score_segment(a, s, g, c, nseg_row, acc_row, epoch, smem);
+  if (g >= nsw) {
+    if (g == nseg_row - 1) compress_new_block(a, s);
+    return;
+  }
+  __syncthreads();
+  select_and_attend<HKV, D>(a, s, g, c, nseg_row, nsw, acc_row, epoch, smem);
+  merge_heads<D>(a, s, g, nsw, epoch, smem);
+  if (g == nseg_row - 1) compress_new_block(a, s);
 }
 
 }  // namespace
@@ -826,7 +821,7 @@ StepPlan step_plan(const Dims& d, int batch, int32_t max_pos_end) {
   StepPlan p{};
   p.c_max = max((int64_t)1, (int64_t)(max_pos_end - 1) / d.r);
   p.n_seg = step_nseg(p.c_max);
-  p.n_split = (d.kB + 1 + kDecodeSplitPB - 1) / kDecodeSplitPB;
+  p.n_split = kDecodeSplits;
   auto align = [](size_t v) { return (v + 255) / 256 * 256; };
   size_t off = align(kStepCtlBytes);
   p.off_pairs = off;
@@ -872,66 +867,57 @@ hipError_t launch_decode_step(const Dims& d, const StepPlan& pl, int batch, cons
                               hipStream_t st) {
   char* ws = static_cast<char*>(workspace);
   const int D = d.head_dim;
-  const int64_t KD = (int64_t)d.kv_heads * D;
-  const int64_t cap_blocks = cap / d.r;
   int capacity = 0;
   if (d.kv_heads == 2 && D == 128) capacity = step_capacity<2, 128>();
   else if (d.kv_heads == 1 && D == 128) capacity = step_capacity<1, 128>();
   else if (d.kv_heads == 2 && D == 64) capacity = step_capacity<2, 64>();
-  if (capacity - 64 < pl.n_split) return hipErrorInvalidConfiguration;
-  const int per_launch = max(1, (capacity - 64) / pl.n_split);
-  for (int r0 = 0; r0 < batch; r0 += per_launch) {
-    const int nb = min(per_launch, batch - r0);
-    StepArgs a;
-    a.q_idx = static_cast<const uint16_t*>(q_idx) + (int64_t)r0 * 4 * 128;
-    a.q = static_cast<const uint16_t*>(q) + (int64_t)r0 * 16 * D;
-    a.k_idx = static_cast<const uint16_t*>(k_idx) + (int64_t)r0 * cap * 128;
-    a.k_cmp = static_cast<uint16_t*>(k_cmp) + (int64_t)r0 * cap_blocks * 128;
-    a.gain = gain;
-    a.kc = static_cast<const uint16_t*>(k_cache) + (int64_t)r0 * cap * KD;
-    a.vc = static_cast<const uint16_t*>(v_cache) + (int64_t)r0 * cap * KD;
-    a.cap = cap;
-    a.cap_blocks = cap_blocks;
-    a.c_cap = min(pl.c_max, cap_blocks);
-    a.q_pos = q_pos + r0;
-    a.kB = d.kB;
-    a.base = d.base;
-    a.eps = (double)d.eps;
-    a.rope_dims = d.rope_dims;
-    a.scale_log2 = d.scale * kLog2e;
-    a.sel = sel + (int64_t)r0 * d.kB;
-    a.cnt = cnt + r0;
-    a.sel_scores = sel_scores ? sel_scores + (int64_t)r0 * d.kB : nullptr;
-    a.out = static_cast<uint16_t*>(out) + (int64_t)r0 * 16 * D;
-    a.lse = lse ? lse + (int64_t)r0 * 16 : nullptr;
-    uint32_t* ctl = reinterpret_cast<uint32_t*>(ws);
-    a.rowcnt = ctl + r0;
-    a.attncnt = ctl + kStepOffAttn + r0;
-    a.err = ctl + kStepOffErr;
-    a.rec = ctl + kStepOffRec + (int64_t)r0 * kStepRecStride;
-    a.pairs = reinterpret_cast<uint2*>(ws + pl.off_pairs) + (int64_t)r0 * pl.n_seg * kStepSegMax;
-    a.cum = reinterpret_cast<uint32_t*>(ws + pl.off_cum) + (int64_t)r0 * pl.n_seg * 128;
-    a.acc = ctl + kStepOffAcc + (int64_t)r0 * 256;
-    a.part = reinterpret_cast<float*>(ws + pl.off_part) + (int64_t)r0 * pl.n_split * part_floats(D);
-    a.n_seg = pl.n_seg;
-    a.n_split = pl.n_split;
-    a.n_score_wg = nb * pl.n_seg;
-    const dim3 grid((unsigned)(nb * (pl.n_seg + pl.n_split)));
-    bool launched = false;
+  // a row's waiting workgroups (at most kDecodeSplits, on the 8 XCDs in
+  // turn) plus one more slot on every XCD must fit
+  if (capacity / 8 < (kDecodeSplits + 7) / 8 + 1) return hipErrorInvalidConfiguration;
+  StepArgs a;
+  a.q_idx = static_cast<const uint16_t*>(q_idx);
+  a.q = static_cast<const uint16_t*>(q);
+  a.k_idx = static_cast<const uint16_t*>(k_idx);
+  a.k_cmp = static_cast<uint16_t*>(k_cmp);
+  a.gain = gain;
+  a.kc = static_cast<const uint16_t*>(k_cache);
+  a.vc = static_cast<const uint16_t*>(v_cache);
+  a.cap = cap;
+  a.cap_blocks = cap / d.r;
+  a.c_cap = min(pl.c_max, a.cap_blocks);
+  a.q_pos = q_pos;
+  a.kB = d.kB;
+  a.base = d.base;
+  a.eps = (double)d.eps;
+  a.rope_dims = d.rope_dims;
+  a.scale_log2 = d.scale * kLog2e;
+  a.sel = sel;
+  a.cnt = cnt;
+  a.sel_scores = sel_scores;
+  a.out = static_cast<uint16_t*>(out);
+  a.lse = lse;
+  uint32_t* ctl = reinterpret_cast<uint32_t*>(ws);
+  a.gen = ctl + kStepOffGen;
+  a.err = ctl + kStepOffErr;
+  a.fc = ctl + kStepOffFc;
+  a.fa = ctl + kStepOffFa;
+  a.acc = ctl + kStepOffAcc;
+  a.pairs = reinterpret_cast<uint2*>(ws + pl.off_pairs);
+  a.cum = reinterpret_cast<uint32_t*>(ws + pl.off_cum);
+  a.part = reinterpret_cast<float*>(ws + pl.off_part);
+  a.n_seg = pl.n_seg;
+  a.pb_per_split = decode_pb_per_split(d.kB + 1);
+  const dim3 grid((unsigned)(batch * pl.n_seg));
 #define QSA_STEP(HKV, DD)                                                              \
-    if (!launched && d.kv_heads == HKV && d.head_dim == DD) {                          \
-      hipLaunchKernelGGL((decode_step_kernel<HKV, DD>), grid, dim3(kNT), 0, st, a);    \
-      launched = true;                                                                 \
-    }
-    QSA_STEP(2, 128)
-    QSA_STEP(1, 128)
-    QSA_STEP(2, 64)
-#undef QSA_STEP
-    if (!launched) return hipErrorInvalidValue;
-    const hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+  if (d.kv_heads == HKV && d.head_dim == DD) {                                         \
+    hipLaunchKernelGGL((decode_step_kernel<HKV, DD>), grid, dim3(kNT), 0, st, a);      \
+    return hipGetLastError();                                                          \
   }
-  return hipSuccess;
+  QSA_STEP(2, 128)
+  QSA_STEP(1, 128)
+  QSA_STEP(2, 64)
+#undef QSA_STEP
+  return hipErrorInvalidValue;
 }
 
 }  // namespace qsa

@@ -555,7 +555,8 @@ qsa_status qsa_offload_stage(const qsa_config* cfg, int32_t batch, const int32_t
 // looked up once per device (hipGetSymbolAddress with that device current)
 // and only that address is handed to kernels.  The first call on a device
 // also enqueues, on its stream, a clear of the control area the fused step
-// expects to find zero; every completed call leaves it zero again.
+// expects to find zero before its first call; later calls keep their state
+// there.
 qsa_status qsa_decode_step_noalloc(const qsa_config* cfg, int32_t batch, const void* q_idx,
                                    const void* q, const void* k_idx, void* k_cmp,
                                    const float* rms_gain, const void* k_cache,

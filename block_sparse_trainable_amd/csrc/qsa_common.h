@@ -211,21 +211,24 @@ hipError_t launch_select(const Dims& d, const SelectPlan& pl, int batch, int n_q
 
 // ------------------------------------------------------ fused decode step ----
 // Score segments of 1024 blocks (a row's last segment also takes a remainder
-// of up to 512 blocks); an id bitmap sized for rows of up to kStepBmWords * 32
-// candidate blocks; a fixed control area at the start of the workspace holds
-// the completion counters, the error word, the per-row selection records and
-// the per-row score-bin suffix counts of up to kStepMaxBatch rows.
+// of up to 512 blocks), rows of up to kStepBmWords * 32 candidate blocks; a
+// fixed control area at the start of the workspace holds, for up to
+// kStepMaxBatch rows, each row's generation word, its scoring flags (one
+// per segment) and split flags, its score-bin counts (two buffers, used in
+// turn), and one error word.
 constexpr int kStepSeg = 1024;
 constexpr int kStepSegMax = kStepSeg + kStepSeg / 2;
 constexpr int kStepBmWords = 8256;
 constexpr int64_t kStepMaxBlocks = (int64_t)kStepBmWords * 32;       // 264,192
 constexpr int kStepMaxBatch = 1024;
-constexpr int kStepRecStride = 528;      // record words per row (>= k_B + 1)
-constexpr int kStepOffAttn = 1024;       // control-area word offsets
+constexpr int kStepFaStride = 264;       // scoring flags per row (>= segments of a row)
+constexpr int kStepFcStride = 32;        // split flags per row (>= attention splits)
+constexpr int kStepOffGen = 0;           // control-area word offsets
 constexpr int kStepOffErr = 2048;
-constexpr int kStepOffRec = 4096;
-constexpr int kStepOffAcc = kStepOffRec + kStepMaxBatch * kStepRecStride;  // [row][256] counts
-constexpr size_t kStepCtlBytes = 4 * ((size_t)kStepOffAcc + (size_t)kStepMaxBatch * 256);
+constexpr int kStepOffFc = 4096;
+constexpr int kStepOffFa = kStepOffFc + kStepMaxBatch * kStepFcStride;
+constexpr int kStepOffAcc = kStepOffFa + kStepMaxBatch * kStepFaStride;  // [row][2][256]
+constexpr size_t kStepCtlBytes = 4 * ((size_t)kStepOffAcc + (size_t)kStepMaxBatch * 2 * 256);
 
 // Score segments of a row with c candidate blocks: 1024 each, the last one
 // also holding a remainder of up to 512 (non-decreasing in c).

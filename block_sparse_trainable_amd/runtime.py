@@ -196,8 +196,8 @@ class DeviceLayer:
         return outputs
 
     def step_workspace(self, max_pos_end: int) -> torch.Tensor:
-        """Zero-filled workspace of the fused decode step (its counters must
-        start at zero; every completed call leaves them zero)."""
+        """Zero-filled workspace of the fused decode step (its control area
+        must be zero before the first call; the calls keep their state there)."""
         n = B.qsa_workspace_size(self.cfg, B.QSA_OP_DECODE_STEP, self.batch, 1, max_pos_end)
         ws = self._ws.get("step")
         if ws is None or ws.numel() < n:
@@ -207,8 +207,8 @@ class DeviceLayer:
 
     def step_error_word(self, ws=None) -> int:
         """The fused step's error word (reads device memory: synchronises).
-        Non-zero means a wait for a selection gave up in some call since the
-        control area was last cleared, and those calls' outputs are invalid."""
+        Non-zero means a wait gave up in some call since the control area was
+        last cleared, and those calls' outputs are invalid."""
         ws = self._ws.get("step") if ws is None else ws
         if ws is None:
             return 0
@@ -217,15 +217,15 @@ class DeviceLayer:
 
     def check_step(self, ws=None) -> None:
         """Raises if the fused step's error word is set, after zero-filling
-        the control area again (a call that gave up can leave records
-        behind that the next call would take as published)."""
+        the control area again (a call that gave up can leave flags and
+        counts behind that the next call would misread)."""
         ws = self._ws.get("step") if ws is None else ws
         err = self.step_error_word(ws)
         if err:
             ws[:B.QSA_STEP_CONTROL_BYTES].zero_()
             torch.cuda.synchronize(self.device)
             raise B.QsaError(B.QSA_ERR_DEVICE,
-                             f"qsa_decode_step: a wait for a selection gave up (error word {err})")
+                             f"qsa_decode_step: a wait gave up (error word {err})")
 
     def decode_step_fused(self, plan, t: int, outputs, ws=None):
         """The same decode step as decode_step, in one launch (qsa_decode_step)."""

@@ -221,13 +221,17 @@ qsa_status qsa_sparse_attn_decode(const qsa_config* cfg, int32_t batch, const vo
  *   sel_blocks, sel_count, sel_scores   as in qsa_select_topk with n_q = 1.
  *   out, lse   as in qsa_sparse_attn_decode.
  *   workspace  >= qsa_workspace_size(QSA_OP_DECODE_STEP, batch, 1,
- *              max_pos_end) bytes.  Its first 3,227,648 bytes are a control
- *              area (completion counters, per-row selection records, per-row
- *              score-bin counts, an error word) that must be ZERO-FILLED
- *              BEFORE ITS FIRST USE; every
- *              completed call leaves it zero again.  Word 2048 (byte 8192) is
- *              the error word: 1 if a wait for a selection ever gave up
- *              (never expected; the outputs of that call are then invalid).
+ *              max_pos_end) bytes.  Its first 3,325,952 bytes are a control
+ *              area that must be ZERO-FILLED BEFORE THE FIRST CALL; between
+ *              calls it holds the calls' own state, which the caller leaves
+ *              alone (zero-filling it again between calls is always
+ *              allowed).  As int32 words: per-row generation words at 0
+ *              (row s: calls made since the last fill), the error word at
+ *              2048, per-row split flags at 4096 + 32 s, per-row scoring
+ *              flags at 36864 + 264 s, and two buffers of 256 per-row
+ *              score-bin counts at 307200 + 512 s.  The error word is 1 if a
+ *              wait ever gave up (never expected; the outputs of that call
+ *              are then invalid, and the area must be zero-filled again).
  * Supported: dtype bf16, block_size 4, idx_heads 4, q_heads 16 with
  * (kv_heads, head_dim) in {(2,128), (2,64), (1,128)}, batch <= 1024 and
  * floor((max_pos_end-1)/r)
@@ -247,8 +251,8 @@ qsa_status qsa_decode_step(const qsa_config* cfg, int32_t batch, const void* q_i
  * as qsa_decode_step, without the workspace: the step workspace is a 32 MiB
  * array in the library's own device memory, one per GPU, held until the
  * process ends.  The call allocates nothing.  The first call on a device
- * also enqueues a clear of the array's control area on its stream; every
- * completed call leaves the control area zero for the next.
+ * also enqueues a clear of the array's control area on its stream; later
+ * calls keep their state there, as qsa_decode_step's calls do.
  *   Limits: sizes whose qsa_workspace_size(QSA_OP_DECODE_STEP, batch, 1,
  *   max_pos_end) exceeds 32 MiB return QSA_ERR_UNSUPPORTED (batch 8 at
  *   256K context needs about 11 MB).

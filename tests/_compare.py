@@ -111,3 +111,31 @@ def stratified_rows(n: int, q_pos0: int, extra=(), k=96, seed=0) -> list:
     rows |= set(int(v) for v in rng.choice(n, size=min(n, k), replace=False))
     rows |= set(int(e) for e in extra if 0 <= e < n)
     return sorted(rows)
+
+
+# Fused decode step control area (int32 words; include/qsa.h): per-row
+# generation words at 0, the error word at 2048, per-row split flags at
+# 4096 + 32 s + k, per-row score-bin counts (two buffers of 256, used by
+# epoch parity) at 307200 + 512 s.
+STEP_GEN, STEP_ERR, STEP_FC, STEP_ACC = 0, 2048, 4096, 307200
+STEP_SPLITS = 17
+
+
+def check_step_control(ws, rows):
+    """After fused steps on workspace ws (rows 0 .. rows-1 stepped at least
+    once since it was zero-filled): no wait gave up; each row's last call
+    raised all its split flags with its own epoch (the row's generation
+    word); the count buffer its next call adds into is clear; rows never
+    stepped are untouched."""
+    import torch
+    from block_sparse_trainable_amd import _binding as B
+    ctl = ws[:B.QSA_STEP_CONTROL_BYTES].view(torch.int32).cpu().numpy().astype(np.int64)
+    assert ctl[STEP_ERR] == 0, "a wait gave up (error word set)"
+    gen = ctl[STEP_GEN:STEP_GEN + 1024]
+    assert (gen[:rows] >= 1).all(), "a row's generation word did not advance"
+    assert (gen[rows:] == 0).all(), "a row that was not stepped has a generation"
+    for s in range(rows):
+        fc = ctl[STEP_FC + 32 * s:STEP_FC + 32 * s + STEP_SPLITS]
+        assert (fc == gen[s]).all(), f"row {s}: split flags {fc} vs epoch {gen[s]}"
+        nxt = STEP_ACC + 512 * s + 256 * ((gen[s] + 1) & 1)
+        assert not ctl[nxt:nxt + 256].any(), f"row {s}: next call's counts not clear"

@@ -103,7 +103,7 @@ def test_workspace_sizes(lib):
     assert qsa.qsa_workspace_size(c, B.QSA_OP_SELECT, 8, 1, 262211) == want
     assert qsa.qsa_workspace_size(c, B.QSA_OP_INDEX_BUILD, 1, 1, 10) == 0
     assert qsa.qsa_workspace_size(c, B.QSA_OP_PREFILL, 1, 100, 100) == 0
-    # decode: 17 splits of 32 pseudo-blocks, each 16 heads x (128 + 2) floats
+    # decode: 17 splits of the token set, each 16 heads x (128 + 2) floats
     assert (qsa.qsa_workspace_size(c, B.QSA_OP_DECODE, 8, 1, 300000)
             == 4 * 8 * 17 * (16 * 128 + 32))
     assert qsa.qsa_workspace_size(cfg(dtype=B.QSA_F32), B.QSA_OP_DECODE, 8, 1, 300000) == 0
@@ -142,7 +142,7 @@ def test_block_sizes(lib):
     with pytest.raises(B.QsaError) as e:          # k_B = 2049 tokens
         qsa.qsa_workspace_size(cfg(block_size=1, token_budget=2049), B.QSA_OP_SELECT, 1, 1, 8)
     assert e.value.status == B.QSA_ERR_UNSUPPORTED and "2048" in str(e.value)
-    # token level: r = 1, k_B = 2048 -> 2049 tokens in slots of 4 -> 513 -> 17 splits
+    # token level: r = 1, k_B = 2048 -> 2049 tokens; decode always keeps 17 splits
     assert (qsa.qsa_workspace_size(cfg(block_size=1), B.QSA_OP_DECODE, 2, 1, 300000)
             == 4 * 2 * 17 * (16 * 128 + 32))
     for op in (B.QSA_OP_BACKWARD, B.QSA_OP_DISTILL, B.QSA_OP_DECODE_STEP):
@@ -152,12 +152,11 @@ def test_block_sizes(lib):
     with pytest.raises(B.QsaError) as e:          # k_B = 17 blocks of 128 = 2176 tokens
         qsa.qsa_workspace_size(cfg(block_size=128, token_budget=2049), B.QSA_OP_SELECT, 1, 1, 8)
     assert e.value.status == B.QSA_ERR_UNSUPPORTED and "2048" in str(e.value)
-    # decode splits count 4-token pseudo-blocks: r = 16, k_B = 128 -> 129 * 4 = 516 -> 17 splits
+    # decode: 17 splits at every block size
     assert (qsa.qsa_workspace_size(cfg(block_size=16), B.QSA_OP_DECODE, 2, 1, 300000)
             == 4 * 2 * 17 * (16 * 128 + 32))
-    # r = 64, k_B = 32 -> 33 * 16 = 528 -> 17 splits; K = 512 -> k_B = 8 -> 9 * 16 = 144 -> 5
     assert (qsa.qsa_workspace_size(cfg(block_size=64, token_budget=512), B.QSA_OP_DECODE, 1, 1,
-                                   300000) == 4 * 5 * (16 * 128 + 32))
+                                   300000) == 4 * 17 * (16 * 128 + 32))
     with pytest.raises(B.QsaError) as e:          # the fused step is built for r = 4 only
         qsa.qsa_decode_step(cfg(block_size=8), 1, FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, 4096,
                             FAKE, 4096, FAKE, FAKE, None, FAKE, None, FAKE, 1 << 30, stream=0)
@@ -216,15 +215,17 @@ def test_product_has_no_oracle_dependency():
 
 def test_decode_step_workspace_size(lib):
     c = cfg()
-    # 3,227,648-byte control area, then (score, id) pairs of the score
+    # 3,325,952-byte control area, then (score, id) pairs of the score
     # segments (room for 1536 each: 1024 plus a remainder of up to 512),
     # per-segment suffix counts (128 words), 17 split states of 16 x (128 + 2)
     batch, mpe = 8, 262211
     c_max = (mpe - 1) // 4
     full, rem = divmod(c_max, 1024)
     nseg = full if rem <= 512 else full + 1
-    want = _al(4 * (4096 + 1024 * 528 + 1024 * 256))
-    assert want == 3227648
+    # generation words, error word, split flags (32 per row), scoring flags
+    # (264 per row), two buffers of 256 score-bin counts per row
+    want = _al(4 * (4096 + 1024 * 32 + 1024 * 264 + 1024 * 2 * 256))
+    assert want == 3325952 == B.QSA_STEP_CONTROL_BYTES
     want = _al(want + 8 * batch * nseg * 1536)
     want = _al(want + 4 * batch * nseg * 128)
     want = _al(want + 4 * batch * 17 * (16 * 128 + 32))

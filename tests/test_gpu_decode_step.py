@@ -8,8 +8,8 @@ k_B and rows crossing k_B, a budget small enough for a single attention
 split, the other head layouts, exact score ties at the threshold, many
 candidates inside one score segment, the all-equal fallback, batches split
 over several launches, graph replay.
-After every call the workspace's counters must be back at zero and its
-error word clear.
+After the calls the workspace's control area must hold each row's flags at
+its epoch, the next call's counts clear and the error word clear.
 """
 import math
 import sys
@@ -25,8 +25,6 @@ from tests import _compare as C
 
 pytestmark = pytest.mark.gpu
 
-CTL_WORDS = 4096 + 1024 * 528 + 1024 * 256   # counters, error word (word 2048), records, bin counts
-ERR_WORD = 2048
 
 
 def say(msg):
@@ -44,10 +42,7 @@ def _gpu():
 
 
 def _ctl_clear(dl, max_pos_end):
-    ws = dl.step_workspace(max_pos_end)
-    ctl = ws[: 4 * CTL_WORDS].view(torch.int32).cpu().numpy()
-    assert not ctl[ERR_WORD], "a wait for a selection gave up"
-    assert not ctl.any(), "counters or flags left non-zero"
+    C.check_step_control(dl.step_workspace(max_pos_end), dl.batch)
 
 
 def _fused_vs_unfused(x, steps, check_oracle_steps=()):
