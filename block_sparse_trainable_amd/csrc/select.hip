@@ -540,7 +540,7 @@ template <int NT, int BATCH, bool PRUNE, int DEPTH, int CAP>
 __global__ __launch_bounds__(NT) void select_row_kernel(FilterArgs a) {
   constexpr int NW = NT / 64;
   constexpr int kRowCap = CAP;
-  constexpr int kSlots = kRowCap + kRowCap / 16 + NT;  // + one trash slot per thread
+  constexpr int kSlots = kRowCap + kRowCap / 16;
   static_assert(NW % 4 == 0, "batch offsets read 4-wave groups of counts");
   __shared__ uint32_t ckey[kSlots];
   __shared__ uint32_t cidx[kSlots];
@@ -667,21 +667,31 @@ __global__ __launch_bounds__(NT) void select_row_kernel(FilterArgs a) {
             v[b][w] &= (2 * w < lim ? 0xFFFFu : 0u) | (2 * w + 1 < lim ? 0xFFFF0000u : 0u);
         }
       }
-      auto k16 = [&](int b, int e) {
-        return ((e & 1) ? (v[b][e >> 1] >> 16) : (v[b][e >> 1] & 0xFFFFu)) << 15;
+      // key e of piece b for a lane-varying e (selects instead of indexing)
+      auto k16v = [&](int b, uint32_t e) {
+        const uint32_t w = (e & 4u) ? ((e & 2u) ? v[b][3] : v[b][2]) : ((e & 2u) ? v[b][1] : v[b][0]);
+        return ((e & 1u) ? (w >> 16) : (w & 0xFFFFu)) << 15;
       };
+      // candidates of piece b: bit e set for key e >= F (the high key of a
+      // word compares whole; the low one after a shift)
       // Index order within the batch is (b, wave, lane, e).  Each lane's
       // count per piece (0..8) is scanned across the wave three pieces at a
       // time in 10-bit fields; the wave totals per piece go through LDS.
       uint32_t excl[BATCH];
+      uint32_t msk[BATCH];
       for (int pass = 0;; ++pass) {
         uint32_t cnt[BATCH];
+        const uint32_t f_hi = (fkey >> 15) << 16;
 #pragma unroll
         for (int b = 0; b < BATCH; ++b) {
-          uint32_t n = 0;
+          uint32_t m = 0;
 #pragma unroll
-          for (int e = 0; e < 8; ++e) n += k16(b, e) >= fkey ? 1u : 0u;
-          cnt[b] = n;
+          for (int w = 0; w < 4; ++w) {
+            m |= (v[b][w] << 16) >= f_hi ? 1u << (2 * w) : 0u;
+            m |= v[b][w] >= f_hi ? 1u << (2 * w + 1) : 0u;
+          }
+          msk[b] = m;
+          cnt[b] = (uint32_t)__popc(m);
         }
 #pragma unroll
         for (int g = 0; g < BATCH; g += 3) {
@@ -749,11 +759,10 @@ __global__ __launch_bounds__(NT) void select_row_kernel(FilterArgs a) {
         }
       }
       if (overflow) break;
-      // wave-uniform offsets in (b, wave) order; non-candidates write to this
-      // lane's trash slot past the pool (every candidate fits: total + btot
-      // <= kRowCap)
+      // wave-uniform offsets in (b, wave) order; each lane writes only its
+      // candidates, in key order (every candidate fits: total + btot <=
+      // kRowCap)
       uint32_t run = total;
-      const uint32_t trash = (uint32_t)(kRowCap + kRowCap / 16) + (uint32_t)tid;
 #pragma unroll
       for (int b = 0; b < BATCH; ++b) {
         uint32_t off = run;
@@ -766,14 +775,11 @@ __global__ __launch_bounds__(NT) void select_row_kernel(FilterArgs a) {
         }
         uint32_t at = off + excl[b];
         const int i0 = base + 8 * (tid + NT * b);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const uint32_t kk = k16(b, e);
-          const bool take = kk >= fkey;
-          const uint32_t slot = take ? pslot(at) : trash;
-          ckey[slot] = kk;
-          cidx[slot] = (uint32_t)(i0 + e);
-          at += take ? 1u : 0u;
+        for (uint32_t m = msk[b]; m != 0u; m &= m - 1u) {
+          const uint32_t e = (uint32_t)__builtin_ctz(m);
+          ckey[pslot(at)] = k16v(b, e);
+          cidx[pslot(at)] = (uint32_t)i0 + e;
+          ++at;
         }
       }
       total = run;
