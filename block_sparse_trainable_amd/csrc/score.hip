@@ -103,7 +103,10 @@ __global__ __launch_bounds__(256) void score_valu_kernel(
 // 16w..16w+15 (4 A row-tiles of 4 queries x 4 heads, kept in registers for
 // the whole segment).  The segment is walked in chunks of 64 blocks; each
 // chunk (64 x 256 B) is staged once in LDS, double-buffered, and read by all
-// four waves as B tiles.
+// four waves as B tiles.  Block b of a chunk sits at LDS row
+// 16 (b mod 4) + b / 4, so B tile t (rows 16t .. 16t + 15) holds blocks
+// 4 l + t: after the chunk's four tiles each lane holds four consecutive
+// blocks of a query, stored with one 8-byte write.
 constexpr int kPQ = 64;       // queries per workgroup
 constexpr int kChunk = 64;    // blocks per LDS chunk
 constexpr int kRowB = 272;    // LDS bytes per block row (256 + 16 pad)
@@ -141,7 +144,7 @@ __global__ __launch_bounds__(256, HIST ? 2 : 3) void score_mfma_prefill_kernel(
   // A operands: row tile rt covers queries j0 + 16w + 4rt + (0..3)
   u32x4 qa[4][4];
   int cq[4];        // candidate count of this lane's output query in each row tile
-  uint32_t drow[4]; // that query's score row, at column l16 (offset into scores)
+  uint32_t drow[4]; // that query's score row, at column 4 l16 (offset into scores)
 #pragma unroll
   for (int rt = 0; rt < 4; ++rt) {
     const int jq_a = j0 + 16 * wave + 4 * rt + (l16 >> 2);  // query of A row l16
@@ -152,7 +155,7 @@ __global__ __launch_bounds__(256, HIST ? 2 : 3) void score_mfma_prefill_kernel(
     for (int kk = 0; kk < 4; ++kk) qa[rt][kk] = ok ? ld16(src + 32 * kk) : u32x4{0, 0, 0, 0};
     const int jq_o = j0 + 16 * wave + 4 * rt + gq;            // query of output rows 4gq..
     cq[rt] = jq_o < n_q ? (int)min(min((pos0 + jq_o) >> o.lr, cap_blocks), W) : 0;
-    drow[rt] = (uint32_t)((jq_o - j0) * W + l16);
+    drow[rt] = (uint32_t)((jq_o - j0) * W + 4 * l16);
   }
   // The tile's rows (queries past n_q have padding rows of their own), so
   // every score store below is unconditional: a lane past its query's
@@ -184,7 +187,8 @@ __global__ __launch_bounds__(256, HIST ? 2 : 3) void score_mfma_prefill_kernel(
     for (int u = 0; u < 4; ++u) {
       const int piece = threadIdx.x + 256 * u;
       const int blk = piece >> 4, col = piece & 15;
-      *reinterpret_cast<u32x4*>(&lds[buf][blk * kRowB + col * 16]) = r[u];
+      const int lrow = 16 * (blk & 3) + (blk >> 2);
+      *reinterpret_cast<u32x4*>(&lds[buf][lrow * kRowB + col * 16]) = r[u];
     }
   };
   uint32_t* hq[4];
@@ -202,6 +206,7 @@ __global__ __launch_bounds__(256, HIST ? 2 : 3) void score_mfma_prefill_kernel(
 
     // two halves of 32 blocks: 8 accumulator tiles live at a time
     const bool full = !HIST || cb + kChunk <= c_wave;
+    uint32_t k01[4];  // 16-bit keys of blocks 4 l16 and 4 l16 + 1, per row tile
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
       f32x4 acc[4][2];
@@ -218,20 +223,28 @@ __global__ __launch_bounds__(256, HIST ? 2 : 3) void score_mfma_prefill_kernel(
                 kk == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : acc[rt][c2], 0, 0, 0);
         }
 
-      // epilogue: lane holds 4 heads of query (4rt + gq) for block 16ct + l16
+      // epilogue: lane holds 4 heads of query (4rt + gq) for block 4 l16 + ct
 #pragma unroll
-      for (int rt = 0; rt < 4; ++rt)
+      for (int rt = 0; rt < 4; ++rt) {
+        float v[2];
 #pragma unroll
         for (int c2 = 0; c2 < 2; ++c2) {
           const int ct = 2 * half + c2;
-          const float v = relu_sum4(acc[rt][c2]);
-          if constexpr (HIST)
-            tile[drow[rt] + (uint32_t)cb + 16 * ct] = v;
-          else
-            tile16[drow[rt] + (uint32_t)cb + 16 * ct] = (uint16_t)(__float_as_uint(v) >> 16);
-          if constexpr (HIST)
-            if (full || cb + 16 * ct + l16 < cq[rt]) hist_add_nonneg(hq[rt], v);
+          v[c2] = relu_sum4(acc[rt][c2]);
+          if constexpr (HIST) {
+            tile[drow[rt] + (uint32_t)cb + ct] = v[c2];
+            if (full || cb + 4 * l16 + ct < cq[rt]) hist_add_nonneg(hq[rt], v[c2]);
+          }
         }
+        if constexpr (!HIST) {
+          // the top halves of the two scores' bits, lower block first
+          const uint32_t w = (__float_as_uint(v[0]) >> 16) | (__float_as_uint(v[1]) & 0xFFFF0000u);
+          if (half == 0)
+            k01[rt] = w;
+          else
+            *reinterpret_cast<uint2*>(tile16 + drow[rt] + (uint32_t)cb) = make_uint2(k01[rt], w);
+        }
+      }
     }
     if (more) {
       store_chunk(buf ^ 1, pre);
