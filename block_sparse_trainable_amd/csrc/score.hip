@@ -171,15 +171,18 @@ __global__ __launch_bounds__(256, HIST ? 2 : 3) void score_mfma_prefill_kernel(
   const int jw = j0 + 16 * wave;
   const int64_t c_wave = jw + 15 < n_q ? min(min((pos0 + jw) >> o.lr, cap_blocks), W) : 0;
 
-  // cooperative chunk load: 1024 pieces of 16 B, four per thread
-  const uint16_t* kbase = k_cmp + (int64_t)s * cap_blocks * 128;
+  // cooperative chunk load: 1024 pieces of 16 B, four per thread, at 32-bit
+  // offsets from the segment's first block
+  const uint16_t* kseg = k_cmp + ((int64_t)s * cap_blocks + b_lo) * 128;
+  const uint32_t last = (uint32_t)(b_hi - 1 - b_lo);
   auto load_chunk = [&](int64_t cb, u32x4 (&r)[4]) {
+    const uint32_t c0 = (uint32_t)(cb - b_lo);
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      const int piece = threadIdx.x + 256 * u;
-      const int blk = piece >> 4, col = piece & 15;
-      const int64_t b = min(cb + blk, b_hi - 1);   // blocks past b_hi score no query
-      r[u] = ld16(kbase + b * 128 + col * 8);
+      const uint32_t piece = threadIdx.x + 256u * u;
+      const uint32_t blk = piece >> 4, col = piece & 15u;
+      const uint32_t b = min(c0 + blk, last);   // blocks past b_hi score no query
+      r[u] = ld16(kseg + (b * 128u + col * 8u));
     }
   };
   auto store_chunk = [&](int buf, const u32x4 (&r)[4]) {

@@ -408,8 +408,9 @@ __global__ __launch_bounds__(kThreads) void filter_select_kernel(FilterArgs a) {
 // rows: the top half of each score's bits, which orders like the score.  One
 // workgroup per row:
 //   1. a strided sample of the row gives its mean and spread, hence a floor F
-//      with, for a roughly normal row, about 2 k_B keys at or above it
-//      (normal upper-tail quantile);
+//      with, for a normal row, about 1.4 k_B keys at or above it (normal
+//      upper-tail quantile; score rows have heavier upper tails, so the pool
+//      holds more);
 //   2. the row is streamed once; the keys >= F are compacted, in index order,
 //      into an LDS pool.  Long rows let F rise when the pool fills: it moves
 //      to the (k_B + kPrune)-th largest key kept so far, still a valid floor
@@ -477,19 +478,19 @@ __device__ __forceinline__ void select_row_global16(const uint16_t* keys, int64_
                                     float* outs, uint32_t* hist, uint32_t* scratch, ExactFn exact) {
   auto key = [&](int64_t i) { return (uint32_t)keys[i] << 15; };
   auto all = [&](int64_t) { return true; };
-  const Radix r = radix_select<NT>(key, all, c, (uint32_t)kB, hist, scratch, 0, 0u, 0u, 1);
+  const Radix r = radix_select<NT, false, 8>(key, all, c, (uint32_t)kB, hist, scratch, 0, 0u, 0u, 1);
   const bool band = r.need < r.avail;
   Radix r2{0u, 0u, 0u, 0u}, r3{0u, 0u, 0u, 0u};
   bool ties = false;
   auto in_band = [&](int64_t i) { return (key(i) & r.mask) == r.prefix; };
   if (band) {
     auto ex = [&](int64_t i) { return exact((uint32_t)i); };
-    r2 = radix_select<NT>(ex, in_band, c, r.need, hist, scratch);
+    r2 = radix_select<NT, false, 8>(ex, in_band, c, r.need, hist, scratch);
     ties = r2.need < r2.avail;
     if (ties) {
       auto ik = [&](int64_t i) { return 0x7FFFFFFFu - (uint32_t)i; };
       auto eq = [&](int64_t i) { return in_band(i) && (exact((uint32_t)i) & r2.mask) == r2.prefix; };
-      r3 = radix_select<NT>(ik, eq, c, r2.need, hist, scratch);
+      r3 = radix_select<NT, false, 8>(ik, eq, c, r2.need, hist, scratch);
     }
   }
   uint32_t written = 0;
@@ -544,7 +545,8 @@ __global__ __launch_bounds__(NT) void select_row_kernel(FilterArgs a) {
   static_assert(NW % 4 == 0, "batch offsets read 4-wave groups of counts");
   __shared__ uint32_t ckey[kSlots];
   __shared__ uint32_t cidx[kSlots];
-  __shared__ uint32_t hist[kRadixBins];
+  // 8-bit radix digits (256 words), or the band: indices, exact scores, ranks
+  __shared__ uint32_t hist[3 * kBandMax];
   __shared__ __attribute__((aligned(16))) uint32_t wt[BATCH * NW];
   __shared__ float fred[3 * NW];
   __shared__ float qs[512];
@@ -621,7 +623,7 @@ __global__ __launch_bounds__(NT) void select_row_kernel(FilterArgs a) {
   }
   const float mu = sm / sn;
   const float sd = sqrtf(fmaxf(sq / sn - mu * mu, 0.0f));
-  const float pfrac = 2.0f * (float)kB / (float)ci;
+  const float pfrac = 1.4f * (float)kB / (float)ci;
   float z = pfrac < 0.5f ? normal_upper_quantile(pfrac) : -INFINITY;
 
   // ---- 2. stream the row into the pool; accept or move the floor ---------
@@ -729,7 +731,7 @@ __global__ __launch_bounds__(NT) void select_row_kernel(FilterArgs a) {
           // down)
           auto pkey = [&](int64_t i) { return ckey[pslot((uint32_t)i)]; };
           auto pall = [&](int64_t) { return true; };
-          const Radix rp = radix_select<NT, true>(pkey, pall, (int64_t)total, (uint32_t)(kB + kPrune), hist,
+          const Radix rp = radix_select<NT, true, 8>(pkey, pall, (int64_t)total, (uint32_t)(kB + kPrune), hist,
                                             scratch, 0, 0u, 0u, 1);
           fkey = max(fkey, rp.prefix);
           constexpr int E = kRowCap / NT;
@@ -804,7 +806,7 @@ __global__ __launch_bounds__(NT) void select_row_kernel(FilterArgs a) {
   // ---- 3. the 16-bit threshold, then exact scores for the keys equal to it
   auto key = [&](int64_t i) { return ckey[pslot((uint32_t)i)]; };
   auto all = [&](int64_t) { return true; };
-  const Radix r = radix_select<NT, true>(key, all, (int64_t)n_f, (uint32_t)kB, hist, scratch, 0, 0u, 0u, 1);
+  const Radix r = radix_select<NT, true, 8>(key, all, (int64_t)n_f, (uint32_t)kB, hist, scratch, 0, 0u, 0u, 1);
   const bool band = r.need < r.avail;
   if (band) {
     // the band (keys equal to T) listed in hist: [0, nb) pool indices, then
@@ -981,9 +983,9 @@ hipError_t launch_select(const Dims& d, const SelectPlan& pl, int batch, int n_q
     const dim3 g((unsigned)((int64_t)batch * n_q));
     const bool big = d.kB > 512;   // the token-level budgets (r < 4)
     if (pl.W <= kRowShortMax && !big)
-      hipLaunchKernelGGL((select_row_kernel<256, 2, false, 1, kRowCap>), g, dim3(256), 0, st, a);
+      hipLaunchKernelGGL((select_row_kernel<256, 4, false, 1, kRowCap>), g, dim3(256), 0, st, a);
     else if (!big)
-      hipLaunchKernelGGL((select_row_kernel<256, 2, true, 1, kRowCap>), g, dim3(256), 0, st, a);
+      hipLaunchKernelGGL((select_row_kernel<256, 4, true, 1, kRowCap>), g, dim3(256), 0, st, a);
     else if (pl.W <= kRowShortMax)
       hipLaunchKernelGGL((select_row_kernel<256, 2, false, 1, kRowCapBig>), g, dim3(256), 0, st, a);
     else

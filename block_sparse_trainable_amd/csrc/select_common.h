@@ -41,24 +41,28 @@ struct Radix {
   uint32_t prefix, mask, need, avail;
 };
 
-// MSB-first radix select (11/11/9-bit digits over key bits 30..0) over n keys
-// key(i), counting only keys with elig(i).  first_pass > 0 starts at a later
-// digit with the bits above it already fixed to prefix0/mask0; last_pass < 2
-// stops early for keys whose low bits are all zero.  hist holds kRadixBins
-// words, scratch NT/64 + 3.  CHEAP: key(i) and elig(i) are cheap reads of
-// any index below n (LDS): they are evaluated four elements at a time,
-// unconditionally, so their latencies overlap; otherwise key(i) is only
-// evaluated for eligible elements.
-template <int NT, bool CHEAP = false, class KeyFn, class EligFn>
+// MSB-first radix select over key bits 30..0 in digits of DB bits from the
+// top (DB = 11: bits 30..20, 19..9, 8..0; DB = 8: 30..23, 22..15, 14..7,
+// 6..0) over n keys key(i), counting only keys with elig(i).  first_pass > 0
+// starts at a later digit with the bits above it already fixed to
+// prefix0/mask0; a last_pass below the last digit stops early for keys whose
+// low bits are all zero.  hist holds 2^DB words, scratch NT/64 + 3.  CHEAP:
+// key(i) and elig(i) are cheap reads of any index below n (LDS): they are
+// evaluated four elements at a time, unconditionally, so their latencies
+// overlap; otherwise key(i) is only evaluated for eligible elements.
+template <int NT, bool CHEAP = false, int DB = 11, class KeyFn, class EligFn>
 __device__ __forceinline__ Radix radix_select(KeyFn key, EligFn elig, int64_t n, uint32_t need_in,
                               uint32_t* hist, uint32_t* scratch, int first_pass = 0,
-                              uint32_t prefix0 = 0u, uint32_t mask0 = 0u, int last_pass = 2) {
+                              uint32_t prefix0 = 0u, uint32_t mask0 = 0u,
+                              int last_pass = (31 + DB - 1) / DB - 1) {
+  static_assert(DB == 8 || DB == 11, "digit widths");
   constexpr int NW = NT / 64;
   const int tid = threadIdx.x;
   Radix r{prefix0, mask0, need_in, 0xFFFFFFFFu};
   for (int pass = first_pass; pass <= last_pass; ++pass) {
-    const int sh = pass == 0 ? 20 : (pass == 1 ? 9 : 0);  // digits: bits 30..20, 19..9, 8..0
-    const int nb = pass == 2 ? 512 : 2048;
+    const int top = 30 - DB * pass;            // the digit's highest bit
+    const int sh = top - DB + 1 > 0 ? top - DB + 1 : 0;
+    const int nb = 1 << (top - sh + 1);
     const uint32_t dmask = (uint32_t)nb - 1u;
     for (int i = tid; i < nb; i += NT) hist[i] = 0;
     __syncthreads();
@@ -87,16 +91,16 @@ __device__ __forceinline__ Radix radix_select(KeyFn key, EligFn elig, int64_t n,
       }
     }
     __syncthreads();
-    // thread t owns the per = nb / NT (8 or 2) bins just below nb - t*per,
-    // read at once, highest first
-    constexpr int kMaxPer = 2048 / NT;
-    const int per = nb / NT;
+    // thread t owns the per = max(nb / NT, 1) bins just below nb - t*per
+    // (none once that is 0), read at once, highest first
+    constexpr int kMaxPer = (1 << DB) / NT > 1 ? (1 << DB) / NT : 1;
+    const int per = nb / NT > 1 ? nb / NT : 1;
     const int hi = nb - tid * per;
     uint32_t hv[kMaxPer];
     uint32_t local = 0;
 #pragma unroll
     for (int e = 0; e < kMaxPer; ++e) {
-      hv[e] = e < per ? hist[hi - 1 - e] : 0u;
+      hv[e] = (e < per && hi - 1 - e >= 0) ? hist[hi - 1 - e] : 0u;
       local += hv[e];
     }
     uint32_t tot;
