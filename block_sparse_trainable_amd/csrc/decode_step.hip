@@ -464,20 +464,23 @@ __device__ __forceinline__ void select_runs(const StepArgs& a, int s, int g, int
       const bool rank_group = m > need2;  // else every group entry is kept
       if (rank_group) {
         // gather the group, packed (key << 32 | ~id) so that the integer
-        // order of distinct entries is the selection order
+        // order of distinct entries is the selection order; slots in thread
+        // order (one scan, no chain of atomics)
+        uint32_t ng = 0;
+#pragma unroll
+        for (int u = 0; u < kFPT; ++u) ng += in_group(u) ? 1u : 0u;
+        uint32_t n_all;
+        uint32_t q = block_excl_scan<kNT>(ng, scr, &n_all);
 #pragma unroll
         for (int u = 0; u < kFPT; ++u) {
           const bool want = in_group(u);
-          const unsigned long long bal = __ballot(want);
-          uint32_t base = 0u;
-          if (lane == 0 && bal) base = atomicAdd(&scr[13], (uint32_t)__popcll(bal));
-          base = __shfl(base, 0);
-          qidx[u] = base + (uint32_t)__popcll(bal & ((1ull << lane) - 1ull));
+          qidx[u] = q;
+          q += want ? 1u : 0u;
           if (want && qidx[u] < (uint32_t)kMkCap)
             mk[qidx[u]] = (v[u] << 32) | (0x7FFFFFFFu - (uint32_t)(v[u] >> 32));
         }
         __syncthreads();
-        const uint32_t n = min(scr[13], (uint32_t)kMkCap);
+        const uint32_t n = min(n_all, (uint32_t)kMkCap);
         if (n <= (uint32_t)kNT) {  // pairwise ranks
           if (tid < 16) mk[n + tid] = 0ull;  // pad with values below every member
           __syncthreads();
@@ -621,16 +624,25 @@ __device__ __forceinline__ void select_runs(const StepArgs& a, int s, int g, int
   __syncthreads();
   int32_t* outsel = a.sel + (int64_t)s * kB;
   float* outsc = a.sel_scores ? a.sel_scores + (int64_t)s * kB : nullptr;
+  // quotients by P and nsw as products with their reciprocals: exact for
+  // these small operands (pos < 2^10), with half a step of margin
+  const float inv_p = 1.0f / (float)P;
+  const float inv_nsw = 1.0f / (float)nsw;
   for (uint32_t i = tid; i < nk; i += kNT) {
     const uint32_t id = kid[i];
     const uint32_t sg = kseg[i];
     const uint32_t lo = sfirst[sg], up = slast[sg];
     uint32_t pos = lo;
-    for (uint32_t j = lo; j <= up; ++j) pos += kid[j] < id ? 1u : 0u;
+    uint32_t j = lo;
+    for (; j + 3u <= up; j += 4u)  // four reads in flight
+      pos += (kid[j] < id ? 1u : 0u) + (kid[j + 1] < id ? 1u : 0u) + (kid[j + 2] < id ? 1u : 0u) +
+             (kid[j + 3] < id ? 1u : 0u);
+    for (; j <= up; ++j) pos += kid[j] < id ? 1u : 0u;
     if (pos >= (uint32_t)count) continue;
-    const int k = (int)pos / P;
-    if (k % nsw != g) continue;  // another workgroup's split
-    sball[(k / nsw) * P + ((int)pos - k * P)] = (int32_t)min((int64_t)id, c - 1);
+    const int k = (int)(((float)pos + 0.5f) * inv_p);
+    const int kl = (int)(((float)k + 0.5f) * inv_nsw);
+    if (k - kl * nsw != g) continue;  // another workgroup's split
+    sball[kl * P + ((int)pos - k * P)] = (int32_t)min((int64_t)id, c - 1);
     outsel[pos] = (int32_t)id;
     if (outsc) outsc[pos] = __uint_as_float(kkey[i]);
   }
