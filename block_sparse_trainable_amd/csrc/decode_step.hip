@@ -69,9 +69,9 @@ namespace {
 
 constexpr int kNT = 256;
 constexpr int kNW = kNT / 64;
-constexpr int kCpw = 2;                          // 64-block chunks per wave per round
-constexpr int kRoundBlocks = kNW * kCpw * 64;    // 512
-constexpr int kMaxRounds = kStepSegMax / kRoundBlocks;  // 3
+constexpr int kCpw = 1;                          // 64-block chunks per wave per round
+constexpr int kRoundBlocks = kNW * kCpw * 64;    // 256
+constexpr int kMaxRounds = kStepSegMax / kRoundBlocks;  // 6
 constexpr int kPerThread = kStepSegMax / kNT;    // 6 scores per thread in the sort
 constexpr int kMaxKB = 512;                      // k_B of the fused step
 constexpr int kFlatCap = 2560;                   // entries with bin >= d* held by a workgroup
@@ -215,11 +215,10 @@ __device__ __forceinline__ void score_segment(const StepArgs& a, int s, int g, i
     for (int kk = 0; kk < 4; ++kk) qa[kk] = ok ? ld16(src + 32 * kk) : u32x4{0, 0, 0, 0};
   }
   const uint16_t* kbase = a.k_cmp + (int64_t)s * a.cap_blocks * 128 + 8 * gq;
-#pragma unroll
-  for (int rd = 0; rd < kMaxRounds; ++rd) {
-    if (rd * kRoundBlocks >= n_here) break;
+  // rounds are software-pipelined: the next round's B-tile loads are in
+  // flight while this round's MFMAs run
+  auto load_round = [&](int rd, u32x4 (&kb)[kCpw][4][4]) {
     const int64_t rb = seg_lo + (int64_t)rd * kRoundBlocks;
-    u32x4 kb[kCpw][4][4];
 #pragma unroll
     for (int cc = 0; cc < kCpw; ++cc)
 #pragma unroll
@@ -230,6 +229,21 @@ __device__ __forceinline__ void score_segment(const StepArgs& a, int s, int g, i
         for (int kk = 0; kk < 4; ++kk)
           kb[cc][ct][kk] = ok ? ld16(kbase + b * 128 + 32 * kk) : u32x4{0, 0, 0, 0};
       }
+  };
+  u32x4 kn[kCpw][4][4];
+  if (n_here > 0) load_round(0, kn);
+#pragma unroll
+  for (int rd = 0; rd < kMaxRounds; ++rd) {
+    if (rd * kRoundBlocks >= n_here) break;
+    const int64_t rb = seg_lo + (int64_t)rd * kRoundBlocks;
+    u32x4 kb[kCpw][4][4];
+#pragma unroll
+    for (int cc = 0; cc < kCpw; ++cc)
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct)
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) kb[cc][ct][kk] = kn[cc][ct][kk];
+    if (rd + 1 < kMaxRounds && (rd + 1) * kRoundBlocks < n_here) load_round(rd + 1, kn);
 #pragma unroll
     for (int cc = 0; cc < kCpw; ++cc)
 #pragma unroll
