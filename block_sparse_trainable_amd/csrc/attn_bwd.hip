@@ -29,6 +29,7 @@
 #include <math.h>
 
 #include "attn_tile.h"
+#include "fast_exp.h"
 #include "qsa_common.h"
 #include "select_common.h"
 
@@ -333,7 +334,7 @@ __global__ __launch_bounds__(256, (HKV == 2 && D == 128) ? 1 : 2) void bwd_query
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const bool ok = b >= 0 && 4 * b + i <= p;
-        const float P = ok ? exp2f(fmaf(sa[st][i], sl2, -lse2)) : 0.0f;
+        const float P = ok ? exp2_fast(fmaf(sa[st][i], sl2, -lse2)) : 0.0f;
         dacc = fmaf(P, dpa[st][i], dacc);
         w1[st][i] = P * (dpa[st][i] - dt);
         w2[st][i] = P;

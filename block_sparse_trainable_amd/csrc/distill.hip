@@ -31,6 +31,7 @@
 #include <math.h>
 
 #include "attn_tile.h"
+#include "fast_exp.h"
 #include "qsa_common.h"
 
 namespace qsa {
@@ -242,6 +243,7 @@ __global__ __launch_bounds__(64 * kTW) void distill_teacher_mfma_kernel(
   // token range of the tile
   const int jl = min(j0 + QT - 1, n_q - 1);
   const int64_t pmax = qpos(jl);
+  const int64_t pmin = qpos(j0);   // positions grow with the row: every query sees tokens <= pmin
   const int64_t tok_end = PASS == 1 ? pmax + 1 : ((pmax >> lr) << lr);
   if (tok_end <= 0) return;
   // this lane's column in group cg: query qcol(cg), head hcol(cg); rows
@@ -316,27 +318,46 @@ __global__ __launch_bounds__(64 * kTW) void distill_teacher_mfma_kernel(
         }
     }
     if constexpr (PASS == 1) {
+      if (t0 + 31 <= pmin) {
+        // every token of the tile is visible to every query here: the max
+        // over raw logits (the scale is positive), one FMA per exponent
 #pragma unroll
-      for (int cg = 0; cg < NCG; ++cg) {
-        float x[2][4], mt = -INFINITY;
-#pragma unroll
-        for (int st = 0; st < 2; ++st)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int64_t tp = t0 + 16 * st + 4 * gq + i;
-            x[st][i] = tp <= (int64_t)pq[cg] ? sa[cg][st][i] * sl2 : -INFINITY;
-            mt = fmaxf(mt, x[st][i]);
-          }
-        mt = wave_max_xor32(wave_max_xor16(mt));
-        const float mn = fmaxf(m[cg], mt);
-        if (mn != -INFINITY) {
+        for (int cg = 0; cg < NCG; ++cg) {
+          float mt = fmaxf(fmaxf(fmaxf(sa[cg][0][0], sa[cg][0][1]), fmaxf(sa[cg][0][2], sa[cg][0][3])),
+                           fmaxf(fmaxf(sa[cg][1][0], sa[cg][1][1]), fmaxf(sa[cg][1][2], sa[cg][1][3])));
+          mt = wave_max_xor32(wave_max_xor16(mt));
+          const float mn = fmaxf(m[cg], mt * sl2);
           float ps = 0.0f;
 #pragma unroll
           for (int st = 0; st < 2; ++st)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) ps += exp2f(x[st][i] - mn);
-          l[cg] = l[cg] * exp2f(m[cg] - mn) + ps;
+            for (int i = 0; i < 4; ++i) ps += exp2_fast(fmaf(sa[cg][st][i], sl2, -mn));
+          l[cg] = l[cg] * exp2_fast(m[cg] - mn) + ps;
           m[cg] = mn;
+        }
+      } else {
+        const int32_t tb = (int32_t)t0 + 4 * gq;   // positions < cap < 2^31
+#pragma unroll
+        for (int cg = 0; cg < NCG; ++cg) {
+          float x[2][4], mt = -INFINITY;
+#pragma unroll
+          for (int st = 0; st < 2; ++st)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              x[st][i] = tb + 16 * st + i <= pq[cg] ? sa[cg][st][i] * sl2 : -INFINITY;
+              mt = fmaxf(mt, x[st][i]);
+            }
+          mt = wave_max_xor32(wave_max_xor16(mt));
+          const float mn = fmaxf(m[cg], mt);
+          if (mn != -INFINITY) {
+            float ps = 0.0f;
+#pragma unroll
+            for (int st = 0; st < 2; ++st)
+#pragma unroll
+              for (int i = 0; i < 4; ++i) ps += exp2_fast(x[st][i] - mn);
+            l[cg] = l[cg] * exp2_fast(m[cg] - mn) + ps;
+            m[cg] = mn;
+          }
         }
       }
     } else {
@@ -351,14 +372,14 @@ __global__ __launch_bounds__(64 * kTW) void distill_teacher_mfma_kernel(
 #pragma unroll
             for (int g = 0; g < HKV; ++g) {
               const int cg = qs * HKV + g;
-              a += exp2f(fmaf(sa[cg][st][i], sl2, -lse2[cg]));
+              a += exp2_fast(fmaf(sa[cg][st][i], sl2, -lse2[cg]));
             }
             // sum over the query's heads held by the lanes of this group
             a = swz_add(a, 1);
             a = swz_add(a, 2);
             a = swz_add(a, 4);
             if constexpr (HKV == 1) a = swz_add(a, 8);
-            v[st][i] = a * (1.0f / 16.0f);
+            v[st][i] = a;   // the head sum; the mean's 1/16 is applied after the unit max
           }
         const int cg0 = qs * HKV;
         if (l16 % G == 0 && qcol(cg0) < n_q) {
@@ -369,7 +390,7 @@ __global__ __launch_bounds__(64 * kTW) void distill_teacher_mfma_kernel(
             const int64_t u = (t0 + 16 * st + 4 * gq) >> 2;
             if (u < nu)
               ws.um[row * ws.Wu + u] =
-                  fmaxf(fmaxf(v[st][0], v[st][1]), fmaxf(v[st][2], v[st][3]));
+                  fmaxf(fmaxf(v[st][0], v[st][1]), fmaxf(v[st][2], v[st][3])) * (1.0f / 16.0f);
           }
         }
       }
@@ -598,7 +619,7 @@ __global__ __launch_bounds__(256) void distill_student_mfma_kernel(
     const int64_t b = b0 + 4 * gq + h;
     if (b < c) {
       const float mn = fmaxf(m, I);
-      l = l * exp2f((m - mn) * kLog2e) + exp2f((I - mn) * kLog2e);
+      l = l * exp2_fast((m - mn) * kLog2e) + exp2_fast((I - mn) * kLog2e);
       m = mn;
       const float t = target(b);
       z += t;
@@ -611,7 +632,7 @@ __global__ __launch_bounds__(256) void distill_student_mfma_kernel(
     float M = fmaxf(m, quad_xor1(m));
     M = fmaxf(M, quad_xor2(M));
     M = wave_max_xor32(wave_max_xor16(M));
-    l = (m == -INFINITY) ? 0.0f : l * exp2f((m - M) * kLog2e);
+    l = (m == -INFINITY) ? 0.0f : l * exp2_fast((m - M) * kLog2e);
     m = M;
   }
   auto sum16 = [&](float v) {
@@ -644,7 +665,7 @@ __global__ __launch_bounds__(256) void distill_student_mfma_kernel(
       bitq[i] = bit;
     }
     const int64_t b = b0 + 4 * gq + h;
-    const float dI = b < c ? exp2f((pick(Iq) - lseI) * kLog2e) - target(b) * invZ : 0.0f;
+    const float dI = b < c ? exp2_fast((pick(Iq) - lseI) * kLog2e) - target(b) * invZ : 0.0f;
     if (valid) {
       const int64_t o = row * ws.W + b;   // W is a multiple of 16
       ws.ib[o] = dI;
