@@ -543,23 +543,36 @@ __global__ __launch_bounds__(256) void distill_kt_kernel(const uint16_t* __restr
   ws.kT[(((int64_t)s * (ws.nbt / 4) + (b >> 2)) * 128 + d) * 4 + (b & 3)] = v;
 }
 
+// One workgroup of four waves per 16 consecutive queries of a sequence; wave w
+// takes queries 4w .. 4w+3 (16 A rows: query x head).  The candidate blocks
+// are walked in chunks of kSC: each chunk's compressed keys (and, in pass 2,
+// their transposed groups) are staged in LDS once for the four waves, the
+// next chunk's loads in flight meanwhile.
+constexpr int kSC = 64;              // blocks per LDS chunk
+constexpr int kSKRow = 256 + 16;     // LDS bytes per staged key row
+constexpr int kSTG = 1024 + 128;     // LDS bytes per staged transposed group of 4 blocks
+
 __global__ __launch_bounds__(256) void distill_student_mfma_kernel(
     const uint16_t* __restrict__ q_idx, const uint16_t* __restrict__ k_cmp, int64_t cap_blocks,
     int batch, int n_q, const int32_t* __restrict__ q_pos0, int64_t cap, int lr, DistillWs ws,
     float* __restrict__ loss, float* __restrict__ dq_idx) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  __shared__ __attribute__((aligned(16))) unsigned char kl[kSC * kSKRow];
+  __shared__ __attribute__((aligned(16))) unsigned char tl[(kSC / 4) * kSTG];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
   const int l16 = lane & 15, gq = lane >> 4;
   const int qn = l16 >> 2, h = l16 & 3;
-  const int wps = (n_q + 3) / 4;                 // waves per sequence
-  const int64_t wg = (int64_t)blockIdx.x * 4 + wave;
-  const int s = (int)(wg / wps);
-  if (s >= batch) return;                        // whole wave
-  const int jb = (int)(wg % wps) * 4;
+  const int tiles = (n_q + 15) / 16;
+  const int s = (int)(blockIdx.x / (unsigned)tiles);
+  const int j0 = (int)(blockIdx.x % (unsigned)tiles) * 16;
+  const int jb = j0 + 4 * wave;
   const int j = jb + qn;
   const bool valid = j < n_q;
   const int64_t row = (int64_t)s * n_q + (valid ? j : n_q - 1);
   const int64_t p = min(max((int64_t)q_pos0[s] + (valid ? j : n_q - 1), (int64_t)0), cap - 1);
   const int64_t c = valid ? p >> lr : 0;
+  // the workgroup's longest row is its last query's (positions grow with j)
+  const int64_t cw = min(max((int64_t)q_pos0[s] + min(j0 + 15, n_q - 1), (int64_t)0), cap - 1) >> lr;
   const int m4 = 1 << (lr - 2);
   u32x4 qb[4];
 #pragma unroll
@@ -577,14 +590,47 @@ __global__ __launch_bounds__(256) void distill_student_mfma_kernel(
   for (int off = 1; off < 64; off <<= 1)
     cmax = max(cmax, (int64_t)__shfl_xor((long long)cmax, off));
   const uint16_t* kbase = k_cmp + (int64_t)s * cap_blocks * 128;
+  const uint16_t* kT = ws.kT + (int64_t)s * (ws.nbt / 4) * 512;
+  const int64_t last_group = ws.nbt / 4 - 1;
   const float* um = ws.um + row * ws.Wu;
-  // dots of the tile at b0: lane holds blocks b0 + 4gq + i for (qn, h)
-  auto dots = [&](int64_t b0, f32x4& acc) {
-    const int64_t kb = min(b0 + l16, cap_blocks - 1);
+  // chunk staging: 1024 pieces of 16 B for the keys (block, 16-byte column)
+  // and 1024 for the transposed groups (group, 16-byte piece), four per thread
+  auto load_k = [&](int64_t ch0, u32x4 (&r)[4]) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int piece = tid + 256 * u;
+      const int64_t b = min(ch0 + (piece >> 4), cap_blocks - 1);
+      r[u] = ld16(kbase + b * 128 + (piece & 15) * 8);
+    }
+  };
+  auto store_k = [&](const u32x4 (&r)[4]) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int piece = tid + 256 * u;
+      *reinterpret_cast<u32x4*>(&kl[(piece >> 4) * kSKRow + (piece & 15) * 16]) = r[u];
+    }
+  };
+  auto load_t = [&](int64_t ch0, u32x4 (&r)[4]) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int piece = tid + 256 * u;
+      const int64_t g = min((ch0 >> 2) + (piece >> 6), last_group);
+      r[u] = ld16(kT + g * 512 + (piece & 63) * 8);
+    }
+  };
+  auto store_t = [&](const u32x4 (&r)[4]) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int piece = tid + 256 * u;
+      *reinterpret_cast<u32x4*>(&tl[(piece >> 6) * kSTG + (piece & 63) * 16]) = r[u];
+    }
+  };
+  // dots of the chunk's tile at row t16: lane holds blocks t16 + 4gq + i for (qn, h)
+  auto dots = [&](int t16, f32x4& acc) {
     acc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
-      const u32x4 a = ld16(kbase + kb * 128 + 32 * kk + 8 * gq);
+      const u32x4 a = *reinterpret_cast<const u32x4*>(&kl[(t16 + l16) * kSKRow + 64 * kk + 16 * gq]);
       acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(qb[kk]), acc, 0, 0, 0);
     }
   };
@@ -610,21 +656,32 @@ __global__ __launch_bounds__(256) void distill_student_mfma_kernel(
   };
   // ---- pass 1: statistics
   float m = -INFINITY, l = 0.0f, z = 0.0f, a = 0.0f, bI = 0.0f;
-  for (int64_t b0 = 0; b0 < cmax; b0 += 16) {
-    f32x4 acc;
-    dots(b0, acc);
-    float Iq[4];
-    quad_sum4(acc, Iq);
-    const float I = pick(Iq);
-    const int64_t b = b0 + 4 * gq + h;
-    if (b < c) {
-      const float mn = fmaxf(m, I);
-      l = l * exp2_fast((m - mn) * kLog2e) + exp2_fast((I - mn) * kLog2e);
-      m = mn;
-      const float t = target(b);
-      z += t;
-      if (t > 0.0f) a += t * logf(t);
-      bI += t * I;
+  u32x4 pk[4], pt[4];
+  if (cw > 0) load_k(0, pk);
+  for (int64_t ch0 = 0; ch0 < cw; ch0 += kSC) {
+    __syncthreads();   // every wave is done with the previous chunk
+    store_k(pk);
+    __syncthreads();
+    if (ch0 + kSC < cw) load_k(ch0 + kSC, pk);
+#pragma unroll
+    for (int t = 0; t < kSC / 16; ++t) {
+      const int64_t b0 = ch0 + 16 * t;
+      if (b0 >= cmax) break;
+      f32x4 acc;
+      dots(16 * t, acc);
+      float Iq[4];
+      quad_sum4(acc, Iq);
+      const float I = pick(Iq);
+      const int64_t b = b0 + 4 * gq + h;
+      if (b < c) {
+        const float mn = fmaxf(m, I);
+        l = l * exp2_fast((m - mn) * kLog2e) + exp2_fast((I - mn) * kLog2e);
+        m = mn;
+        const float tv = target(b);
+        z += tv;
+        if (tv > 0.0f) a += tv * logf(tv);
+        bI += tv * I;
+      }
     }
   }
   // combine the 16 lanes of each query (its quad, and the four gq rows)
@@ -651,43 +708,59 @@ __global__ __launch_bounds__(256) void distill_student_mfma_kernel(
   f32x4 dq[8];
 #pragma unroll
   for (int db = 0; db < 8; ++db) dq[db] = f32x4{0.f, 0.f, 0.f, 0.f};
-  const uint16_t* kT = ws.kT + (int64_t)s * (ws.nbt / 4) * 512;
-  for (int64_t b0 = 0; b0 < cmax; b0 += 16) {
-    f32x4 acc;
-    dots(b0, acc);
-    float Iq[4], bitq[4];
-    quad_sum4(acc, Iq);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {   // the heads' mask bits of block 4gq + i, on every lane
-      float bit = acc[i] > 0.0f ? (float)(1 << h) : 0.0f;
-      bit += quad_xor1(bit);
-      bit += quad_xor2(bit);
-      bitq[i] = bit;
+  if (cw > 0) {
+    load_k(0, pk);
+    load_t(0, pt);
+  }
+  for (int64_t ch0 = 0; ch0 < cw; ch0 += kSC) {
+    __syncthreads();
+    store_k(pk);
+    store_t(pt);
+    __syncthreads();
+    if (ch0 + kSC < cw) {
+      load_k(ch0 + kSC, pk);
+      load_t(ch0 + kSC, pt);
     }
-    const int64_t b = b0 + 4 * gq + h;
-    const float dI = b < c ? exp2_fast((pick(Iq) - lseI) * kLog2e) - target(b) * invZ : 0.0f;
-    if (valid) {
-      const int64_t o = row * ws.W + b;   // W is a multiple of 16
-      ws.ib[o] = dI;
-      ws.mk[o] = (uint8_t)pick(bitq);
-    }
-    // this lane's head over the quad's four blocks: W = dI [dot > 0]
-    const float dIq[4] = {
-        __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(dI), 0x00, 0xF, 0xF, false)),
-        __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(dI), 0x55, 0xF, 0xF, false)),
-        __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(dI), 0xAA, 0xF, 0xF, false)),
-        __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(dI), 0xFF, 0xF, 0xF, false))};
-    float w[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) w[i] = acc[i] > 0.0f ? dIq[i] : 0.0f;
-    bf16x4d whi, wlo;
-    split4(w, whi, wlo);
-    const uint16_t* kt = kT + ((b0 >> 2) + gq) * 512;
+    for (int t = 0; t < kSC / 16; ++t) {
+      const int64_t b0 = ch0 + 16 * t;
+      if (b0 >= cmax) break;
+      f32x4 acc;
+      dots(16 * t, acc);
+      float Iq[4], bitq[4];
+      quad_sum4(acc, Iq);
 #pragma unroll
-    for (int db = 0; db < 8; ++db) {
-      const bf16x4d bk = __builtin_bit_cast(bf16x4d, *reinterpret_cast<const uint2*>(kt + (16 * db + l16) * 4));
-      dq[db] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(whi, bk, dq[db], 0, 0, 0);
-      dq[db] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(wlo, bk, dq[db], 0, 0, 0);
+      for (int i = 0; i < 4; ++i) {   // the heads' mask bits of block 4gq + i, on every lane
+        float bit = acc[i] > 0.0f ? (float)(1 << h) : 0.0f;
+        bit += quad_xor1(bit);
+        bit += quad_xor2(bit);
+        bitq[i] = bit;
+      }
+      const int64_t b = b0 + 4 * gq + h;
+      const float dI = b < c ? exp2_fast((pick(Iq) - lseI) * kLog2e) - target(b) * invZ : 0.0f;
+      if (valid) {
+        const int64_t o = row * ws.W + b;   // W is a multiple of 16
+        ws.ib[o] = dI;
+        ws.mk[o] = (uint8_t)pick(bitq);
+      }
+      // this lane's head over the quad's four blocks: W = dI [dot > 0]
+      const float dIq[4] = {
+          __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(dI), 0x00, 0xF, 0xF, false)),
+          __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(dI), 0x55, 0xF, 0xF, false)),
+          __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(dI), 0xAA, 0xF, 0xF, false)),
+          __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(dI), 0xFF, 0xF, 0xF, false))};
+      float w[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) w[i] = acc[i] > 0.0f ? dIq[i] : 0.0f;
+      bf16x4d whi, wlo;
+      split4(w, whi, wlo);
+      const unsigned char* kt = tl + (4 * t + gq) * kSTG;
+#pragma unroll
+      for (int db = 0; db < 8; ++db) {
+        const bf16x4d bk = __builtin_bit_cast(bf16x4d, *reinterpret_cast<const uint2*>(kt + (16 * db + l16) * 8));
+        dq[db] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(whi, bk, dq[db], 0, 0, 0);
+        dq[db] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(wlo, bk, dq[db], 0, 0, 0);
+      }
     }
   }
   // lane (dim 16db + l16, gq) holds (query gq, head i)
@@ -968,8 +1041,8 @@ hipError_t launch_distill(const Dims& d, int batch, int n_q, const void* q, cons
     const int64_t ntile = ws.nbt / 16;
     hipLaunchKernelGGL(distill_kt_kernel, dim3((unsigned)((ws.nbt * 128 + 255) / 256), (unsigned)batch),
                        dim3(256), 0, st, static_cast<const uint16_t*>(k_cmp), cap_blocks, ws);
-    const int64_t waves = (int64_t)batch * ((n_q + 3) / 4);
-    hipLaunchKernelGGL(distill_student_mfma_kernel, dim3((unsigned)((waves + 3) / 4)), dim3(256),
+    const int64_t groups = (int64_t)batch * ((n_q + 15) / 16);   // 16 queries per workgroup
+    hipLaunchKernelGGL(distill_student_mfma_kernel, dim3((unsigned)groups), dim3(256),
                        0, st, static_cast<const uint16_t*>(q_idx),
                        static_cast<const uint16_t*>(k_cmp), cap_blocks, batch, n_q, q_pos0, cap,
                        d.lr, ws, loss, dq_idx);
