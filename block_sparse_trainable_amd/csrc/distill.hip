@@ -543,16 +543,20 @@ __global__ __launch_bounds__(256) void distill_kt_kernel(const uint16_t* __restr
   ws.kT[(((int64_t)s * (ws.nbt / 4) + (b >> 2)) * 128 + d) * 4 + (b & 3)] = v;
 }
 
-// One workgroup of four waves per 16 consecutive queries of a sequence; wave w
-// takes queries 4w .. 4w+3 (16 A rows: query x head).  The candidate blocks
+// One workgroup of kSW waves per 4 kSW consecutive queries of a sequence; wave
+// w takes queries 4w .. 4w+3 (16 A rows: query x head).  The candidate blocks
 // are walked in chunks of kSC: each chunk's compressed keys (and, in pass 2,
-// their transposed groups) are staged in LDS once for the four waves, the
+// their transposed groups) are staged in LDS once for the workgroup, the
 // next chunk's loads in flight meanwhile.
+constexpr int kSW = 8;               // waves per student workgroup
+constexpr int kSNT = 64 * kSW;
+constexpr int kSQ = 4 * kSW;         // queries per student workgroup
 constexpr int kSC = 64;              // blocks per LDS chunk
+constexpr int kSP = 1024 / kSNT;     // 16-byte staging pieces per thread and array
 constexpr int kSKRow = 256 + 16;     // LDS bytes per staged key row
 constexpr int kSTG = 1024 + 128;     // LDS bytes per staged transposed group of 4 blocks
 
-__global__ __launch_bounds__(256) void distill_student_mfma_kernel(
+__global__ __launch_bounds__(kSNT) void distill_student_mfma_kernel(
     const uint16_t* __restrict__ q_idx, const uint16_t* __restrict__ k_cmp, int64_t cap_blocks,
     int batch, int n_q, const int32_t* __restrict__ q_pos0, int64_t cap, int lr, DistillWs ws,
     float* __restrict__ loss, float* __restrict__ dq_idx) {
@@ -562,9 +566,9 @@ __global__ __launch_bounds__(256) void distill_student_mfma_kernel(
   const int lane = tid & 63, wave = tid >> 6;
   const int l16 = lane & 15, gq = lane >> 4;
   const int qn = l16 >> 2, h = l16 & 3;
-  const int tiles = (n_q + 15) / 16;
+  const int tiles = (n_q + kSQ - 1) / kSQ;
   const int s = (int)(blockIdx.x / (unsigned)tiles);
-  const int j0 = (int)(blockIdx.x % (unsigned)tiles) * 16;
+  const int j0 = (int)(blockIdx.x % (unsigned)tiles) * kSQ;
   const int jb = j0 + 4 * wave;
   const int j = jb + qn;
   const bool valid = j < n_q;
@@ -572,7 +576,7 @@ __global__ __launch_bounds__(256) void distill_student_mfma_kernel(
   const int64_t p = min(max((int64_t)q_pos0[s] + (valid ? j : n_q - 1), (int64_t)0), cap - 1);
   const int64_t c = valid ? p >> lr : 0;
   // the workgroup's longest row is its last query's (positions grow with j)
-  const int64_t cw = min(max((int64_t)q_pos0[s] + min(j0 + 15, n_q - 1), (int64_t)0), cap - 1) >> lr;
+  const int64_t cw = min(max((int64_t)q_pos0[s] + min(j0 + kSQ - 1, n_q - 1), (int64_t)0), cap - 1) >> lr;
   const int m4 = 1 << (lr - 2);
   u32x4 qb[4];
 #pragma unroll
@@ -594,34 +598,34 @@ __global__ __launch_bounds__(256) void distill_student_mfma_kernel(
   const int64_t last_group = ws.nbt / 4 - 1;
   const float* um = ws.um + row * ws.Wu;
   // chunk staging: 1024 pieces of 16 B for the keys (block, 16-byte column)
-  // and 1024 for the transposed groups (group, 16-byte piece), four per thread
-  auto load_k = [&](int64_t ch0, u32x4 (&r)[4]) {
+  // and 1024 for the transposed groups (group, 16-byte piece), kSP per thread
+  auto load_k = [&](int64_t ch0, u32x4 (&r)[kSP]) {
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int piece = tid + 256 * u;
+    for (int u = 0; u < kSP; ++u) {
+      const int piece = tid + kSNT * u;
       const int64_t b = min(ch0 + (piece >> 4), cap_blocks - 1);
       r[u] = ld16(kbase + b * 128 + (piece & 15) * 8);
     }
   };
-  auto store_k = [&](const u32x4 (&r)[4]) {
+  auto store_k = [&](const u32x4 (&r)[kSP]) {
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int piece = tid + 256 * u;
+    for (int u = 0; u < kSP; ++u) {
+      const int piece = tid + kSNT * u;
       *reinterpret_cast<u32x4*>(&kl[(piece >> 4) * kSKRow + (piece & 15) * 16]) = r[u];
     }
   };
-  auto load_t = [&](int64_t ch0, u32x4 (&r)[4]) {
+  auto load_t = [&](int64_t ch0, u32x4 (&r)[kSP]) {
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int piece = tid + 256 * u;
+    for (int u = 0; u < kSP; ++u) {
+      const int piece = tid + kSNT * u;
       const int64_t g = min((ch0 >> 2) + (piece >> 6), last_group);
       r[u] = ld16(kT + g * 512 + (piece & 63) * 8);
     }
   };
-  auto store_t = [&](const u32x4 (&r)[4]) {
+  auto store_t = [&](const u32x4 (&r)[kSP]) {
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int piece = tid + 256 * u;
+    for (int u = 0; u < kSP; ++u) {
+      const int piece = tid + kSNT * u;
       *reinterpret_cast<u32x4*>(&tl[(piece >> 6) * kSTG + (piece & 63) * 16]) = r[u];
     }
   };
@@ -656,7 +660,7 @@ __global__ __launch_bounds__(256) void distill_student_mfma_kernel(
   };
   // ---- pass 1: statistics
   float m = -INFINITY, l = 0.0f, z = 0.0f, a = 0.0f, bI = 0.0f;
-  u32x4 pk[4], pt[4];
+  u32x4 pk[kSP], pt[kSP];
   if (cw > 0) load_k(0, pk);
   for (int64_t ch0 = 0; ch0 < cw; ch0 += kSC) {
     __syncthreads();   // every wave is done with the previous chunk
@@ -1041,8 +1045,8 @@ hipError_t launch_distill(const Dims& d, int batch, int n_q, const void* q, cons
     const int64_t ntile = ws.nbt / 16;
     hipLaunchKernelGGL(distill_kt_kernel, dim3((unsigned)((ws.nbt * 128 + 255) / 256), (unsigned)batch),
                        dim3(256), 0, st, static_cast<const uint16_t*>(k_cmp), cap_blocks, ws);
-    const int64_t groups = (int64_t)batch * ((n_q + 15) / 16);   // 16 queries per workgroup
-    hipLaunchKernelGGL(distill_student_mfma_kernel, dim3((unsigned)groups), dim3(256),
+    const int64_t groups = (int64_t)batch * ((n_q + kSQ - 1) / kSQ);   // kSQ queries per workgroup
+    hipLaunchKernelGGL(distill_student_mfma_kernel, dim3((unsigned)groups), dim3(kSNT),
                        0, st, static_cast<const uint16_t*>(q_idx),
                        static_cast<const uint16_t*>(k_cmp), cap_blocks, batch, n_q, q_pos0, cap,
                        d.lr, ws, loss, dq_idx);
