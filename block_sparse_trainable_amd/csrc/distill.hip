@@ -204,16 +204,11 @@ __global__ __launch_bounds__(kDT) void distill_teacher_kernel(
 // lse per (row, head); PASS 2 turns the logits into probabilities, sums each
 // (query, token)'s 16 heads across lanes, and writes the maximum of the head
 // mean over each 4-token unit below the query's candidate limit.
-__device__ __forceinline__ float swz_add(float v, int pattern_xor) {
-  // ds_swizzle in bit-mask mode: lane' = lane ^ x within each 32-lane half
-  int r;
-  switch (pattern_xor) {
-    case 1: r = __builtin_amdgcn_ds_swizzle(__float_as_int(v), 0x041F); break;
-    case 2: r = __builtin_amdgcn_ds_swizzle(__float_as_int(v), 0x081F); break;
-    case 4: r = __builtin_amdgcn_ds_swizzle(__float_as_int(v), 0x101F); break;
-    default: r = __builtin_amdgcn_ds_swizzle(__float_as_int(v), 0x201F); break;
-  }
-  return v + __int_as_float(r);
+// v plus its value in the lane the DPP control CTRL names (within a 16-lane
+// row): a VALU add with a lane permutation, no LDS traffic
+template <int CTRL>
+__device__ __forceinline__ float dpp_add(float v) {
+  return v + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
 }
 
 constexpr int kTW = 8;    // waves per teacher workgroup
@@ -374,11 +369,13 @@ __global__ __launch_bounds__(64 * kTW) void distill_teacher_mfma_kernel(
               const int cg = qs * HKV + g;
               a += exp2_fast(fmaf(sa[cg][st][i], sl2, -lse2[cg]));
             }
-            // sum over the query's heads held by the lanes of this group
-            a = swz_add(a, 1);
-            a = swz_add(a, 2);
-            a = swz_add(a, 4);
-            if constexpr (HKV == 1) a = swz_add(a, 8);
+            // sum over the query's heads held by the 8 (or 16) lanes of this
+            // group: lane pairs xor 1 and xor 2 of each quad, then the two
+            // quads of each 8-lane half (and the two halves of a row)
+            a = dpp_add<0xB1>(a);    // quad_perm [1,0,3,2]
+            a = dpp_add<0x4E>(a);    // quad_perm [2,3,0,1]
+            a = dpp_add<0x141>(a);   // row_half_mirror
+            if constexpr (HKV == 1) a = dpp_add<0x140>(a);   // row_mirror
             v[st][i] = a;   // the head sum; the mean's 1/16 is applied after the unit max
           }
         const int cg0 = qs * HKV;
