@@ -37,6 +37,7 @@
 
 #include <math.h>
 
+#include "fast_exp.h"
 #include "qsa_common.h"
 
 namespace qsa {
@@ -204,14 +205,14 @@ __device__ __forceinline__ void attn_mfma_tiles(
     mt = wave_max_xor32(wave_max_xor16(mt));
     const float m_new = fmaxf(m_run, mt);
     const bool any = m_new != -INFINITY;
-    const float alpha = any ? exp2f(m_run - m_new) : 1.0f;
+    const float alpha = any ? exp2_fast(m_run - m_new) : 1.0f;
     float pr[2][4];
     float psum = 0.0f;
 #pragma unroll
     for (int st = 0; st < 2; ++st)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        pr[st][i] = any ? exp2f(x[st][i] - m_new) : 0.0f;
+        pr[st][i] = any ? exp2_fast(x[st][i] - m_new) : 0.0f;
         psum += pr[st][i];
       }
     l_run = l_run * alpha + psum;
@@ -298,7 +299,7 @@ __device__ __forceinline__ void attn_mfma_tiles(
     for (int w = 0; w < 4; ++w) {
       float f = -1.0f;
       if (mw[w] != -INFINITY) {
-        f = exp2f(mw[w] - mx);
+        f = exp2_fast(mw[w] - mx);
         z += f * lw[w];
       }
       fac[w * 16 + n] = f;
@@ -373,7 +374,7 @@ __device__ __forceinline__ void lse_merge_splits(const float* ml, const float (&
   for (int k = 0; k < kDecodeSplits; ++k) {
     const float mk = ml[2 * k];
     if (mk != -INFINITY) {
-      const float f = exp2f(mk - mx);
+      const float f = exp2_fast(mk - mx);
       zs += f * ml[2 * k + 1];
       acc += f * o[k];
     }
