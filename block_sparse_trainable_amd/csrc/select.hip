@@ -810,9 +810,10 @@ __global__ __launch_bounds__(NT) void select_row_kernel(FilterArgs a) {
   const bool band = r.need < r.avail;
   if (band) {
     // the band (keys equal to T) listed in hist: [0, nb) pool indices, then
-    // [kBandMax, +nb) exact score bits
+    // [kBandMax, +nb) exact score bits, then [2 kBandMax, +nb) block ids
     uint32_t* blist = hist;
     uint32_t* bval = hist + kBandMax;
+    uint32_t* bid = hist + 2 * kBandMax;
     uint32_t* bcount = &scratch[48];
     if (tid == 0) *bcount = 0u;
     __syncthreads();
@@ -854,35 +855,41 @@ __global__ __launch_bounds__(NT) void select_row_kernel(FilterArgs a) {
           }
 #pragma unroll
           for (int h = 0; h < 4; ++h) acc[h] = row16_sum_to_last(acc[h]);  // the group's lane 15
-          if (g16 == 15 && ent[q] < nb)
+          if (g16 == 15 && ent[q] < nb) {
             bval[ent[q]] = __float_as_uint(relu(acc[0]) + relu(acc[1]) + relu(acc[2]) + relu(acc[3]));
+            bid[ent[q]] = cidx[pslot(blist[ent[q]])];
+          }
         }
       }
     }
     __syncthreads();
     // rank inside the band: larger exact score first, then the lower index;
-    // the r.need best are kept
+    // the r.need best are kept.  The ranks read only the band's own arrays,
+    // so each member's pool slot is updated by its thread right away.
     for (uint32_t e = tid; e < nb; e += NT) {
       const uint32_t ve = bval[e];
-      const uint32_t ie = cidx[pslot(blist[e])];
+      const uint32_t ie = bid[e];
       uint32_t rank = 0;
+#pragma unroll 4
       for (uint32_t f = 0; f < nb; ++f) {
         const uint32_t vf = bval[f];
-        const uint32_t iff = cidx[pslot(blist[f])];
+        const uint32_t iff = bid[f];
         rank += (vf > ve || (vf == ve && iff < ie)) ? 1u : 0u;
       }
-      bval[kBandMax + e] = rank;
-    }
-    __syncthreads();
-    for (uint32_t e = tid; e < nb; e += NT) {
       const uint32_t sl = pslot(blist[e]);
-      ckey[sl] = bval[e];
-      cidx[sl] |= kBand | (bval[kBandMax + e] < r.need ? kBandKept : 0u);
+      ckey[sl] = ve;
+      cidx[sl] = ie | kBand | (rank < r.need ? kBandKept : 0u);
     }
     __syncthreads();
   }
 
   // ---- 4. the ordered output ---------------------------------------------
+  // With k_B <= 512 the kept ids and scores are staged by position in LDS
+  // (hist and qs are free now) and written out in coalesced runs.
+  constexpr bool kStage = CAP <= 3072;
+  static_assert(!kStage || 3 * kBandMax >= 512, "staging room");
+  uint32_t* ostage = hist;
+  float* vstage = qs;
   uint32_t written = 0;
   for (uint32_t base = 0; base < n_f; base += 16 * NT) {
     const uint32_t i0 = base + 16 * tid;
@@ -905,11 +912,26 @@ __global__ __launch_bounds__(NT) void select_row_kernel(FilterArgs a) {
       if (take & (1u << e)) {
         const uint32_t sl = pslot(i0 + e);
         const uint32_t x = cidx[sl];
-        out[pos] = (int32_t)(x & kIdxMask);
-        if (outs) outs[pos] = (x & kBand) ? __uint_as_float(ckey[sl]) : key16_value(ckey[sl]);
+        const float v = (x & kBand) ? __uint_as_float(ckey[sl]) : key16_value(ckey[sl]);
+        if constexpr (kStage) {
+          if (pos < (uint32_t)kB) {
+            ostage[pos] = x & kIdxMask;
+            vstage[pos] = v;
+          }
+        } else {
+          out[pos] = (int32_t)(x & kIdxMask);
+          if (outs) outs[pos] = v;
+        }
         ++pos;
       }
     written += tot;
+  }
+  if constexpr (kStage) {
+    __syncthreads();
+    for (int i = tid; i < kB; i += NT) {
+      out[i] = (int32_t)ostage[i];
+      if (outs) outs[i] = vstage[i];
+    }
   }
   if (tid == 0) a.cnt[row] = kB;
 }
