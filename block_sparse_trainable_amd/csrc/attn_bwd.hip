@@ -181,10 +181,12 @@ __device__ __forceinline__ uint32_t swap8(uint32_t v) {
 }
 __device__ __forceinline__ float swap8f(float v) { return __uint_as_float(swap8(__float_as_uint(v))); }
 
-// (the two-KV-head, 128-dim shape needs about 300 registers: one workgroup
-// per CU, the others two)
-template <int HKV, int D>
-__global__ __launch_bounds__(256, (HKV == 2 && D == 128) ? 1 : 2) void bwd_query_mfma_kernel(
+// TT: tokens of a wave's tile, 32 or 16.  The two-KV-head, 128-dim shape
+// takes 16-token tiles: its V rows held in registers for a 32-token tile
+// need about 300 registers, one wave per SIMD; with 16 the kernel fits two
+// (the k-slots of the dq MFMAs past the tile are zero).
+template <int HKV, int D, int TT>
+__global__ __launch_bounds__(256, 2) void bwd_query_mfma_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kc,
     const uint16_t* __restrict__ vc, int64_t cap, int n_q, const int32_t* __restrict__ q_pos0,
     const int32_t* __restrict__ sel, const int32_t* __restrict__ cnt, int kB, float scale,
@@ -197,7 +199,11 @@ __global__ __launch_bounds__(256, (HKV == 2 && D == 128) ? 1 : 2) void bwd_query
   constexpr int MF = S::MERGE_FLOATS, DP = S::DP;
   constexpr int NACC = HKV == 2 ? 1 : 2;   // accumulator sets (A and B share one with 2 KV heads)
   static_assert(16 * DP <= MF, "a wave's dq part must fit its merge slot");
-  __shared__ __attribute__((aligned(16))) unsigned char lds[S::LDS_BYTES];
+  static_assert(TT == 16 || TT == 32, "tile tokens");
+  constexpr int NST = TT / 16;                 // 16-token halves of a tile
+  constexpr int TILE = TT * ROWB;              // LDS bytes of a wave's K tile
+  constexpr int LB = 4 * TILE > S::MERGE_BYTES ? 4 * TILE : S::MERGE_BYTES;
+  __shared__ __attribute__((aligned(16))) unsigned char lds[LB];
   __shared__ int32_t sbid[kMaxPB];
   __shared__ float dref[16], dpart[4][16];
   __shared__ u32x4 dbs[NK * 64];   // dObd in lane order (kept out of registers)
@@ -280,20 +286,20 @@ __global__ __launch_bounds__(256, (HKV == 2 && D == 128) ? 1 : 2) void bwd_query
 #pragma unroll
     for (int pp = 0; pp < NK; ++pp) acc[a][pp][0] = acc[a][pp][1] = f32x4{0.f, 0.f, 0.f, 0.f};
   float dacc = 0.0f;
-  unsigned char* kt = lds + wave * S::TILE_LDS;
+  unsigned char* kt = lds + wave * TILE;
 
-  for (int pb0 = 8 * wave; pb0 < npb; pb0 += 32) {
+  for (int pb0 = (TT / 4) * wave; pb0 < npb; pb0 += TT) {
     // ---- V rows into A-operand registers
-    u32x4 vreg[2][NK];
+    u32x4 vreg[NST][NK];
 #pragma unroll
-    for (int st = 0; st < 2; ++st) {
+    for (int st = 0; st < NST; ++st) {
       const uint16_t* vp = vbase + trow(pb0, 16 * st + l16) * KD + 8 * gq;
 #pragma unroll
       for (int kk = 0; kk < NK; ++kk) vreg[st][kk] = ld16(vp + 32 * kk);
     }
     // ---- K rows into this wave's LDS tile (lane-ordered 1 KiB per load)
 #pragma unroll
-    for (int u = 0; u < 32 / RPI; ++u) {
+    for (int u = 0; u < TT / RPI; ++u) {
       const int tk = RPI * u + lane / CH;
       const int chunk = (lane % CH) ^ kswz(tk);
       __builtin_amdgcn_global_load_lds(
@@ -301,9 +307,9 @@ __global__ __launch_bounds__(256, (HKV == 2 && D == 128) ? 1 : 2) void bwd_query
           (__attribute__((address_space(3))) void*)(kt + u * 1024), 16, 0, 0);
     }
     // ---- dP^T = V * dObd: lane holds tokens 16st + 4gq + i for head l16
-    f32x4 dpa[2];
+    f32x4 dpa[NST];
 #pragma unroll
-    for (int st = 0; st < 2; ++st) {
+    for (int st = 0; st < NST; ++st) {
       dpa[st] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int kk = 0; kk < NK; ++kk)
@@ -313,9 +319,9 @@ __global__ __launch_bounds__(256, (HKV == 2 && D == 128) ? 1 : 2) void bwd_query
     __builtin_amdgcn_s_waitcnt(0);  // this wave's K tile has landed in LDS
     wave_sync();
     // ---- S^T = K * Qbd from the tile
-    f32x4 sa[2];
+    f32x4 sa[NST];
 #pragma unroll
-    for (int st = 0; st < 2; ++st) {
+    for (int st = 0; st < NST; ++st) {
       const int tk = 16 * st + l16;
       sa[st] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -327,9 +333,11 @@ __global__ __launch_bounds__(256, (HKV == 2 && D == 128) ? 1 : 2) void bwd_query
       }
     }
     // ---- P, D partial, weights P (dP - D~) and P
-    float w1[2][4], w2[2][4];
+    float w1[2][4], w2[2][4];   // half st = 1 stays zero with 16-token tiles
 #pragma unroll
-    for (int st = 0; st < 2; ++st) {
+    for (int i = 0; i < 4; ++i) w1[1][i] = w2[1][i] = 0.0f;
+#pragma unroll
+    for (int st = 0; st < NST; ++st) {
       const int64_t b = bid(pb0 + 4 * st + gq);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -343,7 +351,7 @@ __global__ __launch_bounds__(256, (HKV == 2 && D == 128) ? 1 : 2) void bwd_query
     // the key side's inputs: {P, P (dP - D~)} per token of the row's set
     // ([row][token][head]; tokens past p hold zeros)
 #pragma unroll
-    for (int st = 0; st < 2; ++st) {
+    for (int st = 0; st < NST; ++st) {
       if (pb0 + 4 * st + gq < npb) {
         float2* dst = pw + ((row * max_pb + pb0 + 4 * st + gq) * 4) * 16 + l16;
 #pragma unroll
@@ -395,7 +403,11 @@ __global__ __launch_bounds__(256, (HKV == 2 && D == 128) ? 1 : 2) void bwd_query
       for (int e = 0; e < 8; ++e) {
         const int tr = (e < 4) ? (4 * gq + e) : (16 + 4 * gq + e - 4);
         const int chunk = (4 * pp + (l16 >> 2)) ^ kswz(tr);
-        w[e] = *reinterpret_cast<const uint32_t*>(kt + tr * ROWB + chunk * 16 + 4 * (l16 & 3));
+        // (with 16-token tiles the slots of tokens 16.. hold zero weights:
+        // their K values are read as 0, not from the next wave's tile)
+        w[e] = (TT == 32 || e < 4)
+                   ? *reinterpret_cast<const uint32_t*>(kt + tr * ROWB + chunk * 16 + 4 * (l16 & 3))
+                   : 0u;
       }
       u32x4 a0, a1;
 #pragma unroll
@@ -949,7 +961,8 @@ hipError_t launch_attn_backward(const Dims& d, int batch, int n_q, const void* q
                        glist, cap, n_q, q_pos0, sel, cnt, d.kB, d.lr);
 #define QSA_BWD_MFMA(HKV, DD)                                                                  \
   if (d.kv_heads == HKV && d.head_dim == DD) {                                                 \
-    hipLaunchKernelGGL((bwd_query_mfma_kernel<HKV, DD>), dim3((unsigned)rows), dim3(256), 0, st, \
+    hipLaunchKernelGGL((bwd_query_mfma_kernel<HKV, DD, (HKV == 2 && DD == 128) ? 16 : 32>),    \
+                       dim3((unsigned)rows), dim3(256), 0, st,                                \
                        static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k_cache), \
                        static_cast<const uint16_t*>(v_cache), cap, n_q, q_pos0, sel, cnt, d.kB, \
                        d.scale, static_cast<const uint16_t*>(out), lse,                       \
