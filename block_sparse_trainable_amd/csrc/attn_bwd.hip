@@ -39,7 +39,6 @@ namespace {
 constexpr int kBwdMaxTokens = 2048 + 128;   // r * k_B <= 2048 selected, tail <= r
 constexpr int kNT = 256;
 constexpr int kKeySplit = 2;   // key side: dim groups of waves (1, 2 or 4)
-constexpr int kKeyPF = 2;   // key side: the next entry's loads issued before this one is consumed
 
 template <bool BF16>
 __device__ __forceinline__ float ldx(const void* p, int64_t i) {
@@ -714,6 +713,25 @@ __device__ __forceinline__ bf16x4s pack4(uint32_t a, uint32_t b) {
   return __builtin_bit_cast(bf16x4s, make_uint2(a, b));
 }
 
+// fourth word of a raw buffer resource on gfx9 parts (32-bit data format,
+// no swizzle): offsets past num_records read as zero
+constexpr int kBufWord3 = 0x00020000;
+
+typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
+typedef float f32x2v __attribute__((ext_vector_type(2)));
+
+// bf16 pair of (x, y), nearest-even (one packed conversion on gfx950); with
+// sel = 1 the pair of the remainders x - hi, y - hi left by that rounding:
+// hi + lo carries about 16 significant bits of each value.
+__device__ __forceinline__ uint32_t bf16_pk2(float x, float y) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2v{x, y}, bf16x2v));
+}
+__device__ __forceinline__ uint32_t bf16_hilo2(float x, float y, float sel) {
+  const uint32_t h = bf16_pk2(x, y);
+  return bf16_pk2(fmaf(-sel, __uint_as_float(h << 16), x),
+                  fmaf(-sel, __uint_as_float(h & 0xFFFF0000u), y));
+}
+
 // One workgroup per (sequence, 16-token group); its waves, in kKeySplit
 // groups that each own a share of the Hkv*d dims, take the group's entries in
 // turn.  Per entry, lane (token l16, heads 4gq .. 4gq+3) forms
@@ -724,7 +742,7 @@ __device__ __forceinline__ bf16x4s pack4(uint32_t a, uint32_t b) {
 //     dK[token][dim] += sum_h dS[h][token] q[h][dim],
 //     dV[token][dim] += sum_h  P[h][token] dO[h][dim].
 // The waves' sums meet in LDS and are added to dK (times scale) and dV once.
-template <int HKV, int D, int PF>
+template <int HKV, int D>
 __global__ __launch_bounds__(256, 2) void bwd_key_mfma_kernel(
     BwdIndex gx, const uint2* __restrict__ glist, const float2* __restrict__ pw, int max_pb,
     const uint16_t* __restrict__ qt, const uint16_t* __restrict__ dot,
@@ -760,108 +778,125 @@ __global__ __launch_bounds__(256, 2) void bwd_key_mfma_kernel(
 #pragma unroll
   for (int b = 0; b < NBW; ++b) ak[b] = av[b] = f32x4{0.f, 0.f, 0.f, 0.f};
   const uint2* lst = glist + gx.off[item];
-
-  // {P, weight} of the lane's token for heads 4gq .. 4gq+3, and D - D~
-  auto fetch_pw = [&](uint2 en, float4& a, float4& b, float4& dl) {
-    const int64_t row = en.x >> 4;
-    const uint32_t mask = en.x & 15u;
-    a = b = float4{0.f, 0.f, 0.f, 0.f};
-    if ((mask >> u) & 1u) {
-      const int idx = (int)en.y + __popc(mask & ((1u << u) - 1u));
-      const float4* src =
-          reinterpret_cast<const float4*>(pw + ((row * max_pb + idx) * 4 + t) * 16 + 4 * gq);
-      a = src[0];
-      b = src[1];
-    }
-    dl = *reinterpret_cast<const float4*>(dlt + row * 16 + 4 * gq);
+  // Heads of the lane's A operand and of its B operand's q / dO rows.
+  // Two KV heads: a wave's dims are one KV head's (g), whose 8 query heads
+  // fill half of a 16-head contraction; lanes gq and gq ^ 2 take heads
+  // 8g + 4 (gq & 1) .. + 3, the first pair carrying the bf16 hi part of the
+  // weights and the second the lo part, so k-slots 0..7 and 8..15 of one
+  // MFMA add hi and lo.  One KV head: lane gq takes heads 4gq .. 4gq + 3, and
+  // hi and lo go through two MFMAs.
+  constexpr bool FUSE = HKV == 2;
+  const int g = (16 * bbase) / D;
+  const int hb = FUSE ? 8 * g + 4 * (gq & 1) : 4 * gq;
+  const float lo_sel = (FUSE && gq >= 2) ? 1.0f : 0.0f;
+  // per-lane byte offsets of an entry's loads within the row's {P, weight}
+  // slots and transposed q / dO
+  const uint32_t pw_lane = (uint32_t)(t * 16 + hb) * 8u;
+  uint32_t q_lane[NBW / 2];
+#pragma unroll
+  for (int b = 0; b < NBW; b += 2) {
+    const int grp = (16 * (bbase + b)) / D;
+    q_lane[b / 2] = 2u * (uint32_t)qt_index<HKV, D>(0, grp, 16 * (bbase + b) - grp * D + l16,
+                                                     4 * (gq % (G / 4)));
+  }
+  // lanes whose heads are not the blocks' KV head (one-KV-head layout never
+  // has any) read a neighbour's address and are zeroed when consumed
+  struct Stage {
+    float4 a, b, dl;        // {P, weight} of the lane's token for its 4 heads; D - D~
+    uint2 q4[NBW], d4[NBW]; // transposed q / dO, 4 heads per lane
   };
-  // transposed q / dO of two 16-dim blocks, 4 heads per lane; lanes whose
-  // heads are not the blocks' KV head read a neighbour's address (no extra
-  // traffic) and are zeroed when consumed
-  auto fetch_q = [&](uint2 en, uint2 (&q4)[NBW], uint2 (&d4)[NBW]) {
-    const int64_t row = en.x >> 4;
+  // An entry's loads go through buffer resources built per row in scalar
+  // registers, with the lane offsets fixed above.  Lanes of units outside
+  // the entry, and every lane of a stage past the list, give their {P,
+  // weight} loads an offset past the resource: those return zero without a
+  // memory access, so the A operands of tokens outside the entry are zero
+  // with no branch.  Every fetch thus issues the same loads and the waits
+  // before a stage's use cover that stage's loads only.
+  auto fetch = [&](uint32_t k, uint32_t n, Stage& S) {
+    const uint2 en = sl[min(k, n - 1u)];
+    const uint32_t ex = __builtin_amdgcn_readfirstlane(en.x);
+    const uint32_t ey = __builtin_amdgcn_readfirstlane(en.y);
+    const int64_t row = ex >> 4;
+    const uint32_t mask = k < n ? ex & 15u : 0u;
+    const __amdgpu_buffer_rsrc_t rp = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<float2*>(pw + row * max_pb * 64), 0, max_pb * 512, kBufWord3);
+    const uint32_t off = ((mask >> u) & 1u)
+                             ? (ey + (uint32_t)__popc(mask & ((1u << u) - 1u))) * 512u + pw_lane
+                             : 0x80000000u;
+    S.a = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(rp, off, 0, 0));
+    S.b = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(rp, off + 16u, 0, 0));
+    S.dl = *reinterpret_cast<const float4*>(dlt + row * 16 + hb);
+    const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(qt + row * (16 * D)), 0, 32 * D, kBufWord3);
+    const __amdgpu_buffer_rsrc_t rd = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(dot + row * (16 * D)), 0, 32 * D, kBufWord3);
 #pragma unroll
     for (int b = 0; b < NBW; b += 2) {
-      const int grp = (16 * (bbase + b)) / D;
-      const int64_t o =
-          qt_index<HKV, D>(row, grp, 16 * (bbase + b) - grp * D + l16, 4 * (gq % (G / 4)));
-      const u32x4 qq = *reinterpret_cast<const u32x4*>(qt + o);
-      const u32x4 dd = *reinterpret_cast<const u32x4*>(dot + o);
-      q4[b] = make_uint2(qq[0], qq[1]);
-      q4[b + 1] = make_uint2(qq[2], qq[3]);
-      d4[b] = make_uint2(dd[0], dd[1]);
-      d4[b + 1] = make_uint2(dd[2], dd[3]);
+      const u32x4 qq = __builtin_amdgcn_raw_buffer_load_b128(rq, q_lane[b / 2], 0, 0);
+      const u32x4 dd = __builtin_amdgcn_raw_buffer_load_b128(rd, q_lane[b / 2], 0, 0);
+      S.q4[b] = make_uint2(qq[0], qq[1]);
+      S.q4[b + 1] = make_uint2(qq[2], qq[3]);
+      S.d4[b] = make_uint2(dd[0], dd[1]);
+      S.d4[b + 1] = make_uint2(dd[2], dd[3]);
     }
   };
-  auto consume = [&](const float4& a, const float4& b, const float4& dl, const uint2 (&q4)[NBW],
-                     const uint2 (&d4)[NBW]) {
-    uint32_t sh[4], sl2[4], ph[4], pl[4];
-    auto split = [&](int k, float P, float w, float dlk) {
-      const float dS = fmaf(-dlk, P, w);
-      sh[k] = f32_to_bf16(dS);
-      sl2[k] = f32_to_bf16(dS - bf16_to_f32(sh[k]));
-      ph[k] = f32_to_bf16(P);
-      pl[k] = f32_to_bf16(P - bf16_to_f32(ph[k]));
-    };
-    split(0, a.x, a.y, dl.x);
-    split(1, a.z, a.w, dl.y);
-    split(2, b.x, b.y, dl.z);
-    split(3, b.z, b.w, dl.w);
-    const bf16x4s aSh = pack4(sh[0] | (sh[1] << 16), sh[2] | (sh[3] << 16));
-    const bf16x4s aSl = pack4(sl2[0] | (sl2[1] << 16), sl2[2] | (sl2[3] << 16));
-    const bf16x4s aPh = pack4(ph[0] | (ph[1] << 16), ph[2] | (ph[3] << 16));
-    const bf16x4s aPl = pack4(pl[0] | (pl[1] << 16), pl[2] | (pl[3] << 16));
+  // dS = P (dP - D~) - (D - D~) P and P as bf16 A operands, then the MFMAs
+  auto consume = [&](const Stage& S) {
+    const float s0 = fmaf(-S.dl.x, S.a.x, S.a.y), s1 = fmaf(-S.dl.y, S.a.z, S.a.w);
+    const float s2 = fmaf(-S.dl.z, S.b.x, S.b.y), s3 = fmaf(-S.dl.w, S.b.z, S.b.w);
+    if constexpr (FUSE) {
+      const bf16x4s aS = pack4(bf16_hilo2(s0, s1, lo_sel), bf16_hilo2(s2, s3, lo_sel));
+      const bf16x4s aP = pack4(bf16_hilo2(S.a.x, S.a.z, lo_sel), bf16_hilo2(S.b.x, S.b.z, lo_sel));
 #pragma unroll
-    for (int bb = 0; bb < NBW; ++bb) {
-      const bool mine = (4 * gq) / G == (16 * (bbase + bb)) / D;
-      const uint2 z = make_uint2(0u, 0u);
-      const bf16x4s bq = __builtin_bit_cast(bf16x4s, mine ? q4[bb] : z);
-      const bf16x4s bd = __builtin_bit_cast(bf16x4s, mine ? d4[bb] : z);
-      ak[bb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(aSh, bq, ak[bb], 0, 0, 0);
-      ak[bb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(aSl, bq, ak[bb], 0, 0, 0);
-      av[bb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(aPh, bd, av[bb], 0, 0, 0);
-      av[bb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(aPl, bd, av[bb], 0, 0, 0);
+      for (int bb = 0; bb < NBW; ++bb) {
+        ak[bb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(
+            aS, __builtin_bit_cast(bf16x4s, S.q4[bb]), ak[bb], 0, 0, 0);
+        av[bb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(
+            aP, __builtin_bit_cast(bf16x4s, S.d4[bb]), av[bb], 0, 0, 0);
+      }
+    } else {
+      const bf16x4s aSh = pack4(bf16_pk2(s0, s1), bf16_pk2(s2, s3));
+      const bf16x4s aSl = pack4(bf16_hilo2(s0, s1, 1.0f), bf16_hilo2(s2, s3, 1.0f));
+      const bf16x4s aPh = pack4(bf16_pk2(S.a.x, S.a.z), bf16_pk2(S.b.x, S.b.z));
+      const bf16x4s aPl = pack4(bf16_hilo2(S.a.x, S.a.z, 1.0f), bf16_hilo2(S.b.x, S.b.z, 1.0f));
+#pragma unroll
+      for (int bb = 0; bb < NBW; ++bb) {
+        const bool mine = (4 * gq) / G == (16 * (bbase + bb)) / D;
+        const uint2 z = make_uint2(0u, 0u);
+        const bf16x4s bq = __builtin_bit_cast(bf16x4s, mine ? S.q4[bb] : z);
+        const bf16x4s bd = __builtin_bit_cast(bf16x4s, mine ? S.d4[bb] : z);
+        ak[bb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(aSh, bq, ak[bb], 0, 0, 0);
+        ak[bb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(aSl, bq, ak[bb], 0, 0, 0);
+        av[bb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(aPh, bd, av[bb], 0, 0, 0);
+        av[bb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(aPl, bd, av[bb], 0, 0, 0);
+      }
     }
   };
 
+  const uint32_t wv = __builtin_amdgcn_readfirstlane((uint32_t)wave);
   for (uint32_t base = 0; base < nq; base += LCAP) {
     const uint32_t n = min(nq - base, LCAP);
     __syncthreads();  // the previous chunk's entries are read
     for (uint32_t i = threadIdx.x; i < n; i += 256) sl[i] = lst[base + i];
     __syncthreads();
-    uint32_t k = wave / NS;
-    if (k < n) {
-      // the next entry's loads are issued before this one is consumed
-      // (PF = 1: its {P, weight} and D - D~; PF = 2: everything)
-      uint2 en = sl[k];
-      float4 a, b, dl;
-      uint2 q4[NBW], d4[NBW];
-      fetch_pw(en, a, b, dl);
-      if constexpr (PF == 2) fetch_q(en, q4, d4);
-      for (; k < n; k += STEP) {
-        const uint2 en2 = sl[k + STEP < n ? k + STEP : k];
-        float4 a2, b2, dl2;
-        uint2 q42[NBW], d42[NBW];
-        if constexpr (PF >= 1) fetch_pw(en2, a2, b2, dl2);
-        if constexpr (PF == 2) fetch_q(en2, q42, d42);
-        if constexpr (PF == 0) fetch_pw(en, a, b, dl);
-        if constexpr (PF <= 1) fetch_q(en, q4, d4);
-        consume(a, b, dl, q4, d4);
-        en = en2;
-        if constexpr (PF >= 1) {
-          a = a2;
-          b = b2;
-          dl = dl2;
-        }
-        if constexpr (PF == 2) {
-#pragma unroll
-          for (int bb = 0; bb < NBW; ++bb) {
-            q4[bb] = q42[bb];
-            d4[bb] = d42[bb];
-          }
-        }
-      }
-    }
+    uint32_t k = wv / NS;
+    if (k >= n) continue;
+    // two stages in turn: an entry's loads are issued before the previous
+    // entry is consumed.  The loop's only exit test is at its end (a stage
+    // past the list is consumed with zero weights), so the compiler cannot
+    // sink a fetch past an exit to its use; the scheduling barriers keep
+    // the machine scheduler from doing the same.
+    Stage A, B;
+    fetch(k, n, A);
+    do {
+      fetch(k + STEP, n, B);
+      __builtin_amdgcn_sched_barrier(0);
+      consume(A);
+      fetch(k + 2 * STEP, n, A);
+      __builtin_amdgcn_sched_barrier(0);
+      consume(B);
+      k += 2 * STEP;
+    } while (k < n);
   }
   __syncthreads();
   for (int i = threadIdx.x; i < 2 * 16 * KD; i += 256) sbuf[i] = 0.0f;
@@ -968,7 +1003,7 @@ hipError_t launch_attn_backward(const Dims& d, int batch, int n_q, const void* q
                        d.scale, static_cast<const uint16_t*>(out), lse,                       \
                        static_cast<const uint16_t*>(dout), static_cast<uint16_t*>(dq), dsum, pw, \
                        pl.max_pb, qt, dot, d.lr);                                              \
-    hipLaunchKernelGGL((bwd_key_mfma_kernel<HKV, DD, kKeyPF>), dim3((unsigned)nblk), dim3(256), 0, st, ix, \
+    hipLaunchKernelGGL((bwd_key_mfma_kernel<HKV, DD>), dim3((unsigned)nblk), dim3(256), 0, st, ix, \
                        glist, pw, pl.max_pb, qt, dot, dsum, cap, d.scale, dk, dv);             \
   }
     QSA_BWD_MFMA(2, 128)
