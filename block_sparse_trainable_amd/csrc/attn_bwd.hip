@@ -786,24 +786,32 @@ __global__ __launch_bounds__(256, 2) void bwd_key_mfma_kernel(
   // MFMA add hi and lo.  One KV head: lane gq takes heads 4gq .. 4gq + 3, and
   // hi and lo go through two MFMAs.
   constexpr bool FUSE = HKV == 2;
+  const uint32_t wv = __builtin_amdgcn_readfirstlane((uint32_t)wave);
   const int g = (16 * bbase) / D;
+  const uint32_t gs = (16u * ((wv % NS) * NBW)) / D;   // g, wave-uniform
   const int hb = FUSE ? 8 * g + 4 * (gq & 1) : 4 * gq;
   const float lo_sel = (FUSE && gq >= 2) ? 1.0f : 0.0f;
-  // per-lane byte offsets of an entry's loads within the row's {P, weight}
-  // slots and transposed q / dO
-  const uint32_t pw_lane = (uint32_t)(t * 16 + hb) * 8u;
-  uint32_t q_lane[NBW / 2];
+  // Per-lane byte offsets of an entry's loads within the row's {P, weight}
+  // slots and transposed q / dO.  With two KV heads lanes gq and gq ^ 2 need
+  // the same values, so each is loaded once: lanes gq < 2 load the {P,
+  // weight} pairs of heads hb, hb + 1 and the q / dO of 16-dim blocks 4j,
+  // 4j + 1, lanes gq >= 2 those of heads hb + 2, hb + 3 and blocks 4j + 2,
+  // 4j + 3, and a swap of the wave's halves (v_permlane32_swap) hands every
+  // lane both parts.  D - D~ of the wave's 8 heads is one scalar load.
+  constexpr int NQ = FUSE ? NBW / 4 : NBW / 2;   // 16-byte q (and dO) loads per entry
+  const uint32_t pw_lane = (uint32_t)(t * 16 + hb) * 8u + ((FUSE && gq >= 2) ? 16u : 0u);
+  uint32_t q_lane[NQ];
 #pragma unroll
-  for (int b = 0; b < NBW; b += 2) {
+  for (int j = 0; j < NQ; ++j) {
+    const int b = FUSE ? 4 * j + (gq >= 2 ? 2 : 0) : 2 * j;
     const int grp = (16 * (bbase + b)) / D;
-    q_lane[b / 2] = 2u * (uint32_t)qt_index<HKV, D>(0, grp, 16 * (bbase + b) - grp * D + l16,
-                                                     4 * (gq % (G / 4)));
+    q_lane[j] = 2u * (uint32_t)qt_index<HKV, D>(0, grp, 16 * (bbase + b) - grp * D + l16,
+                                                 4 * (gq % (G / 4)));
   }
-  // lanes whose heads are not the blocks' KV head (one-KV-head layout never
-  // has any) read a neighbour's address and are zeroed when consumed
   struct Stage {
-    float4 a, b, dl;        // {P, weight} of the lane's token for its 4 heads; D - D~
-    uint2 q4[NBW], d4[NBW]; // transposed q / dO, 4 heads per lane
+    u32x4 p0, p1;       // {P, weight} pairs (two KV heads: p0 only, half per lane)
+    f32x4 dl0, dl1;     // D - D~: the wave's heads (two KV heads), else the lane's in dl0
+    u32x4 qx[NQ], dx[NQ];  // transposed q / dO, 4 heads per lane and 16-dim block pair
   };
   // An entry's loads go through buffer resources built per row in scalar
   // registers, with the lane offsets fixed above.  Lanes of units outside
@@ -811,7 +819,8 @@ __global__ __launch_bounds__(256, 2) void bwd_key_mfma_kernel(
   // weight} loads an offset past the resource: those return zero without a
   // memory access, so the A operands of tokens outside the entry are zero
   // with no branch.  Every fetch thus issues the same loads and the waits
-  // before a stage's use cover that stage's loads only.
+  // before a stage's use cover that stage's loads only.  (One-KV-head
+  // layout: lanes whose heads are not a block's KV head never occur.)
   auto fetch = [&](uint32_t k, uint32_t n, Stage& S) {
     const uint2 en = sl[min(k, n - 1u)];
     const uint32_t ex = __builtin_amdgcn_readfirstlane(en.x);
@@ -823,48 +832,84 @@ __global__ __launch_bounds__(256, 2) void bwd_key_mfma_kernel(
     const uint32_t off = ((mask >> u) & 1u)
                              ? (ey + (uint32_t)__popc(mask & ((1u << u) - 1u))) * 512u + pw_lane
                              : 0x80000000u;
-    S.a = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(rp, off, 0, 0));
-    S.b = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(rp, off + 16u, 0, 0));
-    S.dl = *reinterpret_cast<const float4*>(dlt + row * 16 + hb);
+    S.p0 = __builtin_amdgcn_raw_buffer_load_b128(rp, off, 0, 0);
+    if constexpr (FUSE) {
+      typedef const f32x4 __attribute__((address_space(4))) cf32x4;
+      const cf32x4* dp = reinterpret_cast<const cf32x4*>(
+          reinterpret_cast<uintptr_t>(dlt + row * 16 + 8 * gs));
+      S.dl0 = dp[0];
+      S.dl1 = dp[1];
+    } else {
+      S.p1 = __builtin_amdgcn_raw_buffer_load_b128(rp, off + 16u, 0, 0);
+      S.dl0 = *reinterpret_cast<const f32x4*>(dlt + row * 16 + hb);
+    }
     const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint16_t*>(qt + row * (16 * D)), 0, 32 * D, kBufWord3);
     const __amdgpu_buffer_rsrc_t rd = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint16_t*>(dot + row * (16 * D)), 0, 32 * D, kBufWord3);
 #pragma unroll
-    for (int b = 0; b < NBW; b += 2) {
-      const u32x4 qq = __builtin_amdgcn_raw_buffer_load_b128(rq, q_lane[b / 2], 0, 0);
-      const u32x4 dd = __builtin_amdgcn_raw_buffer_load_b128(rd, q_lane[b / 2], 0, 0);
-      S.q4[b] = make_uint2(qq[0], qq[1]);
-      S.q4[b + 1] = make_uint2(qq[2], qq[3]);
-      S.d4[b] = make_uint2(dd[0], dd[1]);
-      S.d4[b + 1] = make_uint2(dd[2], dd[3]);
+    for (int j = 0; j < NQ; ++j) {
+      S.qx[j] = __builtin_amdgcn_raw_buffer_load_b128(rq, q_lane[j], 0, 0);
+      S.dx[j] = __builtin_amdgcn_raw_buffer_load_b128(rd, q_lane[j], 0, 0);
+    }
+  };
+  // lanes 0..31 of the result are x's lanes 0..31 (first) or 32..63 (second),
+  // repeated in lanes 32..63
+  auto halves = [](const u32x4& x, u32x4& lo, u32x4& hi) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const auto r = __builtin_amdgcn_permlane32_swap(x[e], x[e], false, false);
+      lo[e] = r[0];
+      hi[e] = r[1];
     }
   };
   // dS = P (dP - D~) - (D - D~) P and P as bf16 A operands, then the MFMAs
   auto consume = [&](const Stage& S) {
-    const float s0 = fmaf(-S.dl.x, S.a.x, S.a.y), s1 = fmaf(-S.dl.y, S.a.z, S.a.w);
-    const float s2 = fmaf(-S.dl.z, S.b.x, S.b.y), s3 = fmaf(-S.dl.w, S.b.z, S.b.w);
     if constexpr (FUSE) {
+      u32x4 pa, pb;
+      halves(S.p0, pa, pb);
+      const float4 a = __builtin_bit_cast(float4, pa), b = __builtin_bit_cast(float4, pb);
+      const f32x4 dl = (gq & 1) ? S.dl1 : S.dl0;
+      const float s0 = fmaf(-dl[0], a.x, a.y), s1 = fmaf(-dl[1], a.z, a.w);
+      const float s2 = fmaf(-dl[2], b.x, b.y), s3 = fmaf(-dl[3], b.z, b.w);
       const bf16x4s aS = pack4(bf16_hilo2(s0, s1, lo_sel), bf16_hilo2(s2, s3, lo_sel));
-      const bf16x4s aP = pack4(bf16_hilo2(S.a.x, S.a.z, lo_sel), bf16_hilo2(S.b.x, S.b.z, lo_sel));
+      const bf16x4s aP = pack4(bf16_hilo2(a.x, a.z, lo_sel), bf16_hilo2(b.x, b.z, lo_sel));
 #pragma unroll
-      for (int bb = 0; bb < NBW; ++bb) {
-        ak[bb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(
-            aS, __builtin_bit_cast(bf16x4s, S.q4[bb]), ak[bb], 0, 0, 0);
-        av[bb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(
-            aP, __builtin_bit_cast(bf16x4s, S.d4[bb]), av[bb], 0, 0, 0);
+      for (int j = 0; j < NQ; ++j) {
+        u32x4 q01, q23, d01, d23;
+        halves(S.qx[j], q01, q23);
+        halves(S.dx[j], d01, d23);
+        const u32x4 qv[2] = {q01, q23}, dv[2] = {d01, d23};
+#pragma unroll
+        for (int h = 0; h < 4; ++h) {
+          const int bb = 4 * j + h;
+          const uint2 qb = make_uint2(qv[h >> 1][2 * (h & 1)], qv[h >> 1][2 * (h & 1) + 1]);
+          const uint2 db = make_uint2(dv[h >> 1][2 * (h & 1)], dv[h >> 1][2 * (h & 1) + 1]);
+          ak[bb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(
+              aS, __builtin_bit_cast(bf16x4s, qb), ak[bb], 0, 0, 0);
+          av[bb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(
+              aP, __builtin_bit_cast(bf16x4s, db), av[bb], 0, 0, 0);
+        }
       }
     } else {
+      const float4 a = __builtin_bit_cast(float4, S.p0), b = __builtin_bit_cast(float4, S.p1);
+      const f32x4 dl = S.dl0;
+      const float s0 = fmaf(-dl[0], a.x, a.y), s1 = fmaf(-dl[1], a.z, a.w);
+      const float s2 = fmaf(-dl[2], b.x, b.y), s3 = fmaf(-dl[3], b.z, b.w);
       const bf16x4s aSh = pack4(bf16_pk2(s0, s1), bf16_pk2(s2, s3));
       const bf16x4s aSl = pack4(bf16_hilo2(s0, s1, 1.0f), bf16_hilo2(s2, s3, 1.0f));
-      const bf16x4s aPh = pack4(bf16_pk2(S.a.x, S.a.z), bf16_pk2(S.b.x, S.b.z));
-      const bf16x4s aPl = pack4(bf16_hilo2(S.a.x, S.a.z, 1.0f), bf16_hilo2(S.b.x, S.b.z, 1.0f));
+      const bf16x4s aPh = pack4(bf16_pk2(a.x, a.z), bf16_pk2(b.x, b.z));
+      const bf16x4s aPl = pack4(bf16_hilo2(a.x, a.z, 1.0f), bf16_hilo2(b.x, b.z, 1.0f));
 #pragma unroll
       for (int bb = 0; bb < NBW; ++bb) {
         const bool mine = (4 * gq) / G == (16 * (bbase + bb)) / D;
+        const u32x4& qx = S.qx[bb / 2];
+        const u32x4& dx = S.dx[bb / 2];
         const uint2 z = make_uint2(0u, 0u);
-        const bf16x4s bq = __builtin_bit_cast(bf16x4s, mine ? S.q4[bb] : z);
-        const bf16x4s bd = __builtin_bit_cast(bf16x4s, mine ? S.d4[bb] : z);
+        const uint2 qb = make_uint2(qx[2 * (bb & 1)], qx[2 * (bb & 1) + 1]);
+        const uint2 db = make_uint2(dx[2 * (bb & 1)], dx[2 * (bb & 1) + 1]);
+        const bf16x4s bq = __builtin_bit_cast(bf16x4s, mine ? qb : z);
+        const bf16x4s bd = __builtin_bit_cast(bf16x4s, mine ? db : z);
         ak[bb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(aSh, bq, ak[bb], 0, 0, 0);
         ak[bb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(aSl, bq, ak[bb], 0, 0, 0);
         av[bb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(aPh, bd, av[bb], 0, 0, 0);
@@ -873,7 +918,6 @@ __global__ __launch_bounds__(256, 2) void bwd_key_mfma_kernel(
     }
   };
 
-  const uint32_t wv = __builtin_amdgcn_readfirstlane((uint32_t)wave);
   for (uint32_t base = 0; base < nq; base += LCAP) {
     const uint32_t n = min(nq - base, LCAP);
     __syncthreads();  // the previous chunk's entries are read
