@@ -39,6 +39,10 @@ CFLAGS = [
 # would each cost a copy instruction.
 EXTRA = {
     "score.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+    # no NaN reaches the distillation kernels' max and exponent chains (masked
+    # logits are -inf, still honoured): without this each fmaxf of an MFMA
+    # result first quiets its operand, a VALU instruction per score
+    "distill.hip": ["-fno-honor-nans"],
 }
 
 

@@ -208,7 +208,7 @@ __global__ __launch_bounds__(kDT) void distill_teacher_kernel(
 // row): a VALU add with a lane permutation, no LDS traffic
 template <int CTRL>
 __device__ __forceinline__ float dpp_add(float v) {
-  return v + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+  return v + __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, true));
 }
 
 constexpr int kTW = 8;    // waves per teacher workgroup
