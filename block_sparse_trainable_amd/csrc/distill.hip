@@ -314,21 +314,35 @@ __global__ __launch_bounds__(64 * kTW) void distill_teacher_mfma_kernel(
     }
     if constexpr (PASS == 1) {
       if (t0 + 31 <= pmin) {
-        // every token of the tile is visible to every query here: the max
-        // over raw logits (the scale is positive), one FMA per exponent
+        // every token of the tile is visible to every query here.  Each
+        // lane keeps its own (max, sum) over its tokens of the column; the
+        // exponents are taken against the lane's running max as it stands,
+        // and a tile sum above 2^64 (a logit more than 64 above that max, or
+        // the first tile, max = -inf) is redone against the tile's max.  A
+        // max taken from the lane's own logits keeps its largest term >= 1,
+        // so terms lost to underflow are below 2^-126 of the sum, and sums
+        // of terms <= 2^64 stay far from overflow.
 #pragma unroll
         for (int cg = 0; cg < NCG; ++cg) {
-          float mt = fmaxf(fmaxf(fmaxf(sa[cg][0][0], sa[cg][0][1]), fmaxf(sa[cg][0][2], sa[cg][0][3])),
-                           fmaxf(fmaxf(sa[cg][1][0], sa[cg][1][1]), fmaxf(sa[cg][1][2], sa[cg][1][3])));
-          mt = wave_max_xor32(wave_max_xor16(mt));
-          const float mn = fmaxf(m[cg], mt * sl2);
           float ps = 0.0f;
 #pragma unroll
           for (int st = 0; st < 2; ++st)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) ps += exp2_fast(fmaf(sa[cg][st][i], sl2, -mn));
-          l[cg] = l[cg] * exp2_fast(m[cg] - mn) + ps;
-          m[cg] = mn;
+            for (int i = 0; i < 4; ++i) ps += exp2_fast(fmaf(sa[cg][st][i], sl2, -m[cg]));
+          if (!(ps <= 0x1p64f)) {
+            const float mt =
+                fmaxf(fmaxf(fmaxf(sa[cg][0][0], sa[cg][0][1]), fmaxf(sa[cg][0][2], sa[cg][0][3])),
+                      fmaxf(fmaxf(sa[cg][1][0], sa[cg][1][1]), fmaxf(sa[cg][1][2], sa[cg][1][3])));
+            const float mn = fmaxf(m[cg], mt * sl2);   // the scale is positive
+            ps = 0.0f;
+#pragma unroll
+            for (int st = 0; st < 2; ++st)
+#pragma unroll
+              for (int i = 0; i < 4; ++i) ps += exp2_fast(fmaf(sa[cg][st][i], sl2, -mn));
+            l[cg] *= exp2_fast(m[cg] - mn);
+            m[cg] = mn;
+          }
+          l[cg] += ps;
         }
       } else {
         const int32_t tb = (int32_t)t0 + 4 * gq;   // positions < cap < 2^31
@@ -395,11 +409,14 @@ __global__ __launch_bounds__(64 * kTW) void distill_teacher_mfma_kernel(
     __syncthreads();  // every wave is done with this buffer before it is refilled
   }
   if constexpr (PASS == 1) {
+    // the four lanes of a column merge their (max, sum)
 #pragma unroll
     for (int cg = 0; cg < NCG; ++cg) {
-      const float lt = wave_add_xor32(wave_add_xor16(l[cg]));
+      const float M = wave_max_xor32(wave_max_xor16(m[cg]));
+      const float lw = m[cg] == -INFINITY ? 0.0f : l[cg] * exp2_fast(m[cg] - M);
+      const float lt = wave_add_xor32(wave_add_xor16(lw));
       if (gq == 0 && qcol(cg) < n_q)
-        ws.lse[((int64_t)s * n_q + qcol(cg)) * 16 + hcol(cg)] = (m[cg] + log2f(lt)) * kLn2;
+        ws.lse[((int64_t)s * n_q + qcol(cg)) * 16 + hcol(cg)] = (M + log2f(lt)) * kLn2;
     }
   }
 }
