@@ -226,7 +226,7 @@ __global__ __launch_bounds__(64 * kTW) void distill_teacher_mfma_kernel(
   constexpr int NCG = kTCG;            // column groups (= queries) per wave
   constexpr int QT = kTW * NCG;        // query rows per workgroup
   static_assert(NCG % HKV == 0, "a wave's columns must cover every KV head of its queries");
-  __shared__ __attribute__((aligned(16))) unsigned char kbuf[2][32 * ROWB];   // double-buffered
+  __shared__ __attribute__((aligned(16))) unsigned char kbuf[3][32 * ROWB];   // a ring of three
   constexpr int NL = (32 / RPI) / kTW;   // tile loads per lane
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int l16 = lane & 15, gq = lane >> 4;
@@ -280,18 +280,21 @@ __global__ __launch_bounds__(64 * kTW) void distill_teacher_mfma_kernel(
           (__attribute__((address_space(3))) void*)(kbuf[bf] + u * 1024), 16, 0, 0);
     }
   };
+  // Tiles t and t + 32 are in flight when tile t is used.  A wave's loads
+  // return in issue order, so once at most the next tile's NL are pending its
+  // share of this tile has landed; the barrier then makes every wave's share
+  // visible and, since every wave has left the previous tile, frees that
+  // tile's buffer for the tile after next: one barrier per tile.
   load_tile(0, 0);
+  if (32 < tok_end) load_tile(32, 1);
   int bf = 0;
-  for (int64_t t0 = 0; t0 < tok_end; t0 += 32, bf ^= 1) {
-    // the next tile's loads go out first; then wait for this tile's (the
-    // in-order count leaves only the NL loads just issued outstanding)
-    if (t0 + 32 < tok_end) {
-      load_tile(t0 + 32, bf ^ 1);
+  for (int64_t t0 = 0; t0 < tok_end; t0 += 32, bf = bf == 2 ? 0 : bf + 1) {
+    if (t0 + 32 < tok_end)
       __builtin_amdgcn_s_waitcnt(NL | 0x70 | 0xF00);   // vmcnt(NL), expcnt/lgkmcnt any
-    } else {
+    else
       __builtin_amdgcn_s_waitcnt(0);
-    }
     __syncthreads();
+    if (t0 + 64 < tok_end) load_tile(t0 + 64, bf == 0 ? 2 : bf - 1);
     const unsigned char* kt = kbuf[bf];
     // S^T per column group and 16-token half
     f32x4 sa[NCG][2];
@@ -406,7 +409,6 @@ __global__ __launch_bounds__(64 * kTW) void distill_teacher_mfma_kernel(
         }
       }
     }
-    __syncthreads();  // every wave is done with this buffer before it is refilled
   }
   if constexpr (PASS == 1) {
     // the four lanes of a column merge their (max, sum)
