@@ -761,10 +761,14 @@ __global__ __launch_bounds__(256, 2) void bwd_key_mfma_kernel(
   float* sv = sbuf + 16 * KD;
   uint2* sl = reinterpret_cast<uint2*>(sbuf);
   int64_t item;
-  {  // contiguous runs of groups per XCD: neighbouring groups share queries
-    const uint32_t n = gridDim.x, b = blockIdx.x;
-    const uint32_t qn = n / 8u, rn = n % 8u, x = b % 8u;
-    item = (int64_t)(x * qn + min(x, rn) + b / 8u);
+  {  // Newest groups first, the sequences interleaved: the groups at each
+     // sequence's end (its local windows and every query's tail) hold about
+     // twice the entries of the rest, and blocks leave in index order, spread
+     // round-robin over the XCDs, so the longest groups start first and every
+     // XCD gets its share of them.  (The grid is batch * nb blocks.)
+    const uint32_t b = blockIdx.x;
+    const uint32_t batch = gridDim.x / (uint32_t)gx.nb;
+    item = (int64_t)(b % batch) * gx.nb + (gx.nb - 1 - (int64_t)(b / batch));
   }
   const uint32_t nq = gx.cnt[item];
   if (nq == 0u) return;
