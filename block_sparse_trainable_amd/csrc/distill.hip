@@ -242,9 +242,21 @@ __global__ __launch_bounds__(64 * kTW) void distill_teacher_mfma_kernel(
   const int64_t tok_end = PASS == 1 ? pmax + 1 : ((pmax >> lr) << lr);
   if (tok_end <= 0) return;
   // this lane's column in group cg: query qcol(cg), head hcol(cg); rows
-  // past n_q stand in for the last row and write nothing
-  auto qcol = [&](int cg) { return j0 + NCG * wave + (cg / HKV) * QPC + l16 / G; };
-  auto hcol = [&](int cg) { return (cg % HKV) * G + l16 % G; };
+  // past n_q stand in for the last row and write nothing.  Pass 1 with two
+  // KV heads pairs the waves: wave w takes KV head w & 1 for the pair's 4
+  // queries (group cg = queries 2cg, 2cg + 1 x that head's 8 heads), so both
+  // of its groups use the same K fragments (half the LDS reads per score;
+  // the per-head (max, sum) needs nothing from the other head).  Pass 2
+  // sums all 16 heads of a query, so each wave keeps both KV heads there:
+  // group cg = the wave's 2 queries x the 8 heads of KV head cg % HKV.
+  constexpr bool PAIR = HKV == 2 && PASS == 1;
+  static_assert(!PAIR || (NCG == 2 && kTW % 2 == 0), "wave pairs take 4 queries");
+  const int gw = PAIR ? (wave & 1) : 0;   // the wave's KV head when paired
+  auto qcol = [&](int cg) {
+    return PAIR ? j0 + 4 * (wave >> 1) + 2 * cg + (l16 >> 3)
+                : j0 + NCG * wave + (cg / HKV) * QPC + l16 / G;
+  };
+  auto hcol = [&](int cg) { return PAIR ? 8 * gw + (l16 & 7) : (cg % HKV) * G + l16 % G; };
   int32_t pq[NCG];   // positions (cap < 2^31)
   u32x4 qb[NCG][NKD];
   float lse2[NCG];
@@ -304,13 +316,13 @@ __global__ __launch_bounds__(64 * kTW) void distill_teacher_mfma_kernel(
     for (int st = 0; st < 2; ++st) {
       const int tk = 16 * st + l16;
 #pragma unroll
-      for (int g = 0; g < HKV; ++g)
+      for (int g = 0; g < (PAIR ? 1 : HKV); ++g)
 #pragma unroll
         for (int kk = 0; kk < NKD; ++kk) {
-          const int c0 = (g * D + 32 * kk + 8 * gq) / 8;
+          const int c0 = ((PAIR ? gw : g) * D + 32 * kk + 8 * gq) / 8;
           const u32x4 a = *reinterpret_cast<const u32x4*>(kt + tk * ROWB + ((c0 ^ (tk & 15)) * 16));
 #pragma unroll
-          for (int cg = g; cg < NCG; cg += HKV)
+          for (int cg = PAIR ? 0 : g; cg < NCG; cg += PAIR ? 1 : HKV)
             sa[cg][st] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(qb[cg][kk]),
                                                                  sa[cg][st], 0, 0, 0);
         }
