@@ -112,6 +112,7 @@ __global__ __launch_bounds__(256) void attn_generic_kernel(
 }
 
 // ---------------------------------------------------------------- MFMA ----
+constexpr int kSweep = 64;   // prefill walk: rows per sweep (about the workgroups resident per XCD)
 template <int HKV, int D, bool TOK>
 __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kc,
@@ -171,8 +172,16 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(
                    : (int32_t)((c << lm) + (i - nsel));
     load_qbd<HKV, D>(q, row, qb);
     __syncthreads();
+    // One split per row (prefill): the workgroups resident on an XCD (about
+    // kSweep, on runs of consecutive rows) start at staggered times, so each
+    // starts its walk a fraction (p mod kSweep) / kSweep into its list and
+    // wraps.  Rows in flight together are then at the same fraction of
+    // their lists, where neighbouring rows' shared blocks sit, and read them
+    // while they are in that XCD's L2.  The position alone fixes the order,
+    // so a query gives the same bits in any call.
+    const int rot = n_split == 1 ? (int)((p % kSweep) * npb / kSweep) : 0;
     attn_mfma_tiles<HKV, D, false>(qb, kc, vc, cap, s, p, row, item, pb_lo, pb_hi, sbid,
-                                   scale_log2, out, lse, part, n_split, lds);
+                                   scale_log2, out, lse, part, n_split, lds, 0, rot);
   }
 }
 

@@ -119,7 +119,7 @@ __device__ __forceinline__ void attn_mfma_tiles(
     const uint16_t* __restrict__ vc, int64_t cap, int s, int64_t p, int64_t row, int64_t item,
     int pb_lo, int pb_hi, const int32_t* sbid, float scale_log2, uint16_t* __restrict__ out,
     float* __restrict__ lse, float* __restrict__ part, int n_split, unsigned char* lds,
-    int t_hi = 0) {
+    int t_hi = 0, int rot = 0) {
   using S = MfmaShape<HKV, D>;
   constexpr int KD = S::KD, NK = S::NK, ROWB = S::ROWB, G = S::G, CH = S::CH, RPI = S::RPI;
   constexpr int MF = S::MERGE_FLOATS;
@@ -131,8 +131,16 @@ __device__ __forceinline__ void attn_mfma_tiles(
   const int gq = lane >> 4;
   const uint16_t* kbase = kc + (int64_t)s * cap * KD;
   const uint16_t* vbase = vc + (int64_t)s * cap * KD;
-  // block id of pseudo-block pb, -1 outside this work item
-  auto bid = [&](int pb) -> int64_t { return (pb < pb_hi) ? (int64_t)sbid[pb - pb_lo] : -1; };
+  // block id of pseudo-block pb, -1 outside this work item; the walk may
+  // start rot entries into the list and wrap (the softmax sums do not
+  // depend on the order)
+  const int nlist = pb_hi - pb_lo;
+  auto bid = [&](int pb) -> int64_t {
+    if (pb >= pb_hi) return -1;
+    int i = pb - pb_lo + rot;
+    i -= i >= nlist ? nlist : 0;
+    return (int64_t)sbid[i];
+  };
   // token mode: position of list slot sl, -1 past the list
   auto tok = [&](int sl) -> int64_t { return (sl < t_hi) ? (int64_t)sbid[sl - 4 * pb_lo] : -1; };
 
