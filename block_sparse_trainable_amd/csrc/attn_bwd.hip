@@ -39,6 +39,7 @@ namespace {
 constexpr int kBwdMaxTokens = 2048 + 128;   // r * k_B <= 2048 selected, tail <= r
 constexpr int kNT = 256;
 constexpr int kKeySplit = 2;   // key side: dim groups of waves (1, 2 or 4)
+constexpr int kBwdSweep = 64;  // query side: rows per sweep of the walk's start
 
 template <bool BF16>
 __device__ __forceinline__ float ldx(const void* p, int64_t i) {
@@ -287,7 +288,15 @@ __global__ __launch_bounds__(256, 2) void bwd_query_mfma_kernel(
   float dacc = 0.0f;
   unsigned char* kt = lds + wave * TILE;
 
-  for (int pb0 = (TT / 4) * wave; pb0 < npb; pb0 += TT) {
+  // Tiles of TT / 4 list entries, wave w taking tiles w, w + 4, ...  As in
+  // the forward, the walk starts (p mod kBwdSweep) / kBwdSweep of the way
+  // into the list and wraps, so the rows resident on an XCD read shared
+  // blocks together; a tile keeps its list index (pb0), which places its
+  // {P, weight} export, and the sums do not depend on the order.
+  const int ntile = (npb + TT / 4 - 1) / (TT / 4);
+  const int trot = (int)((p % kBwdSweep) * ntile / kBwdSweep);
+  for (int t = wave; t < ntile; t += 4) {
+    const int pb0 = (TT / 4) * (t + trot < ntile ? t + trot : t + trot - ntile);
     // ---- V rows into A-operand registers
     u32x4 vreg[NST][NK];
 #pragma unroll
