@@ -538,26 +538,28 @@ __global__ __launch_bounds__(kDT) void distill_student_kernel(
 // with W as bf16 hi + lo.  dI and the mask bytes go to the workspace for the key
 // side; q_idx is also written transposed (qT) for it.
 __device__ __forceinline__ float quad_xor1(float v) {
-  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false));
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, true));
 }
 __device__ __forceinline__ float quad_xor2(float v) {
-  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false));
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, true));
 }
 __device__ __forceinline__ float quad_first(float v) {
-  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x00, 0xF, 0xF, false));
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x00, 0xF, 0xF, true));
 }
 
 typedef short bf16x4d __attribute__((ext_vector_type(4)));
 
+typedef __bf16 bf16x2p __attribute__((ext_vector_type(2)));
+typedef float f32x2p __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pk_bf16(float x, float y) {   // nearest-even, one instruction
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2p{x, y}, bf16x2p));
+}
 __device__ __forceinline__ void split4(const float (&w)[4], bf16x4d& hi, bf16x4d& lo) {
-  uint32_t h[4], l[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    h[i] = f32_to_bf16(w[i]);
-    l[i] = f32_to_bf16(w[i] - bf16_to_f32(h[i]));
-  }
-  hi = __builtin_bit_cast(bf16x4d, make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16)));
-  lo = __builtin_bit_cast(bf16x4d, make_uint2(l[0] | (l[1] << 16), l[2] | (l[3] << 16)));
+  const uint32_t h0 = pk_bf16(w[0], w[1]), h1 = pk_bf16(w[2], w[3]);
+  const uint32_t l0 = pk_bf16(w[0] - __uint_as_float(h0 << 16), w[1] - __uint_as_float(h0 & 0xFFFF0000u));
+  const uint32_t l1 = pk_bf16(w[2] - __uint_as_float(h1 << 16), w[3] - __uint_as_float(h1 & 0xFFFF0000u));
+  hi = __builtin_bit_cast(bf16x4d, make_uint2(h0, h1));
+  lo = __builtin_bit_cast(bf16x4d, make_uint2(l0, l1));
 }
 
 __global__ __launch_bounds__(256) void distill_kt_kernel(const uint16_t* __restrict__ k_cmp,
@@ -777,10 +779,10 @@ __global__ __launch_bounds__(kSNT) void distill_student_mfma_kernel(
       }
       // this lane's head over the quad's four blocks: W = dI [dot > 0]
       const float dIq[4] = {
-          __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(dI), 0x00, 0xF, 0xF, false)),
-          __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(dI), 0x55, 0xF, 0xF, false)),
-          __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(dI), 0xAA, 0xF, 0xF, false)),
-          __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(dI), 0xFF, 0xF, 0xF, false))};
+          __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(dI), 0x00, 0xF, 0xF, true)),
+          __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(dI), 0x55, 0xF, 0xF, true)),
+          __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(dI), 0xAA, 0xF, 0xF, true)),
+          __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(dI), 0xFF, 0xF, 0xF, true))};
       float w[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) w[i] = acc[i] > 0.0f ? dIq[i] : 0.0f;
