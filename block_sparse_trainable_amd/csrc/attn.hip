@@ -119,21 +119,25 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(
     const uint16_t* __restrict__ vc, int64_t cap, int n_q, const int32_t* __restrict__ q_pos0,
     const int32_t* __restrict__ sel, const int32_t* __restrict__ cnt, int kB, float scale_log2,
     uint16_t* __restrict__ out, float* __restrict__ lse, float* __restrict__ part,
-    int n_split, int pb_per_split, int lr) {
+    int n_split, int pb_per_split, int lr, const int32_t* __restrict__ order) {
   using S = MfmaShape<HKV, D>;
   __shared__ __attribute__((aligned(16))) unsigned char lds[S::LDS_BYTES];
   __shared__ int32_t sbid[TOK ? kMaxTok : kMaxPB];
   // Workgroups are handed to the 8 XCDs in turn (workgroup b to XCD b % 8):
-  // give each XCD one contiguous run of items, so that neighbouring queries,
-  // whose selections overlap, share an L2.  A bijection for any grid size.
+  // give each XCD one contiguous run of items, so that the queries it holds
+  // at once, whose selections overlap, share an L2.  A bijection for any
+  // grid size.
   int64_t item;
   {
     const uint32_t n = gridDim.x, b = blockIdx.x;
     const uint32_t q = n / 8u, r = n % 8u, x = b % 8u;
     item = (int64_t)(x * q + min(x, r) + b / 8u);
   }
-  const int64_t row = item / n_split;
+  int64_t row = item / n_split;
   const int split = (int)(item % n_split);
+  // prefill with a row order (one split per row): item i attends row
+  // order[i], so rows that read the same region of the cache run together
+  if (order) row = min(max((int64_t)order[item], (int64_t)0), (int64_t)gridDim.x - 1);
   const int s = (int)(row / n_q);
   const int j = (int)(row % n_q);
   const int64_t p = min(max((int64_t)q_pos0[s] + j, (int64_t)0), cap - 1);
@@ -210,6 +214,136 @@ __global__ __launch_bounds__(D) void attn_merge_kernel(const float* __restrict__
 }
 
 
+// ---------------------------------------------------------- row order ----
+// Prefill rows are independent, so the order in which the attention runs
+// them is free; what the L2 of an XCD can catch depends on it.  Where a
+// query's selected blocks cluster in one region of the cache, rows are
+// grouped by that region: the rows of a group then run together on one XCD
+// and read the region's K/V rows while they are in its L2.  A region is
+// 1,024 tokens (1 MB of K and V at 2 x 128 bf16 dims, a quarter of an XCD's
+// L2), binned modulo kOrderBins per row.  A row counts as clustered when its
+// most frequent region holds at least 1/8 of its selected blocks and at
+// least 4 times the share an even spread over its candidates would give it;
+// the other rows keep their natural order, after the clustered ones, where
+// neighbouring positions share their candidate ranges.  The order changes
+// no result: every row computes the same bits wherever it runs.
+constexpr int kOrderRegionShift = 10;  // log2 tokens per region
+constexpr int kOrderBins = 1024;       // region bins of one row's histogram
+constexpr int kOrderKeys = 8192;       // sort keys: batch x bins per sequence
+constexpr int kOrderMinRows = 1024;    // fewer rows do not fill the XCDs twice
+
+int order_bins_per_seq(int batch) {
+  return kOrderKeys / batch < kOrderBins ? kOrderKeys / batch : kOrderBins;
+}
+
+// One wave per row: key[row] = s * nb + (the row's most frequent region bin
+// mod nb, the lower bin on ties) for a clustered row, -1 otherwise.
+__global__ __launch_bounds__(256) void attn_order_key_kernel(
+    const int32_t* __restrict__ sel, const int32_t* __restrict__ cnt,
+    const int32_t* __restrict__ q_pos0, int n_q, int rows, int64_t cap, int kB, int lr, int nb,
+    int32_t* __restrict__ key) {
+  __shared__ uint32_t h[4][kOrderBins];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int row = blockIdx.x * 4 + wave;
+  const bool live = row < rows;
+  for (int i = lane; i < kOrderBins; i += 64) h[wave][i] = 0u;
+  __syncthreads();
+  int s = 0, count = 0;
+  int64_t c = 0;
+  if (live) {
+    s = row / n_q;
+    const int64_t p = min(max((int64_t)q_pos0[s] + row % n_q, (int64_t)0), cap - 1);
+    c = p >> lr;
+    count = (int)min((int64_t)max(cnt[row], 0), min((int64_t)kB, c));
+    const int32_t* srow = sel + (int64_t)row * kB;
+    for (int i = lane; i < count; i += 64) {
+      const int64_t b = min(max((int64_t)srow[i], (int64_t)0), c - 1);
+      atomicAdd(&h[wave][((b << lr) >> kOrderRegionShift) & (kOrderBins - 1)], 1u);
+    }
+  }
+  __syncthreads();
+  // (count << 16) | (0xFFFF - bin): the largest is the most frequent bin,
+  // the lower one on ties (counts stay below 2^16)
+  uint32_t best = 0u;
+  for (int i = lane; i < kOrderBins; i += 64)
+    best = max(best, (h[wave][i] << 16) | (uint32_t)(0xFFFF - i));
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) best = max(best, (uint32_t)__shfl_xor((int)best, off));
+  if (live && lane == 0) {
+    const int64_t top = best >> 16;
+    const int bin = (int)(0xFFFF - (best & 0xFFFFu));
+    // top / count >= 1/8 and >= 4 * (region blocks) / c
+    const int64_t region_blocks = (int64_t)1 << (kOrderRegionShift > lr ? kOrderRegionShift - lr : 0);
+    const bool clustered = count > 0 && 8 * top >= count && top * c >= 4 * region_blocks * count;
+    key[row] = clustered ? s * nb + bin % nb : -1;
+  }
+}
+
+// One workgroup: order[] becomes a permutation of 0 .. rows-1 -- the
+// clustered rows by key (keys < nkeys <= kOrderKeys; rows of one key in any
+// order among themselves), then the others in their natural order.
+__global__ __launch_bounds__(1024) void attn_order_sort_kernel(const int32_t* __restrict__ key,
+                                                               int rows, int nkeys,
+                                                               int32_t* __restrict__ order) {
+  __shared__ uint32_t h[kOrderKeys];
+  __shared__ uint32_t part[1024 / 64];
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  for (int i = t; i < kOrderKeys; i += 1024) h[i] = 0u;
+  __syncthreads();
+  for (int r = t; r < rows; r += 1024) {
+    const int k = key[r];
+    if (k >= 0) atomicAdd(&h[min(k, nkeys - 1)], 1u);
+  }
+  __syncthreads();
+  // exclusive scan: thread t owns keys 8t .. 8t+7
+  constexpr int PER = kOrderKeys / 1024;
+  uint32_t v[PER], sum = 0u;
+#pragma unroll
+  for (int k = 0; k < PER; ++k) { v[k] = h[PER * t + k]; sum += v[k]; }
+  uint32_t inc = sum;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const uint32_t o = (uint32_t)__shfl_up((int)inc, off);
+    if (lane >= off) inc += o;
+  }
+  if (lane == 63) part[wave] = inc;
+  __syncthreads();
+  uint32_t base = 0u, clustered = 0u;
+  for (int w = 0; w < 1024 / 64; ++w) {
+    base += w < wave ? part[w] : 0u;
+    clustered += part[w];
+  }
+  uint32_t run = base + inc - sum;
+#pragma unroll
+  for (int k = 0; k < PER; ++k) { h[PER * t + k] = run; run += v[k]; }
+  __syncthreads();
+  for (int r = t; r < rows; r += 1024) {
+    const int k = key[r];
+    if (k >= 0) {
+      const uint32_t pos = atomicAdd(&h[min(k, nkeys - 1)], 1u);
+      if (pos < (uint32_t)rows) order[pos] = r;
+    }
+  }
+  // the other rows, in order: 1,024 per round, ranked by ballots
+  uint32_t done = clustered;
+  for (int r0 = 0; r0 < rows; r0 += 1024) {
+    const int r = r0 + t;
+    const bool other = r < rows && key[r] < 0;
+    const uint64_t m = __ballot(other);
+    __syncthreads();  // the previous round's part[] reads are over
+    if (lane == 0) part[wave] = (uint32_t)__popcll(m);
+    __syncthreads();
+    uint32_t before = 0u, total = 0u;
+    for (int w = 0; w < 1024 / 64; ++w) {
+      before += w < wave ? part[w] : 0u;
+      total += part[w];
+    }
+    const uint32_t pos = done + before + (uint32_t)__popcll(m & ((1ull << lane) - 1ull));
+    if (other && pos < (uint32_t)rows) order[pos] = r;
+    done += total;
+  }
+}
+
 bool use_mfma(const Dims& d) {
   return d.bf16 && d.q_heads == 16 &&
          ((d.kv_heads == 2 && (d.head_dim == 64 || d.head_dim == 128)) ||
@@ -224,27 +358,52 @@ int max_pseudo_blocks(const Dims& d) {
 
 int decode_splits(const Dims&) { return kDecodeSplits; }
 
+// Prefill calls on the MFMA path with enough rows order them (batch <=
+// 1024 leaves at least 8 region bins per sequence).
+bool use_order(const Dims& d, int batch, int rows, bool decode) {
+  return !decode && rows >= kOrderMinRows && batch <= kOrderKeys / 8 && use_mfma(d);
+}
+
+// Workspace of a prefill call that orders its rows: key [rows], order [rows].
+size_t order_bytes(int rows) { return 2 * sizeof(int32_t) * (size_t)rows; }
+
 template <int HKV, int D>
-hipError_t launch_mfma(const Dims& d, int rows, int n_q, const void* q, const void* kc,
+hipError_t launch_mfma(const Dims& d, int batch, int n_q, const void* q, const void* kc,
                        const void* vc, int64_t cap, const int32_t* q_pos0, const int32_t* sel,
                        const int32_t* cnt, void* out, float* lse, void* ws, bool decode,
                        hipStream_t st) {
+  const int rows = batch * n_q;
   const float sl2 = d.scale * kLog2e;
   const int ns = decode ? decode_splits(d) : 1;
   float* part = decode ? static_cast<float*>(ws) : nullptr;
+  const int32_t* order = nullptr;
+  if (use_order(d, batch, rows, decode)) {
+    int32_t* key = static_cast<int32_t*>(ws);
+    int32_t* ord = key + rows;
+    const int nb = order_bins_per_seq(batch);
+    hipLaunchKernelGGL(attn_order_key_kernel, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, st,
+                       sel, cnt, q_pos0, n_q, rows, cap, d.kB, d.lr, nb, key);
+    hipLaunchKernelGGL(attn_order_sort_kernel, dim3(1), dim3(1024), 0, st, key, rows, batch * nb,
+                       ord);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    order = ord;
+  }
   const dim3 grid((unsigned)(rows * ns));
   if (d.lr < 2)
     hipLaunchKernelGGL((attn_mfma_kernel<HKV, D, true>), grid, dim3(256), 0, st,
                        static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(kc),
                        static_cast<const uint16_t*>(vc), cap, n_q, q_pos0, sel, cnt, d.kB, sl2,
                        static_cast<uint16_t*>(out), lse, part, ns,
-                       decode ? decode_pb_per_split(max_pseudo_blocks(d)) : max_pseudo_blocks(d), d.lr);
+                       decode ? decode_pb_per_split(max_pseudo_blocks(d)) : max_pseudo_blocks(d), d.lr,
+                       order);
   else
     hipLaunchKernelGGL((attn_mfma_kernel<HKV, D, false>), grid, dim3(256), 0, st,
                        static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(kc),
                        static_cast<const uint16_t*>(vc), cap, n_q, q_pos0, sel, cnt, d.kB, sl2,
                        static_cast<uint16_t*>(out), lse, part, ns,
-                       decode ? decode_pb_per_split(max_pseudo_blocks(d)) : max_pseudo_blocks(d), d.lr);
+                       decode ? decode_pb_per_split(max_pseudo_blocks(d)) : max_pseudo_blocks(d), d.lr,
+                       order);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || !decode) return e;
   hipLaunchKernelGGL((attn_merge_kernel<D>), dim3((unsigned)(rows * 16)), dim3(D), 0, st, part,
@@ -254,7 +413,9 @@ hipError_t launch_mfma(const Dims& d, int rows, int n_q, const void* q, const vo
 
 }  // namespace
 
-size_t attn_workspace_bytes(const Dims& d, int rows, bool decode) {
+size_t attn_workspace_bytes(const Dims& d, int batch, int n_q, bool decode) {
+  const int rows = batch * n_q;
+  if (use_order(d, batch, rows, decode)) return order_bytes(rows);
   if (!decode || !use_mfma(d)) return 0;
   return sizeof(float) * (size_t)rows * decode_splits(d) * part_floats(d.head_dim);
 }
@@ -267,7 +428,7 @@ hipError_t launch_attn(const Dims& d, int batch, int n_q, const void* q, const v
   if (use_mfma(d)) {
 #define QSA_MFMA(HKV, DD)                                                                     \
   if (d.kv_heads == HKV && d.head_dim == DD)                                                 \
-    return launch_mfma<HKV, DD>(d, rows, n_q, q, k_cache, v_cache, cap, q_pos0, sel, cnt, out, \
+    return launch_mfma<HKV, DD>(d, batch, n_q, q, k_cache, v_cache, cap, q_pos0, sel, cnt, out, \
                                 lse, workspace, decode, st);
     QSA_MFMA(2, 128)
     QSA_MFMA(1, 128)

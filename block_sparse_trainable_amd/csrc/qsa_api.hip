@@ -194,8 +194,8 @@ qsa_status qsa_workspace_size(const qsa_config* cfg, int32_t op, int32_t batch, 
   switch (op) {
     case QSA_OP_INDEX_BUILD: *bytes = 0; break;
     case QSA_OP_SELECT: *bytes = select_ws(d, batch, n_q, max_pos_end); break;
-    case QSA_OP_PREFILL: *bytes = qsa::attn_workspace_bytes(d, batch * n_q, false); break;
-    case QSA_OP_DECODE: *bytes = qsa::attn_workspace_bytes(d, batch, true); break;
+    case QSA_OP_PREFILL: *bytes = qsa::attn_workspace_bytes(d, batch, n_q, false); break;
+    case QSA_OP_DECODE: *bytes = qsa::attn_workspace_bytes(d, batch, 1, true); break;
     case QSA_OP_DECODE_STEP: *bytes = qsa::step_plan(d, batch, max_pos_end).bytes; break;
     case QSA_OP_BACKWARD: *bytes = qsa::bwd_workspace_bytes(d, batch, n_q, max_pos_end); break;
     case QSA_OP_DISTILL: *bytes = qsa::distill_workspace_bytes(d, batch, n_q, max_pos_end); break;
@@ -310,7 +310,7 @@ static qsa_status attn_common(const char* fn, const qsa_config* cfg, int32_t bat
   QSA_REQUIRE_PTR(out, 4);
   if (lse && !aligned(lse, 4))
     return fail(QSA_ERR_INVALID_ARGUMENT, "%s: lse must be 4-byte aligned", fn);
-  const size_t need = qsa::attn_workspace_bytes(d, batch * n_q, decode);
+  const size_t need = qsa::attn_workspace_bytes(d, batch, n_q, decode);
   if (need > 0) {
     if (!workspace || workspace_bytes < need)
       return fail(QSA_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn, need,

@@ -254,8 +254,9 @@ hipError_t launch_decode_step(const Dims& d, const StepPlan& pl, int batch, cons
                               float* sel_scores, void* out, float* lse, void* workspace,
                               hipStream_t st);
 
-// Decode attention workspace: the per-split partial states.
-size_t attn_workspace_bytes(const Dims& d, int rows, bool decode);
+// Attention workspace: the decode splits' partial states, or the prefill
+// row order (MFMA path, 1,024 rows or more).
+size_t attn_workspace_bytes(const Dims& d, int batch, int n_q, bool decode);
 
 // Attention backward: transposed index (per-block query lists) and per-head D.
 hipError_t launch_offload_stage(const Dims& d, int batch, const int32_t* q_pos,

@@ -208,6 +208,28 @@ def test_chunked_equals_monolithic_bitwise():
     assert torch.equal(dl.k_cmp, dl2.k_cmp)
 
 
+def test_row_order_changes_no_bit():
+    say("prefill attention: one call over 2 x 3,000 rows (rows run in region order) == "
+        "the same rows in calls of 1,000 rows (natural order)")
+    x = synth.chunked(cache=20000, chunk=3000, batch=2, window=2048, n_far=6)
+    dl = DeviceLayer(x)
+    dl.build_prefix(x.cache_len)
+    outs = dl.alloc_prefill_outputs()
+    outs[3].fill_(float("nan"))   # a row the ordered call skipped stays NaN
+    outs[4].fill_(float("nan"))
+    sel, cnt, _, out, lse = dl.prefill_chunk(outs)
+    end = int(x.q_pos0.max()) + x.n_q
+    for j0 in range(0, x.n_q, 500):   # 2 x 500 rows per call: no reordering
+        n = min(500, x.n_q - j0)
+        o2 = torch.full_like(out[:, j0:j0 + n], float("nan")).contiguous()
+        l2 = torch.full_like(lse[:, j0:j0 + n], float("nan")).contiguous()
+        dl.attend_prefill(dl.q[:, j0:j0 + n].contiguous(), dl.i32(x.q_pos0 + j0), end,
+                          sel[:, j0:j0 + n].contiguous(), cnt[:, j0:j0 + n].contiguous(), o2, l2)
+        torch.cuda.synchronize()
+        assert torch.equal(out[:, j0:j0 + n], o2), f"rows {j0}..{j0 + n}: output differs"
+        assert torch.equal(lse[:, j0:j0 + n], l2), f"rows {j0}..{j0 + n}: lse differs"
+
+
 def test_prefill_deterministic():
     say("determinism")
     x = synth.prefill(n=2100)
