@@ -119,7 +119,8 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(
     const uint16_t* __restrict__ vc, int64_t cap, int n_q, const int32_t* __restrict__ q_pos0,
     const int32_t* __restrict__ sel, const int32_t* __restrict__ cnt, int kB, float scale_log2,
     uint16_t* __restrict__ out, float* __restrict__ lse, float* __restrict__ part,
-    int n_split, int pb_per_split, int lr, const int32_t* __restrict__ order) {
+    int n_split, int pb_per_split, int lr, const int32_t* __restrict__ order,
+    const int32_t* __restrict__ first) {
   using S = MfmaShape<HKV, D>;
   __shared__ __attribute__((aligned(16))) unsigned char lds[S::LDS_BYTES];
   __shared__ int32_t sbid[TOK ? kMaxTok : kMaxPB];
@@ -176,14 +177,21 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(
                    : (int32_t)((c << lm) + (i - nsel));
     load_qbd<HKV, D>(q, row, qb);
     __syncthreads();
-    // One split per row (prefill): the workgroups resident on an XCD (about
-    // kSweep, on runs of consecutive rows) start at staggered times, so each
-    // starts its walk a fraction (p mod kSweep) / kSweep into its list and
-    // wraps.  Rows in flight together are then at the same fraction of
-    // their lists, where neighbouring rows' shared blocks sit, and read them
-    // while they are in that XCD's L2.  The position alone fixes the order,
-    // so a query gives the same bits in any call.
-    const int rot = n_split == 1 ? (int)((p % kSweep) * npb / kSweep) : 0;
+    // One split per row (prefill): the walk starts rot entries into the
+    // list and wraps.  A row whose selection clusters in one region starts
+    // at that region's first block: it runs among rows of the same region
+    // (see the row order below), which read the region while it is in
+    // their XCD's L2.  Any other row runs among its neighbours in position,
+    // which start at staggered times, so it starts a fraction
+    // (p mod kSweep) / kSweep into its list: rows in flight together are
+    // then at the same fraction of their lists, where neighbouring rows'
+    // shared blocks sit.  The row's own selection and position fix the
+    // start, so a query gives the same bits in any call.
+    int rot = n_split == 1 ? (int)((p % kSweep) * npb / kSweep) : 0;
+    if (first) {
+      const int f = first[row];
+      if (f >= 0) rot = min(f << lm, npb - 1);
+    }
     attn_mfma_tiles<HKV, D, false>(qb, kc, vc, cap, s, p, row, item, pb_lo, pb_hi, sbid,
                                    scale_log2, out, lse, part, n_split, lds, 0, rot);
   }
@@ -233,15 +241,17 @@ constexpr int kOrderKeys = 8192;       // sort keys: batch x bins per sequence
 constexpr int kOrderMinRows = 1024;    // fewer rows do not fill the XCDs twice
 
 int order_bins_per_seq(int batch) {
-  return kOrderKeys / batch < kOrderBins ? kOrderKeys / batch : kOrderBins;
+  const int nb = kOrderKeys / batch < kOrderBins ? kOrderKeys / batch : kOrderBins;
+  return nb > 0 ? nb : 1;
 }
 
 // One wave per row: key[row] = s * nb + (the row's most frequent region bin
-// mod nb, the lower bin on ties) for a clustered row, -1 otherwise.
+// mod nb, the lower bin on ties) and first[row] = the index of its first
+// selected block in that bin for a clustered row; -1 and -1 otherwise.
 __global__ __launch_bounds__(256) void attn_order_key_kernel(
     const int32_t* __restrict__ sel, const int32_t* __restrict__ cnt,
     const int32_t* __restrict__ q_pos0, int n_q, int rows, int64_t cap, int kB, int lr, int nb,
-    int32_t* __restrict__ key) {
+    int32_t* __restrict__ key, int32_t* __restrict__ first) {
   __shared__ uint32_t h[4][kOrderBins];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int row = blockIdx.x * 4 + wave;
@@ -250,12 +260,12 @@ __global__ __launch_bounds__(256) void attn_order_key_kernel(
   __syncthreads();
   int s = 0, count = 0;
   int64_t c = 0;
+  const int32_t* srow = sel + (int64_t)(live ? row : 0) * kB;
   if (live) {
     s = row / n_q;
     const int64_t p = min(max((int64_t)q_pos0[s] + row % n_q, (int64_t)0), cap - 1);
     c = p >> lr;
     count = (int)min((int64_t)max(cnt[row], 0), min((int64_t)kB, c));
-    const int32_t* srow = sel + (int64_t)row * kB;
     for (int i = lane; i < count; i += 64) {
       const int64_t b = min(max((int64_t)srow[i], (int64_t)0), c - 1);
       atomicAdd(&h[wave][((b << lr) >> kOrderRegionShift) & (kOrderBins - 1)], 1u);
@@ -269,13 +279,22 @@ __global__ __launch_bounds__(256) void attn_order_key_kernel(
     best = max(best, (h[wave][i] << 16) | (uint32_t)(0xFFFF - i));
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) best = max(best, (uint32_t)__shfl_xor((int)best, off));
+  const int64_t top = best >> 16;
+  const int bin = (int)(0xFFFF - (best & 0xFFFFu));
+  // top / count >= 1/8 and >= 4 * (region blocks) / c
+  const int64_t region_blocks = (int64_t)1 << (kOrderRegionShift - lr);
+  const bool clustered = count > 0 && 8 * top >= count && top * c >= 4 * region_blocks * count;
+  // the first list entry in the top bin
+  int f = 0x7FFFFFFF;
+  for (int i = lane; i < count; i += 64) {
+    const int64_t b = min(max((int64_t)srow[i], (int64_t)0), c - 1);
+    if ((int)(((b << lr) >> kOrderRegionShift) & (kOrderBins - 1)) == bin) f = min(f, i);
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) f = min(f, __shfl_xor(f, off));
   if (live && lane == 0) {
-    const int64_t top = best >> 16;
-    const int bin = (int)(0xFFFF - (best & 0xFFFFu));
-    // top / count >= 1/8 and >= 4 * (region blocks) / c
-    const int64_t region_blocks = (int64_t)1 << (kOrderRegionShift > lr ? kOrderRegionShift - lr : 0);
-    const bool clustered = count > 0 && 8 * top >= count && top * c >= 4 * region_blocks * count;
     key[row] = clustered ? s * nb + bin % nb : -1;
+    first[row] = clustered && f < count ? f : -1;
   }
 }
 
@@ -364,8 +383,11 @@ bool use_order(const Dims& d, int batch, int rows, bool decode) {
   return !decode && rows >= kOrderMinRows && batch <= kOrderKeys / 8 && use_mfma(d);
 }
 
-// Workspace of a prefill call that orders its rows: key [rows], order [rows].
-size_t order_bytes(int rows) { return 2 * sizeof(int32_t) * (size_t)rows; }
+// Workspace of a prefill call on the MFMA path: key [rows], first [rows],
+// and order [rows] when it orders its rows.
+size_t order_bytes(int rows, bool sorted) {
+  return (sorted ? 3 : 2) * sizeof(int32_t) * (size_t)rows;
+}
 
 template <int HKV, int D>
 hipError_t launch_mfma(const Dims& d, int batch, int n_q, const void* q, const void* kc,
@@ -377,17 +399,20 @@ hipError_t launch_mfma(const Dims& d, int batch, int n_q, const void* q, const v
   const int ns = decode ? decode_splits(d) : 1;
   float* part = decode ? static_cast<float*>(ws) : nullptr;
   const int32_t* order = nullptr;
-  if (use_order(d, batch, rows, decode)) {
+  const int32_t* first = nullptr;
+  if (!decode) {
     int32_t* key = static_cast<int32_t*>(ws);
-    int32_t* ord = key + rows;
+    int32_t* fst = key + rows;
     const int nb = order_bins_per_seq(batch);
     hipLaunchKernelGGL(attn_order_key_kernel, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, st,
-                       sel, cnt, q_pos0, n_q, rows, cap, d.kB, d.lr, nb, key);
-    hipLaunchKernelGGL(attn_order_sort_kernel, dim3(1), dim3(1024), 0, st, key, rows, batch * nb,
-                       ord);
+                       sel, cnt, q_pos0, n_q, rows, cap, d.kB, d.lr, nb, key, fst);
+    if (use_order(d, batch, rows, decode))
+      hipLaunchKernelGGL(attn_order_sort_kernel, dim3(1), dim3(1024), 0, st, key, rows,
+                         batch * nb, fst + rows);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    order = ord;
+    first = fst;
+    if (use_order(d, batch, rows, decode)) order = fst + rows;
   }
   const dim3 grid((unsigned)(rows * ns));
   if (d.lr < 2)
@@ -396,14 +421,14 @@ hipError_t launch_mfma(const Dims& d, int batch, int n_q, const void* q, const v
                        static_cast<const uint16_t*>(vc), cap, n_q, q_pos0, sel, cnt, d.kB, sl2,
                        static_cast<uint16_t*>(out), lse, part, ns,
                        decode ? decode_pb_per_split(max_pseudo_blocks(d)) : max_pseudo_blocks(d), d.lr,
-                       order);
+                       order, first);
   else
     hipLaunchKernelGGL((attn_mfma_kernel<HKV, D, false>), grid, dim3(256), 0, st,
                        static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(kc),
                        static_cast<const uint16_t*>(vc), cap, n_q, q_pos0, sel, cnt, d.kB, sl2,
                        static_cast<uint16_t*>(out), lse, part, ns,
                        decode ? decode_pb_per_split(max_pseudo_blocks(d)) : max_pseudo_blocks(d), d.lr,
-                       order);
+                       order, first);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || !decode) return e;
   hipLaunchKernelGGL((attn_merge_kernel<D>), dim3((unsigned)(rows * 16)), dim3(D), 0, st, part,
@@ -415,8 +440,8 @@ hipError_t launch_mfma(const Dims& d, int batch, int n_q, const void* q, const v
 
 size_t attn_workspace_bytes(const Dims& d, int batch, int n_q, bool decode) {
   const int rows = batch * n_q;
-  if (use_order(d, batch, rows, decode)) return order_bytes(rows);
-  if (!decode || !use_mfma(d)) return 0;
+  if (!use_mfma(d)) return 0;
+  if (!decode) return order_bytes(rows, use_order(d, batch, rows, decode));
   return sizeof(float) * (size_t)rows * decode_splits(d) * part_floats(d.head_dim);
 }
 

@@ -171,13 +171,14 @@ qsa_status qsa_select_topk(const qsa_config* cfg, int32_t batch, int32_t n_q,
  *              unordered list of distinct complete blocks b < floor(p/r)).
  *   out        (dtype) [batch][n_q][q_heads][head_dim].
  *   lse        float [batch][n_q][q_heads] natural-log normaliser, or NULL.
- *   workspace  >= qsa_workspace_size(QSA_OP_PREFILL, ...): 8 bytes per query
- *              row (a sort key and a slot of the row order) when the call
- *              orders its rows -- bf16, 16 query heads with (kv_heads,
- *              head_dim) in {(2,128), (2,64), (1,128)}, batch*n_q >= 1024 and
- *              batch <= 1024 -- else 0 bytes.  Rows whose selections share a
- *              region of the cache are run together so that their K/V reads
- *              hit the same L2; the order changes no output bit.
+ *   workspace  >= qsa_workspace_size(QSA_OP_PREFILL, ...).  For bf16 with 16
+ *              query heads and (kv_heads, head_dim) in {(2,128), (2,64),
+ *              (1,128)}: 8 bytes per query row (a sort key and a walk start),
+ *              12 when batch*n_q >= 1024 and batch <= 1024 (plus a slot of the
+ *              row order); else 0 bytes.  Rows whose selections cluster in
+ *              one region of the cache are run together, each starting its
+ *              walk in that region, so that their K/V reads hit the same L2.
+ *              A row's bits depend on its own inputs only, not on the call.
  */
 qsa_status qsa_sparse_attn_prefill(const qsa_config* cfg, int32_t batch, int32_t n_q,
                                    const void* q, const void* k_cache, const void* v_cache,

@@ -102,9 +102,10 @@ def test_workspace_sizes(lib):
     want = _al(want + 4 * rows)
     assert qsa.qsa_workspace_size(c, B.QSA_OP_SELECT, 8, 1, 262211) == want
     assert qsa.qsa_workspace_size(c, B.QSA_OP_INDEX_BUILD, 1, 1, 10) == 0
-    assert qsa.qsa_workspace_size(c, B.QSA_OP_PREFILL, 1, 100, 100) == 0
-    # prefill with 1,024 rows or more: a sort key and an order slot per row
-    assert qsa.qsa_workspace_size(c, B.QSA_OP_PREFILL, 2, 8192, 139264) == 8 * 2 * 8192
+    # prefill: a sort key and a walk start per row, and with 1,024 rows or
+    # more an order slot
+    assert qsa.qsa_workspace_size(c, B.QSA_OP_PREFILL, 1, 100, 100) == 8 * 100
+    assert qsa.qsa_workspace_size(c, B.QSA_OP_PREFILL, 2, 8192, 139264) == 12 * 2 * 8192
     assert qsa.qsa_workspace_size(cfg(dtype=B.QSA_F32), B.QSA_OP_PREFILL, 2, 8192, 139264) == 0
     # decode: 17 splits of the token set, each 16 heads x (128 + 2) floats
     assert (qsa.qsa_workspace_size(c, B.QSA_OP_DECODE, 8, 1, 300000)
