@@ -403,16 +403,11 @@ hipError_t launch_mfma(const Dims& d, int batch, int n_q, const void* q, const v
   if (!decode) {
     int32_t* key = static_cast<int32_t*>(ws);
     int32_t* fst = key + rows;
-    const int nb = order_bins_per_seq(batch);
-    hipLaunchKernelGGL(attn_order_key_kernel, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, st,
-                       sel, cnt, q_pos0, n_q, rows, cap, d.kB, d.lr, nb, key, fst);
-    if (use_order(d, batch, rows, decode))
-      hipLaunchKernelGGL(attn_order_sort_kernel, dim3(1), dim3(1024), 0, st, key, rows,
-                         batch * nb, fst + rows);
-    const hipError_t e = hipGetLastError();
+    int32_t* ord = use_order(d, batch, rows, decode) ? fst + rows : nullptr;
+    const hipError_t e = launch_row_order(d, batch, n_q, q_pos0, cap, sel, cnt, key, fst, ord, st);
     if (e != hipSuccess) return e;
     first = fst;
-    if (use_order(d, batch, rows, decode)) order = fst + rows;
+    order = ord;
   }
   const dim3 grid((unsigned)(rows * ns));
   if (d.lr < 2)
@@ -437,6 +432,23 @@ hipError_t launch_mfma(const Dims& d, int batch, int n_q, const void* q, const v
 }
 
 }  // namespace
+
+bool row_order_sorts(const Dims& d, int batch, int n_q) {
+  return use_order(d, batch, batch * n_q, false);
+}
+
+hipError_t launch_row_order(const Dims& d, int batch, int n_q, const int32_t* q_pos0,
+                            int64_t cap, const int32_t* sel, const int32_t* cnt, int32_t* key,
+                            int32_t* first, int32_t* order, hipStream_t st) {
+  const int rows = batch * n_q;
+  const int nb = order_bins_per_seq(batch);
+  hipLaunchKernelGGL(attn_order_key_kernel, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, st,
+                     sel, cnt, q_pos0, n_q, rows, cap, d.kB, d.lr, nb, key, first);
+  if (order)
+    hipLaunchKernelGGL(attn_order_sort_kernel, dim3(1), dim3(1024), 0, st, key, rows,
+                       batch * nb, order);
+  return hipGetLastError();
+}
 
 size_t attn_workspace_bytes(const Dims& d, int batch, int n_q, bool decode) {
   const int rows = batch * n_q;

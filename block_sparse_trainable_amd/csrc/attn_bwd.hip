@@ -193,7 +193,7 @@ __global__ __launch_bounds__(256, 2) void bwd_query_mfma_kernel(
     const uint16_t* __restrict__ out, const float* __restrict__ lse,
     const uint16_t* __restrict__ dout, uint16_t* __restrict__ dq, float* __restrict__ dlt,
     float2* __restrict__ pw, int max_pb, uint16_t* __restrict__ qt, uint16_t* __restrict__ dot,
-    int lr) {
+    int lr, const int32_t* __restrict__ order, const int32_t* __restrict__ first) {
   using S = MfmaShape<HKV, D>;
   constexpr int KD = S::KD, NK = S::NK, ROWB = S::ROWB, CH = S::CH, RPI = S::RPI;
   constexpr int MF = S::MERGE_FLOATS, DP = S::DP;
@@ -208,11 +208,14 @@ __global__ __launch_bounds__(256, 2) void bwd_query_mfma_kernel(
   __shared__ float dref[16], dpart[4][16];
   __shared__ u32x4 dbs[NK * 64];   // dObd in lane order (kept out of registers)
   int64_t row;
-  {  // contiguous runs of rows per XCD (workgroup b goes to XCD b % 8)
+  {  // contiguous runs of items per XCD (workgroup b goes to XCD b % 8)
     const uint32_t n = gridDim.x, b = blockIdx.x;
     const uint32_t qn = n / 8u, rn = n % 8u, x = b % 8u;
     row = (int64_t)(x * qn + min(x, rn) + b / 8u);
   }
+  // as in the forward: item i takes row order[i], rows whose selections
+  // cluster in one region of the cache running together
+  if (order) row = min(max((int64_t)order[row], (int64_t)0), (int64_t)gridDim.x - 1);
   const int s = (int)(row / n_q);
   const int j = (int)(row % n_q);
   const int64_t p = min(max((int64_t)q_pos0[s] + j, (int64_t)0), cap - 1);
@@ -289,12 +292,18 @@ __global__ __launch_bounds__(256, 2) void bwd_query_mfma_kernel(
   unsigned char* kt = lds + wave * TILE;
 
   // Tiles of TT / 4 list entries, wave w taking tiles w, w + 4, ...  As in
-  // the forward, the walk starts (p mod kBwdSweep) / kBwdSweep of the way
-  // into the list and wraps, so the rows resident on an XCD read shared
-  // blocks together; a tile keeps its list index (pb0), which places its
-  // {P, weight} export, and the sums do not depend on the order.
+  // the forward, the walk starts at the tile holding the first block of the
+  // row's top region when its selection clusters there, else
+  // (p mod kBwdSweep) / kBwdSweep of the way into the list, and wraps, so
+  // the rows resident on an XCD read shared blocks together; a tile keeps
+  // its list index (pb0), which places its {P, weight} export, and the sums
+  // do not depend on the order.
   const int ntile = (npb + TT / 4 - 1) / (TT / 4);
-  const int trot = (int)((p % kBwdSweep) * ntile / kBwdSweep);
+  int trot = (int)((p % kBwdSweep) * ntile / kBwdSweep);
+  if (first) {
+    const int f = first[row];
+    if (f >= 0) trot = min((f << lm) / (TT / 4), ntile - 1);
+  }
   for (int t = wave; t < ntile; t += 4) {
     const int pb0 = (TT / 4) * (t + trot < ntile ? t + trot : t + trot - ntile);
     // ---- V rows into A-operand registers
@@ -991,7 +1000,7 @@ struct BwdPlan {
   bool mfma;
   int64_t nb;   // blocks (generic) or 16-token groups (MFMA) per sequence
   int max_pb;   // 4-token units of a largest token set
-  size_t off_cnt, off_cur, off_off, off_list, off_dsum, off_qt, off_dot, off_pw, bytes;
+  size_t off_cnt, off_cur, off_off, off_list, off_dsum, off_qt, off_dot, off_pw, off_ord, bytes;
 };
 
 BwdPlan bwd_plan(const Dims& d, int batch, int n_q, int32_t max_pos_end) {
@@ -1014,6 +1023,7 @@ BwdPlan bwd_plan(const Dims& d, int batch, int n_q, int32_t max_pos_end) {
     p.off_qt = o;  o = al(o + 2 * rows * hd * (size_t)d.head_dim);
     p.off_dot = o; o = al(o + 2 * rows * hd * (size_t)d.head_dim);
     p.off_pw = o;  o = al(o + 8 * rows * (size_t)p.max_pb * 4 * hd);
+    p.off_ord = o; o = al(o + 3 * 4 * rows);   // row order: key, first, order
   }
   p.bytes = o;
   return p;
@@ -1051,6 +1061,12 @@ hipError_t launch_attn_backward(const Dims& d, int batch, int n_q, const void* q
     hipLaunchKernelGGL(bwd_scan_kernel, dim3(1), dim3(kNT), 0, st, ix, nblk);
     hipLaunchKernelGGL((bwd_group_list_kernel<true>), dim3((unsigned)rows), dim3(kNT), 0, st, ix,
                        glist, cap, n_q, q_pos0, sel, cnt, d.kB, d.lr);
+    int32_t* okey = reinterpret_cast<int32_t*>(ws + pl.off_ord);
+    int32_t* ofirst = okey + rows;
+    int32_t* oorder = row_order_sorts(d, batch, n_q) ? ofirst + rows : nullptr;
+    const hipError_t e = launch_row_order(d, batch, n_q, q_pos0, cap, sel, cnt, okey, ofirst,
+                                          oorder, st);
+    if (e != hipSuccess) return e;
 #define QSA_BWD_MFMA(HKV, DD)                                                                  \
   if (d.kv_heads == HKV && d.head_dim == DD) {                                                 \
     hipLaunchKernelGGL((bwd_query_mfma_kernel<HKV, DD, (HKV == 2 && DD == 128) ? 16 : 32>),    \
@@ -1059,7 +1075,7 @@ hipError_t launch_attn_backward(const Dims& d, int batch, int n_q, const void* q
                        static_cast<const uint16_t*>(v_cache), cap, n_q, q_pos0, sel, cnt, d.kB, \
                        d.scale, static_cast<const uint16_t*>(out), lse,                       \
                        static_cast<const uint16_t*>(dout), static_cast<uint16_t*>(dq), dsum, pw, \
-                       pl.max_pb, qt, dot, d.lr);                                              \
+                       pl.max_pb, qt, dot, d.lr, oorder, ofirst);                              \
     hipLaunchKernelGGL((bwd_key_mfma_kernel<HKV, DD>), dim3((unsigned)nblk), dim3(256), 0, st, ix, \
                        glist, pw, pl.max_pb, qt, dot, dsum, cap, d.scale, dk, dv);             \
   }

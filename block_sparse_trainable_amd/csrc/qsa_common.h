@@ -258,6 +258,16 @@ hipError_t launch_decode_step(const Dims& d, const StepPlan& pl, int batch, cons
 // row order (MFMA path, 1,024 rows or more).
 size_t attn_workspace_bytes(const Dims& d, int batch, int n_q, bool decode);
 
+// Row order of a prefill-shaped call (one work item per query row): per
+// row a sort key and the list index where its walk starts (-1: the
+// position's own start), and, when row_order_sorts(), order[] = the rows
+// grouped by the region their selection clusters in, then the rest in
+// natural order.  key, first and order hold batch * n_q int32 each.
+bool row_order_sorts(const Dims& d, int batch, int n_q);
+hipError_t launch_row_order(const Dims& d, int batch, int n_q, const int32_t* q_pos0,
+                            int64_t cap, const int32_t* sel, const int32_t* cnt, int32_t* key,
+                            int32_t* first, int32_t* order, hipStream_t st);
+
 // Attention backward: transposed index (per-block query lists) and per-head D.
 hipError_t launch_offload_stage(const Dims& d, int batch, const int32_t* q_pos,
                                 const int32_t* sel, const int32_t* cnt, const void* k_host_dev,

@@ -316,8 +316,10 @@ const char* qsa_last_error(void);  /* thread-local text of the last failure */
  *              max_pos_end): transposed query lists and per-head sums; for
  *              bf16 layers with 16 query heads also q/dO transposed and
  *              8 bytes per (query, token of its set, head) of softmax
- *              values -- about 4.3 GB for 16,384 queries at k_B = 512.
- *              Nothing is kept in it between calls.
+ *              values -- about 4.3 GB for 16,384 queries at k_B = 512 --
+ *              and 12 bytes per query of row order (queries whose
+ *              selections cluster in one region of the cache run together,
+ *              as in the forward).  Nothing is kept in it between calls.
  * Supported: kv_heads <= 2 (any dtype, head_dim, block size the forward
  * takes); sel_blocks ascending without repeats, as qsa_select_topk writes
  * them.  dq is deterministic; dk/dv sum each token's queries in an order

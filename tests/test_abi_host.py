@@ -271,7 +271,8 @@ def test_backward_validation_and_workspace(lib):
     c = cfg(token_budget=256)                         # k_B = 64
     # MFMA shapes: counters per 16-token group, lists of uint2 (one per unit
     # of a largest token set, k_B + 1 at r = 4), D - D~ per head, q and dO
-    # transposed, {P, weight} per (token of the set, head)
+    # transposed, {P, weight} per (token of the set, head), and the row order
+    # (sort key, walk start, order slot per row)
     ng = (1000 + 15) // 16
     want = _al(4 * 2 * ng)
     want = _al(want + 4 * 2 * ng)
@@ -281,6 +282,7 @@ def test_backward_validation_and_workspace(lib):
     want = _al(want + 2 * 1000 * 16 * 128)
     want = _al(want + 2 * 1000 * 16 * 128)
     want = _al(want + 8 * 1000 * 65 * 4 * 16)
+    want = _al(want + 12 * 1000)
     assert qsa.qsa_workspace_size(c, B.QSA_OP_BACKWARD, 2, 500, 1000) == want
     # other shapes (fp32 here): per-block counters and lists, per-head D
     c32 = cfg(token_budget=256, dtype=B.QSA_F32, q_heads=4, kv_heads=1, head_dim=64)
