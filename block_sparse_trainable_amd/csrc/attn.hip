@@ -124,6 +124,10 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(
   using S = MfmaShape<HKV, D>;
   __shared__ __attribute__((aligned(16))) unsigned char lds[S::LDS_BYTES];
   __shared__ int32_t sbid[TOK ? kMaxTok : kMaxPB];
+  // the software-pipelined tile walk (two 128-dim KV heads): its query
+  // operand is read from LDS
+  constexpr bool PIPE = !TOK && HKV == 2 && D == 128;
+  __shared__ u32x4 qlds[PIPE ? S::NK * 64 : 1];
   // Workgroups are handed to the 8 XCDs in turn (workgroup b to XCD b % 8):
   // give each XCD one contiguous run of items, so that the queries it holds
   // at once, whose selections overlap, share an L2.  A bijection for any
@@ -176,6 +180,10 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(
                                (i & ((1 << lm) - 1)))
                    : (int32_t)((c << lm) + (i - nsel));
     load_qbd<HKV, D>(q, row, qb);
+    if (PIPE && threadIdx.x < 64) {
+#pragma unroll
+      for (int kk = 0; kk < S::NK; ++kk) qlds[kk * 64 + threadIdx.x] = qb[kk];
+    }
     __syncthreads();
     // One split per row (prefill): the walk starts rot entries into the
     // list and wraps.  A row whose selection clusters in one region starts
@@ -192,8 +200,9 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(
       const int f = first[row];
       if (f >= 0) rot = min(f << lm, npb - 1);
     }
-    attn_mfma_tiles<HKV, D, false>(qb, kc, vc, cap, s, p, row, item, pb_lo, pb_hi, sbid,
-                                   scale_log2, out, lse, part, n_split, lds, 0, rot);
+    attn_mfma_tiles<HKV, D, false, false, PIPE>(qb, kc, vc, cap, s, p, row, item, pb_lo, pb_hi,
+                                                 sbid, scale_log2, out, lse, part, n_split, lds,
+                                                 0, rot, qlds);
   }
 }
 

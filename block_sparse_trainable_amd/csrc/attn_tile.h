@@ -103,6 +103,13 @@ __device__ __forceinline__ void load_qbd(const uint16_t* __restrict__ q, int64_t
   }
 }
 
+// s_waitcnt immediate (gfx9 encoding) for vmcnt <= 2 NK with no expcnt or
+// lgkmcnt wait: vmcnt bits [3:0] and [15:14], expcnt [6:4] = 7, lgkmcnt
+// [11:8] = 15.
+template <int NK>
+constexpr int kWaitVm2NK = ((2 * NK) & 15) | (((2 * NK) >> 4) << 14) | (7 << 4) | (15 << 8);
+static_assert(2 * 8 < 64, "vmcnt has 6 bits");
+
 // Attends query row `row` (sequence s, position p) over pseudo-blocks
 // [pb_lo, pb_hi) whose block ids the caller has put in sbid[0 ..) (the tail
 // block c = floor(p/4) included as an ordinary id), for work item `item` =
@@ -112,14 +119,15 @@ __device__ __forceinline__ void load_qbd(const uint16_t* __restrict__ q, int64_t
 // log-sum-exp; otherwise the split's (m, l, O) state goes to part (with
 // coherent stores when COHERENT: another workgroup of the same kernel reads
 // it).  lds: MfmaShape::LDS_BYTES bytes.  Called by all 256 threads after a
-// barrier that publishes sbid.
-template <int HKV, int D, bool COHERENT, bool TOK = false>
+// barrier that publishes sbid (and, with PIPE, qlds: the query operand
+// qb of every lane, [NK][64] in lane order).
+template <int HKV, int D, bool COHERENT, bool TOK = false, bool PIPE = false>
 __device__ __forceinline__ void attn_mfma_tiles(
     const u32x4 (&qb)[MfmaShape<HKV, D>::NK], const uint16_t* __restrict__ kc,
     const uint16_t* __restrict__ vc, int64_t cap, int s, int64_t p, int64_t row, int64_t item,
     int pb_lo, int pb_hi, const int32_t* sbid, float scale_log2, uint16_t* __restrict__ out,
     float* __restrict__ lse, float* __restrict__ part, int n_split, unsigned char* lds,
-    int t_hi = 0, int rot = 0) {
+    int t_hi = 0, int rot = 0, const u32x4* qlds = nullptr) {
   using S = MfmaShape<HKV, D>;
   constexpr int KD = S::KD, NK = S::NK, ROWB = S::ROWB, G = S::G, CH = S::CH, RPI = S::RPI;
   constexpr int MF = S::MERGE_FLOATS;
@@ -150,9 +158,8 @@ __device__ __forceinline__ void attn_mfma_tiles(
   for (int pp = 0; pp < NK; ++pp) oacc[pp][0] = oacc[pp][1] = f32x4{0.f, 0.f, 0.f, 0.f};
   unsigned char* vt = lds + wave * S::TILE_LDS;
 
-  for (int pb0 = pb_lo + 8 * wave; pb0 < pb_hi; pb0 += 32) {
-    // ---- K rows straight into A-operand registers (needed first)
-    u32x4 kreg[2][NK];
+  // K rows of the tile at pb0 straight into A-operand registers
+  auto load_k = [&](int pb0, u32x4 (&kreg)[2][NK]) {
 #pragma unroll
     for (int st = 0; st < 2; ++st) {
       const int tk = 16 * st + l16;
@@ -169,8 +176,10 @@ __device__ __forceinline__ void attn_mfma_tiles(
 #pragma unroll
       for (int kk = 0; kk < NK; ++kk) kreg[st][kk] = ld16(kp + 32 * kk);
     }
-    // ---- V rows of the tile's 32 tokens: straight from HBM into this wave's
-    // LDS tile (lane-ordered 1 KiB per instruction, chunk-swizzled)
+  };
+  // V rows of the tile's 32 tokens: straight from HBM into this wave's LDS
+  // tile (lane-ordered 1 KiB per instruction, chunk-swizzled)
+  auto load_v = [&](int pb0) {
 #pragma unroll
     for (int u = 0; u < 32 / RPI; ++u) {
       const int tk = RPI * u + lane / CH;
@@ -188,16 +197,44 @@ __device__ __forceinline__ void attn_mfma_tiles(
           (const __attribute__((address_space(1))) void*)(vbase + rp * KD + chunk * 8),
           (__attribute__((address_space(3))) void*)(vt + u * 1024), 16, 0, 0);
     }
-    // ---- S^T = K * Qbd: lane holds tokens 16st + 4gq + i for head l16
-    f32x4 sacc[2];
-#pragma unroll
-    for (int st = 0; st < 2; ++st) {
-      sacc[st] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int kk = 0; kk < NK; ++kk)
-        sacc[st] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kreg[st][kk]),
-                                                           as_bf16x8(qb[kk]), sacc[st], 0, 0, 0);
+  };
+
+  // PIPE: a software pipeline per wave.  The next tile's K loads are issued
+  // as soon as this tile's scores have consumed kreg, so they fly during
+  // the softmax and the P.V products; the next tile's V loads, issued once
+  // the P.V products have read this tile's V from LDS, fly during the next
+  // tile's scores and softmax.  The compiler counts loads into registers
+  // and loads into LDS as events that may complete out of order, so any
+  // wait it places for kreg while V loads are in flight is a wait for all
+  // of them: an explicit full wait before each V issue leaves kreg complete,
+  // and it places none.  It takes ~30 more VGPRs and the query operand is
+  // read from LDS, so only the two-128-dim-KV-head shape uses it.
+  // Otherwise each tile issues its K and V loads at its start.
+  u32x4 kreg[2][NK];
+  if constexpr (PIPE) {
+    load_k(pb_lo + 8 * wave, kreg);   // (a wave without tiles reads row p)
+    __builtin_amdgcn_s_waitcnt(0);
+    load_v(pb_lo + 8 * wave);
+  }
+  for (int pb0 = pb_lo + 8 * wave; pb0 < pb_hi; pb0 += 32) {
+    const bool more = PIPE && pb0 + 32 < pb_hi;
+    if constexpr (!PIPE) {
+      load_k(pb0, kreg);
+      load_v(pb0);
     }
+    // ---- S^T = K * Qbd: lane holds tokens 16st + 4gq + i for head l16
+    // (PIPE reads the query operand from LDS, qlds[kk * 64 + lane], which
+    // leaves its registers to the pipeline)
+    f32x4 sacc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+    for (int kk = 0; kk < NK; ++kk) {
+      const u32x4 qv = PIPE ? qlds[kk * 64 + lane] : qb[kk];
+#pragma unroll
+      for (int st = 0; st < 2; ++st)
+        sacc[st] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kreg[st][kk]),
+                                                           as_bf16x8(qv), sacc[st], 0, 0, 0);
+    }
+    if (more) load_k(pb0 + 32, kreg);
     float x[2][4];
     float mt = -INFINITY;
 #pragma unroll
@@ -236,7 +273,12 @@ __device__ __forceinline__ void attn_mfma_tiles(
       const int st = e >> 1, i0 = 2 * (e & 1);
       pv[e] = f32_to_bf16(pr[st][i0]) | (f32_to_bf16(pr[st][i0 + 1]) << 16);
     }
-    __builtin_amdgcn_s_waitcnt(0);  // this wave's V tile has landed in LDS
+    // this wave's V tile has landed in LDS: every load but the next tile's
+    // 2 NK K loads, issued after it, is done (vmcnt counts in issue order)
+    if (more)
+      __builtin_amdgcn_s_waitcnt(kWaitVm2NK<NK>);
+    else
+      __builtin_amdgcn_s_waitcnt(0);
     wave_sync();
     // ---- O^T += V^T * P^T; k-slot (gq, e) <-> token (e<4 ? 4gq+e : 16+4gq+e-4)
 #pragma unroll
@@ -260,7 +302,12 @@ __device__ __forceinline__ void attn_mfma_tiles(
                                                             oacc[pp][1], 0, 0, 0);
     }
     wave_sync();  // all reads of this tile issued before the next tile's loads
+    if (more) {
+      __builtin_amdgcn_s_waitcnt(0);  // the next K has landed in kreg
+      load_v(pb0 + 32);
+    }
   }
+  if constexpr (PIPE) __builtin_amdgcn_s_waitcnt(0);  // (a wave without tiles: its loads)
 
   // ---- merge the four waves' states: per head, M = max_w m_w,
   // f_w = 2^(m_w - M) (waves without tokens skipped), Z = sum_w f_w l_w,
