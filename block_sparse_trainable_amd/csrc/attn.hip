@@ -275,10 +275,23 @@ __global__ __launch_bounds__(256) void attn_order_key_kernel(
     const int64_t p = min(max((int64_t)q_pos0[s] + row % n_q, (int64_t)0), cap - 1);
     c = p >> lr;
     count = (int)min((int64_t)max(cnt[row], 0), min((int64_t)kB, c));
-    for (int i = lane; i < count; i += 64) {
+    // lane l counts entries [l*E, l*E + E) in runs of equal bins: an
+    // ascending list has few runs, so few (contended) LDS atomics
+    const int E = (count + 63) >> 6;
+    const int i1 = min(count, (lane + 1) * E);
+    int cur = 0;
+    uint32_t run = 0u;
+    for (int i = lane * E; i < i1; ++i) {
       const int64_t b = min(max((int64_t)srow[i], (int64_t)0), c - 1);
-      atomicAdd(&h[wave][((b << lr) >> kOrderRegionShift) & (kOrderBins - 1)], 1u);
+      const int bin = (int)(((b << lr) >> kOrderRegionShift) & (kOrderBins - 1));
+      if (bin != cur) {
+        if (run) atomicAdd(&h[wave][cur], run);
+        cur = bin;
+        run = 0u;
+      }
+      ++run;
     }
+    if (run) atomicAdd(&h[wave][cur], run);
   }
   __syncthreads();
   // (count << 16) | (0xFFFF - bin): the largest is the most frequent bin,
