@@ -172,8 +172,9 @@ qsa_status qsa_select_topk(const qsa_config* cfg, int32_t batch, int32_t n_q,
  *   out        (dtype) [batch][n_q][q_heads][head_dim].
  *   lse        float [batch][n_q][q_heads] natural-log normaliser, or NULL.
  *   workspace  >= qsa_workspace_size(QSA_OP_PREFILL, ...).  For bf16 with 16
- *              query heads and (kv_heads, head_dim) in {(2,128), (2,64),
- *              (1,128)}: 8 bytes per query row (a sort key and a walk start),
+ *              query heads, (kv_heads, head_dim) in {(2,128), (2,64),
+ *              (1,128)} and block_size >= 2: 8 bytes per query row (a sort
+ *              key and a walk start),
  *              12 when batch*n_q >= 1024 and batch <= 1024 (plus a slot of the
  *              row order); else 0 bytes.  Rows whose selections cluster in
  *              one region of the cache are run together, each starting its
