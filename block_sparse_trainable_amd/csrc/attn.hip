@@ -113,8 +113,12 @@ __global__ __launch_bounds__(256) void attn_generic_kernel(
 
 // ---------------------------------------------------------------- MFMA ----
 constexpr int kSweep = 64;   // prefill walk: rows per sweep (about the workgroups resident per XCD)
-template <int HKV, int D, bool TOK>
-__global__ __launch_bounds__(256, 2) void attn_mfma_kernel(
+// T16: the 16-token tile walk, three workgroups per CU (prefill of the two-
+// 128-dim-KV-head shape, not the token mode); otherwise 32-token tiles, two
+// per CU.  Decode splits keep the 32-token walk: the fused decode step
+// attends with it and must give the same bits.
+template <int HKV, int D, bool TOK, bool T16>
+__global__ __launch_bounds__(256, (T16 ? 3 : 2)) void attn_mfma_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kc,
     const uint16_t* __restrict__ vc, int64_t cap, int n_q, const int32_t* __restrict__ q_pos0,
     const int32_t* __restrict__ sel, const int32_t* __restrict__ cnt, int kB, float scale_log2,
@@ -122,12 +126,11 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(
     int n_split, int pb_per_split, int lr, const int32_t* __restrict__ order,
     const int32_t* __restrict__ first) {
   using S = MfmaShape<HKV, D>;
-  __shared__ __attribute__((aligned(16))) unsigned char lds[S::LDS_BYTES];
+  static_assert(!T16 || (!TOK && HKV == 2 && D == 128), "16-token walk: two 128-dim KV heads");
+  __shared__ __attribute__((aligned(16))) unsigned char lds[T16 ? S::LDS16_BYTES : S::LDS_BYTES];
   __shared__ int32_t sbid[TOK ? kMaxTok : kMaxPB];
-  // the software-pipelined tile walk (two 128-dim KV heads): its query
-  // operand is read from LDS
-  constexpr bool PIPE = !TOK && HKV == 2 && D == 128;
-  __shared__ u32x4 qlds[PIPE ? S::NK * 64 : 1];
+  // the 16-token walk reads its query operand from LDS
+  __shared__ u32x4 qlds[T16 ? S::NK * 64 : 1];
   // Workgroups are handed to the 8 XCDs in turn (workgroup b to XCD b % 8):
   // give each XCD one contiguous run of items, so that the queries it holds
   // at once, whose selections overlap, share an L2.  A bijection for any
@@ -191,7 +194,7 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(
                                (i & ((1 << lm) - 1)))
                    : (int32_t)((c << lm) + (i - nsel));
     load_qbd<HKV, D>(q, row, qb);
-    if (PIPE && threadIdx.x < 64) {
+    if (T16 && threadIdx.x < 64) {
 #pragma unroll
       for (int kk = 0; kk < S::NK; ++kk) qlds[kk * 64 + threadIdx.x] = qb[kk];
     }
@@ -206,14 +209,18 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(
     // then at the same fraction of their lists, where neighbouring rows'
     // shared blocks sit.  The row's own selection and position fix the
     // start, so a query gives the same bits in any call.
-    int rot = n_split == 1 ? (int)((p % kSweep) * npb / kSweep) : 0;
+    constexpr int SW = T16 ? 3 * kSweep / 2 : kSweep;   // resident rows per XCD
+    int rot = n_split == 1 ? (int)((p % SW) * npb / SW) : 0;
     if (first) {
       const int f = first[row];
       if (f >= 0) rot = min(f << lm, npb - 1);
     }
-    attn_mfma_tiles<HKV, D, false, false, PIPE>(qb, kc, vc, cap, s, p, row, item, pb_lo, pb_hi,
-                                                 sbid, scale_log2, out, lse, part, n_split, lds,
-                                                 0, rot, qlds);
+    if constexpr (T16)
+      attn_mfma_tiles16<HKV, D>(qlds, kc, vc, cap, s, p, row, item, pb_lo, pb_hi, sbid,
+                                scale_log2, out, lse, part, n_split, lds, rot);
+    else
+      attn_mfma_tiles<HKV, D, false>(qb, kc, vc, cap, s, p, row, item, pb_lo, pb_hi, sbid,
+                                     scale_log2, out, lse, part, n_split, lds, 0, rot);
   }
 }
 
@@ -448,15 +455,22 @@ hipError_t launch_mfma(const Dims& d, int batch, int n_q, const void* q, const v
     order = ord;
   }
   const dim3 grid((unsigned)(rows * ns));
-  if (d.lr < 2)
-    hipLaunchKernelGGL((attn_mfma_kernel<HKV, D, true>), grid, dim3(256), 0, st,
+  constexpr bool kT16 = HKV == 2 && D == 128;
+  if (d.lr >= 2 && !decode && kT16)
+    hipLaunchKernelGGL((attn_mfma_kernel<HKV, D, false, kT16>), grid, dim3(256), 0, st,
+                       static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(kc),
+                       static_cast<const uint16_t*>(vc), cap, n_q, q_pos0, sel, cnt, d.kB, sl2,
+                       static_cast<uint16_t*>(out), lse, part, ns, max_pseudo_blocks(d), d.lr,
+                       order, first);
+  else if (d.lr < 2)
+    hipLaunchKernelGGL((attn_mfma_kernel<HKV, D, true, false>), grid, dim3(256), 0, st,
                        static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(kc),
                        static_cast<const uint16_t*>(vc), cap, n_q, q_pos0, sel, cnt, d.kB, sl2,
                        static_cast<uint16_t*>(out), lse, part, ns,
                        decode ? decode_pb_per_split(max_pseudo_blocks(d)) : max_pseudo_blocks(d), d.lr,
                        order, first);
   else
-    hipLaunchKernelGGL((attn_mfma_kernel<HKV, D, false>), grid, dim3(256), 0, st,
+    hipLaunchKernelGGL((attn_mfma_kernel<HKV, D, false, false>), grid, dim3(256), 0, st,
                        static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(kc),
                        static_cast<const uint16_t*>(vc), cap, n_q, q_pos0, sel, cnt, d.kB, sl2,
                        static_cast<uint16_t*>(out), lse, part, ns,

@@ -57,6 +57,9 @@ struct MfmaShape {
   // the four V tiles, or the wave merge: 4 states + per-head factors, Z, M
   static constexpr int MERGE_BYTES = 4 * MERGE_FLOATS * 4 + (4 * HQ + 2 * HQ) * 4;
   static constexpr int LDS_BYTES = (4 * TILE_LDS > MERGE_BYTES) ? 4 * TILE_LDS : MERGE_BYTES;
+  // 16-token tiles (attn_mfma_tiles16): half the V tile per wave
+  static constexpr int TILE16_LDS = 16 * ROWB;
+  static constexpr int LDS16_BYTES = (4 * TILE16_LDS > MERGE_BYTES) ? 4 * TILE16_LDS : MERGE_BYTES;
   static_assert(CH == 16 || CH == 32, "the V swizzle needs 16 or 32 chunks per row");
 };
 
@@ -110,205 +113,21 @@ template <int NK>
 constexpr int kWaitVm2NK = ((2 * NK) & 15) | (((2 * NK) >> 4) << 14) | (7 << 4) | (15 << 8);
 static_assert(2 * 8 < 64, "vmcnt has 6 bits");
 
-// Attends query row `row` (sequence s, position p) over pseudo-blocks
-// [pb_lo, pb_hi) whose block ids the caller has put in sbid[0 ..) (the tail
-// block c = floor(p/4) included as an ordinary id), for work item `item` =
-// row * n_split + split.  TOK (token mode): sbid[i] is instead the position
-// of token slot 4*pb_lo + i, and slots at or past t_hi are empty.
-// n_split == 1 writes the bf16 output and the
-// log-sum-exp; otherwise the split's (m, l, O) state goes to part (with
-// coherent stores when COHERENT: another workgroup of the same kernel reads
-// it).  lds: MfmaShape::LDS_BYTES bytes.  Called by all 256 threads after a
-// barrier that publishes sbid (and, with PIPE, qlds: the query operand
-// qb of every lane, [NK][64] in lane order).
-template <int HKV, int D, bool COHERENT, bool TOK = false, bool PIPE = false>
-__device__ __forceinline__ void attn_mfma_tiles(
-    const u32x4 (&qb)[MfmaShape<HKV, D>::NK], const uint16_t* __restrict__ kc,
-    const uint16_t* __restrict__ vc, int64_t cap, int s, int64_t p, int64_t row, int64_t item,
-    int pb_lo, int pb_hi, const int32_t* sbid, float scale_log2, uint16_t* __restrict__ out,
-    float* __restrict__ lse, float* __restrict__ part, int n_split, unsigned char* lds,
-    int t_hi = 0, int rot = 0, const u32x4* qlds = nullptr) {
+// Merges the four waves' (m, l, O) states of one work item and writes the
+// bf16 output and log-sum-exp (n_split == 1) or the split's state to part
+// (with coherent stores when COHERENT).  Called by all 256 threads; lds:
+// MfmaShape::MERGE_BYTES bytes no wave reads any more.
+template <int HKV, int D, bool COHERENT>
+__device__ __forceinline__ void attn_merge_waves(
+    float m_run, float l_run, const f32x4 (&oacc)[MfmaShape<HKV, D>::NK][2], int64_t row,
+    int64_t item, uint16_t* __restrict__ out, float* __restrict__ lse,
+    float* __restrict__ part, int n_split, unsigned char* lds) {
   using S = MfmaShape<HKV, D>;
-  constexpr int KD = S::KD, NK = S::NK, ROWB = S::ROWB, G = S::G, CH = S::CH, RPI = S::RPI;
-  constexpr int MF = S::MERGE_FLOATS;
-  static_assert(S::MERGE_BYTES <= S::LDS_BYTES, "merge area must fit");
-
+  constexpr int NK = S::NK, G = S::G, MF = S::MERGE_FLOATS;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int l16 = lane & 15;
   const int gq = lane >> 4;
-  const uint16_t* kbase = kc + (int64_t)s * cap * KD;
-  const uint16_t* vbase = vc + (int64_t)s * cap * KD;
-  // block id of pseudo-block pb, -1 outside this work item; the walk may
-  // start rot entries into the list and wrap (the softmax sums do not
-  // depend on the order)
-  const int nlist = pb_hi - pb_lo;
-  auto bid = [&](int pb) -> int64_t {
-    if (pb >= pb_hi) return -1;
-    int i = pb - pb_lo + rot;
-    i -= i >= nlist ? nlist : 0;
-    return (int64_t)sbid[i];
-  };
-  // token mode: position of list slot sl, -1 past the list
-  auto tok = [&](int sl) -> int64_t { return (sl < t_hi) ? (int64_t)sbid[sl - 4 * pb_lo] : -1; };
-
-  float m_run = -INFINITY, l_run = 0.0f;
-  f32x4 oacc[NK][2];
-#pragma unroll
-  for (int pp = 0; pp < NK; ++pp) oacc[pp][0] = oacc[pp][1] = f32x4{0.f, 0.f, 0.f, 0.f};
-  unsigned char* vt = lds + wave * S::TILE_LDS;
-
-  // K rows of the tile at pb0 straight into A-operand registers
-  auto load_k = [&](int pb0, u32x4 (&kreg)[2][NK]) {
-#pragma unroll
-    for (int st = 0; st < 2; ++st) {
-      const int tk = 16 * st + l16;
-      int64_t rp;
-      if constexpr (TOK) {
-        const int64_t tp = tok(4 * pb0 + tk);
-        rp = tp >= 0 ? tp : p;
-      } else {
-        const int64_t b = bid(pb0 + (tk >> 2));
-        const int64_t tp = 4 * b + (tk & 3);
-        rp = (b >= 0 && tp <= p) ? tp : p;
-      }
-      const uint16_t* kp = kbase + rp * KD + 8 * gq;
-#pragma unroll
-      for (int kk = 0; kk < NK; ++kk) kreg[st][kk] = ld16(kp + 32 * kk);
-    }
-  };
-  // V rows of the tile's 32 tokens: straight from HBM into this wave's LDS
-  // tile (lane-ordered 1 KiB per instruction, chunk-swizzled)
-  auto load_v = [&](int pb0) {
-#pragma unroll
-    for (int u = 0; u < 32 / RPI; ++u) {
-      const int tk = RPI * u + lane / CH;
-      const int chunk = (lane % CH) ^ vswz(tk);
-      int64_t rp;
-      if constexpr (TOK) {
-        const int64_t tp = tok(4 * pb0 + tk);
-        rp = tp >= 0 ? tp : p;
-      } else {
-        const int64_t b = bid(pb0 + (tk >> 2));
-        const int64_t tp = 4 * b + (tk & 3);
-        rp = (b >= 0 && tp <= p) ? tp : p;
-      }
-      __builtin_amdgcn_global_load_lds(
-          (const __attribute__((address_space(1))) void*)(vbase + rp * KD + chunk * 8),
-          (__attribute__((address_space(3))) void*)(vt + u * 1024), 16, 0, 0);
-    }
-  };
-
-  // PIPE: a software pipeline per wave.  The next tile's K loads are issued
-  // as soon as this tile's scores have consumed kreg, so they fly during
-  // the softmax and the P.V products; the next tile's V loads, issued once
-  // the P.V products have read this tile's V from LDS, fly during the next
-  // tile's scores and softmax.  The compiler counts loads into registers
-  // and loads into LDS as events that may complete out of order, so any
-  // wait it places for kreg while V loads are in flight is a wait for all
-  // of them: an explicit full wait before each V issue leaves kreg complete,
-  // and it places none.  It takes ~30 more VGPRs and the query operand is
-  // read from LDS, so only the two-128-dim-KV-head shape uses it.
-  // Otherwise each tile issues its K and V loads at its start.
-  u32x4 kreg[2][NK];
-  if constexpr (PIPE) {
-    load_k(pb_lo + 8 * wave, kreg);   // (a wave without tiles reads row p)
-    __builtin_amdgcn_s_waitcnt(0);
-    load_v(pb_lo + 8 * wave);
-  }
-  for (int pb0 = pb_lo + 8 * wave; pb0 < pb_hi; pb0 += 32) {
-    const bool more = PIPE && pb0 + 32 < pb_hi;
-    if constexpr (!PIPE) {
-      load_k(pb0, kreg);
-      load_v(pb0);
-    }
-    // ---- S^T = K * Qbd: lane holds tokens 16st + 4gq + i for head l16
-    // (PIPE reads the query operand from LDS, qlds[kk * 64 + lane], which
-    // leaves its registers to the pipeline)
-    f32x4 sacc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
-#pragma unroll
-    for (int kk = 0; kk < NK; ++kk) {
-      const u32x4 qv = PIPE ? qlds[kk * 64 + lane] : qb[kk];
-#pragma unroll
-      for (int st = 0; st < 2; ++st)
-        sacc[st] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kreg[st][kk]),
-                                                           as_bf16x8(qv), sacc[st], 0, 0, 0);
-    }
-    if (more) load_k(pb0 + 32, kreg);
-    float x[2][4];
-    float mt = -INFINITY;
-#pragma unroll
-    for (int st = 0; st < 2; ++st) {
-      const int64_t b = TOK ? 0 : bid(pb0 + 4 * st + gq);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const bool ok = TOK ? 4 * (pb0 + 4 * st + gq) + i < t_hi : (b >= 0 && 4 * b + i <= p);
-        x[st][i] = ok ? sacc[st][i] * scale_log2 : -INFINITY;
-        mt = fmaxf(mt, x[st][i]);
-      }
-    }
-    mt = wave_max_xor32(wave_max_xor16(mt));
-    const float m_new = fmaxf(m_run, mt);
-    const bool any = m_new != -INFINITY;
-    const float alpha = any ? exp2_fast(m_run - m_new) : 1.0f;
-    float pr[2][4];
-    float psum = 0.0f;
-#pragma unroll
-    for (int st = 0; st < 2; ++st)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        pr[st][i] = any ? exp2_fast(x[st][i] - m_new) : 0.0f;
-        psum += pr[st][i];
-      }
-    l_run = l_run * alpha + psum;
-    m_run = m_new;
-#pragma unroll
-    for (int pp = 0; pp < NK; ++pp) {
-      oacc[pp][0] *= alpha;
-      oacc[pp][1] *= alpha;
-    }
-    u32x4 pv;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int st = e >> 1, i0 = 2 * (e & 1);
-      pv[e] = f32_to_bf16(pr[st][i0]) | (f32_to_bf16(pr[st][i0 + 1]) << 16);
-    }
-    // this wave's V tile has landed in LDS: every load but the next tile's
-    // 2 NK K loads, issued after it, is done (vmcnt counts in issue order)
-    if (more)
-      __builtin_amdgcn_s_waitcnt(kWaitVm2NK<NK>);
-    else
-      __builtin_amdgcn_s_waitcnt(0);
-    wave_sync();
-    // ---- O^T += V^T * P^T; k-slot (gq, e) <-> token (e<4 ? 4gq+e : 16+4gq+e-4)
-#pragma unroll
-    for (int pp = 0; pp < NK; ++pp) {
-      uint32_t w[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int tr = (e < 4) ? (4 * gq + e) : (16 + 4 * gq + e - 4);
-        const int chunk = (4 * pp + (l16 >> 2)) ^ vswz(tr);
-        w[e] = *reinterpret_cast<const uint32_t*>(vt + tr * ROWB + chunk * 16 + 4 * (l16 & 3));
-      }
-      u32x4 a0, a1;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        a0[e] = (w[2 * e] & 0xFFFFu) | (w[2 * e + 1] << 16);
-        a1[e] = (w[2 * e] >> 16) | (w[2 * e + 1] & 0xFFFF0000u);
-      }
-      oacc[pp][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a0), as_bf16x8(pv),
-                                                            oacc[pp][0], 0, 0, 0);
-      oacc[pp][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a1), as_bf16x8(pv),
-                                                            oacc[pp][1], 0, 0, 0);
-    }
-    wave_sync();  // all reads of this tile issued before the next tile's loads
-    if (more) {
-      __builtin_amdgcn_s_waitcnt(0);  // the next K has landed in kreg
-      load_v(pb0 + 32);
-    }
-  }
-  if constexpr (PIPE) __builtin_amdgcn_s_waitcnt(0);  // (a wave without tiles: its loads)
-
   // ---- merge the four waves' states: per head, M = max_w m_w,
   // f_w = 2^(m_w - M) (waves without tokens skipped), Z = sum_w f_w l_w,
   // O = sum_w f_w O_w, in wave order
@@ -411,6 +230,327 @@ __device__ __forceinline__ void attn_mfma_tiles(
       }
     }
   }
+}
+
+// The walk of attn_mfma_tiles in 16-token tiles (prefill and decode splits
+// of the two-KV-head shapes; not the token mode): wave w takes tiles of 4
+// pseudo-blocks at pb_lo + 4 w, pb_lo + 4 w + 16, ...  Half the V tile per
+// wave, half the K registers and P.V products of 16 x 16 x 16 (the k-slots
+// are the tile's 16 tokens), so the kernel fits three workgroups per CU
+// instead of two: more gathers in flight per CU, which is what bounds this
+// walk once the L2 catches the shared blocks.  Software-pipelined per wave:
+// the next tile's K loads are issued as soon as this tile's scores have
+// consumed kreg (they fly during the softmax), its V loads after a full
+// wait that follows this tile's P.V products (they fly during the next
+// tile's scores and softmax).  The compiler counts loads into registers and
+// loads into LDS as events that may complete out of order, so any wait it
+// placed for kreg while V loads fly would be a wait for all of them; the
+// explicit full wait before each V issue leaves kreg complete, and it
+// places none.  qlds: the query operand qb of every lane, [NK][64] in lane
+// order (kept out of registers), published with sbid.
+template <int HKV, int D>
+__device__ __forceinline__ void attn_mfma_tiles16(
+    const u32x4* qlds, const uint16_t* __restrict__ kc, const uint16_t* __restrict__ vc,
+    int64_t cap, int s, int64_t p, int64_t row, int64_t item, int pb_lo, int pb_hi,
+    const int32_t* sbid, float scale_log2, uint16_t* __restrict__ out, float* __restrict__ lse,
+    float* __restrict__ part, int n_split, unsigned char* lds, int rot) {
+  using S = MfmaShape<HKV, D>;
+  constexpr int KD = S::KD, NK = S::NK, ROWB = S::ROWB, CH = S::CH, RPI = S::RPI;
+  static_assert(S::MERGE_BYTES <= S::LDS16_BYTES, "merge area must fit");
+  typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int l16 = lane & 15;
+  const int gq = lane >> 4;
+  const uint16_t* kbase = kc + (int64_t)s * cap * KD;
+  const uint16_t* vbase = vc + (int64_t)s * cap * KD;
+  const int nlist = pb_hi - pb_lo;
+  auto bid = [&](int pb) -> int64_t {
+    if (pb >= pb_hi) return -1;
+    int i = pb - pb_lo + rot;
+    i -= i >= nlist ? nlist : 0;
+    return (int64_t)sbid[i];
+  };
+  // row of token tk (0..15) of the tile at pb0; a masked token reads row p
+  auto trow = [&](int pb0, int tk) -> int64_t {
+    const int64_t b = bid(pb0 + (tk >> 2));
+    const int64_t tp = 4 * b + (tk & 3);
+    return (b >= 0 && tp <= p) ? tp : p;
+  };
+  unsigned char* vt = lds + wave * S::TILE16_LDS;
+  auto load_k = [&](int pb0, u32x4 (&kreg)[NK]) {
+    const uint16_t* kp = kbase + trow(pb0, l16) * KD + 8 * gq;
+#pragma unroll
+    for (int kk = 0; kk < NK; ++kk) kreg[kk] = ld16(kp + 32 * kk);
+  };
+  auto load_v = [&](int pb0) {
+#pragma unroll
+    for (int u = 0; u < 16 / RPI; ++u) {
+      const int tk = RPI * u + lane / CH;
+      const int chunk = (lane % CH) ^ vswz(tk);
+      __builtin_amdgcn_global_load_lds(
+          (const __attribute__((address_space(1))) void*)(vbase + trow(pb0, tk) * KD + chunk * 8),
+          (__attribute__((address_space(3))) void*)(vt + u * 1024), 16, 0, 0);
+    }
+  };
+
+  float m_run = -INFINITY, l_run = 0.0f;
+  f32x4 oacc[NK][2];
+#pragma unroll
+  for (int pp = 0; pp < NK; ++pp) oacc[pp][0] = oacc[pp][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+  u32x4 kreg[NK];
+  load_k(pb_lo + 4 * wave, kreg);   // (a wave without tiles reads row p)
+  __builtin_amdgcn_s_waitcnt(0);
+  load_v(pb_lo + 4 * wave);
+  for (int pb0 = pb_lo + 4 * wave; pb0 < pb_hi; pb0 += 16) {
+    const bool more = pb0 + 16 < pb_hi;
+    // ---- S^T = K * Qbd: lane holds tokens 4gq + i for head l16
+    f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kk = 0; kk < NK; ++kk)
+      sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kreg[kk]),
+                                                     as_bf16x8(qlds[kk * 64 + lane]), sacc, 0,
+                                                     0, 0);
+    if (more) load_k(pb0 + 16, kreg);
+    float x[4];
+    float mt = -INFINITY;
+    {
+      const int64_t b = bid(pb0 + gq);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const bool ok = b >= 0 && 4 * b + i <= p;
+        x[i] = ok ? sacc[i] * scale_log2 : -INFINITY;
+        mt = fmaxf(mt, x[i]);
+      }
+    }
+    mt = wave_max_xor32(wave_max_xor16(mt));
+    const float m_new = fmaxf(m_run, mt);
+    const bool any = m_new != -INFINITY;
+    const float alpha = any ? exp2_fast(m_run - m_new) : 1.0f;
+    float pr[4];
+    float psum = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      pr[i] = any ? exp2_fast(x[i] - m_new) : 0.0f;
+      psum += pr[i];
+    }
+    l_run = l_run * alpha + psum;
+    m_run = m_new;
+#pragma unroll
+    for (int pp = 0; pp < NK; ++pp) {
+      oacc[pp][0] *= alpha;
+      oacc[pp][1] *= alpha;
+    }
+    // P^T operand: k-slot (gq, e) <-> token 4gq + e, column = head l16
+    s16x4 pv;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) pv[e] = (short)f32_to_bf16(pr[e]);
+    // this wave's V tile has landed in LDS (the compiler also waits for
+    // every load before the LDS reads below: see attn_mfma_tiles)
+    if (more)
+      __builtin_amdgcn_s_waitcnt(kWaitVm2NK<NK / 2>);
+    else
+      __builtin_amdgcn_s_waitcnt(0);
+    wave_sync();
+    // ---- O^T += V^T * P^T: A row l16 <-> dims 32 pp + 2 l16 (+1 for a1)
+#pragma unroll
+    for (int pp = 0; pp < NK; ++pp) {
+      uint32_t w[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int tr = 4 * gq + e;
+        const int chunk = (4 * pp + (l16 >> 2)) ^ vswz(tr);
+        w[e] = *reinterpret_cast<const uint32_t*>(vt + tr * ROWB + chunk * 16 + 4 * (l16 & 3));
+      }
+      s16x4 a0, a1;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        a0[e] = (short)(w[e] & 0xFFFFu);
+        a1[e] = (short)(w[e] >> 16);
+      }
+      oacc[pp][0] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a0, pv, oacc[pp][0], 0, 0, 0);
+      oacc[pp][1] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a1, pv, oacc[pp][1], 0, 0, 0);
+    }
+    wave_sync();  // all reads of this tile issued before the next tile's loads
+    if (more) {
+      __builtin_amdgcn_s_waitcnt(0);  // the next K has landed in kreg
+      load_v(pb0 + 16);
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(0);  // (a wave without tiles: its loads)
+
+  attn_merge_waves<HKV, D, false>(m_run, l_run, oacc, row, item, out, lse, part, n_split, lds);
+}
+
+// Attends query row `row` (sequence s, position p) over pseudo-blocks
+// [pb_lo, pb_hi) whose block ids the caller has put in sbid[0 ..) (the tail
+// block c = floor(p/4) included as an ordinary id), for work item `item` =
+// row * n_split + split.  TOK (token mode): sbid[i] is instead the position
+// of token slot 4*pb_lo + i, and slots at or past t_hi are empty.
+// n_split == 1 writes the bf16 output and the
+// log-sum-exp; otherwise the split's (m, l, O) state goes to part (with
+// coherent stores when COHERENT: another workgroup of the same kernel reads
+// it).  lds: MfmaShape::LDS_BYTES bytes.  Called by all 256 threads after a
+// barrier that publishes sbid.
+template <int HKV, int D, bool COHERENT, bool TOK = false>
+__device__ __forceinline__ void attn_mfma_tiles(
+    const u32x4 (&qb)[MfmaShape<HKV, D>::NK], const uint16_t* __restrict__ kc,
+    const uint16_t* __restrict__ vc, int64_t cap, int s, int64_t p, int64_t row, int64_t item,
+    int pb_lo, int pb_hi, const int32_t* sbid, float scale_log2, uint16_t* __restrict__ out,
+    float* __restrict__ lse, float* __restrict__ part, int n_split, unsigned char* lds,
+    int t_hi = 0, int rot = 0) {
+  using S = MfmaShape<HKV, D>;
+  constexpr int KD = S::KD, NK = S::NK, ROWB = S::ROWB, G = S::G, CH = S::CH, RPI = S::RPI;
+  constexpr int MF = S::MERGE_FLOATS;
+  static_assert(S::MERGE_BYTES <= S::LDS_BYTES, "merge area must fit");
+
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int l16 = lane & 15;
+  const int gq = lane >> 4;
+  const uint16_t* kbase = kc + (int64_t)s * cap * KD;
+  const uint16_t* vbase = vc + (int64_t)s * cap * KD;
+  // block id of pseudo-block pb, -1 outside this work item; the walk may
+  // start rot entries into the list and wrap (the softmax sums do not
+  // depend on the order)
+  const int nlist = pb_hi - pb_lo;
+  auto bid = [&](int pb) -> int64_t {
+    if (pb >= pb_hi) return -1;
+    int i = pb - pb_lo + rot;
+    i -= i >= nlist ? nlist : 0;
+    return (int64_t)sbid[i];
+  };
+  // token mode: position of list slot sl, -1 past the list
+  auto tok = [&](int sl) -> int64_t { return (sl < t_hi) ? (int64_t)sbid[sl - 4 * pb_lo] : -1; };
+
+  float m_run = -INFINITY, l_run = 0.0f;
+  f32x4 oacc[NK][2];
+#pragma unroll
+  for (int pp = 0; pp < NK; ++pp) oacc[pp][0] = oacc[pp][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+  unsigned char* vt = lds + wave * S::TILE_LDS;
+
+  // K rows of the tile at pb0 straight into A-operand registers
+  auto load_k = [&](int pb0, u32x4 (&kreg)[2][NK]) {
+#pragma unroll
+    for (int st = 0; st < 2; ++st) {
+      const int tk = 16 * st + l16;
+      int64_t rp;
+      if constexpr (TOK) {
+        const int64_t tp = tok(4 * pb0 + tk);
+        rp = tp >= 0 ? tp : p;
+      } else {
+        const int64_t b = bid(pb0 + (tk >> 2));
+        const int64_t tp = 4 * b + (tk & 3);
+        rp = (b >= 0 && tp <= p) ? tp : p;
+      }
+      const uint16_t* kp = kbase + rp * KD + 8 * gq;
+#pragma unroll
+      for (int kk = 0; kk < NK; ++kk) kreg[st][kk] = ld16(kp + 32 * kk);
+    }
+  };
+  // V rows of the tile's 32 tokens: straight from HBM into this wave's LDS
+  // tile (lane-ordered 1 KiB per instruction, chunk-swizzled)
+  auto load_v = [&](int pb0) {
+#pragma unroll
+    for (int u = 0; u < 32 / RPI; ++u) {
+      const int tk = RPI * u + lane / CH;
+      const int chunk = (lane % CH) ^ vswz(tk);
+      int64_t rp;
+      if constexpr (TOK) {
+        const int64_t tp = tok(4 * pb0 + tk);
+        rp = tp >= 0 ? tp : p;
+      } else {
+        const int64_t b = bid(pb0 + (tk >> 2));
+        const int64_t tp = 4 * b + (tk & 3);
+        rp = (b >= 0 && tp <= p) ? tp : p;
+      }
+      __builtin_amdgcn_global_load_lds(
+          (const __attribute__((address_space(1))) void*)(vbase + rp * KD + chunk * 8),
+          (__attribute__((address_space(3))) void*)(vt + u * 1024), 16, 0, 0);
+    }
+  };
+
+  // each tile issues its K and V loads at its start
+  u32x4 kreg[2][NK];
+  for (int pb0 = pb_lo + 8 * wave; pb0 < pb_hi; pb0 += 32) {
+    load_k(pb0, kreg);
+    load_v(pb0);
+    // ---- S^T = K * Qbd: lane holds tokens 16st + 4gq + i for head l16
+    f32x4 sacc[2];
+#pragma unroll
+    for (int st = 0; st < 2; ++st) {
+      sacc[st] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kk = 0; kk < NK; ++kk)
+        sacc[st] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kreg[st][kk]),
+                                                           as_bf16x8(qb[kk]), sacc[st], 0, 0, 0);
+    }
+    float x[2][4];
+    float mt = -INFINITY;
+#pragma unroll
+    for (int st = 0; st < 2; ++st) {
+      const int64_t b = TOK ? 0 : bid(pb0 + 4 * st + gq);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const bool ok = TOK ? 4 * (pb0 + 4 * st + gq) + i < t_hi : (b >= 0 && 4 * b + i <= p);
+        x[st][i] = ok ? sacc[st][i] * scale_log2 : -INFINITY;
+        mt = fmaxf(mt, x[st][i]);
+      }
+    }
+    mt = wave_max_xor32(wave_max_xor16(mt));
+    const float m_new = fmaxf(m_run, mt);
+    const bool any = m_new != -INFINITY;
+    const float alpha = any ? exp2_fast(m_run - m_new) : 1.0f;
+    float pr[2][4];
+    float psum = 0.0f;
+#pragma unroll
+    for (int st = 0; st < 2; ++st)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        pr[st][i] = any ? exp2_fast(x[st][i] - m_new) : 0.0f;
+        psum += pr[st][i];
+      }
+    l_run = l_run * alpha + psum;
+    m_run = m_new;
+#pragma unroll
+    for (int pp = 0; pp < NK; ++pp) {
+      oacc[pp][0] *= alpha;
+      oacc[pp][1] *= alpha;
+    }
+    u32x4 pv;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int st = e >> 1, i0 = 2 * (e & 1);
+      pv[e] = f32_to_bf16(pr[st][i0]) | (f32_to_bf16(pr[st][i0 + 1]) << 16);
+    }
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's V tile has landed in LDS
+    wave_sync();
+    // ---- O^T += V^T * P^T; k-slot (gq, e) <-> token (e<4 ? 4gq+e : 16+4gq+e-4)
+#pragma unroll
+    for (int pp = 0; pp < NK; ++pp) {
+      uint32_t w[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int tr = (e < 4) ? (4 * gq + e) : (16 + 4 * gq + e - 4);
+        const int chunk = (4 * pp + (l16 >> 2)) ^ vswz(tr);
+        w[e] = *reinterpret_cast<const uint32_t*>(vt + tr * ROWB + chunk * 16 + 4 * (l16 & 3));
+      }
+      u32x4 a0, a1;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        a0[e] = (w[2 * e] & 0xFFFFu) | (w[2 * e + 1] << 16);
+        a1[e] = (w[2 * e] >> 16) | (w[2 * e + 1] & 0xFFFF0000u);
+      }
+      oacc[pp][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a0), as_bf16x8(pv),
+                                                            oacc[pp][0], 0, 0, 0);
+      oacc[pp][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a1), as_bf16x8(pv),
+                                                            oacc[pp][1], 0, 0, 0);
+    }
+    wave_sync();  // all reads of this tile issued before the next tile's loads
+  }
+
+  attn_merge_waves<HKV, D, COHERENT>(m_run, l_run, oacc, row, item, out, lse, part, n_split, lds);
 }
 
 // Log-sum-exp merge of one (row, head, dim) over a row's kDecodeSplits split
