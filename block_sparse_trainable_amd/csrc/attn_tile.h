@@ -266,11 +266,13 @@ __device__ __forceinline__ void attn_mfma_tiles16(
   const uint16_t* kbase = kc + (int64_t)s * cap * KD;
   const uint16_t* vbase = vc + (int64_t)s * cap * KD;
   const int nlist = pb_hi - pb_lo;
+  // (branch-free: the LDS read is clamped into the list, its value
+  // discarded past the list)
   auto bid = [&](int pb) -> int64_t {
-    if (pb >= pb_hi) return -1;
     int i = pb - pb_lo + rot;
     i -= i >= nlist ? nlist : 0;
-    return (int64_t)sbid[i];
+    const int32_t v = sbid[max(min(i, nlist - 1), 0)];
+    return pb < pb_hi ? (int64_t)v : (int64_t)-1;
   };
   // row of token tk (0..15) of the tile at pb0; a masked token reads row p
   auto trow = [&](int pb0, int tk) -> int64_t {
@@ -337,10 +339,14 @@ __device__ __forceinline__ void attn_mfma_tiles16(
     }
     l_run = l_run * alpha + psum;
     m_run = m_new;
+    // once the running maxima settle most tiles leave every alpha at 1:
+    // skipping the 4 NK multiplies by 1.0 changes no bit
+    if (__any(alpha != 1.0f)) {
 #pragma unroll
-    for (int pp = 0; pp < NK; ++pp) {
-      oacc[pp][0] *= alpha;
-      oacc[pp][1] *= alpha;
+      for (int pp = 0; pp < NK; ++pp) {
+        oacc[pp][0] *= alpha;
+        oacc[pp][1] *= alpha;
+      }
     }
     // P^T operand: k-slot (gq, e) <-> token 4gq + e, column = head l16
     s16x4 pv;
