@@ -256,14 +256,15 @@ __global__ __launch_bounds__(D) void attn_merge_kernel(const float* __restrict__
 // grouped by that region: the rows of a group then run together on one XCD
 // and read the region's K/V rows while they are in its L2.  A region is
 // 1,024 tokens (1 MB of K and V at 2 x 128 bf16 dims, a quarter of an XCD's
-// L2), binned modulo kOrderBins per row.  A row counts as clustered when its
-// most frequent region holds at least 1/8 of its selected blocks and at
-// least 4 times the share an even spread over its candidates would give it;
+// L2); a row's regions are binned modulo kOrderBins (256 regions span 256K
+// tokens).  A row counts as clustered when its most frequent region holds at
+// least 1/8 of its selected blocks and at least 4 times the share an even
+// spread over its candidates would give it;
 // the other rows keep their natural order, after the clustered ones, where
 // neighbouring positions share their candidate ranges.  The order changes
 // no result: every row computes the same bits wherever it runs.
 constexpr int kOrderRegionShift = 10;  // log2 tokens per region
-constexpr int kOrderBins = 1024;       // region bins of one row's histogram
+constexpr int kOrderBins = 256;        // region bins of one row's histogram
 constexpr int kOrderKeys = 8192;       // sort keys: batch x bins per sequence
 constexpr int kOrderMinRows = 1024;    // fewer rows do not fill the XCDs twice
 
@@ -383,7 +384,12 @@ __global__ __launch_bounds__(1024) void attn_order_sort_kernel(const int32_t* __
       if (pos < (uint32_t)rows) order[pos] = r;
     }
   }
-  // the other rows, in order: 1,024 per round, ranked by ballots
+  // the other rows, in order: with no clustered row that is the identity;
+  // otherwise 1,024 rows per round, ranked by ballots
+  if (clustered == 0u) {
+    for (int r = t; r < rows; r += 1024) order[r] = r;
+    return;
+  }
   uint32_t done = clustered;
   for (int r0 = 0; r0 < rows; r0 += 1024) {
     const int r = r0 + t;
