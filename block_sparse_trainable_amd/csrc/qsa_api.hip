@@ -165,7 +165,7 @@ qsa_status scratch_for_current_device(const char* fn, void** ptr, bool* first) {
 
 extern "C" {
 
-int32_t qsa_abi_version(void) { return 1; }
+int32_t qsa_abi_version(void) { return 2; }
 
 const char* qsa_last_error(void) { return g_err; }
 

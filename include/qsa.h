@@ -436,7 +436,9 @@ qsa_status qsa_offload_stage(const qsa_config* cfg, int32_t batch, const int32_t
                              int32_t* stage_sel, int32_t* stage_cnt, int32_t* stage_pos,
                              int32_t* stats, hipStream_t stream);
 
-int32_t qsa_abi_version(void);     /* 1 */
+/* qsa_abi_version -- 2: the prefill attention and the backward take a
+ * workspace for their row order (version 1 took none for the prefill).    */
+int32_t qsa_abi_version(void);
 
 #ifdef __cplusplus
 }

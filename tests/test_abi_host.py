@@ -49,7 +49,7 @@ def test_exports_every_declared_symbol(lib):
     for n in names:
         assert n in exported, n
         assert hasattr(lib, n)
-    assert lib.qsa_abi_version() == 1
+    assert lib.qsa_abi_version() == 2
 
 
 def test_config_struct_layout_matches_header():
