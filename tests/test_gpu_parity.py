@@ -230,6 +230,41 @@ def test_row_order_changes_no_bit():
         assert torch.equal(lse[:, j0:j0 + n], l2), f"rows {j0}..{j0 + n}: lse differs"
 
 
+def test_prefill_attention_takes_unordered_lists():
+    say("prefill attention: each row's selection in a seeded random order (2 x 3,000 rows, "
+        "row order on) == the ascending lists, and sampled rows == the oracle")
+    x = synth.chunked(cache=20000, chunk=3000, batch=2, window=2048, n_far=6)
+    dl, outs = _run_prefill(x)
+    sel, cnt, _, out, lse = outs
+    rng = np.random.default_rng(7)
+    sel_h = sel.cpu().numpy().copy()
+    cnt_h = cnt.cpu().numpy()
+    for s in range(x.batch):
+        for j in range(x.n_q):
+            c = int(cnt_h[s, j])
+            sel_h[s, j, :c] = rng.permutation(sel_h[s, j, :c])
+    shuf = torch.tensor(sel_h, device=sel.device)
+    o2 = torch.full_like(out, float("nan"))
+    l2 = torch.full_like(lse, float("nan"))
+    end = int(x.q_pos0.max()) + x.n_q
+    dl.attend_prefill(dl.q, dl.i32(x.q_pos0), end, shuf, cnt, o2, l2)
+    torch.cuda.synchronize()
+    a, b = to_f32(out), to_f32(o2)
+    assert np.isfinite(b).all(), "a row was not written"
+    assert np.abs(a - b).max() <= C.ATOL["bf16"]
+    assert np.abs(lse.cpu().numpy() - l2.cpu().numpy()).max() <= C.LSE_ATOL["bf16"]
+    lay = x.layout
+    scale = 1.0 / math.sqrt(lay.head_dim)
+    for s in range(x.batch):
+        K = C.f64(x.k[s], "bf16")
+        V = C.f64(x.v[s], "bf16")
+        for j in (0, 1, 777, 2998, 2999):
+            p = int(x.q_pos0[s]) + j
+            c = int(cnt_h[s, j])
+            C.check_attention(p, np.sort(sel_h[s, j, :c]), C.f64(x.q[s, j], "bf16"), K, V,
+                              b[s, j], l2.cpu().numpy()[s, j], scale, "bf16")
+
+
 def test_prefill_deterministic():
     say("determinism")
     x = synth.prefill(n=2100)
