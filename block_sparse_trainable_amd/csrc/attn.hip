@@ -259,14 +259,14 @@ __global__ __launch_bounds__(D) void attn_merge_kernel(const float* __restrict__
 // L2); a row's regions are binned modulo kOrderBins (256 regions span 256K
 // tokens).  A row counts as clustered when its most frequent region holds at
 // least 1/8 of its selected blocks and at least 4 times the share an even
-// spread over its candidates would give it;
-// the other rows keep their natural order, after the clustered ones, where
-// neighbouring positions share their candidate ranges.  The order changes
-// no result: every row computes the same bits wherever it runs.
+// spread over its candidates would give it; the other rows keep their
+// natural order, after the clustered ones, where neighbouring positions
+// share their candidate ranges.  The order changes no result: every row
+// computes the same bits wherever it runs.
 constexpr int kOrderRegionShift = 10;  // log2 tokens per region
 constexpr int kOrderBins = 256;        // region bins of one row's histogram
 constexpr int kOrderKeys = 8192;       // sort keys: batch x bins per sequence
-constexpr int kOrderMinRows = 1024;    // fewer rows do not fill the XCDs twice
+constexpr int kOrderMinRows = 1024;    // smaller calls keep the natural order
 
 int order_bins_per_seq(int batch) {
   const int nb = kOrderKeys / batch < kOrderBins ? kOrderKeys / batch : kOrderBins;
@@ -325,14 +325,17 @@ __global__ __launch_bounds__(256) void attn_order_key_kernel(
   // top / count >= 1/8 and >= 4 * (region blocks) / c
   const int64_t region_blocks = (int64_t)1 << (kOrderRegionShift - lr);
   const bool clustered = count > 0 && 8 * top >= count && top * c >= 4 * region_blocks * count;
-  // the first list entry in the top bin
+  // the first list entry in the top bin (a clustered row only; the test is
+  // uniform over the wave)
   int f = 0x7FFFFFFF;
-  for (int i = lane; i < count; i += 64) {
-    const int64_t b = min(max((int64_t)srow[i], (int64_t)0), c - 1);
-    if ((int)(((b << lr) >> kOrderRegionShift) & (kOrderBins - 1)) == bin) f = min(f, i);
-  }
+  if (clustered) {
+    for (int i = lane; i < count; i += 64) {
+      const int64_t b = min(max((int64_t)srow[i], (int64_t)0), c - 1);
+      if ((int)(((b << lr) >> kOrderRegionShift) & (kOrderBins - 1)) == bin) f = min(f, i);
+    }
 #pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) f = min(f, __shfl_xor(f, off));
+    for (int off = 32; off >= 1; off >>= 1) f = min(f, __shfl_xor(f, off));
+  }
   if (live && lane == 0) {
     key[row] = clustered ? s * nb + bin % nb : -1;
     first[row] = clustered && f < count ? f : -1;
