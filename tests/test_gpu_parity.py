@@ -13,6 +13,7 @@ import pytest
 import torch
 
 from oracle import qsa_oracle as O
+from block_sparse_trainable_amd import _binding as B
 from block_sparse_trainable_amd import synth
 from block_sparse_trainable_amd.runtime import DeviceLayer, bf16_bits, to_f32
 from tests import _compare as C
@@ -208,16 +209,26 @@ def test_chunked_equals_monolithic_bitwise():
     assert torch.equal(dl.k_cmp, dl2.k_cmp)
 
 
-def test_row_order_changes_no_bit():
-    say("prefill attention: one call over 2 x 3,000 rows (rows run in region order) == "
+@pytest.mark.parametrize("r", [4, 2, 16])
+def test_row_order_changes_no_bit(r):
+    say(f"prefill attention r={r}: one call over 2 x 3,000 rows (rows run in region order) == "
         "the same rows in calls of 1,000 rows (natural order)")
-    x = synth.chunked(cache=20000, chunk=3000, batch=2, window=2048, n_far=6)
+    x = synth.chunked(cache=20000, chunk=3000, batch=2, window=2048, n_far=6,
+                      layout=synth.Layout(block_size=r))
     dl = DeviceLayer(x)
     dl.build_prefix(x.cache_len)
     outs = dl.alloc_prefill_outputs()
     outs[3].fill_(float("nan"))   # a row the ordered call skipped stays NaN
     outs[4].fill_(float("nan"))
     sel, cnt, _, out, lse = dl.prefill_chunk(outs)
+    torch.cuda.synchronize()
+    # the call's workspace holds [sort key | walk start | order] per row: the
+    # order is a permutation and the workload has clustered rows (key >= 0)
+    rows = x.batch * x.n_q
+    ws = dl.workspace(B.QSA_OP_PREFILL, x.batch, x.n_q, int(x.q_pos0.max()) + x.n_q)
+    w = ws[:12 * rows].view(torch.int32).cpu().numpy()
+    assert (np.sort(w[2 * rows:3 * rows]) == np.arange(rows)).all()
+    assert (w[:rows] >= 0).sum() > rows // 4, "too few clustered rows to exercise the order"
     end = int(x.q_pos0.max()) + x.n_q
     for j0 in range(0, x.n_q, 500):   # 2 x 500 rows per call: no reordering
         n = min(500, x.n_q - j0)
